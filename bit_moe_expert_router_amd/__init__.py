@@ -1,0 +1,164 @@
+"""Routed mixture-of-experts layer on MI355X (gfx950).
+
+Thin ctypes binding over ``libmoe.so`` (declared in ``include/moe.h``): argument
+marshalling only, every step of the layer runs in the library's HIP kernels.
+PyTorch supplies device memory and streams.  The functions keep the C-ABI's
+names (``moe_route``, ``moe_forward``, ``set_expert_table`` ...) and take torch
+tensors where the C side takes device pointers.
+
+There is no fallback: if the HIP library is missing, importing this package
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_E_ARG, MOE_E_UNSUPPORTED, MOE_E_NOMEM, MOE_E_HIP, MOE_E_STATE = range(6)
+_STATUS = {0: "MOE_OK", 1: "MOE_E_ARG", 2: "MOE_E_UNSUPPORTED", 3: "MOE_E_NOMEM",
+           4: "MOE_E_HIP", 5: "MOE_E_STATE"}
+
+
+class moe_cfg(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("bits", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("scale_f16", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int32)]
+
+
+class moe_expert_ref(ctypes.Structure):
+    _fields_ = [("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p)]
+
+
+EXPORTS = ("moe_create", "moe_destroy", "moe_workspace_bytes", "moe_workspace_init",
+           "set_expert_table", "moe_expert_table_device", "moe_set_shared", "moe_route",
+           "moe_forward", "moe_rmsnorm_bf16", "moe_last_error")
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int
+    lib.moe_create.argtypes = [ctypes.POINTER(moe_cfg), i32, ctypes.POINTER(vp)]
+    lib.moe_destroy.argtypes = [vp]
+    lib.moe_workspace_bytes.argtypes = [vp, i32]
+    lib.moe_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_workspace_init.argtypes = [vp, vp, ctypes.c_size_t, vp]
+    lib.set_expert_table.argtypes = [vp, i32, ctypes.POINTER(moe_expert_ref), vp]
+    lib.moe_expert_table_device.argtypes = [vp, i32]
+    lib.moe_expert_table_device.restype = vp
+    lib.moe_set_shared.argtypes = [vp, i32, vp, vp, vp]
+    lib.moe_route.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.moe_forward.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                ctypes.c_size_t, vp]
+    lib.moe_rmsnorm_bf16.argtypes = [vp, vp, vp, i32, ctypes.c_float, vp, vp]
+    lib.moe_last_error.restype = ctypes.c_char_p
+    for f in ("moe_create", "moe_destroy", "moe_workspace_init", "set_expert_table",
+              "moe_set_shared", "moe_route", "moe_forward", "moe_rmsnorm_bf16"):
+        getattr(lib, f).restype = st
+    return lib
+
+
+lib = _load()
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.moe_last_error().decode()
+        super().__init__(f"{where}: {_STATUS.get(status, status)}: {msg}")
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoEError(status, where)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ------------------------------------------------------------------ C-ABI wrappers
+def moe_create(hidden, inter, n_experts, top_k, bits, group, scale_f16, shared_inter,
+               max_tokens, n_layers=1) -> int:
+    cfg = moe_cfg(hidden, inter, n_experts, top_k, bits, group, int(scale_f16), shared_inter,
+                  max_tokens)
+    out = ctypes.c_void_p()
+    _check(lib.moe_create(ctypes.byref(cfg), n_layers, ctypes.byref(out)), "moe_create")
+    return out.value
+
+
+def moe_destroy(ctx: int):
+    _check(lib.moe_destroy(ctx), "moe_destroy")
+
+
+def moe_workspace_bytes(ctx: int, n_tokens: int) -> int:
+    return lib.moe_workspace_bytes(ctx, n_tokens)
+
+
+def moe_workspace_init(ctx: int, ws, stream=None):
+    _check(lib.moe_workspace_init(ctx, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_workspace_init")
+
+
+def set_expert_table(ctx: int, layer: int, refs: Sequence[tuple], stream=None):
+    """refs[e] = (gate_ptr, up_ptr, down_ptr) device addresses, logical order."""
+    arr = (moe_expert_ref * len(refs))(*[moe_expert_ref(g, u, d) for g, u, d in refs])
+    _check(lib.set_expert_table(ctx, layer, arr, _stream(stream)), "set_expert_table")
+
+
+def moe_expert_table_device(ctx: int, layer: int) -> int:
+    return lib.moe_expert_table_device(ctx, layer) or 0
+
+
+def moe_set_shared(ctx: int, layer: int, gate, up, down):
+    _check(lib.moe_set_shared(ctx, layer, _ptr(gate), _ptr(up), _ptr(down)), "moe_set_shared")
+
+
+def moe_route(ctx: int, x_bf16, T: int, w_router, bias, topk_ids, topk_w, expert_offsets,
+              sorted_pairs, pair_pos, ws, stream=None):
+    _check(lib.moe_route(ctx, _ptr(x_bf16), T, _ptr(w_router), _ptr(bias), _ptr(topk_ids),
+                         _ptr(topk_w), _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(pair_pos),
+                         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_route")
+
+
+def moe_forward(ctx: int, layer: int, x_bf16, T: int, topk_ids, topk_w, expert_offsets,
+                sorted_pairs, pair_pos, out, pair_out, ws, stream=None):
+    _check(lib.moe_forward(ctx, layer, _ptr(x_bf16), T, _ptr(topk_ids), _ptr(topk_w),
+                           _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(pair_pos), _ptr(out),
+                           _ptr(pair_out), _ptr(ws), ws.numel() * ws.element_size(),
+                           _stream(stream)),
+           "moe_forward")
+
+
+def moe_last_error() -> str:
+    return lib.moe_last_error().decode()
+
+
+def moe_rmsnorm_bf16(ctx: int, resid, add, T: int, eps: float, y_bf16, stream=None):
+    _check(lib.moe_rmsnorm_bf16(ctx, _ptr(resid), _ptr(add), T, eps, _ptr(y_bf16),
+                                _stream(stream)),
+           "moe_rmsnorm_bf16")
+
+
+from .layer import MoELayer, RoutingBuffers  # noqa: E402,F401

@@ -1,0 +1,214 @@
+// api.hip -- the extern "C" boundary of libmoe.so (declared in include/moe.h):
+// argument checks, the device pointer tables, workspace geometry and dispatch.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "common.h"
+
+
+struct moe_ctx {
+  moe_cfg cfg;
+  int n_layers;
+  moe_expert_ref* d_tables;       // [n_layers][E] on the device
+  std::vector<char> table_set;    // per layer
+  struct Shared {
+    const void *g, *u, *d;
+  };
+  std::vector<Shared> shared;     // per layer
+};
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+moe_status ok() {
+  g_err[0] = 0;
+  return MOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+moe_status check_cfg(const moe_cfg& c) {
+  if (c.hidden <= 0 || c.inter <= 0 || c.n_experts <= 0 || c.top_k <= 0 || c.max_tokens <= 0)
+    return fail(MOE_E_ARG, "cfg: sizes must be positive");
+  if (!((c.bits == 3 && c.group == 128) || (c.bits == 4 && c.group == 32)))
+    return fail(MOE_E_UNSUPPORTED, "cfg: (bits, group) = (%d, %d) unsupported; use (3,128) or (4,32)",
+                c.bits, c.group);
+  if (c.hidden % 64 || c.inter % 64 || c.hidden % c.group || c.inter % c.group)
+    return fail(MOE_E_UNSUPPORTED, "cfg: hidden and inter must be multiples of 64 and of the group");
+  if (c.n_experts > 1024) return fail(MOE_E_UNSUPPORTED, "cfg: at most 1024 experts");
+  if (c.top_k > 16 || c.top_k > c.n_experts) return fail(MOE_E_UNSUPPORTED, "cfg: top_k must be <= min(16, E)");
+  if (c.shared_inter < 0) return fail(MOE_E_ARG, "cfg: shared_inter < 0");
+  if (c.shared_inter > 0 && (c.shared_inter % 256 || c.hidden % 256))
+    return fail(MOE_E_UNSUPPORTED, "cfg: shared expert needs hidden and shared_inter multiples of 256");
+  if ((int64_t)c.max_tokens * c.top_k > (1 << 30)) return fail(MOE_E_UNSUPPORTED, "cfg: max_tokens too large");
+  if (c.scale_f16 != 0 && c.scale_f16 != 1) return fail(MOE_E_ARG, "cfg: scale_f16 must be 0 or 1");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err; }
+
+moe_status moe_create(const moe_cfg* cfg, int32_t n_layers, moe_ctx** out) {
+  if (!cfg || !out) return fail(MOE_E_ARG, "moe_create: null argument");
+  *out = nullptr;
+  if (n_layers <= 0) return fail(MOE_E_ARG, "moe_create: n_layers must be positive");
+  moe_status st = check_cfg(*cfg);
+  if (st != MOE_OK) return st;
+  moe_ctx* c = new (std::nothrow) moe_ctx();
+  if (!c) return fail(MOE_E_NOMEM, "moe_create: host allocation");
+  c->cfg = *cfg;
+  c->n_layers = n_layers;
+  c->table_set.assign(n_layers, 0);
+  c->shared.assign(n_layers, moe_ctx::Shared{nullptr, nullptr, nullptr});
+  size_t tb = sizeof(moe_expert_ref) * (size_t)n_layers * cfg->n_experts;
+  if (hipMalloc(&c->d_tables, tb) != hipSuccess) {
+    delete c;
+    return fail(MOE_E_NOMEM, "moe_create: device tables (%zu bytes)", tb);
+  }
+  *out = c;
+  return ok();
+}
+
+moe_status moe_destroy(moe_ctx* ctx) {
+  if (!ctx) return ok();
+  (void)hipDeviceSynchronize();
+  (void)hipFree(ctx->d_tables);
+  delete ctx;
+  return ok();
+}
+
+size_t moe_workspace_bytes(const moe_ctx* ctx, int32_t n_tokens) {
+  if (!ctx || n_tokens < 0 || n_tokens > ctx->cfg.max_tokens) return 0;
+  return (size_t)moe::ws_layout(ctx->cfg, n_tokens).total;
+}
+
+moe_status moe_workspace_init(const moe_ctx* ctx, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  if (!ctx || !ws) return fail(MOE_E_ARG, "moe_workspace_init: null argument");
+  if (ws_bytes < 256) return fail(MOE_E_ARG, "moe_workspace_init: workspace too small");
+  hipStream_t s = (hipStream_t)stream;
+  return hip_status(moe::launch_zero_i32((int32_t*)ws, 64, s), "moe_workspace_init");
+}
+
+moe_status set_expert_table(moe_ctx* ctx, int32_t layer, const moe_expert_ref* host_table,
+                            moe_stream_t stream) {
+  if (!ctx || !host_table) return fail(MOE_E_ARG, "set_expert_table: null argument");
+  if (layer < 0 || layer >= ctx->n_layers) return fail(MOE_E_ARG, "set_expert_table: bad layer %d", layer);
+  const int E = ctx->cfg.n_experts;
+  for (int e = 0; e < E; ++e) {
+    const moe_expert_ref& r = host_table[e];
+    if (!r.gate || !r.up || !r.down)
+      return fail(MOE_E_ARG, "set_expert_table: expert %d has a null blob", e);
+    if (!aligned(r.gate, 256) || !aligned(r.up, 256) || !aligned(r.down, 256))
+      return fail(MOE_E_ARG, "set_expert_table: expert %d blob not 256-byte aligned", e);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err = hipMemcpyAsync(ctx->d_tables + (size_t)layer * E, host_table,
+                                  sizeof(moe_expert_ref) * E, hipMemcpyHostToDevice, s);
+  if (err != hipSuccess) return hip_status(err, "set_expert_table");
+  // the host table may be reused by the caller right after return
+  err = hipStreamSynchronize(s);
+  if (err != hipSuccess) return hip_status(err, "set_expert_table");
+  ctx->table_set[layer] = 1;
+  return ok();
+}
+
+void* moe_expert_table_device(moe_ctx* ctx, int32_t layer) {
+  if (!ctx || layer < 0 || layer >= ctx->n_layers) return nullptr;
+  return ctx->d_tables + (size_t)layer * ctx->cfg.n_experts;
+}
+
+moe_status moe_set_shared(moe_ctx* ctx, int32_t layer, const void* gate, const void* up,
+                          const void* down) {
+  if (!ctx) return fail(MOE_E_ARG, "moe_set_shared: null context");
+  if (layer < 0 || layer >= ctx->n_layers) return fail(MOE_E_ARG, "moe_set_shared: bad layer %d", layer);
+  const bool any = gate || up || down, all = gate && up && down;
+  if (any && !all) return fail(MOE_E_ARG, "moe_set_shared: give all three matrices or none");
+  if (any && ctx->cfg.shared_inter <= 0)
+    return fail(MOE_E_STATE, "moe_set_shared: context created without a shared expert");
+  if (any && (!aligned(gate, 16) || !aligned(up, 16) || !aligned(down, 16)))
+    return fail(MOE_E_ARG, "moe_set_shared: matrices must be 16-byte aligned");
+  ctx->shared[layer] = moe_ctx::Shared{gate, up, down};
+  return ok();
+}
+
+moe_status moe_route(moe_ctx* ctx, const void* x_bf16, int32_t T, const float* w_router,
+                     const float* bias, int32_t* topk_ids, float* topk_w,
+                     int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pair_pos,
+                     void* ws, size_t ws_bytes, moe_stream_t stream) {
+  if (!ctx) return fail(MOE_E_ARG, "moe_route: null context");
+  const moe_cfg& c = ctx->cfg;
+  if (T < 0 || T > c.max_tokens) return fail(MOE_E_ARG, "moe_route: T=%d outside [0, %d]", T, c.max_tokens);
+  if (T == 0) return ok();
+  if (!x_bf16 || !w_router || !topk_ids || !topk_w || !expert_offsets || !sorted_pairs || !pair_pos || !ws)
+    return fail(MOE_E_ARG, "moe_route: null pointer argument");
+  if (!aligned(x_bf16, 16) || !aligned(w_router, 16) || !aligned(ws, 256))
+    return fail(MOE_E_ARG, "moe_route: x and w_router must be 16-byte aligned, ws 256-byte aligned");
+  const moe::WsLayout L = moe::ws_layout(c, T);
+  if (ws_bytes < (size_t)L.total)
+    return fail(MOE_E_ARG, "moe_route: workspace %zu bytes < %lld needed", ws_bytes, (long long)L.total);
+  uint8_t* w8 = (uint8_t*)ws;
+  hipError_t e = moe::launch_route(c, (const uint16_t*)x_bf16, T, w_router, bias, topk_ids, topk_w,
+                                   expert_offsets, sorted_pairs, pair_pos,
+                                   (double*)(w8 + L.logits), (hipStream_t)stream);
+  return hip_status(e, "moe_route launch");
+}
+
+moe_status moe_forward(moe_ctx* ctx, int32_t layer, const void* x_bf16, int32_t T,
+                       const int32_t* topk_ids, const float* topk_w,
+                       const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                       const int32_t* pair_pos, float* out, float* pair_out, void* ws,
+                       size_t ws_bytes, moe_stream_t stream) {
+  if (!ctx) return fail(MOE_E_ARG, "moe_forward: null context");
+  const moe_cfg& c = ctx->cfg;
+  if (layer < 0 || layer >= ctx->n_layers) return fail(MOE_E_ARG, "moe_forward: bad layer %d", layer);
+  if (T < 0 || T > c.max_tokens) return fail(MOE_E_ARG, "moe_forward: T=%d outside [0, %d]", T, c.max_tokens);
+  if (!ctx->table_set[layer]) return fail(MOE_E_STATE, "moe_forward: expert table of layer %d never set", layer);
+  if (T == 0) return ok();
+  if (!x_bf16 || !topk_ids || !topk_w || !expert_offsets || !sorted_pairs || !pair_pos || !out || !ws)
+    return fail(MOE_E_ARG, "moe_forward: null pointer argument");
+  if (!aligned(x_bf16, 16) || !aligned(out, 16) || !aligned(ws, 256) || (pair_out && !aligned(pair_out, 16)))
+    return fail(MOE_E_ARG, "moe_forward: x, out, pair_out must be 16-byte aligned, ws 256-byte aligned");
+  const moe::WsLayout L = moe::ws_layout(c, T);
+  if (ws_bytes < (size_t)L.total)
+    return fail(MOE_E_ARG, "moe_forward: workspace %zu bytes < %lld needed", ws_bytes, (long long)L.total);
+  const moe_ctx::Shared& sh = ctx->shared[layer];
+  moe::FwdArgs f{&c, ctx->d_tables + (size_t)layer * c.n_experts, sh.g, sh.u, sh.d,
+                 (const uint16_t*)x_bf16, T, topk_ids, topk_w, expert_offsets, sorted_pairs,
+                 pair_pos, out, pair_out, (uint8_t*)ws};
+  return hip_status(moe::launch_forward(f, (hipStream_t)stream), "moe_forward launch");
+}
+
+moe_status moe_rmsnorm_bf16(const moe_ctx* ctx, float* resid, const float* add, int32_t T,
+                            float eps, void* y_bf16, moe_stream_t stream) {
+  if (!ctx) return fail(MOE_E_ARG, "moe_rmsnorm_bf16: null context");
+  if (T < 0 || T > ctx->cfg.max_tokens) return fail(MOE_E_ARG, "moe_rmsnorm_bf16: bad T=%d", T);
+  if (T == 0) return ok();
+  if (!resid || !y_bf16) return fail(MOE_E_ARG, "moe_rmsnorm_bf16: null pointer argument");
+  if (!(eps >= 0.f)) return fail(MOE_E_ARG, "moe_rmsnorm_bf16: eps must be >= 0");
+  return hip_status(moe::launch_rmsnorm(resid, add, T, ctx->cfg.hidden, eps, (uint16_t*)y_bf16,
+                                        (hipStream_t)stream),
+                    "moe_rmsnorm_bf16 launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,190 @@
+// common.h -- internal definitions shared by the HIP sources of libmoe.so.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+__host__ __device__ constexpr int64_t align256(int64_t n) { return (n + 255) / 256 * 256; }
+
+// Byte geometry of one packed matrix [rows][cols] (format v1 in moe.h).
+struct MatGeom {
+  int rows, cols, bits, group;
+  __host__ __device__ int n_groups() const { return cols / group; }
+  __host__ __device__ int unit_bytes() const { return bits * group / 8; }
+  __host__ __device__ int chunks() const { return bits * group / 128; }
+  __host__ __device__ int64_t codes_bytes() const {
+    return (int64_t)(rows / 64) * n_groups() * 64 * unit_bytes();
+  }
+  __host__ __device__ int64_t scales_off() const { return align256(codes_bytes()); }
+  __host__ __device__ int64_t bytes() const {
+    return scales_off() + align256((int64_t)rows * n_groups() * 2);
+  }
+};
+
+// bfloat16 / fp16 helpers (bit patterns carried as uint16_t)
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+__device__ __forceinline__ float scale_to_f32(uint16_t s, bool f16) {
+  return f16 ? f16_to_f32(s) : bf16_to_f32(s);
+}
+
+// Force a uniform constant into a VGPR so that the bit-select below compiles to
+// v_and_or_b32 (mask from an SGPR, magic from this VGPR) instead of two
+// literal-operand instructions.
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(v));
+  return r;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ---------------------------------------------------------------- unit decode
+// A unit (one row, one group of G codes) is decoded into G/2 registers, each a
+// pair of bfloat16 values (B + c_{2P}, B + c_{2P+1}) for a per-pair constant B:
+// the 3-bit code sits in the top mantissa bits of a bf16 whose exponent makes
+// one code step equal 1.0, so OR-ing an exponent pattern onto the masked field
+// yields B + c exactly.  B depends only on the field position:
+//   field at bits 1..3 of a half -> pattern 0x4280 (64 + c)
+//   field at bits 4..6           -> pattern 0x4100 (8 + c)
+//   field at bits 0..2           -> pattern 0x4300 (128 + c)
+// The dot product of these pairs with activations x therefore equals
+//   sum_k (q_k + off_k) x_k,  off_k = B_k + 2^(bits-1),
+// and the kernels subtract the per-group constant sum_k off_k x_k, computed once
+// per activation vector and group.
+template <int BITS>
+struct UnitCodec;
+
+template <>
+struct UnitCodec<3> {
+  static constexpr int G = 128, WORDS = 12, CHUNKS = 3, PAIRS = 64;
+  // offset of pair P: fields 0 and 2 of a word use B = 64, fields 1, 3, 4 use
+  // B = 8, pairs 60..63 (the spare bits) use B = 128; zero point 4.
+  __host__ __device__ static constexpr float pair_off(int P) {
+    return P >= 60 ? 132.f : ((P % 5 == 0 || P % 5 == 2) ? 68.f : 12.f);
+  }
+  __device__ __forceinline__ static void decode(const uint32_t (&w)[WORDS], uint32_t (&p)[PAIRS]) {
+    const uint32_t m64 = in_vgpr(0x42804280u), m8 = in_vgpr(0x41004100u),
+                   m128 = in_vgpr(0x43004300u);
+#pragma unroll
+    for (int d = 0; d < 12; ++d) {
+      uint32_t v = w[d];
+      uint32_t t = v >> 6;
+      p[5 * d + 0] = (v & 0x000E000Eu) | m64;          // bits 1..3
+      p[5 * d + 1] = (v & 0x00700070u) | m8;           // bits 4..6
+      p[5 * d + 2] = (t & 0x000E000Eu) | m64;          // bits 7..9
+      p[5 * d + 3] = (t & 0x00700070u) | m8;           // bits 10..12
+      p[5 * d + 4] = ((v >> 9) & 0x00700070u) | m8;    // bits 13..15
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      uint32_t a = w[3 * m], b = w[3 * m + 1], c = w[3 * m + 2];
+      uint32_t v = (a & 0x00010001u) | m128;
+      v |= (b << 1) & 0x00020002u;
+      v |= (c << 2) & 0x00040004u;
+      p[60 + m] = v;
+    }
+  }
+};
+
+template <>
+struct UnitCodec<4> {
+  static constexpr int G = 32, WORDS = 4, CHUNKS = 1, PAIRS = 16;
+  __host__ __device__ static constexpr float pair_off(int) { return 136.f; }  // B 128, zero 8
+  __device__ __forceinline__ static void decode(const uint32_t (&w)[WORDS], uint32_t (&p)[PAIRS]) {
+    const uint32_t m128 = in_vgpr(0x43004300u);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) p[4 * d + f] = ((w[d] >> (4 * f)) & 0x000F000Fu) | m128;
+    }
+  }
+};
+
+// ---------------------------------------------------------------- workspace
+// Layout of the caller's workspace for T tokens (byte offsets, 256-aligned).
+struct WsLayout {
+  int64_t counters;   // int32[64]: zero between calls
+  int64_t logits;     // double[T][E]
+  int64_t active;     // int32[E + 1]: active expert ids ascending, then count at [E]
+  int64_t xcorr;      // float[T][H/G]: per-token per-group activation offset sums
+  int64_t h_hi;       // uint16[P][I]: bf16 high part of h, rows by sorted position
+  int64_t h_lo;       // uint16[P][I]: bf16 remainder of h
+  int64_t hcorr;      // float[P][I/min(G,64)]: partial offset sums of h
+  int64_t pair_out;   // float[P][H] (used when the caller passes no pair_out)
+  int64_t sh_h;       // float[T][Is]: shared expert h
+  int64_t sh_out;     // float[T][H]: shared expert output
+  int64_t total;
+};
+
+__host__ inline WsLayout ws_layout(const moe_cfg& c, int T) {
+  WsLayout L{};
+  int64_t P = (int64_t)T * c.top_k;
+  int64_t o = 0;
+  auto take = [&](int64_t bytes) {
+    int64_t r = o;
+    o += align256(bytes > 0 ? bytes : 0);
+    return r;
+  };
+  L.counters = take(64 * 4);
+  L.logits = take((int64_t)T * c.n_experts * 8);
+  L.active = take((int64_t)(c.n_experts + 1) * 4);
+  L.xcorr = take((int64_t)T * (c.hidden / c.group) * 4);
+  L.h_hi = take(P * c.inter * 2);
+  L.h_lo = take(P * c.inter * 2);
+  int hseg = c.group < 64 ? c.group : 64;
+  L.hcorr = take(P * (c.inter / hseg) * 4);
+  L.pair_out = take(P * c.hidden * 4);
+  L.sh_h = take((int64_t)T * c.shared_inter * 4);
+  L.sh_out = take((int64_t)T * c.hidden * 4);
+  L.total = o;
+  return L;
+}
+
+// ---------------------------------------------------------------- launchers
+struct FwdArgs {
+  const moe_cfg* c;
+  const moe_expert_ref* table;  // this layer's device table
+  const void* sg;               // shared expert (or null)
+  const void* su;
+  const void* sd;
+  const uint16_t* x;
+  int T;
+  const int32_t* ids;
+  const float* w;
+  const int32_t* offsets;
+  const int32_t* sorted_pairs;
+  const int32_t* pair_pos;
+  float* out;
+  float* pair_out;              // null: workspace
+  uint8_t* ws;
+};
+
+hipError_t launch_route(const moe_cfg& c, const uint16_t* x, int T, const float* wr,
+                        const float* bias, int32_t* ids, float* w, int32_t* offsets,
+                        int32_t* sorted_pairs, int32_t* pair_pos, double* logits, hipStream_t s);
+hipError_t launch_forward(const FwdArgs& f, hipStream_t s);
+hipError_t launch_rmsnorm(float* resid, const float* add, int T, int H, float eps, uint16_t* y,
+                          hipStream_t s);
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
+
+}  // namespace moe

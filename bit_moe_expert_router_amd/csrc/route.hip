@@ -1,0 +1,260 @@
+// route.hip -- router logits, top-k with renormalised softmax weights, and the
+// bit-exact grouping of (token, pick) pairs by expert.
+//
+// Routing picks the top-8 of 288 experts per token per MoE layer (page
+// "GLM-5.3-Flash EXL3 3.05bpw on 1x RTX 3090 -- RAM/NVMe expert tiering", field
+// summary); the picks are then deduplicated into a per-layer expert union with
+// each expert's token list (page "0xSero/glm53-flash-offload", paragraphs
+// "Elastic CLOCK expert cache" and "Batched decode").  The router function itself
+// is not printed on the pages; it is the softmax over logits x.Wr^T + bias with
+// the top-k weights renormalised.
+//
+// Logits are accumulated in fp64: a bf16 x fp32 product is exact in fp64, so the
+// selection equals the exact-arithmetic one up to the rounding of a 5120-term
+// fp64 sum (relative 1e-15), far below the smallest 8th/9th-logit margins the
+// workloads produce.  Every reduction has a fixed order (no float atomics).
+#include "common.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- logits, small T
+// Block = one expert x up to 8 tokens; 256 threads stride over H in float4 steps.
+constexpr int kLogitTok = 8;
+
+__global__ __launch_bounds__(256) void k_logits_small(const uint16_t* __restrict__ x, int T,
+                                                      int H, int E,
+                                                      const float* __restrict__ wr,
+                                                      const float* __restrict__ bias,
+                                                      double* __restrict__ logits) {
+  const int e = blockIdx.x;
+  const int t0 = blockIdx.y * kLogitTok;
+  const int nt = min(kLogitTok, T - t0);
+  const float4* w4 = reinterpret_cast<const float4*>(wr + (int64_t)e * H);
+  double acc[kLogitTok];
+#pragma unroll
+  for (int j = 0; j < kLogitTok; ++j) acc[j] = 0.0;
+  for (int i = threadIdx.x; i < H / 4; i += 256) {
+    float4 w = w4[i];
+#pragma unroll
+    for (int j = 0; j < kLogitTok; ++j) {
+      if (j < nt) {
+        const uint2 xv = reinterpret_cast<const uint2*>(x + (int64_t)(t0 + j) * H)[i];
+        acc[j] = fma((double)bf16_to_f32((uint16_t)xv.x), (double)w.x, acc[j]);
+        acc[j] = fma((double)bf16_to_f32((uint16_t)(xv.x >> 16)), (double)w.y, acc[j]);
+        acc[j] = fma((double)bf16_to_f32((uint16_t)xv.y), (double)w.z, acc[j]);
+        acc[j] = fma((double)bf16_to_f32((uint16_t)(xv.y >> 16)), (double)w.w, acc[j]);
+      }
+    }
+  }
+  __shared__ double red[4][kLogitTok];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < kLogitTok; ++j) {
+    double v = acc[j];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0) red[wv][j] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < nt) {
+    const int j = threadIdx.x;
+    double v = ((red[0][j] + red[1][j]) + red[2][j]) + red[3][j];
+    if (bias) v += (double)bias[e];
+    logits[(int64_t)(t0 + j) * E + e] = v;
+  }
+}
+
+// ---------------------------------------------------------------- logits, large T
+// Tiled fp64 product: block = 32 tokens x 32 experts, 256 threads with 2x2
+// outputs each, reduction dim staged through LDS in steps of 32.
+constexpr int kLT = 32, kLE = 32, kLK = 32;
+
+__global__ __launch_bounds__(256) void k_logits_tiled(const uint16_t* __restrict__ x, int T,
+                                                      int H, int E,
+                                                      const float* __restrict__ wr,
+                                                      const float* __restrict__ bias,
+                                                      double* __restrict__ logits) {
+  __shared__ double xs[kLK][kLT + 1];
+  __shared__ double ws[kLK][kLE + 1];
+  const int t0 = blockIdx.y * kLT, e0 = blockIdx.x * kLE;
+  const int tid = threadIdx.x;
+  const int ti = (tid % 16) * 2, ei = (tid / 16) * 2;
+  double acc[2][2] = {{0.0, 0.0}, {0.0, 0.0}};
+  for (int k0 = 0; k0 < H; k0 += kLK) {
+    for (int i = tid; i < kLT * kLK; i += 256) {
+      int r = i / kLK, c = i % kLK;
+      int t = t0 + r, e = e0 + r;
+      xs[c][r] = t < T ? (double)bf16_to_f32(x[(int64_t)t * H + k0 + c]) : 0.0;
+      ws[c][r] = e < E ? (double)wr[(int64_t)e * H + k0 + c] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int c = 0; c < kLK; ++c) {
+      double a0 = xs[c][ti], a1 = xs[c][ti + 1];
+      double b0 = ws[c][ei], b1 = ws[c][ei + 1];
+      acc[0][0] = fma(a0, b0, acc[0][0]);
+      acc[0][1] = fma(a0, b1, acc[0][1]);
+      acc[1][0] = fma(a1, b0, acc[1][0]);
+      acc[1][1] = fma(a1, b1, acc[1][1]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      int t = t0 + ti + i, e = e0 + ei + j;
+      if (t < T && e < E) logits[(int64_t)t * E + e] = acc[i][j] + (bias ? (double)bias[e] : 0.0);
+    }
+}
+
+// ---------------------------------------------------------------- top-k + weights
+// One wave per token.  Each lane keeps the logits of experts lane, lane+64, ...;
+// K rounds of a butterfly arg-max over (value desc, id asc) pick the experts in
+// output order.  Weights: exp(l_k - l_0) / sum_j exp(l_j - l_0) in fp64.
+constexpr int kMaxPerLane = 16;  // E <= 1024
+constexpr int kMaxK = 16;
+
+__device__ __forceinline__ bool better(double va, int ia, double vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+__global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits, int T, int E,
+                                              int K, int32_t* __restrict__ ids,
+                                              float* __restrict__ wout) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const double* l = logits + (int64_t)t * E;
+  double v[kMaxPerLane];
+  const int per = (E + 63) / 64;
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    int e = lane + 64 * i;
+    v[i] = (i < per && e < E) ? l[e] : -INFINITY;
+  }
+  uint32_t taken = 0;  // bit i: v[i] already picked
+  double lk[kMaxK];
+  int ik[kMaxK];
+  for (int k = 0; k < K; ++k) {
+    double bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) {
+      int e = lane + 64 * i;
+      if (i < per && e < E && !(taken >> i & 1u) && better(v[i], e, bv, bi)) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      double ov = __shfl_xor(bv, o);
+      int oi = __shfl_xor(bi, o);
+      if (better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    lk[k] = bv;
+    ik[k] = bi;
+  }
+  if (lane == 0) {
+    double den = 0.0;
+    for (int k = 0; k < K; ++k) den += exp(lk[k] - lk[0]);
+    for (int k = 0; k < K; ++k) {
+      ids[t * K + k] = ik[k];
+      wout[t * K + k] = (float)(exp(lk[k] - lk[0]) / den);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- grouping
+// One wave.  Pairs are taken 64 at a time in pair order; lanes holding the same
+// expert id are matched with one ballot per id bit, which gives each pair its
+// rank among equal ids in the chunk and the chunk's count per id.  Pass 1 counts,
+// an exclusive scan gives the offsets, pass 2 scatters (stable by pair index).
+// Ids outside [0, E) are left out (pair_pos = -1).  Integer only: bit-exact.
+__device__ __forceinline__ uint64_t match_mask(int e, int nbits) {
+  uint64_t m = __ballot(1);
+  for (int b = 0; b < nbits; ++b) {
+    uint64_t bal = __ballot((e >> b) & 1);
+    m &= ((e >> b) & 1) ? bal : ~bal;
+  }
+  return m;
+}
+
+__global__ __launch_bounds__(64) void k_permute(const int32_t* __restrict__ ids, int P, int E,
+                                                int32_t* __restrict__ offsets,
+                                                int32_t* __restrict__ sorted_pairs,
+                                                int32_t* __restrict__ pair_pos) {
+  __shared__ int cnt[1025];
+  __shared__ int run[1024];
+  const int lane = threadIdx.x;
+  int nbits = 0;
+  while ((1 << nbits) < E + 1) ++nbits;  // ids in [-1, E] fit (E means "invalid")
+  for (int e = lane; e < E; e += 64) {
+    cnt[e] = 0;
+    run[e] = 0;
+  }
+  __syncthreads();
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int c0 = 0; c0 < P; c0 += 64) {
+    int p = c0 + lane;
+    int e = p < P ? ids[p] : -1;
+    bool ok = p < P && e >= 0 && e < E;
+    int key = ok ? e : E;
+    uint64_t m = match_mask(key, nbits);
+    if (ok && (m & lt) == 0) cnt[e] += __popcll(m);
+    __syncthreads();
+  }
+  if (lane == 0) {
+    int s = 0;
+    for (int e = 0; e < E; ++e) {
+      int c = cnt[e];
+      cnt[e] = s;
+      s += c;
+    }
+    cnt[E] = s;
+  }
+  __syncthreads();
+  for (int e = lane; e <= E; e += 64) offsets[e] = cnt[e];
+  for (int c0 = 0; c0 < P; c0 += 64) {
+    int p = c0 + lane;
+    int e = p < P ? ids[p] : -1;
+    bool ok = p < P && e >= 0 && e < E;
+    int key = ok ? e : E;
+    uint64_t m = match_mask(key, nbits);
+    int pos = -1;
+    if (ok) {
+      pos = cnt[e] + run[e] + __popcll(m & lt);
+      sorted_pairs[pos] = p;
+    }
+    if (p < P) pair_pos[p] = pos;
+    __syncthreads();
+    if (ok && (m & lt) == 0) run[e] += __popcll(m);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_route(const moe_cfg& c, const uint16_t* x, int T, const float* wr,
+                        const float* bias, int32_t* ids, float* w, int32_t* offsets,
+                        int32_t* sorted_pairs, int32_t* pair_pos, double* logits,
+                        hipStream_t s) {
+  const int H = c.hidden, E = c.n_experts, K = c.top_k;
+  if (T <= 64) {
+    hipLaunchKernelGGL(k_logits_small, dim3(E, (T + kLogitTok - 1) / kLogitTok), dim3(256), 0, s,
+                       x, T, H, E, wr, bias, logits);
+  } else {
+    hipLaunchKernelGGL(k_logits_tiled, dim3((E + kLE - 1) / kLE, (T + kLT - 1) / kLT), dim3(256),
+                       0, s, x, T, H, E, wr, bias, logits);
+  }
+  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, K, ids, w);
+  hipLaunchKernelGGL(k_permute, dim3(1), dim3(64), 0, s, ids, T * K, E, offsets, sorted_pairs,
+                     pair_pos);
+  return hipGetLastError();
+}
+
+}  // namespace moe

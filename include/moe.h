@@ -1,0 +1,173 @@
+/* moe.h -- C-ABI of libmoe.so: the routed mixture-of-experts layer on gfx950.
+ *
+ * The layer (GLM-5.3-Flash class): each token picks the top-K of E experts
+ * (K = 8 of E = 288 per layer in that model; page "GLM-5.3-Flash EXL3 3.05bpw on
+ * 1x RTX 3090 -- RAM/NVMe expert tiering", field summary), the picks are grouped
+ * by expert, each picked expert runs a SwiGLU FFN (gate, up, down matrices, each
+ * reached through a per-layer pointer table that can be rewritten in place; page
+ * "GLM-5.3-Flash EXL3 3.05bpw on 1x RTX PRO 6000 - GPU expert cache, host-RAM
+ * streaming", field config.expert_cache.mechanism), and the expert outputs are
+ * summed with the routing weights, plus an optional always-on shared expert
+ * (page "0xSero/glm53-flash-offload", paragraph "Decode kernels (fast mode)").
+ *
+ * Conventions.  Unless stated otherwise every pointer is DEVICE memory, owned by
+ * the caller, and every call is stream-ordered on `stream` (a hipStream_t; NULL =
+ * the null stream), returns without waiting for the device, makes no device
+ * allocation and no host<->device copy except where stated, and can be captured
+ * in a HIP graph.  Status codes report host-side argument checks; faults inside
+ * kernels surface at the caller's next synchronisation.  No C++ exception crosses
+ * this boundary.  One host thread may use a context at a time; calls that run
+ * concurrently on different streams need distinct workspaces.
+ *
+ * Packed weight format (v1).  A matrix W[N][Kd] (N outputs, Kd reduction; N % 64
+ * == 0, Kd % G == 0) stores unsigned codes c with W[n][k] = (c - 2^(bits-1)) *
+ * s[n][k/G], one 16-bit scale (bf16 or fp16) per row and group of G consecutive
+ * reduction elements.  Supported (bits, G): (3, 128) and (4, 32).
+ *   codes region: tiles t = (n/64)*(Kd/G) + g, one per 64 rows and one group.  A
+ *     tile holds 64 units, unit u = row 64*(n/64) + u, each bits*G/8 bytes split
+ *     into C = bits*G/128 chunks of 16 bytes; chunk j of tile t starts at byte
+ *     (t*C + j)*1024 and unit u's part of it at +16u (one wave64 16-byte load per
+ *     chunk reads 1024 contiguous bytes).  A unit's 32-bit little-endian words
+ *     are its chunks' words in order.
+ *   code i of a unit (reduction index g*G + i), P = i/2, half h = i%2:
+ *     4-bit, G = 32, 4 words:   c = (w[P/4] >> (16h + 4*(P%4))) & 15
+ *     3-bit, G = 128, 12 words: P < 60: c = (w[P/5] >> (16h + off[P%5])) & 7,
+ *                               off = {1, 4, 7, 10, 13};
+ *                               P >= 60, m = P - 60: bit b of c is bit 16h of
+ *                               w[3m + b].
+ *   scales region: at the next 256-byte boundary after the codes, row-major
+ *     [N][Kd/G] 16-bit scales; the matrix blob ends at the following 256-byte
+ *     boundary.  Blobs must be 256-byte aligned.
+ * An expert is three blobs: gate [I][H], up [I][H], down [H][I].  At H = 5120,
+ * I = 1536, 3-bit G = 128 an expert is 9,216,000 bytes (3.125 bits per weight).
+ * The shared expert is three row-major bfloat16 matrices gate [Is][H], up [Is][H],
+ * down [H][Is].
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_ctx moe_ctx;
+typedef void* moe_stream_t; /* a hipStream_t */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_E_ARG = 1,          /* invalid argument (null, misaligned, out of range)    */
+  MOE_E_UNSUPPORTED = 2,  /* unsupported shape or format                          */
+  MOE_E_NOMEM = 3,        /* host or device allocation failed (moe_create only)   */
+  MOE_E_HIP = 4,          /* a HIP call or kernel launch failed                   */
+  MOE_E_STATE = 5         /* context not ready (e.g. expert table never set)      */
+} moe_status;
+
+typedef struct {
+  int32_t hidden;        /* H                                                     */
+  int32_t inter;         /* I, routed expert intermediate size                    */
+  int32_t n_experts;     /* E, routed experts per layer (<= 1024)                 */
+  int32_t top_k;         /* K (1 <= K <= min(E, 16))                              */
+  int32_t bits;          /* 3 or 4                                                */
+  int32_t group;         /* 128 for 3-bit, 32 for 4-bit                           */
+  int32_t scale_f16;     /* 1: fp16 scales, 0: bf16 scales                        */
+  int32_t shared_inter;  /* Is, 0 = no shared expert                              */
+  int32_t max_tokens;    /* largest T accepted by moe_route / moe_forward         */
+} moe_cfg;
+
+/* One expert's three packed blobs (device pointers, 256-byte aligned). */
+typedef struct {
+  const void* gate;
+  const void* up;
+  const void* down;
+} moe_expert_ref;
+
+/* Create a context for n_layers layers of shape *cfg.  Allocates only the device
+ * pointer tables (3 pointers per expert per layer) and the shared-expert pointer
+ * slots.  H and I must be multiples of 64 and of G; Is a multiple of 64.
+ * Returns MOE_E_UNSUPPORTED for other shapes, MOE_E_NOMEM on allocation failure. */
+moe_status moe_create(const moe_cfg* cfg, int32_t n_layers, moe_ctx** out);
+
+/* Free the context's tables.  Waits for the device to finish with them. */
+moe_status moe_destroy(moe_ctx* ctx);
+
+/* Workspace bytes that moe_route and moe_forward need for n_tokens tokens
+ * (0 if n_tokens is out of range).  One workspace serves both calls. */
+size_t moe_workspace_bytes(const moe_ctx* ctx, int32_t n_tokens);
+
+/* Zero the workspace's counters; must run once on a new workspace before its
+ * first use (zero-filled memory also qualifies).  Every later call leaves them
+ * zero again.  Uses a fill kernel, not a memset. */
+moe_status moe_workspace_init(const moe_ctx* ctx, void* ws, size_t ws_bytes,
+                              moe_stream_t stream);
+
+/* Copy one layer's pointer table: host_table[e] (HOST array of E entries, in
+ * logical expert order) gives expert e's three blobs.  The copy is
+ * stream-ordered (host to device); only pointers are copied, so the blobs must
+ * outlive the table entries.  A remap to other physical slots is another call;
+ * results depend only on the logical ids, never on where the bytes are. */
+moe_status set_expert_table(moe_ctx* ctx, int32_t layer, const moe_expert_ref* host_table,
+                            moe_stream_t stream);
+
+/* Device address of a layer's table (E entries of moe_expert_ref, logical
+ * order), for in-place rewrites by device code.  NULL on a bad layer. */
+void* moe_expert_table_device(moe_ctx* ctx, int32_t layer);
+
+/* Set a layer's shared expert (row-major bfloat16 gate [Is][H], up [Is][H],
+ * down [H][Is]); NULLs clear it.  Only pointers are kept. */
+moe_status moe_set_shared(moe_ctx* ctx, int32_t layer, const void* gate, const void* up,
+                          const void* down);
+
+/* Route T tokens.
+ *   x_bf16    [T][H] bfloat16 activations
+ *   w_router  [E][H] fp32 router matrix; bias [E] fp32 or NULL
+ *   logits l[t][e] = sum_h x[t][h] * w_router[e][h] + bias[e], accumulated in fp64
+ *   (every product is exact in fp64), so the selection is the exact-arithmetic one
+ *   up to summation-order rounding;
+ *   topk_ids  [T][K] int32: the K largest logits, descending, ties to the lower id
+ *   topk_w    [T][K] fp32: softmax over all experts restricted to the K picks and
+ *             renormalised, w_k = exp(l_k - l_0) / sum_j exp(l_j - l_0)
+ *   expert_offsets [E+1] int32, sorted_pairs [T*K] int32, pair_pos [T*K] int32:
+ *             pairs p = t*K + k grouped by logical expert (ascending), stable by p:
+ *             expert e owns positions expert_offsets[e] .. expert_offsets[e+1]-1,
+ *             sorted_pairs[i] is the pair at position i, pair_pos[p] its position.
+ *   ws        workspace of at least moe_workspace_bytes(ctx, T) bytes, 256-aligned.
+ * T = 0 returns MOE_OK and launches nothing. */
+moe_status moe_route(moe_ctx* ctx, const void* x_bf16, int32_t T, const float* w_router,
+                     const float* bias, int32_t* topk_ids, float* topk_w,
+                     int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pair_pos,
+                     void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Expert FFNs and combine for one layer, given routing (from moe_route or from
+ * the caller, in the same layout).
+ *   out       [T][H] fp32: out[t] = sum_{k=0..K-1} topk_w[t][k] * y(t,k) (k
+ *             ascending, no atomics, bit-reproducible) + shared(x_t) if set
+ *   pair_out  [T*K][H] fp32 or NULL: unweighted expert output of the pair at each
+ *             sorted position (row i belongs to pair sorted_pairs[i])
+ *   y(t,k) = down . (silu(gate . x_t) * (up . x_t)) of expert topk_ids[t][k],
+ *   accumulated in fp32 from exact integer codes and bf16 activations with the
+ *   group scale applied per group.
+ * Caller-supplied routing must be consistent (offsets from the same ids); a pair
+ * whose id is outside [0, E) must be left out of the grouping (pair_pos = -1) and
+ * then contributes nothing.  Returns MOE_E_STATE if the layer's table was never set. */
+moe_status moe_forward(moe_ctx* ctx, int32_t layer, const void* x_bf16, int32_t T,
+                       const int32_t* topk_ids, const float* topk_w,
+                       const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                       const int32_t* pair_pos, float* out, float* pair_out, void* ws,
+                       size_t ws_bytes, moe_stream_t stream);
+
+/* Stack glue between layers: y_bf16[t] = bf16(x[t] / sqrt(mean(x[t]^2) + eps))
+ * (unit gain, round to nearest even) for fp32 x [T][H]; and, if resid is not
+ * NULL, resid[t][h] += add[t][h] first (fp32), normalising the updated resid. */
+moe_status moe_rmsnorm_bf16(const moe_ctx* ctx, float* resid, const float* add, int32_t T,
+                            float eps, void* y_bf16, moe_stream_t stream);
+
+/* Detail string of the last non-OK status on this thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,246 @@
+"""HIP path vs the fp64 oracle on the same seeded bytes, through the C-ABI.
+
+Routing ids, offsets, sorted pairs and pair positions must match bit-exactly;
+every expert output y(t,k) must be within relative RMS 2e-3 of the oracle's (the
+pages report ~1e-3 per expert against fp64 for their own CPU and fused GPU
+kernels: page "0xSero/glm53-flash-offload", paragraph "Reference: a
+teacher-forced panel"), and so must every token's combined output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth.device import DeviceLayer, x_device
+from tests.gpu_util import HostExperts, make_layer_api, rel_err, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+W_TOL = 2e-7  # routing weights: fp64 values rounded to fp32
+
+_layers = {}
+
+
+def layer_for(name, device, slots=None):
+    key = (name, None if slots is None else tuple(slots))
+    if key not in _layers:
+        cfg = synth.CONFIGS[name]
+        _layers[key] = DeviceLayer.generate(cfg, 0, device, slots=slots)
+    return _layers[key]
+
+
+def check_routing(cfg, xh, res):
+    ids, w, gap, _ = oracle.route(xh, synth.router_f32(cfg), synth.zipf_bias(cfg), cfg.top_k)
+    assert np.array_equal(res["ids"], ids), "routing ids differ"
+    assert np.all(np.abs(res["w"] - w) <= W_TOL * np.maximum(w, 1e-30) + 1e-12)
+    off, sp, pp = oracle.permute(ids, cfg.n_experts)
+    assert np.array_equal(res["offsets"], off)
+    assert np.array_equal(res["sorted"], sp)
+    assert np.array_equal(res["pos"], pp)
+    return ids, w
+
+
+def test_device_fill_matches_host_generator(gpu):
+    for name, experts in (("c1", range(16)), ("c3", (0, 17, 287))):
+        say(f"[fill] {name}")
+        cfg = synth.CONFIGS[name]
+        dl = layer_for(name, gpu)
+        for e in experts:
+            assert np.array_equal(dl.expert_host(e), synth.expert_blob(cfg, 0, e)), (name, e)
+        if cfg.shared_inter:
+            host = synth.shared_weights(cfg)
+            for dev_t, h in zip(dl.shared, host):
+                assert np.array_equal(dev_t.cpu().numpy().view(np.uint16), h)
+
+
+ROUTE_CASES = [("c1", 4), ("c1", 1), ("c1", 37), ("c2", 1), ("c2", 2), ("c2", 5), ("c3", 8),
+               ("c3", 64), ("c3", 65), ("c3", 300), ("c5", 8192)]
+
+
+@pytest.mark.parametrize("name,T", ROUTE_CASES)
+def test_routing_bit_exact(gpu, name, T):
+    say(f"[route] {name} T={T}")
+    cfg = synth.CONFIGS[name]
+    dl = layer_for(name, gpu)
+    xh, xd = x_device(cfg, gpu, tokens=T)
+    ml = make_layer_api(cfg, dl, T)
+    r = ml.route(xd, dl.router, dl.bias)
+    torch.cuda.synchronize()
+    res = dict(ids=r.topk_ids.cpu().numpy(), w=r.topk_w.cpu().numpy(),
+               offsets=r.expert_offsets.cpu().numpy(), sorted=r.sorted_pairs.cpu().numpy(),
+               pos=r.pair_pos.cpu().numpy())
+    check_routing(cfg, xh, res)
+    ml.close()
+
+
+FFN_CASES = [("c1", 4), ("c1", 1), ("c1", 13), ("c2", 1), ("c2", 3), ("c3", 8), ("c3", 9)]
+
+
+@pytest.mark.parametrize("name,T", FFN_CASES)
+def test_expert_outputs_all_pairs(gpu, name, T):
+    say(f"[ffn] {name} T={T}")
+    cfg = synth.CONFIGS[name]
+    dl = layer_for(name, gpu)
+    xh, xd = x_device(cfg, gpu, tokens=T)
+    res = run_gpu(cfg, dl, xd)
+    ids, w = check_routing(cfg, xh, res)
+    he = HostExperts(cfg)
+    worst = 0.0
+    for p in range(T * cfg.top_k):
+        t, e = p // cfg.top_k, ids.reshape(-1)[p]
+        y = he.ffn(xh[t], e)
+        r = rel_err(res["pair_out"][res["pos"][p]], y)
+        worst = max(worst, r)
+        assert r <= TOL, (name, T, p, e, r)
+    # combined output of every token against the oracle's full layer
+    tabs = [[he.blobs(e)[m] for e in range(cfg.n_experts)] for m in range(3)]
+    out, _ = oracle.moe_layer(xh, ids, w, *tabs, cfg.inter, cfg.bits, cfg.group, cfg.scale_f16,
+                              he.shared())
+    for t in range(T):
+        assert rel_err(res["out"][t], out[t]) <= TOL, (name, T, t)
+    say(f"[ffn] {name} T={T} worst pair rel err {worst:.3e}")
+
+
+def test_prefill_chunk_sampled(gpu):
+    """8,192-token chunk: routing of every token is bit-exact; expert outputs are
+    checked on a sample of pairs (the hottest and coldest experts' first and last
+    pairs plus random ones) and the combined output on a sample of tokens."""
+    name, T = "c5", 8192
+    say(f"[prefill] {name} T={T}")
+    cfg = synth.CONFIGS[name]
+    dl = layer_for(name, gpu)
+    xh, xd = x_device(cfg, gpu, tokens=T)
+    res = run_gpu(cfg, dl, xd)
+    ids, w = check_routing(cfg, xh, res)
+    off, sp = res["offsets"], res["sorted"]
+    counts = np.diff(off)
+    hot, cold = int(np.argmax(counts)), int(np.argmin(np.where(counts > 0, counts, 1 << 30)))
+    pairs = {sp[off[hot]], sp[off[hot + 1] - 1], sp[off[cold]], sp[off[cold + 1] - 1]}
+    rng = np.random.default_rng(0)
+    pairs |= set(rng.integers(0, T * cfg.top_k, size=16).tolist())
+    he = HostExperts(cfg)
+    for p in sorted(pairs):
+        t, e = p // cfg.top_k, ids.reshape(-1)[p]
+        r = rel_err(res["pair_out"][res["pos"][p]], he.ffn(xh[t], e))
+        assert r <= TOL, (p, e, r)
+    for t in rng.integers(0, T, size=2).tolist():
+        ref = sum(w[t, k] * he.ffn(xh[t], ids[t, k]) for k in range(cfg.top_k))
+        assert rel_err(res["out"][t], ref) <= TOL, t
+    say(f"[prefill] hot expert {hot} has {counts[hot]} pairs")
+
+
+# ------------------------------------------------------------------ invariants
+def test_run_twice_bit_identical(gpu):
+    say("[inv] run twice")
+    cfg = synth.CONFIGS["c3"]
+    dl = layer_for("c3", gpu)
+    _, xd = x_device(cfg, gpu)
+    a = run_gpu(cfg, dl, xd)
+    b = run_gpu(cfg, dl, xd, ml=a["ml"])
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["pair_out"], b["pair_out"])
+
+
+def test_token_reorder_permutes_outputs(gpu):
+    say("[inv] reorder")
+    cfg = synth.CONFIGS["c3"]
+    dl = layer_for("c3", gpu)
+    xh, xd = x_device(cfg, gpu)
+    a = run_gpu(cfg, dl, xd)
+    perm = np.array([5, 2, 7, 0, 1, 6, 3, 4])
+    b = run_gpu(cfg, dl, xd[torch.from_numpy(perm).to(gpu)].contiguous())
+    assert np.array_equal(b["ids"], a["ids"][perm])
+    assert np.array_equal(b["out"], a["out"][perm])
+
+
+def test_remap_bit_identical(gpu):
+    """the same logical experts at other physical slots give bit-identical results"""
+    say("[inv] remap")
+    cfg = synth.CONFIGS["c3"]
+    dl = layer_for("c3", gpu)
+    other = synth.permutation(cfg.n_experts, 1234, 0, synth.SYN_SLOT_PERM)
+    assert not np.array_equal(other, dl.slots)
+    dl2 = layer_for("c3", gpu, slots=other)
+    _, xd = x_device(cfg, gpu)
+    a = run_gpu(cfg, dl, xd)
+    b = run_gpu(cfg, dl2, xd)
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["pair_out"], b["pair_out"])
+    # remapping one context's table in place of the old one does the same
+    ml = a["ml"]
+    ml.set_table(0, dl2.refs)
+    c = run_gpu(cfg, dl2, xd, ml=ml)
+    assert np.array_equal(a["out"], c["out"])
+
+
+def _caller_routing(ml, ids, w, E, device):
+    from bit_moe_expert_router_amd import RoutingBuffers
+    off, sp, pp = oracle.permute(ids, E)
+    T, K = ids.shape
+    sp_full = np.zeros(T * K, dtype=np.int32)
+    sp_full[:sp.size] = sp
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to(device)
+    return RoutingBuffers(t(ids, np.int32), t(w, np.float32), t(off, np.int32),
+                          t(sp_full, np.int32), t(pp, np.int32))
+
+
+def test_zero_weight_pair_equals_dropped_pair(gpu):
+    say("[inv] zero weight")
+    cfg = synth.CONFIGS["c3"]
+    dl = layer_for("c3", gpu)
+    xh, xd = x_device(cfg, gpu)
+    a = run_gpu(cfg, dl, xd)
+    ids, w = a["ids"].copy(), a["w"].copy()
+    w[3, 5] = 0.0
+    r0 = _caller_routing(a["ml"], ids, w, cfg.n_experts, gpu)
+    b = run_gpu(cfg, dl, xd, ml=a["ml"], routing=r0)
+    ids_d = ids.copy()
+    ids_d[3, 5] = -1
+    r1 = _caller_routing(a["ml"], ids_d, w, cfg.n_experts, gpu)
+    c = run_gpu(cfg, dl, xd, ml=a["ml"], routing=r1)
+    assert np.array_equal(b["out"], c["out"])
+    # and the dropped pair matches the oracle's treatment of an id outside [0, E)
+    he = HostExperts(cfg)
+    tabs = [[he.blobs(e)[m] for e in range(cfg.n_experts)] for m in range(3)]
+    ref, _ = oracle.moe_layer(xh, ids_d, w.astype(np.float64), *tabs, cfg.inter, cfg.bits,
+                              cfg.group, cfg.scale_f16, he.shared())
+    assert rel_err(c["out"][3], ref[3]) <= TOL
+
+
+# ------------------------------------------------------------------ status codes
+def test_status_codes(gpu):
+    import bit_moe_expert_router_amd as m
+    say("[abi] status codes")
+    cfg = synth.CONFIGS["c1"]
+    dl = layer_for("c1", gpu)
+    xh, xd = x_device(cfg, gpu, tokens=4)
+    ml = m.MoELayer(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.bits, cfg.group,
+                    cfg.scale_f16, 0, 4, 1, gpu)
+    r = ml.routing(4)
+    out = torch.empty((4, cfg.hidden), dtype=torch.float32, device=gpu)
+    with pytest.raises(m.MoEError) as ei:  # table never set
+        ml.forward(0, xd, r, out)
+    assert ei.value.status == m.MOE_E_STATE
+    ml.set_table(0, dl.refs)
+    x5 = torch.zeros((5, cfg.hidden), dtype=torch.int16, device=gpu)
+    with pytest.raises(m.MoEError) as ei:  # T above max_tokens
+        ml.route(x5, dl.router)
+    assert ei.value.status == m.MOE_E_ARG
+    small = torch.zeros(1024, dtype=torch.uint8, device=gpu)
+    with pytest.raises(m.MoEError) as ei:  # workspace too small
+        m.moe_route(ml.ctx, xd, 4, dl.router, None, r.topk_ids, r.topk_w, r.expert_offsets,
+                    r.sorted_pairs, r.pair_pos, small)
+    assert ei.value.status == m.MOE_E_ARG
+    with pytest.raises(m.MoEError) as ei:  # misaligned activations
+        m.moe_route(ml.ctx, xd.data_ptr() + 2, 3, dl.router, None, r.topk_ids, r.topk_w,
+                    r.expert_offsets, r.sorted_pairs, r.pair_pos, ml.ws)
+    assert ei.value.status == m.MOE_E_ARG
+    bad = list(dl.refs)
+    bad[3] = (bad[3][0] + 16, bad[3][1], bad[3][2])
+    with pytest.raises(m.MoEError) as ei:  # blob not 256-byte aligned
+        ml.set_table(0, bad)
+    assert ei.value.status == m.MOE_E_ARG
+    # T = 0 is a no-op
+    m.moe_route(ml.ctx, xd, 0, dl.router, None, r.topk_ids, r.topk_w, r.expert_offsets,
+                r.sorted_pairs, r.pair_pos, ml.ws)
+    ml.close()
