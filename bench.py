@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-MoE layer hot path on one MI355X.
+
+A step is one pass of the whole layer (routing: logits, top-k, grouping; experts:
+gate/up + SwiGLU, down; shared expert when the workload has one; weighted
+combine) over one batch of synthetic tokens whose inputs are already resident in
+HBM.  The default workload is one GLM-5.3-Flash-shaped MoE layer at decode batch
+1 (hidden 5120, expert intermediate 1536, 288 experts, top-8, 3-bit group-128
+weights with bf16 scales, Zipf(1.1) router bias).  Steps rotate over several
+resident copies of the layer (distinct weights, router and bias) so that no step
+is served from the 256 MB last-level cache.
+
+Prints ONE JSON line: tokens/s over the timed steps, the dominant kernel's
+achieved expert-weight bandwidth against the 8 TB/s HBM peak (kernel durations
+from HIP events the library records on its launch stream), and the fp64 CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "MoE-layer tokens/s (decode b=1..8, prefill 8K) + expert-weight HBM GB/s vs peak"
+
+WORKLOAD_TEXT = {
+    "c1": "tiny MoE layer: H 256, I 128, 16 experts, top-2, 4-bit G32 fp16 scales",
+    "c2": "one GLM-5.3-Flash-shaped MoE layer at decode: H 5120, I 1536, 288 experts, top-8, "
+          "3-bit G128 bf16 scales, Zipf(1.1) router bias",
+    "c3": "GLM-shaped MoE layer at decode batch 8 + bf16 shared expert (I 1536), expert pointer "
+          "table remapped to a seeded slot permutation, Zipf(1.1) bias",
+    "c5": "8,192-token prefill chunk through one GLM-shaped MoE layer (3-bit G128), Zipf(1.1) bias",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c5"])
+    ap.add_argument("--tokens", type=int, default=None, help="batch (default: the workload's)")
+    ap.add_argument("--uniform", action="store_true", help="no Zipf router bias")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="resident layer copies the steps rotate over (default: 16 at decode)")
+    ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the CPU-oracle baseline sample (0: skip)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; a multi-GPU run is not part of it "
+                                   "(expert or data parallel sharding is described in DESIGN.md)",
+                          "n_gpus": a.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from synth.device import DeviceLayer
+    import bit_moe_expert_router_amd as moe
+
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[a.workload]
+    if a.tokens:
+        cfg = cfg.with_(tokens=a.tokens)
+    if a.uniform:
+        cfg = cfg.with_(zipf=False)
+    T = cfg.tokens
+    decode = T <= 64
+    L = a.layers or (16 if decode else 1)
+
+    # ---------------------------------------------------------- resident inputs
+    t0 = time.time()
+    layers = [DeviceLayer.generate(cfg, l, dev) for l in range(L)]
+    xh = synth.x_bf16(cfg)
+    xd = torch.from_numpy(xh.view(np.int16)).to(dev)
+    ml = moe.MoELayer(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.bits, cfg.group,
+                      cfg.scale_f16, cfg.shared_inter, T, L, dev)
+    for l, dl in enumerate(layers):
+        ml.set_table(l, dl.refs)
+        if dl.shared is not None:
+            ml.set_shared(l, *dl.shared)
+    out = torch.empty((T, cfg.hidden), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+
+    def step(l):
+        dl = layers[l]
+        r = ml.route(xd, dl.router, dl.bias)
+        ml.forward(l, xd, r, out)
+
+    # distinct experts per layer (deterministic: same x, same layer -> same routing)
+    U = []
+    for l in range(L):
+        step(l)
+        torch.cuda.synchronize()
+        off = ml.rb.expert_offsets.cpu().numpy()
+        U.append(int((np.diff(off) > 0).sum()))
+
+    graphs = None
+    if not a.eager:
+        graphs = []
+        s = torch.cuda.Stream(device=dev)
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for l in range(L):
+                step(l)  # warm the capture stream
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for l in range(L):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(l)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(i):
+        if graphs is not None:
+            graphs[i % L].replay()
+        else:
+            step(i % L)
+
+    for i in range(a.warmup):
+        run(i)
+    torch.cuda.synchronize()
+
+    # ---------------------------------------------------------- timed region
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record()
+    for i in range(a.steps):
+        run(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = ev0.elapsed_time(ev1) / a.steps
+    tokens_per_s = T * a.steps / wall
+
+    # ---------------------------------------------------------- kernel timing
+    eb = synth.expert_bytes(cfg)
+    glay, ulay, dlay = synth.expert_layouts(cfg)
+    kern = {}
+    if not a.no_kernel_timing:
+        moe.moe_profile_read()  # drop anything recorded before
+        moe.moe_profile_enable(True)
+        for i in range(a.steps):
+            step(i % L)
+        torch.cuda.synchronize()
+        moe.moe_profile_enable(False)
+        kern = moe.moe_profile_read()
+    # algorithmic bytes over the kernel-timing pass (same step sequence)
+    u_steps = [U[i % L] for i in range(a.steps)]
+    gu_bytes = sum(u * (glay.nbytes + ulay.nbytes) for u in u_steps)
+    dn_bytes = sum(u * dlay.nbytes for u in u_steps)
+    roof = None
+    extra = {}
+    if kern:
+        gu_ms, gu_n = kern.get("gateup", (0.0, 0))
+        dn_ms, dn_n = kern.get("down", (0.0, 0))
+        ach = gu_bytes / (gu_ms * 1e-3) / 1e9 if gu_ms else None
+        roof = {"bound": "hbm", "achieved": round(ach, 1) if ach else None, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4) if ach else None,
+                "traffic": None, "kernel": "k_gateup (gate+up GEMV, SwiGLU)",
+                "avg_us": round(gu_ms / gu_n * 1e3, 2) if gu_n else None,
+                "bytes_per_launch": round(gu_bytes / a.steps)}
+        extra["kernels_us"] = {k: round(v[0] / v[1] * 1e3, 2) for k, v in kern.items() if v[1]}
+        if dn_ms:
+            extra["down_GBs"] = round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1)
+        tot_ms = sum(v[0] for v in kern.values())
+        extra["expert_bytes_per_step"] = round((gu_bytes + dn_bytes) / a.steps)
+        extra["expert_GBs_over_kernel_time"] = round((gu_bytes + dn_bytes) / (tot_ms * 1e-3) / 1e9, 1)
+    extra["expert_GBs_over_step"] = round((gu_bytes + dn_bytes) / a.steps / (ms_step * 1e-3) / 1e9, 1)
+    extra["distinct_experts_per_step"] = round(float(np.mean(u_steps)), 2)
+    extra["graph_replay"] = graphs is not None
+    extra["input_gen_s"] = round(gen_s, 1)
+
+    if a.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        extra["calib_copy_bytes"] = 1 << 30
+
+    # ---------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if a.cpu_seconds > 0:
+        cpu = cpu_baseline(cfg, L, a.cpu_seconds)
+
+    res = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded counter-based generator; random 3-bit codes and scales, "
+                "N(0,1) bf16 activations, N(0,0.02) fp32 router)",
+        "config": {"workload": f"{a.workload}: {WORKLOAD_TEXT[a.workload]}", "tokens": T,
+                   "layers_rotated": L, "hidden": cfg.hidden, "inter": cfg.inter,
+                   "experts": cfg.n_experts, "top_k": cfg.top_k, "bits": cfg.bits,
+                   "group": cfg.group, "zipf": cfg.zipf, "shared_inter": cfg.shared_inter},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(res))
+    ml.close()
+
+
+def cpu_baseline(cfg, L, budget_s):
+    """fp64 oracle (the test reference, untuned) on the host cores: routing, every
+    pick's expert FFN and the combine of one batch per step, rotating over the
+    same layers; timed until the budget is spent.  Batches above 16 tokens are
+    sampled: the first 16 tokens of the batch are routed and computed per step."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    off = synth.matrix_offsets(cfg)
+    T = min(cfg.tokens, 16)
+    xh = synth.x_bf16(cfg)[:T]
+    cache = {}
+    steps, spent = 0, 0.0
+    while spent < budget_s:
+        l = steps % L
+        if l not in cache:
+            wr, bias = synth.router_f32(cfg, l), synth.zipf_bias(cfg, l)
+            ids, _, _, _ = oracle.route(xh, wr, bias, cfg.top_k)
+            blobs = {int(e): synth.expert_blob(cfg, l, int(e)) for e in np.unique(ids)}
+            tabs = [[blobs[e][off[m]:(off[m + 1] if m < 2 else None)] if e in blobs else
+                     np.zeros(16, np.uint8) for e in range(cfg.n_experts)] for m in range(3)]
+            cache[l] = (wr, bias, tabs, synth.shared_weights(cfg, l))
+        wr, bias, tabs, shared = cache[l]
+        t0 = time.perf_counter()  # input generation above is not timed
+        ids, w, _, _ = oracle.route(xh, wr, bias, cfg.top_k)
+        oracle.moe_layer(xh, ids, w, *tabs, cfg.inter, cfg.bits, cfg.group, cfg.scale_f16, shared)
+        spent += time.perf_counter() - t0
+        steps += 1
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(T * steps / spent, 3), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{steps} steps of {T} token(s) of the same workload (routing + every "
+                      f"pick's fp64 expert FFN + combine, rotating over {min(L, steps)} layers), "
+                      f"{spent:.1f} s, {threads} OpenMP threads"}
+
+
+if __name__ == "__main__":
+    main()

@@ -37,7 +37,8 @@ class moe_expert_ref(ctypes.Structure):
 
 EXPORTS = ("moe_create", "moe_destroy", "moe_workspace_bytes", "moe_workspace_init",
            "set_expert_table", "moe_expert_table_device", "moe_set_shared", "moe_route",
-           "moe_forward", "moe_rmsnorm_bf16", "moe_last_error")
+           "moe_forward", "moe_rmsnorm_bf16", "moe_last_error", "moe_profile_enable",
+           "moe_profile_read")
 
 
 def _load():
@@ -59,6 +60,11 @@ def _load():
                                 ctypes.c_size_t, vp]
     lib.moe_rmsnorm_bf16.argtypes = [vp, vp, vp, i32, ctypes.c_float, vp, vp]
     lib.moe_last_error.restype = ctypes.c_char_p
+    lib.moe_profile_enable.argtypes = [i32]
+    lib.moe_profile_enable.restype = st
+    lib.moe_profile_read.argtypes = [i32, ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_int64)]
+    lib.moe_profile_read.restype = i32
     for f in ("moe_create", "moe_destroy", "moe_workspace_init", "set_expert_table",
               "moe_set_shared", "moe_route", "moe_forward", "moe_rmsnorm_bf16"):
         getattr(lib, f).restype = st
@@ -153,6 +159,20 @@ def moe_forward(ctx: int, layer: int, x_bf16, T: int, topk_ids, topk_w, expert_o
 
 def moe_last_error() -> str:
     return lib.moe_last_error().decode()
+
+
+def moe_profile_enable(on: bool):
+    _check(lib.moe_profile_enable(int(bool(on))), "moe_profile_enable")
+
+
+def moe_profile_read(max_kernels: int = 32) -> dict:
+    """{kernel name: (total ms, launches)} since the last read (waits for the events)"""
+    names = ctypes.create_string_buffer(32 * max_kernels)
+    ms = (ctypes.c_double * max_kernels)()
+    n = (ctypes.c_int64 * max_kernels)()
+    k = lib.moe_profile_read(max_kernels, names, ms, n)
+    raw = names.raw
+    return {raw[32 * i:32 * i + 32].split(b"\0")[0].decode(): (ms[i], n[i]) for i in range(k)}
 
 
 def moe_rmsnorm_bf16(ctx: int, resid, add, T: int, eps: float, y_bf16, stream=None):

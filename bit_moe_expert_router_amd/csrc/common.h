@@ -160,6 +160,22 @@ __host__ inline WsLayout ws_layout(const moe_cfg& c, int T) {
   return L;
 }
 
+// ---------------------------------------------------------------- profiling
+enum KernelId {
+  KID_LOGITS = 0, KID_TOPK, KID_PERMUTE, KID_PLAN, KID_GATEUP, KID_DOWN, KID_SH_GATEUP,
+  KID_SH_DOWN, KID_COMBINE, KID_RMSNORM, KID_ZERO, KID_COUNT
+};
+void prof_begin(int kid, hipStream_t s);
+void prof_end(int kid, hipStream_t s);
+
+// launch a kernel, bracketed by profiling events when profiling is enabled
+#define MOE_LAUNCH(kid, kernel, grid, block, shmem, stream, ...)                   \
+  do {                                                                             \
+    ::moe::prof_begin(kid, stream);                                                \
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);           \
+    ::moe::prof_end(kid, stream);                                                  \
+  } while (0)
+
 // ---------------------------------------------------------------- launchers
 struct FwdArgs {
   const moe_cfg* c;

@@ -430,24 +430,24 @@ hipError_t launch_forward_t(const FwdArgs& f, hipStream_t s) {
   float* sh_out = reinterpret_cast<float*>(f.ws + L.sh_out);
   const int ngx = H / C::G;
   const int plan_blocks = (T * ngx + 255) / 256;
-  hipLaunchKernelGGL(k_plan<BITS>, dim3(plan_blocks > 0 ? plan_blocks : 1), dim3(256), 0, s,
+  MOE_LAUNCH(KID_PLAN, k_plan<BITS>, dim3(plan_blocks > 0 ? plan_blocks : 1), dim3(256), 0, s,
                      f.offsets, E, f.x, T, H, active, xcorr);
   const int maxU = min(E, T * K);
-  hipLaunchKernelGGL(k_gateup<BITS>, dim3(maxU, I / 64), dim3(64 * kGUWaves), 0, s, f.table,
+  MOE_LAUNCH(KID_GATEUP, k_gateup<BITS>, dim3(maxU, I / 64), dim3(64 * kGUWaves), 0, s, f.table,
                      active, E, f.offsets, f.sorted_pairs, K, f.x, H, I, c.scale_f16, xcorr, h_hi,
                      h_lo, hcorr);
-  hipLaunchKernelGGL(k_down<BITS>, dim3(maxU, H / 64), dim3(64 * kDNWaves), 0, s, f.table, active,
+  MOE_LAUNCH(KID_DOWN, k_down<BITS>, dim3(maxU, H / 64), dim3(64 * kDNWaves), 0, s, f.table, active,
                      E, f.offsets, H, I, c.scale_f16, h_hi, h_lo, hcorr, pair_out);
   const bool has_shared = c.shared_inter > 0 && f.sg && f.su && f.sd;
   if (has_shared) {
     const int Is = c.shared_inter;
-    hipLaunchKernelGGL(k_shared_gateup, dim3(Is / kShRows), dim3(256), 0, s,
+    MOE_LAUNCH(KID_SH_GATEUP, k_shared_gateup, dim3(Is / kShRows), dim3(256), 0, s,
                        reinterpret_cast<const uint16_t*>(f.sg),
                        reinterpret_cast<const uint16_t*>(f.su), f.x, T, H, Is, sh_h);
-    hipLaunchKernelGGL(k_shared_down, dim3(H / kShRows), dim3(256), 0, s,
+    MOE_LAUNCH(KID_SH_DOWN, k_shared_down, dim3(H / kShRows), dim3(256), 0, s,
                        reinterpret_cast<const uint16_t*>(f.sd), sh_h, T, H, Is, sh_out);
   }
-  hipLaunchKernelGGL(k_combine, dim3((H + 255) / 256, T), dim3(256), 0, s, pair_out, f.pair_pos,
+  MOE_LAUNCH(KID_COMBINE, k_combine, dim3((H + 255) / 256, T), dim3(256), 0, s, pair_out, f.pair_pos,
                      f.w, K, H, has_shared ? sh_out : nullptr, f.out);
   return hipGetLastError();
 }
@@ -458,12 +458,12 @@ hipError_t launch_forward(const FwdArgs& f, hipStream_t s) {
 
 hipError_t launch_rmsnorm(float* resid, const float* add, int T, int H, float eps, uint16_t* y,
                           hipStream_t s) {
-  hipLaunchKernelGGL(k_rmsnorm, dim3(T), dim3(256), 0, s, resid, add, H, eps, y);
+  MOE_LAUNCH(KID_RMSNORM, k_rmsnorm, dim3(T), dim3(256), 0, s, resid, add, H, eps, y);
   return hipGetLastError();
 }
 
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s) {
-  hipLaunchKernelGGL(k_zero_i32, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
+  MOE_LAUNCH(KID_ZERO, k_zero_i32, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
   return hipGetLastError();
 }
 

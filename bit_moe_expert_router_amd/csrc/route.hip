@@ -245,14 +245,14 @@ hipError_t launch_route(const moe_cfg& c, const uint16_t* x, int T, const float*
                         hipStream_t s) {
   const int H = c.hidden, E = c.n_experts, K = c.top_k;
   if (T <= 64) {
-    hipLaunchKernelGGL(k_logits_small, dim3(E, (T + kLogitTok - 1) / kLogitTok), dim3(256), 0, s,
+    MOE_LAUNCH(KID_LOGITS, k_logits_small, dim3(E, (T + kLogitTok - 1) / kLogitTok), dim3(256), 0, s,
                        x, T, H, E, wr, bias, logits);
   } else {
-    hipLaunchKernelGGL(k_logits_tiled, dim3((E + kLE - 1) / kLE, (T + kLT - 1) / kLT), dim3(256),
+    MOE_LAUNCH(KID_LOGITS, k_logits_tiled, dim3((E + kLE - 1) / kLE, (T + kLT - 1) / kLT), dim3(256),
                        0, s, x, T, H, E, wr, bias, logits);
   }
-  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, K, ids, w);
-  hipLaunchKernelGGL(k_permute, dim3(1), dim3(64), 0, s, ids, T * K, E, offsets, sorted_pairs,
+  MOE_LAUNCH(KID_TOPK, k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, K, ids, w);
+  MOE_LAUNCH(KID_PERMUTE, k_permute, dim3(1), dim3(64), 0, s, ids, T * K, E, offsets, sorted_pairs,
                      pair_pos);
   return hipGetLastError();
 }

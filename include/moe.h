@@ -164,6 +164,15 @@ moe_status moe_forward(moe_ctx* ctx, int32_t layer, const void* x_bf16, int32_t 
 moe_status moe_rmsnorm_bf16(const moe_ctx* ctx, float* resid, const float* add, int32_t T,
                             float eps, void* y_bf16, moe_stream_t stream);
 
+/* Kernel timing.  While enabled (process-wide), every kernel the library
+ * launches is bracketed by two HIP events recorded on its launch stream.
+ * moe_profile_read waits for the recorded events, writes up to max_kernels
+ * entries (names: max_kernels x 32 chars, NUL-terminated, HOST memory; total_ms
+ * and launches: HOST arrays) for the kernels launched since the last read, and
+ * returns the number of entries.  Not for use while a stream is being captured. */
+moe_status moe_profile_enable(int32_t on);
+int32_t moe_profile_read(int32_t max_kernels, char* names, double* total_ms, int64_t* launches);
+
 /* Detail string of the last non-OK status on this thread ("" if none). */
 const char* moe_last_error(void);
 
