@@ -54,6 +54,9 @@ moe_status check_cfg(const moe_cfg& c) {
   if (c.hidden % 64 || c.inter % 64 || c.hidden % c.group || c.inter % c.group)
     return fail(MOE_E_UNSUPPORTED, "cfg: hidden and inter must be multiples of 64 and of the group");
   if (c.n_experts > 1024) return fail(MOE_E_UNSUPPORTED, "cfg: at most 1024 experts");
+  if (c.hidden / c.group > 64 || c.inter / c.group > 32 || c.hidden > 8192 || c.inter > 8192)
+    return fail(MOE_E_UNSUPPORTED,
+                "cfg: at most 64 groups along hidden, 32 along inter, and sizes <= 8192");
   if (c.top_k > 16 || c.top_k > c.n_experts) return fail(MOE_E_UNSUPPORTED, "cfg: top_k must be <= min(16, E)");
   if (c.shared_inter < 0) return fail(MOE_E_ARG, "cfg: shared_inter < 0");
   if (c.shared_inter > 0 && (c.shared_inter % 256 || c.hidden % 256))
@@ -105,9 +108,9 @@ size_t moe_workspace_bytes(const moe_ctx* ctx, int32_t n_tokens) {
 
 moe_status moe_workspace_init(const moe_ctx* ctx, void* ws, size_t ws_bytes, moe_stream_t stream) {
   if (!ctx || !ws) return fail(MOE_E_ARG, "moe_workspace_init: null argument");
-  if (ws_bytes < 256) return fail(MOE_E_ARG, "moe_workspace_init: workspace too small");
+  if (ws_bytes < (size_t)moe::kCounters * 4) return fail(MOE_E_ARG, "moe_workspace_init: workspace too small");
   hipStream_t s = (hipStream_t)stream;
-  return hip_status(moe::launch_zero_i32((int32_t*)ws, 64, s), "moe_workspace_init");
+  return hip_status(moe::launch_zero_i32((int32_t*)ws, moe::kCounters, s), "moe_workspace_init");
 }
 
 moe_status set_expert_table(moe_ctx* ctx, int32_t layer, const moe_expert_ref* host_table,
@@ -170,7 +173,8 @@ moe_status moe_route(moe_ctx* ctx, const void* x_bf16, int32_t T, const float* w
   uint8_t* w8 = (uint8_t*)ws;
   hipError_t e = moe::launch_route(c, (const uint16_t*)x_bf16, T, w_router, bias, topk_ids, topk_w,
                                    expert_offsets, sorted_pairs, pair_pos,
-                                   (double*)(w8 + L.logits), (hipStream_t)stream);
+                                   (double*)(w8 + L.logits), (int32_t*)(w8 + L.counters),
+                                   (hipStream_t)stream);
   return hip_status(e, "moe_route launch");
 }
 

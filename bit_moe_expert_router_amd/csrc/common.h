@@ -26,6 +26,13 @@ struct MatGeom {
   }
 };
 
+// Pointers read from the expert table are generic; loads through them would
+// compile to flat loads, which also count against the scalar-load counter.  The
+// blobs are device global memory, so they are cast to the global address space.
+typedef const uint8_t __attribute__((address_space(1)))* gbytes_t;
+typedef const uint16_t __attribute__((address_space(1)))* gu16_t;
+__device__ __forceinline__ gbytes_t as_global(const void* p) { return (gbytes_t)p; }
+
 // bfloat16 / fp16 helpers (bit patterns carried as uint16_t)
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
@@ -49,6 +56,14 @@ __device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
   uint32_t r;
   asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(v));
   return r;
+}
+
+// Workgroup barrier for LDS hand-offs only.  __syncthreads() also orders global
+// memory, which on gfx950 waits for every outstanding vector load (vmcnt(0)),
+// including weight loads issued ahead on purpose; here only this wave's LDS
+// operations are waited for.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -82,6 +97,30 @@ struct UnitCodec<3> {
   __host__ __device__ static constexpr float pair_off(int P) {
     return P >= 60 ? 132.f : ((P % 5 == 0 || P % 5 == 2) ? 68.f : 12.f);
   }
+  // visit (P, pair) in order, expanding each pair right before its use
+  template <class F>
+  __device__ __forceinline__ static void for_each_pair(const uint32_t (&w)[WORDS], F&& f) {
+    const uint32_t m64 = in_vgpr(0x42804280u), m8 = in_vgpr(0x41004100u),
+                   m128 = in_vgpr(0x43004300u);
+#pragma unroll
+    for (int d = 0; d < 12; ++d) {
+      const uint32_t v = w[d];
+      const uint32_t t = v >> 6;
+      f(5 * d + 0, (v & 0x000E000Eu) | m64);
+      f(5 * d + 1, (v & 0x00700070u) | m8);
+      f(5 * d + 2, (t & 0x000E000Eu) | m64);
+      f(5 * d + 3, (t & 0x00700070u) | m8);
+      f(5 * d + 4, ((v >> 9) & 0x00700070u) | m8);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t a = w[3 * m], b = w[3 * m + 1], c = w[3 * m + 2];
+      uint32_t v = (a & 0x00010001u) | m128;
+      v |= (b << 1) & 0x00020002u;
+      v |= (c << 2) & 0x00040004u;
+      f(60 + m, v);
+    }
+  }
   __device__ __forceinline__ static void decode(const uint32_t (&w)[WORDS], uint32_t (&p)[PAIRS]) {
     const uint32_t m64 = in_vgpr(0x42804280u), m8 = in_vgpr(0x41004100u),
                    m128 = in_vgpr(0x43004300u);
@@ -110,6 +149,15 @@ template <>
 struct UnitCodec<4> {
   static constexpr int G = 32, WORDS = 4, CHUNKS = 1, PAIRS = 16;
   __host__ __device__ static constexpr float pair_off(int) { return 136.f; }  // B 128, zero 8
+  template <class F>
+  __device__ __forceinline__ static void for_each_pair(const uint32_t (&w)[WORDS], F&& f) {
+    const uint32_t m128 = in_vgpr(0x43004300u);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) f(4 * d + k, ((w[d] >> (4 * k)) & 0x000F000Fu) | m128);
+    }
+  }
   __device__ __forceinline__ static void decode(const uint32_t (&w)[WORDS], uint32_t (&p)[PAIRS]) {
     const uint32_t m128 = in_vgpr(0x43004300u);
 #pragma unroll
@@ -121,15 +169,14 @@ struct UnitCodec<4> {
 };
 
 // ---------------------------------------------------------------- workspace
+// counters reserved for cross-block signalling (kept zero between calls)
+constexpr int kCounters = 1024;
+constexpr int kMaxKParts = 4;  // gate/up reduction-dimension split (H/G <= 80)
 // Layout of the caller's workspace for T tokens (byte offsets, 256-aligned).
 struct WsLayout {
-  int64_t counters;   // int32[64]: zero between calls
+  int64_t counters;   // int32[kCounters]: zero between calls
   int64_t logits;     // double[T][E]
-  int64_t active;     // int32[E + 1]: active expert ids ascending, then count at [E]
-  int64_t xcorr;      // float[T][H/G]: per-token per-group activation offset sums
-  int64_t h_hi;       // uint16[P][I]: bf16 high part of h, rows by sorted position
-  int64_t h_lo;       // uint16[P][I]: bf16 remainder of h
-  int64_t hcorr;      // float[P][I/min(G,64)]: partial offset sums of h
+  int64_t gu;         // float[2*KP][P][I]: partial gate and up products, rows by sorted position
   int64_t pair_out;   // float[P][H] (used when the caller passes no pair_out)
   int64_t sh_h;       // float[T][Is]: shared expert h
   int64_t sh_out;     // float[T][H]: shared expert output
@@ -145,14 +192,9 @@ __host__ inline WsLayout ws_layout(const moe_cfg& c, int T) {
     o += align256(bytes > 0 ? bytes : 0);
     return r;
   };
-  L.counters = take(64 * 4);
+  L.counters = take(kCounters * 4);
   L.logits = take((int64_t)T * c.n_experts * 8);
-  L.active = take((int64_t)(c.n_experts + 1) * 4);
-  L.xcorr = take((int64_t)T * (c.hidden / c.group) * 4);
-  L.h_hi = take(P * c.inter * 2);
-  L.h_lo = take(P * c.inter * 2);
-  int hseg = c.group < 64 ? c.group : 64;
-  L.hcorr = take(P * (c.inter / hseg) * 4);
+  L.gu = take(2 * kMaxKParts * P * c.inter * 4);
   L.pair_out = take(P * c.hidden * 4);
   L.sh_h = take((int64_t)T * c.shared_inter * 4);
   L.sh_out = take((int64_t)T * c.hidden * 4);
@@ -197,7 +239,8 @@ struct FwdArgs {
 
 hipError_t launch_route(const moe_cfg& c, const uint16_t* x, int T, const float* wr,
                         const float* bias, int32_t* ids, float* w, int32_t* offsets,
-                        int32_t* sorted_pairs, int32_t* pair_pos, double* logits, hipStream_t s);
+                        int32_t* sorted_pairs, int32_t* pair_pos, double* logits,
+                        int32_t* counter, hipStream_t s);
 hipError_t launch_forward(const FwdArgs& f, hipStream_t s);
 hipError_t launch_rmsnorm(float* resid, const float* add, int T, int H, float eps, uint16_t* y,
                           hipStream_t s);

@@ -22,255 +22,417 @@
 
 namespace moe {
 
-// ---------------------------------------------------------------- plan
-// active[0..U-1] = experts with at least one pair, ascending; active[E] = U.
-// xcorr[t][g] = sum_k off_k * x[t][g*G + k] (k ascending), the offset sum that
-// the unit codec's dot products carry.
-template <int BITS>
-__global__ __launch_bounds__(256) void k_plan(const int32_t* __restrict__ offsets, int E,
-                                              const uint16_t* __restrict__ x, int T, int H,
-                                              int32_t* __restrict__ active,
-                                              float* __restrict__ xcorr) {
-  using C = UnitCodec<BITS>;
-  const int ng = H / C::G;
-  const int item = blockIdx.x * 256 + threadIdx.x;
-  if (item < T * ng) {
-    const int t = item / ng, g = item % ng;
-    const uint32_t* xp = reinterpret_cast<const uint32_t*>(x + (int64_t)t * H + g * C::G);
-    float acc = 0.f;
-    for (int P = 0; P < C::PAIRS; ++P) {
-      uint32_t v = xp[P];
-      acc = fmaf(C::pair_off(P), bf16_to_f32((uint16_t)v), acc);
-      acc = fmaf(C::pair_off(P), bf16_to_f32((uint16_t)(v >> 16)), acc);
-    }
-    xcorr[item] = acc;
-  }
-  if (blockIdx.x == 0) {
-    __shared__ int wsum[4];
-    // E <= 1024: four passes of 256 experts
-    int base = 0;
-    for (int e0 = 0; e0 < E; e0 += 256) {
-      const int e = e0 + threadIdx.x;
-      const bool on = e < E && offsets[e + 1] > offsets[e];
-      const uint64_t bal = __ballot(on);
-      const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-      if (lane == 0) wsum[wv] = __popcll(bal);
-      __syncthreads();
-      int pre = base;
-      for (int i = 0; i < wv; ++i) pre += wsum[i];
-      pre += __popcll(bal & ((1ull << lane) - 1ull));
-      if (on) active[pre] = e;
-      base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
-      __syncthreads();
-    }
-    if (threadIdx.x == 0) active[E] = base;
-  }
-}
-
-// ---------------------------------------------------------------- gate/up
-// Block (a, strip): active expert a, rows [64*strip, 64*strip+64) of gate and up,
-// all groups; 8 waves take groups g = wave, wave+8, ...; tokens in batches of
-// kNT.  Per (row, token): g = sum_groups s * (dot - xcorr), same for u; then
-// h = silu(g) * u, stored as bf16 hi + bf16 remainder (h to ~2^-16 relative) at
-// the pair's sorted position, plus the offset sums of h per segment of
-// min(G, 64) rows for the down matrix.
-constexpr int kNT = 8;
-constexpr int kGUWaves = 8;
-
-struct TokRef {
-  int pos;  // sorted position of the pair
-  int tok;  // token index
+// ---------------------------------------------------------------- active experts
+// The a-th expert (ascending logical id) that owns at least one pair, the number
+// U of such experts, its segment of the grouping and its table entry.
+// Wave-cooperative (every lane returns the same values).  Each lane loads the
+// offsets and the table entries of its candidate experts lane + 64*i in the same
+// round trip, so the expert's weight addresses are known after one memory
+// latency instead of two.  E <= 1024.
+struct Active {
+  int e;     // -1 if a >= U
+  int U;
+  int seg0;  // first sorted position of the expert's pairs
+  int n;     // number of pairs
+  const void* ptr[3];  // gate, up, down
 };
 
-template <int BITS>
-__device__ __forceinline__ void load_unit(const uint8_t* codes, int64_t tile, int lane,
-                                          uint32_t (&w)[UnitCodec<BITS>::WORDS]) {
-  using C = UnitCodec<BITS>;
+__device__ __forceinline__ Active find_active(const int32_t* __restrict__ offsets,
+                                              const moe_expert_ref* __restrict__ table, int E,
+                                              int a) {
+  const int lane = threadIdx.x & 63;
+  constexpr int kSpec = 5;  // candidates per lane whose table entry is fetched up front
+  const int nch = (E + 63) / 64;
+  int lo[16], hi[16];
+  moe_expert_ref ref[kSpec];
 #pragma unroll
-  for (int j = 0; j < C::CHUNKS; ++j) {
-    const uint4 v = *reinterpret_cast<const uint4*>(codes + (tile * C::CHUNKS + j) * 1024 + 16 * lane);
-    w[4 * j + 0] = v.x;
-    w[4 * j + 1] = v.y;
-    w[4 * j + 2] = v.z;
-    w[4 * j + 3] = v.w;
+  for (int i = 0; i < 16; ++i) {
+    if (i < nch) {  // uniform
+      const int e = lane + 64 * i;
+      lo[i] = (e < E) ? offsets[e] : 0;
+      hi[i] = (e < E) ? offsets[e + 1] : 0;
+      if (i < kSpec) ref[i] = e < E ? table[e] : moe_expert_ref{nullptr, nullptr, nullptr};
+    }
   }
+  Active r{-1, 0, 0, 0, {nullptr, nullptr, nullptr}};
+  int U = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i < nch) {
+      const bool nz = hi[i] > lo[i];
+      const uint64_t bal = __ballot(nz);
+      const int cnt = __popcll(bal);
+      if (r.e < 0 && a < U + cnt) {  // uniform: the a-th active expert is in this chunk
+        // lane holding it: the (a-U)-th set bit of bal
+        uint64_t m = bal;
+        for (int k = 0; k < a - U; ++k) m &= m - 1;
+        const int src = __ffsll((unsigned long long)m) - 1;
+        r.e = 64 * i + src;
+        r.seg0 = __shfl(lo[i], src);
+        r.n = __shfl(hi[i], src) - r.seg0;
+        if (i < kSpec) {
+          r.ptr[0] = (const void*)__shfl((long long)ref[i].gate, src);
+          r.ptr[1] = (const void*)__shfl((long long)ref[i].up, src);
+          r.ptr[2] = (const void*)__shfl((long long)ref[i].down, src);
+        } else {
+          const moe_expert_ref t = table[r.e];
+          r.ptr[0] = t.gate;
+          r.ptr[1] = t.up;
+          r.ptr[2] = t.down;
+        }
+      }
+      U += cnt;
+    }
+  }
+  r.U = U;
+  return r;
 }
 
+// ---------------------------------------------------------------- unit loads
+// A 16-bit scale is fetched as the aligned dword that contains it (the scales
+// region is 256-byte aligned, so the dword lies inside it) and selected at use.
+__device__ __forceinline__ uint32_t load_scale_dword(gu16_t sc, int64_t idx) {
+  typedef const uint32_t __attribute__((address_space(1)))* gu32_t;
+  return *(gu32_t)(sc + (idx & ~(int64_t)1));
+}
+__device__ __forceinline__ uint16_t scale_from_dword(uint32_t w, int64_t idx) {
+  return (uint16_t)(w >> ((idx & 1) * 16));
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 template <int BITS>
-__global__ __launch_bounds__(512) void k_gateup(
-    const moe_expert_ref* __restrict__ table, const int32_t* __restrict__ active, int E,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs, int K,
-    const uint16_t* __restrict__ x, int H, int I, int scale_f16, const float* __restrict__ xcorr,
-    uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo, float* __restrict__ hcorr) {
+__device__ __forceinline__ void load_unit4(gbytes_t codes, int64_t tile, int lane,
+                                           u32x4 (&w)[UnitCodec<BITS>::CHUNKS]) {
   using C = UnitCodec<BITS>;
-  const int a = blockIdx.x;
-  const int U = active[E];
-  if (a >= U) return;
-  const int e = active[a];
-  const int seg0 = offsets[e], n_e = offsets[e + 1] - seg0;
-  const int strip = blockIdx.y;
+  typedef const u32x4 __attribute__((address_space(1)))* gu4_t;
+#pragma unroll
+  for (int j = 0; j < C::CHUNKS; ++j)
+    w[j] = *(gu4_t)(codes + (tile * C::CHUNKS + j) * 1024 + 16 * lane);
+}
+
+// The unit's words, passed through an empty asm so that the decode that follows
+// stays inside the token loop (hoisting every group's decoded pairs out of it
+// would need GPW * 128 registers).
+template <int BITS>
+__device__ __forceinline__ void unit_words(const u32x4 (&c)[UnitCodec<BITS>::CHUNKS],
+                                           uint32_t (&w)[UnitCodec<BITS>::WORDS]) {
+#pragma unroll
+  for (int j = 0; j < UnitCodec<BITS>::CHUNKS; ++j) {
+    w[4 * j + 0] = c[j].x;
+    w[4 * j + 1] = c[j].y;
+    w[4 * j + 2] = c[j].z;
+    w[4 * j + 3] = c[j].w;
+  }
+#pragma unroll
+  for (int k = 0; k < UnitCodec<BITS>::WORDS; ++k) asm volatile("" : "+v"(w[k]));
+}
+
+// Offset sums cs[j][g] = sum_k off_k * v[j][g*G + k] of nc rows of bf16 values
+// staged in LDS (row stride `stride` elements), all threads of the block taking
+// part: items (j, g, quarter) sum a quarter of a group's pairs each, in pair
+// order, then one thread per (j, g) adds the four quarters in order.
+template <int BITS>
+__device__ __forceinline__ void offset_sums_lds(const uint16_t* v, int stride, int nc, int ng,
+                                                float* part, float* cs, int nthreads) {
+  using C = UnitCodec<BITS>;
+  constexpr int QP = C::PAIRS / 4;  // pairs per quarter (a multiple of 4)
+  for (int i = threadIdx.x; i < nc * ng * 4; i += nthreads) {
+    const int q = i % 4, jg = i / 4, j = jg / ng, g = jg % ng;
+    const uint4* src = reinterpret_cast<const uint4*>(v + j * stride + g * C::G) + q * (QP / 4);
+    float acc = 0.f;
+#pragma unroll
+    for (int r = 0; r < QP / 4; ++r) {
+      const uint4 w = src[r];
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float off = C::pair_off(q * QP + 4 * r + k);
+        acc = fmaf(off, bf16_to_f32((uint16_t)(ws[k] >> 16)),
+                   fmaf(off, bf16_to_f32((uint16_t)ws[k]), acc));
+      }
+    }
+    part[i] = acc;
+  }
+  lds_barrier();
+  for (int i = threadIdx.x; i < nc * ng; i += nthreads)
+    cs[i] = ((part[4 * i] + part[4 * i + 1]) + part[4 * i + 2]) + part[4 * i + 3];
+  lds_barrier();
+}
+
+// ---------------------------------------------------------------- gate / up
+// Block (a, strip, m*KP + kp): matrix m (0 gate, 1 up) of the a-th active
+// expert, rows [64*strip, 64*strip+64), part kp of the reduction dimension (a
+// contiguous range of groups); 4 waves take groups g0 + wave + 4*i, i < GPW.
+//
+// Memory schedule.  Every wave issues the vector loads of all its groups' codes
+// and scales at entry, so the whole weight stream is in flight after one memory
+// latency.  The activations take the scalar path instead (s_load into SGPRs,
+// the second operand of v_dot2_f32_bf16): they do not queue behind the weight
+// stream, so each group is computed as soon as its own codes arrive.  The
+// per-group offset sums of the activations (what the unit codec's dot products
+// carry) come from vector loads that are only needed at the very end.
+//
+// Tokens run two at a time against the resident weights; each pair is expanded
+// right before its dot products.  The partial product (fp32) goes to
+// gu[m*KP + kp][pos][row] at the pair's sorted position; the parts are added in
+// kp order, with SwiGLU, where the down matrix reads them.
+constexpr int kGUWaves = 4;
+constexpr int kTokPerPass = 2;
+
+// Sum over the 64 lanes in a fixed order (row prefix sums by DPP, then the row
+// totals), returned to every lane; deterministic, no LDS traffic.
+template <int CTRL>
+__device__ __forceinline__ float dpp_shift(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int BITS>
+__device__ __forceinline__ float wave_sum_uniform(float v) {
+  v += dpp_shift<0x111>(v);  // row_shr:1
+  v += dpp_shift<0x112>(v);  // row_shr:2
+  v += dpp_shift<0x114>(v);  // row_shr:4
+  v += dpp_shift<0x118>(v);  // row_shr:8
+  v += dpp_shift<0x142>(v);  // row_bcast:15
+  v += dpp_shift<0x143>(v);  // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+template <int BITS, int GPW>
+__global__ __launch_bounds__(256, 2) void k_gateup(
+    const moe_expert_ref* __restrict__ table, int E, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_pairs, int K,
+    const uint16_t* __restrict__ x,  // read-only: dot operands through scalar loads
+    const uint16_t* x_vec,           // the same activations; not restrict, so that its vector
+                                     // loads stay ahead of the weight loads
+    int H, int I,
+    int P, int KP, int scale_f16, float* __restrict__ gu) {
+  using C = UnitCodec<BITS>;
+  __shared__ float red[kGUWaves][kTokPerPass][64];
+  const int ng = H / C::G;
+
+  const Active act = find_active(offsets, table, E, blockIdx.x);
+  if (act.e < 0) return;
+  const int seg0 = __builtin_amdgcn_readfirstlane(act.seg0);
+  const int n_e = __builtin_amdgcn_readfirstlane(act.n);
+  const int strip = blockIdx.y, m = blockIdx.z / KP, kp = blockIdx.z % KP;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ng = H / C::G;
   const MatGeom gm{I, H, BITS, C::G};
-  const uint8_t* gate = reinterpret_cast<const uint8_t*>(table[e].gate);
-  const uint8_t* up = reinterpret_cast<const uint8_t*>(table[e].up);
-  const uint16_t* gsc = reinterpret_cast<const uint16_t*>(gate + gm.scales_off());
-  const uint16_t* usc = reinterpret_cast<const uint16_t*>(up + gm.scales_off());
+  const gbytes_t mat = as_global(m ? act.ptr[1] : act.ptr[0]);
+  const gu16_t msc = (gu16_t)(mat + gm.scales_off());
   const int row = strip * 64 + lane;
+  const int gpb = (ng + KP - 1) / KP, g0 = kp * gpb, g1 = min(ng, g0 + gpb);
   const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
-  const int hseg = C::G < 64 ? C::G : 64;
+  const uint32_t* xv32 = reinterpret_cast<const uint32_t*>(x_vec);
 
-  __shared__ float red[kGUWaves][2][kNT][64];
-  __shared__ float hc[kNT][64];
+  // activation pairs of this wave's groups for the offset sums (lane = pair),
+  // requested before the weights so that their waits never wait for the weights
+  auto load_xo = [&](int t, uint32_t (&xo)[GPW]) {
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+      const int g = min(g0 + wv + kGUWaves * i, g1 - 1);
+      const int pl = lane < C::PAIRS ? lane : 0;
+      xo[i] = xv32[((int64_t)t * H + g * C::G) / 2 + pl];
+    }
+  };
+  int t0 = sorted_pairs[seg0] / K;
+  int t1 = n_e > 1 ? sorted_pairs[seg0 + 1] / K : t0;
+  uint32_t xo0[GPW], xo1[GPW];
+  load_xo(t0, xo0);
+  load_xo(t1, xo1);
+  asm volatile("" ::: "memory");
 
-  for (int b0 = 0; b0 < n_e; b0 += kNT) {
-    const int nt = min(kNT, n_e - b0);
-    int tok[kNT];
+  // weights: all groups of this wave at once (group index clamped, not branched
+  // on, so that the waits the compiler places stay exact)
+  u32x4 cw[GPW][C::CHUNKS];
+  uint32_t sr[GPW];  // the aligned dword holding the scale (any 16-bit handling here would wait)
 #pragma unroll
-    for (int j = 0; j < kNT; ++j) tok[j] = j < nt ? sorted_pairs[seg0 + b0 + j] / K : 0;
-    float ag[kNT], au[kNT];
+  for (int i = 0; i < GPW; ++i) {
+    const int g = min(g0 + wv + kGUWaves * i, g1 - 1);
+    load_unit4<BITS>(mat, (int64_t)strip * ng + g, lane, cw[i]);
+    sr[i] = load_scale_dword(msc, (int64_t)row * ng + g);
+  }
+  asm volatile("" ::: "memory");
+
+  for (int b0 = 0; b0 < n_e; b0 += kTokPerPass) {
+    const bool two = b0 + 1 < n_e;
+    if (b0 > 0) {
+      t0 = sorted_pairs[seg0 + b0] / K;
+      t1 = two ? sorted_pairs[seg0 + b0 + 1] / K : t0;
+      load_xo(t0, xo0);
+      load_xo(t1, xo1);
+    }
+    float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-    for (int j = 0; j < kNT; ++j) ag[j] = au[j] = 0.f;
-    for (int g = wv; g < ng; g += kGUWaves) {
-      const int64_t tile = (int64_t)strip * ng + g;
-      uint32_t wg[C::WORDS], wu[C::WORDS];
-      load_unit<BITS>(gate, tile, lane, wg);
-      load_unit<BITS>(up, tile, lane, wu);
-      const float sg = scale_to_f32(gsc[(int64_t)row * ng + g], scale_f16);
-      const float su = scale_to_f32(usc[(int64_t)row * ng + g], scale_f16);
-      uint32_t p[C::PAIRS];
-      C::decode(wg, p);
-#pragma unroll
-      for (int j = 0; j < kNT; ++j) {
-        if (j < nt) {
-          const uint32_t* xr = x32 + ((int64_t)tok[j] * H + g * C::G) / 2;
-          float d = -xcorr[(int64_t)tok[j] * ng + g];
-#pragma unroll
-          for (int P = 0; P < C::PAIRS; ++P) d = dot2_bf16(p[P], xr[P], d);
-          ag[j] = fmaf(sg, d, ag[j]);
+    for (int i = 0; i < GPW; ++i) {
+      const int g = g0 + wv + kGUWaves * i;
+      if (g < g1) {
+        const uint32_t* x0 = x32 + ((int64_t)t0 * H + g * C::G) / 2;
+        const uint32_t* x1 = x32 + ((int64_t)t1 * H + g * C::G) / 2;
+        uint32_t sraw = sr[i];
+        asm volatile("" : "+v"(sraw));  // convert here, not hoisted ahead of the loads
+        const float sc = scale_to_f32(scale_from_dword(sraw, (int64_t)row * ng + g), scale_f16);
+        uint32_t w[C::WORDS];
+        float d0 = 0.f, d1 = 0.f;
+        unit_words<BITS>(cw[i], w);
+        if (two) {
+          C::for_each_pair(w, [&](int Pp, uint32_t pr) {
+            d0 = dot2_bf16(pr, x0[Pp], d0);
+            d1 = dot2_bf16(pr, x1[Pp], d1);
+          });
+          a1 = fmaf(sc, d1, a1);
+        } else {
+          C::for_each_pair(w, [&](int Pp, uint32_t pr) { d0 = dot2_bf16(pr, x0[Pp], d0); });
         }
+        a0 = fmaf(sc, d0, a0);
       }
-      C::decode(wu, p);
+    }
+    // subtract sum_g s_g * (offset sum of group g)
 #pragma unroll
-      for (int j = 0; j < kNT; ++j) {
-        if (j < nt) {
-          const uint32_t* xr = x32 + ((int64_t)tok[j] * H + g * C::G) / 2;
-          float d = -xcorr[(int64_t)tok[j] * ng + g];
-#pragma unroll
-          for (int P = 0; P < C::PAIRS; ++P) d = dot2_bf16(p[P], xr[P], d);
-          au[j] = fmaf(su, d, au[j]);
+    for (int i = 0; i < GPW; ++i) {
+      const int g = g0 + wv + kGUWaves * i;
+      if (g < g1) {
+        uint32_t sraw = sr[i];
+        asm volatile("" : "+v"(sraw));
+        const float sc = scale_to_f32(scale_from_dword(sraw, (int64_t)row * ng + g), scale_f16);
+        const float off = lane < C::PAIRS ? C::pair_off(lane) : 0.f;
+        const float c0 = wave_sum_uniform<BITS>(
+            off * bf16_to_f32((uint16_t)xo0[i]) + off * bf16_to_f32((uint16_t)(xo0[i] >> 16)));
+        a0 = fmaf(-sc, c0, a0);
+        if (two) {
+          const float c1 = wave_sum_uniform<BITS>(
+              off * bf16_to_f32((uint16_t)xo1[i]) + off * bf16_to_f32((uint16_t)(xo1[i] >> 16)));
+          a1 = fmaf(-sc, c1, a1);
         }
       }
     }
-#pragma unroll
-    for (int j = 0; j < kNT; ++j) {
-      red[wv][0][j][lane] = ag[j];
-      red[wv][1][j][lane] = au[j];
-    }
-    __syncthreads();
-    // wave j (< nt) finishes token j: lane = row
-    if (wv < nt) {
+    red[wv][0][lane] = a0;
+    red[wv][1][lane] = a1;
+    lds_barrier();
+    if (wv < (two ? 2 : 1)) {
       const int j = wv;
-      float gs = 0.f, us = 0.f;
+      float y = 0.f;
 #pragma unroll
-      for (int w = 0; w < kGUWaves; ++w) {
-        gs += red[w][0][j][lane];
-        us += red[w][1][j][lane];
-      }
-      const float h = gs / (1.f + __expf(-gs)) * us;
-      const uint16_t hi = f32_to_bf16_rne(h);
-      const uint16_t lo = f32_to_bf16_rne(h - bf16_to_f32(hi));
-      const int64_t pos = seg0 + b0 + j;
-      h_hi[pos * I + row] = hi;
-      h_lo[pos * I + row] = lo;
-      // offset of this row as a reduction index of the down matrix
-      const float off = UnitCodec<BITS>::pair_off((row % C::G) / 2);
-      hc[j][lane] = off * bf16_to_f32(hi) + off * bf16_to_f32(lo);
+      for (int w = 0; w < kGUWaves; ++w) y += red[w][j][lane];
+      gu[((int64_t)blockIdx.z * P + seg0 + b0 + j) * I + row] = y;
     }
-    __syncthreads();
-    if (threadIdx.x < nt * (64 / hseg)) {
-      const int j = threadIdx.x / (64 / hseg), s = threadIdx.x % (64 / hseg);
-      float acc = 0.f;
-      for (int r = 0; r < hseg; ++r) acc += hc[j][s * hseg + r];
-      const int64_t pos = seg0 + b0 + j;
-      hcorr[pos * (I / hseg) + (strip * 64) / hseg + s] = acc;
-    }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
 // ---------------------------------------------------------------- down
-// Block (a, strip): rows [64*strip, +64) of the down matrix of active expert a,
-// 4 waves take groups g = wave, wave+4, ...; each token's h (hi and lo pairs)
-// comes through scalar loads.  y goes to pair_out at the pair's sorted position.
+// Block (a, strip): rows [64*strip, +64) of the down matrix of the a-th active
+// expert; 4 waves take groups g = wave + 4*i, i < GPW, loaded into registers at
+// entry.  While they are in flight the block forms h = silu(g) * u for its
+// tokens from the gate and up products, as bf16 hi + bf16 remainder (h to
+// ~2^-16 relative) in LDS, with the per-group offset sums of hi and lo.  Tokens
+// two at a time; y goes to pair_out at the pair's sorted position.
 constexpr int kDNWaves = 4;
+constexpr int kHChunk = 4;  // tokens' h staged in LDS at a time
 
-template <int BITS>
+__host__ __device__ constexpr int down_lds_bytes(int I, int G) {
+  return kHChunk * I * 4 + 2 * kHChunk * (I / G) * 4 * 5;
+}
+
+template <int BITS, int GPW>
 __global__ __launch_bounds__(256) void k_down(
-    const moe_expert_ref* __restrict__ table, const int32_t* __restrict__ active, int E,
-    const int32_t* __restrict__ offsets, int H, int I, int scale_f16,
-    const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo,
-    const float* __restrict__ hcorr, float* __restrict__ pair_out) {
+    const moe_expert_ref* __restrict__ table, int E, const int32_t* __restrict__ offsets, int H,
+    int I, int P, int KP, int scale_f16, const float* __restrict__ gu, float* __restrict__ pair_out) {
   using C = UnitCodec<BITS>;
-  const int a = blockIdx.x;
-  const int U = active[E];
-  if (a >= U) return;
-  const int e = active[a];
-  const int seg0 = offsets[e], n_e = offsets[e + 1] - seg0;
+  extern __shared__ __align__(16) uint8_t dyn[];
+  const int ng = I / C::G;
+  uint16_t* hs = reinterpret_cast<uint16_t*>(dyn);                  // [kHChunk * 2][I]: hi, lo
+  float* cs = reinterpret_cast<float*>(dyn + kHChunk * I * 4);       // [kHChunk * 2][ng]
+  float* part = cs + 2 * kHChunk * ng;                               // [kHChunk * 2][ng][4]
+  __shared__ float red[kDNWaves][kTokPerPass][64];
+
+  const Active act = find_active(offsets, table, E, blockIdx.x);
+  if (act.e < 0) return;
+  const int seg0 = __builtin_amdgcn_readfirstlane(act.seg0);
+  const int n_e = __builtin_amdgcn_readfirstlane(act.n);
   const int strip = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ng = I / C::G;
-  const int hseg = C::G < 64 ? C::G : 64;
-  const int nseg = I / hseg, seg_per_g = C::G / hseg;
   const MatGeom gm{H, I, BITS, C::G};
-  const uint8_t* down = reinterpret_cast<const uint8_t*>(table[e].down);
-  const uint16_t* dsc = reinterpret_cast<const uint16_t*>(down + gm.scales_off());
+  const gbytes_t down = as_global(act.ptr[2]);
+  const gu16_t dsc = (gu16_t)(down + gm.scales_off());
   const int row = strip * 64 + lane;
-  __shared__ float red[kDNWaves][kNT][64];
 
-  for (int b0 = 0; b0 < n_e; b0 += kNT) {
-    const int nt = min(kNT, n_e - b0);
-    float acc[kNT];
+  u32x4 cw[GPW][C::CHUNKS];
+  uint32_t sr[GPW];  // the aligned dword holding the scale (any 16-bit handling here would wait)
 #pragma unroll
-    for (int j = 0; j < kNT; ++j) acc[j] = 0.f;
-    for (int g = wv; g < ng; g += kDNWaves) {
-      const int64_t tile = (int64_t)strip * ng + g;
-      uint32_t w[C::WORDS];
-      load_unit<BITS>(down, tile, lane, w);
-      const float s = scale_to_f32(dsc[(int64_t)row * ng + g], scale_f16);
-      uint32_t p[C::PAIRS];
-      C::decode(w, p);
-#pragma unroll
-      for (int j = 0; j < kNT; ++j) {
-        if (j < nt) {
-          const int64_t pos = seg0 + b0 + j;
-          const uint32_t* hh = reinterpret_cast<const uint32_t*>(h_hi + pos * I + g * C::G);
-          const uint32_t* hl = reinterpret_cast<const uint32_t*>(h_lo + pos * I + g * C::G);
-          float corr = 0.f;
-          for (int q = 0; q < seg_per_g; ++q) corr += hcorr[pos * nseg + g * seg_per_g + q];
-          float d = -corr;
-#pragma unroll
-          for (int P = 0; P < C::PAIRS; ++P) d = dot2_bf16(p[P], hh[P], d);
-#pragma unroll
-          for (int P = 0; P < C::PAIRS; ++P) d = dot2_bf16(p[P], hl[P], d);
-          acc[j] = fmaf(s, d, acc[j]);
-        }
+  for (int i = 0; i < GPW; ++i) {
+    const int g = min(wv + kDNWaves * i, ng - 1);
+    load_unit4<BITS>(down, (int64_t)strip * ng + g, lane, cw[i]);
+    sr[i] = load_scale_dword(dsc, (int64_t)row * ng + g);
+  }
+
+  for (int c0 = 0; c0 < n_e; c0 += kHChunk) {
+    const int nc = min(kHChunk, n_e - c0);
+    lds_barrier();
+    for (int i = threadIdx.x; i < nc * I; i += 64 * kDNWaves) {
+      const int j = i / I, k = i % I;
+      const int64_t pos = seg0 + c0 + j;
+      float gv = 0.f, uv = 0.f;
+      for (int q = 0; q < KP; ++q) {
+        gv += gu[((int64_t)q * P + pos) * I + k];
+        uv += gu[((int64_t)(KP + q) * P + pos) * I + k];
       }
+      const float h = gv / (1.f + __expf(-gv)) * uv;
+      const uint16_t hi = f32_to_bf16_rne(h);
+      hs[(2 * j) * I + k] = hi;
+      hs[(2 * j + 1) * I + k] = f32_to_bf16_rne(h - bf16_to_f32(hi));
     }
+    lds_barrier();
+    // rows 2j (hi) and 2j+1 (lo): offset sums of both; the dot uses their sum
+    offset_sums_lds<BITS>(hs, I, 2 * nc, ng, part, cs, 64 * kDNWaves);
+    for (int jp = 0; jp < nc; jp += kTokPerPass) {
+      const bool two = jp + 1 < nc;
+      const int j1 = two ? jp + 1 : jp;
+      float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-    for (int j = 0; j < kNT; ++j) red[wv][j][lane] = acc[j];
-    __syncthreads();
-    if (wv == 0) {
-      for (int j = 0; j < nt; ++j) {
+      for (int i = 0; i < GPW; ++i) {
+        const int g = wv + kDNWaves * i;
+        if (g < ng) {
+          uint32_t wd[C::WORDS];
+          unit_words<BITS>(cw[i], wd);
+          uint32_t sraw = sr[i];
+          asm volatile("" : "+v"(sraw));
+          const float s = scale_to_f32(scale_from_dword(sraw, (int64_t)row * ng + g), scale_f16);
+          const uint32_t* hh0 = reinterpret_cast<const uint32_t*>(hs + (jp * 2 + 0) * I + g * C::G);
+          const uint32_t* hl0 = reinterpret_cast<const uint32_t*>(hs + (jp * 2 + 1) * I + g * C::G);
+          const uint32_t* hh1 = reinterpret_cast<const uint32_t*>(hs + (j1 * 2 + 0) * I + g * C::G);
+          const uint32_t* hl1 = reinterpret_cast<const uint32_t*>(hs + (j1 * 2 + 1) * I + g * C::G);
+          const float k0 = cs[(2 * jp) * ng + g] + cs[(2 * jp + 1) * ng + g];
+          const float k1 = cs[(2 * j1) * ng + g] + cs[(2 * j1 + 1) * ng + g];
+          float d0 = 0.f, d1 = 0.f;
+          if (two) {
+            C::for_each_pair(wd, [&](int Pp, uint32_t pr) {
+              d0 = dot2_bf16(pr, hl0[Pp], dot2_bf16(pr, hh0[Pp], d0));
+              d1 = dot2_bf16(pr, hl1[Pp], dot2_bf16(pr, hh1[Pp], d1));
+            });
+            a1 = fmaf(s, d1 - k1, a1);
+          } else {
+            C::for_each_pair(wd, [&](int Pp, uint32_t pr) {
+              d0 = dot2_bf16(pr, hl0[Pp], dot2_bf16(pr, hh0[Pp], d0));
+            });
+          }
+          a0 = fmaf(s, d0 - k0, a0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      red[wv][0][lane] = a0;
+      red[wv][1][lane] = a1;
+      lds_barrier();
+      if (wv < (two ? 2 : 1)) {
+        const int j = wv;
         float y = 0.f;
 #pragma unroll
-        for (int w = 0; w < kDNWaves; ++w) y += red[w][j][lane];
-        pair_out[(int64_t)(seg0 + b0 + j) * H + row] = y;
+        for (int ww = 0; ww < kDNWaves; ++ww) y += red[ww][j][lane];
+        pair_out[(int64_t)(seg0 + c0 + jp + j) * H + row] = y;
       }
+      lds_barrier();
     }
-    __syncthreads();
   }
 }
 
@@ -298,6 +460,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ pair_
 // Row-major bf16 weights.  Block = 8 rows x 32 lanes per row (each lane reads 8
 // consecutive bf16 per step, a half-wave covers 256 of a row); fp32 FMAs.
 constexpr int kShRows = 8;
+constexpr int kNT = 8;  // tokens per pass of the shared-expert kernels
 
 __device__ __forceinline__ float half_wave_sum(float v) {
 #pragma unroll
@@ -420,35 +583,50 @@ hipError_t launch_forward_t(const FwdArgs& f, hipStream_t s) {
   const moe_cfg& c = *f.c;
   const int H = c.hidden, I = c.inter, E = c.n_experts, K = c.top_k, T = f.T;
   const WsLayout L = ws_layout(c, T);
-  int32_t* active = reinterpret_cast<int32_t*>(f.ws + L.active);
-  float* xcorr = reinterpret_cast<float*>(f.ws + L.xcorr);
-  uint16_t* h_hi = reinterpret_cast<uint16_t*>(f.ws + L.h_hi);
-  uint16_t* h_lo = reinterpret_cast<uint16_t*>(f.ws + L.h_lo);
-  float* hcorr = reinterpret_cast<float*>(f.ws + L.hcorr);
+  float* gu = reinterpret_cast<float*>(f.ws + L.gu);
   float* pair_out = f.pair_out ? f.pair_out : reinterpret_cast<float*>(f.ws + L.pair_out);
   float* sh_h = reinterpret_cast<float*>(f.ws + L.sh_h);
   float* sh_out = reinterpret_cast<float*>(f.ws + L.sh_out);
-  const int ngx = H / C::G;
-  const int plan_blocks = (T * ngx + 255) / 256;
-  MOE_LAUNCH(KID_PLAN, k_plan<BITS>, dim3(plan_blocks > 0 ? plan_blocks : 1), dim3(256), 0, s,
-                     f.offsets, E, f.x, T, H, active, xcorr);
   const int maxU = min(E, T * K);
-  MOE_LAUNCH(KID_GATEUP, k_gateup<BITS>, dim3(maxU, I / 64), dim3(64 * kGUWaves), 0, s, f.table,
-                     active, E, f.offsets, f.sorted_pairs, K, f.x, H, I, c.scale_f16, xcorr, h_hi,
-                     h_lo, hcorr);
-  MOE_LAUNCH(KID_DOWN, k_down<BITS>, dim3(maxU, H / 64), dim3(64 * kDNWaves), 0, s, f.table, active,
-                     E, f.offsets, H, I, c.scale_f16, h_hi, h_lo, hcorr, pair_out);
+  // gate/up: reduction dim split over KP blocks of at most 4 waves x 5 groups
+  const int ngh = H / C::G;
+  const int KP = (ngh + 5 * kGUWaves - 1) / (5 * kGUWaves);  // <= kMaxKParts for H/G <= 64
+  const int gpw_gu = ((ngh + KP - 1) / KP + kGUWaves - 1) / kGUWaves;
+  const int gpw_dn = (I / C::G + kDNWaves - 1) / kDNWaves;
+  const int lds_dn = down_lds_bytes(I, C::G);
+#define MOE_GU(N)                                                                               \
+  case N:                                                                                       \
+    MOE_LAUNCH(KID_GATEUP, (k_gateup<BITS, N>), dim3(maxU, I / 64, 2 * KP), dim3(64 * kGUWaves),\
+               0, s, f.table, E, f.offsets, f.sorted_pairs, K, f.x, f.x, H, I, T * K, KP,       \
+               c.scale_f16, gu);                                                                \
+    break;
+  switch (gpw_gu) {
+    MOE_GU(1) MOE_GU(2) MOE_GU(3) MOE_GU(4) MOE_GU(5) MOE_GU(6) MOE_GU(7) MOE_GU(8)
+    MOE_GU(9) MOE_GU(10) MOE_GU(11) MOE_GU(12) MOE_GU(13) MOE_GU(14) MOE_GU(15) MOE_GU(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_GU
+#define MOE_DN(N)                                                                               \
+  case N:                                                                                       \
+    MOE_LAUNCH(KID_DOWN, (k_down<BITS, N>), dim3(maxU, H / 64), dim3(64 * kDNWaves), lds_dn, s, \
+               f.table, E, f.offsets, H, I, T * K, KP, c.scale_f16, gu, pair_out);              \
+    break;
+  switch (gpw_dn) {
+    MOE_DN(1) MOE_DN(2) MOE_DN(3) MOE_DN(4) MOE_DN(5) MOE_DN(6) MOE_DN(7) MOE_DN(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_DN
   const bool has_shared = c.shared_inter > 0 && f.sg && f.su && f.sd;
   if (has_shared) {
     const int Is = c.shared_inter;
     MOE_LAUNCH(KID_SH_GATEUP, k_shared_gateup, dim3(Is / kShRows), dim3(256), 0, s,
-                       reinterpret_cast<const uint16_t*>(f.sg),
-                       reinterpret_cast<const uint16_t*>(f.su), f.x, T, H, Is, sh_h);
+               reinterpret_cast<const uint16_t*>(f.sg), reinterpret_cast<const uint16_t*>(f.su),
+               f.x, T, H, Is, sh_h);
     MOE_LAUNCH(KID_SH_DOWN, k_shared_down, dim3(H / kShRows), dim3(256), 0, s,
-                       reinterpret_cast<const uint16_t*>(f.sd), sh_h, T, H, Is, sh_out);
+               reinterpret_cast<const uint16_t*>(f.sd), sh_h, T, H, Is, sh_out);
   }
-  MOE_LAUNCH(KID_COMBINE, k_combine, dim3((H + 255) / 256, T), dim3(256), 0, s, pair_out, f.pair_pos,
-                     f.w, K, H, has_shared ? sh_out : nullptr, f.out);
+  MOE_LAUNCH(KID_COMBINE, k_combine, dim3((H + 255) / 256, T), dim3(256), 0, s, pair_out,
+               f.pair_pos, f.w, K, H, has_shared ? sh_out : nullptr, f.out);
   return hipGetLastError();
 }
 

@@ -109,65 +109,74 @@ __global__ __launch_bounds__(256) void k_logits_tiled(const uint16_t* __restrict
 }
 
 // ---------------------------------------------------------------- top-k + weights
-// One wave per token.  Each lane keeps the logits of experts lane, lane+64, ...;
-// K rounds of a butterfly arg-max over (value desc, id asc) pick the experts in
-// output order.  Weights: exp(l_k - l_0) / sum_j exp(l_j - l_0) in fp64.
-constexpr int kMaxPerLane = 16;  // E <= 1024
+// Rank counting: expert e is pick number r = #{e' : l[e'] > l[e] or (l[e'] == l[e]
+// and e' < e)}, so the picks come out in output order (descending logit, ties to
+// the lower id) without any data-dependent reduction order.  One block per token:
+// the token's logits are staged in LDS, the E*E comparisons are split over the
+// block's threads and the partial ranks summed with integer LDS atomics (exact).
+// Weights: w_k = exp(l_k - l_0) / sum_{j<K} exp(l_j - l_0) in fp64, the sum taken
+// in k order by one thread.
+constexpr int kMaxE = 1024;
 constexpr int kMaxK = 16;
+constexpr int kTopkThreads = 1024;
 
-__device__ __forceinline__ bool better(double va, int ia, double vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
+__device__ void block_topk(const double* __restrict__ l_global, int E, int K, double* ls, int* rank,
+                           double* top_l, int* top_id, int32_t* __restrict__ ids_out,
+                           float* __restrict__ w_out, int32_t* ids_lds) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kTopkThreads) {
+    ls[e] = l_global[e];
+    rank[e] = 0;
+  }
+  __syncthreads();
+  // thread -> (expert slot, quarter of the comparison range)
+  const int q = tid / 256, slot = tid % 256;
+  const int c0 = q * E / 4, c1 = (q + 1) * E / 4;
+  for (int e = slot; e < E; e += 256) {
+    const double v = ls[e];
+    int r = 0;
+    for (int c = c0; c < c1; ++c) {
+      const double o = ls[c];
+      r += (o > v) | ((o == v) & (c < e));
+    }
+    atomicAdd(&rank[e], r);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kTopkThreads) {
+    const int r = rank[e];
+    if (r < K) {
+      top_l[r] = ls[e];
+      top_id[r] = e;
+    }
+  }
+  __syncthreads();
+  // thread k < K: term_k = exp(l_k - l_0); thread 0 sums the K terms in k order
+  if (tid < K) top_l[kMaxK + tid] = exp(top_l[tid] - top_l[0]);
+  __syncthreads();
+  if (tid == 0) {
+    double den = 0.0;
+    for (int k = 0; k < K; ++k) den += top_l[kMaxK + k];
+    top_l[2 * kMaxK] = den;
+  }
+  __syncthreads();
+  if (tid < K) {
+    ids_out[tid] = top_id[tid];
+    w_out[tid] = (float)(top_l[kMaxK + tid] / top_l[2 * kMaxK]);
+    if (ids_lds) ids_lds[tid] = top_id[tid];
+  }
+  __syncthreads();
 }
 
-__global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits, int T, int E,
-                                              int K, int32_t* __restrict__ ids,
-                                              float* __restrict__ wout) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const double* l = logits + (int64_t)t * E;
-  double v[kMaxPerLane];
-  const int per = (E + 63) / 64;
-#pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
-    int e = lane + 64 * i;
-    v[i] = (i < per && e < E) ? l[e] : -INFINITY;
-  }
-  uint32_t taken = 0;  // bit i: v[i] already picked
-  double lk[kMaxK];
-  int ik[kMaxK];
-  for (int k = 0; k < K; ++k) {
-    double bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-      int e = lane + 64 * i;
-      if (i < per && e < E && !(taken >> i & 1u) && better(v[i], e, bv, bi)) {
-        bv = v[i];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      double ov = __shfl_xor(bv, o);
-      int oi = __shfl_xor(bi, o);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    lk[k] = bv;
-    ik[k] = bi;
-  }
-  if (lane == 0) {
-    double den = 0.0;
-    for (int k = 0; k < K; ++k) den += exp(lk[k] - lk[0]);
-    for (int k = 0; k < K; ++k) {
-      ids[t * K + k] = ik[k];
-      wout[t * K + k] = (float)(exp(lk[k] - lk[0]) / den);
-    }
-  }
+__global__ __launch_bounds__(kTopkThreads) void k_topk(const double* __restrict__ logits, int T,
+                                                       int E, int K, int32_t* __restrict__ ids,
+                                                       float* __restrict__ wout) {
+  __shared__ double ls[kMaxE];
+  __shared__ int rank[kMaxE];
+  __shared__ double top_l[2 * kMaxK + 1];
+  __shared__ int top_id[kMaxK];
+  const int t = blockIdx.x;
+  block_topk(logits + (int64_t)t * E, E, K, ls, rank, top_l, top_id, ids + t * K, wout + t * K,
+             nullptr);
 }
 
 // ---------------------------------------------------------------- grouping
@@ -185,75 +194,117 @@ __device__ __forceinline__ uint64_t match_mask(int e, int nbits) {
   return m;
 }
 
-__global__ __launch_bounds__(64) void k_permute(const int32_t* __restrict__ ids, int P, int E,
-                                                int32_t* __restrict__ offsets,
-                                                int32_t* __restrict__ sorted_pairs,
-                                                int32_t* __restrict__ pair_pos) {
-  __shared__ int cnt[1025];
-  __shared__ int run[1024];
-  const int lane = threadIdx.x;
+// exclusive scan of cnt[0..E) in LDS by one wave (E <= 1024), total in cnt[E]
+__device__ __forceinline__ void wave_exclusive_scan(int* cnt, int E) {
+  const int lane = threadIdx.x & 63;
+  const int per = (E + 63) / 64;
+  const int b = lane * per;
+  int loc = 0;
+  for (int i = 0; i < per; ++i)
+    if (b + i < E) loc += cnt[b + i];
+  int inc = loc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  int run = inc - loc;
+  for (int i = 0; i < per; ++i)
+    if (b + i < E) {
+      const int c = cnt[b + i];
+      cnt[b + i] = run;
+      run += c;
+    }
+  if (lane == 63) cnt[E] = inc;
+}
+
+// stable grouping of P pairs by one wave; ids read through `ids` (global or LDS)
+__device__ void wave_group(const int32_t* ids, int P, int E, int* cnt, int* run,
+                           int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
+                           int32_t* __restrict__ pair_pos) {
+  const int lane = threadIdx.x & 63;
   int nbits = 0;
-  while ((1 << nbits) < E + 1) ++nbits;  // ids in [-1, E] fit (E means "invalid")
+  while ((1 << nbits) < E + 1) ++nbits;  // keys in [0, E]; E marks an invalid id
   for (int e = lane; e < E; e += 64) {
     cnt[e] = 0;
     run[e] = 0;
   }
-  __syncthreads();
   const uint64_t lt = (1ull << lane) - 1ull;
   for (int c0 = 0; c0 < P; c0 += 64) {
-    int p = c0 + lane;
-    int e = p < P ? ids[p] : -1;
-    bool ok = p < P && e >= 0 && e < E;
-    int key = ok ? e : E;
-    uint64_t m = match_mask(key, nbits);
+    const int p = c0 + lane;
+    const int e = p < P ? ids[p] : -1;
+    const bool ok = p < P && e >= 0 && e < E;
+    const uint64_t m = match_mask(ok ? e : E, nbits);
     if (ok && (m & lt) == 0) cnt[e] += __popcll(m);
-    __syncthreads();
   }
-  if (lane == 0) {
-    int s = 0;
-    for (int e = 0; e < E; ++e) {
-      int c = cnt[e];
-      cnt[e] = s;
-      s += c;
-    }
-    cnt[E] = s;
-  }
-  __syncthreads();
+  wave_exclusive_scan(cnt, E);
   for (int e = lane; e <= E; e += 64) offsets[e] = cnt[e];
   for (int c0 = 0; c0 < P; c0 += 64) {
-    int p = c0 + lane;
-    int e = p < P ? ids[p] : -1;
-    bool ok = p < P && e >= 0 && e < E;
-    int key = ok ? e : E;
-    uint64_t m = match_mask(key, nbits);
+    const int p = c0 + lane;
+    const int e = p < P ? ids[p] : -1;
+    const bool ok = p < P && e >= 0 && e < E;
+    const uint64_t m = match_mask(ok ? e : E, nbits);
     int pos = -1;
     if (ok) {
       pos = cnt[e] + run[e] + __popcll(m & lt);
       sorted_pairs[pos] = p;
     }
     if (p < P) pair_pos[p] = pos;
-    __syncthreads();
     if (ok && (m & lt) == 0) run[e] += __popcll(m);
-    __syncthreads();
   }
+}
+
+__global__ __launch_bounds__(64) void k_permute(const int32_t* __restrict__ ids, int P, int E,
+                                                int32_t* __restrict__ offsets,
+                                                int32_t* __restrict__ sorted_pairs,
+                                                int32_t* __restrict__ pair_pos) {
+  __shared__ int cnt[1025];
+  __shared__ int run[1024];
+  wave_group(ids, P, E, cnt, run, offsets, sorted_pairs, pair_pos);
+}
+
+// ---------------------------------------------------------------- top-k + grouping, small T
+// Decode batches (T * K <= 64): one block picks the top-k of every token (as
+// above) and its first wave groups the T*K pairs; one launch instead of two.
+__global__ __launch_bounds__(kTopkThreads) void k_topk_group_small(
+    const double* __restrict__ logits, int T, int E, int K, int32_t* __restrict__ ids,
+    float* __restrict__ wout, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
+    int32_t* __restrict__ pair_pos) {
+  __shared__ double ls[kMaxE];
+  __shared__ int rank[kMaxE];
+  __shared__ double top_l[2 * kMaxK + 1];
+  __shared__ int top_id[kMaxK];
+  __shared__ int32_t s_ids[64];
+  __shared__ int cnt[kMaxE + 1];
+  __shared__ int run[kMaxE];
+  for (int t = 0; t < T; ++t)
+    block_topk(logits + (int64_t)t * E, E, K, ls, rank, top_l, top_id, ids + t * K, wout + t * K,
+               s_ids + t * K);
+  if (threadIdx.x < 64) wave_group(s_ids, T * K, E, cnt, run, offsets, sorted_pairs, pair_pos);
 }
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_route(const moe_cfg& c, const uint16_t* x, int T, const float* wr,
                         const float* bias, int32_t* ids, float* w, int32_t* offsets,
                         int32_t* sorted_pairs, int32_t* pair_pos, double* logits,
-                        hipStream_t s) {
+                        int32_t* counter, hipStream_t s) {
   const int H = c.hidden, E = c.n_experts, K = c.top_k;
+  (void)counter;
   if (T <= 64) {
     MOE_LAUNCH(KID_LOGITS, k_logits_small, dim3(E, (T + kLogitTok - 1) / kLogitTok), dim3(256), 0, s,
-                       x, T, H, E, wr, bias, logits);
+               x, T, H, E, wr, bias, logits);
   } else {
     MOE_LAUNCH(KID_LOGITS, k_logits_tiled, dim3((E + kLE - 1) / kLE, (T + kLT - 1) / kLT), dim3(256),
-                       0, s, x, T, H, E, wr, bias, logits);
+               0, s, x, T, H, E, wr, bias, logits);
   }
-  MOE_LAUNCH(KID_TOPK, k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, K, ids, w);
+  if (T * K <= 64) {
+    MOE_LAUNCH(KID_TOPK, k_topk_group_small, dim3(1), dim3(kTopkThreads), 0, s, logits, T, E, K,
+               ids, w, offsets, sorted_pairs, pair_pos);
+    return hipGetLastError();
+  }
+  MOE_LAUNCH(KID_TOPK, k_topk, dim3(T), dim3(kTopkThreads), 0, s, logits, T, E, K, ids, w);
   MOE_LAUNCH(KID_PERMUTE, k_permute, dim3(1), dim3(64), 0, s, ids, T * K, E, offsets, sorted_pairs,
-                     pair_pos);
+             pair_pos);
   return hipGetLastError();
 }
 

@@ -244,3 +244,43 @@ def test_status_codes(gpu):
     m.moe_route(ml.ctx, xd, 0, dl.router, None, r.topk_ids, r.topk_w, r.expert_offsets,
                 r.sorted_pairs, r.pair_pos, ml.ws)
     ml.close()
+
+
+# ------------------------------------------------------------------ graph replay
+@pytest.mark.parametrize("name,T", [("c2", 1), ("c3", 8), ("c3", 5)])
+def test_graph_replay_matches_eager(gpu, name, T):
+    """route + forward captured in one HIP graph: every replay (with eager work of
+    other batch sizes in between, which moves the workspace counters and
+    buffers) equals the eager result bit for bit"""
+    say(f"[graph] {name} T={T}")
+    cfg = synth.CONFIGS[name]
+    dl = layer_for(name, gpu)
+    xh, xd = x_device(cfg, gpu, tokens=T)
+    ml = make_layer_api(cfg, dl, 16)
+    out = torch.empty((T, cfg.hidden), dtype=torch.float32, device=gpu)
+    r = ml.route(xd, dl.router, dl.bias)
+    ml.forward(0, xd, r, out)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    s = torch.cuda.Stream(device=gpu)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        r = ml.route(xd, dl.router, dl.bias)
+        ml.forward(0, xd, r, out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        r = ml.route(xd, dl.router, dl.bias)
+        ml.forward(0, xd, r, out)
+    _, x_other = x_device(cfg, gpu, tokens=16)
+    other = torch.empty((16, cfg.hidden), dtype=torch.float32, device=gpu)
+    for rep in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs"
+        ro = ml.route(x_other, dl.router, dl.bias)  # eager work between replays
+        ml.forward(0, x_other, ro, other)
+        torch.cuda.synchronize()
+    ml.close()
