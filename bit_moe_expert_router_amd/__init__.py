@@ -56,7 +56,7 @@ def _load():
     lib.moe_expert_table_device.restype = vp
     lib.moe_set_shared.argtypes = [vp, i32, vp, vp, vp]
     lib.moe_route.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
-    lib.moe_forward.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+    lib.moe_forward.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp,
                                 ctypes.c_size_t, vp]
     lib.moe_rmsnorm_bf16.argtypes = [vp, vp, vp, i32, ctypes.c_float, vp, vp]
     lib.moe_last_error.restype = ctypes.c_char_p
@@ -149,9 +149,9 @@ def moe_route(ctx: int, x_bf16, T: int, w_router, bias, topk_ids, topk_w, expert
 
 
 def moe_forward(ctx: int, layer: int, x_bf16, T: int, topk_ids, topk_w, expert_offsets,
-                sorted_pairs, pair_pos, out, pair_out, ws, stream=None):
+                sorted_pairs, out, pair_out, ws, stream=None):
     _check(lib.moe_forward(ctx, layer, _ptr(x_bf16), T, _ptr(topk_ids), _ptr(topk_w),
-                           _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(pair_pos), _ptr(out),
+                           _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(out),
                            _ptr(pair_out), _ptr(ws), ws.numel() * ws.element_size(),
                            _stream(stream)),
            "moe_forward")

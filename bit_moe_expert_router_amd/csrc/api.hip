@@ -180,16 +180,15 @@ moe_status moe_route(moe_ctx* ctx, const void* x_bf16, int32_t T, const float* w
 
 moe_status moe_forward(moe_ctx* ctx, int32_t layer, const void* x_bf16, int32_t T,
                        const int32_t* topk_ids, const float* topk_w,
-                       const int32_t* expert_offsets, const int32_t* sorted_pairs,
-                       const int32_t* pair_pos, float* out, float* pair_out, void* ws,
-                       size_t ws_bytes, moe_stream_t stream) {
+                       const int32_t* expert_offsets, const int32_t* sorted_pairs, float* out,
+                       float* pair_out, void* ws, size_t ws_bytes, moe_stream_t stream) {
   if (!ctx) return fail(MOE_E_ARG, "moe_forward: null context");
   const moe_cfg& c = ctx->cfg;
   if (layer < 0 || layer >= ctx->n_layers) return fail(MOE_E_ARG, "moe_forward: bad layer %d", layer);
   if (T < 0 || T > c.max_tokens) return fail(MOE_E_ARG, "moe_forward: T=%d outside [0, %d]", T, c.max_tokens);
   if (!ctx->table_set[layer]) return fail(MOE_E_STATE, "moe_forward: expert table of layer %d never set", layer);
   if (T == 0) return ok();
-  if (!x_bf16 || !topk_ids || !topk_w || !expert_offsets || !sorted_pairs || !pair_pos || !out || !ws)
+  if (!x_bf16 || !topk_ids || !topk_w || !expert_offsets || !sorted_pairs || !out || !ws)
     return fail(MOE_E_ARG, "moe_forward: null pointer argument");
   if (!aligned(x_bf16, 16) || !aligned(out, 16) || !aligned(ws, 256) || (pair_out && !aligned(pair_out, 16)))
     return fail(MOE_E_ARG, "moe_forward: x, out, pair_out must be 16-byte aligned, ws 256-byte aligned");
@@ -199,7 +198,7 @@ moe_status moe_forward(moe_ctx* ctx, int32_t layer, const void* x_bf16, int32_t 
   const moe_ctx::Shared& sh = ctx->shared[layer];
   moe::FwdArgs f{&c, ctx->d_tables + (size_t)layer * c.n_experts, sh.g, sh.u, sh.d,
                  (const uint16_t*)x_bf16, T, topk_ids, topk_w, expert_offsets, sorted_pairs,
-                 pair_pos, out, pair_out, (uint8_t*)ws};
+                 out, pair_out, (uint8_t*)ws};
   return hip_status(moe::launch_forward(f, (hipStream_t)stream), "moe_forward launch");
 }
 

@@ -231,7 +231,6 @@ struct FwdArgs {
   const float* w;
   const int32_t* offsets;
   const int32_t* sorted_pairs;
-  const int32_t* pair_pos;
   float* out;
   float* pair_out;              // null: workspace
   uint8_t* ws;

@@ -128,38 +128,6 @@ __device__ __forceinline__ void unit_words(const u32x4 (&c)[UnitCodec<BITS>::CHU
   for (int k = 0; k < UnitCodec<BITS>::WORDS; ++k) asm volatile("" : "+v"(w[k]));
 }
 
-// Offset sums cs[j][g] = sum_k off_k * v[j][g*G + k] of nc rows of bf16 values
-// staged in LDS (row stride `stride` elements), all threads of the block taking
-// part: items (j, g, quarter) sum a quarter of a group's pairs each, in pair
-// order, then one thread per (j, g) adds the four quarters in order.
-template <int BITS>
-__device__ __forceinline__ void offset_sums_lds(const uint16_t* v, int stride, int nc, int ng,
-                                                float* part, float* cs, int nthreads) {
-  using C = UnitCodec<BITS>;
-  constexpr int QP = C::PAIRS / 4;  // pairs per quarter (a multiple of 4)
-  for (int i = threadIdx.x; i < nc * ng * 4; i += nthreads) {
-    const int q = i % 4, jg = i / 4, j = jg / ng, g = jg % ng;
-    const uint4* src = reinterpret_cast<const uint4*>(v + j * stride + g * C::G) + q * (QP / 4);
-    float acc = 0.f;
-#pragma unroll
-    for (int r = 0; r < QP / 4; ++r) {
-      const uint4 w = src[r];
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float off = C::pair_off(q * QP + 4 * r + k);
-        acc = fmaf(off, bf16_to_f32((uint16_t)(ws[k] >> 16)),
-                   fmaf(off, bf16_to_f32((uint16_t)ws[k]), acc));
-      }
-    }
-    part[i] = acc;
-  }
-  lds_barrier();
-  for (int i = threadIdx.x; i < nc * ng; i += nthreads)
-    cs[i] = ((part[4 * i] + part[4 * i + 1]) + part[4 * i + 2]) + part[4 * i + 3];
-  lds_barrier();
-}
-
 // ---------------------------------------------------------------- gate / up
 // Block (a, strip, m*KP + kp): matrix m (0 gate, 1 up) of the a-th active
 // expert, rows [64*strip, 64*strip+64), part kp of the reduction dimension (a
@@ -323,27 +291,109 @@ __global__ __launch_bounds__(256, 2) void k_gateup(
 // ---------------------------------------------------------------- down
 // Block (a, strip): rows [64*strip, +64) of the down matrix of the a-th active
 // expert; 4 waves take groups g = wave + 4*i, i < GPW, loaded into registers at
-// entry.  While they are in flight the block forms h = silu(g) * u for its
-// tokens from the gate and up products, as bf16 hi + bf16 remainder (h to
-// ~2^-16 relative) in LDS, with the per-group offset sums of hi and lo.  Tokens
-// two at a time; y goes to pair_out at the pair's sorted position.
+// entry.  The block requests the gate/up partial products of its first tokens
+// (they sit in L2) before its weights, so h = silu(g) * u is formed while the
+// weights are in flight.  h is kept in LDS as bf16 hi + bf16 remainder (h to
+// ~2^-16 relative), with each group's offset sum sum_k off_k * (hi_k + lo_k)
+// reduced over the lanes that formed the group.  Tokens two at a time; y goes to
+// row p = t*K + k of pair_out.
 constexpr int kDNWaves = 4;
 constexpr int kHChunk = 4;  // tokens' h staged in LDS at a time
+constexpr int kSB = 2;      // float4 items of h per thread per staging batch
 
 __host__ __device__ constexpr int down_lds_bytes(int I, int G) {
-  return kHChunk * I * 4 + 2 * kHChunk * (I / G) * 4 * 5;
+  return kHChunk * I * 4 + kHChunk * (I / G) * 4;
+}
+
+// gate and up partial products of float4 item i4 of a chunk of tokens (token j =
+// i4 / (I/4) of the chunk); parts q >= KP repeat part KP-1 and are dropped at use,
+// so every load is unconditional.
+struct HItem {
+  float4 g[kMaxKParts], u[kMaxKParts];
+};
+
+__device__ __forceinline__ void h_load(const float* __restrict__ gu, int64_t P, int I, int KP,
+                                       int64_t pos0, int tot4, int i4, HItem& it) {
+  const int I4 = I / 4;
+  const int ic = min(i4, tot4 - 1);
+  const int j = ic / I4, k4 = ic - j * I4;
+  const float4* base = reinterpret_cast<const float4*>(gu) + (pos0 + j) * I4 + k4;
+  const int64_t part = P * I4;
+#pragma unroll
+  for (int q = 0; q < kMaxKParts; ++q) {
+    const int qq = min(q, KP - 1);
+    it.g[q] = base[qq * part];
+    it.u[q] = base[(KP + qq) * part];
+  }
+}
+
+// Sum over the aligned lanes of one group (32 lanes for G = 128, 8 for G = 32,
+// one float4 item each), valid in the group's last lane; fixed order.
+template <int BITS>
+__device__ __forceinline__ float group_lane_sum(float v) {
+  v += dpp_shift<0x111>(v);
+  v += dpp_shift<0x112>(v);
+  v += dpp_shift<0x114>(v);
+  if (BITS == 3) {
+    v += dpp_shift<0x118>(v);
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+  }
+  return v;
+}
+
+// h of one item to LDS (hi row 2j, lo row 2j+1) and its share of the group's
+// offset sum, written to kc[j][g] by the group's last lane.  Every lane of the
+// wave calls it (the lane sum needs them all); only items < tot4 store.
+template <int BITS>
+__device__ __forceinline__ void h_store(const HItem& it, int KP, int I, int tot4, int i4,
+                                        uint16_t* hs, float* kc) {
+  using C = UnitCodec<BITS>;
+  const int I4 = I / 4;
+  const int ic = min(i4, tot4 - 1);
+  const int j = ic / I4, k4 = ic - j * I4;
+  float4 g = it.g[0], u = it.u[0];
+#pragma unroll
+  for (int q = 1; q < kMaxKParts; ++q)
+    if (q < KP) {
+      g.x += it.g[q].x; g.y += it.g[q].y; g.z += it.g[q].z; g.w += it.g[q].w;
+      u.x += it.u[q].x; u.y += it.u[q].y; u.z += it.u[q].z; u.w += it.u[q].w;
+    }
+  const float gv[4] = {g.x, g.y, g.z, g.w}, uv[4] = {u.x, u.y, u.z, u.w};
+  uint16_t hi[4], lo[4];
+  float hsum[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float h = gv[e] * __builtin_amdgcn_rcpf(1.f + __expf(-gv[e])) * uv[e];
+    hi[e] = f32_to_bf16_rne(h);
+    lo[e] = f32_to_bf16_rne(h - bf16_to_f32(hi[e]));
+    hsum[e] = bf16_to_f32(hi[e]) + bf16_to_f32(lo[e]);
+  }
+  const int kg = (4 * k4) % C::G;  // element index of hi[0] within its group
+  const float o0 = C::pair_off(kg / 2), o1 = C::pair_off(kg / 2 + 1);
+  const float part = group_lane_sum<BITS>(o0 * (hsum[0] + hsum[1]) + o1 * (hsum[2] + hsum[3]));
+  if (i4 < tot4) {
+    uint2 vh, vl;
+    vh.x = hi[0] | ((uint32_t)hi[1] << 16);
+    vh.y = hi[2] | ((uint32_t)hi[3] << 16);
+    vl.x = lo[0] | ((uint32_t)lo[1] << 16);
+    vl.y = lo[2] | ((uint32_t)lo[3] << 16);
+    *reinterpret_cast<uint2*>(hs + (2 * j) * I + 4 * k4) = vh;
+    *reinterpret_cast<uint2*>(hs + (2 * j + 1) * I + 4 * k4) = vl;
+    if (kg + 4 == C::G) kc[j * (I / C::G) + (4 * k4) / C::G] = part;
+  }
 }
 
 template <int BITS, int GPW>
 __global__ __launch_bounds__(256) void k_down(
-    const moe_expert_ref* __restrict__ table, int E, const int32_t* __restrict__ offsets, int H,
-    int I, int P, int KP, int scale_f16, const float* __restrict__ gu, float* __restrict__ pair_out) {
+    const moe_expert_ref* __restrict__ table, int E, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_pairs, int H, int I, int P, int KP, int scale_f16,
+    const float* __restrict__ gu, float* __restrict__ pair_out) {
   using C = UnitCodec<BITS>;
+  constexpr int NT = 64 * kDNWaves;
   extern __shared__ __align__(16) uint8_t dyn[];
   const int ng = I / C::G;
-  uint16_t* hs = reinterpret_cast<uint16_t*>(dyn);                  // [kHChunk * 2][I]: hi, lo
-  float* cs = reinterpret_cast<float*>(dyn + kHChunk * I * 4);       // [kHChunk * 2][ng]
-  float* part = cs + 2 * kHChunk * ng;                               // [kHChunk * 2][ng][4]
+  uint16_t* hs = reinterpret_cast<uint16_t*>(dyn);             // [kHChunk * 2][I]: hi, lo
+  float* kc = reinterpret_cast<float*>(dyn + kHChunk * I * 4);  // [kHChunk][ng]
   __shared__ float red[kDNWaves][kTokPerPass][64];
 
   const Active act = find_active(offsets, table, E, blockIdx.x);
@@ -357,6 +407,16 @@ __global__ __launch_bounds__(256) void k_down(
   const gbytes_t down = as_global(act.ptr[2]);
   const gu16_t dsc = (gu16_t)(down + gm.scales_off());
   const int row = strip * 64 + lane;
+  const int I4 = I / 4;
+
+  // pair ids of the expert's first 64 positions (lane = position), then the first
+  // staging batch of the first chunk, all ahead of the weights
+  const int pids = sorted_pairs[seg0 + min(lane, n_e - 1)];
+  const int nc0 = min(kHChunk, n_e);
+  HItem it[kSB];
+#pragma unroll
+  for (int r = 0; r < kSB; ++r) h_load(gu, P, I, KP, seg0, nc0 * I4, threadIdx.x + NT * r, it[r]);
+  asm volatile("" ::: "memory");
 
   u32x4 cw[GPW][C::CHUNKS];
   uint32_t sr[GPW];  // the aligned dword holding the scale (any 16-bit handling here would wait)
@@ -366,26 +426,9 @@ __global__ __launch_bounds__(256) void k_down(
     load_unit4<BITS>(down, (int64_t)strip * ng + g, lane, cw[i]);
     sr[i] = load_scale_dword(dsc, (int64_t)row * ng + g);
   }
+  asm volatile("" ::: "memory");
 
-  for (int c0 = 0; c0 < n_e; c0 += kHChunk) {
-    const int nc = min(kHChunk, n_e - c0);
-    lds_barrier();
-    for (int i = threadIdx.x; i < nc * I; i += 64 * kDNWaves) {
-      const int j = i / I, k = i % I;
-      const int64_t pos = seg0 + c0 + j;
-      float gv = 0.f, uv = 0.f;
-      for (int q = 0; q < KP; ++q) {
-        gv += gu[((int64_t)q * P + pos) * I + k];
-        uv += gu[((int64_t)(KP + q) * P + pos) * I + k];
-      }
-      const float h = gv / (1.f + __expf(-gv)) * uv;
-      const uint16_t hi = f32_to_bf16_rne(h);
-      hs[(2 * j) * I + k] = hi;
-      hs[(2 * j + 1) * I + k] = f32_to_bf16_rne(h - bf16_to_f32(hi));
-    }
-    lds_barrier();
-    // rows 2j (hi) and 2j+1 (lo): offset sums of both; the dot uses their sum
-    offset_sums_lds<BITS>(hs, I, 2 * nc, ng, part, cs, 64 * kDNWaves);
+  auto dots = [&](int c0, int nc) {
     for (int jp = 0; jp < nc; jp += kTokPerPass) {
       const bool two = jp + 1 < nc;
       const int j1 = two ? jp + 1 : jp;
@@ -403,8 +446,8 @@ __global__ __launch_bounds__(256) void k_down(
           const uint32_t* hl0 = reinterpret_cast<const uint32_t*>(hs + (jp * 2 + 1) * I + g * C::G);
           const uint32_t* hh1 = reinterpret_cast<const uint32_t*>(hs + (j1 * 2 + 0) * I + g * C::G);
           const uint32_t* hl1 = reinterpret_cast<const uint32_t*>(hs + (j1 * 2 + 1) * I + g * C::G);
-          const float k0 = cs[(2 * jp) * ng + g] + cs[(2 * jp + 1) * ng + g];
-          const float k1 = cs[(2 * j1) * ng + g] + cs[(2 * j1 + 1) * ng + g];
+          const float k0 = kc[jp * ng + g];
+          const float k1 = kc[j1 * ng + g];
           float d0 = 0.f, d1 = 0.f;
           if (two) {
             C::for_each_pair(wd, [&](int Pp, uint32_t pr) {
@@ -429,31 +472,68 @@ __global__ __launch_bounds__(256) void k_down(
         float y = 0.f;
 #pragma unroll
         for (int ww = 0; ww < kDNWaves; ++ww) y += red[ww][j][lane];
-        pair_out[(int64_t)(seg0 + c0 + jp + j) * H + row] = y;
+        const int idx = c0 + jp + j;  // wave-uniform
+        const int p = idx < 64 ? __builtin_amdgcn_readlane(pids, idx) : sorted_pairs[seg0 + idx];
+        pair_out[(int64_t)p * H + row] = y;
       }
       lds_barrier();
     }
+  };
+
+  // chunk 0: the batch already loaded, then the rest
+  {
+    const int tot4 = nc0 * I4;
+#pragma unroll
+    for (int r = 0; r < kSB; ++r) h_store<BITS>(it[r], KP, I, tot4, threadIdx.x + NT * r, hs, kc);
+    for (int b = NT * kSB; b < tot4; b += NT * kSB) {
+#pragma unroll
+      for (int r = 0; r < kSB; ++r) h_load(gu, P, I, KP, seg0, tot4, b + threadIdx.x + NT * r, it[r]);
+#pragma unroll
+      for (int r = 0; r < kSB; ++r) h_store<BITS>(it[r], KP, I, tot4, b + threadIdx.x + NT * r, hs, kc);
+    }
+    lds_barrier();
+    dots(0, nc0);
+  }
+  for (int c0 = kHChunk; c0 < n_e; c0 += kHChunk) {
+    const int nc = min(kHChunk, n_e - c0);
+    const int tot4 = nc * I4;
+    for (int b = 0; b < tot4; b += NT * kSB) {
+#pragma unroll
+      for (int r = 0; r < kSB; ++r)
+        h_load(gu, P, I, KP, seg0 + c0, tot4, b + threadIdx.x + NT * r, it[r]);
+#pragma unroll
+      for (int r = 0; r < kSB; ++r) h_store<BITS>(it[r], KP, I, tot4, b + threadIdx.x + NT * r, hs, kc);
+    }
+    lds_barrier();
+    dots(c0, nc);
   }
 }
 
 // ---------------------------------------------------------------- combine
-// out[t][n] = sum_k w[t][k] * pair_out[pair_pos[t*K+k]][n] (k ascending; pairs
-// left out of the grouping are skipped) + shared[t][n].
+// out[t][n] = sum_k w[t][k] * pair_out[t*K + k][n] (k ascending; pairs whose id is
+// outside [0, E) were left out of the grouping and are skipped) + shared[t][n].
+// All KM rows are requested at once (k >= K repeats row K-1 and is dropped), so
+// the combine costs one memory round trip.
+template <int KM>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ pair_out,
-                                                 const int32_t* __restrict__ pair_pos,
-                                                 const float* __restrict__ w, int K, int H,
+                                                 const int32_t* __restrict__ ids,
+                                                 const float* __restrict__ w, int K, int E, int H,
                                                  const float* __restrict__ shared,
                                                  float* __restrict__ out) {
   const int t = blockIdx.y;
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= H) return;
+  const int n = min((int)(blockIdx.x * 256 + threadIdx.x), H - 1);
+  float y[KM];
+#pragma unroll
+  for (int k = 0; k < KM; ++k) y[k] = pair_out[((int64_t)t * K + min(k, K - 1)) * H + n];
+  const float sh = shared ? shared[(int64_t)t * H + n] : 0.f;
   float acc = 0.f;
-  for (int k = 0; k < K; ++k) {
-    const int pos = pair_pos[t * K + k];
-    if (pos >= 0) acc = fmaf(w[t * K + k], pair_out[(int64_t)pos * H + n], acc);
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    const int id = ids[t * K + min(k, K - 1)];
+    if (k < K && id >= 0 && id < E) acc = fmaf(w[t * K + min(k, K - 1)], y[k], acc);
   }
-  if (shared) acc += shared[(int64_t)t * H + n];
-  out[(int64_t)t * H + n] = acc;
+  if (shared) acc += sh;
+  if (blockIdx.x * 256 + threadIdx.x < H) out[(int64_t)t * H + n] = acc;
 }
 
 // ---------------------------------------------------------------- shared expert
@@ -601,15 +681,14 @@ hipError_t launch_forward_t(const FwdArgs& f, hipStream_t s) {
                c.scale_f16, gu);                                                                \
     break;
   switch (gpw_gu) {
-    MOE_GU(1) MOE_GU(2) MOE_GU(3) MOE_GU(4) MOE_GU(5) MOE_GU(6) MOE_GU(7) MOE_GU(8)
-    MOE_GU(9) MOE_GU(10) MOE_GU(11) MOE_GU(12) MOE_GU(13) MOE_GU(14) MOE_GU(15) MOE_GU(16)
+    MOE_GU(1) MOE_GU(2) MOE_GU(3) MOE_GU(4) MOE_GU(5)
     default: return hipErrorInvalidValue;
   }
 #undef MOE_GU
 #define MOE_DN(N)                                                                               \
   case N:                                                                                       \
     MOE_LAUNCH(KID_DOWN, (k_down<BITS, N>), dim3(maxU, H / 64), dim3(64 * kDNWaves), lds_dn, s, \
-               f.table, E, f.offsets, H, I, T * K, KP, c.scale_f16, gu, pair_out);              \
+               f.table, E, f.offsets, f.sorted_pairs, H, I, T * K, KP, c.scale_f16, gu, pair_out);              \
     break;
   switch (gpw_dn) {
     MOE_DN(1) MOE_DN(2) MOE_DN(3) MOE_DN(4) MOE_DN(5) MOE_DN(6) MOE_DN(7) MOE_DN(8)
@@ -625,8 +704,13 @@ hipError_t launch_forward_t(const FwdArgs& f, hipStream_t s) {
     MOE_LAUNCH(KID_SH_DOWN, k_shared_down, dim3(H / kShRows), dim3(256), 0, s,
                reinterpret_cast<const uint16_t*>(f.sd), sh_h, T, H, Is, sh_out);
   }
-  MOE_LAUNCH(KID_COMBINE, k_combine, dim3((H + 255) / 256, T), dim3(256), 0, s, pair_out,
-               f.pair_pos, f.w, K, H, has_shared ? sh_out : nullptr, f.out);
+  if (K <= 8) {
+    MOE_LAUNCH(KID_COMBINE, k_combine<8>, dim3((H + 255) / 256, T), dim3(256), 0, s, pair_out,
+               f.ids, f.w, K, E, H, has_shared ? sh_out : nullptr, f.out);
+  } else {
+    MOE_LAUNCH(KID_COMBINE, k_combine<16>, dim3((H + 255) / 256, T), dim3(256), 0, s, pair_out,
+               f.ids, f.w, K, E, H, has_shared ? sh_out : nullptr, f.out);
+  }
   return hipGetLastError();
 }
 

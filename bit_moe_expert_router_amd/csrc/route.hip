@@ -13,13 +13,20 @@
 // selection equals the exact-arithmetic one up to the rounding of a 5120-term
 // fp64 sum (relative 1e-15), far below the smallest 8th/9th-logit margins the
 // workloads produce.  Every reduction has a fixed order (no float atomics).
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
 
 // ---------------------------------------------------------------- logits, small T
-// Block = one expert x up to 8 tokens; 256 threads stride over H in float4 steps.
-constexpr int kLogitTok = 8;
+// Block = one expert x up to 4 tokens; 256 threads stride over H in float4 steps,
+// each thread issuing all its loads of a batch (8 float4 of the router row and
+// the matching activations of every token) before using any, so a 5120-wide row
+// costs one memory round trip.  Items past the row end load the last item and
+// use a zero router value.
+constexpr int kLogitTok = 4;
+constexpr int kLogitBatch = 8;
 
 __global__ __launch_bounds__(256) void k_logits_small(const uint16_t* __restrict__ x, int T,
                                                       int H, int E,
@@ -29,20 +36,31 @@ __global__ __launch_bounds__(256) void k_logits_small(const uint16_t* __restrict
   const int e = blockIdx.x;
   const int t0 = blockIdx.y * kLogitTok;
   const int nt = min(kLogitTok, T - t0);
+  const int H4 = H / 4;
   const float4* w4 = reinterpret_cast<const float4*>(wr + (int64_t)e * H);
   double acc[kLogitTok];
 #pragma unroll
   for (int j = 0; j < kLogitTok; ++j) acc[j] = 0.0;
-  for (int i = threadIdx.x; i < H / 4; i += 256) {
-    float4 w = w4[i];
+  for (int b = 0; b < H4; b += 256 * kLogitBatch) {
+    float4 w[kLogitBatch];
+    uint2 xv[kLogitTok][kLogitBatch];
 #pragma unroll
-    for (int j = 0; j < kLogitTok; ++j) {
-      if (j < nt) {
-        const uint2 xv = reinterpret_cast<const uint2*>(x + (int64_t)(t0 + j) * H)[i];
-        acc[j] = fma((double)bf16_to_f32((uint16_t)xv.x), (double)w.x, acc[j]);
-        acc[j] = fma((double)bf16_to_f32((uint16_t)(xv.x >> 16)), (double)w.y, acc[j]);
-        acc[j] = fma((double)bf16_to_f32((uint16_t)xv.y), (double)w.z, acc[j]);
-        acc[j] = fma((double)bf16_to_f32((uint16_t)(xv.y >> 16)), (double)w.w, acc[j]);
+    for (int r = 0; r < kLogitBatch; ++r) {
+      const int i = min(b + (int)threadIdx.x + 256 * r, H4 - 1);
+      w[r] = w4[i];
+#pragma unroll
+      for (int j = 0; j < kLogitTok; ++j)
+        xv[j][r] = reinterpret_cast<const uint2*>(x + (int64_t)(t0 + min(j, nt - 1)) * H)[i];
+    }
+#pragma unroll
+    for (int r = 0; r < kLogitBatch; ++r) {
+      if (b + (int)threadIdx.x + 256 * r >= H4) w[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int j = 0; j < kLogitTok; ++j) {
+        acc[j] = fma((double)bf16_to_f32((uint16_t)xv[j][r].x), (double)w[r].x, acc[j]);
+        acc[j] = fma((double)bf16_to_f32((uint16_t)(xv[j][r].x >> 16)), (double)w[r].y, acc[j]);
+        acc[j] = fma((double)bf16_to_f32((uint16_t)xv[j][r].y), (double)w[r].z, acc[j]);
+        acc[j] = fma((double)bf16_to_f32((uint16_t)(xv[j][r].y >> 16)), (double)w[r].w, acc[j]);
       }
     }
   }
@@ -50,10 +68,12 @@ __global__ __launch_bounds__(256) void k_logits_small(const uint16_t* __restrict
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
   for (int j = 0; j < kLogitTok; ++j) {
-    double v = acc[j];
+    if (j < nt) {
+      double v = acc[j];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    if (lane == 0) red[wv][j] = v;
+      for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+      if (lane == 0) red[wv][j] = v;
+    }
   }
   __syncthreads();
   if (threadIdx.x < nt) {
@@ -109,74 +129,103 @@ __global__ __launch_bounds__(256) void k_logits_tiled(const uint16_t* __restrict
 }
 
 // ---------------------------------------------------------------- top-k + weights
-// Rank counting: expert e is pick number r = #{e' : l[e'] > l[e] or (l[e'] == l[e]
-// and e' < e)}, so the picks come out in output order (descending logit, ties to
-// the lower id) without any data-dependent reduction order.  One block per token:
-// the token's logits are staged in LDS, the E*E comparisons are split over the
-// block's threads and the partial ranks summed with integer LDS atomics (exact).
-// Weights: w_k = exp(l_k - l_0) / sum_{j<K} exp(l_j - l_0) in fp64, the sum taken
-// in k order by one thread.
+// One wave per token.  Each lane keeps the logits of experts lane + 64*i.  Each
+// of the K rounds takes the wave maximum of the remaining logits (DPP row
+// shifts, then the row totals), then the lowest id among the lanes that hold it
+// (same reduction on ids): the picks come out in output order (descending logit,
+// ties to the lower id).  Lane k keeps pick k.  Weights: lane k < K computes
+// exp(l_k - l_0) in fp64; every lane adds the K terms in k order.
 constexpr int kMaxE = 1024;
-constexpr int kMaxK = 16;
-constexpr int kTopkThreads = 1024;
+constexpr int kMaxPerLane = kMaxE / 64;
 
-__device__ void block_topk(const double* __restrict__ l_global, int E, int K, double* ls, int* rank,
-                           double* top_l, int* top_id, int32_t* __restrict__ ids_out,
-                           float* __restrict__ w_out, int32_t* ids_lds) {
-  const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += kTopkThreads) {
-    ls[e] = l_global[e];
-    rank[e] = 0;
-  }
-  __syncthreads();
-  // thread -> (expert slot, quarter of the comparison range)
-  const int q = tid / 256, slot = tid % 256;
-  const int c0 = q * E / 4, c1 = (q + 1) * E / 4;
-  for (int e = slot; e < E; e += 256) {
-    const double v = ls[e];
-    int r = 0;
-    for (int c = c0; c < c1; ++c) {
-      const double o = ls[c];
-      r += (o > v) | ((o == v) & (c < e));
-    }
-    atomicAdd(&rank[e], r);
-  }
-  __syncthreads();
-  for (int e = tid; e < E; e += kTopkThreads) {
-    const int r = rank[e];
-    if (r < K) {
-      top_l[r] = ls[e];
-      top_id[r] = e;
-    }
-  }
-  __syncthreads();
-  // thread k < K: term_k = exp(l_k - l_0); thread 0 sums the K terms in k order
-  if (tid < K) top_l[kMaxK + tid] = exp(top_l[tid] - top_l[0]);
-  __syncthreads();
-  if (tid == 0) {
-    double den = 0.0;
-    for (int k = 0; k < K; ++k) den += top_l[kMaxK + k];
-    top_l[2 * kMaxK] = den;
-  }
-  __syncthreads();
-  if (tid < K) {
-    ids_out[tid] = top_id[tid];
-    w_out[tid] = (float)(top_l[kMaxK + tid] / top_l[2 * kMaxK]);
-    if (ids_lds) ids_lds[tid] = top_id[tid];
-  }
-  __syncthreads();
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v, int fill) {
+  return __builtin_amdgcn_update_dpp(fill, v, CTRL, 0xF, 0xF, false);
+}
+// 64-bit max over the wave (every lane gets the result)
+__device__ __forceinline__ double wave_max_f64(double v) {
+  auto step = [&](auto ctrl) {
+    constexpr int C = decltype(ctrl)::value;
+    const int lo = __double2loint(v), hi = __double2hiint(v);
+    const double o = __hiloint2double(dpp_i<C>(hi, 0xFFF00000), dpp_i<C>(lo, 0));  // fill = -inf
+    v = fmax(v, o);
+  };
+  step(std::integral_constant<int, 0x111>{});
+  step(std::integral_constant<int, 0x112>{});
+  step(std::integral_constant<int, 0x114>{});
+  step(std::integral_constant<int, 0x118>{});
+  step(std::integral_constant<int, 0x142>{});
+  step(std::integral_constant<int, 0x143>{});
+  const int lo = __builtin_amdgcn_readlane(__double2loint(v), 63);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(v), 63);
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ int wave_min_i32(int v) {
+  v = min(v, dpp_i<0x111>(v, 0x7FFFFFFF));
+  v = min(v, dpp_i<0x112>(v, 0x7FFFFFFF));
+  v = min(v, dpp_i<0x114>(v, 0x7FFFFFFF));
+  v = min(v, dpp_i<0x118>(v, 0x7FFFFFFF));
+  v = min(v, dpp_i<0x142>(v, 0x7FFFFFFF));
+  v = min(v, dpp_i<0x143>(v, 0x7FFFFFFF));
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
-__global__ __launch_bounds__(kTopkThreads) void k_topk(const double* __restrict__ logits, int T,
-                                                       int E, int K, int32_t* __restrict__ ids,
-                                                       float* __restrict__ wout) {
-  __shared__ double ls[kMaxE];
-  __shared__ int rank[kMaxE];
-  __shared__ double top_l[2 * kMaxK + 1];
-  __shared__ int top_id[kMaxK];
-  const int t = blockIdx.x;
-  block_topk(logits + (int64_t)t * E, E, K, ls, rank, top_l, top_id, ids + t * K, wout + t * K,
-             nullptr);
+// this lane's pick (lane < K) and its weight; -1 for other lanes
+__device__ __forceinline__ int wave_topk(const double* __restrict__ l, int E, int K, float* wk) {
+  const int lane = threadIdx.x & 63;
+  const int per = (E + 63) / 64;
+  double v[kMaxPerLane];
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = (i < per && e < E) ? l[e] : -INFINITY;
+  }
+  double my_l = -INFINITY;
+  int my_id = -1;
+  for (int k = 0; k < K; ++k) {
+    // local best: highest value, lowest id among equals (ids grow with i)
+    double bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) {
+      const int e = lane + 64 * i;
+      if (i < per && e < E && v[i] > bv) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+    const double m = wave_max_f64(bv);
+    const int id = wave_min_i32(bv == m ? bi : 0x7FFFFFFF);
+    if ((id & 63) == lane) {
+#pragma unroll
+      for (int i = 0; i < kMaxPerLane; ++i)
+        if (i == (id >> 6)) v[i] = -INFINITY;  // taken
+    }
+    if (lane == k) {
+      my_l = m;
+      my_id = id;
+    }
+  }
+  const double l0 = __shfl(my_l, 0);
+  const double term = lane < K ? exp(my_l - l0) : 0.0;
+  double den = 0.0;
+  for (int k = 0; k < K; ++k) den += __shfl(term, k);
+  *wk = (float)(term / den);
+  return lane < K ? my_id : -1;
+}
+
+__global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits, int T, int E,
+                                              int K, int32_t* __restrict__ ids,
+                                              float* __restrict__ wout) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float wk;
+  const int id = wave_topk(logits + (int64_t)t * E, E, K, &wk);
+  if (lane < K) {
+    ids[t * K + lane] = id;
+    wout[t * K + lane] = wk;
+  }
 }
 
 // ---------------------------------------------------------------- grouping
@@ -258,28 +307,32 @@ __global__ __launch_bounds__(64) void k_permute(const int32_t* __restrict__ ids,
                                                 int32_t* __restrict__ offsets,
                                                 int32_t* __restrict__ sorted_pairs,
                                                 int32_t* __restrict__ pair_pos) {
-  __shared__ int cnt[1025];
-  __shared__ int run[1024];
+  __shared__ int cnt[kMaxE + 1];
+  __shared__ int run[kMaxE];
   wave_group(ids, P, E, cnt, run, offsets, sorted_pairs, pair_pos);
 }
 
 // ---------------------------------------------------------------- top-k + grouping, small T
-// Decode batches (T * K <= 64): one block picks the top-k of every token (as
-// above) and its first wave groups the T*K pairs; one launch instead of two.
-__global__ __launch_bounds__(kTopkThreads) void k_topk_group_small(
+// Decode batches (T <= 16, T * K <= 64): wave t picks the top-k of token t, then
+// the first wave groups the T*K pairs; one launch instead of two.
+__global__ __launch_bounds__(1024) void k_topk_group_small(
     const double* __restrict__ logits, int T, int E, int K, int32_t* __restrict__ ids,
     float* __restrict__ wout, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
     int32_t* __restrict__ pair_pos) {
-  __shared__ double ls[kMaxE];
-  __shared__ int rank[kMaxE];
-  __shared__ double top_l[2 * kMaxK + 1];
-  __shared__ int top_id[kMaxK];
   __shared__ int32_t s_ids[64];
   __shared__ int cnt[kMaxE + 1];
   __shared__ int run[kMaxE];
-  for (int t = 0; t < T; ++t)
-    block_topk(logits + (int64_t)t * E, E, K, ls, rank, top_l, top_id, ids + t * K, wout + t * K,
-               s_ids + t * K);
+  const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
+  if (t < T) {
+    float wk;
+    const int id = wave_topk(logits + (int64_t)t * E, E, K, &wk);
+    if (lane < K) {
+      ids[t * K + lane] = id;
+      wout[t * K + lane] = wk;
+      s_ids[t * K + lane] = id;
+    }
+  }
+  __syncthreads();
   if (threadIdx.x < 64) wave_group(s_ids, T * K, E, cnt, run, offsets, sorted_pairs, pair_pos);
 }
 
@@ -290,19 +343,19 @@ hipError_t launch_route(const moe_cfg& c, const uint16_t* x, int T, const float*
                         int32_t* counter, hipStream_t s) {
   const int H = c.hidden, E = c.n_experts, K = c.top_k;
   (void)counter;
-  if (T <= 64) {
+  if (T <= 32) {
     MOE_LAUNCH(KID_LOGITS, k_logits_small, dim3(E, (T + kLogitTok - 1) / kLogitTok), dim3(256), 0, s,
                x, T, H, E, wr, bias, logits);
   } else {
     MOE_LAUNCH(KID_LOGITS, k_logits_tiled, dim3((E + kLE - 1) / kLE, (T + kLT - 1) / kLT), dim3(256),
                0, s, x, T, H, E, wr, bias, logits);
   }
-  if (T * K <= 64) {
-    MOE_LAUNCH(KID_TOPK, k_topk_group_small, dim3(1), dim3(kTopkThreads), 0, s, logits, T, E, K,
+  if (T <= 16 && T * K <= 64) {
+    MOE_LAUNCH(KID_TOPK, k_topk_group_small, dim3(1), dim3(64 * T), 0, s, logits, T, E, K,
                ids, w, offsets, sorted_pairs, pair_pos);
     return hipGetLastError();
   }
-  MOE_LAUNCH(KID_TOPK, k_topk, dim3(T), dim3(kTopkThreads), 0, s, logits, T, E, K, ids, w);
+  MOE_LAUNCH(KID_TOPK, k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, K, ids, w);
   MOE_LAUNCH(KID_PERMUTE, k_permute, dim3(1), dim3(64), 0, s, ids, T * K, E, offsets, sorted_pairs,
              pair_pos);
   return hipGetLastError();

@@ -75,7 +75,7 @@ class MoELayer:
     def forward(self, layer, x_bf16, r: RoutingBuffers, out, pair_out=None, stream=None):
         T = x_bf16.shape[0]
         moe_forward(self.ctx, layer, x_bf16, T, r.topk_ids, r.topk_w, r.expert_offsets,
-                    r.sorted_pairs, r.pair_pos, out, pair_out, self.ws, stream)
+                    r.sorted_pairs, out, pair_out, self.ws, stream)
         return out
 
     def rmsnorm_bf16(self, resid, add, y_bf16, eps=1e-6, stream=None):

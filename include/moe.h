@@ -140,23 +140,24 @@ moe_status moe_route(moe_ctx* ctx, const void* x_bf16, int32_t T, const float* w
                      int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pair_pos,
                      void* ws, size_t ws_bytes, moe_stream_t stream);
 
-/* Expert FFNs and combine for one layer, given routing (from moe_route or from
- * the caller, in the same layout).
+/* Expert FFNs and combine for one layer, given routing (topk_ids, topk_w,
+ * expert_offsets, sorted_pairs from moe_route, or from the caller in the same
+ * layout; pair_pos is not needed here).
  *   out       [T][H] fp32: out[t] = sum_{k=0..K-1} topk_w[t][k] * y(t,k) (k
  *             ascending, no atomics, bit-reproducible) + shared(x_t) if set
- *   pair_out  [T*K][H] fp32 or NULL: unweighted expert output of the pair at each
- *             sorted position (row i belongs to pair sorted_pairs[i])
+ *   pair_out  [T*K][H] fp32 or NULL: row t*K + k is the unweighted expert output
+ *             y(t,k); rows of pairs left out of the grouping are not written
  *   y(t,k) = down . (silu(gate . x_t) * (up . x_t)) of expert topk_ids[t][k],
  *   accumulated in fp32 from exact integer codes and bf16 activations with the
  *   group scale applied per group.
- * Caller-supplied routing must be consistent (offsets from the same ids); a pair
- * whose id is outside [0, E) must be left out of the grouping (pair_pos = -1) and
- * then contributes nothing.  Returns MOE_E_STATE if the layer's table was never set. */
+ * Caller-supplied routing must be consistent (offsets and sorted_pairs from the
+ * same ids); a pair whose id is outside [0, E) must be left out of the grouping
+ * and then contributes nothing.  Returns MOE_E_STATE if the layer's table was
+ * never set. */
 moe_status moe_forward(moe_ctx* ctx, int32_t layer, const void* x_bf16, int32_t T,
                        const int32_t* topk_ids, const float* topk_w,
-                       const int32_t* expert_offsets, const int32_t* sorted_pairs,
-                       const int32_t* pair_pos, float* out, float* pair_out, void* ws,
-                       size_t ws_bytes, moe_stream_t stream);
+                       const int32_t* expert_offsets, const int32_t* sorted_pairs, float* out,
+                       float* pair_out, void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* Stack glue between layers: y_bf16[t] = bf16(x[t] / sqrt(mean(x[t]^2) + eps))
  * (unit gain, round to nearest even) for fp32 x [T][H]; and, if resid is not
