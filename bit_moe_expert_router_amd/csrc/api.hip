@@ -103,7 +103,12 @@ moe_status moe_destroy(moe_ctx* ctx) {
 
 size_t moe_workspace_bytes(const moe_ctx* ctx, int32_t n_tokens) {
   if (!ctx || n_tokens < 0 || n_tokens > ctx->cfg.max_tokens) return 0;
-  return (size_t)moe::ws_layout(ctx->cfg, n_tokens).total;
+  // enough for every T <= n_tokens: the decode layout grows with T up to the mode
+  // switch, the prefill layout from there on
+  const int64_t dec = moe::ws_layout(ctx->cfg, n_tokens < moe::kDecodeMaxTokens ? n_tokens
+                                                                                : moe::kDecodeMaxTokens).total;
+  const int64_t all = moe::ws_layout(ctx->cfg, n_tokens).total;
+  return (size_t)(dec > all ? dec : all);
 }
 
 moe_status moe_workspace_init(const moe_ctx* ctx, void* ws, size_t ws_bytes, moe_stream_t stream) {

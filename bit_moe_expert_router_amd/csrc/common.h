@@ -172,11 +172,29 @@ struct UnitCodec<4> {
 // counters reserved for cross-block signalling (kept zero between calls)
 constexpr int kCounters = 1024;
 constexpr int kMaxKParts = 4;  // gate/up reduction-dimension split (H/G <= 80)
+
+// Batches up to this many tokens run the GEMV (decode) kernels; larger ones the
+// matrix-core (prefill) kernels when the shape allows them.
+constexpr int kDecodeMaxTokens = 64;
+constexpr int kPrefillTileRows = 128;  // sorted pair positions per prefill tile
+__host__ __device__ inline bool prefill_eligible(const moe_cfg& c, int T) {
+  return T > kDecodeMaxTokens && c.hidden % 128 == 0 && c.inter % 128 == 0;
+}
+// upper bound of the prefill tile count: ceil(n_e / 128) summed over the experts
+__host__ __device__ inline int64_t prefill_max_tiles(int64_t P, int64_t E) {
+  return (P + kPrefillTileRows - 1) / kPrefillTileRows + (E < P ? E : P);
+}
+
 // Layout of the caller's workspace for T tokens (byte offsets, 256-aligned).
+// Regions a mode does not use have size 0.
 struct WsLayout {
   int64_t counters;   // int32[kCounters]: zero between calls
   int64_t logits;     // double[T][E]
-  int64_t gu;         // float[2*KP][P][I]: partial gate and up products, rows by sorted position
+  int64_t gu;         // decode: float[2*KP][P][I]: partial gate and up products, rows by sorted position
+  int64_t x16;        // prefill: fp16[T][H] activations scaled by 2^-xshift[t]
+  int64_t xshift;     // prefill: int32[T]
+  int64_t h16;        // prefill: fp16[P][I] h rows by sorted position
+  int64_t tiles;      // prefill: int32[1 + 2*max_tiles] tile plan
   int64_t pair_out;   // float[P][H] (used when the caller passes no pair_out)
   int64_t sh_h;       // float[T][Is]: shared expert h
   int64_t sh_out;     // float[T][H]: shared expert output
@@ -194,7 +212,12 @@ __host__ inline WsLayout ws_layout(const moe_cfg& c, int T) {
   };
   L.counters = take(kCounters * 4);
   L.logits = take((int64_t)T * c.n_experts * 8);
-  L.gu = take(2 * kMaxKParts * P * c.inter * 4);
+  const bool pf = prefill_eligible(c, T);
+  L.gu = take(pf ? 0 : 2 * kMaxKParts * P * c.inter * 4);
+  L.x16 = take(pf ? (int64_t)T * c.hidden * 2 : 0);
+  L.xshift = take(pf ? (int64_t)T * 4 : 0);
+  L.h16 = take(pf ? P * c.inter * 2 : 0);
+  L.tiles = take(pf ? (1 + 2 * prefill_max_tiles(P, c.n_experts)) * 4 : 0);
   L.pair_out = take(P * c.hidden * 4);
   L.sh_h = take((int64_t)T * c.shared_inter * 4);
   L.sh_out = take((int64_t)T * c.hidden * 4);
@@ -205,7 +228,7 @@ __host__ inline WsLayout ws_layout(const moe_cfg& c, int T) {
 // ---------------------------------------------------------------- profiling
 enum KernelId {
   KID_LOGITS = 0, KID_TOPK, KID_PERMUTE, KID_PLAN, KID_GATEUP, KID_DOWN, KID_SH_GATEUP,
-  KID_SH_DOWN, KID_COMBINE, KID_RMSNORM, KID_ZERO, KID_COUNT
+  KID_SH_DOWN, KID_COMBINE, KID_RMSNORM, KID_ZERO, KID_XPREP, KID_COUNT
 };
 void prof_begin(int kid, hipStream_t s);
 void prof_end(int kid, hipStream_t s);
@@ -236,6 +259,7 @@ struct FwdArgs {
   uint8_t* ws;
 };
 
+hipError_t launch_prefill(const FwdArgs& f, const WsLayout& L, float* pair_out, hipStream_t s);
 hipError_t launch_route(const moe_cfg& c, const uint16_t* x, int T, const float* wr,
                         const float* bias, int32_t* ids, float* w, int32_t* offsets,
                         int32_t* sorted_pairs, int32_t* pair_pos, double* logits,

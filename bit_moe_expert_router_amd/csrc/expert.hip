@@ -667,34 +667,39 @@ hipError_t launch_forward_t(const FwdArgs& f, hipStream_t s) {
   float* pair_out = f.pair_out ? f.pair_out : reinterpret_cast<float*>(f.ws + L.pair_out);
   float* sh_h = reinterpret_cast<float*>(f.ws + L.sh_h);
   float* sh_out = reinterpret_cast<float*>(f.ws + L.sh_out);
-  const int maxU = min(E, T * K);
-  // gate/up: reduction dim split over KP blocks of at most 4 waves x 5 groups
-  const int ngh = H / C::G;
-  const int KP = (ngh + 5 * kGUWaves - 1) / (5 * kGUWaves);  // <= kMaxKParts for H/G <= 64
-  const int gpw_gu = ((ngh + KP - 1) / KP + kGUWaves - 1) / kGUWaves;
-  const int gpw_dn = (I / C::G + kDNWaves - 1) / kDNWaves;
-  const int lds_dn = down_lds_bytes(I, C::G);
-#define MOE_GU(N)                                                                               \
-  case N:                                                                                       \
-    MOE_LAUNCH(KID_GATEUP, (k_gateup<BITS, N>), dim3(maxU, I / 64, 2 * KP), dim3(64 * kGUWaves),\
-               0, s, f.table, E, f.offsets, f.sorted_pairs, K, f.x, f.x, H, I, T * K, KP,       \
-               c.scale_f16, gu);                                                                \
-    break;
-  switch (gpw_gu) {
-    MOE_GU(1) MOE_GU(2) MOE_GU(3) MOE_GU(4) MOE_GU(5)
-    default: return hipErrorInvalidValue;
+  if (prefill_eligible(c, T)) {
+    const hipError_t err = launch_prefill(f, L, pair_out, s);
+    if (err != hipSuccess) return err;
+  } else {
+    const int maxU = min(E, T * K);
+    // gate/up: reduction dim split over KP blocks of at most 4 waves x 5 groups
+    const int ngh = H / C::G;
+    const int KP = (ngh + 5 * kGUWaves - 1) / (5 * kGUWaves);  // <= kMaxKParts for H/G <= 64
+    const int gpw_gu = ((ngh + KP - 1) / KP + kGUWaves - 1) / kGUWaves;
+    const int gpw_dn = (I / C::G + kDNWaves - 1) / kDNWaves;
+    const int lds_dn = down_lds_bytes(I, C::G);
+  #define MOE_GU(N)                                                                               \
+    case N:                                                                                       \
+      MOE_LAUNCH(KID_GATEUP, (k_gateup<BITS, N>), dim3(maxU, I / 64, 2 * KP), dim3(64 * kGUWaves),\
+                 0, s, f.table, E, f.offsets, f.sorted_pairs, K, f.x, f.x, H, I, T * K, KP,       \
+                 c.scale_f16, gu);                                                                \
+      break;
+    switch (gpw_gu) {
+      MOE_GU(1) MOE_GU(2) MOE_GU(3) MOE_GU(4) MOE_GU(5)
+      default: return hipErrorInvalidValue;
+    }
+  #undef MOE_GU
+  #define MOE_DN(N)                                                                               \
+    case N:                                                                                       \
+      MOE_LAUNCH(KID_DOWN, (k_down<BITS, N>), dim3(maxU, H / 64), dim3(64 * kDNWaves), lds_dn, s, \
+                 f.table, E, f.offsets, f.sorted_pairs, H, I, T * K, KP, c.scale_f16, gu, pair_out);              \
+      break;
+    switch (gpw_dn) {
+      MOE_DN(1) MOE_DN(2) MOE_DN(3) MOE_DN(4) MOE_DN(5) MOE_DN(6) MOE_DN(7) MOE_DN(8)
+      default: return hipErrorInvalidValue;
+    }
+  #undef MOE_DN
   }
-#undef MOE_GU
-#define MOE_DN(N)                                                                               \
-  case N:                                                                                       \
-    MOE_LAUNCH(KID_DOWN, (k_down<BITS, N>), dim3(maxU, H / 64), dim3(64 * kDNWaves), lds_dn, s, \
-               f.table, E, f.offsets, f.sorted_pairs, H, I, T * K, KP, c.scale_f16, gu, pair_out);              \
-    break;
-  switch (gpw_dn) {
-    MOE_DN(1) MOE_DN(2) MOE_DN(3) MOE_DN(4) MOE_DN(5) MOE_DN(6) MOE_DN(7) MOE_DN(8)
-    default: return hipErrorInvalidValue;
-  }
-#undef MOE_DN
   const bool has_shared = c.shared_inter > 0 && f.sg && f.su && f.sd;
   if (has_shared) {
     const int Is = c.shared_inter;

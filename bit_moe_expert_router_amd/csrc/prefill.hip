@@ -1,0 +1,456 @@
+// prefill.hip -- the routed experts of a prefill chunk as grouped matrix products
+// on the matrix cores (v_mfma_f32_16x16x32_f16).
+//
+// A prefill chunk routes thousands of tokens (8,192 per chunk on the pages' model:
+// page "0xSero/glm53-flash-offload", paragraph on prefill staging of chunks of at
+// least 8,192 picks per layer), so each picked expert sees many rows and its
+// gate/up/down products are dense contractions: [n_e x H] . [H x I] and
+// [n_e x I] . [I x H] per expert.
+//
+// Operands.  A packed weight W[n][k] = q[n][k] * s[n][k/G] with q = c - 2^(bits-1)
+// a small integer and s a bf16 scale: the product q*s has at most 3 + 8
+// significant bits, so it is exact in fp16 (fp16 scales: rounded to nearest).
+// The weights are expanded in LDS to fp16 W16 = q*s, one code pair per 32-bit
+// word: shift and mask the two codes into the mantissas of 1024.0 (1024 + c),
+// then one packed fp16 add of -(1024 + 2^(bits-1)) and one packed multiply by s;
+// and the activations are fp16 copies of the bf16 tokens scaled
+// by a per-token power of two (exact for every normal fp16 value, so the fp16
+// range never clips a token).  Accumulation is fp32 throughout the reduction.
+//
+// Gate/up: tile = 128 sorted pair positions of one expert x 64 rows of both the
+// gate and the up matrix, so the epilogue forms h = silu(g) * u directly and
+// stores it once (fp16).  Down: tile = 128 positions x 128 rows of H; y goes to
+// pair_out row p = t*K + k.  Both walk the reduction in steps of 128 elements
+// (one 3-bit group or four 4-bit groups): global loads of step s+1 are in flight
+// while the matrix cores work on step s out of LDS.
+#include "common.h"
+
+namespace moe {
+
+constexpr int kPM = 128;           // sorted pair positions per tile
+constexpr int kPK = 128;           // reduction elements per step
+constexpr int kLdsRow = kPK + 8;   // fp16 per LDS row (16-byte pad: conflict-free 16-byte reads)
+constexpr int kGuN = 64;           // gate/up rows per block, of each matrix
+constexpr int kDnN = 128;          // down rows per block
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4p __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- activations to fp16
+// x16[t] = fp16(x[t] * 2^-s_t) with s_t the smallest shift >= 0 that keeps the
+// token's largest magnitude below 2^15; xshift[t] = s_t.
+__global__ __launch_bounds__(256) void k_xprep(const uint16_t* __restrict__ x, int H,
+                                               uint16_t* __restrict__ x16,
+                                               int32_t* __restrict__ xshift) {
+  const int t = blockIdx.x;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (int64_t)t * H);
+  const int n8 = H / 8;
+  int m = 0;
+  for (int i = threadIdx.x; i < n8; i += 256) {
+    const uint4 v = xr[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = max(m, (int)max((w[j] >> 7) & 0xFF, (w[j] >> 23) & 0xFF));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o));
+  __shared__ int red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = max(max(red[0], red[1]), max(red[2], red[3]));
+  // biased exponent m: magnitude < 2^(m - 126); keep it below 2^15
+  const int s = max(0, m - 126 - 15);
+  if (threadIdx.x == 0) xshift[t] = s;
+  uint4* yr = reinterpret_cast<uint4*>(x16 + (int64_t)t * H);
+  for (int i = threadIdx.x; i < n8; i += 256) {
+    const uint4 v = xr[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const _Float16 lo = (_Float16)ldexpf(bf16_to_f32((uint16_t)w[j]), -s);
+      const _Float16 hi = (_Float16)ldexpf(bf16_to_f32((uint16_t)(w[j] >> 16)), -s);
+      o[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    yr[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// ---------------------------------------------------------------- tile plan
+// tiles[0] = number of tiles; tiles[1 + 2j] = expert, tiles[2 + 2j] = first sorted
+// position of tile j.  Experts in ascending order, ceil(n_e / 128) tiles each.
+__global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ offsets, int E,
+                                               int32_t* __restrict__ tiles) {
+  __shared__ int wsum[16];
+  const int e = threadIdx.x, lane = e & 63, wv = e >> 6;
+  const int lo = e < E ? offsets[e] : 0;
+  const int n = e < E ? offsets[e + 1] - lo : 0;
+  const int nt = (n + kPM - 1) / kPM;
+  int inc = nt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) wsum[wv] = inc;
+  __syncthreads();
+  int base = inc - nt, total = 0;
+  for (int w = 0; w < 16; ++w) {
+    if (w < wv) base += wsum[w];
+    total += wsum[w];
+  }
+  for (int j = 0; j < nt; ++j) {
+    tiles[1 + 2 * (base + j)] = e;
+    tiles[2 + 2 * (base + j)] = lo + j * kPM;
+  }
+  if (e == 0) tiles[0] = total;
+}
+
+// ---------------------------------------------------------------- weight expansion
+// Expand the code pairs a thread owns in one 128-element step into fp16 q*s pairs
+// in its LDS row `wr` (fp16 elements, k = 0 at wr[0]).
+//
+// 3-bit, G = 128: the thread owns half hw of the unit: words 6hw .. 6hw+5, i.e.
+// pairs 30hw .. 30hw+29 (word j/5, field offset {1,4,7,10,13}[j%5] in both halves)
+// and the two spare pairs 60 + 2hw + mm (bit b of the code at bit 0 / 16 of word
+// 3(2hw + mm) + b).
+// 4-bit, G = 32: the thread owns units 2hw, 2hw+1 of the step's four groups
+// (4 words, pair P at word P/4, field offset 4(P%4)).
+__device__ __forceinline__ uint32_t q_times_s(uint32_t field_pair, half2v bias, half2v s2) {
+  // field_pair: a code at bits 0..3 of each 16-bit half
+  const half2v v = __builtin_bit_cast(half2v, field_pair | 0x64006400u);  // 1024 + c
+  return __builtin_bit_cast(uint32_t, (v + bias) * s2);                    // (c - z) * s
+}
+
+template <int BITS>
+struct StepLoad;
+
+template <>
+struct StepLoad<3> {
+  uint32_t w[6];
+  uint32_t sraw;
+  __device__ __forceinline__ void load(gbytes_t mat, int64_t tile, int lane, int hw, gu16_t sc,
+                                       int64_t sidx) {
+    typedef const u32x4p __attribute__((address_space(1)))* g4;
+    typedef const u32x2 __attribute__((address_space(1)))* g2;
+    const gbytes_t base = mat + tile * 3 * 1024 + 16 * lane;
+    if (hw == 0) {
+      const u32x4p a = *(g4)(base);
+      const u32x2 b = *(g2)(base + 1024);
+      w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y;
+    } else {
+      const u32x2 a = *(g2)(base + 1024 + 8);
+      const u32x4p b = *(g4)(base + 2048);
+      w[0] = a.x; w[1] = a.y; w[2] = b.x; w[3] = b.y; w[4] = b.z; w[5] = b.w;
+    }
+    typedef const uint16_t __attribute__((address_space(1)))* g16;
+    sraw = *(g16)(sc + sidx);
+  }
+  __device__ __forceinline__ void expand(int hw, int scale_f16, _Float16* wr) const {
+    const _Float16 s = scale_f16 ? __builtin_bit_cast(_Float16, (uint16_t)sraw)
+                                 : (_Float16)bf16_to_f32((uint16_t)sraw);
+    const half2v s2 = {s, s};
+    const half2v z = {(_Float16)-1028.f, (_Float16)-1028.f};
+    constexpr int off[5] = {1, 4, 7, 10, 13};
+    uint32_t* out = reinterpret_cast<uint32_t*>(wr) + 30 * hw;  // pair P at out[P - 30hw]
+#pragma unroll
+    for (int j = 0; j < 30; j += 2) {
+      const uint32_t p0 = q_times_s((w[j / 5] >> off[j % 5]) & 0x00070007u, z, s2);
+      const uint32_t p1 = q_times_s((w[(j + 1) / 5] >> off[(j + 1) % 5]) & 0x00070007u, z, s2);
+      *reinterpret_cast<u32x2*>(out + j) = u32x2{p0, p1};
+    }
+    uint32_t sp[2];
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      const uint32_t c = (w[3 * mm] & 0x00010001u) | ((w[3 * mm + 1] & 0x00010001u) << 1) |
+                         ((w[3 * mm + 2] & 0x00010001u) << 2);
+      sp[mm] = q_times_s(c, z, s2);
+    }
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint32_t*>(wr) + 60 + 2 * hw) = u32x2{sp[0], sp[1]};
+  }
+};
+
+template <>
+struct StepLoad<4> {
+  uint32_t w[8];
+  uint32_t sraw;  // scales of the two groups (the dword holding both)
+  __device__ __forceinline__ void load(gbytes_t mat, int64_t tile, int lane, int hw, gu16_t sc,
+                                       int64_t sidx) {
+    typedef const u32x4p __attribute__((address_space(1)))* g4;
+    // tile = index of the step's first group's tile; units 2hw, 2hw+1 follow it
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const u32x4p a = *(g4)(mat + (tile + 2 * hw + u) * 1024 + 16 * lane);
+      w[4 * u] = a.x; w[4 * u + 1] = a.y; w[4 * u + 2] = a.z; w[4 * u + 3] = a.w;
+    }
+    typedef const uint32_t __attribute__((address_space(1)))* g32;
+    sraw = *(g32)(sc + sidx);  // sidx is even: both scales in one dword
+  }
+  __device__ __forceinline__ void expand(int hw, int scale_f16, _Float16* wr) const {
+    const half2v z = {(_Float16)-1032.f, (_Float16)-1032.f};
+    uint32_t* out = reinterpret_cast<uint32_t*>(wr) + 32 * hw;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint16_t sb = (uint16_t)(sraw >> (16 * u));
+      const _Float16 s = scale_f16 ? __builtin_bit_cast(_Float16, sb) : (_Float16)bf16_to_f32(sb);
+      const half2v s2 = {s, s};
+#pragma unroll
+      for (int P = 0; P < 16; P += 2) {
+        const uint32_t p0 = q_times_s((w[4 * u + P / 4] >> (4 * (P % 4))) & 0x000F000Fu, z, s2);
+        const uint32_t p1 =
+            q_times_s((w[4 * u + (P + 1) / 4] >> (4 * ((P + 1) % 4))) & 0x000F000Fu, z, s2);
+        *reinterpret_cast<u32x2*>(out + 16 * u + P) = u32x2{p0, p1};
+      }
+    }
+  }
+};
+
+// Work item of block b when the grid (a multiple of 8 blocks) is split into
+// eight contiguous ranges, one per XCD (blocks are dealt to the XCDs in turn):
+// neighbouring items, which share activations and weights, share an L2.
+__device__ __forceinline__ int xcd_item(int b, int nb) { return (b % 8) * (nb / 8) + b / 8; }
+
+// 16-byte global loads of one step of activation rows: thread (r, hx) holds
+// elements [64hx, 64hx + 64) of the step for row r.
+struct RowLoad {
+  u32x4p v[8];
+  __device__ __forceinline__ void load(const uint16_t* row_k0) {
+    const u32x4p* p = reinterpret_cast<const u32x4p*>(row_k0);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = p[c];
+  }
+  __device__ __forceinline__ void store(_Float16* lds_row) const {
+    u32x4p* p = reinterpret_cast<u32x4p*>(lds_row);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) p[c] = v[c];
+  }
+};
+
+__device__ __forceinline__ half8 lds_frag(const _Float16* base) {
+  return *reinterpret_cast<const half8*>(base);
+}
+
+// ---------------------------------------------------------------- gate / up
+// Block: tile (expert e, positions m0 .. m0+127) x rows [64 nt, 64 nt + 64) of the
+// gate and the up matrix.  Waves 2 x 2: wave (wm, wn) owns positions
+// [64wm, 64wm+64) and rows [32wn, 32wn+32) of both matrices (16 accumulator tiles
+// of 16 x 16).  h16[pos][row] = fp16(silu(g) * u), g and u rescaled by 2^s_t.
+template <int BITS>
+__global__ __launch_bounds__(256, 2) void k_gateup_mfma(
+    const moe_expert_ref* __restrict__ table, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ sorted_pairs, int K,
+    const uint16_t* __restrict__ x16, const int32_t* __restrict__ xshift, int H, int I,
+    int scale_f16, uint16_t* __restrict__ h16) {
+  using C = UnitCodec<BITS>;
+  __shared__ __align__(16) _Float16 xs[kPM * kLdsRow];
+  __shared__ __align__(16) _Float16 wsm[2 * kGuN * kLdsRow];
+  __shared__ int s_shift[kPM];
+  const int nI = I / kGuN;
+  const int item = xcd_item(blockIdx.x, gridDim.x);
+  const int tile = item / nI, nt = item % nI;
+  if (tile >= tiles[0]) return;
+  const int e = tiles[1 + 2 * tile], m0 = tiles[2 + 2 * tile];
+  const int rows = min(kPM, offsets[e + 1] - m0);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+
+  // activation rows: thread (r, hx)
+  const int r = tid >> 1, hx = tid & 1;
+  const int tok = sorted_pairs[m0 + min(r, rows - 1)] / K;
+  const uint16_t* xrow = x16 + (int64_t)tok * H + 64 * hx;
+  if (hx == 0) s_shift[r] = xshift[tok];
+  // weights: thread (m, hw, row)
+  const int m = tid >> 7, hw = (tid >> 6) & 1, wrow = lane;
+  const moe_expert_ref ref = table[e];
+  const gbytes_t mat = as_global(m ? ref.up : ref.gate);
+  const MatGeom gm{I, H, BITS, C::G};
+  const gu16_t msc = (gu16_t)(mat + gm.scales_off());
+  const int ng = H / C::G;
+  const int gps = kPK / C::G;  // groups per step
+  const int64_t tile0 = (int64_t)nt * ng;
+  const int64_t srow = (int64_t)(nt * 64 + wrow) * ng;
+  _Float16* wr = wsm + (m * kGuN + wrow) * kLdsRow;
+
+  const int wm = wv >> 1, wn = wv & 1;
+  const int fr = lane & 15, fk = 8 * (lane >> 4);
+  f32x4 acc[2][4][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[a][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nsteps = H / kPK;
+  RowLoad xl;
+  StepLoad<BITS> wl;
+  xl.load(xrow);
+  wl.load(mat, tile0, wrow, hw, msc, srow + (BITS == 4 ? 2 * hw : 0));
+  for (int s = 0; s < nsteps; ++s) {
+    xl.store(xs + r * kLdsRow + 64 * hx);
+    wl.expand(hw, scale_f16, wr);
+    lds_barrier();
+    if (s + 1 < nsteps) {
+      xl.load(xrow + (s + 1) * kPK);
+      const int g = (s + 1) * gps;
+      wl.load(mat, tile0 + g, wrow, hw, msc, srow + g + (BITS == 4 ? 2 * hw : 0));
+    }
+#pragma unroll
+    for (int kk = 0; kk < kPK / 32; ++kk) {
+      half8 a[4], bg[2], bu[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = lds_frag(xs + (64 * wm + 16 * i + fr) * kLdsRow + 32 * kk + fk);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        bg[j] = lds_frag(wsm + (32 * wn + 16 * j + fr) * kLdsRow + 32 * kk + fk);
+        bu[j] = lds_frag(wsm + (kGuN + 32 * wn + 16 * j + fr) * kLdsRow + 32 * kk + fk);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[0][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bg[j], acc[0][i][j], 0, 0, 0);
+          acc[1][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bu[j], acc[1][i][j], 0, 0, 0);
+        }
+    }
+    lds_barrier();
+  }
+  // epilogue: lane holds column fr of each 16 x 16 tile, rows 4*(lane/16) + q
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int pr = 64 * wm + 16 * i + 4 * (lane >> 4) + q;
+      const int sh = s_shift[pr];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float g = ldexpf(acc[0][i][j][q], sh), u = ldexpf(acc[1][i][j][q], sh);
+        const float h = g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
+        const int col = nt * kGuN + 32 * wn + 16 * j + fr;
+        if (pr < rows) h16[(int64_t)(m0 + pr) * I + col] = __builtin_bit_cast(uint16_t, (_Float16)h);
+      }
+    }
+}
+
+// ---------------------------------------------------------------- down
+// Block: tile (expert e, positions m0 .. m0+127) x rows [128 nt, 128 nt + 128) of
+// the down matrix.  Waves 2 x 2: wave (wm, wn) owns positions [64wm, 64wm+64) and
+// rows [64wn, 64wn+64) (16 tiles).  pair_out[sorted_pairs[pos]][row] = y.
+template <int BITS>
+__global__ __launch_bounds__(256, 2) void k_down_mfma(
+    const moe_expert_ref* __restrict__ table, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ sorted_pairs, int P,
+    const uint16_t* __restrict__ h16, int H, int I, int scale_f16, float* __restrict__ pair_out) {
+  using C = UnitCodec<BITS>;
+  __shared__ __align__(16) _Float16 xs[kPM * kLdsRow];
+  __shared__ __align__(16) _Float16 wsm[kDnN * kLdsRow];
+  __shared__ int s_pair[kPM];
+  const int nH = H / kDnN;
+  const int item = xcd_item(blockIdx.x, gridDim.x);
+  const int tile = item / nH, nt = item % nH;
+  if (tile >= tiles[0]) return;
+  const int e = tiles[1 + 2 * tile], m0 = tiles[2 + 2 * tile];
+  const int rows = min(kPM, offsets[e + 1] - m0);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+
+  const int r = tid >> 1, hx = tid & 1;
+  const int pos = min(m0 + r, P - 1);
+  const uint16_t* hrow = h16 + (int64_t)pos * I + 64 * hx;
+  if (hx == 0) s_pair[r] = sorted_pairs[pos];
+  // weights: thread (hw, tl, row): 64-row tile tl of the block's two
+  const int hw = tid >> 7, tl = (tid >> 6) & 1, wrow = lane;
+  const gbytes_t mat = as_global(table[e].down);
+  const MatGeom gm{H, I, BITS, C::G};
+  const gu16_t msc = (gu16_t)(mat + gm.scales_off());
+  const int ng = I / C::G;
+  const int gps = kPK / C::G;
+  const int trow = nt * 2 + tl;  // 64-row tile index of the matrix
+  const int64_t tile0 = (int64_t)trow * ng;
+  const int64_t srow = (int64_t)(trow * 64 + wrow) * ng;
+  _Float16* wr = wsm + (tl * 64 + wrow) * kLdsRow;
+
+  const int wm = wv >> 1, wn = wv & 1;
+  const int fr = lane & 15, fk = 8 * (lane >> 4);
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nsteps = I / kPK;
+  RowLoad xl;
+  StepLoad<BITS> wl;
+  xl.load(hrow);
+  wl.load(mat, tile0, wrow, hw, msc, srow + (BITS == 4 ? 2 * hw : 0));
+  for (int s = 0; s < nsteps; ++s) {
+    xl.store(xs + r * kLdsRow + 64 * hx);
+    wl.expand(hw, scale_f16, wr);
+    lds_barrier();
+    if (s + 1 < nsteps) {
+      xl.load(hrow + (s + 1) * kPK);
+      const int g = (s + 1) * gps;
+      wl.load(mat, tile0 + g, wrow, hw, msc, srow + g + (BITS == 4 ? 2 * hw : 0));
+    }
+#pragma unroll
+    for (int kk = 0; kk < kPK / 32; ++kk) {
+      half8 a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = lds_frag(xs + (64 * wm + 16 * i + fr) * kLdsRow + 32 * kk + fk);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = lds_frag(wsm + (64 * wn + 16 * j + fr) * kLdsRow + 32 * kk + fk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    lds_barrier();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int pr = 64 * wm + 16 * i + 4 * (lane >> 4) + q;
+      if (pr < rows) {
+        const int p = s_pair[pr];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          pair_out[(int64_t)p * H + nt * kDnN + 64 * wn + 16 * j + fr] = acc[i][j][q];
+      }
+    }
+}
+
+// ---------------------------------------------------------------- launcher
+static_assert(kPM == kPrefillTileRows, "tile rows");
+static_assert(kPK == 128 && kDnN == 128 && kGuN == 64, "prefill_eligible assumes these");
+
+template <int BITS>
+static hipError_t launch_prefill_t(const FwdArgs& f, const WsLayout& L, float* pair_out,
+                                   hipStream_t s) {
+  const moe_cfg& c = *f.c;
+  const int H = c.hidden, I = c.inter, E = c.n_experts, K = c.top_k, T = f.T, P = T * K;
+  uint16_t* x16 = reinterpret_cast<uint16_t*>(f.ws + L.x16);
+  int32_t* xshift = reinterpret_cast<int32_t*>(f.ws + L.xshift);
+  uint16_t* h16 = reinterpret_cast<uint16_t*>(f.ws + L.h16);
+  int32_t* tiles = reinterpret_cast<int32_t*>(f.ws + L.tiles);
+  const int64_t max_tiles = prefill_max_tiles(P, E);
+  auto round8 = [](int64_t n) { return (int)((n + 7) / 8 * 8); };
+  MOE_LAUNCH(KID_XPREP, k_xprep, dim3(T), dim3(256), 0, s, f.x, H, x16, xshift);
+  MOE_LAUNCH(KID_PLAN, k_plan, dim3(1), dim3(1024), 0, s, f.offsets, E, tiles);
+  MOE_LAUNCH(KID_GATEUP, k_gateup_mfma<BITS>, dim3(round8(max_tiles * (I / kGuN))),
+             dim3(256), 0, s, f.table, f.offsets, tiles, f.sorted_pairs, K, x16, xshift, H, I,
+             c.scale_f16, h16);
+  MOE_LAUNCH(KID_DOWN, k_down_mfma<BITS>, dim3(round8(max_tiles * (H / kDnN))),
+             dim3(256), 0, s, f.table, f.offsets, tiles, f.sorted_pairs, P, h16, H, I,
+             c.scale_f16, pair_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const FwdArgs& f, const WsLayout& L, float* pair_out, hipStream_t s) {
+  return f.c->bits == 3 ? launch_prefill_t<3>(f, L, pair_out, s)
+                        : launch_prefill_t<4>(f, L, pair_out, s);
+}
+
+}  // namespace moe

@@ -93,8 +93,12 @@ moe_status moe_create(const moe_cfg* cfg, int32_t n_layers, moe_ctx** out);
 /* Free the context's tables.  Waits for the device to finish with them. */
 moe_status moe_destroy(moe_ctx* ctx);
 
-/* Workspace bytes that moe_route and moe_forward need for n_tokens tokens
- * (0 if n_tokens is out of range).  One workspace serves both calls. */
+/* Workspace bytes that moe_route and moe_forward need for any T <= n_tokens
+ * tokens (0 if n_tokens is out of range).  One workspace serves both calls.
+ * Batches of T <= 64 tokens run the GEMV kernels; larger ones the matrix-core
+ * kernels (when H and I are multiples of 128), whose activation copies are fp16
+ * scaled by a per-token power of two and whose h = silu(g)*u is held in fp16
+ * (|h| must stay below 65504). */
 size_t moe_workspace_bytes(const moe_ctx* ctx, int32_t n_tokens);
 
 /* Zero the workspace's counters; must run once on a new workspace before its

@@ -75,7 +75,10 @@ def test_routing_bit_exact(gpu, name, T):
     ml.close()
 
 
-FFN_CASES = [("c1", 4), ("c1", 1), ("c1", 13), ("c2", 1), ("c2", 3), ("c3", 8), ("c3", 9)]
+# decode batches run the GEMV kernels; T > 64 the matrix-core (prefill) kernels:
+# the 4-bit/G32/fp16-scale shape at T = 300 and the GLM shape just past the switch
+FFN_CASES = [("c1", 4), ("c1", 1), ("c1", 13), ("c2", 1), ("c2", 3), ("c3", 8), ("c3", 9),
+             ("c1", 300), ("c2", 65)]
 
 
 @pytest.mark.parametrize("name,T", FFN_CASES)
@@ -129,6 +132,42 @@ def test_prefill_chunk_sampled(gpu):
         ref = sum(w[t, k] * he.ffn(xh[t], ids[t, k]) for k in range(cfg.top_k))
         assert rel_err(res["out"][t], ref) <= TOL, t
     say(f"[prefill] hot expert {hot} has {counts[hot]} pairs")
+
+
+def test_prefill_ragged_tiles(gpu):
+    """300 tokens through the matrix-core kernels at the GLM shape with the shared
+    expert: every pair of the hottest expert (several 128-row tiles, the last one
+    ragged), every pair of experts with a single pair, random pairs, and the
+    combined output (routed + shared) of sampled tokens."""
+    name, T = "c3", 300
+    say(f"[prefill] {name} T={T}")
+    cfg = synth.CONFIGS[name]
+    dl = layer_for(name, gpu)
+    xh, xd = x_device(cfg, gpu, tokens=T)
+    res = run_gpu(cfg, dl, xd)
+    ids, w = check_routing(cfg, xh, res)
+    off, sp = res["offsets"], res["sorted"]
+    counts = np.diff(off)
+    hot = int(np.argmax(counts))
+    assert counts[hot] > 128 and counts[hot] % 128 != 0, counts[hot]
+    pairs = set(sp[off[hot]:off[hot + 1]].tolist())
+    singles = np.nonzero(counts == 1)[0][:2]
+    pairs |= {int(sp[off[e]]) for e in singles}
+    rng = np.random.default_rng(1)
+    pairs |= set(rng.integers(0, T * cfg.top_k, size=32).tolist())
+    he = HostExperts(cfg)
+    worst = 0.0
+    for p in sorted(pairs):
+        t, e = p // cfg.top_k, ids.reshape(-1)[p]
+        r = rel_err(res["pair_out"][p], he.ffn(xh[t], e))
+        worst = max(worst, r)
+        assert r <= TOL, (p, e, r)
+    sh = he.shared()
+    for t in rng.integers(0, T, size=3).tolist():
+        ref = sum(w[t, k] * he.ffn(xh[t], ids[t, k]) for k in range(cfg.top_k))
+        ref = ref + oracle.shared_ffn(synth.bf16_to_f32(xh[t]).astype(np.float64), *sh)
+        assert rel_err(res["out"][t], ref) <= TOL, t
+    say(f"[prefill] hot expert {hot}: {counts[hot]} pairs; worst pair rel err {worst:.3e}")
 
 
 # ------------------------------------------------------------------ invariants
