@@ -190,6 +190,7 @@ __host__ __device__ inline int64_t prefill_max_tiles(int64_t P, int64_t E) {
 struct WsLayout {
   int64_t counters;   // int32[kCounters]: zero between calls
   int64_t logits;     // double[T][E]
+  int64_t ghist;      // int32[ceil(P/1024)][E]: per-chunk expert counts, then bases (grouping)
   int64_t gu;         // decode: float[2*KP][P][I]: partial gate and up products, rows by sorted position
   int64_t x16;        // prefill: fp16[T][H] activations scaled by 2^-xshift[t]
   int64_t xshift;     // prefill: int32[T]
@@ -212,6 +213,7 @@ __host__ inline WsLayout ws_layout(const moe_cfg& c, int T) {
   };
   L.counters = take(kCounters * 4);
   L.logits = take((int64_t)T * c.n_experts * 8);
+  L.ghist = take((P + 1023) / 1024 * c.n_experts * 4);
   const bool pf = prefill_eligible(c, T);
   L.gu = take(pf ? 0 : 2 * kMaxKParts * P * c.inter * 4);
   L.x16 = take(pf ? (int64_t)T * c.hidden * 2 : 0);
@@ -263,7 +265,7 @@ hipError_t launch_prefill(const FwdArgs& f, const WsLayout& L, float* pair_out, 
 hipError_t launch_route(const moe_cfg& c, const uint16_t* x, int T, const float* wr,
                         const float* bias, int32_t* ids, float* w, int32_t* offsets,
                         int32_t* sorted_pairs, int32_t* pair_pos, double* logits,
-                        int32_t* counter, hipStream_t s);
+                        int32_t* ghist, hipStream_t s);
 hipError_t launch_forward(const FwdArgs& f, hipStream_t s);
 hipError_t launch_rmsnorm(float* resid, const float* add, int T, int H, float eps, uint16_t* y,
                           hipStream_t s);

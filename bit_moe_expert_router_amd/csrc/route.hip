@@ -85,46 +85,85 @@ __global__ __launch_bounds__(256) void k_logits_small(const uint16_t* __restrict
 }
 
 // ---------------------------------------------------------------- logits, large T
-// Tiled fp64 product: block = 32 tokens x 32 experts, 256 threads with 2x2
-// outputs each, reduction dim staged through LDS in steps of 32.
-constexpr int kLT = 32, kLE = 32, kLK = 32;
+// fp64 matrix cores (v_mfma_f64_16x16x4_f64): block = 64 tokens x 64 experts, four
+// waves of 32 x 32; the reduction dim in steps of 32 staged through LDS as fp64
+// (bf16 and fp32 inputs widen exactly), the next step's global loads in flight
+// during the current step's products.  Every product is exact; the sums are fp64.
+constexpr int kLT = 64, kLE = 64, kLK = 32;
+constexpr int kLRow = kLK + 4;  // doubles per LDS row (2-way bank conflicts at most)
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void k_logits_tiled(const uint16_t* __restrict__ x, int T,
-                                                      int H, int E,
-                                                      const float* __restrict__ wr,
-                                                      const float* __restrict__ bias,
-                                                      double* __restrict__ logits) {
-  __shared__ double xs[kLK][kLT + 1];
-  __shared__ double ws[kLK][kLE + 1];
+__global__ __launch_bounds__(256) void k_logits_mfma(const uint16_t* __restrict__ x, int T, int H,
+                                                     int E, const float* __restrict__ wr,
+                                                     const float* __restrict__ bias,
+                                                     double* __restrict__ logits) {
+  __shared__ __align__(16) double xs[kLT * kLRow];
+  __shared__ __align__(16) double ws[kLE * kLRow];
   const int t0 = blockIdx.y * kLT, e0 = blockIdx.x * kLE;
-  const int tid = threadIdx.x;
-  const int ti = (tid % 16) * 2, ei = (tid / 16) * 2;
-  double acc[2][2] = {{0.0, 0.0}, {0.0, 0.0}};
-  for (int k0 = 0; k0 < H; k0 += kLK) {
-    for (int i = tid; i < kLT * kLK; i += 256) {
-      int r = i / kLK, c = i % kLK;
-      int t = t0 + r, e = e0 + r;
-      xs[c][r] = t < T ? (double)bf16_to_f32(x[(int64_t)t * H + k0 + c]) : 0.0;
-      ws[c][r] = e < E ? (double)wr[(int64_t)e * H + k0 + c] : 0.0;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // loader: thread (row, 8 consecutive k)
+  const int lr = tid >> 2, lk = (tid & 3) * 8;
+  const bool xok = t0 + lr < T, wok = e0 + lr < E;
+  const uint16_t* xp = x + (int64_t)min(t0 + lr, T - 1) * H + lk;
+  const float* wp = wr + (int64_t)min(e0 + lr, E - 1) * H + lk;
+  uint4 xv;
+  float4 wv0, wv1;
+  auto load = [&](int k0) {
+    xv = *reinterpret_cast<const uint4*>(xp + k0);
+    wv0 = *reinterpret_cast<const float4*>(wp + k0);
+    wv1 = *reinterpret_cast<const float4*>(wp + k0 + 4);
+  };
+  auto stage = [&]() {
+    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+    double* xd = xs + lr * kLRow + lk;
+    double* wd = ws + lr * kLRow + lk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xd[2 * j] = xok ? (double)bf16_to_f32((uint16_t)xw[j]) : 0.0;
+      xd[2 * j + 1] = xok ? (double)bf16_to_f32((uint16_t)(xw[j] >> 16)) : 0.0;
     }
+    const float wf[8] = {wv0.x, wv0.y, wv0.z, wv0.w, wv1.x, wv1.y, wv1.z, wv1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wd[j] = wok ? (double)wf[j] : 0.0;
+  };
+  const int wm = wv >> 1, wn = wv & 1;
+  const int fr = lane & 15, fk = lane >> 4;
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+  load(0);
+  for (int k0 = 0; k0 < H; k0 += kLK) {
+    stage();
     __syncthreads();
-#pragma unroll 8
-    for (int c = 0; c < kLK; ++c) {
-      double a0 = xs[c][ti], a1 = xs[c][ti + 1];
-      double b0 = ws[c][ei], b1 = ws[c][ei + 1];
-      acc[0][0] = fma(a0, b0, acc[0][0]);
-      acc[0][1] = fma(a0, b1, acc[0][1]);
-      acc[1][0] = fma(a1, b0, acc[1][0]);
-      acc[1][1] = fma(a1, b1, acc[1][1]);
+    if (k0 + kLK < H) load(k0 + kLK);
+#pragma unroll
+    for (int kk = 0; kk < kLK; kk += 4) {
+      double a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = xs[(32 * wm + 16 * i + fr) * kLRow + kk + fk];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = ws[(32 * wn + 16 * j + fr) * kLRow + kk + fk];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
     }
     __syncthreads();
   }
+  // lane holds expert column fr, token rows fk + 4q of each 16 x 16 tile
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      int t = t0 + ti + i, e = e0 + ei + j;
-      if (t < T && e < E) logits[(int64_t)t * E + e] = acc[i][j] + (bias ? (double)bias[e] : 0.0);
+      const int e = e0 + 32 * wn + 16 * j + fr;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = t0 + 32 * wm + 16 * i + fk + 4 * q;
+        if (t < T && e < E) logits[(int64_t)t * E + e] = acc[i][j][q] + (bias ? (double)bias[e] : 0.0);
+      }
     }
 }
 
@@ -312,6 +351,96 @@ __global__ __launch_bounds__(64) void k_permute(const int32_t* __restrict__ ids,
   wave_group(ids, P, E, cnt, run, offsets, sorted_pairs, pair_pos);
 }
 
+// ---------------------------------------------------------------- grouping, many pairs
+// Chunks of kGChunk pairs, one wave each.  Count: per-chunk histograms by the same
+// ballot matching.  Scan (one block): per expert, the exclusive prefix over the
+// chunks, then the exclusive prefix over the experts, giving each (chunk, expert)
+// its first sorted position.  Scatter: each chunk again in pair order from its
+// bases.  The same stable order as the single-wave grouping; integer only.
+constexpr int kGChunk = 1024;
+
+__global__ __launch_bounds__(64) void k_group_count(const int32_t* __restrict__ ids, int P, int E,
+                                                    int32_t* __restrict__ hist) {
+  __shared__ int cnt[kMaxE];
+  const int lane = threadIdx.x;
+  int nbits = 0;
+  while ((1 << nbits) < E + 1) ++nbits;
+  for (int e = lane; e < E; e += 64) cnt[e] = 0;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  const int c0 = blockIdx.x * kGChunk, c1 = min(P, c0 + kGChunk);
+  for (int b = c0; b < c1; b += 64) {
+    const int p = b + lane;
+    const int e = p < c1 ? ids[p] : -1;
+    const bool ok = p < c1 && e >= 0 && e < E;
+    const uint64_t m = match_mask(ok ? e : E, nbits);
+    if (ok && (m & lt) == 0) cnt[e] += __popcll(m);
+  }
+  for (int e = lane; e < E; e += 64) hist[(int64_t)blockIdx.x * E + e] = cnt[e];
+}
+
+__global__ __launch_bounds__(1024) void k_group_scan(int32_t* __restrict__ hist, int nb, int E,
+                                                     int32_t* __restrict__ offsets) {
+  __shared__ int wsum[16];
+  const int e = threadIdx.x, lane = e & 63, wv = e >> 6;
+  int run = 0;
+  if (e < E) {
+    for (int b0 = 0; b0 < nb; b0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) c[j] = b0 + j < nb ? hist[(int64_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (b0 + j < nb) hist[(int64_t)(b0 + j) * E + e] = run;
+        run += c[j];
+      }
+    }
+  }
+  int inc = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) wsum[wv] = inc;
+  __syncthreads();
+  int base = inc - run, total = 0;
+  for (int w = 0; w < 16; ++w) {
+    if (w < wv) base += wsum[w];
+    total += wsum[w];
+  }
+  if (e < E) {
+    offsets[e] = base;
+    for (int b = 0; b < nb; ++b) hist[(int64_t)b * E + e] += base;
+  }
+  if (e == 0) offsets[E] = total;
+}
+
+__global__ __launch_bounds__(64) void k_group_scatter(const int32_t* __restrict__ ids, int P, int E,
+                                                      const int32_t* __restrict__ hist,
+                                                      int32_t* __restrict__ sorted_pairs,
+                                                      int32_t* __restrict__ pair_pos) {
+  __shared__ int run[kMaxE];
+  const int lane = threadIdx.x;
+  int nbits = 0;
+  while ((1 << nbits) < E + 1) ++nbits;
+  for (int e = lane; e < E; e += 64) run[e] = hist[(int64_t)blockIdx.x * E + e];
+  const uint64_t lt = (1ull << lane) - 1ull;
+  const int c0 = blockIdx.x * kGChunk, c1 = min(P, c0 + kGChunk);
+  for (int b = c0; b < c1; b += 64) {
+    const int p = b + lane;
+    const int e = p < c1 ? ids[p] : -1;
+    const bool ok = p < c1 && e >= 0 && e < E;
+    const uint64_t m = match_mask(ok ? e : E, nbits);
+    int pos = -1;
+    if (ok) {
+      pos = run[e] + __popcll(m & lt);
+      sorted_pairs[pos] = p;
+    }
+    if (p < c1) pair_pos[p] = pos;
+    if (ok && (m & lt) == 0) run[e] += __popcll(m);
+  }
+}
+
 // ---------------------------------------------------------------- top-k + grouping, small T
 // Decode batches (T <= 16, T * K <= 64): wave t picks the top-k of token t, then
 // the first wave groups the T*K pairs; one launch instead of two.
@@ -340,24 +469,31 @@ __global__ __launch_bounds__(1024) void k_topk_group_small(
 hipError_t launch_route(const moe_cfg& c, const uint16_t* x, int T, const float* wr,
                         const float* bias, int32_t* ids, float* w, int32_t* offsets,
                         int32_t* sorted_pairs, int32_t* pair_pos, double* logits,
-                        int32_t* counter, hipStream_t s) {
-  const int H = c.hidden, E = c.n_experts, K = c.top_k;
-  (void)counter;
+                        int32_t* ghist, hipStream_t s) {
+  const int H = c.hidden, E = c.n_experts, K = c.top_k, P = T * K;
   if (T <= 32) {
     MOE_LAUNCH(KID_LOGITS, k_logits_small, dim3(E, (T + kLogitTok - 1) / kLogitTok), dim3(256), 0, s,
                x, T, H, E, wr, bias, logits);
   } else {
-    MOE_LAUNCH(KID_LOGITS, k_logits_tiled, dim3((E + kLE - 1) / kLE, (T + kLT - 1) / kLT), dim3(256),
+    MOE_LAUNCH(KID_LOGITS, k_logits_mfma, dim3((E + kLE - 1) / kLE, (T + kLT - 1) / kLT), dim3(256),
                0, s, x, T, H, E, wr, bias, logits);
   }
-  if (T <= 16 && T * K <= 64) {
+  if (T <= 16 && P <= 64) {
     MOE_LAUNCH(KID_TOPK, k_topk_group_small, dim3(1), dim3(64 * T), 0, s, logits, T, E, K,
                ids, w, offsets, sorted_pairs, pair_pos);
     return hipGetLastError();
   }
   MOE_LAUNCH(KID_TOPK, k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, K, ids, w);
-  MOE_LAUNCH(KID_PERMUTE, k_permute, dim3(1), dim3(64), 0, s, ids, T * K, E, offsets, sorted_pairs,
-             pair_pos);
+  if (P <= 4 * kGChunk) {
+    MOE_LAUNCH(KID_PERMUTE, k_permute, dim3(1), dim3(64), 0, s, ids, P, E, offsets, sorted_pairs,
+               pair_pos);
+  } else {
+    const int nb = (P + kGChunk - 1) / kGChunk;
+    MOE_LAUNCH(KID_PERMUTE, k_group_count, dim3(nb), dim3(64), 0, s, ids, P, E, ghist);
+    MOE_LAUNCH(KID_PERMUTE, k_group_scan, dim3(1), dim3(1024), 0, s, ghist, nb, E, offsets);
+    MOE_LAUNCH(KID_PERMUTE, k_group_scatter, dim3(nb), dim3(64), 0, s, ids, P, E, ghist,
+               sorted_pairs, pair_pos);
+  }
   return hipGetLastError();
 }
 
