@@ -21,8 +21,8 @@
 // gate and the up matrix, so the epilogue forms h = silu(g) * u directly and
 // stores it once (fp16).  Down: tile = 128 positions x 128 rows of H; y goes to
 // pair_out row p = t*K + k.  Both walk the reduction in steps of 128 elements
-// (one 3-bit group or four 4-bit groups): global loads of step s+1 are in flight
-// while the matrix cores work on step s out of LDS.
+// (one 3-bit group or four 4-bit groups): global loads of steps s+1 and s+2 are
+// in flight (two register stages) while the matrix cores work on step s out of LDS.
 #include "common.h"
 
 namespace moe {
@@ -113,39 +113,40 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ offse
 // Expand the code pairs a thread owns in one 128-element step into fp16 q*s pairs
 // in its LDS row `wr` (fp16 elements, k = 0 at wr[0]).
 //
-// 3-bit, G = 128: the thread owns half hw of the unit: words 6hw .. 6hw+5, i.e.
-// pairs 30hw .. 30hw+29 (word j/5, field offset {1,4,7,10,13}[j%5] in both halves)
-// and the two spare pairs 60 + 2hw + mm (bit b of the code at bit 0 / 16 of word
-// 3(2hw + mm) + b).
-// 4-bit, G = 32: the thread owns units 2hw, 2hw+1 of the step's four groups
-// (4 words, pair P at word P/4, field offset 4(P%4)).
-__device__ __forceinline__ uint32_t q_times_s(uint32_t field_pair, half2v bias, half2v s2) {
-  // field_pair: a code at bits 0..3 of each 16-bit half
-  const half2v v = __builtin_bit_cast(half2v, field_pair | 0x64006400u);  // 1024 + c
-  return __builtin_bit_cast(uint32_t, (v + bias) * s2);                    // (c - z) * s
+// 3-bit, G = 128: pair P < 60 sits at field offset {1,4,7,10,13}[P%5] of both
+// halves of word P/5; spare pair 60 + m has bit b of its code at bit 0 / 16 of
+// word 3m + b.  4-bit, G = 32: the thread owns units 2hw, 2hw+1 of the step's
+// four groups (4 words, pair P at word P/4, field offset 4(P%4)).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t b) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(mask), "v"(b));
+  return r;
+}
+// a code at bits 0..2 (3-bit) or 0..3 (4-bit) of each 16-bit half of `shifted`
+__device__ __forceinline__ uint32_t q_times_s(uint32_t shifted, uint32_t mask, uint32_t magic,
+                                              half2v bias, half2v s2) {
+  const half2v v = __builtin_bit_cast(half2v, and_or(shifted, mask, magic));  // 1024 + c
+  return __builtin_bit_cast(uint32_t, (v + bias) * s2);                       // (c - z) * s
 }
 
 template <int BITS>
 struct StepLoad;
 
+// 3-bit, G = 128: half hw = 0 owns pairs 0..31 and spare pairs 60, 61 (words 0..6),
+// half 1 owns pairs 32..59 and spare pairs 62, 63 (words 6..11); each half writes
+// whole 16-byte chunks (4 pairs) of its LDS row.
 template <>
 struct StepLoad<3> {
-  uint32_t w[6];
+  uint32_t w[8];  // hw 0: words 0..7; hw 1: words 4..11
   uint32_t sraw;
   __device__ __forceinline__ void load(gbytes_t mat, int64_t tile, int lane, int hw, gu16_t sc,
                                        int64_t sidx) {
     typedef const u32x4p __attribute__((address_space(1)))* g4;
-    typedef const u32x2 __attribute__((address_space(1)))* g2;
-    const gbytes_t base = mat + tile * 3 * 1024 + 16 * lane;
-    if (hw == 0) {
-      const u32x4p a = *(g4)(base);
-      const u32x2 b = *(g2)(base + 1024);
-      w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y;
-    } else {
-      const u32x2 a = *(g2)(base + 1024 + 8);
-      const u32x4p b = *(g4)(base + 2048);
-      w[0] = a.x; w[1] = a.y; w[2] = b.x; w[3] = b.y; w[4] = b.z; w[5] = b.w;
-    }
+    const gbytes_t base = mat + tile * 3 * 1024 + 16 * lane + 1024 * hw;
+    const u32x4p a = *(g4)(base);
+    const u32x4p b = *(g4)(base + 1024);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
     typedef const uint16_t __attribute__((address_space(1)))* g16;
     sraw = *(g16)(sc + sidx);
   }
@@ -154,22 +155,30 @@ struct StepLoad<3> {
                                  : (_Float16)bf16_to_f32((uint16_t)sraw);
     const half2v s2 = {s, s};
     const half2v z = {(_Float16)-1028.f, (_Float16)-1028.f};
+    const uint32_t mask = 0x00070007u, magic = 0x64006400u;
     constexpr int off[5] = {1, 4, 7, 10, 13};
-    uint32_t* out = reinterpret_cast<uint32_t*>(wr) + 30 * hw;  // pair P at out[P - 30hw]
+    u32x4p* out = reinterpret_cast<u32x4p*>(wr);  // chunk q = pairs 4q .. 4q+3
+    // word W of the unit sits at w[W - wb] (wb = 0 for half 0, 4 for half 1)
+    auto pair = [&](int P, int wb) {  // field pair P < 60
+      return q_times_s(w[P / 5 - wb] >> off[P % 5], mask, magic, z, s2);
+    };
+    auto spare = [&](int m, int wb) {  // spare pair 60 + m: words 3m .. 3m+2
+      const int b0 = 3 * m - wb;
+      const uint32_t c = (w[b0] & 0x00010001u) | ((w[b0 + 1] & 0x00010001u) << 1) |
+                         ((w[b0 + 2] & 0x00010001u) << 2);
+      return q_times_s(c, mask, magic, z, s2);
+    };
+    if (hw == 0) {
 #pragma unroll
-    for (int j = 0; j < 30; j += 2) {
-      const uint32_t p0 = q_times_s((w[j / 5] >> off[j % 5]) & 0x00070007u, z, s2);
-      const uint32_t p1 = q_times_s((w[(j + 1) / 5] >> off[(j + 1) % 5]) & 0x00070007u, z, s2);
-      *reinterpret_cast<u32x2*>(out + j) = u32x2{p0, p1};
-    }
-    uint32_t sp[2];
+      for (int q = 0; q < 8; ++q)
+        out[q] = u32x4p{pair(4 * q, 0), pair(4 * q + 1, 0), pair(4 * q + 2, 0), pair(4 * q + 3, 0)};
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint32_t*>(wr) + 60) = u32x2{spare(0, 0), spare(1, 0)};
+    } else {
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-      const uint32_t c = (w[3 * mm] & 0x00010001u) | ((w[3 * mm + 1] & 0x00010001u) << 1) |
-                         ((w[3 * mm + 2] & 0x00010001u) << 2);
-      sp[mm] = q_times_s(c, z, s2);
+      for (int q = 8; q < 15; ++q)
+        out[q] = u32x4p{pair(4 * q, 4), pair(4 * q + 1, 4), pair(4 * q + 2, 4), pair(4 * q + 3, 4)};
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint32_t*>(wr) + 62) = u32x2{spare(2, 4), spare(3, 4)};
     }
-    *reinterpret_cast<u32x2*>(reinterpret_cast<uint32_t*>(wr) + 60 + 2 * hw) = u32x2{sp[0], sp[1]};
   }
 };
 
@@ -191,18 +200,18 @@ struct StepLoad<4> {
   }
   __device__ __forceinline__ void expand(int hw, int scale_f16, _Float16* wr) const {
     const half2v z = {(_Float16)-1032.f, (_Float16)-1032.f};
-    uint32_t* out = reinterpret_cast<uint32_t*>(wr) + 32 * hw;
+    const uint32_t mask = 0x000F000Fu, magic = 0x64006400u;
+    u32x4p* out = reinterpret_cast<u32x4p*>(wr) + 8 * hw;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const uint16_t sb = (uint16_t)(sraw >> (16 * u));
       const _Float16 s = scale_f16 ? __builtin_bit_cast(_Float16, sb) : (_Float16)bf16_to_f32(sb);
       const half2v s2 = {s, s};
 #pragma unroll
-      for (int P = 0; P < 16; P += 2) {
-        const uint32_t p0 = q_times_s((w[4 * u + P / 4] >> (4 * (P % 4))) & 0x000F000Fu, z, s2);
-        const uint32_t p1 =
-            q_times_s((w[4 * u + (P + 1) / 4] >> (4 * ((P + 1) % 4))) & 0x000F000Fu, z, s2);
-        *reinterpret_cast<u32x2*>(out + 16 * u + P) = u32x2{p0, p1};
+      for (int d = 0; d < 4; ++d) {  // word d of the unit holds pairs 4d .. 4d+3
+        const uint32_t x = w[4 * u + d];
+        out[4 * u + d] = u32x4p{q_times_s(x, mask, magic, z, s2), q_times_s(x >> 4, mask, magic, z, s2),
+                                q_times_s(x >> 8, mask, magic, z, s2), q_times_s(x >> 12, mask, magic, z, s2)};
       }
     }
   }
@@ -213,19 +222,19 @@ struct StepLoad<4> {
 // neighbouring items, which share activations and weights, share an L2.
 __device__ __forceinline__ int xcd_item(int b, int nb) { return (b % 8) * (nb / 8) + b / 8; }
 
-// 16-byte global loads of one step of activation rows: thread (r, hx) holds
-// elements [64hx, 64hx + 64) of the step for row r.
+// 16-byte global loads of one step (128 elements, 256 bytes) of activation rows:
+// lane l of wave w reads chunk l % 16 of rows 32w + 4c + l / 16, c < 8, so each
+// load instruction covers four whole 256-byte row segments.  roff[c] is row c's
+// element offset (+ the lane's chunk) from the array base.
 struct RowLoad {
   u32x4p v[8];
-  __device__ __forceinline__ void load(const uint16_t* row_k0) {
-    const u32x4p* p = reinterpret_cast<const u32x4p*>(row_k0);
+  __device__ __forceinline__ void load(const uint16_t* base, const uint32_t (&roff)[8], int koff) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) v[c] = p[c];
+    for (int c = 0; c < 8; ++c) v[c] = *reinterpret_cast<const u32x4p*>(base + roff[c] + koff);
   }
-  __device__ __forceinline__ void store(_Float16* lds_row) const {
-    u32x4p* p = reinterpret_cast<u32x4p*>(lds_row);
+  __device__ __forceinline__ void store(_Float16* xs, int row0, int chunk) const {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) p[c] = v[c];
+    for (int c = 0; c < 8; ++c) *reinterpret_cast<u32x4p*>(xs + (row0 + 4 * c) * kLdsRow + 8 * chunk) = v[c];
   }
 };
 
@@ -256,11 +265,16 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(
   const int rows = min(kPM, offsets[e + 1] - m0);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
-  // activation rows: thread (r, hx)
-  const int r = tid >> 1, hx = tid & 1;
-  const int tok = sorted_pairs[m0 + min(r, rows - 1)] / K;
-  const uint16_t* xrow = x16 + (int64_t)tok * H + 64 * hx;
-  if (hx == 0) s_shift[r] = xshift[tok];
+  // activation rows: lane chunk of rows row0 + 4c
+  const int chunk = lane & 15, row0 = 32 * wv + (lane >> 4);
+  uint32_t roff[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int row = row0 + 4 * c;
+    const int tok = sorted_pairs[m0 + min(row, rows - 1)] / K;
+    roff[c] = (uint32_t)tok * (uint32_t)H + 8 * chunk;
+    if (chunk == 0) s_shift[row] = xshift[tok];
+  }
   // weights: thread (m, hw, row)
   const int m = tid >> 7, hw = (tid >> 6) & 1, wrow = lane;
   const moe_expert_ref ref = table[e];
@@ -275,6 +289,8 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(
 
   const int wm = wv >> 1, wn = wv & 1;
   const int fr = lane & 15, fk = 8 * (lane >> 4);
+  // 16-row sub-tiles of this wave that hold valid positions (the rest are skipped)
+  const int ni = min(4, max(0, (rows - 64 * wm + 15) / 16));
   f32x4 acc[2][4][2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -284,39 +300,56 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(
       for (int j = 0; j < 2; ++j) acc[a][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nsteps = H / kPK;
-  RowLoad xl;
-  StepLoad<BITS> wl;
-  xl.load(xrow);
-  wl.load(mat, tile0, wrow, hw, msc, srow + (BITS == 4 ? 2 * hw : 0));
-  for (int s = 0; s < nsteps; ++s) {
-    xl.store(xs + r * kLdsRow + 64 * hx);
-    wl.expand(hw, scale_f16, wr);
-    lds_barrier();
-    if (s + 1 < nsteps) {
-      xl.load(xrow + (s + 1) * kPK);
-      const int g = (s + 1) * gps;
-      wl.load(mat, tile0 + g, wrow, hw, msc, srow + g + (BITS == 4 ? 2 * hw : 0));
-    }
+  // two register stages: the loads of steps s+1 and s+2 are in flight while the
+  // matrix cores work on step s
+  RowLoad xl[2];
+  StepLoad<BITS> wl[2];
+  auto issue = [&](int st, int b) {
+    const int g = st * gps;
+    xl[b].load(x16, roff, st * kPK);
+    wl[b].load(mat, tile0 + g, wrow, hw, msc, srow + g + (BITS == 4 ? 2 * hw : 0));
+  };
+  auto compute = [&]() {
 #pragma unroll
     for (int kk = 0; kk < kPK / 32; ++kk) {
       half8 a[4], bg[2], bu[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = lds_frag(xs + (64 * wm + 16 * i + fr) * kLdsRow + 32 * kk + fk);
+      if (ni == 0) break;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         bg[j] = lds_frag(wsm + (32 * wn + 16 * j + fr) * kLdsRow + 32 * kk + fk);
         bu[j] = lds_frag(wsm + (kGuN + 32 * wn + 16 * j + fr) * kLdsRow + 32 * kk + fk);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        if (i < ni) {
+          a[i] = lds_frag(xs + (64 * wm + 16 * i + fr) * kLdsRow + 32 * kk + fk);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          acc[0][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bg[j], acc[0][i][j], 0, 0, 0);
-          acc[1][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bu[j], acc[1][i][j], 0, 0, 0);
+          for (int j = 0; j < 2; ++j) {
+            acc[0][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bg[j], acc[0][i][j], 0, 0, 0);
+            acc[1][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bu[j], acc[1][i][j], 0, 0, 0);
+          }
         }
+      }
     }
+  };
+  // every issue is unconditional (past the end it repeats the last step), so the
+  // waits before a stage's use count only the loads of the other stage
+  auto run_stage = [&](int b, int next) {
+    xl[b].store(xs, row0, chunk);
+    wl[b].expand(hw, scale_f16, wr);
     lds_barrier();
+    issue(min(next, nsteps - 1), b);
+    compute();
+    lds_barrier();
+  };
+  issue(0, 0);
+  issue(min(1, nsteps - 1), 1);
+  int s = 0;
+  for (; s + 1 < nsteps; s += 2) {
+    run_stage(0, s + 2);
+    run_stage(1, s + 3);
   }
+  if (s < nsteps) run_stage(0, s + 2);
   // epilogue: lane holds column fr of each 16 x 16 tile, rows 4*(lane/16) + q
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -355,10 +388,15 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(
   const int rows = min(kPM, offsets[e + 1] - m0);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
-  const int r = tid >> 1, hx = tid & 1;
-  const int pos = min(m0 + r, P - 1);
-  const uint16_t* hrow = h16 + (int64_t)pos * I + 64 * hx;
-  if (hx == 0) s_pair[r] = sorted_pairs[pos];
+  const int chunk = lane & 15, row0 = 32 * wv + (lane >> 4);
+  uint32_t roff[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int row = row0 + 4 * c;
+    const int pos = min(m0 + row, P - 1);
+    roff[c] = (uint32_t)pos * (uint32_t)I + 8 * chunk;
+    if (chunk == 0) s_pair[row] = sorted_pairs[pos];
+  }
   // weights: thread (hw, tl, row): 64-row tile tl of the block's two
   const int hw = tid >> 7, tl = (tid >> 6) & 1, wrow = lane;
   const gbytes_t mat = as_global(table[e].down);
@@ -373,6 +411,7 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(
 
   const int wm = wv >> 1, wn = wv & 1;
   const int fr = lane & 15, fk = 8 * (lane >> 4);
+  const int ni = min(4, max(0, (rows - 64 * wm + 15) / 16));
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -380,34 +419,49 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nsteps = I / kPK;
-  RowLoad xl;
-  StepLoad<BITS> wl;
-  xl.load(hrow);
-  wl.load(mat, tile0, wrow, hw, msc, srow + (BITS == 4 ? 2 * hw : 0));
-  for (int s = 0; s < nsteps; ++s) {
-    xl.store(xs + r * kLdsRow + 64 * hx);
-    wl.expand(hw, scale_f16, wr);
-    lds_barrier();
-    if (s + 1 < nsteps) {
-      xl.load(hrow + (s + 1) * kPK);
-      const int g = (s + 1) * gps;
-      wl.load(mat, tile0 + g, wrow, hw, msc, srow + g + (BITS == 4 ? 2 * hw : 0));
-    }
+  RowLoad xl[2];
+  StepLoad<BITS> wl[2];
+  auto issue = [&](int st, int b) {
+    const int g = st * gps;
+    xl[b].load(h16, roff, st * kPK);
+    wl[b].load(mat, tile0 + g, wrow, hw, msc, srow + g + (BITS == 4 ? 2 * hw : 0));
+  };
+  auto compute = [&]() {
 #pragma unroll
     for (int kk = 0; kk < kPK / 32; ++kk) {
       half8 a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = lds_frag(xs + (64 * wm + 16 * i + fr) * kLdsRow + 32 * kk + fk);
+      if (ni == 0) break;
 #pragma unroll
       for (int j = 0; j < 4; ++j) b[j] = lds_frag(wsm + (64 * wn + 16 * j + fr) * kLdsRow + 32 * kk + fk);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        if (i < ni) {
+          a[i] = lds_frag(xs + (64 * wm + 16 * i + fr) * kLdsRow + 32 * kk + fk);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+      }
     }
+  };
+  // every issue is unconditional (past the end it repeats the last step), so the
+  // waits before a stage's use count only the loads of the other stage
+  auto run_stage = [&](int b, int next) {
+    xl[b].store(xs, row0, chunk);
+    wl[b].expand(hw, scale_f16, wr);
     lds_barrier();
+    issue(min(next, nsteps - 1), b);
+    compute();
+    lds_barrier();
+  };
+  issue(0, 0);
+  issue(min(1, nsteps - 1), 1);
+  int s = 0;
+  for (; s + 1 < nsteps; s += 2) {
+    run_stage(0, s + 2);
+    run_stage(1, s + 3);
   }
+  if (s < nsteps) run_stage(0, s + 2);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
