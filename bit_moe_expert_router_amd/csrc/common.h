@@ -192,6 +192,7 @@ struct WsLayout {
   int64_t logits;     // double[T][E]
   int64_t ghist;      // int32[ceil(P/1024)][E]: per-chunk expert counts, then bases (grouping)
   int64_t gu;         // decode: float[2*KP][P][I]: partial gate and up products, rows by sorted position
+  int64_t hdec;       // decode: bf16[2][P][I]: h hi rows, then h lo rows, by sorted position
   int64_t x16;        // prefill: fp16[T][H] activations scaled by 2^-xshift[t]
   int64_t xshift;     // prefill: int32[T]
   int64_t h16;        // prefill: fp16[P][I] h rows by sorted position
@@ -216,6 +217,7 @@ __host__ inline WsLayout ws_layout(const moe_cfg& c, int T) {
   L.ghist = take((P + 1023) / 1024 * c.n_experts * 4);
   const bool pf = prefill_eligible(c, T);
   L.gu = take(pf ? 0 : 2 * kMaxKParts * P * c.inter * 4);
+  L.hdec = take(pf ? 0 : 2 * P * c.inter * 2);
   L.x16 = take(pf ? (int64_t)T * c.hidden * 2 : 0);
   L.xshift = take(pf ? (int64_t)T * 4 : 0);
   L.h16 = take(pf ? P * c.inter * 2 : 0);
@@ -230,7 +232,7 @@ __host__ inline WsLayout ws_layout(const moe_cfg& c, int T) {
 // ---------------------------------------------------------------- profiling
 enum KernelId {
   KID_LOGITS = 0, KID_TOPK, KID_PERMUTE, KID_PLAN, KID_GATEUP, KID_DOWN, KID_SH_GATEUP,
-  KID_SH_DOWN, KID_COMBINE, KID_RMSNORM, KID_ZERO, KID_XPREP, KID_COUNT
+  KID_SH_DOWN, KID_COMBINE, KID_RMSNORM, KID_ZERO, KID_XPREP, KID_SWIGLU, KID_COUNT
 };
 void prof_begin(int kid, hipStream_t s);
 void prof_end(int kid, hipStream_t s);

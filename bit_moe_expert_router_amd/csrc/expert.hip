@@ -133,20 +133,24 @@ __device__ __forceinline__ void unit_words(const u32x4 (&c)[UnitCodec<BITS>::CHU
 // expert, rows [64*strip, 64*strip+64), part kp of the reduction dimension (a
 // contiguous range of groups); 4 waves take groups g0 + wave + 4*i, i < GPW.
 //
-// Memory schedule.  Every wave issues the vector loads of all its groups' codes
-// and scales at entry, so the whole weight stream is in flight after one memory
-// latency.  The activations take the scalar path instead (s_load into SGPRs,
-// the second operand of v_dot2_f32_bf16): they do not queue behind the weight
-// stream, so each group is computed as soon as its own codes arrive.  The
-// per-group offset sums of the activations (what the unit codec's dot products
-// carry) come from vector loads that are only needed at the very end.
+// Memory schedule.  Each wave first requests the activations of its groups for
+// up to kXTok of the expert's tokens (they go to the wave's own LDS region), then
+// all of its groups' codes and scales, so the whole weight stream is in flight
+// after one memory latency and stays in registers.  The token passes then read
+// the activations from LDS (one broadcast 16-byte read gives four pairs), so no
+// pass waits on memory; experts with more than kXTok tokens stage the next
+// tokens when the first ones are done.  The per-group offset sums of the
+// activations (what the unit codec's dot products carry) come from the same LDS
+// copy.
 //
-// Tokens run two at a time against the resident weights; each pair is expanded
-// right before its dot products.  The partial product (fp32) goes to
+// Tokens run two at a time against the resident weights; each code pair is
+// expanded right before its dot products.  The partial product (fp32) goes to
 // gu[m*KP + kp][pos][row] at the pair's sorted position; the parts are added in
 // kp order, with SwiGLU, where the down matrix reads them.
 constexpr int kGUWaves = 4;
 constexpr int kTokPerPass = 2;
+// tokens whose activations a wave stages at a time: XT (2 for batches of at most
+// two tokens, else 8)
 
 // Sum over the 64 lanes in a fixed order (row prefix sums by DPP, then the row
 // totals), returned to every lane; deterministic, no LDS traffic.
@@ -165,8 +169,150 @@ __device__ __forceinline__ float wave_sum_uniform(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-template <int BITS, int GPW>
+// Stage the activations of tokens c0 .. c0+nt-1 of the expert (token index of
+// position j held by lane j in `tok`) for the wave's groups g_i = gbase + 4i
+// (clamped to glast) into xs[j][i][pair] (bf16 pairs).  16-byte pieces: piece q
+// covers token q / (GPW*PC), group (q / PC) % GPW, pairs 4*(q % PC) .. +3.
+template <int BITS, int GPW, int XT>
+struct XStage {
+  using C = UnitCodec<BITS>;
+  static constexpr int PC = C::G / 8;                    // 16-byte pieces per group
+  static constexpr int NQ = XT * GPW * PC;               // pieces of a full chunk
+  static constexpr int IT = (NQ + 63) / 64;              // pieces per lane
+  u32x4 v[IT];
+  __device__ __forceinline__ void load(const uint16_t* x, int H, int tok, int c0, int nt,
+                                       int gbase, int glast, int lane) {
+    typedef const u32x4 __attribute__((address_space(1)))* g4;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int q = min(it * 64 + lane, NQ - 1);
+      const int j = q / (GPW * PC), i = (q / PC) % GPW, pc = q % PC;
+      const int tj = __shfl(tok, c0 + min(j, nt - 1));
+      const int g = min(gbase + kGUWaves * i, glast);
+      v[it] = *(g4)(as_global(x + (int64_t)tj * H + g * C::G + 8 * pc));
+    }
+  }
+  __device__ __forceinline__ void store(uint32_t* xs, int lane) const {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int q = it * 64 + lane;
+      if (q < NQ) *reinterpret_cast<u32x4*>(xs + 4 * q) = v[it];
+    }
+  }
+};
+
+template <int BITS, int GPW, int XT>
 __global__ __launch_bounds__(256, 2) void k_gateup(
+    const moe_expert_ref* __restrict__ table, int E, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_pairs, int K, const uint16_t* __restrict__ x, int H, int I,
+    int P, int KP, int scale_f16, float* __restrict__ gu) {
+  using C = UnitCodec<BITS>;
+  using XS = XStage<BITS, GPW, XT>;
+  constexpr int XW = XT * GPW * C::PAIRS;  // bf16 pairs per wave
+  __shared__ float red[kGUWaves][kTokPerPass][64];
+  __shared__ __align__(16) uint32_t xs_all[kGUWaves * XW];
+  const int ng = H / C::G;
+
+  const Active act = find_active(offsets, table, E, blockIdx.x);
+  if (act.e < 0) return;
+  const int seg0 = __builtin_amdgcn_readfirstlane(act.seg0);
+  const int n_e = __builtin_amdgcn_readfirstlane(act.n);
+  const int strip = blockIdx.y, m = blockIdx.z / KP, kp = blockIdx.z % KP;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const MatGeom gm{I, H, BITS, C::G};
+  const gbytes_t mat = as_global(m ? act.ptr[1] : act.ptr[0]);
+  const gu16_t msc = (gu16_t)(mat + gm.scales_off());
+  const int row = strip * 64 + lane;
+  const int gpb = (ng + KP - 1) / KP, g0 = kp * gpb, g1 = min(ng, g0 + gpb);
+  uint32_t* xs = xs_all + wv * XW;
+
+  // token of each of the expert's positions (lane = position; n_e <= 64 at decode)
+  int tok = sorted_pairs[seg0 + min(lane, n_e - 1)] / K;
+  XS xst;
+  int nt = min(n_e, XT);
+  xst.load(x, H, tok, 0, nt, g0 + wv, g1 - 1, lane);
+  asm volatile("" ::: "memory");
+
+  // weights: all groups of this wave at once (group index clamped, not branched
+  // on, so that the waits the compiler places stay exact)
+  u32x4 cw[GPW][C::CHUNKS];
+  uint32_t sr[GPW];  // the aligned dword holding the scale (any 16-bit handling here would wait)
+#pragma unroll
+  for (int i = 0; i < GPW; ++i) {
+    const int g = min(g0 + wv + kGUWaves * i, g1 - 1);
+    load_unit4<BITS>(mat, (int64_t)strip * ng + g, lane, cw[i]);
+    sr[i] = load_scale_dword(msc, (int64_t)row * ng + g);
+  }
+  asm volatile("" ::: "memory");
+
+  const float off = lane < C::PAIRS ? C::pair_off(lane) : 0.f;
+  xst.store(xs, lane);  // the first tokens (waits for them only, not for the weights)
+  for (int c0 = 0; c0 < n_e; c0 += XT) {
+    if (c0 > 0) {  // next tokens; positions come 64 per lane window
+      nt = min(n_e - c0, XT);
+      if (c0 % 64 == 0) tok = sorted_pairs[seg0 + c0 + min(lane, n_e - c0 - 1)] / K;
+      xst.load(x, H, tok, c0 % 64, nt, g0 + wv, g1 - 1, lane);
+      xst.store(xs, lane);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's own LDS writes
+    for (int b0 = 0; b0 < nt; b0 += kTokPerPass) {
+      const bool two = b0 + 1 < nt;
+      const int j1 = two ? b0 + 1 : b0;
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < GPW; ++i) {
+        const int g = g0 + wv + kGUWaves * i;
+        if (g < g1) {
+          const uint32_t* x0 = xs + (b0 * GPW + i) * C::PAIRS;
+          const uint32_t* x1 = xs + (j1 * GPW + i) * C::PAIRS;
+          uint32_t sraw = sr[i];
+          asm volatile("" : "+v"(sraw));  // convert here, not hoisted ahead of the loads
+          const float sc = scale_to_f32(scale_from_dword(sraw, (int64_t)row * ng + g), scale_f16);
+          // offset sums of the two tokens' activations over the group
+          const uint32_t p0 = lane < C::PAIRS ? x0[lane] : 0u;
+          const uint32_t p1 = lane < C::PAIRS ? x1[lane] : 0u;
+          const float c0s = wave_sum_uniform<BITS>(off * bf16_to_f32((uint16_t)p0) +
+                                                   off * bf16_to_f32((uint16_t)(p0 >> 16)));
+          uint32_t w[C::WORDS];
+          float d0 = 0.f, d1 = 0.f;
+          unit_words<BITS>(cw[i], w);
+          if (two) {
+            const float c1s = wave_sum_uniform<BITS>(off * bf16_to_f32((uint16_t)p1) +
+                                                     off * bf16_to_f32((uint16_t)(p1 >> 16)));
+            C::for_each_pair(w, [&](int Pp, uint32_t pr) {
+              d0 = dot2_bf16(pr, x0[Pp], d0);
+              d1 = dot2_bf16(pr, x1[Pp], d1);
+            });
+            a1 = fmaf(sc, d1 - c1s, a1);
+          } else {
+            C::for_each_pair(w, [&](int Pp, uint32_t pr) { d0 = dot2_bf16(pr, x0[Pp], d0); });
+          }
+          a0 = fmaf(sc, d0 - c0s, a0);
+        }
+      }
+      red[wv][0][lane] = a0;
+      red[wv][1][lane] = a1;
+      lds_barrier();
+      if (wv < (two ? 2 : 1)) {
+        const int j = wv;
+        float y = 0.f;
+#pragma unroll
+        for (int w = 0; w < kGUWaves; ++w) y += red[w][j][lane];
+        gu[((int64_t)blockIdx.z * P + seg0 + c0 + b0 + j) * I + row] = y;
+      }
+      lds_barrier();
+    }
+  }
+}
+
+// Batches of one or two tokens (a single pass): the activations take the scalar
+// path instead (s_load into SGPRs, the second operand of v_dot2_f32_bf16), which
+// keeps the kernel at three waves per SIMD so the whole weight stream of a
+// decode step is in flight at once; the offset sums come from vector loads that
+// are requested before the weights.
+template <int BITS, int GPW>
+__global__ __launch_bounds__(256, 2) void k_gateup_smem(
     const moe_expert_ref* __restrict__ table, int E, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pairs, int K,
     const uint16_t* __restrict__ x,  // read-only: dot operands through scalar loads
@@ -288,113 +434,96 @@ __global__ __launch_bounds__(256, 2) void k_gateup(
   }
 }
 
+// ---------------------------------------------------------------- SwiGLU
+// h of every grouped pair position: h = silu(sum_q g_q) * (sum_q u_q), parts
+// added in kp order, kept as bf16 hi + bf16 remainder (h to ~2^-16 relative):
+// hh[pos][k], hl[pos][k].  One block per position; positions past the grouped
+// pairs (ids left out) are skipped.
+__global__ __launch_bounds__(256) void k_swiglu(const float* __restrict__ gu,
+                                                const int32_t* __restrict__ offsets, int E, int P,
+                                                int I, int KP, uint16_t* __restrict__ hh,
+                                                uint16_t* __restrict__ hl) {
+  const int pos = blockIdx.x;
+  if (pos >= offsets[E]) return;
+  const int I4 = I / 4;
+  const float4* g4 = reinterpret_cast<const float4*>(gu);
+  for (int k4 = threadIdx.x; k4 < I4; k4 += 256) {
+    float4 pg[kMaxKParts], pu[kMaxKParts];
+#pragma unroll
+    for (int q = 0; q < kMaxKParts; ++q) {
+      const int qq = min(q, KP - 1);
+      pg[q] = g4[((int64_t)qq * P + pos) * I4 + k4];
+      pu[q] = g4[((int64_t)(KP + qq) * P + pos) * I4 + k4];
+    }
+    float4 g = pg[0], u = pu[0];
+#pragma unroll
+    for (int q = 1; q < kMaxKParts; ++q)
+      if (q < KP) {
+        g.x += pg[q].x; g.y += pg[q].y; g.z += pg[q].z; g.w += pg[q].w;
+        u.x += pu[q].x; u.y += pu[q].y; u.z += pu[q].z; u.w += pu[q].w;
+      }
+    const float gv[4] = {g.x, g.y, g.z, g.w}, uv[4] = {u.x, u.y, u.z, u.w};
+    uint16_t hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float h = gv[e] * __builtin_amdgcn_rcpf(1.f + __expf(-gv[e])) * uv[e];
+      hi[e] = f32_to_bf16_rne(h);
+      lo[e] = f32_to_bf16_rne(h - bf16_to_f32(hi[e]));
+    }
+    const int64_t o = (int64_t)pos * I + 4 * k4;
+    *reinterpret_cast<uint2*>(hh + o) = make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
+    *reinterpret_cast<uint2*>(hl + o) = make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+  }
+}
+
 // ---------------------------------------------------------------- down
 // Block (a, strip): rows [64*strip, +64) of the down matrix of the a-th active
-// expert; 4 waves take groups g = wave + 4*i, i < GPW, loaded into registers at
-// entry.  The block requests the gate/up partial products of its first tokens
-// (they sit in L2) before its weights, so h = silu(g) * u is formed while the
-// weights are in flight.  h is kept in LDS as bf16 hi + bf16 remainder (h to
-// ~2^-16 relative), with each group's offset sum sum_k off_k * (hi_k + lo_k)
-// reduced over the lanes that formed the group.  Tokens two at a time; y goes to
-// row p = t*K + k of pair_out.
+// expert; 4 waves take groups g = wave + 4*i, i < GPW.  The same schedule as the
+// gate/up kernel: each wave requests h (hi and lo rows) of up to XT of the
+// expert's positions for its groups into its own LDS region, then its weights;
+// the token passes run from LDS with two dot products per code pair (hi, lo).
+// y goes to row p = t*K + k of pair_out.
 constexpr int kDNWaves = 4;
-constexpr int kHChunk = 4;  // tokens' h staged in LDS at a time
-constexpr int kSB = 2;      // float4 items of h per thread per staging batch
 
-__host__ __device__ constexpr int down_lds_bytes(int I, int G) {
-  return kHChunk * I * 4 + kHChunk * (I / G) * 4;
-}
-
-// gate and up partial products of float4 item i4 of a chunk of tokens (token j =
-// i4 / (I/4) of the chunk); parts q >= KP repeat part KP-1 and are dropped at use,
-// so every load is unconditional.
-struct HItem {
-  float4 g[kMaxKParts], u[kMaxKParts];
+template <int BITS, int GPW, int XT>
+struct HStage {
+  using C = UnitCodec<BITS>;
+  static constexpr int PC = C::G / 8;             // 16-byte pieces per group row
+  static constexpr int NQ = XT * GPW * 2 * PC;    // pieces of a full chunk (hi and lo)
+  static constexpr int IT = (NQ + 63) / 64;
+  u32x4 v[IT];
+  __device__ __forceinline__ void load(const uint16_t* hh, const uint16_t* hl, int I, int pos0,
+                                       int nt, int gbase, int glast, int lane) {
+    typedef const u32x4 __attribute__((address_space(1)))* g4;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int q = min(it * 64 + lane, NQ - 1);
+      const int j = q / (GPW * 2 * PC), i = (q / (2 * PC)) % GPW, sel = (q / PC) % 2, pc = q % PC;
+      const int g = min(gbase + kDNWaves * i, glast);
+      const uint16_t* src = (sel ? hl : hh) + (int64_t)(pos0 + min(j, nt - 1)) * I + g * C::G + 8 * pc;
+      v[it] = *(g4)(as_global(src));
+    }
+  }
+  __device__ __forceinline__ void store(uint32_t* xs, int lane) const {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int q = it * 64 + lane;
+      if (q < NQ) *reinterpret_cast<u32x4*>(xs + 4 * q) = v[it];
+    }
+  }
 };
 
-__device__ __forceinline__ void h_load(const float* __restrict__ gu, int64_t P, int I, int KP,
-                                       int64_t pos0, int tot4, int i4, HItem& it) {
-  const int I4 = I / 4;
-  const int ic = min(i4, tot4 - 1);
-  const int j = ic / I4, k4 = ic - j * I4;
-  const float4* base = reinterpret_cast<const float4*>(gu) + (pos0 + j) * I4 + k4;
-  const int64_t part = P * I4;
-#pragma unroll
-  for (int q = 0; q < kMaxKParts; ++q) {
-    const int qq = min(q, KP - 1);
-    it.g[q] = base[qq * part];
-    it.u[q] = base[(KP + qq) * part];
-  }
-}
-
-// Sum over the aligned lanes of one group (32 lanes for G = 128, 8 for G = 32,
-// one float4 item each), valid in the group's last lane; fixed order.
-template <int BITS>
-__device__ __forceinline__ float group_lane_sum(float v) {
-  v += dpp_shift<0x111>(v);
-  v += dpp_shift<0x112>(v);
-  v += dpp_shift<0x114>(v);
-  if (BITS == 3) {
-    v += dpp_shift<0x118>(v);
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
-  }
-  return v;
-}
-
-// h of one item to LDS (hi row 2j, lo row 2j+1) and its share of the group's
-// offset sum, written to kc[j][g] by the group's last lane.  Every lane of the
-// wave calls it (the lane sum needs them all); only items < tot4 store.
-template <int BITS>
-__device__ __forceinline__ void h_store(const HItem& it, int KP, int I, int tot4, int i4,
-                                        uint16_t* hs, float* kc) {
-  using C = UnitCodec<BITS>;
-  const int I4 = I / 4;
-  const int ic = min(i4, tot4 - 1);
-  const int j = ic / I4, k4 = ic - j * I4;
-  float4 g = it.g[0], u = it.u[0];
-#pragma unroll
-  for (int q = 1; q < kMaxKParts; ++q)
-    if (q < KP) {
-      g.x += it.g[q].x; g.y += it.g[q].y; g.z += it.g[q].z; g.w += it.g[q].w;
-      u.x += it.u[q].x; u.y += it.u[q].y; u.z += it.u[q].z; u.w += it.u[q].w;
-    }
-  const float gv[4] = {g.x, g.y, g.z, g.w}, uv[4] = {u.x, u.y, u.z, u.w};
-  uint16_t hi[4], lo[4];
-  float hsum[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float h = gv[e] * __builtin_amdgcn_rcpf(1.f + __expf(-gv[e])) * uv[e];
-    hi[e] = f32_to_bf16_rne(h);
-    lo[e] = f32_to_bf16_rne(h - bf16_to_f32(hi[e]));
-    hsum[e] = bf16_to_f32(hi[e]) + bf16_to_f32(lo[e]);
-  }
-  const int kg = (4 * k4) % C::G;  // element index of hi[0] within its group
-  const float o0 = C::pair_off(kg / 2), o1 = C::pair_off(kg / 2 + 1);
-  const float part = group_lane_sum<BITS>(o0 * (hsum[0] + hsum[1]) + o1 * (hsum[2] + hsum[3]));
-  if (i4 < tot4) {
-    uint2 vh, vl;
-    vh.x = hi[0] | ((uint32_t)hi[1] << 16);
-    vh.y = hi[2] | ((uint32_t)hi[3] << 16);
-    vl.x = lo[0] | ((uint32_t)lo[1] << 16);
-    vl.y = lo[2] | ((uint32_t)lo[3] << 16);
-    *reinterpret_cast<uint2*>(hs + (2 * j) * I + 4 * k4) = vh;
-    *reinterpret_cast<uint2*>(hs + (2 * j + 1) * I + 4 * k4) = vl;
-    if (kg + 4 == C::G) kc[j * (I / C::G) + (4 * k4) / C::G] = part;
-  }
-}
-
-template <int BITS, int GPW>
-__global__ __launch_bounds__(256) void k_down(
+template <int BITS, int GPW, int XT>
+__global__ __launch_bounds__(256, 2) void k_down(
     const moe_expert_ref* __restrict__ table, int E, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_pairs, int H, int I, int P, int KP, int scale_f16,
-    const float* __restrict__ gu, float* __restrict__ pair_out) {
+    const int32_t* __restrict__ sorted_pairs, int H, int I, int scale_f16,
+    const uint16_t* __restrict__ hh, const uint16_t* __restrict__ hl, float* __restrict__ pair_out) {
   using C = UnitCodec<BITS>;
-  constexpr int NT = 64 * kDNWaves;
-  extern __shared__ __align__(16) uint8_t dyn[];
-  const int ng = I / C::G;
-  uint16_t* hs = reinterpret_cast<uint16_t*>(dyn);             // [kHChunk * 2][I]: hi, lo
-  float* kc = reinterpret_cast<float*>(dyn + kHChunk * I * 4);  // [kHChunk][ng]
+  using HS = HStage<BITS, GPW, XT>;
+  constexpr int XW = XT * GPW * 2 * C::PAIRS;  // uint32 per wave: [token][group][hi|lo][pair]
   __shared__ float red[kDNWaves][kTokPerPass][64];
+  __shared__ __align__(16) uint32_t xs_all[kDNWaves * XW];
+  const int ng = I / C::G;
 
   const Active act = find_active(offsets, table, E, blockIdx.x);
   if (act.e < 0) return;
@@ -407,15 +536,14 @@ __global__ __launch_bounds__(256) void k_down(
   const gbytes_t down = as_global(act.ptr[2]);
   const gu16_t dsc = (gu16_t)(down + gm.scales_off());
   const int row = strip * 64 + lane;
-  const int I4 = I / 4;
+  uint32_t* xs = xs_all + wv * XW;
 
-  // pair ids of the expert's first 64 positions (lane = position), then the first
-  // staging batch of the first chunk, all ahead of the weights
-  const int pids = sorted_pairs[seg0 + min(lane, n_e - 1)];
-  const int nc0 = min(kHChunk, n_e);
-  HItem it[kSB];
-#pragma unroll
-  for (int r = 0; r < kSB; ++r) h_load(gu, P, I, KP, seg0, nc0 * I4, threadIdx.x + NT * r, it[r]);
+  // pair ids of the expert's first 64 positions (lane = position), then h of the
+  // first positions, all ahead of the weights
+  int pids = sorted_pairs[seg0 + min(lane, n_e - 1)];
+  HS hst;
+  int nt = min(n_e, XT);
+  hst.load(hh, hl, I, seg0, nt, wv, ng - 1, lane);
   asm volatile("" ::: "memory");
 
   u32x4 cw[GPW][C::CHUNKS];
@@ -428,41 +556,54 @@ __global__ __launch_bounds__(256) void k_down(
   }
   asm volatile("" ::: "memory");
 
-  auto dots = [&](int c0, int nc) {
-    for (int jp = 0; jp < nc; jp += kTokPerPass) {
-      const bool two = jp + 1 < nc;
+  const float off = lane < C::PAIRS ? C::pair_off(lane) : 0.f;
+  auto osum = [&](const uint32_t* hhp, const uint32_t* hlp) {
+    const uint32_t a = lane < C::PAIRS ? hhp[lane] : 0u, b = lane < C::PAIRS ? hlp[lane] : 0u;
+    return wave_sum_uniform<BITS>(off * ((bf16_to_f32((uint16_t)a) + bf16_to_f32((uint16_t)(a >> 16))) +
+                                         (bf16_to_f32((uint16_t)b) + bf16_to_f32((uint16_t)(b >> 16)))));
+  };
+  hst.store(xs, lane);
+  for (int c0 = 0; c0 < n_e; c0 += XT) {
+    if (c0 > 0) {
+      nt = min(n_e - c0, XT);
+      hst.load(hh, hl, I, seg0 + c0, nt, wv, ng - 1, lane);
+      hst.store(xs, lane);
+      if (c0 % 64 == 0) pids = sorted_pairs[seg0 + c0 + min(lane, n_e - c0 - 1)];
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's own LDS writes
+    for (int jp = 0; jp < nt; jp += kTokPerPass) {
+      const bool two = jp + 1 < nt;
       const int j1 = two ? jp + 1 : jp;
       float a0 = 0.f, a1 = 0.f;
 #pragma unroll
       for (int i = 0; i < GPW; ++i) {
         const int g = wv + kDNWaves * i;
         if (g < ng) {
+          const uint32_t* hh0 = xs + ((jp * GPW + i) * 2 + 0) * C::PAIRS;
+          const uint32_t* hl0 = xs + ((jp * GPW + i) * 2 + 1) * C::PAIRS;
+          const uint32_t* hh1 = xs + ((j1 * GPW + i) * 2 + 0) * C::PAIRS;
+          const uint32_t* hl1 = xs + ((j1 * GPW + i) * 2 + 1) * C::PAIRS;
           uint32_t wd[C::WORDS];
           unit_words<BITS>(cw[i], wd);
           uint32_t sraw = sr[i];
           asm volatile("" : "+v"(sraw));
-          const float s = scale_to_f32(scale_from_dword(sraw, (int64_t)row * ng + g), scale_f16);
-          const uint32_t* hh0 = reinterpret_cast<const uint32_t*>(hs + (jp * 2 + 0) * I + g * C::G);
-          const uint32_t* hl0 = reinterpret_cast<const uint32_t*>(hs + (jp * 2 + 1) * I + g * C::G);
-          const uint32_t* hh1 = reinterpret_cast<const uint32_t*>(hs + (j1 * 2 + 0) * I + g * C::G);
-          const uint32_t* hl1 = reinterpret_cast<const uint32_t*>(hs + (j1 * 2 + 1) * I + g * C::G);
-          const float k0 = kc[jp * ng + g];
-          const float k1 = kc[j1 * ng + g];
+          const float sc = scale_to_f32(scale_from_dword(sraw, (int64_t)row * ng + g), scale_f16);
+          const float k0 = osum(hh0, hl0);
           float d0 = 0.f, d1 = 0.f;
           if (two) {
+            const float k1 = osum(hh1, hl1);
             C::for_each_pair(wd, [&](int Pp, uint32_t pr) {
               d0 = dot2_bf16(pr, hl0[Pp], dot2_bf16(pr, hh0[Pp], d0));
               d1 = dot2_bf16(pr, hl1[Pp], dot2_bf16(pr, hh1[Pp], d1));
             });
-            a1 = fmaf(s, d1 - k1, a1);
+            a1 = fmaf(sc, d1 - k1, a1);
           } else {
             C::for_each_pair(wd, [&](int Pp, uint32_t pr) {
               d0 = dot2_bf16(pr, hl0[Pp], dot2_bf16(pr, hh0[Pp], d0));
             });
           }
-          a0 = fmaf(s, d0 - k0, a0);
+          a0 = fmaf(sc, d0 - k0, a0);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
       red[wv][0][lane] = a0;
       red[wv][1][lane] = a1;
@@ -472,40 +613,12 @@ __global__ __launch_bounds__(256) void k_down(
         float y = 0.f;
 #pragma unroll
         for (int ww = 0; ww < kDNWaves; ++ww) y += red[ww][j][lane];
-        const int idx = c0 + jp + j;  // wave-uniform
-        const int p = idx < 64 ? __builtin_amdgcn_readlane(pids, idx) : sorted_pairs[seg0 + idx];
+        const int idx = (c0 + jp + j) % 64;  // wave-uniform
+        const int p = __builtin_amdgcn_readlane(pids, idx);
         pair_out[(int64_t)p * H + row] = y;
       }
       lds_barrier();
     }
-  };
-
-  // chunk 0: the batch already loaded, then the rest
-  {
-    const int tot4 = nc0 * I4;
-#pragma unroll
-    for (int r = 0; r < kSB; ++r) h_store<BITS>(it[r], KP, I, tot4, threadIdx.x + NT * r, hs, kc);
-    for (int b = NT * kSB; b < tot4; b += NT * kSB) {
-#pragma unroll
-      for (int r = 0; r < kSB; ++r) h_load(gu, P, I, KP, seg0, tot4, b + threadIdx.x + NT * r, it[r]);
-#pragma unroll
-      for (int r = 0; r < kSB; ++r) h_store<BITS>(it[r], KP, I, tot4, b + threadIdx.x + NT * r, hs, kc);
-    }
-    lds_barrier();
-    dots(0, nc0);
-  }
-  for (int c0 = kHChunk; c0 < n_e; c0 += kHChunk) {
-    const int nc = min(kHChunk, n_e - c0);
-    const int tot4 = nc * I4;
-    for (int b = 0; b < tot4; b += NT * kSB) {
-#pragma unroll
-      for (int r = 0; r < kSB; ++r)
-        h_load(gu, P, I, KP, seg0 + c0, tot4, b + threadIdx.x + NT * r, it[r]);
-#pragma unroll
-      for (int r = 0; r < kSB; ++r) h_store<BITS>(it[r], KP, I, tot4, b + threadIdx.x + NT * r, hs, kc);
-    }
-    lds_barrier();
-    dots(c0, nc);
   }
 }
 
@@ -677,22 +790,37 @@ hipError_t launch_forward_t(const FwdArgs& f, hipStream_t s) {
     const int KP = (ngh + 5 * kGUWaves - 1) / (5 * kGUWaves);  // <= kMaxKParts for H/G <= 64
     const int gpw_gu = ((ngh + KP - 1) / KP + kGUWaves - 1) / kGUWaves;
     const int gpw_dn = (I / C::G + kDNWaves - 1) / kDNWaves;
-    const int lds_dn = down_lds_bytes(I, C::G);
   #define MOE_GU(N)                                                                               \
     case N:                                                                                       \
-      MOE_LAUNCH(KID_GATEUP, (k_gateup<BITS, N>), dim3(maxU, I / 64, 2 * KP), dim3(64 * kGUWaves),\
-                 0, s, f.table, E, f.offsets, f.sorted_pairs, K, f.x, f.x, H, I, T * K, KP,       \
-                 c.scale_f16, gu);                                                                \
+      if (T <= 2) {                                                                               \
+        MOE_LAUNCH(KID_GATEUP, (k_gateup_smem<BITS, N>), dim3(maxU, I / 64, 2 * KP),              \
+                   dim3(64 * kGUWaves), 0, s, f.table, E, f.offsets, f.sorted_pairs, K, f.x, f.x, \
+                   H, I, T * K, KP, c.scale_f16, gu);                                             \
+      } else {                                                                                    \
+        MOE_LAUNCH(KID_GATEUP, (k_gateup<BITS, N, 8>), dim3(maxU, I / 64, 2 * KP),                \
+                   dim3(64 * kGUWaves), 0, s, f.table, E, f.offsets, f.sorted_pairs, K, f.x, H,   \
+                   I, T * K, KP, c.scale_f16, gu);                                                \
+      }                                                                                           \
       break;
     switch (gpw_gu) {
       MOE_GU(1) MOE_GU(2) MOE_GU(3) MOE_GU(4) MOE_GU(5)
       default: return hipErrorInvalidValue;
     }
   #undef MOE_GU
+    float* hbuf = reinterpret_cast<float*>(f.ws + L.hdec);
+    uint16_t* hh = reinterpret_cast<uint16_t*>(hbuf);
+    uint16_t* hl = hh + (int64_t)T * K * I;
+    MOE_LAUNCH(KID_SWIGLU, k_swiglu, dim3(T * K), dim3(256), 0, s, gu, f.offsets, E, T * K, I, KP,
+               hh, hl);
   #define MOE_DN(N)                                                                               \
     case N:                                                                                       \
-      MOE_LAUNCH(KID_DOWN, (k_down<BITS, N>), dim3(maxU, H / 64), dim3(64 * kDNWaves), lds_dn, s, \
-                 f.table, E, f.offsets, f.sorted_pairs, H, I, T * K, KP, c.scale_f16, gu, pair_out);              \
+      if (T <= 2) {                                                                               \
+        MOE_LAUNCH(KID_DOWN, (k_down<BITS, N, 2>), dim3(maxU, H / 64), dim3(64 * kDNWaves), 0, s, \
+                   f.table, E, f.offsets, f.sorted_pairs, H, I, c.scale_f16, hh, hl, pair_out);   \
+      } else {                                                                                    \
+        MOE_LAUNCH(KID_DOWN, (k_down<BITS, N, 8>), dim3(maxU, H / 64), dim3(64 * kDNWaves), 0, s, \
+                   f.table, E, f.offsets, f.sorted_pairs, H, I, c.scale_f16, hh, hl, pair_out);   \
+      }                                                                                           \
       break;
     switch (gpw_dn) {
       MOE_DN(1) MOE_DN(2) MOE_DN(3) MOE_DN(4) MOE_DN(5) MOE_DN(6) MOE_DN(7) MOE_DN(8)

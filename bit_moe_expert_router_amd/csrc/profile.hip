@@ -18,7 +18,7 @@ namespace {
 
 const char* const kNames[KID_COUNT] = {"route_logits", "route_topk", "route_permute", "plan",
                                        "gateup",       "down",       "shared_gateup", "shared_down",
-                                       "combine",      "rmsnorm",    "zero",          "xprep"};
+                                       "combine",      "rmsnorm",    "zero",          "xprep",        "swiglu"};
 
 struct Rec {
   int kid;

@@ -175,7 +175,6 @@ __global__ __launch_bounds__(256) void k_logits_mfma(const uint16_t* __restrict_
 // ties to the lower id).  Lane k keeps pick k.  Weights: lane k < K computes
 // exp(l_k - l_0) in fp64; every lane adds the K terms in k order.
 constexpr int kMaxE = 1024;
-constexpr int kMaxPerLane = kMaxE / 64;
 
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int v, int fill) {
@@ -209,40 +208,60 @@ __device__ __forceinline__ int wave_min_i32(int v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
-// this lane's pick (lane < K) and its weight; -1 for other lanes
+// this lane's pick (lane < K) and its weight; -1 for other lanes.
+// Each lane first sorts its PER candidates (experts lane + 64i) by descending
+// logit with an odd-even transposition network (swaps only on a strictly larger
+// value, so equal logits keep ascending id order).  Round k then takes the wave
+// maximum of the lane heads; the lane holding it (the lowest id among several,
+// on exact ties) pops its head.
+template <int PER>
 __device__ __forceinline__ int wave_topk(const double* __restrict__ l, int E, int K, float* wk) {
   const int lane = threadIdx.x & 63;
-  const int per = (E + 63) / 64;
-  double v[kMaxPerLane];
+  double v[PER];
+  int id[PER];
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
+  for (int i = 0; i < PER; ++i) {
     const int e = lane + 64 * i;
-    v[i] = (i < per && e < E) ? l[e] : -INFINITY;
+    v[i] = e < E ? l[e] : -INFINITY;
+    id[i] = e < E ? e : 0x7FFFFFFF;
   }
+#pragma unroll
+  for (int r = 0; r < PER; ++r)
+#pragma unroll
+    for (int i = r & 1; i + 1 < PER; i += 2) {
+      const bool sw = v[i + 1] > v[i];
+      const double a = v[i], b2 = v[i + 1];
+      const int ia = id[i], ib = id[i + 1];
+      v[i] = sw ? b2 : a;
+      v[i + 1] = sw ? a : b2;
+      id[i] = sw ? ib : ia;
+      id[i + 1] = sw ? ia : ib;
+    }
   double my_l = -INFINITY;
   int my_id = -1;
   for (int k = 0; k < K; ++k) {
-    // local best: highest value, lowest id among equals (ids grow with i)
-    double bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-      const int e = lane + 64 * i;
-      if (i < per && e < E && v[i] > bv) {
-        bv = v[i];
-        bi = e;
-      }
+    const double m = wave_max_f64(v[0]);
+    const uint64_t hold = __ballot(v[0] == m && id[0] != 0x7FFFFFFF);
+    int win;
+    if (__popcll(hold) == 1) {
+      win = __ffsll((unsigned long long)hold) - 1;
+    } else {  // equal logits in several lanes: the lowest id wins
+      const int best = wave_min_i32(v[0] == m ? id[0] : 0x7FFFFFFF);
+      win = __ffsll((unsigned long long)__ballot(v[0] == m && id[0] == best)) - 1;
     }
-    const double m = wave_max_f64(bv);
-    const int id = wave_min_i32(bv == m ? bi : 0x7FFFFFFF);
-    if ((id & 63) == lane) {
+    const int pick = __builtin_amdgcn_readlane(id[0], win);
+    if (lane == win) {
 #pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i)
-        if (i == (id >> 6)) v[i] = -INFINITY;  // taken
+      for (int i = 0; i + 1 < PER; ++i) {
+        v[i] = v[i + 1];
+        id[i] = id[i + 1];
+      }
+      v[PER - 1] = -INFINITY;
+      id[PER - 1] = 0x7FFFFFFF;
     }
     if (lane == k) {
       my_l = m;
-      my_id = id;
+      my_id = pick;
     }
   }
   const double l0 = __shfl(my_l, 0);
@@ -253,6 +272,7 @@ __device__ __forceinline__ int wave_topk(const double* __restrict__ l, int E, in
   return lane < K ? my_id : -1;
 }
 
+template <int PER>
 __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits, int T, int E,
                                               int K, int32_t* __restrict__ ids,
                                               float* __restrict__ wout) {
@@ -260,7 +280,7 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits,
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   float wk;
-  const int id = wave_topk(logits + (int64_t)t * E, E, K, &wk);
+  const int id = wave_topk<PER>(logits + (int64_t)t * E, E, K, &wk);
   if (lane < K) {
     ids[t * K + lane] = id;
     wout[t * K + lane] = wk;
@@ -443,18 +463,85 @@ __global__ __launch_bounds__(64) void k_group_scatter(const int32_t* __restrict_
 
 // ---------------------------------------------------------------- top-k + grouping, small T
 // Decode batches (T <= 16, T * K <= 64): wave t picks the top-k of token t, then
-// the first wave groups the T*K pairs; one launch instead of two.
+// the first wave groups the T*K pairs, one pair per lane.  A pair's key is
+// (expert id, pair index); its sorted position is the number of smaller keys,
+// counted bit by bit from the top with one ballot per key bit.  Offsets: each
+// expert's first pair writes its pair count into a zeroed LDS histogram, which
+// a DPP prefix sum turns into the exclusive scan.  Integer only: bit-exact.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  // inclusive prefix sum over the 64 lanes (row prefix sums, then row carries)
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false); // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false); // row_bcast:31
+  return v;
+}
+
+__device__ __forceinline__ void wave_group_small(int id, int P, int E, int* cnt,
+                                                 int32_t* __restrict__ offsets,
+                                                 int32_t* __restrict__ sorted_pairs,
+                                                 int32_t* __restrict__ pair_pos) {
+  const int lane = threadIdx.x & 63;
+  int nbits = 0;
+  while ((1 << nbits) < E + 1) ++nbits;
+  const bool ok = lane < P && id >= 0 && id < E;
+  const int key = ok ? id : E;  // invalid pairs sort after every expert
+  const uint64_t lt = (1ull << lane) - 1ull;
+  const uint64_t live = __ballot(lane < P);
+  // lanes with a smaller key, and lanes with the same key
+  uint64_t eq = live;
+  int less = 0;
+  for (int b = nbits - 1; b >= 0; --b) {
+    const uint64_t bal = __ballot(lane < P && ((key >> b) & 1));
+    if ((key >> b) & 1) {
+      less += __popcll(eq & ~bal);
+      eq &= bal;
+    } else {
+      eq &= ~bal;
+    }
+  }
+  const int pos = less + __popcll(eq & lt);
+  if (ok) sorted_pairs[pos] = lane;
+  if (lane < P) pair_pos[lane] = ok ? pos : -1;
+  // histogram of the valid pairs, then the exclusive scan over the experts
+  const int per = (E + 64) / 64;  // entries 0..E
+  for (int i = 0; i < per; ++i) {
+    const int e = lane * per + i;
+    if (e <= E) cnt[e] = 0;
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the zeros land first
+  if (ok && (eq & lt) == 0) cnt[id] = __popcll(eq);
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  int c[17];
+  int loc = 0;
+#pragma unroll
+  for (int i = 0; i < 17; ++i) {
+    const int e = lane * per + i;
+    c[i] = (i < per && e <= E) ? cnt[e] : 0;
+    loc += c[i];
+  }
+  int run = wave_incl_scan(loc) - loc;
+#pragma unroll
+  for (int i = 0; i < 17; ++i) {
+    const int e = lane * per + i;
+    if (i < per && e <= E) offsets[e] = run;
+    run += c[i];
+  }
+}
+
+template <int PER>
 __global__ __launch_bounds__(1024) void k_topk_group_small(
     const double* __restrict__ logits, int T, int E, int K, int32_t* __restrict__ ids,
     float* __restrict__ wout, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
     int32_t* __restrict__ pair_pos) {
   __shared__ int32_t s_ids[64];
   __shared__ int cnt[kMaxE + 1];
-  __shared__ int run[kMaxE];
   const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
   if (t < T) {
     float wk;
-    const int id = wave_topk(logits + (int64_t)t * E, E, K, &wk);
+    const int id = wave_topk<PER>(logits + (int64_t)t * E, E, K, &wk);
     if (lane < K) {
       ids[t * K + lane] = id;
       wout[t * K + lane] = wk;
@@ -462,7 +549,10 @@ __global__ __launch_bounds__(1024) void k_topk_group_small(
     }
   }
   __syncthreads();
-  if (threadIdx.x < 64) wave_group(s_ids, T * K, E, cnt, run, offsets, sorted_pairs, pair_pos);
+  if (threadIdx.x < 64) {
+    const int P = T * K;
+    wave_group_small(lane < P ? s_ids[lane] : -1, P, E, cnt, offsets, sorted_pairs, pair_pos);
+  }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -478,12 +568,29 @@ hipError_t launch_route(const moe_cfg& c, const uint16_t* x, int T, const float*
     MOE_LAUNCH(KID_LOGITS, k_logits_mfma, dim3((E + kLE - 1) / kLE, (T + kLT - 1) / kLT), dim3(256),
                0, s, x, T, H, E, wr, bias, logits);
   }
+  const int per = (E + 63) / 64;
+#define MOE_PER_SWITCH(X)                                                    \
+  switch (per <= 8 ? per : 16) {                                             \
+    X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(16)                            \
+    default: return hipErrorInvalidValue;                                    \
+  }
   if (T <= 16 && P <= 64) {
-    MOE_LAUNCH(KID_TOPK, k_topk_group_small, dim3(1), dim3(64 * T), 0, s, logits, T, E, K,
-               ids, w, offsets, sorted_pairs, pair_pos);
+#define MOE_TGS(N)                                                                             \
+  case N:                                                                                      \
+    MOE_LAUNCH(KID_TOPK, k_topk_group_small<N>, dim3(1), dim3(64 * T), 0, s, logits, T, E, K,  \
+               ids, w, offsets, sorted_pairs, pair_pos);                                       \
+    break;
+    MOE_PER_SWITCH(MOE_TGS)
+#undef MOE_TGS
     return hipGetLastError();
   }
-  MOE_LAUNCH(KID_TOPK, k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, K, ids, w);
+#define MOE_TK(N)                                                                              \
+  case N:                                                                                      \
+    MOE_LAUNCH(KID_TOPK, k_topk<N>, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, K, ids, w); \
+    break;
+  MOE_PER_SWITCH(MOE_TK)
+#undef MOE_TK
+#undef MOE_PER_SWITCH
   if (P <= 4 * kGChunk) {
     MOE_LAUNCH(KID_PERMUTE, k_permute, dim3(1), dim3(64), 0, s, ids, P, E, offsets, sorted_pairs,
                pair_pos);
