@@ -36,6 +36,8 @@ WORKLOAD_TEXT = {
           "3-bit G128 bf16 scales, Zipf(1.1) router bias",
     "c3": "GLM-shaped MoE layer at decode batch 8 + bf16 shared expert (I 1536), expert pointer "
           "table remapped to a seeded slot permutation, Zipf(1.1) bias",
+    "c4": "42-layer stack of GLM-shaped MoE layers at decode batch 4 (RMSNorm glue, shared experts, "
+          "remapped tables, own Zipf bias per layer)",
     "c5": "8,192-token prefill chunk through one GLM-shaped MoE layer (3-bit G128), Zipf(1.1) bias",
 }
 
@@ -45,7 +47,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c5"])
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--tokens", type=int, default=None, help="batch (default: the workload's)")
     ap.add_argument("--uniform", action="store_true", help="no Zipf router bias")
     ap.add_argument("--layers", type=int, default=None,
@@ -82,7 +84,8 @@ def main():
         cfg = cfg.with_(zipf=False)
     T = cfg.tokens
     decode = T <= 64
-    L = a.layers or (16 if decode else 1)
+    stack = cfg.layers > 1
+    L = cfg.layers if stack else (a.layers or (16 if decode else 1))
 
     # ---------------------------------------------------------- resident inputs
     t0 = time.time()
@@ -99,18 +102,37 @@ def main():
     torch.cuda.synchronize()
     gen_s = time.time() - t0
 
+    if stack:
+        from bit_moe_expert_router_amd.layer import stack_forward
+        resid = torch.from_numpy(
+            synth.normal_f32(T * cfg.hidden, cfg.seed, 0, synth.SYN_X, 1.0).reshape(T, cfg.hidden)).to(dev)
+        ybuf = torch.empty((T, cfg.hidden), dtype=torch.int16, device=dev)
+        routers = [dl.router for dl in layers]
+        biases = [dl.bias for dl in layers]
+
     def step(l):
+        if stack:  # one pass through every layer of the stack
+            stack_forward(ml, resid, out, routers, biases, ybuf, out)
+            return
         dl = layers[l]
         r = ml.route(xd, dl.router, dl.bias)
         ml.forward(l, xd, r, out)
 
     # distinct experts per layer (deterministic: same x, same layer -> same routing)
     U = []
-    for l in range(L):
-        step(l)
+    if stack:
+        out.zero_()
+        seen = []
+        stack_forward(ml, resid, out, routers, biases, ybuf, out,
+                      on_layer=lambda l, y_, r, o_: seen.append(r.expert_offsets.clone()))
         torch.cuda.synchronize()
-        off = ml.rb.expert_offsets.cpu().numpy()
-        U.append(int((np.diff(off) > 0).sum()))
+        U = [int((np.diff(o.cpu().numpy()) > 0).sum()) for o in seen]
+    else:
+        for l in range(L):
+            step(l)
+            torch.cuda.synchronize()
+            off = ml.rb.expert_offsets.cpu().numpy()
+            U.append(int((np.diff(off) > 0).sum()))
 
     graphs = None
     if not a.eager:
@@ -118,11 +140,11 @@ def main():
         s = torch.cuda.Stream(device=dev)
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            for l in range(L):
+            for l in range(1 if stack else L):
                 step(l)  # warm the capture stream
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
-        for l in range(L):
+        for l in range(1 if stack else L):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 step(l)
@@ -131,7 +153,7 @@ def main():
 
     def run(i):
         if graphs is not None:
-            graphs[i % L].replay()
+            graphs[i % len(graphs)].replay()
         else:
             step(i % L)
 
@@ -156,16 +178,18 @@ def main():
     eb = synth.expert_bytes(cfg)
     glay, ulay, dlay = synth.expert_layouts(cfg)
     kern = {}
+    kt_steps = min(a.steps, 10) if stack else a.steps
     if not a.no_kernel_timing:
         moe.moe_profile_read()  # drop anything recorded before
         moe.moe_profile_enable(True)
-        for i in range(a.steps):
+        for i in range(kt_steps):
             step(i % L)
         torch.cuda.synchronize()
         moe.moe_profile_enable(False)
         kern = moe.moe_profile_read()
-    # algorithmic bytes over the kernel-timing pass (same step sequence)
-    u_steps = [U[i % L] for i in range(a.steps)]
+    # algorithmic bytes over the kernel-timing pass (same step sequence); a stack
+    # step launches every layer once
+    u_steps = [U[i % L] for i in range(kt_steps)] if not stack else [u for _ in range(kt_steps) for u in U]
     gu_bytes = sum(u * (glay.nbytes + ulay.nbytes) for u in u_steps)
     dn_bytes = sum(u * dlay.nbytes for u in u_steps)
     roof = None
@@ -194,14 +218,14 @@ def main():
                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4) if ach else None,
                     "traffic": None, "kernel": "k_gateup (gate+up GEMV, SwiGLU)",
                     "avg_us": round(gu_ms / gu_n * 1e3, 2) if gu_n else None,
-                    "bytes_per_launch": round(gu_bytes / a.steps)}
+                    "bytes_per_launch": round(gu_bytes / len(u_steps))}
             if dn_ms:
                 extra["down_GBs"] = round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1)
         extra["kernels_us"] = {k: round(v[0] / v[1] * 1e3, 2) for k, v in kern.items() if v[1]}
         tot_ms = sum(v[0] for v in kern.values())
-        extra["expert_bytes_per_step"] = round((gu_bytes + dn_bytes) / a.steps)
+        extra["expert_bytes_per_step"] = round((gu_bytes + dn_bytes) / kt_steps)
         extra["expert_GBs_over_kernel_time"] = round((gu_bytes + dn_bytes) / (tot_ms * 1e-3) / 1e9, 1)
-    extra["expert_GBs_over_step"] = round((gu_bytes + dn_bytes) / a.steps / (ms_step * 1e-3) / 1e9, 1)
+    extra["expert_GBs_over_step"] = round((gu_bytes + dn_bytes) / kt_steps / (ms_step * 1e-3) / 1e9, 1)
     extra["distinct_experts_per_step"] = round(float(np.mean(u_steps)), 2)
     extra["graph_replay"] = graphs is not None
     extra["input_gen_s"] = round(gen_s, 1)
@@ -216,7 +240,7 @@ def main():
     # ---------------------------------------------------------- CPU oracle baseline
     cpu = None
     if a.cpu_seconds > 0:
-        cpu = cpu_baseline(cfg, L, a.cpu_seconds)
+        cpu = cpu_baseline(cfg, L, a.cpu_seconds, layers_per_step=L if stack else 1)
 
     res = {
         "metric": METRIC,
@@ -244,11 +268,12 @@ def main():
     ml.close()
 
 
-def cpu_baseline(cfg, L, budget_s):
+def cpu_baseline(cfg, L, budget_s, layers_per_step=1):
     """fp64 oracle (the test reference, untuned) on the host cores: routing, every
-    pick's expert FFN and the combine of one batch per step, rotating over the
+    pick's expert FFN and the combine of one batch per layer, rotating over the
     same layers; timed until the budget is spent.  Batches above 16 tokens are
-    sampled: the first 16 tokens of the batch are routed and computed per step."""
+    sampled: the first 16 tokens of the batch are routed and computed per layer.
+    A step of a stack is layers_per_step such layers."""
     import numpy as np
 
     import oracle
@@ -275,11 +300,12 @@ def cpu_baseline(cfg, L, budget_s):
         spent += time.perf_counter() - t0
         steps += 1
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(T * steps / spent, 3), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{steps} steps of {T} token(s) of the same workload (routing + every "
-                      f"pick's fp64 expert FFN + combine, rotating over {min(L, steps)} layers), "
-                      f"{spent:.1f} s, {threads} OpenMP threads"}
+    return {"value": round(T * steps / spent / layers_per_step, 3), "unit": "tokens/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{steps} layer evaluations of {T} token(s) of the same workload (routing + "
+                      f"every pick's fp64 expert FFN + combine, rotating over {min(L, steps)} "
+                      f"layers; a step is {layers_per_step} layer(s)), {spent:.1f} s, "
+                      f"{threads} OpenMP threads"}
 
 
 if __name__ == "__main__":

@@ -81,3 +81,23 @@ class MoELayer:
     def rmsnorm_bf16(self, resid, add, y_bf16, eps=1e-6, stream=None):
         moe_rmsnorm_bf16(self.ctx, resid, add, resid.shape[0], eps, y_bf16, stream)
         return y_bf16
+
+
+def stack_forward(ml: MoELayer, resid, add, routers, biases, y, out, on_layer=None, stream=None):
+    """One pass of a stack of MoE layers on the residual stream:
+    x <- x + MoE_l(bf16(RMSNorm(x))) for l = 0 .. L-1.
+
+    resid: fp32 [T, H], updated in place; add: fp32 [T, H] or None, the output
+    still to be added to resid before the first layer (the previous pass's last
+    layer).  Each layer's output lands in `out` and is added to resid by the next
+    layer's normalisation, so after the pass resid + out is the stack's output.
+    y: bf16 [T, H] scratch for the normalised layer input.  on_layer(l, y, r,
+    out) is called after layer l is enqueued.
+    """
+    for l in range(len(routers)):
+        ml.rmsnorm_bf16(resid, add if l == 0 else out, y, stream=stream)
+        r = ml.route(y, routers[l], biases[l], stream=stream)
+        ml.forward(l, y, r, out, stream=stream)
+        if on_layer is not None:
+            on_layer(l, y, r, out)
+    return resid, out
