@@ -168,10 +168,66 @@ struct UnitCodec<4> {
   }
 };
 
+// ---------------------------------------------------------------- unit loads (decode)
+// A 16-bit scale is fetched as the aligned dword that contains it (the scales
+// region is 256-byte aligned, so the dword lies inside it) and selected at use.
+__device__ __forceinline__ uint32_t load_scale_dword(gu16_t sc, int64_t idx) {
+  typedef const uint32_t __attribute__((address_space(1)))* gu32_t;
+  return *(gu32_t)(sc + (idx & ~(int64_t)1));
+}
+__device__ __forceinline__ uint16_t scale_from_dword(uint32_t w, int64_t idx) {
+  return (uint16_t)(w >> ((idx & 1) * 16));
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int BITS>
+__device__ __forceinline__ void load_unit4(gbytes_t codes, int64_t tile, int lane,
+                                           u32x4 (&w)[UnitCodec<BITS>::CHUNKS]) {
+  using C = UnitCodec<BITS>;
+  typedef const u32x4 __attribute__((address_space(1)))* gu4_t;
+#pragma unroll
+  for (int j = 0; j < C::CHUNKS; ++j)
+    w[j] = *(gu4_t)(codes + (tile * C::CHUNKS + j) * 1024 + 16 * lane);
+}
+
+// The unit's words, passed through an empty asm so that the decode that follows
+// stays inside the token loop (hoisting every group's decoded pairs out of it
+// would need GPW * 128 registers).
+template <int BITS>
+__device__ __forceinline__ void unit_words(const u32x4 (&c)[UnitCodec<BITS>::CHUNKS],
+                                           uint32_t (&w)[UnitCodec<BITS>::WORDS]) {
+#pragma unroll
+  for (int j = 0; j < UnitCodec<BITS>::CHUNKS; ++j) {
+    w[4 * j + 0] = c[j].x;
+    w[4 * j + 1] = c[j].y;
+    w[4 * j + 2] = c[j].z;
+    w[4 * j + 3] = c[j].w;
+  }
+#pragma unroll
+  for (int k = 0; k < UnitCodec<BITS>::WORDS; ++k) asm volatile("" : "+v"(w[k]));
+}
+
+// Sum over the 64 lanes in a fixed order (row prefix sums by DPP, then the row
+// totals), returned to every lane; deterministic, no LDS traffic.
+template <int CTRL>
+__device__ __forceinline__ float dpp_shift(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int BITS>
+__device__ __forceinline__ float wave_sum_uniform(float v) {
+  v += dpp_shift<0x111>(v);  // row_shr:1
+  v += dpp_shift<0x112>(v);  // row_shr:2
+  v += dpp_shift<0x114>(v);  // row_shr:4
+  v += dpp_shift<0x118>(v);  // row_shr:8
+  v += dpp_shift<0x142>(v);  // row_bcast:15
+  v += dpp_shift<0x143>(v);  // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // ---------------------------------------------------------------- workspace
 // counters reserved for cross-block signalling (kept zero between calls)
 constexpr int kCounters = 1024;
-constexpr int kMaxKParts = 4;  // gate/up reduction-dimension split (H/G <= 80)
 
 // Batches up to this many tokens run the GEMV (decode) kernels; larger ones the
 // matrix-core (prefill) kernels when the shape allows them.
@@ -191,15 +247,19 @@ struct WsLayout {
   int64_t counters;   // int32[kCounters]: zero between calls
   int64_t logits;     // double[T][E]
   int64_t ghist;      // int32[ceil(P/1024)][E]: per-chunk expert counts, then bases (grouping)
-  int64_t gu;         // decode: float[2*KP][P][I]: partial gate and up products, rows by sorted position
+  int64_t act;        // decode: int32 U (64-byte header), then the active-expert list (40 B each)
+  int64_t gpart;      // decode: float[2*NCH][P][I]: gate then up partial products per
+                      //   chunk of reduction groups, rows by sorted position
   int64_t hdec;       // decode: bf16[2][P][I]: h hi rows, then h lo rows, by sorted position
+  int64_t dpart;      // decode: float[NCHd][P][H]: down partial products per chunk, rows by pair
   int64_t x16;        // prefill: fp16[T][H] activations scaled by 2^-xshift[t]
   int64_t xshift;     // prefill: int32[T]
   int64_t h16;        // prefill: fp16[P][I] h rows by sorted position
   int64_t tiles;      // prefill: int32[1 + 2*max_tiles] tile plan
   int64_t pair_out;   // float[P][H] (used when the caller passes no pair_out)
+  int64_t sh_part;    // float[2*4][T][Is]: shared gate and up partial sums per slice
   int64_t sh_h;       // float[T][Is]: shared expert h
-  int64_t sh_out;     // float[T][H]: shared expert output
+  int64_t sh_out;     // float[2][T][H]: shared expert output slices
   int64_t total;
 };
 
@@ -216,15 +276,20 @@ __host__ inline WsLayout ws_layout(const moe_cfg& c, int T) {
   L.logits = take((int64_t)T * c.n_experts * 8);
   L.ghist = take((P + 1023) / 1024 * c.n_experts * 4);
   const bool pf = prefill_eligible(c, T);
-  L.gu = take(pf ? 0 : 2 * kMaxKParts * P * c.inter * 4);
+  // chunks of 4 (gate/up) and 3 (down) reduction groups per decode work item
+  const int64_t nch_gu = (c.hidden / c.group + 3) / 4, nch_dn = (c.inter / c.group + 2) / 3;
+  L.act = take(pf ? 0 : 64 + 40 * (int64_t)c.n_experts);
+  L.gpart = take(pf ? 0 : 2 * nch_gu * P * c.inter * 4);
   L.hdec = take(pf ? 0 : 2 * P * c.inter * 2);
+  L.dpart = take(pf ? 0 : nch_dn * P * c.hidden * 4);
   L.x16 = take(pf ? (int64_t)T * c.hidden * 2 : 0);
   L.xshift = take(pf ? (int64_t)T * 4 : 0);
   L.h16 = take(pf ? P * c.inter * 2 : 0);
   L.tiles = take(pf ? (1 + 2 * prefill_max_tiles(P, c.n_experts)) * 4 : 0);
-  L.pair_out = take(P * c.hidden * 4);
+  L.pair_out = take(pf ? P * c.hidden * 4 : 0);
+  L.sh_part = take(8 * (int64_t)T * c.shared_inter * 4);
   L.sh_h = take((int64_t)T * c.shared_inter * 4);
-  L.sh_out = take((int64_t)T * c.hidden * 4);
+  L.sh_out = take(2 * (int64_t)T * c.hidden * 4);
   L.total = o;
   return L;
 }
@@ -264,6 +329,10 @@ struct FwdArgs {
 };
 
 hipError_t launch_prefill(const FwdArgs& f, const WsLayout& L, float* pair_out, hipStream_t s);
+hipError_t launch_decode(const FwdArgs& f, const WsLayout& L, float* shared_out, int nsh,
+                         hipStream_t s);
+hipError_t launch_shared(const FwdArgs& f, const WsLayout& L, hipStream_t s, float** out,
+                         int* nslices);
 hipError_t launch_route(const moe_cfg& c, const uint16_t* x, int T, const float* wr,
                         const float* bias, int32_t* ids, float* w, int32_t* offsets,
                         int32_t* sorted_pairs, int32_t* pair_pos, double* logits,

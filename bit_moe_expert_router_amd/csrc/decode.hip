@@ -1,0 +1,801 @@
+// decode.hip -- the routed experts of a decode batch (at most 64 tokens) as
+// persistent, wave-level GEMVs over packed low-bit weights.
+//
+// Each picked expert runs gate, up and down matrices reached through the layer's
+// pointer table (page "GLM-5.3-Flash EXL3 3.05bpw on 1x RTX PRO 6000 - GPU expert
+// cache, host-RAM streaming", field config.expert_cache.mechanism); a decode step
+// reads every picked expert's bytes once, so HBM bandwidth bounds it.
+//
+// Work decomposition.  A plan kernel lists the active experts (those owning at
+// least one pair) with their pair segment and blob pointers.  The GEMV kernels
+// then run a fixed grid of waves that take work items in turn: an item is (active
+// expert, 64-row strip, matrix, chunk of GPW reduction groups).  A wave requests
+// the item's codes and scales (one 16-byte load per chunk of a 64-row tile: 1,024
+// contiguous bytes per wave) and the activations of its groups for up to XT of
+// the expert's tokens (into the wave's own LDS region), then forms the partial
+// products of its 64 rows for every token and writes them to a partial buffer,
+// one slice per chunk.  No item waits on another: there are no block barriers
+// and no cross-wave reductions, and a wave that finishes an item starts the
+// next one at once, so the weight stream stays in flight.  The slices are added
+// in chunk order by the SwiGLU pass (gate/up) and by the combine (down): results
+// are deterministic.
+//
+// Arithmetic (as in the unit codec): codes are expanded two at a time into bf16
+// (B + c) and multiplied with bf16 activation pairs by v_dot2_f32_bf16 in fp32; the
+// per-group constant sum_k (B_k + z) x_k is subtracted, then the group scale
+// applied.  The down matrix takes h as bf16 hi + bf16 remainder (two products per
+// code pair).
+#include <algorithm>
+
+#include "common.h"
+
+namespace moe {
+
+typedef uint32_t u32x4d __attribute__((ext_vector_type(4)));
+
+struct ActEntry {
+  int32_t e, seg0, n, pad;
+  const void* ptr[3];  // gate, up, down
+};
+
+// ---------------------------------------------------------------- plan
+// act_hdr[0] = U, the number of experts owning at least one pair; act[a] for
+// a < U in ascending expert id.
+__global__ __launch_bounds__(1024) void k_plan_decode(const int32_t* __restrict__ offsets,
+                                                      const moe_expert_ref* __restrict__ table,
+                                                      int E, int32_t* __restrict__ act_hdr,
+                                                      ActEntry* __restrict__ act) {
+  __shared__ int wsum[16];
+  const int e = threadIdx.x, lane = e & 63, wv = e >> 6;
+  const int lo = e < E ? offsets[e] : 0;
+  const int n = e < E ? offsets[e + 1] - lo : 0;
+  const int f = n > 0 ? 1 : 0;
+  int inc = f;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) wsum[wv] = inc;
+  __syncthreads();
+  int a = inc - f, total = 0;
+  for (int w = 0; w < 16; ++w) {
+    if (w < wv) a += wsum[w];
+    total += wsum[w];
+  }
+  if (f) {
+    const moe_expert_ref r = table[e];
+    ActEntry ent;
+    ent.e = e;
+    ent.seg0 = lo;
+    ent.n = n;
+    ent.pad = 0;
+    ent.ptr[0] = r.gate;
+    ent.ptr[1] = r.up;
+    ent.ptr[2] = r.down;
+    act[a] = ent;
+  }
+  if (e == 0) act_hdr[0] = total;
+}
+
+// ---------------------------------------------------------------- GEMV
+// MODE 0: gate and up (R = I rows, reduction D = H); activations are the bf16
+// token rows xa[T][H]; out[(m*NCH + ch)*P + pos][row] (pos = sorted position).
+// MODE 1: down (R = H, D = I); activations are h hi rows xa[P][I] and lo rows
+// xb[P][I] by sorted position; out[ch*P + p][row] (p = pair id t*K + k).
+template <int BITS, int GPW, int XT, int MODE, int WPS>
+__global__ __launch_bounds__(256, WPS) void k_gemv(
+    const int32_t* __restrict__ act_hdr, const ActEntry* __restrict__ act,
+    const int32_t* __restrict__ sorted_pairs, int K, const uint16_t* __restrict__ xa,
+    const uint16_t* __restrict__ xb, int R, int D, int P, int scale_f16, float* __restrict__ out) {
+  using C = UnitCodec<BITS>;
+  constexpr int NM = MODE == 0 ? 2 : 1;        // matrices per expert
+  constexpr int NS = MODE == 0 ? 1 : 2;        // activation rows per token (x; or h hi, lo)
+  constexpr int PC = C::G / 8;                 // 16-byte pieces per group row
+  constexpr int NQ = XT * GPW * NS * PC;       // pieces of a staged chunk of tokens
+  constexpr int IT = (NQ + 63) / 64;
+  constexpr int XW = XT * GPW * NS * C::PAIRS;  // uint32 per wave: [token][group][row][pair]
+  __shared__ __align__(16) uint32_t xs_all[4 * XW];
+  typedef const u32x4d __attribute__((address_space(1)))* g4;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint32_t* xs = xs_all + wv * XW;
+  const int ng = D / C::G, NCH = (ng + GPW - 1) / GPW, nstrips = R / 64;
+  const int per_a = nstrips * NM * NCH;
+  const int total = act_hdr[0] * per_a;
+  const int nw = gridDim.x * 4;
+  const float off = lane < C::PAIRS ? C::pair_off(lane) : 0.f;
+  const MatGeom gm{R, D, BITS, C::G};
+
+  for (int item = blockIdx.x * 4 + wv; item < total; item += nw) {
+    const int a = item / per_a, r0 = item - a * per_a;
+    const int strip = r0 / (NM * NCH), r1 = r0 - strip * (NM * NCH);
+    const int m = r1 / NCH, ch = r1 - m * NCH;
+    const int seg0 = act[a].seg0, n_e = act[a].n;
+    const gbytes_t mat = as_global(act[a].ptr[MODE == 0 ? m : 2]);
+    const gu16_t msc = (gu16_t)(mat + gm.scales_off());
+    const int row = strip * 64 + lane;
+    const int g0 = ch * GPW, g1 = min(ng, g0 + GPW);
+    // pair id of each of the expert's first 64 positions (lane = position)
+    int pl = sorted_pairs[seg0 + min(lane, n_e - 1)];
+
+    // the item's codes and scales (group index clamped, not branched on)
+    u32x4 cw[GPW][C::CHUNKS];
+    uint32_t sr[GPW];
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+      const int g = min(g0 + i, g1 - 1);
+      load_unit4<BITS>(mat, (int64_t)strip * ng + g, lane, cw[i]);
+      sr[i] = load_scale_dword(msc, (int64_t)row * ng + g);
+    }
+
+    for (int c0 = 0; c0 < n_e; c0 += XT) {
+      if (c0 > 0 && c0 % 64 == 0) pl = sorted_pairs[seg0 + c0 + min(lane, n_e - c0 - 1)];
+      const int nt = min(n_e - c0, XT);
+      // activations of tokens c0 .. c0+nt-1 for the item's groups
+      u32x4d v[IT];
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int q = min(it * 64 + lane, NQ - 1);
+        const int j = min(q / (GPW * NS * PC), nt - 1), i = (q / (NS * PC)) % GPW;
+        const int sel = (q / PC) % NS, pc = q % PC;
+        const int g = min(g0 + i, g1 - 1);
+        const uint16_t* src;
+        if (MODE == 0) {
+          const int tok = __shfl(pl, (c0 % 64) + j) / K;
+          src = xa + (int64_t)tok * D + g * C::G + 8 * pc;
+        } else {
+          src = (sel ? xb : xa) + (int64_t)(seg0 + c0 + j) * D + g * C::G + 8 * pc;
+        }
+        v[it] = *(g4)(as_global(src));
+      }
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int q = it * 64 + lane;
+        if (q < NQ) *reinterpret_cast<u32x4d*>(xs + 4 * q) = v[it];
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's own LDS writes
+
+      for (int jp = 0; jp < nt; jp += 2) {
+        const bool two = jp + 1 < nt;
+        const int j1 = two ? jp + 1 : jp;
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < GPW; ++i) {
+          if (g0 + i < g1) {
+            const uint32_t* x0 = xs + (jp * GPW + i) * NS * C::PAIRS;
+            const uint32_t* x1 = xs + (j1 * GPW + i) * NS * C::PAIRS;
+            uint32_t sraw = sr[i];
+            asm volatile("" : "+v"(sraw));  // convert here, not hoisted ahead of the loads
+            const float sc =
+                scale_to_f32(scale_from_dword(sraw, (int64_t)row * ng + g0 + i), scale_f16);
+            // offset sums of the activations over the group (every staged row)
+            auto osum = [&](const uint32_t* xr) {
+              float t = 0.f;
+#pragma unroll
+              for (int s = 0; s < NS; ++s) {
+                const uint32_t pr = lane < C::PAIRS ? xr[s * C::PAIRS + lane] : 0u;
+                t += bf16_to_f32((uint16_t)pr) + bf16_to_f32((uint16_t)(pr >> 16));
+              }
+              return wave_sum_uniform<BITS>(off * t);
+            };
+            uint32_t w[C::WORDS];
+            unit_words<BITS>(cw[i], w);
+            float d0 = 0.f, d1 = 0.f;
+            const float k0 = osum(x0);
+            if (two) {
+              const float k1 = osum(x1);
+              C::for_each_pair(w, [&](int Pp, uint32_t pr) {
+                if (NS == 2) {
+                  d0 = dot2_bf16(pr, x0[C::PAIRS + Pp], dot2_bf16(pr, x0[Pp], d0));
+                  d1 = dot2_bf16(pr, x1[C::PAIRS + Pp], dot2_bf16(pr, x1[Pp], d1));
+                } else {
+                  d0 = dot2_bf16(pr, x0[Pp], d0);
+                  d1 = dot2_bf16(pr, x1[Pp], d1);
+                }
+              });
+              a1 = fmaf(sc, d1 - k1, a1);
+            } else {
+              C::for_each_pair(w, [&](int Pp, uint32_t pr) {
+                if (NS == 2) d0 = dot2_bf16(pr, x0[C::PAIRS + Pp], dot2_bf16(pr, x0[Pp], d0));
+                else d0 = dot2_bf16(pr, x0[Pp], d0);
+              });
+            }
+            a0 = fmaf(sc, d0 - k0, a0);
+          }
+        }
+        if (MODE == 0) {
+          float* o = out + ((int64_t)(m * NCH + ch) * P + seg0 + c0 + jp) * R + row;
+          o[0] = a0;
+          if (two) o[R] = a1;
+        } else {
+          const int p0 = __builtin_amdgcn_readlane(pl, (c0 + jp) % 64);
+          out[((int64_t)ch * P + p0) * R + row] = a0;
+          if (two) {
+            const int p1 = __builtin_amdgcn_readlane(pl, (c0 + jp + 1) % 64);
+            out[((int64_t)ch * P + p1) * R + row] = a1;
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- one or two tokens
+// Batches of one or two tokens have a single token pass per expert, and the
+// latency chain of the step dominates; they keep a block-level schedule with one
+// kernel launch fewer: block (a, strip, m*KP + kp) finds the a-th active expert
+// itself (one round trip for the offsets and the table entries together), its
+// four waves take groups g0 + wave + 4*i of part kp of the reduction, and the
+// waves' sums meet in LDS.
+constexpr int kGUWaves = 4;
+constexpr int kTokPerPass = 2;
+constexpr int kMaxKParts = 4;
+
+// ---------------------------------------------------------------- active experts
+// The a-th expert (ascending logical id) that owns at least one pair, the number
+// U of such experts, its segment of the grouping and its table entry.
+// Wave-cooperative (every lane returns the same values).  Each lane loads the
+// offsets and the table entries of its candidate experts lane + 64*i in the same
+// round trip, so the expert's weight addresses are known after one memory
+// latency instead of two.  E <= 1024.
+struct Active {
+  int e;     // -1 if a >= U
+  int U;
+  int seg0;  // first sorted position of the expert's pairs
+  int n;     // number of pairs
+  const void* ptr[3];  // gate, up, down
+};
+
+__device__ __forceinline__ Active find_active(const int32_t* __restrict__ offsets,
+                                              const moe_expert_ref* __restrict__ table, int E,
+                                              int a) {
+  const int lane = threadIdx.x & 63;
+  constexpr int kSpec = 5;  // candidates per lane whose table entry is fetched up front
+  const int nch = (E + 63) / 64;
+  int lo[16], hi[16];
+  moe_expert_ref ref[kSpec];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i < nch) {  // uniform
+      const int e = lane + 64 * i;
+      lo[i] = (e < E) ? offsets[e] : 0;
+      hi[i] = (e < E) ? offsets[e + 1] : 0;
+      if (i < kSpec) ref[i] = e < E ? table[e] : moe_expert_ref{nullptr, nullptr, nullptr};
+    }
+  }
+  Active r{-1, 0, 0, 0, {nullptr, nullptr, nullptr}};
+  int U = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i < nch) {
+      const bool nz = hi[i] > lo[i];
+      const uint64_t bal = __ballot(nz);
+      const int cnt = __popcll(bal);
+      if (r.e < 0 && a < U + cnt) {  // uniform: the a-th active expert is in this chunk
+        // lane holding it: the (a-U)-th set bit of bal
+        uint64_t m = bal;
+        for (int k = 0; k < a - U; ++k) m &= m - 1;
+        const int src = __ffsll((unsigned long long)m) - 1;
+        r.e = 64 * i + src;
+        r.seg0 = __shfl(lo[i], src);
+        r.n = __shfl(hi[i], src) - r.seg0;
+        if (i < kSpec) {
+          r.ptr[0] = (const void*)__shfl((long long)ref[i].gate, src);
+          r.ptr[1] = (const void*)__shfl((long long)ref[i].up, src);
+          r.ptr[2] = (const void*)__shfl((long long)ref[i].down, src);
+        } else {
+          const moe_expert_ref t = table[r.e];
+          r.ptr[0] = t.gate;
+          r.ptr[1] = t.up;
+          r.ptr[2] = t.down;
+        }
+      }
+      U += cnt;
+    }
+  }
+  r.U = U;
+  return r;
+}
+
+// Batches of one or two tokens (a single pass): the activations take the scalar
+// path instead (s_load into SGPRs, the second operand of v_dot2_f32_bf16), which
+// keeps the kernel at three waves per SIMD so the whole weight stream of a
+// decode step is in flight at once; the offset sums come from vector loads that
+// are requested before the weights.
+template <int BITS, int GPW>
+__global__ __launch_bounds__(256, 2) void k_gateup_smem(
+    const moe_expert_ref* __restrict__ table, int E, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_pairs, int K,
+    const uint16_t* __restrict__ x,  // read-only: dot operands through scalar loads
+    const uint16_t* x_vec,           // the same activations; not restrict, so that its vector
+                                     // loads stay ahead of the weight loads
+    int H, int I,
+    int P, int KP, int scale_f16, float* __restrict__ gu) {
+  using C = UnitCodec<BITS>;
+  __shared__ float red[kGUWaves][kTokPerPass][64];
+  const int ng = H / C::G;
+
+  const Active act = find_active(offsets, table, E, blockIdx.x);
+  if (act.e < 0) return;
+  const int seg0 = __builtin_amdgcn_readfirstlane(act.seg0);
+  const int n_e = __builtin_amdgcn_readfirstlane(act.n);
+  const int strip = blockIdx.y, m = blockIdx.z / KP, kp = blockIdx.z % KP;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const MatGeom gm{I, H, BITS, C::G};
+  const gbytes_t mat = as_global(m ? act.ptr[1] : act.ptr[0]);
+  const gu16_t msc = (gu16_t)(mat + gm.scales_off());
+  const int row = strip * 64 + lane;
+  const int gpb = (ng + KP - 1) / KP, g0 = kp * gpb, g1 = min(ng, g0 + gpb);
+  const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
+  const uint32_t* xv32 = reinterpret_cast<const uint32_t*>(x_vec);
+
+  // activation pairs of this wave's groups for the offset sums (lane = pair),
+  // requested before the weights so that their waits never wait for the weights
+  auto load_xo = [&](int t, uint32_t (&xo)[GPW]) {
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+      const int g = min(g0 + wv + kGUWaves * i, g1 - 1);
+      const int pl = lane < C::PAIRS ? lane : 0;
+      xo[i] = xv32[((int64_t)t * H + g * C::G) / 2 + pl];
+    }
+  };
+  int t0 = sorted_pairs[seg0] / K;
+  int t1 = n_e > 1 ? sorted_pairs[seg0 + 1] / K : t0;
+  uint32_t xo0[GPW], xo1[GPW];
+  load_xo(t0, xo0);
+  load_xo(t1, xo1);
+  asm volatile("" ::: "memory");
+
+  // weights: all groups of this wave at once (group index clamped, not branched
+  // on, so that the waits the compiler places stay exact)
+  u32x4 cw[GPW][C::CHUNKS];
+  uint32_t sr[GPW];  // the aligned dword holding the scale (any 16-bit handling here would wait)
+#pragma unroll
+  for (int i = 0; i < GPW; ++i) {
+    const int g = min(g0 + wv + kGUWaves * i, g1 - 1);
+    load_unit4<BITS>(mat, (int64_t)strip * ng + g, lane, cw[i]);
+    sr[i] = load_scale_dword(msc, (int64_t)row * ng + g);
+  }
+  asm volatile("" ::: "memory");
+
+  for (int b0 = 0; b0 < n_e; b0 += kTokPerPass) {
+    const bool two = b0 + 1 < n_e;
+    if (b0 > 0) {
+      t0 = sorted_pairs[seg0 + b0] / K;
+      t1 = two ? sorted_pairs[seg0 + b0 + 1] / K : t0;
+      load_xo(t0, xo0);
+      load_xo(t1, xo1);
+    }
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+      const int g = g0 + wv + kGUWaves * i;
+      if (g < g1) {
+        const uint32_t* x0 = x32 + ((int64_t)t0 * H + g * C::G) / 2;
+        const uint32_t* x1 = x32 + ((int64_t)t1 * H + g * C::G) / 2;
+        uint32_t sraw = sr[i];
+        asm volatile("" : "+v"(sraw));  // convert here, not hoisted ahead of the loads
+        const float sc = scale_to_f32(scale_from_dword(sraw, (int64_t)row * ng + g), scale_f16);
+        uint32_t w[C::WORDS];
+        float d0 = 0.f, d1 = 0.f;
+        unit_words<BITS>(cw[i], w);
+        if (two) {
+          C::for_each_pair(w, [&](int Pp, uint32_t pr) {
+            d0 = dot2_bf16(pr, x0[Pp], d0);
+            d1 = dot2_bf16(pr, x1[Pp], d1);
+          });
+          a1 = fmaf(sc, d1, a1);
+        } else {
+          C::for_each_pair(w, [&](int Pp, uint32_t pr) { d0 = dot2_bf16(pr, x0[Pp], d0); });
+        }
+        a0 = fmaf(sc, d0, a0);
+      }
+    }
+    // subtract sum_g s_g * (offset sum of group g)
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+      const int g = g0 + wv + kGUWaves * i;
+      if (g < g1) {
+        uint32_t sraw = sr[i];
+        asm volatile("" : "+v"(sraw));
+        const float sc = scale_to_f32(scale_from_dword(sraw, (int64_t)row * ng + g), scale_f16);
+        const float off = lane < C::PAIRS ? C::pair_off(lane) : 0.f;
+        const float c0 = wave_sum_uniform<BITS>(
+            off * bf16_to_f32((uint16_t)xo0[i]) + off * bf16_to_f32((uint16_t)(xo0[i] >> 16)));
+        a0 = fmaf(-sc, c0, a0);
+        if (two) {
+          const float c1 = wave_sum_uniform<BITS>(
+              off * bf16_to_f32((uint16_t)xo1[i]) + off * bf16_to_f32((uint16_t)(xo1[i] >> 16)));
+          a1 = fmaf(-sc, c1, a1);
+        }
+      }
+    }
+    red[wv][0][lane] = a0;
+    red[wv][1][lane] = a1;
+    lds_barrier();
+    if (wv < (two ? 2 : 1)) {
+      const int j = wv;
+      float y = 0.f;
+#pragma unroll
+      for (int w = 0; w < kGUWaves; ++w) y += red[w][j][lane];
+      gu[((int64_t)blockIdx.z * P + seg0 + b0 + j) * I + row] = y;
+    }
+    lds_barrier();
+  }
+}
+
+// SwiGLU of the one/two-token path (KP partial products per matrix)
+// h of every grouped pair position: h = silu(sum_q g_q) * (sum_q u_q), parts
+// added in kp order, kept as bf16 hi + bf16 remainder (h to ~2^-16 relative):
+// hh[pos][k], hl[pos][k].  One block per position; positions past the grouped
+// pairs (ids left out) are skipped.
+__global__ __launch_bounds__(256) void k_swiglu_kp(const float* __restrict__ gu,
+                                                const int32_t* __restrict__ offsets, int E, int P,
+                                                int I, int KP, uint16_t* __restrict__ hh,
+                                                uint16_t* __restrict__ hl) {
+  const int pos = blockIdx.x;
+  if (pos >= offsets[E]) return;
+  const int I4 = I / 4;
+  const float4* g4 = reinterpret_cast<const float4*>(gu);
+  for (int k4 = threadIdx.x; k4 < I4; k4 += 256) {
+    float4 pg[kMaxKParts], pu[kMaxKParts];
+#pragma unroll
+    for (int q = 0; q < kMaxKParts; ++q) {
+      const int qq = min(q, KP - 1);
+      pg[q] = g4[((int64_t)qq * P + pos) * I4 + k4];
+      pu[q] = g4[((int64_t)(KP + qq) * P + pos) * I4 + k4];
+    }
+    float4 g = pg[0], u = pu[0];
+#pragma unroll
+    for (int q = 1; q < kMaxKParts; ++q)
+      if (q < KP) {
+        g.x += pg[q].x; g.y += pg[q].y; g.z += pg[q].z; g.w += pg[q].w;
+        u.x += pu[q].x; u.y += pu[q].y; u.z += pu[q].z; u.w += pu[q].w;
+      }
+    const float gv[4] = {g.x, g.y, g.z, g.w}, uv[4] = {u.x, u.y, u.z, u.w};
+    uint16_t hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float h = gv[e] * __builtin_amdgcn_rcpf(1.f + __expf(-gv[e])) * uv[e];
+      hi[e] = f32_to_bf16_rne(h);
+      lo[e] = f32_to_bf16_rne(h - bf16_to_f32(hi[e]));
+    }
+    const int64_t o = (int64_t)pos * I + 4 * k4;
+    *reinterpret_cast<uint2*>(hh + o) = make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
+    *reinterpret_cast<uint2*>(hl + o) = make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+  }
+}
+
+// down of the one/two-token path
+// Block (a, strip): rows [64*strip, +64) of the down matrix of the a-th active
+// expert; 4 waves take groups g = wave + 4*i, i < GPW.  The same schedule as the
+// gate/up kernel: each wave requests h (hi and lo rows) of up to XT of the
+// expert's positions for its groups into its own LDS region, then its weights;
+// the token passes run from LDS with two dot products per code pair (hi, lo).
+// y goes to row p = t*K + k of pair_out.
+constexpr int kDNWaves = 4;
+
+template <int BITS, int GPW, int XT>
+struct HStageBlk {
+  using C = UnitCodec<BITS>;
+  static constexpr int PC = C::G / 8;             // 16-byte pieces per group row
+  static constexpr int NQ = XT * GPW * 2 * PC;    // pieces of a full chunk (hi and lo)
+  static constexpr int IT = (NQ + 63) / 64;
+  u32x4 v[IT];
+  __device__ __forceinline__ void load(const uint16_t* hh, const uint16_t* hl, int I, int pos0,
+                                       int nt, int gbase, int glast, int lane) {
+    typedef const u32x4 __attribute__((address_space(1)))* g4;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int q = min(it * 64 + lane, NQ - 1);
+      const int j = q / (GPW * 2 * PC), i = (q / (2 * PC)) % GPW, sel = (q / PC) % 2, pc = q % PC;
+      const int g = min(gbase + kDNWaves * i, glast);
+      const uint16_t* src = (sel ? hl : hh) + (int64_t)(pos0 + min(j, nt - 1)) * I + g * C::G + 8 * pc;
+      v[it] = *(g4)(as_global(src));
+    }
+  }
+  __device__ __forceinline__ void store(uint32_t* xs, int lane) const {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int q = it * 64 + lane;
+      if (q < NQ) *reinterpret_cast<u32x4*>(xs + 4 * q) = v[it];
+    }
+  }
+};
+
+template <int BITS, int GPW, int XT>
+__global__ __launch_bounds__(256, 2) void k_down_blk(
+    const moe_expert_ref* __restrict__ table, int E, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_pairs, int H, int I, int scale_f16,
+    const uint16_t* __restrict__ hh, const uint16_t* __restrict__ hl, float* __restrict__ pair_out) {
+  using C = UnitCodec<BITS>;
+  using HS = HStageBlk<BITS, GPW, XT>;
+  constexpr int XW = XT * GPW * 2 * C::PAIRS;  // uint32 per wave: [token][group][hi|lo][pair]
+  __shared__ float red[kDNWaves][kTokPerPass][64];
+  __shared__ __align__(16) uint32_t xs_all[kDNWaves * XW];
+  const int ng = I / C::G;
+
+  const Active act = find_active(offsets, table, E, blockIdx.x);
+  if (act.e < 0) return;
+  const int seg0 = __builtin_amdgcn_readfirstlane(act.seg0);
+  const int n_e = __builtin_amdgcn_readfirstlane(act.n);
+  const int strip = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const MatGeom gm{H, I, BITS, C::G};
+  const gbytes_t down = as_global(act.ptr[2]);
+  const gu16_t dsc = (gu16_t)(down + gm.scales_off());
+  const int row = strip * 64 + lane;
+  uint32_t* xs = xs_all + wv * XW;
+
+  // pair ids of the expert's first 64 positions (lane = position), then h of the
+  // first positions, all ahead of the weights
+  int pids = sorted_pairs[seg0 + min(lane, n_e - 1)];
+  HS hst;
+  int nt = min(n_e, XT);
+  hst.load(hh, hl, I, seg0, nt, wv, ng - 1, lane);
+  asm volatile("" ::: "memory");
+
+  u32x4 cw[GPW][C::CHUNKS];
+  uint32_t sr[GPW];  // the aligned dword holding the scale (any 16-bit handling here would wait)
+#pragma unroll
+  for (int i = 0; i < GPW; ++i) {
+    const int g = min(wv + kDNWaves * i, ng - 1);
+    load_unit4<BITS>(down, (int64_t)strip * ng + g, lane, cw[i]);
+    sr[i] = load_scale_dword(dsc, (int64_t)row * ng + g);
+  }
+  asm volatile("" ::: "memory");
+
+  const float off = lane < C::PAIRS ? C::pair_off(lane) : 0.f;
+  auto osum = [&](const uint32_t* hhp, const uint32_t* hlp) {
+    const uint32_t a = lane < C::PAIRS ? hhp[lane] : 0u, b = lane < C::PAIRS ? hlp[lane] : 0u;
+    return wave_sum_uniform<BITS>(off * ((bf16_to_f32((uint16_t)a) + bf16_to_f32((uint16_t)(a >> 16))) +
+                                         (bf16_to_f32((uint16_t)b) + bf16_to_f32((uint16_t)(b >> 16)))));
+  };
+  hst.store(xs, lane);
+  for (int c0 = 0; c0 < n_e; c0 += XT) {
+    if (c0 > 0) {
+      nt = min(n_e - c0, XT);
+      hst.load(hh, hl, I, seg0 + c0, nt, wv, ng - 1, lane);
+      hst.store(xs, lane);
+      if (c0 % 64 == 0) pids = sorted_pairs[seg0 + c0 + min(lane, n_e - c0 - 1)];
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's own LDS writes
+    for (int jp = 0; jp < nt; jp += kTokPerPass) {
+      const bool two = jp + 1 < nt;
+      const int j1 = two ? jp + 1 : jp;
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < GPW; ++i) {
+        const int g = wv + kDNWaves * i;
+        if (g < ng) {
+          const uint32_t* hh0 = xs + ((jp * GPW + i) * 2 + 0) * C::PAIRS;
+          const uint32_t* hl0 = xs + ((jp * GPW + i) * 2 + 1) * C::PAIRS;
+          const uint32_t* hh1 = xs + ((j1 * GPW + i) * 2 + 0) * C::PAIRS;
+          const uint32_t* hl1 = xs + ((j1 * GPW + i) * 2 + 1) * C::PAIRS;
+          uint32_t wd[C::WORDS];
+          unit_words<BITS>(cw[i], wd);
+          uint32_t sraw = sr[i];
+          asm volatile("" : "+v"(sraw));
+          const float sc = scale_to_f32(scale_from_dword(sraw, (int64_t)row * ng + g), scale_f16);
+          const float k0 = osum(hh0, hl0);
+          float d0 = 0.f, d1 = 0.f;
+          if (two) {
+            const float k1 = osum(hh1, hl1);
+            C::for_each_pair(wd, [&](int Pp, uint32_t pr) {
+              d0 = dot2_bf16(pr, hl0[Pp], dot2_bf16(pr, hh0[Pp], d0));
+              d1 = dot2_bf16(pr, hl1[Pp], dot2_bf16(pr, hh1[Pp], d1));
+            });
+            a1 = fmaf(sc, d1 - k1, a1);
+          } else {
+            C::for_each_pair(wd, [&](int Pp, uint32_t pr) {
+              d0 = dot2_bf16(pr, hl0[Pp], dot2_bf16(pr, hh0[Pp], d0));
+            });
+          }
+          a0 = fmaf(sc, d0 - k0, a0);
+        }
+      }
+      red[wv][0][lane] = a0;
+      red[wv][1][lane] = a1;
+      lds_barrier();
+      if (wv < (two ? 2 : 1)) {
+        const int j = wv;
+        float y = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kDNWaves; ++ww) y += red[ww][j][lane];
+        const int idx = (c0 + jp + j) % 64;  // wave-uniform
+        const int p = __builtin_amdgcn_readlane(pids, idx);
+        pair_out[(int64_t)p * H + row] = y;
+      }
+      lds_barrier();
+    }
+  }
+}
+
+// ---------------------------------------------------------------- SwiGLU
+// h[pos][k] = silu(sum_ch g_ch) * (sum_ch u_ch), slices added in chunk order,
+// as bf16 hi + bf16 remainder (h to ~2^-16 relative).  Positions past the
+// grouped pairs are skipped.
+constexpr int kMaxChunks = 16;
+
+__global__ __launch_bounds__(256) void k_swiglu_sum(const float* __restrict__ part,
+                                                    const int32_t* __restrict__ offsets, int E,
+                                                    int P, int I, int NCH,
+                                                    uint16_t* __restrict__ hh,
+                                                    uint16_t* __restrict__ hl) {
+  const int pos = blockIdx.y;
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (pos >= offsets[E] || k >= I) return;
+  float pg[kMaxChunks], pu[kMaxChunks];
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const int cc = min(c, NCH - 1);
+    pg[c] = part[((int64_t)cc * P + pos) * I + k];
+    pu[c] = part[((int64_t)(NCH + cc) * P + pos) * I + k];
+  }
+  float g = pg[0], u = pu[0];
+#pragma unroll
+  for (int c = 1; c < kMaxChunks; ++c)
+    if (c < NCH) {
+      g += pg[c];
+      u += pu[c];
+    }
+  const float h = g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
+  const uint16_t hi = f32_to_bf16_rne(h);
+  hh[(int64_t)pos * I + k] = hi;
+  hl[(int64_t)pos * I + k] = f32_to_bf16_rne(h - bf16_to_f32(hi));
+}
+
+// ---------------------------------------------------------------- combine
+// y(t,k) = sum_ch part[ch][t*K+k] (chunk order); out[t] = sum_k w[t][k] y(t,k)
+// (k ascending; pairs whose id is outside [0, E) are skipped) + the shared
+// expert's nsh slices shared[q][t] (added in order);
+// pair_out[t*K+k] = y(t,k) when requested.
+template <int KM, int MC>
+__global__ __launch_bounds__(256) void k_combine_parts(const float* __restrict__ part, int NCH,
+                                                       int P, const int32_t* __restrict__ ids,
+                                                       const float* __restrict__ w, int K, int E,
+                                                       int H, const float* __restrict__ shared,
+                                                       int nsh, int T, float* __restrict__ out,
+                                                       float* __restrict__ pair_out) {
+  const int t = blockIdx.y;
+  const int n = min((int)(blockIdx.x * 256 + threadIdx.x), H - 1);
+  float y[KM][MC];
+#pragma unroll
+  for (int k = 0; k < KM; ++k)
+#pragma unroll
+    for (int c = 0; c < MC; ++c)
+      y[k][c] = part[((int64_t)min(c, NCH - 1) * P + (int64_t)t * K + min(k, K - 1)) * H + n];
+  float acc = 0.f;
+  const bool in = blockIdx.x * 256 + threadIdx.x < H;
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    const int id = ids[t * K + min(k, K - 1)];
+    if (k < K && id >= 0 && id < E) {
+      float v = y[k][0];
+#pragma unroll
+      for (int c = 1; c < MC; ++c)
+        if (c < NCH) v += y[k][c];
+      acc = fmaf(w[t * K + min(k, K - 1)], v, acc);
+      if (pair_out && in) pair_out[((int64_t)t * K + k) * H + n] = v;
+    }
+  }
+  if (shared) {  // the shared expert's slices, in slice order
+    float sh = 0.f;
+    for (int q = 0; q < nsh; ++q) sh += shared[((int64_t)q * T + t) * H + n];
+    acc += sh;
+  }
+  if (in) out[(int64_t)t * H + n] = acc;
+}
+
+// ---------------------------------------------------------------- launcher
+static int compute_units() {
+  static int n = 0;
+  if (!n) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
+// Reduction groups per work item: 4 for gate/up and 3 for down (h hi and lo
+// staged), at three waves per SIMD.
+constexpr int kDecGPW = 4;
+constexpr int kDecGPWd = 3;
+
+template <int BITS>
+static hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* shared_out, int nsh,
+                                  hipStream_t s) {
+  using C = UnitCodec<BITS>;
+  const moe_cfg& c = *f.c;
+  const int H = c.hidden, I = c.inter, E = c.n_experts, K = c.top_k, T = f.T, P = T * K;
+  int32_t* act_hdr = reinterpret_cast<int32_t*>(f.ws + L.act);
+  ActEntry* act = reinterpret_cast<ActEntry*>(f.ws + L.act + 64);
+  float* gpart = reinterpret_cast<float*>(f.ws + L.gpart);
+  static_assert(sizeof(ActEntry) == 40, "act list entries are 40 bytes");
+  float* dpart = reinterpret_cast<float*>(f.ws + L.dpart);
+  uint16_t* hh = reinterpret_cast<uint16_t*>(f.ws + L.hdec);
+  uint16_t* hl = hh + (int64_t)P * I;
+  const int maxU = min(E, P);
+  const int nch_gu = (H / C::G + kDecGPW - 1) / kDecGPW;
+  const int nch_dn = (I / C::G + kDecGPWd - 1) / kDecGPWd;
+  // blocks of four waves (one per SIMD), wps waves per SIMD resident
+  auto grid_for = [&](int64_t items, int wps) {
+    return (int)std::min<int64_t>((items + 3) / 4, (int64_t)compute_units() * wps);
+  };
+  const int64_t items_gu = (int64_t)maxU * (I / 64) * 2 * nch_gu;
+  const int64_t items_dn = (int64_t)maxU * (H / 64) * nch_dn;
+
+  if (T <= 2) {  // block-level path: no plan kernel
+    const int ngh = H / C::G;
+    const int KP = (ngh + 5 * kGUWaves - 1) / (5 * kGUWaves);  // <= kMaxKParts for H/G <= 64
+    const int gpw_gu = ((ngh + KP - 1) / KP + kGUWaves - 1) / kGUWaves;
+    const int gpw_dn = (I / C::G + kDNWaves - 1) / kDNWaves;
+    float* y = f.pair_out ? f.pair_out : dpart;  // pair-order expert outputs
+#define MOE_GU(N)                                                                                \
+  case N:                                                                                        \
+    MOE_LAUNCH(KID_GATEUP, (k_gateup_smem<BITS, N>), dim3(maxU, I / 64, 2 * KP),                 \
+               dim3(64 * kGUWaves), 0, s, f.table, E, f.offsets, f.sorted_pairs, K, f.x, f.x, H, I, \
+               P, KP, c.scale_f16, gpart);                                                       \
+    break;
+    switch (gpw_gu) {
+      MOE_GU(1) MOE_GU(2) MOE_GU(3) MOE_GU(4) MOE_GU(5)
+      default: return hipErrorInvalidValue;
+    }
+#undef MOE_GU
+    MOE_LAUNCH(KID_SWIGLU, k_swiglu_kp, dim3(P), dim3(256), 0, s, gpart, f.offsets, E, P, I, KP, hh,
+               hl);
+#define MOE_DN(N)                                                                                \
+  case N:                                                                                        \
+    MOE_LAUNCH(KID_DOWN, (k_down_blk<BITS, N, 2>), dim3(maxU, H / 64), dim3(64 * kDNWaves), 0, s,  \
+               f.table, E, f.offsets, f.sorted_pairs, H, I, c.scale_f16, hh, hl, y);             \
+    break;
+    switch (gpw_dn) {
+      MOE_DN(1) MOE_DN(2) MOE_DN(3) MOE_DN(4) MOE_DN(5) MOE_DN(6) MOE_DN(7) MOE_DN(8)
+      default: return hipErrorInvalidValue;
+    }
+#undef MOE_DN
+    // y holds every pair's output in pair order: a single "chunk"
+    if (K <= 8) {
+      MOE_LAUNCH(KID_COMBINE, (k_combine_parts<8, 1>), dim3((H + 255) / 256, T), dim3(256), 0, s, y,
+                 1, P, f.ids, f.w, K, E, H, shared_out, nsh, T, f.out, nullptr);
+    } else {
+      MOE_LAUNCH(KID_COMBINE, (k_combine_parts<16, 1>), dim3((H + 255) / 256, T), dim3(256), 0, s,
+                 y, 1, P, f.ids, f.w, K, E, H, shared_out, nsh, T, f.out, nullptr);
+    }
+    return hipGetLastError();
+  }
+
+  MOE_LAUNCH(KID_PLAN, k_plan_decode, dim3(1), dim3(1024), 0, s, f.offsets, f.table, E, act_hdr,
+             act);
+  MOE_LAUNCH(KID_GATEUP, (k_gemv<BITS, kDecGPW, 8, 0, 3>), dim3(grid_for(items_gu, 3)),
+             dim3(256), 0, s, act_hdr, act, f.sorted_pairs, K, f.x, nullptr, I, H, P, c.scale_f16,
+             gpart);
+  MOE_LAUNCH(KID_SWIGLU, k_swiglu_sum, dim3((I + 255) / 256, P), dim3(256), 0, s, gpart, f.offsets,
+             E, P, I, nch_gu, hh, hl);
+  MOE_LAUNCH(KID_DOWN, (k_gemv<BITS, kDecGPWd, 4, 1, 3>), dim3(grid_for(items_dn, 3)), dim3(256),
+             0, s, act_hdr, act, f.sorted_pairs, K, hh, hl, H, I, P, c.scale_f16, dpart);
+  // MC: chunks of the down reduction read per pair (I/G <= 32 groups, 3 per chunk)
+#define MOE_CMB(KM, MC)                                                                        \
+  MOE_LAUNCH(KID_COMBINE, (k_combine_parts<KM, MC>), dim3((H + 255) / 256, T), dim3(256), 0, s, \
+             dpart, nch_dn, P, f.ids, f.w, K, E, H, shared_out, nsh, T, f.out, f.pair_out)
+  if (K <= 8) {
+    if (nch_dn <= 4) MOE_CMB(8, 4); else MOE_CMB(8, 12);
+  } else {
+    if (nch_dn <= 4) MOE_CMB(16, 4); else MOE_CMB(16, 12);
+  }
+#undef MOE_CMB
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const FwdArgs& f, const WsLayout& L, float* shared_out, int nsh,
+                         hipStream_t s) {
+  return f.c->bits == 3 ? launch_decode_t<3>(f, L, shared_out, nsh, s)
+                        : launch_decode_t<4>(f, L, shared_out, nsh, s);
+}
+
+}  // namespace moe
