@@ -11,8 +11,9 @@ resident copies of the layer (distinct weights, router and bias) so that no step
 is served from the 256 MB last-level cache.
 
 Prints ONE JSON line: tokens/s over the timed steps, the dominant kernel's
-achieved expert-weight bandwidth against the 8 TB/s HBM peak (kernel durations
-from HIP events the library records on its launch stream), and the fp64 CPU
+achieved expert-weight bandwidth against the 8 TB/s HBM peak (prefill: matrix-core
+flops against the dense fp16 peak; kernel durations from HIP events that each
+launch timestamps at the kernel's start and end on its stream), and the fp64 CPU
 oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -206,19 +207,24 @@ def main():
             ach = gu_flops * gu_n / (gu_ms * 1e-3) / 1e12 if gu_ms else None
             roof = {"bound": "mfma", "achieved": round(ach, 1) if ach else None,
                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4) if ach else None, "traffic": None,
+                    "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4) if ach else None,
+                    "traffic": measured_traffic("k_gateup_mfma", a.workload),
                     "kernel": "k_gateup_mfma (grouped gate+up GEMM, SwiGLU epilogue)",
+                    "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
                     "avg_us": round(gu_ms / gu_n * 1e3, 2) if gu_n else None,
                     "flops_per_launch": gu_flops}
             if dn_ms:
                 extra["down_TFLOPs"] = round(dn_flops * dn_n / (dn_ms * 1e-3) / 1e12, 1)
         else:
             ach = gu_bytes / (gu_ms * 1e-3) / 1e9 if gu_ms else None
+            gu_kernel = "k_gateup_smem" if T <= 2 else "k_gemv (gate/up)"
             roof = {"bound": "hbm", "achieved": round(ach, 1) if ach else None, "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4) if ach else None,
-                    "traffic": None, "kernel": "k_gateup (gate+up GEMV, SwiGLU)",
+                    "traffic": measured_traffic(gu_kernel, a.workload),
+                    "kernel": gu_kernel + " (gate and up GEMV)",
                     "avg_us": round(gu_ms / gu_n * 1e3, 2) if gu_n else None,
-                    "bytes_per_launch": round(gu_bytes / len(u_steps))}
+                    "bytes_per_launch": round(gu_bytes / len(u_steps)),
+                    "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)"}
             if dn_ms:
                 extra["down_GBs"] = round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1)
         extra["kernels_us"] = {k: round(v[0] / v[1] * 1e3, 2) for k, v in kern.items() if v[1]}
@@ -266,6 +272,28 @@ def main():
     }
     print(json.dumps(res))
     ml.close()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE, calibrated against a
+    plain device copy), or None when there is none for this workload or the kernel's
+    sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        ent = json.load(fh).get("kernels", {}).get(kernel)
+    if not ent or ent.get("workload") != workload:
+        return None
+    h = hashlib.sha256()
+    for src in ent["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != ent["sha256_16"]:
+        return None
+    return ent["hbm_bytes_per_launch"]
 
 
 def cpu_baseline(cfg, L, budget_s, layers_per_step=1):

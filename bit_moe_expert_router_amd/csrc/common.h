@@ -1,5 +1,6 @@
 // common.h -- internal definitions shared by the HIP sources of libmoe.so.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -299,15 +300,18 @@ enum KernelId {
   KID_LOGITS = 0, KID_TOPK, KID_PERMUTE, KID_PLAN, KID_GATEUP, KID_DOWN, KID_SH_GATEUP,
   KID_SH_DOWN, KID_COMBINE, KID_RMSNORM, KID_ZERO, KID_XPREP, KID_SWIGLU, KID_COUNT
 };
-void prof_begin(int kid, hipStream_t s);
-void prof_end(int kid, hipStream_t s);
+// when profiling is on: a pair of events for the next launch of kernel kid
+bool prof_events(int kid, hipEvent_t* b, hipEvent_t* e);
 
-// launch a kernel, bracketed by profiling events when profiling is enabled
-#define MOE_LAUNCH(kid, kernel, grid, block, shmem, stream, ...)                   \
-  do {                                                                             \
-    ::moe::prof_begin(kid, stream);                                                \
-    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);           \
-    ::moe::prof_end(kid, stream);                                                  \
+// launch a kernel; when profiling is on, with start and end events that the
+// launch itself timestamps
+#define MOE_LAUNCH(kid, kernel, grid, block, shmem, stream, ...)                          \
+  do {                                                                                    \
+    hipEvent_t _moe_b, _moe_e;                                                            \
+    if (::moe::prof_events(kid, &_moe_b, &_moe_e))                                        \
+      hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, _moe_b, _moe_e, 0, __VA_ARGS__); \
+    else                                                                                  \
+      hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                \
   } while (0)
 
 // ---------------------------------------------------------------- launchers

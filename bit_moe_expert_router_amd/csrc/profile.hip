@@ -1,10 +1,11 @@
 // profile.hip -- optional per-kernel timing with HIP events.
 //
-// When enabled (moe_profile_enable), every kernel the library launches is
-// bracketed by a pair of HIP events recorded on the launch stream; the elapsed
-// times are accumulated per kernel name when moe_profile_read is called.  Off by
-// default; when off, the launch path checks one flag.  Not for use under stream
-// capture.
+// When enabled (moe_profile_enable), every kernel the library launches carries a
+// pair of HIP events that the launch itself timestamps at the kernel's start and
+// end (hipExtLaunchKernelGGL), so the elapsed time is the kernel's own duration,
+// not the dispatch latency around it; the times are accumulated per kernel name
+// when moe_profile_read is called.  Off by default; when off, the launch path
+// checks one flag.  Not for use under stream capture.
 #include <string.h>
 
 #include <mutex>
@@ -53,27 +54,21 @@ Profiler& prof() {
 
 bool prof_on() { return prof().on; }
 
-void prof_begin(int kid, hipStream_t s) {
+bool prof_events(int kid, hipEvent_t* b, hipEvent_t* e) {
   Profiler& p = prof();
-  if (!p.on) return;
+  if (!p.on) return false;
   std::lock_guard<std::mutex> g(p.mu);
-  hipEvent_t b = p.get();
-  if (!b) return;
-  (void)hipEventRecord(b, s);
-  p.open = Rec{kid, b, nullptr};
-}
-
-void prof_end(int kid, hipStream_t s) {
-  Profiler& p = prof();
-  if (!p.on) return;
-  std::lock_guard<std::mutex> g(p.mu);
-  if (p.open.kid != kid || !p.open.b) return;
-  hipEvent_t e = p.get();
-  if (!e) return;
-  (void)hipEventRecord(e, s);
-  p.open.e = e;
-  p.recs.push_back(p.open);
-  p.open = Rec{-1, nullptr, nullptr};
+  hipEvent_t eb = p.get();
+  if (!eb) return false;
+  hipEvent_t ee = p.get();
+  if (!ee) {
+    p.pool.push_back(eb);
+    return false;
+  }
+  p.recs.push_back(Rec{kid, eb, ee});
+  *b = eb;
+  *e = ee;
+  return true;
 }
 
 }  // namespace moe

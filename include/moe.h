@@ -170,7 +170,8 @@ moe_status moe_rmsnorm_bf16(const moe_ctx* ctx, float* resid, const float* add, 
                             float eps, void* y_bf16, moe_stream_t stream);
 
 /* Kernel timing.  While enabled (process-wide), every kernel the library
- * launches is bracketed by two HIP events recorded on its launch stream.
+ * launches carries two HIP events that the launch timestamps at the kernel's
+ * start and end (the kernel's own duration, without the dispatch latency).
  * moe_profile_read waits for the recorded events, writes up to max_kernels
  * entries (names: max_kernels x 32 chars, NUL-terminated, HOST memory; total_ms
  * and launches: HOST arrays) for the kernels launched since the last read, and
