@@ -19,6 +19,10 @@ struct moe_ctx {
     const void *g, *u, *d;
   };
   std::vector<Shared> shared;     // per layer
+  // the shared expert runs on a second stream (default priority) between a fork
+  // event recorded on the caller's stream and a join event the combine waits for
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 };
 
 namespace {
@@ -89,6 +93,16 @@ moe_status moe_create(const moe_cfg* cfg, int32_t n_layers, moe_ctx** out) {
     delete c;
     return fail(MOE_E_NOMEM, "moe_create: device tables (%zu bytes)", tb);
   }
+  if (cfg->shared_inter > 0 &&
+      (hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess ||
+       hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming) != hipSuccess ||
+       hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming) != hipSuccess)) {
+    if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
+    if (c->side) (void)hipStreamDestroy(c->side);
+    (void)hipFree(c->d_tables);
+    delete c;
+    return fail(MOE_E_HIP, "moe_create: shared-expert stream or events");
+  }
   *out = c;
   return ok();
 }
@@ -97,6 +111,9 @@ moe_status moe_destroy(moe_ctx* ctx) {
   if (!ctx) return ok();
   (void)hipDeviceSynchronize();
   (void)hipFree(ctx->d_tables);
+  if (ctx->ev_join) (void)hipEventDestroy(ctx->ev_join);
+  if (ctx->ev_fork) (void)hipEventDestroy(ctx->ev_fork);
+  if (ctx->side) (void)hipStreamDestroy(ctx->side);
   delete ctx;
   return ok();
 }
@@ -203,7 +220,7 @@ moe_status moe_forward(moe_ctx* ctx, int32_t layer, const void* x_bf16, int32_t 
   const moe_ctx::Shared& sh = ctx->shared[layer];
   moe::FwdArgs f{&c, ctx->d_tables + (size_t)layer * c.n_experts, sh.g, sh.u, sh.d,
                  (const uint16_t*)x_bf16, T, topk_ids, topk_w, expert_offsets, sorted_pairs,
-                 out, pair_out, (uint8_t*)ws};
+                 out, pair_out, (uint8_t*)ws, ctx->side, ctx->ev_fork, ctx->ev_join};
   return hip_status(moe::launch_forward(f, (hipStream_t)stream), "moe_forward launch");
 }
 

@@ -330,11 +330,13 @@ struct FwdArgs {
   float* out;
   float* pair_out;              // null: workspace
   uint8_t* ws;
+  hipStream_t side;             // shared-expert stream, fork and join events (or null)
+  hipEvent_t ev_fork, ev_join;
 };
 
 hipError_t launch_prefill(const FwdArgs& f, const WsLayout& L, float* pair_out, hipStream_t s);
 hipError_t launch_decode(const FwdArgs& f, const WsLayout& L, float* shared_out, int nsh,
-                         hipStream_t s);
+                         hipEvent_t join, hipStream_t s);
 hipError_t launch_shared(const FwdArgs& f, const WsLayout& L, hipStream_t s, float** out,
                          int* nslices);
 hipError_t launch_route(const moe_cfg& c, const uint16_t* x, int T, const float* wr,

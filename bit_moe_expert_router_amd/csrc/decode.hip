@@ -709,7 +709,7 @@ constexpr int kDecGPWd = 3;
 
 template <int BITS>
 static hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* shared_out, int nsh,
-                                  hipStream_t s) {
+                                  hipEvent_t join, hipStream_t s) {
   using C = UnitCodec<BITS>;
   const moe_cfg& c = *f.c;
   const int H = c.hidden, I = c.inter, E = c.n_experts, K = c.top_k, T = f.T, P = T * K;
@@ -760,6 +760,10 @@ static hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* sh
     }
 #undef MOE_DN
     // y holds every pair's output in pair order: a single "chunk"
+    if (join) {
+      const hipError_t e = hipStreamWaitEvent(s, join, 0);
+      if (e != hipSuccess) return e;
+    }
     if (K <= 8) {
       MOE_LAUNCH(KID_COMBINE, (k_combine_parts<8, 1>), dim3((H + 255) / 256, T), dim3(256), 0, s, y,
                  1, P, f.ids, f.w, K, E, H, shared_out, nsh, T, f.out, nullptr);
@@ -779,6 +783,10 @@ static hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* sh
              E, P, I, nch_gu, hh, hl);
   MOE_LAUNCH(KID_DOWN, (k_gemv<BITS, kDecGPWd, 4, 1, 3>), dim3(grid_for(items_dn, 3)), dim3(256),
              0, s, act_hdr, act, f.sorted_pairs, K, hh, hl, H, I, P, c.scale_f16, dpart);
+  if (join) {
+    const hipError_t e = hipStreamWaitEvent(s, join, 0);
+    if (e != hipSuccess) return e;
+  }
   // MC: chunks of the down reduction read per pair (I/G <= 32 groups, 3 per chunk)
 #define MOE_CMB(KM, MC)                                                                        \
   MOE_LAUNCH(KID_COMBINE, (k_combine_parts<KM, MC>), dim3((H + 255) / 256, T), dim3(256), 0, s, \
@@ -793,9 +801,9 @@ static hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* sh
 }
 
 hipError_t launch_decode(const FwdArgs& f, const WsLayout& L, float* shared_out, int nsh,
-                         hipStream_t s) {
-  return f.c->bits == 3 ? launch_decode_t<3>(f, L, shared_out, nsh, s)
-                        : launch_decode_t<4>(f, L, shared_out, nsh, s);
+                         hipEvent_t join, hipStream_t s) {
+  return f.c->bits == 3 ? launch_decode_t<3>(f, L, shared_out, nsh, join, s)
+                        : launch_decode_t<4>(f, L, shared_out, nsh, join, s);
 }
 
 }  // namespace moe

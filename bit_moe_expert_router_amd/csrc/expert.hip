@@ -258,22 +258,46 @@ hipError_t launch_shared(const FwdArgs& f, const WsLayout& L, hipStream_t s, flo
 }
 
 // ---------------------------------------------------------------- rmsnorm glue
-// resid += add (if given); y = bf16(resid / sqrt(mean(resid^2) + eps)), one block
-// per token, fixed-order reduction.
+// resid += add (if given); y = bf16(resid / sqrt(mean(resid^2) + eps)), fixed-
+// order reduction.  One block per token; each thread requests all of its 16-byte pieces of the
+// residual (and of the addend) at once, so the kernel is one memory round trip
+// deep: H/4 pieces over 256 threads, at most kRnPieces per thread (H <= 8192).
+constexpr int kRnPieces = 8;
+
 __global__ __launch_bounds__(256) void k_rmsnorm(float* __restrict__ resid,
                                                  const float* __restrict__ add, int H, float eps,
                                                  uint16_t* __restrict__ y) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
   const int t = blockIdx.x;
-  float* r = resid + (int64_t)t * H;
-  float ss = 0.f;
-  for (int h = threadIdx.x; h < H; h += 256) {
-    float v = r[h];
-    if (add) {
-      v += add[(int64_t)t * H + h];
-      r[h] = v;
-    }
-    ss = fmaf(v, v, ss);
+  const int H4 = H / 4;
+  f4* r = reinterpret_cast<f4*>(resid + (int64_t)t * H);
+  const f4* ad = add ? reinterpret_cast<const f4*>(add + (int64_t)t * H) : nullptr;
+  f4 v[kRnPieces];
+#pragma unroll
+  for (int i = 0; i < kRnPieces; ++i) {
+    const int q = min((int)threadIdx.x + 256 * i, H4 - 1);
+    v[i] = r[q];
   }
+  if (ad) {
+    f4 a[kRnPieces];
+#pragma unroll
+    for (int i = 0; i < kRnPieces; ++i) a[i] = ad[min((int)threadIdx.x + 256 * i, H4 - 1)];
+#pragma unroll
+    for (int i = 0; i < kRnPieces; ++i) {
+      v[i] += a[i];
+      const int q = threadIdx.x + 256 * i;
+      if (q < H4) r[q] = v[i];
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRnPieces; ++i)
+    if ((int)threadIdx.x + 256 * i < H4) {
+      ss = fmaf(v[i].x, v[i].x, ss);
+      ss = fmaf(v[i].y, v[i].y, ss);
+      ss = fmaf(v[i].z, v[i].z, ss);
+      ss = fmaf(v[i].w, v[i].w, ss);
+    }
   __shared__ float part[4];
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
@@ -281,7 +305,16 @@ __global__ __launch_bounds__(256) void k_rmsnorm(float* __restrict__ resid,
   __syncthreads();
   const float tot = ((part[0] + part[1]) + part[2]) + part[3];
   const float inv = 1.f / sqrtf(tot / (float)H + eps);
-  for (int h = threadIdx.x; h < H; h += 256) y[(int64_t)t * H + h] = f32_to_bf16_rne(r[h] * inv);
+  uint2* yo = reinterpret_cast<uint2*>(y + (int64_t)t * H);
+#pragma unroll
+  for (int i = 0; i < kRnPieces; ++i) {
+    const int q = threadIdx.x + 256 * i;
+    if (q < H4) {
+      const uint32_t lo = f32_to_bf16_rne(v[i].x * inv) | ((uint32_t)f32_to_bf16_rne(v[i].y * inv) << 16);
+      const uint32_t hi = f32_to_bf16_rne(v[i].z * inv) | ((uint32_t)f32_to_bf16_rne(v[i].w * inv) << 16);
+      yo[q] = make_uint2(lo, hi);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- counters init
@@ -300,13 +333,29 @@ hipError_t launch_forward_t(const FwdArgs& f, hipStream_t s) {
   const bool has_shared = c.shared_inter > 0 && f.sg && f.su && f.sd;
   float* sh_out = nullptr;
   int nsh = 0;
+  hipEvent_t join = nullptr;
   if (has_shared) {
-    const hipError_t err = launch_shared(f, L, s, &sh_out, &nsh);
+    // the shared expert needs only x: it runs on the side stream while the
+    // routed experts run on s; the combine waits for it
+    const bool fork = f.side && f.ev_fork && f.ev_join;
+    hipStream_t ss = fork ? f.side : s;
+    if (fork) {
+      hipError_t e = hipEventRecord(f.ev_fork, s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(f.side, f.ev_fork, 0);
+      if (e != hipSuccess) return e;
+    }
+    const hipError_t err = launch_shared(f, L, ss, &sh_out, &nsh);
     if (err != hipSuccess) return err;
+    if (fork) {
+      const hipError_t e = hipEventRecord(f.ev_join, f.side);
+      if (e != hipSuccess) return e;
+      join = f.ev_join;
+    }
   }
-  if (!prefill_eligible(c, T)) return launch_decode(f, L, sh_out, nsh, s);
+  if (!prefill_eligible(c, T)) return launch_decode(f, L, sh_out, nsh, join, s);
   float* pair_out = f.pair_out ? f.pair_out : reinterpret_cast<float*>(f.ws + L.pair_out);
-  const hipError_t err = launch_prefill(f, L, pair_out, s);
+  hipError_t err = launch_prefill(f, L, pair_out, s);
+  if (err == hipSuccess && join) err = hipStreamWaitEvent(s, join, 0);
   if (err != hipSuccess) return err;
   if (K <= 8) {
     MOE_LAUNCH(KID_COMBINE, k_combine<8>, dim3((H + 255) / 256, T), dim3(256), 0, s, pair_out,

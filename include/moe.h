@@ -17,7 +17,10 @@
  * in a HIP graph.  Status codes report host-side argument checks; faults inside
  * kernels surface at the caller's next synchronisation.  No C++ exception crosses
  * this boundary.  One host thread may use a context at a time; calls that run
- * concurrently on different streams need distinct workspaces.
+ * concurrently on different streams need distinct workspaces and contexts (a
+ * context with a shared expert owns a second stream and two events: moe_forward
+ * runs the shared expert there, forked from and joined back into `stream`; the
+ * fork and join are stream-ordered and can be captured).
  *
  * Packed weight format (v1).  A matrix W[N][Kd] (N outputs, Kd reduction; N % 64
  * == 0, Kd % G == 0) stores unsigned codes c with W[n][k] = (c - 2^(bits-1)) *
@@ -85,8 +88,8 @@ typedef struct {
 } moe_expert_ref;
 
 /* Create a context for n_layers layers of shape *cfg.  Allocates only the device
- * pointer tables (3 pointers per expert per layer) and the shared-expert pointer
- * slots.  H and I must be multiples of 64 and of G; Is a multiple of 64.
+ * pointer tables (3 pointers per expert per layer), the shared-expert pointer
+ * slots and, when shared_inter > 0, the shared expert's stream and two events.  H and I must be multiples of 64 and of G; Is a multiple of 64.
  * Returns MOE_E_UNSUPPORTED for other shapes, MOE_E_NOMEM on allocation failure. */
 moe_status moe_create(const moe_cfg* cfg, int32_t n_layers, moe_ctx** out);
 
