@@ -426,48 +426,6 @@ __global__ __launch_bounds__(256, 2) void k_gateup_smem(
   }
 }
 
-// SwiGLU of the one/two-token path (KP partial products per matrix)
-// h of every grouped pair position: h = silu(sum_q g_q) * (sum_q u_q), parts
-// added in kp order, kept as bf16 hi + bf16 remainder (h to ~2^-16 relative):
-// hh[pos][k], hl[pos][k].  One block per position; positions past the grouped
-// pairs (ids left out) are skipped.
-__global__ __launch_bounds__(256) void k_swiglu_kp(const float* __restrict__ gu,
-                                                const int32_t* __restrict__ offsets, int E, int P,
-                                                int I, int KP, uint16_t* __restrict__ hh,
-                                                uint16_t* __restrict__ hl) {
-  const int pos = blockIdx.x;
-  if (pos >= offsets[E]) return;
-  const int I4 = I / 4;
-  const float4* g4 = reinterpret_cast<const float4*>(gu);
-  for (int k4 = threadIdx.x; k4 < I4; k4 += 256) {
-    float4 pg[kMaxKParts], pu[kMaxKParts];
-#pragma unroll
-    for (int q = 0; q < kMaxKParts; ++q) {
-      const int qq = min(q, KP - 1);
-      pg[q] = g4[((int64_t)qq * P + pos) * I4 + k4];
-      pu[q] = g4[((int64_t)(KP + qq) * P + pos) * I4 + k4];
-    }
-    float4 g = pg[0], u = pu[0];
-#pragma unroll
-    for (int q = 1; q < kMaxKParts; ++q)
-      if (q < KP) {
-        g.x += pg[q].x; g.y += pg[q].y; g.z += pg[q].z; g.w += pg[q].w;
-        u.x += pu[q].x; u.y += pu[q].y; u.z += pu[q].z; u.w += pu[q].w;
-      }
-    const float gv[4] = {g.x, g.y, g.z, g.w}, uv[4] = {u.x, u.y, u.z, u.w};
-    uint16_t hi[4], lo[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float h = gv[e] * __builtin_amdgcn_rcpf(1.f + __expf(-gv[e])) * uv[e];
-      hi[e] = f32_to_bf16_rne(h);
-      lo[e] = f32_to_bf16_rne(h - bf16_to_f32(hi[e]));
-    }
-    const int64_t o = (int64_t)pos * I + 4 * k4;
-    *reinterpret_cast<uint2*>(hh + o) = make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
-    *reinterpret_cast<uint2*>(hl + o) = make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
-  }
-}
-
 // down of the one/two-token path
 // Block (a, strip): rows [64*strip, +64) of the down matrix of the a-th active
 // expert; 4 waves take groups g = wave + 4*i, i < GPW.  The same schedule as the
@@ -477,41 +435,67 @@ __global__ __launch_bounds__(256) void k_swiglu_kp(const float* __restrict__ gu,
 // y goes to row p = t*K + k of pair_out.
 constexpr int kDNWaves = 4;
 
-template <int BITS, int GPW, int XT>
-struct HStageBlk {
+// h of the wave's groups for up to XT positions, formed from the KP gate and up
+// partial products (added in part order, as the SwiGLU pass of the larger
+// batches does): item q = (token j, group i, pair p) of the wave; lane-strided.
+template <int BITS, int GPW, int XT, int KP>
+struct HFromParts {
   using C = UnitCodec<BITS>;
-  static constexpr int PC = C::G / 8;             // 16-byte pieces per group row
-  static constexpr int NQ = XT * GPW * 2 * PC;    // pieces of a full chunk (hi and lo)
-  static constexpr int IT = (NQ + 63) / 64;
-  u32x4 v[IT];
-  __device__ __forceinline__ void load(const uint16_t* hh, const uint16_t* hl, int I, int pos0,
-                                       int nt, int gbase, int glast, int lane) {
-    typedef const u32x4 __attribute__((address_space(1)))* g4;
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  static constexpr int NI = XT * GPW * C::PAIRS;
+  static constexpr int IT = (NI + 63) / 64;
+  f32x2 g[IT][KP], u[IT][KP];
+  __device__ __forceinline__ void load(const float* part, int P, int I, int pos0, int nt,
+                                       int gbase, int glast, int lane) {
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int q = min(it * 64 + lane, NQ - 1);
-      const int j = q / (GPW * 2 * PC), i = (q / (2 * PC)) % GPW, sel = (q / PC) % 2, pc = q % PC;
-      const int g = min(gbase + kDNWaves * i, glast);
-      const uint16_t* src = (sel ? hl : hh) + (int64_t)(pos0 + min(j, nt - 1)) * I + g * C::G + 8 * pc;
-      v[it] = *(g4)(as_global(src));
+      const int q = min(it * 64 + lane, NI - 1);
+      const int j = q / (GPW * C::PAIRS), i = (q / C::PAIRS) % GPW, pp = q % C::PAIRS;
+      const int gg = min(gbase + kDNWaves * i, glast);
+      const int64_t pos = pos0 + min(j, nt - 1);
+      const int k = gg * C::G + 2 * pp;
+#pragma unroll
+      for (int r = 0; r < KP; ++r) {
+        g[it][r] = *reinterpret_cast<const f32x2*>(part + ((int64_t)r * P + pos) * I + k);
+        u[it][r] = *reinterpret_cast<const f32x2*>(part + ((int64_t)(KP + r) * P + pos) * I + k);
+      }
     }
   }
   __device__ __forceinline__ void store(uint32_t* xs, int lane) const {
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int q = it * 64 + lane;
-      if (q < NQ) *reinterpret_cast<u32x4*>(xs + 4 * q) = v[it];
+      if (q < NI) {
+        f32x2 gs = g[it][0], us = u[it][0];
+#pragma unroll
+        for (int r = 1; r < KP; ++r) {
+          gs += g[it][r];
+          us += u[it][r];
+        }
+        uint32_t hi = 0, lo = 0;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float gv = e ? gs.y : gs.x, uv = e ? us.y : us.x;
+          const float h = gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * uv;
+          const uint16_t bh = f32_to_bf16_rne(h);
+          hi |= (uint32_t)bh << (16 * e);
+          lo |= (uint32_t)f32_to_bf16_rne(h - bf16_to_f32(bh)) << (16 * e);
+        }
+        const int j = q / (GPW * C::PAIRS), i = (q / C::PAIRS) % GPW, pp = q % C::PAIRS;
+        xs[((j * GPW + i) * 2 + 0) * C::PAIRS + pp] = hi;
+        xs[((j * GPW + i) * 2 + 1) * C::PAIRS + pp] = lo;
+      }
     }
   }
 };
 
-template <int BITS, int GPW, int XT>
+template <int BITS, int GPW, int XT, int KP>
 __global__ __launch_bounds__(256, 2) void k_down_blk(
     const moe_expert_ref* __restrict__ table, int E, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_pairs, int H, int I, int scale_f16,
-    const uint16_t* __restrict__ hh, const uint16_t* __restrict__ hl, float* __restrict__ pair_out) {
+    const int32_t* __restrict__ sorted_pairs, int H, int I, int P, int scale_f16,
+    const float* __restrict__ part, float* __restrict__ pair_out) {
   using C = UnitCodec<BITS>;
-  using HS = HStageBlk<BITS, GPW, XT>;
+  using HS = HFromParts<BITS, GPW, XT, KP>;
   constexpr int XW = XT * GPW * 2 * C::PAIRS;  // uint32 per wave: [token][group][hi|lo][pair]
   __shared__ float red[kDNWaves][kTokPerPass][64];
   __shared__ __align__(16) uint32_t xs_all[kDNWaves * XW];
@@ -535,7 +519,7 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
   int pids = sorted_pairs[seg0 + min(lane, n_e - 1)];
   HS hst;
   int nt = min(n_e, XT);
-  hst.load(hh, hl, I, seg0, nt, wv, ng - 1, lane);
+  hst.load(part, P, I, seg0, nt, wv, ng - 1, lane);
   asm volatile("" ::: "memory");
 
   u32x4 cw[GPW][C::CHUNKS];
@@ -558,7 +542,7 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
   for (int c0 = 0; c0 < n_e; c0 += XT) {
     if (c0 > 0) {
       nt = min(n_e - c0, XT);
-      hst.load(hh, hl, I, seg0 + c0, nt, wv, ng - 1, lane);
+      hst.load(part, P, I, seg0 + c0, nt, wv, ng - 1, lane);
       hst.store(xs, lane);
       if (c0 % 64 == 0) pids = sorted_pairs[seg0 + c0 + min(lane, n_e - c0 - 1)];
     }
@@ -747,17 +731,26 @@ static hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* sh
       default: return hipErrorInvalidValue;
     }
 #undef MOE_GU
-    MOE_LAUNCH(KID_SWIGLU, k_swiglu_kp, dim3(P), dim3(256), 0, s, gpart, f.offsets, E, P, I, KP, hh,
-               hl);
-#define MOE_DN(N)                                                                                \
+    // down: h formed from the KP gate and up parts while staging (no SwiGLU launch)
+#define MOE_DN(N, KPT)                                                                           \
   case N:                                                                                        \
-    MOE_LAUNCH(KID_DOWN, (k_down_blk<BITS, N, 2>), dim3(maxU, H / 64), dim3(64 * kDNWaves), 0, s,  \
-               f.table, E, f.offsets, f.sorted_pairs, H, I, c.scale_f16, hh, hl, y);             \
+    MOE_LAUNCH(KID_DOWN, (k_down_blk<BITS, N, 2, KPT>), dim3(maxU, H / 64), dim3(64 * kDNWaves), \
+               0, s, f.table, E, f.offsets, f.sorted_pairs, H, I, P, c.scale_f16, gpart, y);     \
     break;
-    switch (gpw_dn) {
-      MOE_DN(1) MOE_DN(2) MOE_DN(3) MOE_DN(4) MOE_DN(5) MOE_DN(6) MOE_DN(7) MOE_DN(8)
+#define MOE_DN_KP(KPT)                                                                           \
+    switch (gpw_dn) {                                                                            \
+      MOE_DN(1, KPT) MOE_DN(2, KPT) MOE_DN(3, KPT) MOE_DN(4, KPT)                                \
+      MOE_DN(5, KPT) MOE_DN(6, KPT) MOE_DN(7, KPT) MOE_DN(8, KPT)                                \
+      default: return hipErrorInvalidValue;                                                      \
+    }
+    switch (KP) {
+      case 1: MOE_DN_KP(1) break;
+      case 2: MOE_DN_KP(2) break;
+      case 3: MOE_DN_KP(3) break;
+      case 4: MOE_DN_KP(4) break;
       default: return hipErrorInvalidValue;
     }
+#undef MOE_DN_KP
 #undef MOE_DN
     // y holds every pair's output in pair order: a single "chunk"
     if (join) {
