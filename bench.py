@@ -8,7 +8,10 @@ HBM.  The default workload is one GLM-5.3-Flash-shaped MoE layer at decode batch
 1 (hidden 5120, expert intermediate 1536, 288 experts, top-8, 3-bit group-128
 weights with bf16 scales, Zipf(1.1) router bias).  Steps rotate over several
 resident copies of the layer (distinct weights, router and bias) so that no step
-is served from the 256 MB last-level cache.
+is served from the 256 MB last-level cache.  The timed steps are replays of HIP
+graphs that each hold several consecutive layer steps (a decoder replays one graph
+over all its layers), so the per-replay launch cost is shared as it is there; every
+step in a graph does the whole layer on its own layer's weights.
 
 Prints ONE JSON line: tokens/s over the timed steps, the dominant kernel's
 achieved expert-weight bandwidth against the 8 TB/s HBM peak (prefill: matrix-core
@@ -54,6 +57,10 @@ def parse():
     ap.add_argument("--layers", type=int, default=None,
                     help="resident layer copies the steps rotate over (default: 16 at decode)")
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--graph-steps", type=int, default=8,
+                    help="consecutive layer steps captured in one HIP graph for the single-layer "
+                         "workloads (as a decoder replays one graph over many layers); the largest "
+                         "value up to this that divides both --steps and the rotated layer count")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU-oracle baseline sample (0: skip)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -135,6 +142,12 @@ def main():
             off = ml.rb.expert_offsets.cpu().numpy()
             U.append(int((np.diff(off) > 0).sum()))
 
+    # G consecutive steps per graph (a stack step is already a whole pass)
+    G = 1
+    if not stack and not a.eager:
+        G = max(1, min(a.graph_steps, L, a.steps))
+        while a.steps % G or L % G:
+            G -= 1
     graphs = None
     if not a.eager:
         graphs = []
@@ -145,20 +158,21 @@ def main():
                 step(l)  # warm the capture stream
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
-        for l in range(1 if stack else L):
+        for j in range(1 if stack else L // G):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step(l)
+                for i in range(G):
+                    step(j * G + i)
             graphs.append(g)
         torch.cuda.synchronize()
 
-    def run(i):
+    def run(i):  # steps i .. i+G-1
         if graphs is not None:
-            graphs[i % len(graphs)].replay()
+            graphs[(i // G) % len(graphs)].replay()
         else:
             step(i % L)
 
-    for i in range(a.warmup):
+    for i in range(0, max(a.warmup, G), G):
         run(i)
     torch.cuda.synchronize()
 
@@ -167,7 +181,7 @@ def main():
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     ev0.record()
-    for i in range(a.steps):
+    for i in range(0, a.steps, G):
         run(i)
     ev1.record()
     torch.cuda.synchronize()
@@ -234,6 +248,7 @@ def main():
     extra["expert_GBs_over_step"] = round((gu_bytes + dn_bytes) / kt_steps / (ms_step * 1e-3) / 1e9, 1)
     extra["distinct_experts_per_step"] = round(float(np.mean(u_steps)), 2)
     extra["graph_replay"] = graphs is not None
+    extra["steps_per_graph"] = G if graphs is not None else None
     extra["input_gen_s"] = round(gen_s, 1)
 
     if a.calib_copy:

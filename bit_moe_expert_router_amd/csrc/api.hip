@@ -196,7 +196,7 @@ moe_status moe_route(moe_ctx* ctx, const void* x_bf16, int32_t T, const float* w
   hipError_t e = moe::launch_route(c, (const uint16_t*)x_bf16, T, w_router, bias, topk_ids, topk_w,
                                    expert_offsets, sorted_pairs, pair_pos,
                                    (double*)(w8 + L.logits), (int32_t*)(w8 + L.ghist),
-                                   (hipStream_t)stream);
+                                   (int32_t*)(w8 + L.counters), (hipStream_t)stream);
   return hip_status(e, "moe_route launch");
 }
 

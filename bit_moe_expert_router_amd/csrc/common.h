@@ -226,9 +226,42 @@ __device__ __forceinline__ float wave_sum_uniform(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// ---------------------------------------------------------------- cross-block hand-off
+// Kernels whose last-arriving block finishes the work.  The blocks' results go
+// out as agent-scope relaxed atomic stores (written through to the memory side
+// that every compute unit shares), each block waits until its own stores have
+// completed (vmcnt(0)) before it takes its ticket, and the last block reads the
+// results with agent-scope loads (which do not hit stale L2 lines).  There is
+// no cache-wide fence: a device-scope __threadfence() writes back and
+// invalidates the block's whole L2, microseconds per block when hundreds of
+// blocks do it.
+template <typename T>
+__device__ __forceinline__ void st_coherent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_coherent(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores have completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// ticket of a block (called by one thread after every wave's wait_stores and a
+// block barrier): the arrival count before this block
+__device__ __forceinline__ int take_ticket(int32_t* ctr) {
+  return __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---------------------------------------------------------------- workspace
-// counters reserved for cross-block signalling (kept zero between calls)
+// counters reserved for cross-block signalling (kept zero between calls): the
+// block that finds itself last to arrive does a kernel's final step and resets
+// its counter.  [kCtrRoute]: the routing kernel of small batches; [kCtrStrip +
+// s]: the blocks of 64-row strip s of the one/two-token down kernel.
 constexpr int kCounters = 1024;
+constexpr int kCtrRoute = 0;
+constexpr int kCtrStrip = 64;
 
 // Batches up to this many tokens run the GEMV (decode) kernels; larger ones the
 // matrix-core (prefill) kernels when the shape allows them.
@@ -298,7 +331,7 @@ __host__ inline WsLayout ws_layout(const moe_cfg& c, int T) {
 // ---------------------------------------------------------------- profiling
 enum KernelId {
   KID_LOGITS = 0, KID_TOPK, KID_PERMUTE, KID_PLAN, KID_GATEUP, KID_DOWN, KID_SH_GATEUP,
-  KID_SH_DOWN, KID_COMBINE, KID_RMSNORM, KID_ZERO, KID_XPREP, KID_SWIGLU, KID_COUNT
+  KID_SH_DOWN, KID_COMBINE, KID_RMSNORM, KID_ZERO, KID_XPREP, KID_SWIGLU, KID_ROUTE, KID_COUNT
 };
 // when profiling is on: a pair of events for the next launch of kernel kid
 bool prof_events(int kid, hipEvent_t* b, hipEvent_t* e);
@@ -342,7 +375,7 @@ hipError_t launch_shared(const FwdArgs& f, const WsLayout& L, hipStream_t s, flo
 hipError_t launch_route(const moe_cfg& c, const uint16_t* x, int T, const float* wr,
                         const float* bias, int32_t* ids, float* w, int32_t* offsets,
                         int32_t* sorted_pairs, int32_t* pair_pos, double* logits,
-                        int32_t* ghist, hipStream_t s);
+                        int32_t* ghist, int32_t* counters, hipStream_t s);
 hipError_t launch_forward(const FwdArgs& f, hipStream_t s);
 hipError_t launch_rmsnorm(float* resid, const float* add, int T, int H, float eps, uint16_t* y,
                           hipStream_t s);

@@ -331,25 +331,9 @@ __global__ __launch_bounds__(256, 2) void k_gateup_smem(
   const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
   const uint32_t* xv32 = reinterpret_cast<const uint32_t*>(x_vec);
 
-  // activation pairs of this wave's groups for the offset sums (lane = pair),
-  // requested before the weights so that their waits never wait for the weights
-  auto load_xo = [&](int t, uint32_t (&xo)[GPW]) {
-#pragma unroll
-    for (int i = 0; i < GPW; ++i) {
-      const int g = min(g0 + wv + kGUWaves * i, g1 - 1);
-      const int pl = lane < C::PAIRS ? lane : 0;
-      xo[i] = xv32[((int64_t)t * H + g * C::G) / 2 + pl];
-    }
-  };
-  int t0 = sorted_pairs[seg0] / K;
-  int t1 = n_e > 1 ? sorted_pairs[seg0 + 1] / K : t0;
-  uint32_t xo0[GPW], xo1[GPW];
-  load_xo(t0, xo0);
-  load_xo(t1, xo1);
-  asm volatile("" ::: "memory");
-
-  // weights: all groups of this wave at once (group index clamped, not branched
-  // on, so that the waits the compiler places stay exact)
+  // weights first: all groups of this wave at once (group index clamped, not
+  // branched on, so that the waits the compiler places stay exact); they need
+  // nothing but the expert's address
   u32x4 cw[GPW][C::CHUNKS];
   uint32_t sr[GPW];  // the aligned dword holding the scale (any 16-bit handling here would wait)
 #pragma unroll
@@ -359,6 +343,24 @@ __global__ __launch_bounds__(256, 2) void k_gateup_smem(
     sr[i] = load_scale_dword(msc, (int64_t)row * ng + g);
   }
   asm volatile("" ::: "memory");
+
+  // then the tokens (scalar loads, which the weights do not wait for) and the
+  // activation pairs of this wave's groups for the offset sums (lane = pair),
+  // needed only after the dot products
+  auto load_xo = [&](int t, uint32_t (&xo)[GPW]) {
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+      const int g = min(g0 + wv + kGUWaves * i, g1 - 1);
+      const int pl = lane < C::PAIRS ? lane : 0;
+      xo[i] = xv32[((int64_t)t * H + g * C::G) / 2 + pl];
+    }
+  };
+  const int sp0 = sorted_pairs[seg0], sp1 = sorted_pairs[seg0 + min(1, n_e - 1)];
+  int t0 = sp0 / K;
+  int t1 = n_e > 1 ? sp1 / K : t0;
+  uint32_t xo0[GPW], xo1[GPW];
+  load_xo(t0, xo0);
+  load_xo(t1, xo1);
 
   for (int b0 = 0; b0 < n_e; b0 += kTokPerPass) {
     const bool two = b0 + 1 < n_e;
@@ -432,8 +434,42 @@ __global__ __launch_bounds__(256, 2) void k_gateup_smem(
 // gate/up kernel: each wave requests h (hi and lo rows) of up to XT of the
 // expert's positions for its groups into its own LDS region, then its weights;
 // the token passes run from LDS with two dot products per code pair (hi, lo).
-// y goes to row p = t*K + k of pair_out.
+// y goes to row p = t*K + k of pair_out (stored written-through).  When `out` is
+// given, the block of each strip that takes the last ticket also forms
+// that strip's 64 columns of out[t] = sum_k w[t][k] y(t,k) (k ascending, pairs
+// with an id outside [0, E) skipped) + the shared expert's slices (added in
+// order): the same arithmetic, in the same order, as the combine kernel, one
+// launch fewer.  It resets the strip's ticket counter for the next call.
 constexpr int kDNWaves = 4;
+constexpr int kCombineMaxK = 16;
+
+// columns [64*strip, +64) of out for T <= 4 tokens (thread = (t, column))
+__device__ __forceinline__ void combine_strip(const float* y, const int32_t* __restrict__ ids,
+                                              const float* __restrict__ w, int K, int E, int H,
+                                              const float* shared, int nsh, int T, int strip,
+                                              float* __restrict__ out) {
+  const int t = threadIdx.x >> 6;
+  if (t >= T) return;
+  const int n = strip * 64 + (threadIdx.x & 63);
+  float v[kCombineMaxK];
+#pragma unroll
+  for (int k = 0; k < kCombineMaxK; ++k)
+    v[k] = ld_coherent(y + ((int64_t)t * K + min(k, K - 1)) * H + n);
+  float acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < kCombineMaxK; ++k) {
+    if (k < K) {
+      const int id = ids[t * K + k];
+      if (id >= 0 && id < E) acc = fmaf(w[t * K + k], v[k], acc);
+    }
+  }
+  if (shared) {
+    float sh = 0.f;
+    for (int q = 0; q < nsh; ++q) sh += shared[((int64_t)q * T + t) * H + n];
+    acc += sh;
+  }
+  out[(int64_t)t * H + n] = acc;
+}
 
 // h of the wave's groups for up to XT positions, formed from the KP gate and up
 // partial products (added in part order, as the SwiGLU pass of the larger
@@ -493,7 +529,9 @@ template <int BITS, int GPW, int XT, int KP>
 __global__ __launch_bounds__(256, 2) void k_down_blk(
     const moe_expert_ref* __restrict__ table, int E, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pairs, int H, int I, int P, int scale_f16,
-    const float* __restrict__ part, float* __restrict__ pair_out) {
+    const float* __restrict__ part, float* pair_out, const int32_t* __restrict__ ids,
+    const float* __restrict__ wts, int K, int T, const float* shared, int nsh,
+    int32_t* __restrict__ ctr, float* __restrict__ out) {
   using C = UnitCodec<BITS>;
   using HS = HFromParts<BITS, GPW, XT, KP>;
   constexpr int XW = XT * GPW * 2 * C::PAIRS;  // uint32 per wave: [token][group][hi|lo][pair]
@@ -502,10 +540,14 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
   const int ng = I / C::G;
 
   const Active act = find_active(offsets, table, E, blockIdx.x);
-  if (act.e < 0) return;
+  const int strip = blockIdx.y;
+  if (act.e < 0) {  // no expert for this block; with none at all, block 0 combines
+    if (out && act.U == 0 && blockIdx.x == 0)
+      combine_strip(pair_out, ids, wts, K, E, H, shared, nsh, T, strip, out);
+    return;
+  }
   const int seg0 = __builtin_amdgcn_readfirstlane(act.seg0);
   const int n_e = __builtin_amdgcn_readfirstlane(act.n);
-  const int strip = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const MatGeom gm{H, I, BITS, C::G};
@@ -591,9 +633,20 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
         for (int ww = 0; ww < kDNWaves; ++ww) y += red[ww][j][lane];
         const int idx = (c0 + jp + j) % 64;  // wave-uniform
         const int p = __builtin_amdgcn_readlane(pids, idx);
-        pair_out[(int64_t)p * H + row] = y;
+        st_coherent(pair_out + (int64_t)p * H + row, y);
       }
       lds_barrier();
+    }
+  }
+  if (out) {  // the strip's last block combines
+    __shared__ int s_last;
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = take_ticket(ctr + strip) == act.U - 1;
+    __syncthreads();
+    if (s_last) {
+      combine_strip(pair_out, ids, wts, K, E, H, shared, nsh, T, strip, out);
+      if (threadIdx.x == 0) st_coherent(ctr + strip, 0);
     }
   }
 }
@@ -731,11 +784,20 @@ static hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* sh
       default: return hipErrorInvalidValue;
     }
 #undef MOE_GU
-    // down: h formed from the KP gate and up parts while staging (no SwiGLU launch)
+    // down: h formed from the KP gate and up parts while staging (no SwiGLU
+    // launch); each strip's last block combines (no combine launch)
+    const bool fuse = K <= kCombineMaxK && H / 64 <= kCounters - kCtrStrip;
+    int32_t* ctr = reinterpret_cast<int32_t*>(f.ws + L.counters) + kCtrStrip;
+    float* cout = fuse ? f.out : nullptr;
+    if (join) {  // the combine adds the shared expert's output
+      const hipError_t e = hipStreamWaitEvent(s, join, 0);
+      if (e != hipSuccess) return e;
+    }
 #define MOE_DN(N, KPT)                                                                           \
   case N:                                                                                        \
     MOE_LAUNCH(KID_DOWN, (k_down_blk<BITS, N, 2, KPT>), dim3(maxU, H / 64), dim3(64 * kDNWaves), \
-               0, s, f.table, E, f.offsets, f.sorted_pairs, H, I, P, c.scale_f16, gpart, y);     \
+               0, s, f.table, E, f.offsets, f.sorted_pairs, H, I, P, c.scale_f16, gpart, y,      \
+               f.ids, f.w, K, T, shared_out, nsh, ctr, cout);                                    \
     break;
 #define MOE_DN_KP(KPT)                                                                           \
     switch (gpw_dn) {                                                                            \
@@ -752,11 +814,8 @@ static hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* sh
     }
 #undef MOE_DN_KP
 #undef MOE_DN
+    if (fuse) return hipGetLastError();
     // y holds every pair's output in pair order: a single "chunk"
-    if (join) {
-      const hipError_t e = hipStreamWaitEvent(s, join, 0);
-      if (e != hipSuccess) return e;
-    }
     if (K <= 8) {
       MOE_LAUNCH(KID_COMBINE, (k_combine_parts<8, 1>), dim3((H + 255) / 256, T), dim3(256), 0, s, y,
                  1, P, f.ids, f.w, K, E, H, shared_out, nsh, T, f.out, nullptr);

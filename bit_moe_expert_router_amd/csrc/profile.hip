@@ -19,7 +19,8 @@ namespace {
 
 const char* const kNames[KID_COUNT] = {"route_logits", "route_topk", "route_permute", "plan",
                                        "gateup",       "down",       "shared_gateup", "shared_down",
-                                       "combine",      "rmsnorm",    "zero",          "xprep",        "swiglu"};
+                                       "combine",      "rmsnorm",    "zero",          "xprep",        "swiglu",
+                                       "route"};
 
 struct Rec {
   int kid;

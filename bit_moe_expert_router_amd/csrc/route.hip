@@ -20,19 +20,21 @@
 namespace moe {
 
 // ---------------------------------------------------------------- logits, small T
-// Block = one expert x up to 4 tokens; 256 threads stride over H in float4 steps,
-// each thread issuing all its loads of a batch (8 float4 of the router row and
-// the matching activations of every token) before using any, so a 5120-wide row
-// costs one memory round trip.  Items past the row end load the last item and
-// use a zero router value.
+// Block = one expert x up to NT (1, 2 or 4) tokens; 256 threads stride over H in
+// float4 steps, each thread issuing all its loads of a batch (8 float4 of the
+// router row and the matching activations of every token) before using any, so
+// a 5120-wide row costs one memory round trip.  Items past the row end load the
+// last item and use a zero router value.
 constexpr int kLogitTok = 4;
 constexpr int kLogitBatch = 8;
 
-__global__ __launch_bounds__(256) void k_logits_small(const uint16_t* __restrict__ x, int T,
-                                                      int H, int E,
-                                                      const float* __restrict__ wr,
-                                                      const float* __restrict__ bias,
-                                                      double* __restrict__ logits) {
+// Block (e, token chunk): logits of expert e for tokens t0 .. t0+NT-1.
+template <int NT>
+__device__ __forceinline__ void logits_small_block(const uint16_t* __restrict__ x, int T, int H,
+                                                   int E, const float* __restrict__ wr,
+                                                   const float* __restrict__ bias,
+                                                   double* __restrict__ logits) {
+  constexpr int kLogitTok = NT;
   const int e = blockIdx.x;
   const int t0 = blockIdx.y * kLogitTok;
   const int nt = min(kLogitTok, T - t0);
@@ -80,8 +82,16 @@ __global__ __launch_bounds__(256) void k_logits_small(const uint16_t* __restrict
     const int j = threadIdx.x;
     double v = ((red[0][j] + red[1][j]) + red[2][j]) + red[3][j];
     if (bias) v += (double)bias[e];
-    logits[(int64_t)(t0 + j) * E + e] = v;
+    st_coherent(logits + (int64_t)(t0 + j) * E + e, v);
   }
+}
+
+__global__ __launch_bounds__(256) void k_logits_small(const uint16_t* __restrict__ x, int T,
+                                                      int H, int E,
+                                                      const float* __restrict__ wr,
+                                                      const float* __restrict__ bias,
+                                                      double* __restrict__ logits) {
+  logits_small_block<kLogitTok>(x, T, H, E, wr, bias, logits);
 }
 
 // ---------------------------------------------------------------- logits, large T
@@ -222,7 +232,7 @@ __device__ __forceinline__ int wave_topk(const double* __restrict__ l, int E, in
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane + 64 * i;
-    v[i] = e < E ? l[e] : -INFINITY;
+    v[i] = e < E ? ld_coherent(l + e) : -INFINITY;
     id[i] = e < E ? e : 0x7FFFFFFF;
   }
 #pragma unroll
@@ -461,11 +471,11 @@ __global__ __launch_bounds__(64) void k_group_scatter(const int32_t* __restrict_
   }
 }
 
-// ---------------------------------------------------------------- top-k + grouping, small T
-// Decode batches (T <= 16, T * K <= 64): wave t picks the top-k of token t, then
-// the first wave groups the T*K pairs, one pair per lane.  A pair's key is
-// (expert id, pair index); its sorted position is the number of smaller keys,
-// counted bit by bit from the top with one ballot per key bit.  Offsets: each
+// ---------------------------------------------------------------- grouping, small T
+// Decode batches (T <= 16, T * K <= 64): one wave groups the T*K pairs, one pair
+// per lane.  A pair's key is (expert id, pair index); its sorted position is the
+// number of smaller keys, counted bit by bit from the top with one ballot per
+// key bit.  Offsets: each
 // expert's first pair writes its pair count into a zeroed LDS histogram, which
 // a DPP prefix sum turns into the exclusive scan.  Integer only: bit-exact.
 __device__ __forceinline__ int wave_incl_scan(int v) {
@@ -531,6 +541,8 @@ __device__ __forceinline__ void wave_group_small(int id, int P, int E, int* cnt,
   }
 }
 
+// Decode batches of 3 to 16 tokens: wave t picks the top-k of token t, then the
+// first wave groups the pairs (one launch after the logits).
 template <int PER>
 __global__ __launch_bounds__(1024) void k_topk_group_small(
     const double* __restrict__ logits, int T, int E, int K, int32_t* __restrict__ ids,
@@ -555,24 +567,82 @@ __global__ __launch_bounds__(1024) void k_topk_group_small(
   }
 }
 
+// ---------------------------------------------------------------- one launch, small T
+// Logits, top-k and grouping of a batch of one or two tokens in one kernel: the
+// logit blocks above (logits stored written-through), then the block that takes
+// the last ticket, whose loads see every block's logits, picks the top-k of every
+// token (wave w takes token w) and its first wave groups the pairs.  It resets
+// the ticket counter for the next call.  (Larger batches pick in a kernel of
+// their own with one wave per token: the last block's four waves would take
+// their tokens in turn.)
+template <int NT, int PER>
+__global__ __launch_bounds__(256) void k_route_small(
+    const uint16_t* __restrict__ x, int T, int H, int E, const float* __restrict__ wr,
+    const float* __restrict__ bias, double* logits, int K, int32_t* __restrict__ ids,
+    float* __restrict__ wout, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
+    int32_t* __restrict__ pair_pos, int32_t* __restrict__ ctr) {
+  logits_small_block<NT>(x, T, H, E, wr, bias, logits);
+  __shared__ int s_last;
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = take_ticket(ctr) == (int)(gridDim.x * gridDim.y) - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __shared__ int32_t s_ids[64];
+  __shared__ int cnt[kMaxE + 1];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wv < T) {
+    const int t = wv;
+    float wk;
+    const int id = wave_topk<PER>(logits + (int64_t)t * E, E, K, &wk);
+    if (lane < K) {
+      ids[t * K + lane] = id;
+      wout[t * K + lane] = wk;
+      s_ids[t * K + lane] = id;
+    }
+  }
+  __syncthreads();
+  if (wv == 0) {
+    const int P = T * K;
+    wave_group_small(lane < P ? s_ids[lane] : -1, P, E, cnt, offsets, sorted_pairs, pair_pos);
+    if (lane == 0) st_coherent(ctr, 0);
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 hipError_t launch_route(const moe_cfg& c, const uint16_t* x, int T, const float* wr,
                         const float* bias, int32_t* ids, float* w, int32_t* offsets,
                         int32_t* sorted_pairs, int32_t* pair_pos, double* logits,
-                        int32_t* ghist, hipStream_t s) {
+                        int32_t* ghist, int32_t* counters, hipStream_t s) {
   const int H = c.hidden, E = c.n_experts, K = c.top_k, P = T * K;
+  const int per = (E + 63) / 64;
+#define MOE_PER_SWITCH(X)                                                    \
+  switch (per <= 8 ? per : 16) {                                             \
+    X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(16)                            \
+    default: return hipErrorInvalidValue;                                    \
+  }
+  if (T <= 2 && P <= 64) {  // one launch
+    int32_t* ctr = counters + kCtrRoute;
+#define MOE_RS(N)                                                                               \
+  case N:                                                                                       \
+    if (T == 1)                                                                                 \
+      MOE_LAUNCH(KID_ROUTE, (k_route_small<1, N>), dim3(E), dim3(256), 0, s, x, T, H, E, wr,    \
+                 bias, logits, K, ids, w, offsets, sorted_pairs, pair_pos, ctr);                \
+    else                                                                                        \
+      MOE_LAUNCH(KID_ROUTE, (k_route_small<2, N>), dim3(E), dim3(256), 0, s, x, T, H, E, wr,    \
+                 bias, logits, K, ids, w, offsets, sorted_pairs, pair_pos, ctr);                \
+    break;
+    MOE_PER_SWITCH(MOE_RS)
+#undef MOE_RS
+    return hipGetLastError();
+  }
   if (T <= 32) {
     MOE_LAUNCH(KID_LOGITS, k_logits_small, dim3(E, (T + kLogitTok - 1) / kLogitTok), dim3(256), 0, s,
                x, T, H, E, wr, bias, logits);
   } else {
     MOE_LAUNCH(KID_LOGITS, k_logits_mfma, dim3((E + kLE - 1) / kLE, (T + kLT - 1) / kLT), dim3(256),
                0, s, x, T, H, E, wr, bias, logits);
-  }
-  const int per = (E + 63) / 64;
-#define MOE_PER_SWITCH(X)                                                    \
-  switch (per <= 8 ? per : 16) {                                             \
-    X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(16)                            \
-    default: return hipErrorInvalidValue;                                    \
   }
   if (T <= 16 && P <= 64) {
 #define MOE_TGS(N)                                                                             \

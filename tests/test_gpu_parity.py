@@ -55,8 +55,8 @@ def test_device_fill_matches_host_generator(gpu):
                 assert np.array_equal(dev_t.cpu().numpy().view(np.uint16), h)
 
 
-ROUTE_CASES = [("c1", 4), ("c1", 1), ("c1", 37), ("c2", 1), ("c2", 2), ("c2", 5), ("c3", 8),
-               ("c3", 64), ("c3", 65), ("c3", 300), ("c5", 8192)]
+ROUTE_CASES = [("c1", 4), ("c1", 1), ("c1", 16), ("c1", 37), ("c2", 1), ("c2", 2), ("c2", 5),
+               ("c3", 8), ("c3", 64), ("c3", 65), ("c3", 300), ("c5", 8192)]
 
 
 @pytest.mark.parametrize("name,T", ROUTE_CASES)
@@ -77,8 +77,8 @@ def test_routing_bit_exact(gpu, name, T):
 
 # decode batches run the GEMV kernels; T > 64 the matrix-core (prefill) kernels:
 # the 4-bit/G32/fp16-scale shape at T = 300 and the GLM shape just past the switch
-FFN_CASES = [("c1", 4), ("c1", 1), ("c1", 13), ("c2", 1), ("c2", 3), ("c3", 8), ("c3", 9),
-             ("c1", 300), ("c2", 65)]
+FFN_CASES = [("c1", 4), ("c1", 1), ("c1", 13), ("c2", 1), ("c2", 3), ("c3", 1), ("c3", 2),
+             ("c3", 8), ("c3", 9), ("c1", 300), ("c2", 65)]
 
 
 @pytest.mark.parametrize("name,T", FFN_CASES)
@@ -244,6 +244,45 @@ def test_zero_weight_pair_equals_dropped_pair(gpu):
     ref, _ = oracle.moe_layer(xh, ids_d, w.astype(np.float64), *tabs, cfg.inter, cfg.bits,
                               cfg.group, cfg.scale_f16, he.shared())
     assert rel_err(c["out"][3], ref[3]) <= TOL
+
+
+@pytest.mark.parametrize("name,T", [("c2", 1), ("c3", 1), ("c3", 2)])
+def test_small_batch_all_pairs_dropped(gpu, name, T):
+    """one/two-token batches with every pair left out: no expert runs, and each
+    token's output is the shared expert's alone (zero without one)"""
+    say(f"[inv] all dropped {name} T={T}")
+    cfg = synth.CONFIGS[name]
+    dl = layer_for(name, gpu)
+    xh, xd = x_device(cfg, gpu, tokens=T)
+    ids = np.full((T, cfg.top_k), -1, dtype=np.int32)
+    w = np.full((T, cfg.top_k), 1.0 / cfg.top_k, dtype=np.float32)
+    ml = make_layer_api(cfg, dl, T)
+    res = run_gpu(cfg, dl, xd, ml=ml, routing=_caller_routing(ml, ids, w, cfg.n_experts, gpu))
+    he = HostExperts(cfg)
+    dummy = [[np.zeros(16, np.uint8)] * cfg.n_experts for _ in range(3)]
+    ref, _ = oracle.moe_layer(xh, ids, w.astype(np.float64), *dummy, cfg.inter, cfg.bits,
+                              cfg.group, cfg.scale_f16, he.shared())
+    for t in range(T):
+        if he.shared() is None:
+            assert not np.any(res["out"][t]), t
+        else:
+            assert rel_err(res["out"][t], ref[t]) <= TOL, t
+    ml.close()
+
+
+def test_counters_left_zero(gpu):
+    """the workspace's cross-block counters are zero again after every call"""
+    say("[inv] counters")
+    cfg = synth.CONFIGS["c3"]
+    dl = layer_for("c3", gpu)
+    ml = make_layer_api(cfg, dl, 64)
+    for T in (1, 2, 5, 8, 64):
+        _, xd = x_device(cfg, gpu, tokens=T)
+        for _ in range(2):
+            run_gpu(cfg, dl, xd, ml=ml)
+        ctr = ml.ws[:4096].view(torch.int32)
+        assert int(torch.count_nonzero(ctr)) == 0, T
+    ml.close()
 
 
 # ------------------------------------------------------------------ status codes
