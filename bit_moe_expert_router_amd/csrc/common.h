@@ -275,6 +275,11 @@ __host__ __device__ inline int64_t prefill_max_tiles(int64_t P, int64_t E) {
   return (P + kPrefillTileRows - 1) / kPrefillTileRows + (E < P ? E : P);
 }
 
+// Reduction groups per decode GEMV work item (gate/up, down): three each, which
+// keeps the kernels free of register spills at three waves per SIMD.
+constexpr int kDecGPW = 3;
+constexpr int kDecGPWd = 3;
+
 // Layout of the caller's workspace for T tokens (byte offsets, 256-aligned).
 // Regions a mode does not use have size 0.
 struct WsLayout {
@@ -310,8 +315,9 @@ __host__ inline WsLayout ws_layout(const moe_cfg& c, int T) {
   L.logits = take((int64_t)T * c.n_experts * 8);
   L.ghist = take((P + 1023) / 1024 * c.n_experts * 4);
   const bool pf = prefill_eligible(c, T);
-  // chunks of 4 (gate/up) and 3 (down) reduction groups per decode work item
-  const int64_t nch_gu = (c.hidden / c.group + 3) / 4, nch_dn = (c.inter / c.group + 2) / 3;
+  // chunks of kDecGPW (gate/up) and kDecGPWd (down) reduction groups per decode work item
+  const int64_t nch_gu = (c.hidden / c.group + kDecGPW - 1) / kDecGPW;
+  const int64_t nch_dn = (c.inter / c.group + kDecGPWd - 1) / kDecGPWd;
   L.act = take(pf ? 0 : 64 + 40 * (int64_t)c.n_experts);
   L.gpart = take(pf ? 0 : 2 * nch_gu * P * c.inter * 4);
   L.hdec = take(pf ? 0 : 2 * P * c.inter * 2);

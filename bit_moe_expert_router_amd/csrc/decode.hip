@@ -8,13 +8,16 @@
 //
 // Work decomposition.  A plan kernel lists the active experts (those owning at
 // least one pair) with their pair segment and blob pointers.  The GEMV kernels
-// then run a fixed grid of waves that take work items in turn: an item is (active
-// expert, 64-row strip, matrix, chunk of GPW reduction groups).  A wave requests
-// the item's codes and scales (one 16-byte load per chunk of a 64-row tile: 1,024
-// contiguous bytes per wave) and the activations of its groups for up to XT of
-// the expert's tokens (into the wave's own LDS region), then forms the partial
-// products of its 64 rows for every token and writes them to a partial buffer,
-// one slice per chunk.  No item waits on another: there are no block barriers
+// then run a fixed grid of waves that take work items in a zig-zag order: an
+// item is (active expert, 64-row strip, matrix, chunk of GPW reduction groups).
+// A wave requests the item's codes and scales first (one 16-byte load per chunk
+// of a 64-row tile: 1,024 contiguous bytes per wave), then the activations of its
+// groups for up to XT of the expert's tokens, then forms the partial products of
+// its 64 rows for every token and writes them to a partial buffer, one slice per
+// chunk.  The activations reach the dot products through scalar loads (one load
+// of 8 pairs serves all 64 lanes); a broadcast through LDS or a vector load would
+// move every byte 64 times, which made items with several tokens LDS-bound.  No
+// item waits on another: there are no block barriers
 // and no cross-wave reductions, and a wave that finishes an item starts the
 // next one at once, so the weight stream stays in flight.  The slices are added
 // in chunk order by the SwiGLU pass (gate/up) and by the combine (down): results
@@ -40,30 +43,56 @@ struct ActEntry {
 
 // ---------------------------------------------------------------- plan
 // act_hdr[0] = U, the number of experts owning at least one pair; act[a] for
-// a < U in ascending expert id.
+// a < U lists them by descending pair count (count clamped at 63), ties by
+// ascending expert id, so that the GEMVs' zig-zag item order gives every wave a
+// similar mix of heavy and light items.  The order only schedules work: where
+// an item's results land depends on the item alone.
+constexpr int kPlanKeys = 65;  // 0..63: 63 - min(n, 63) for active experts; 64: inactive
+
 __global__ __launch_bounds__(1024) void k_plan_decode(const int32_t* __restrict__ offsets,
                                                       const moe_expert_ref* __restrict__ table,
                                                       int E, int32_t* __restrict__ act_hdr,
                                                       ActEntry* __restrict__ act) {
-  __shared__ int wsum[16];
+  __shared__ int cntw[16][kPlanKeys];  // per wave and key: experts (then the exclusive prefix over waves)
+  __shared__ int base[kPlanKeys];      // exclusive prefix over keys of the totals
   const int e = threadIdx.x, lane = e & 63, wv = e >> 6;
+  for (int i = e; i < 16 * kPlanKeys; i += 1024) (&cntw[0][0])[i] = 0;
   const int lo = e < E ? offsets[e] : 0;
   const int n = e < E ? offsets[e + 1] - lo : 0;
-  const int f = n > 0 ? 1 : 0;
-  int inc = f;
+  const int key = n > 0 ? 63 - min(n, 63) : 64;
+  // lanes of this wave with the same key (one ballot per key bit)
+  uint64_t eq = __ballot(1);
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(inc, o);
-    if (lane >= o) inc += y;
+  for (int b = 0; b < 7; ++b) {
+    const uint64_t bal = __ballot((key >> b) & 1);
+    eq &= ((key >> b) & 1) ? bal : ~bal;
   }
-  if (lane == 63) wsum[wv] = inc;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  const int below = __popcll(eq & lt);
   __syncthreads();
-  int a = inc - f, total = 0;
-  for (int w = 0; w < 16; ++w) {
-    if (w < wv) a += wsum[w];
-    total += wsum[w];
+  if (below == 0) cntw[wv][key] = __popcll(eq);
+  __syncthreads();
+  if (e < kPlanKeys) {  // thread k: prefix of key k over the waves, and its total
+    int run = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int c = cntw[w][e];
+      cntw[w][e] = run;
+      run += c;
+    }
+    base[e] = run;
   }
-  if (f) {
+  __syncthreads();
+  if (e == 0) {  // exclusive prefix over the keys (65 entries)
+    int run = 0;
+    for (int k = 0; k < kPlanKeys; ++k) {
+      const int c = base[k];
+      base[k] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  if (n > 0) {
+    const int a = base[key] + cntw[wv][key] + below;
     const moe_expert_ref r = table[e];
     ActEntry ent;
     ent.e = e;
@@ -75,7 +104,7 @@ __global__ __launch_bounds__(1024) void k_plan_decode(const int32_t* __restrict_
     ent.ptr[2] = r.down;
     act[a] = ent;
   }
-  if (e == 0) act_hdr[0] = total;
+  if (e == 0) act_hdr[0] = base[64];
 }
 
 // ---------------------------------------------------------------- GEMV
@@ -95,8 +124,8 @@ __global__ __launch_bounds__(256, WPS) void k_gemv(
   constexpr int NQ = XT * GPW * NS * PC;       // pieces of a staged chunk of tokens
   constexpr int IT = (NQ + 63) / 64;
   constexpr int XW = XT * GPW * NS * C::PAIRS;  // uint32 per wave: [token][group][row][pair]
+  static_assert(XW == 4 * NQ, "a staged piece is 16 bytes");
   __shared__ __align__(16) uint32_t xs_all[4 * XW];
-  typedef const u32x4d __attribute__((address_space(1)))* g4;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint32_t* xs = xs_all + wv * XW;
@@ -107,7 +136,12 @@ __global__ __launch_bounds__(256, WPS) void k_gemv(
   const float off = lane < C::PAIRS ? C::pair_off(lane) : 0.f;
   const MatGeom gm{R, D, BITS, C::G};
 
-  for (int item = blockIdx.x * 4 + wv; item < total; item += nw) {
+  // zig-zag over the waves: round r takes items r*nw .. r*nw + nw-1, forwards
+  // on even rounds and backwards on odd ones
+  const int w_id = blockIdx.x * 4 + wv;
+  for (int r = 0; r * nw < total; ++r) {
+    const int item = r * nw + ((r & 1) ? nw - 1 - w_id : w_id);
+    if (item >= total) continue;
     const int a = item / per_a, r0 = item - a * per_a;
     const int strip = r0 / (NM * NCH), r1 = r0 - strip * (NM * NCH);
     const int m = r1 / NCH, ch = r1 - m * NCH;
@@ -116,10 +150,9 @@ __global__ __launch_bounds__(256, WPS) void k_gemv(
     const gu16_t msc = (gu16_t)(mat + gm.scales_off());
     const int row = strip * 64 + lane;
     const int g0 = ch * GPW, g1 = min(ng, g0 + GPW);
-    // pair id of each of the expert's first 64 positions (lane = position)
-    int pl = sorted_pairs[seg0 + min(lane, n_e - 1)];
 
-    // the item's codes and scales (group index clamped, not branched on)
+    // the item's codes and scales first: they need only the expert's address
+    // (group index clamped, not branched on)
     u32x4 cw[GPW][C::CHUNKS];
     uint32_t sr[GPW];
 #pragma unroll
@@ -128,43 +161,77 @@ __global__ __launch_bounds__(256, WPS) void k_gemv(
       load_unit4<BITS>(mat, (int64_t)strip * ng + g, lane, cw[i]);
       sr[i] = load_scale_dword(msc, (int64_t)row * ng + g);
     }
+    asm volatile("" ::: "memory");
+    // staging index math from a copy of the lane id, redone per item rather than
+    // hoisted out of the item loop (where it would be spilled)
+    int lq = lane;
+    asm volatile("" : "+v"(lq));
 
     for (int c0 = 0; c0 < n_e; c0 += XT) {
-      if (c0 > 0 && c0 % 64 == 0) pl = sorted_pairs[seg0 + c0 + min(lane, n_e - c0 - 1)];
       const int nt = min(n_e - c0, XT);
-      // activations of tokens c0 .. c0+nt-1 for the item's groups
-      u32x4d v[IT];
+      // pair ids of positions c0 .. c0+XT-1 (clamped to the expert's last):
+      // uniform, so scalar loads, which the activation loads need not wait for
+      // behind the weights
+      int pid[XT];
+#pragma unroll
+      for (int j = 0; j < XT; ++j) {
+        pid[j] = sorted_pairs[seg0 + c0 + min(j, nt - 1)];
+        asm volatile("" : "+s"(pid[j]));  // each a scalar load of its own
+      }
+      // activations of tokens c0 .. c0+nt-1 for the item's groups, staged in
+      // the wave's LDS region (lane = pair) for the offset sums; the dot
+      // products read the same rows through scalar loads.  (A global->LDS copy
+      // instruction would save the registers, but the compiler then no longer
+      // treats the activations as read-only and turns every scalar load into a
+      // 64-lane broadcast load.)  The wave's earlier LDS reads have completed
+      // before the region is overwritten.
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
 #pragma unroll
       for (int it = 0; it < IT; ++it) {
-        const int q = min(it * 64 + lane, NQ - 1);
-        const int j = min(q / (GPW * NS * PC), nt - 1), i = (q / (NS * PC)) % GPW;
-        const int sel = (q / PC) % NS, pc = q % PC;
+        const int q = it * 64 + lq;
+        const int qc = min(q, NQ - 1);
+        const int j = min(qc / (GPW * NS * PC), nt - 1), i = (qc / (NS * PC)) % GPW;
+        const int sel = (qc / PC) % NS, pc = qc % PC;
         const int g = min(g0 + i, g1 - 1);
         const uint16_t* src;
         if (MODE == 0) {
-          const int tok = __shfl(pl, (c0 % 64) + j) / K;
-          src = xa + (int64_t)tok * D + g * C::G + 8 * pc;
+          int pj = pid[0];
+#pragma unroll
+          for (int jj = 1; jj < XT; ++jj) pj = j == jj ? pid[jj] : pj;
+          src = xa + (int64_t)(pj / K) * D + g * C::G + 8 * pc;
         } else {
           src = (sel ? xb : xa) + (int64_t)(seg0 + c0 + j) * D + g * C::G + 8 * pc;
         }
-        v[it] = *(g4)(as_global(src));
-      }
-#pragma unroll
-      for (int it = 0; it < IT; ++it) {
-        const int q = it * 64 + lane;
-        if (q < NQ) *reinterpret_cast<u32x4d*>(xs + 4 * q) = v[it];
+        if (NQ % 64 == 0 || q < NQ)
+          *reinterpret_cast<u32x4d*>(xs + 4 * q) = *reinterpret_cast<const u32x4d*>(src);
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's own LDS writes
 
       for (int jp = 0; jp < nt; jp += 2) {
         const bool two = jp + 1 < nt;
         const int j1 = two ? jp + 1 : jp;
+        // the two tokens' activation rows in global memory (uniform addresses:
+        // the dot products take them through scalar loads, one load per 8 or 16
+        // pairs for the whole wave)
+        const uint32_t *r0a, *r0b, *r1a, *r1b;
+        if (MODE == 0) {
+          const int t0 = sorted_pairs[seg0 + c0 + jp] / K, t1 = sorted_pairs[seg0 + c0 + j1] / K;
+          r0a = r0b = reinterpret_cast<const uint32_t*>(xa + (int64_t)t0 * D);
+          r1a = r1b = reinterpret_cast<const uint32_t*>(xa + (int64_t)t1 * D);
+        } else {
+          r0a = reinterpret_cast<const uint32_t*>(xa + (int64_t)(seg0 + c0 + jp) * D);
+          r0b = reinterpret_cast<const uint32_t*>(xb + (int64_t)(seg0 + c0 + jp) * D);
+          r1a = reinterpret_cast<const uint32_t*>(xa + (int64_t)(seg0 + c0 + j1) * D);
+          r1b = reinterpret_cast<const uint32_t*>(xb + (int64_t)(seg0 + c0 + j1) * D);
+        }
         float a0 = 0.f, a1 = 0.f;
 #pragma unroll
         for (int i = 0; i < GPW; ++i) {
           if (g0 + i < g1) {
             const uint32_t* x0 = xs + (jp * GPW + i) * NS * C::PAIRS;
             const uint32_t* x1 = xs + (j1 * GPW + i) * NS * C::PAIRS;
+            const int go = (g0 + i) * C::G / 2;
+            const uint32_t *s0a = r0a + go, *s0b = r0b + go, *s1a = r1a + go, *s1b = r1b + go;
             uint32_t sraw = sr[i];
             asm volatile("" : "+v"(sraw));  // convert here, not hoisted ahead of the loads
             const float sc =
@@ -187,18 +254,18 @@ __global__ __launch_bounds__(256, WPS) void k_gemv(
               const float k1 = osum(x1);
               C::for_each_pair(w, [&](int Pp, uint32_t pr) {
                 if (NS == 2) {
-                  d0 = dot2_bf16(pr, x0[C::PAIRS + Pp], dot2_bf16(pr, x0[Pp], d0));
-                  d1 = dot2_bf16(pr, x1[C::PAIRS + Pp], dot2_bf16(pr, x1[Pp], d1));
+                  d0 = dot2_bf16(pr, s0b[Pp], dot2_bf16(pr, s0a[Pp], d0));
+                  d1 = dot2_bf16(pr, s1b[Pp], dot2_bf16(pr, s1a[Pp], d1));
                 } else {
-                  d0 = dot2_bf16(pr, x0[Pp], d0);
-                  d1 = dot2_bf16(pr, x1[Pp], d1);
+                  d0 = dot2_bf16(pr, s0a[Pp], d0);
+                  d1 = dot2_bf16(pr, s1a[Pp], d1);
                 }
               });
               a1 = fmaf(sc, d1 - k1, a1);
             } else {
               C::for_each_pair(w, [&](int Pp, uint32_t pr) {
-                if (NS == 2) d0 = dot2_bf16(pr, x0[C::PAIRS + Pp], dot2_bf16(pr, x0[Pp], d0));
-                else d0 = dot2_bf16(pr, x0[Pp], d0);
+                if (NS == 2) d0 = dot2_bf16(pr, s0b[Pp], dot2_bf16(pr, s0a[Pp], d0));
+                else d0 = dot2_bf16(pr, s0a[Pp], d0);
               });
             }
             a0 = fmaf(sc, d0 - k0, a0);
@@ -209,12 +276,8 @@ __global__ __launch_bounds__(256, WPS) void k_gemv(
           o[0] = a0;
           if (two) o[R] = a1;
         } else {
-          const int p0 = __builtin_amdgcn_readlane(pl, (c0 + jp) % 64);
-          out[((int64_t)ch * P + p0) * R + row] = a0;
-          if (two) {
-            const int p1 = __builtin_amdgcn_readlane(pl, (c0 + jp + 1) % 64);
-            out[((int64_t)ch * P + p1) * R + row] = a1;
-          }
+          out[((int64_t)ch * P + pid[jp]) * R + row] = a0;
+          if (two) out[((int64_t)ch * P + pid[jp + 1]) * R + row] = a1;
         }
       }
     }
@@ -654,9 +717,8 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
 // ---------------------------------------------------------------- SwiGLU
 // h[pos][k] = silu(sum_ch g_ch) * (sum_ch u_ch), slices added in chunk order,
 // as bf16 hi + bf16 remainder (h to ~2^-16 relative).  Positions past the
-// grouped pairs are skipped.
-constexpr int kMaxChunks = 16;
-
+// grouped pairs are skipped.  MC >= NCH bounds the chunk slices read per element.
+template <int MC>
 __global__ __launch_bounds__(256) void k_swiglu_sum(const float* __restrict__ part,
                                                     const int32_t* __restrict__ offsets, int E,
                                                     int P, int I, int NCH,
@@ -665,16 +727,16 @@ __global__ __launch_bounds__(256) void k_swiglu_sum(const float* __restrict__ pa
   const int pos = blockIdx.y;
   const int k = blockIdx.x * 256 + threadIdx.x;
   if (pos >= offsets[E] || k >= I) return;
-  float pg[kMaxChunks], pu[kMaxChunks];
+  float pg[MC], pu[MC];
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
+  for (int c = 0; c < MC; ++c) {
     const int cc = min(c, NCH - 1);
     pg[c] = part[((int64_t)cc * P + pos) * I + k];
     pu[c] = part[((int64_t)(NCH + cc) * P + pos) * I + k];
   }
   float g = pg[0], u = pu[0];
 #pragma unroll
-  for (int c = 1; c < kMaxChunks; ++c)
+  for (int c = 1; c < MC; ++c)
     if (c < NCH) {
       g += pg[c];
       u += pu[c];
@@ -739,10 +801,6 @@ static int compute_units() {
   return n;
 }
 
-// Reduction groups per work item: 4 for gate/up and 3 for down (h hi and lo
-// staged), at three waves per SIMD.
-constexpr int kDecGPW = 4;
-constexpr int kDecGPWd = 3;
 
 template <int BITS>
 static hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* shared_out, int nsh,
@@ -831,9 +889,14 @@ static hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* sh
   MOE_LAUNCH(KID_GATEUP, (k_gemv<BITS, kDecGPW, 8, 0, 3>), dim3(grid_for(items_gu, 3)),
              dim3(256), 0, s, act_hdr, act, f.sorted_pairs, K, f.x, nullptr, I, H, P, c.scale_f16,
              gpart);
-  MOE_LAUNCH(KID_SWIGLU, k_swiglu_sum, dim3((I + 255) / 256, P), dim3(256), 0, s, gpart, f.offsets,
-             E, P, I, nch_gu, hh, hl);
-  MOE_LAUNCH(KID_DOWN, (k_gemv<BITS, kDecGPWd, 4, 1, 3>), dim3(grid_for(items_dn, 3)), dim3(256),
+#define MOE_SW(MC)                                                                            \
+  MOE_LAUNCH(KID_SWIGLU, k_swiglu_sum<MC>, dim3((I + 255) / 256, P), dim3(256), 0, s, gpart,      \
+             f.offsets, E, P, I, nch_gu, hh, hl)
+  if (nch_gu <= 8) MOE_SW(8); else if (nch_gu <= 16) MOE_SW(16); else MOE_SW(24);
+#undef MOE_SW
+  // (launch bounds of two waves per SIMD let the down kernel's register use settle
+  // at 165, still three waves per SIMD, without the spill a bound of three forces)
+  MOE_LAUNCH(KID_DOWN, (k_gemv<BITS, kDecGPWd, 4, 1, 2>), dim3(grid_for(items_dn, 3)), dim3(256),
              0, s, act_hdr, act, f.sorted_pairs, K, hh, hl, H, I, P, c.scale_f16, dpart);
   if (join) {
     const hipError_t e = hipStreamWaitEvent(s, join, 0);
