@@ -334,6 +334,29 @@ __host__ inline WsLayout ws_layout(const moe_cfg& c, int T) {
   return L;
 }
 
+// ---------------------------------------------------------------- phase trace
+// Builds with -DMOE_TRACE only: thread 0 of a block stores the constant-rate
+// real-time counter (100 MHz) at named points of a kernel into a per-source
+// device array, which moe_trace_read_<source> copies to the host.  Other builds
+// compile the marks to nothing.
+#ifdef MOE_TRACE
+#define MOE_TRACE_DECL static __device__ unsigned long long g_moe_trace[1 << 14];
+#define MOE_TR(slot)                                                           \
+  do {                                                                         \
+    if (threadIdx.x == 0) g_moe_trace[(slot)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#define MOE_TRACE_EXPORT(name)                                                             \
+  extern "C" int moe_trace_read_##name(void* dst, size_t n) {                              \
+    return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(g_moe_trace), n, 0, hipMemcpyDeviceToHost); \
+  }
+#else
+#define MOE_TRACE_DECL
+#define MOE_TR(slot) \
+  do {               \
+  } while (0)
+#define MOE_TRACE_EXPORT(name)
+#endif
+
 // ---------------------------------------------------------------- profiling
 enum KernelId {
   KID_LOGITS = 0, KID_TOPK, KID_PERMUTE, KID_PLAN, KID_GATEUP, KID_DOWN, KID_SH_GATEUP,

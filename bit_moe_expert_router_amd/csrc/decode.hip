@@ -34,6 +34,8 @@
 
 namespace moe {
 
+MOE_TRACE_DECL
+
 typedef uint32_t u32x4d __attribute__((ext_vector_type(4)));
 
 struct ActEntry {
@@ -378,8 +380,11 @@ __global__ __launch_bounds__(256, 2) void k_gateup_smem(
   using C = UnitCodec<BITS>;
   __shared__ float red[kGUWaves][kTokPerPass][64];
   const int ng = H / C::G;
+  const int tb = 4 * (blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+  MOE_TR(tb);
 
   const Active act = find_active(offsets, table, E, blockIdx.x);
+  MOE_TR(tb + 1);
   if (act.e < 0) return;
   const int seg0 = __builtin_amdgcn_readfirstlane(act.seg0);
   const int n_e = __builtin_amdgcn_readfirstlane(act.n);
@@ -477,6 +482,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_smem(
         }
       }
     }
+    MOE_TR(tb + 2);
     red[wv][0][lane] = a0;
     red[wv][1][lane] = a1;
     lds_barrier();
@@ -489,6 +495,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_smem(
     }
     lds_barrier();
   }
+  MOE_TR(tb + 3);
 }
 
 // down of the one/two-token path
@@ -601,8 +608,11 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
   __shared__ float red[kDNWaves][kTokPerPass][64];
   __shared__ __align__(16) uint32_t xs_all[kDNWaves * XW];
   const int ng = I / C::G;
+  const int tb = 4096 + 8 * (blockIdx.x + gridDim.x * blockIdx.y);
+  MOE_TR(tb);
 
   const Active act = find_active(offsets, table, E, blockIdx.x);
+  MOE_TR(tb + 1);
   const int strip = blockIdx.y;
   if (act.e < 0) {  // no expert for this block; with none at all, block 0 combines
     if (out && act.U == 0 && blockIdx.x == 0)
@@ -644,6 +654,7 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
                                          (bf16_to_f32((uint16_t)b) + bf16_to_f32((uint16_t)(b >> 16)))));
   };
   hst.store(xs, lane);
+  MOE_TR(tb + 2);
   for (int c0 = 0; c0 < n_e; c0 += XT) {
     if (c0 > 0) {
       nt = min(n_e - c0, XT);
@@ -686,6 +697,7 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
           a0 = fmaf(sc, d0 - k0, a0);
         }
       }
+      MOE_TR(tb + 3);
       red[wv][0][lane] = a0;
       red[wv][1][lane] = a1;
       lds_barrier();
@@ -706,10 +718,12 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
     wait_stores();
     __syncthreads();
     if (threadIdx.x == 0) s_last = take_ticket(ctr + strip) == act.U - 1;
-    __syncthreads();
+    MOE_TR(tb + 4);
+    lds_barrier();
     if (s_last) {
       combine_strip(pair_out, ids, wts, K, E, H, shared, nsh, T, strip, out);
       if (threadIdx.x == 0) st_coherent(ctr + strip, 0);
+      MOE_TR(tb + 5);
     }
   }
 }
@@ -920,5 +934,7 @@ hipError_t launch_decode(const FwdArgs& f, const WsLayout& L, float* shared_out,
   return f.c->bits == 3 ? launch_decode_t<3>(f, L, shared_out, nsh, join, s)
                         : launch_decode_t<4>(f, L, shared_out, nsh, join, s);
 }
+
+MOE_TRACE_EXPORT(decode)
 
 }  // namespace moe

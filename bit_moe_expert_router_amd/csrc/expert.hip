@@ -100,13 +100,13 @@ __global__ __launch_bounds__(256) void k_shared_gateup(const uint16_t* __restric
       u4[st] = *reinterpret_cast<const u32x4*>(wu + (int64_t)r * H + kb + 256 * st + 8 * sub);
     }
     asm volatile("" ::: "memory");
-    __syncthreads();  // the previous pass is done with xs
+    lds_barrier();  // the previous pass is done with xs
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int q = it * 256 + threadIdx.x;
       if (q < NQ) *reinterpret_cast<u32x4*>(xs + 4 * q) = xv[it];
     }
-    __syncthreads();
+    lds_barrier();
     float ag[kNT], au[kNT];
 #pragma unroll
     for (int j = 0; j < kNT; ++j) {
@@ -175,13 +175,13 @@ __global__ __launch_bounds__(256) void k_shared_down(const uint16_t* __restrict_
     for (int st = 0; st < S; ++st)
       d4[st] = *reinterpret_cast<const u32x4*>(wd + (int64_t)r * Is + kb + 256 * st + 8 * sub);
     asm volatile("" ::: "memory");
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int q = it * 256 + threadIdx.x;
       if (q < NQ) *reinterpret_cast<f32x4s*>(hsl + 4 * q) = hv[it];
     }
-    __syncthreads();
+    lds_barrier();
     float acc[kNT];
 #pragma unroll
     for (int j = 0; j < kNT; ++j) {

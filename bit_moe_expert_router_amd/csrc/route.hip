@@ -19,6 +19,8 @@
 
 namespace moe {
 
+MOE_TRACE_DECL
+
 // ---------------------------------------------------------------- logits, small T
 // Block = one expert x up to NT (1, 2 or 4) tokens; 256 threads stride over H in
 // float4 steps, each thread issuing all its loads of a batch (8 float4 of the
@@ -83,6 +85,76 @@ __device__ __forceinline__ void logits_small_block(const uint16_t* __restrict__ 
     double v = ((red[0][j] + red[1][j]) + red[2][j]) + red[3][j];
     if (bias) v += (double)bias[e];
     st_coherent(logits + (int64_t)(t0 + j) * E + e, v);
+  }
+}
+
+// Block b = experts b*EPB .. b*EPB+EPB-1 x NT tokens: the same per-thread order
+// as the block above (items tid + 256*r of the row, r ascending), so the logits
+// are the same; one block for several experts cuts the number of blocks that
+// meet at the routing kernel's ticket counter, where every arrival is serialised.
+constexpr int kRowBatch = 5;  // float4 items of a row per thread per round trip
+template <int NT, int EPB>
+__device__ __forceinline__ void logits_multi_block(const uint16_t* __restrict__ x, int T, int H,
+                                                   int E, const float* __restrict__ wr,
+                                                   const float* __restrict__ bias,
+                                                   double* __restrict__ logits) {
+  const int e0 = blockIdx.x * EPB;
+  const int H4 = H / 4;
+  const int tid = threadIdx.x;
+  double acc[EPB][NT];
+#pragma unroll
+  for (int j = 0; j < EPB; ++j)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[j][t] = 0.0;
+  for (int b = 0; b < H4; b += 256 * kRowBatch) {
+    float4 w[EPB][kRowBatch];
+    uint2 xv[NT][kRowBatch];
+#pragma unroll
+    for (int r = 0; r < kRowBatch; ++r) {
+      const int i = min(b + tid + 256 * r, H4 - 1);
+#pragma unroll
+      for (int j = 0; j < EPB; ++j)
+        w[j][r] = reinterpret_cast<const float4*>(wr + (int64_t)min(e0 + j, E - 1) * H)[i];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        xv[t][r] = reinterpret_cast<const uint2*>(x + (int64_t)min(t, T - 1) * H)[i];
+    }
+#pragma unroll
+    for (int r = 0; r < kRowBatch; ++r) {
+      if (b + tid + 256 * r < H4) {
+#pragma unroll
+        for (int j = 0; j < EPB; ++j)
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            double a = acc[j][t];
+            a = fma((double)bf16_to_f32((uint16_t)xv[t][r].x), (double)w[j][r].x, a);
+            a = fma((double)bf16_to_f32((uint16_t)(xv[t][r].x >> 16)), (double)w[j][r].y, a);
+            a = fma((double)bf16_to_f32((uint16_t)xv[t][r].y), (double)w[j][r].z, a);
+            a = fma((double)bf16_to_f32((uint16_t)(xv[t][r].y >> 16)), (double)w[j][r].w, a);
+            acc[j][t] = a;
+          }
+      }
+    }
+  }
+  __shared__ double red[4][EPB * NT];
+  const int lane = tid & 63, wv = tid >> 6;
+#pragma unroll
+  for (int j = 0; j < EPB; ++j)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      double v = acc[j][t];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+      if (lane == 0) red[wv][j * NT + t] = v;
+    }
+  __syncthreads();
+  if (tid < EPB * NT) {
+    const int j = tid / NT, t = tid % NT, e = e0 + j;
+    if (e < E && t < T) {
+      double v = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+      if (bias) v += (double)bias[e];
+      st_coherent(logits + (int64_t)t * E + e, v);
+    }
   }
 }
 
@@ -218,14 +290,41 @@ __device__ __forceinline__ int wave_min_i32(int v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
+__device__ __forceinline__ int wave_max_i32(int v) {
+  v = max(v, dpp_i<0x111>(v, INT_MIN));
+  v = max(v, dpp_i<0x112>(v, INT_MIN));
+  v = max(v, dpp_i<0x114>(v, INT_MIN));
+  v = max(v, dpp_i<0x118>(v, INT_MIN));
+  v = max(v, dpp_i<0x142>(v, INT_MIN));
+  v = max(v, dpp_i<0x143>(v, INT_MIN));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+// a lane's double, read by every lane
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(v), lane);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(v), lane);
+  return __hiloint2double(hi, lo);
+}
+// Order-preserving 32-bit key of a double: its nearest float, as an integer
+// that compares like the float (both zeros map to 0).  Rounding to float never
+// reverses an order, so a strictly larger key means a strictly larger value;
+// only equal keys need the exact comparison.
+__device__ __forceinline__ int coarse_key(double v) {
+  const float f = (float)v;
+  const int b = __float_as_int(f);
+  return f == 0.f ? 0 : (b ^ ((b >> 31) & 0x7FFFFFFF));
+}
+
 // this lane's pick (lane < K) and its weight; -1 for other lanes.
 // Each lane first sorts its PER candidates (experts lane + 64i) by descending
 // logit with an odd-even transposition network (swaps only on a strictly larger
-// value, so equal logits keep ascending id order).  Round k then takes the wave
-// maximum of the lane heads; the lane holding it (the lowest id among several,
-// on exact ties) pops its head.
+// value, so equal logits keep ascending id order).  Round k then finds the wave
+// maximum of the lane heads: first on their 32-bit keys (one DPP max), and only
+// when several lanes share the largest key, exactly in fp64 among those lanes,
+// the lowest id winning on equal logits.  The winning lane pops its head.
 template <int PER>
-__device__ __forceinline__ int wave_topk(const double* __restrict__ l, int E, int K, float* wk) {
+__device__ __forceinline__ int wave_topk(const double* __restrict__ l, int E, int K, float* wk,
+                                         int trace = -1) {
   const int lane = threadIdx.x & 63;
   double v[PER];
   int id[PER];
@@ -247,19 +346,24 @@ __device__ __forceinline__ int wave_topk(const double* __restrict__ l, int E, in
       id[i] = sw ? ib : ia;
       id[i + 1] = sw ? ia : ib;
     }
+  if (trace >= 0) MOE_TR(trace);
   double my_l = -INFINITY;
   int my_id = -1;
+  int key = id[0] != 0x7FFFFFFF ? coarse_key(v[0]) : INT_MIN;
   for (int k = 0; k < K; ++k) {
-    const double m = wave_max_f64(v[0]);
-    const uint64_t hold = __ballot(v[0] == m && id[0] != 0x7FFFFFFF);
+    const int mk = wave_max_i32(key);
+    const uint64_t cand = __ballot(key == mk && id[0] != 0x7FFFFFFF);
     int win;
-    if (__popcll(hold) == 1) {
-      win = __ffsll((unsigned long long)hold) - 1;
-    } else {  // equal logits in several lanes: the lowest id wins
-      const int best = wave_min_i32(v[0] == m ? id[0] : 0x7FFFFFFF);
-      win = __ffsll((unsigned long long)__ballot(v[0] == m && id[0] == best)) - 1;
+    if (__popcll(cand) == 1) {
+      win = __ffsll((unsigned long long)cand) - 1;
+    } else {  // several lanes share the largest key: exact maximum, then the lowest id
+      const bool c = (cand >> lane) & 1;
+      const double m = wave_max_f64(c ? v[0] : -INFINITY);
+      const int best = wave_min_i32(c && v[0] == m ? id[0] : 0x7FFFFFFF);
+      win = __ffsll((unsigned long long)__ballot(c && v[0] == m && id[0] == best)) - 1;
     }
     const int pick = __builtin_amdgcn_readlane(id[0], win);
+    const double pl = readlane_f64(v[0], win);
     if (lane == win) {
 #pragma unroll
       for (int i = 0; i + 1 < PER; ++i) {
@@ -268,16 +372,18 @@ __device__ __forceinline__ int wave_topk(const double* __restrict__ l, int E, in
       }
       v[PER - 1] = -INFINITY;
       id[PER - 1] = 0x7FFFFFFF;
+      key = id[0] != 0x7FFFFFFF ? coarse_key(v[0]) : INT_MIN;
     }
     if (lane == k) {
-      my_l = m;
+      my_l = pl;
       my_id = pick;
     }
   }
-  const double l0 = __shfl(my_l, 0);
+  if (trace >= 0) MOE_TR(trace + 1);
+  const double l0 = readlane_f64(my_l, 0);
   const double term = lane < K ? exp(my_l - l0) : 0.0;
   double den = 0.0;
-  for (int k = 0; k < K; ++k) den += __shfl(term, k);
+  for (int k = 0; k < K; ++k) den += readlane_f64(term, k);
   *wk = (float)(term / den);
   return lane < K ? my_id : -1;
 }
@@ -472,39 +578,29 @@ __global__ __launch_bounds__(64) void k_group_scatter(const int32_t* __restrict_
 }
 
 // ---------------------------------------------------------------- grouping, small T
-// Decode batches (T <= 16, T * K <= 64): one wave groups the T*K pairs, one pair
-// per lane.  A pair's key is (expert id, pair index); its sorted position is the
-// number of smaller keys, counted bit by bit from the top with one ballot per
-// key bit.  Offsets: each
-// expert's first pair writes its pair count into a zeroed LDS histogram, which
-// a DPP prefix sum turns into the exclusive scan.  Integer only: bit-exact.
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  // inclusive prefix sum over the 64 lanes (row prefix sums, then row carries)
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
-  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false); // row_bcast:15
-  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false); // row_bcast:31
-  return v;
-}
-
-__device__ __forceinline__ void wave_group_small(int id, int P, int E, int* cnt,
+// Grouping of at most 64 pairs by one wave.  Lane p (pair p < P) has key id_p
+// (E for an id outside [0, E)).  Its sorted position is the number of pairs with
+// a smaller (key, pair index), counted from the top key bit down with one ballot
+// per bit.  With the valid keys placed in sorted order in s_key[128] (LDS),
+// offsets[e] is the number of them below e, found by a branch-free binary search
+// (lane l takes e = l + 64*i).  The result is the stable counting sort; pairs with an invalid
+// id are left out (pair_pos = -1).  Integer only: bit-exact.
+template <int NOFF>  // NOFF * 64 > E
+__device__ __forceinline__ void wave_group_small(int id, int P, int E, int* s_key,
                                                  int32_t* __restrict__ offsets,
                                                  int32_t* __restrict__ sorted_pairs,
                                                  int32_t* __restrict__ pair_pos) {
   const int lane = threadIdx.x & 63;
   int nbits = 0;
   while ((1 << nbits) < E + 1) ++nbits;
-  const bool ok = lane < P && id >= 0 && id < E;
-  const int key = ok ? id : E;  // invalid pairs sort after every expert
+  const bool live = lane < P;
+  const bool ok = live && id >= 0 && id < E;
+  const int key = ok ? id : E;
   const uint64_t lt = (1ull << lane) - 1ull;
-  const uint64_t live = __ballot(lane < P);
-  // lanes with a smaller key, and lanes with the same key
-  uint64_t eq = live;
+  uint64_t eq = __ballot(live);
   int less = 0;
   for (int b = nbits - 1; b >= 0; --b) {
-    const uint64_t bal = __ballot(lane < P && ((key >> b) & 1));
+    const uint64_t bal = __ballot(live && ((key >> b) & 1));
     if ((key >> b) & 1) {
       less += __popcll(eq & ~bal);
       eq &= bal;
@@ -513,31 +609,31 @@ __device__ __forceinline__ void wave_group_small(int id, int P, int E, int* cnt,
     }
   }
   const int pos = less + __popcll(eq & lt);
-  if (ok) sorted_pairs[pos] = lane;
-  if (lane < P) pair_pos[lane] = ok ? pos : -1;
-  // histogram of the valid pairs, then the exclusive scan over the experts
-  const int per = (E + 64) / 64;  // entries 0..E
-  for (int i = 0; i < per; ++i) {
-    const int e = lane * per + i;
-    if (e <= E) cnt[e] = 0;
+  // sorted keys in s_key[0 .. nvalid), INT_MAX above (LDS operations of one wave
+  // take effect in order, so the keys overwrite the fill)
+  s_key[lane] = INT_MAX;
+  s_key[64 + lane] = INT_MAX;
+  if (ok) {
+    sorted_pairs[pos] = lane;
+    s_key[pos] = key;
   }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the zeros land first
-  if (ok && (eq & lt) == 0) cnt[id] = __popcll(eq);
-  __builtin_amdgcn_s_waitcnt(0xc07f);
-  int c[17];
-  int loc = 0;
+  if (live) pair_pos[lane] = ok ? pos : -1;
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS writes have landed
+  int below[NOFF];
 #pragma unroll
-  for (int i = 0; i < 17; ++i) {
-    const int e = lane * per + i;
-    c[i] = (i < per && e <= E) ? cnt[e] : 0;
-    loc += c[i];
+  for (int i = 0; i < NOFF; ++i) below[i] = 0;
+#pragma unroll
+  for (int step = 64; step >= 1; step >>= 1) {
+    int kj[NOFF];
+#pragma unroll
+    for (int i = 0; i < NOFF; ++i) kj[i] = s_key[below[i] + step - 1];
+#pragma unroll
+    for (int i = 0; i < NOFF; ++i) below[i] = kj[i] < lane + 64 * i ? below[i] + step : below[i];
   }
-  int run = wave_incl_scan(loc) - loc;
 #pragma unroll
-  for (int i = 0; i < 17; ++i) {
-    const int e = lane * per + i;
-    if (i < per && e <= E) offsets[e] = run;
-    run += c[i];
+  for (int i = 0; i < NOFF; ++i) {
+    const int e = lane + 64 * i;
+    if (e <= E) offsets[e] = below[i];
   }
 }
 
@@ -549,7 +645,7 @@ __global__ __launch_bounds__(1024) void k_topk_group_small(
     float* __restrict__ wout, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
     int32_t* __restrict__ pair_pos) {
   __shared__ int32_t s_ids[64];
-  __shared__ int cnt[kMaxE + 1];
+  __shared__ int s_key[128];
   const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
   if (t < T) {
     float wk;
@@ -560,54 +656,66 @@ __global__ __launch_bounds__(1024) void k_topk_group_small(
       s_ids[t * K + lane] = id;
     }
   }
-  __syncthreads();
+  // (an LDS-only barrier: __syncthreads() would also wait for the stores above)
+  lds_barrier();
   if (threadIdx.x < 64) {
     const int P = T * K;
-    wave_group_small(lane < P ? s_ids[lane] : -1, P, E, cnt, offsets, sorted_pairs, pair_pos);
+    wave_group_small<PER + 1>(lane < P ? s_ids[lane] : -1, P, E, s_key, offsets, sorted_pairs,
+                              pair_pos);
   }
 }
 
 // ---------------------------------------------------------------- one launch, small T
 // Logits, top-k and grouping of a batch of one or two tokens in one kernel: the
-// logit blocks above (logits stored written-through), then the block that takes
+// multi-expert logit blocks above (logits stored written-through), then the block that takes
 // the last ticket, whose loads see every block's logits, picks the top-k of every
 // token (wave w takes token w) and its first wave groups the pairs.  It resets
 // the ticket counter for the next call.  (Larger batches pick in a kernel of
 // their own with one wave per token: the last block's four waves would take
 // their tokens in turn.)
+#ifndef MOE_ROUTE_EPB
+#define MOE_ROUTE_EPB 2
+#endif
+constexpr int kRouteEPB = MOE_ROUTE_EPB;  // experts per logit block of the one-launch routing
 template <int NT, int PER>
 __global__ __launch_bounds__(256) void k_route_small(
     const uint16_t* __restrict__ x, int T, int H, int E, const float* __restrict__ wr,
     const float* __restrict__ bias, double* logits, int K, int32_t* __restrict__ ids,
     float* __restrict__ wout, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
     int32_t* __restrict__ pair_pos, int32_t* __restrict__ ctr) {
-  logits_small_block<NT>(x, T, H, E, wr, bias, logits);
+  MOE_TR(4 * blockIdx.x);
+  logits_multi_block<NT, kRouteEPB>(x, T, H, E, wr, bias, logits);
+  MOE_TR(4 * blockIdx.x + 1);
   __shared__ int s_last;
   wait_stores();
   __syncthreads();
   if (threadIdx.x == 0) s_last = take_ticket(ctr) == (int)(gridDim.x * gridDim.y) - 1;
-  __syncthreads();
+  MOE_TR(4 * blockIdx.x + 2);
+  lds_barrier();
   if (!s_last) return;
   __shared__ int32_t s_ids[64];
-  __shared__ int cnt[kMaxE + 1];
+  __shared__ int s_key[128];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wv < T) {
     const int t = wv;
     float wk;
-    const int id = wave_topk<PER>(logits + (int64_t)t * E, E, K, &wk);
+    const int id = wave_topk<PER>(logits + (int64_t)t * E, E, K, &wk, 2002);
     if (lane < K) {
       ids[t * K + lane] = id;
       wout[t * K + lane] = wk;
       s_ids[t * K + lane] = id;
     }
   }
-  __syncthreads();
+  MOE_TR(2000);
+  lds_barrier();  // s_ids only; the stores above need not have completed
   if (wv == 0) {
     const int P = T * K;
-    wave_group_small(lane < P ? s_ids[lane] : -1, P, E, cnt, offsets, sorted_pairs, pair_pos);
+    wave_group_small<PER + 1>(lane < P ? s_ids[lane] : -1, P, E, s_key, offsets, sorted_pairs,
+                              pair_pos);
     if (lane == 0) st_coherent(ctr, 0);
   }
+  MOE_TR(2001);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -624,13 +732,14 @@ hipError_t launch_route(const moe_cfg& c, const uint16_t* x, int T, const float*
   }
   if (T <= 2 && P <= 64) {  // one launch
     int32_t* ctr = counters + kCtrRoute;
+    const int nbr = (E + kRouteEPB - 1) / kRouteEPB;
 #define MOE_RS(N)                                                                               \
   case N:                                                                                       \
     if (T == 1)                                                                                 \
-      MOE_LAUNCH(KID_ROUTE, (k_route_small<1, N>), dim3(E), dim3(256), 0, s, x, T, H, E, wr,    \
+      MOE_LAUNCH(KID_ROUTE, (k_route_small<1, N>), dim3(nbr), dim3(256), 0, s, x, T, H, E, wr,  \
                  bias, logits, K, ids, w, offsets, sorted_pairs, pair_pos, ctr);                \
     else                                                                                        \
-      MOE_LAUNCH(KID_ROUTE, (k_route_small<2, N>), dim3(E), dim3(256), 0, s, x, T, H, E, wr,    \
+      MOE_LAUNCH(KID_ROUTE, (k_route_small<2, N>), dim3(nbr), dim3(256), 0, s, x, T, H, E, wr,  \
                  bias, logits, K, ids, w, offsets, sorted_pairs, pair_pos, ctr);                \
     break;
     MOE_PER_SWITCH(MOE_RS)
@@ -673,5 +782,7 @@ hipError_t launch_route(const moe_cfg& c, const uint16_t* x, int T, const float*
   }
   return hipGetLastError();
 }
+
+MOE_TRACE_EXPORT(route)
 
 }  // namespace moe
