@@ -29,6 +29,7 @@
 // applied.  The down matrix takes h as bf16 hi + bf16 remainder (two products per
 // code pair).
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -295,6 +296,10 @@ __global__ __launch_bounds__(256, WPS) void k_gemv(
 // waves' sums meet in LDS.
 constexpr int kGUWaves = 4;
 constexpr int kTokPerPass = 2;
+#ifndef MOE_GU_AHEAD
+#define MOE_GU_AHEAD 2
+#endif
+constexpr int kGUAhead = MOE_GU_AHEAD;  // weight groups a gate/up wave has in flight
 constexpr int kMaxKParts = 4;
 
 // ---------------------------------------------------------------- active experts
@@ -369,7 +374,7 @@ __device__ __forceinline__ Active find_active(const int32_t* __restrict__ offset
 // decode step is in flight at once; the offset sums come from vector loads that
 // are requested before the weights.
 template <int BITS, int GPW>
-__global__ __launch_bounds__(256, 2) void k_gateup_smem(
+__global__ __launch_bounds__(256, 3) void k_gateup_smem(
     const moe_expert_ref* __restrict__ table, int E, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pairs, int K,
     const uint16_t* __restrict__ x,  // read-only: dot operands through scalar loads
@@ -399,22 +404,22 @@ __global__ __launch_bounds__(256, 2) void k_gateup_smem(
   const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
   const uint32_t* xv32 = reinterpret_cast<const uint32_t*>(x_vec);
 
-  // weights first: all groups of this wave at once (group index clamped, not
-  // branched on, so that the waits the compiler places stay exact); they need
-  // nothing but the expert's address
-  u32x4 cw[GPW][C::CHUNKS];
-  uint32_t sr[GPW];  // the aligned dword holding the scale (any 16-bit handling here would wait)
-#pragma unroll
-  for (int i = 0; i < GPW; ++i) {
+  // weights first: the first kGUAhead groups of this wave (group index clamped,
+  // not branched on, so that the waits the compiler places stay exact); they
+  // need nothing but the expert's address.  Each later group is requested right
+  // after the products of the group kGUAhead before it: the requests of the
+  // whole grid then complete in waves, and every wave's products run while its
+  // later groups are still streaming (with every group requested at once, all
+  // of a wave's data lands near the end of the stream and the products follow
+  // it).
+  auto issue = [&](int i, u32x4 (&cw)[GPW][C::CHUNKS], uint32_t (&sr)[GPW]) {
     const int g = min(g0 + wv + kGUWaves * i, g1 - 1);
     load_unit4<BITS>(mat, (int64_t)strip * ng + g, lane, cw[i]);
     sr[i] = load_scale_dword(msc, (int64_t)row * ng + g);
-  }
-  asm volatile("" ::: "memory");
-
-  // then the tokens (scalar loads, which the weights do not wait for) and the
-  // activation pairs of this wave's groups for the offset sums (lane = pair),
-  // needed only after the dot products
+  };
+  // the activation pairs of this wave's groups for the offset sums (lane =
+  // pair) go first: vector loads complete in order, and these (cache hits) are
+  // then not queued behind the weight stream
   auto load_xo = [&](int t, uint32_t (&xo)[GPW]) {
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
@@ -424,20 +429,24 @@ __global__ __launch_bounds__(256, 2) void k_gateup_smem(
     }
   };
   const int sp0 = sorted_pairs[seg0], sp1 = sorted_pairs[seg0 + min(1, n_e - 1)];
-  int t0 = sp0 / K;
-  int t1 = n_e > 1 ? sp1 / K : t0;
   uint32_t xo0[GPW], xo1[GPW];
-  load_xo(t0, xo0);
-  load_xo(t1, xo1);
+  load_xo(sp0 / K, xo0);
+  load_xo(sp1 / K, xo1);  // (sp1 = sp0 for a single position)
+  asm volatile("" ::: "memory");
+  u32x4 cw[GPW][C::CHUNKS];
+  uint32_t sr[GPW];  // the aligned dword holding the scale (any 16-bit handling here would wait)
+#pragma unroll
+  for (int i = 0; i < GPW; ++i)
+    if (i < kGUAhead) issue(i, cw, sr);
+  asm volatile("" ::: "memory");
 
-  for (int b0 = 0; b0 < n_e; b0 += kTokPerPass) {
+  // one pass over positions b0, b0+1 of the expert with weights cwp/srp; the
+  // first pass requests the later groups as it goes (ROLL)
+  auto pass = [&](int b0, u32x4 (&cwp)[GPW][C::CHUNKS], uint32_t (&srp)[GPW], auto roll) {
+    constexpr bool ROLL = decltype(roll)::value;
     const bool two = b0 + 1 < n_e;
-    if (b0 > 0) {
-      t0 = sorted_pairs[seg0 + b0] / K;
-      t1 = two ? sorted_pairs[seg0 + b0 + 1] / K : t0;
-      load_xo(t0, xo0);
-      load_xo(t1, xo1);
-    }
+    const int t0 = sorted_pairs[seg0 + b0] / K;
+    const int t1 = two ? sorted_pairs[seg0 + b0 + 1] / K : t0;
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
@@ -445,12 +454,12 @@ __global__ __launch_bounds__(256, 2) void k_gateup_smem(
       if (g < g1) {
         const uint32_t* x0 = x32 + ((int64_t)t0 * H + g * C::G) / 2;
         const uint32_t* x1 = x32 + ((int64_t)t1 * H + g * C::G) / 2;
-        uint32_t sraw = sr[i];
+        uint32_t sraw = srp[i];
         asm volatile("" : "+v"(sraw));  // convert here, not hoisted ahead of the loads
         const float sc = scale_to_f32(scale_from_dword(sraw, (int64_t)row * ng + g), scale_f16);
         uint32_t w[C::WORDS];
         float d0 = 0.f, d1 = 0.f;
-        unit_words<BITS>(cw[i], w);
+        unit_words<BITS>(cwp[i], w);
         if (two) {
           C::for_each_pair(w, [&](int Pp, uint32_t pr) {
             d0 = dot2_bf16(pr, x0[Pp], d0);
@@ -462,22 +471,29 @@ __global__ __launch_bounds__(256, 2) void k_gateup_smem(
         }
         a0 = fmaf(sc, d0, a0);
       }
+      if (ROLL && i + kGUAhead < GPW) {
+        asm volatile("" ::: "memory");
+        issue(i + kGUAhead, cwp, srp);
+        asm volatile("" ::: "memory");
+      }
     }
     // subtract sum_g s_g * (offset sum of group g)
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
       const int g = g0 + wv + kGUWaves * i;
       if (g < g1) {
-        uint32_t sraw = sr[i];
+        uint32_t sraw = srp[i];
         asm volatile("" : "+v"(sraw));
         const float sc = scale_to_f32(scale_from_dword(sraw, (int64_t)row * ng + g), scale_f16);
         const float off = lane < C::PAIRS ? C::pair_off(lane) : 0.f;
+        uint32_t xa = xo0[i], xb = xo1[i];
+        asm volatile("" : "+v"(xa), "+v"(xb));  // used here, not hoisted ahead of the weights
         const float c0 = wave_sum_uniform<BITS>(
-            off * bf16_to_f32((uint16_t)xo0[i]) + off * bf16_to_f32((uint16_t)(xo0[i] >> 16)));
+            off * bf16_to_f32((uint16_t)xa) + off * bf16_to_f32((uint16_t)(xa >> 16)));
         a0 = fmaf(-sc, c0, a0);
         if (two) {
           const float c1 = wave_sum_uniform<BITS>(
-              off * bf16_to_f32((uint16_t)xo1[i]) + off * bf16_to_f32((uint16_t)(xo1[i] >> 16)));
+              off * bf16_to_f32((uint16_t)xb) + off * bf16_to_f32((uint16_t)(xb >> 16)));
           a1 = fmaf(-sc, c1, a1);
         }
       }
@@ -494,6 +510,19 @@ __global__ __launch_bounds__(256, 2) void k_gateup_smem(
       gu[((int64_t)blockIdx.z * P + seg0 + b0 + j) * I + row] = y;
     }
     lds_barrier();
+  };
+  pass(0, cw, sr, std::true_type{});
+  // more than two positions (a token that lists the expert twice): later passes
+  // request the groups again, in the same way
+  for (int b0 = kTokPerPass; b0 < n_e; b0 += kTokPerPass) {
+    load_xo(sorted_pairs[seg0 + b0] / K, xo0);
+    load_xo(sorted_pairs[seg0 + min(b0 + 1, n_e - 1)] / K, xo1);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < GPW; ++i)
+      if (i < kGUAhead) issue(i, cw, sr);
+    asm volatile("" ::: "memory");
+    pass(b0, cw, sr, std::true_type{});
   }
   MOE_TR(tb + 3);
 }

@@ -270,6 +270,40 @@ def test_small_batch_all_pairs_dropped(gpu, name, T):
     ml.close()
 
 
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_small_batch_repeated_expert(gpu, name):
+    """two tokens that list one expert twice each (caller-supplied routing): the
+    expert owns four positions, more than a single pass of the one/two-token
+    kernels takes, so their later passes run; every pair and the combined output
+    against the oracle"""
+    say(f"[ffn] repeated expert {name} T=2")
+    cfg = synth.CONFIGS[name]
+    dl = layer_for(name, gpu)
+    T = 2
+    xh, xd = x_device(cfg, gpu, tokens=T)
+    ml = make_layer_api(cfg, dl, T)
+    a = run_gpu(cfg, dl, xd, ml=ml)
+    ids, w = a["ids"].copy(), a["w"].copy()
+    e = int(ids[0, 0])
+    ids[0, 1] = e
+    ids[1, 0] = e
+    ids[1, 1] = e
+    r = _caller_routing(ml, ids, w, cfg.n_experts, gpu)
+    b = run_gpu(cfg, dl, xd, ml=ml, routing=r)
+    assert np.diff(b["offsets"])[e] == 4
+    he = HostExperts(cfg)
+    for t in range(T):
+        for k in range(cfg.top_k):
+            ref = he.ffn(xh[t], int(ids[t, k]))
+            assert rel_err(b["pair_out"][t * cfg.top_k + k], ref) <= TOL, (t, k)
+    tabs = [[he.blobs(q)[m] for q in range(cfg.n_experts)] for m in range(3)]
+    out_ref, _ = oracle.moe_layer(xh, ids, w.astype(np.float64), *tabs, cfg.inter, cfg.bits,
+                                  cfg.group, cfg.scale_f16, he.shared())
+    for t in range(T):
+        assert rel_err(b["out"][t], out_ref[t]) <= TOL, t
+    ml.close()
+
+
 def test_counters_left_zero(gpu):
     """the workspace's cross-block counters are zero again after every call"""
     say("[inv] counters")
