@@ -88,7 +88,7 @@ __device__ __forceinline__ void logits_small_block(const uint16_t* __restrict__ 
   }
 }
 
-// Block b = experts b*EPB .. b*EPB+EPB-1 x NT tokens: the same per-thread order
+// Block (b, c) = experts b*EPB .. b*EPB+EPB-1 x tokens c*NT .. c*NT+NT-1: the same per-thread order
 // as the block above (items tid + 256*r of the row, r ascending), so the logits
 // are the same; one block for several experts cuts the number of blocks that
 // meet at the routing kernel's ticket counter, where every arrival is serialised.
@@ -98,7 +98,7 @@ __device__ __forceinline__ void logits_multi_block(const uint16_t* __restrict__ 
                                                    int E, const float* __restrict__ wr,
                                                    const float* __restrict__ bias,
                                                    double* __restrict__ logits) {
-  const int e0 = blockIdx.x * EPB;
+  const int e0 = blockIdx.x * EPB, t0 = blockIdx.y * NT;
   const int H4 = H / 4;
   const int tid = threadIdx.x;
   double acc[EPB][NT];
@@ -117,7 +117,7 @@ __device__ __forceinline__ void logits_multi_block(const uint16_t* __restrict__ 
         w[j][r] = reinterpret_cast<const float4*>(wr + (int64_t)min(e0 + j, E - 1) * H)[i];
 #pragma unroll
       for (int t = 0; t < NT; ++t)
-        xv[t][r] = reinterpret_cast<const uint2*>(x + (int64_t)min(t, T - 1) * H)[i];
+        xv[t][r] = reinterpret_cast<const uint2*>(x + (int64_t)min(t0 + t, T - 1) * H)[i];
     }
 #pragma unroll
     for (int r = 0; r < kRowBatch; ++r) {
@@ -150,10 +150,10 @@ __device__ __forceinline__ void logits_multi_block(const uint16_t* __restrict__ 
   __syncthreads();
   if (tid < EPB * NT) {
     const int j = tid / NT, t = tid % NT, e = e0 + j;
-    if (e < E && t < T) {
+    if (e < E && t0 + t < T) {
       double v = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
       if (bias) v += (double)bias[e];
-      st_coherent(logits + (int64_t)t * E + e, v);
+      st_coherent(logits + (int64_t)(t0 + t) * E + e, v);
     }
   }
 }
@@ -667,40 +667,38 @@ __global__ __launch_bounds__(1024) void k_topk_group_small(
 
 // ---------------------------------------------------------------- one launch, small T
 // Logits, top-k and grouping of a batch of one or two tokens in one kernel: the
-// multi-expert logit blocks above (logits stored written-through), then the block that takes
-// the last ticket, whose loads see every block's logits, picks the top-k of every
-// token (wave w takes token w) and its first wave groups the pairs.  It resets
-// the ticket counter for the next call.  (Larger batches pick in a kernel of
-// their own with one wave per token: the last block's four waves would take
-// their tokens in turn.)
-#ifndef MOE_ROUTE_EPB
-#define MOE_ROUTE_EPB 2
-#endif
-constexpr int kRouteEPB = MOE_ROUTE_EPB;  // experts per logit block of the one-launch routing
-template <int NT, int PER>
+// multi-expert logit blocks above (logits stored written-through), then the
+// block that takes the last ticket, whose loads see every block's logits, picks
+// the top-k of every token (wave w takes tokens w, w+4, ...) and its first wave
+// groups the pairs.  It resets the ticket counter for the next call.  Larger
+// batches pick their tokens faster in a kernel of their own with one wave per
+// token (here the last block's four waves would take their tokens in turn:
+// 17.7 us at eight tokens against 14.8 us for the two launches).
+constexpr int kRouteMaxT = 2;
+template <int NT, int PER, int EPB>
 __global__ __launch_bounds__(256) void k_route_small(
     const uint16_t* __restrict__ x, int T, int H, int E, const float* __restrict__ wr,
     const float* __restrict__ bias, double* logits, int K, int32_t* __restrict__ ids,
     float* __restrict__ wout, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
     int32_t* __restrict__ pair_pos, int32_t* __restrict__ ctr) {
-  MOE_TR(4 * blockIdx.x);
-  logits_multi_block<NT, kRouteEPB>(x, T, H, E, wr, bias, logits);
-  MOE_TR(4 * blockIdx.x + 1);
+  const int bid = blockIdx.x + gridDim.x * blockIdx.y;
+  MOE_TR(4 * bid);
+  logits_multi_block<NT, EPB>(x, T, H, E, wr, bias, logits);
+  MOE_TR(4 * bid + 1);
   __shared__ int s_last;
   wait_stores();
   __syncthreads();
   if (threadIdx.x == 0) s_last = take_ticket(ctr) == (int)(gridDim.x * gridDim.y) - 1;
-  MOE_TR(4 * blockIdx.x + 2);
+  MOE_TR(4 * bid + 2);
   lds_barrier();
   if (!s_last) return;
   __shared__ int32_t s_ids[64];
   __shared__ int s_key[128];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wv < T) {
-    const int t = wv;
+  for (int t = wv; t < T; t += 4) {
     float wk;
-    const int id = wave_topk<PER>(logits + (int64_t)t * E, E, K, &wk, 2002);
+    const int id = wave_topk<PER>(logits + (int64_t)t * E, E, K, &wk, t == 0 ? 2002 : -1);
     if (lane < K) {
       ids[t * K + lane] = id;
       wout[t * K + lane] = wk;
@@ -730,16 +728,16 @@ hipError_t launch_route(const moe_cfg& c, const uint16_t* x, int T, const float*
     X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(16)                            \
     default: return hipErrorInvalidValue;                                    \
   }
-  if (T <= 2 && P <= 64) {  // one launch
+  if (T <= kRouteMaxT && P <= 64) {  // one launch
     int32_t* ctr = counters + kCtrRoute;
-    const int nbr = (E + kRouteEPB - 1) / kRouteEPB;
+    const dim3 g1((E + 1) / 2);  // two experts per logit block
 #define MOE_RS(N)                                                                               \
   case N:                                                                                       \
     if (T == 1)                                                                                 \
-      MOE_LAUNCH(KID_ROUTE, (k_route_small<1, N>), dim3(nbr), dim3(256), 0, s, x, T, H, E, wr,  \
+      MOE_LAUNCH(KID_ROUTE, (k_route_small<1, N, 2>), g1, dim3(256), 0, s, x, T, H, E, wr,     \
                  bias, logits, K, ids, w, offsets, sorted_pairs, pair_pos, ctr);                \
     else                                                                                        \
-      MOE_LAUNCH(KID_ROUTE, (k_route_small<2, N>), dim3(nbr), dim3(256), 0, s, x, T, H, E, wr,  \
+      MOE_LAUNCH(KID_ROUTE, (k_route_small<2, N, 2>), g1, dim3(256), 0, s, x, T, H, E, wr,     \
                  bias, logits, K, ids, w, offsets, sorted_pairs, pair_pos, ctr);                \
     break;
     MOE_PER_SWITCH(MOE_RS)
