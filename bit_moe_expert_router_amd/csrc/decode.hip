@@ -29,7 +29,6 @@
 // applied.  The down matrix takes h as bf16 hi + bf16 remainder (two products per
 // code pair).
 #include <algorithm>
-#include <type_traits>
 
 #include "common.h"
 
@@ -440,10 +439,10 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
     if (i < kGUAhead) issue(i, cw, sr);
   asm volatile("" ::: "memory");
 
-  // one pass over positions b0, b0+1 of the expert with weights cwp/srp; the
-  // first pass requests the later groups as it goes (ROLL)
-  auto pass = [&](int b0, u32x4 (&cwp)[GPW][C::CHUNKS], uint32_t (&srp)[GPW], auto roll) {
-    constexpr bool ROLL = decltype(roll)::value;
+  // one pass over positions b0, b0+1 of the expert with weights cwp/srp (the
+  // first kGUAhead groups already requested; the pass requests the later ones
+  // as it goes)
+  auto pass = [&](int b0, u32x4 (&cwp)[GPW][C::CHUNKS], uint32_t (&srp)[GPW]) {
     const bool two = b0 + 1 < n_e;
     const int t0 = sorted_pairs[seg0 + b0] / K;
     const int t1 = two ? sorted_pairs[seg0 + b0 + 1] / K : t0;
@@ -471,7 +470,7 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
         }
         a0 = fmaf(sc, d0, a0);
       }
-      if (ROLL && i + kGUAhead < GPW) {
+      if (i + kGUAhead < GPW) {
         asm volatile("" ::: "memory");
         issue(i + kGUAhead, cwp, srp);
         asm volatile("" ::: "memory");
@@ -511,7 +510,7 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
     }
     lds_barrier();
   };
-  pass(0, cw, sr, std::true_type{});
+  pass(0, cw, sr);
   // more than two positions (a token that lists the expert twice): later passes
   // request the groups again, in the same way
   for (int b0 = kTokPerPass; b0 < n_e; b0 += kTokPerPass) {
@@ -522,7 +521,7 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
     for (int i = 0; i < GPW; ++i)
       if (i < kGUAhead) issue(i, cw, sr);
     asm volatile("" ::: "memory");
-    pass(b0, cw, sr, std::true_type{});
+    pass(b0, cw, sr);
   }
   MOE_TR(tb + 3);
 }
