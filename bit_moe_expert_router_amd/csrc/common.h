@@ -287,6 +287,8 @@ struct WsLayout {
   int64_t logits;     // double[T][E]
   int64_t ghist;      // int32[ceil(P/1024)][E]: per-chunk expert counts, then bases (grouping)
   int64_t act;        // decode: int32 U (64-byte header), then the active-expert list (40 B each)
+  int64_t osx;        // decode: float[T][H/G]: per token and reduction group, the offset sum
+                      //   sum_P off_P (x_2P + x_2P+1) of the gate/up codec
   int64_t gpart;      // decode: float[2*NCH][P][I]: gate then up partial products per
                       //   chunk of reduction groups, rows by sorted position
   int64_t hdec;       // decode: bf16[2][P][I]: h hi rows, then h lo rows, by sorted position
@@ -319,6 +321,7 @@ __host__ inline WsLayout ws_layout(const moe_cfg& c, int T) {
   const int64_t nch_gu = (c.hidden / c.group + kDecGPW - 1) / kDecGPW;
   const int64_t nch_dn = (c.inter / c.group + kDecGPWd - 1) / kDecGPWd;
   L.act = take(pf ? 0 : 64 + 40 * (int64_t)c.n_experts);
+  L.osx = take(pf ? 0 : (int64_t)T * (c.hidden / c.group) * 4);
   L.gpart = take(pf ? 0 : 2 * nch_gu * P * c.inter * 4);
   L.hdec = take(pf ? 0 : 2 * P * c.inter * 2);
   L.dpart = take(pf ? 0 : nch_dn * P * c.hidden * 4);
@@ -340,10 +343,15 @@ __host__ inline WsLayout ws_layout(const moe_cfg& c, int T) {
 // device array, which moe_trace_read_<source> copies to the host.  Other builds
 // compile the marks to nothing.
 #ifdef MOE_TRACE
-#define MOE_TRACE_DECL static __device__ unsigned long long g_moe_trace[1 << 14];
+#define MOE_TRACE_DECL static __device__ unsigned long long g_moe_trace[1 << 15];
 #define MOE_TR(slot)                                                           \
   do {                                                                         \
     if (threadIdx.x == 0) g_moe_trace[(slot)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+// the same, by lane 0 of each wave
+#define MOE_TRW(slot)                                                                  \
+  do {                                                                                 \
+    if ((threadIdx.x & 63) == 0) g_moe_trace[(slot)] = __builtin_amdgcn_s_memrealtime(); \
   } while (0)
 #define MOE_TRACE_EXPORT(name)                                                             \
   extern "C" int moe_trace_read_##name(void* dst, size_t n) {                              \
@@ -353,6 +361,9 @@ __host__ inline WsLayout ws_layout(const moe_cfg& c, int T) {
 #define MOE_TRACE_DECL
 #define MOE_TR(slot) \
   do {               \
+  } while (0)
+#define MOE_TRW(slot) \
+  do {                \
   } while (0)
 #define MOE_TRACE_EXPORT(name)
 #endif

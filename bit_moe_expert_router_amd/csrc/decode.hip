@@ -51,13 +51,36 @@ struct ActEntry {
 // an item's results land depends on the item alone.
 constexpr int kPlanKeys = 65;  // 0..63: 63 - min(n, 63) for active experts; 64: inactive
 
+// Blocks 1.. of the same launch form, for every token t and reduction group g of
+// the gate/up matrices, the codec's offset sum osx[t][g] = sum_P off_P (x_2P +
+// x_2P+1) (one wave per (t, g), lane = pair, the fixed-order wave sum), which the
+// gate/up GEMV subtracts per group instead of reducing it in every work item;
+// block 0 builds the list.
+template <int BITS>
 __global__ __launch_bounds__(1024) void k_plan_decode(const int32_t* __restrict__ offsets,
                                                       const moe_expert_ref* __restrict__ table,
                                                       int E, int32_t* __restrict__ act_hdr,
-                                                      ActEntry* __restrict__ act) {
+                                                      ActEntry* __restrict__ act,
+                                                      const uint16_t* __restrict__ x, int T, int H,
+                                                      float* __restrict__ osx) {
+  using C = UnitCodec<BITS>;
   __shared__ int cntw[16][kPlanKeys];  // per wave and key: experts (then the exclusive prefix over waves)
   __shared__ int base[kPlanKeys];      // exclusive prefix over keys of the totals
   const int e = threadIdx.x, lane = e & 63, wv = e >> 6;
+  if (blockIdx.x > 0) {  // blocks 1.. : one (t, g) item per wave
+    const int ngx = H / C::G;
+    const int it = (blockIdx.x - 1) * 16 + wv;
+    if (it < T * ngx) {
+      const int t = it / ngx, g = it - t * ngx;
+      const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
+      const float off = lane < C::PAIRS ? C::pair_off(lane) : 0.f;
+      const uint32_t pr = lane < C::PAIRS ? x32[((int64_t)t * H + g * C::G) / 2 + lane] : 0u;
+      const float v = wave_sum_uniform<BITS>(off * (bf16_to_f32((uint16_t)pr) +
+                                                    bf16_to_f32((uint16_t)(pr >> 16))));
+      if (lane == 0) osx[it] = v;
+    }
+    return;
+  }
   for (int i = e; i < 16 * kPlanKeys; i += 1024) (&cntw[0][0])[i] = 0;
   const int lo = e < E ? offsets[e] : 0;
   const int n = e < E ? offsets[e + 1] - lo : 0;
@@ -118,7 +141,8 @@ template <int BITS, int GPW, int XT, int MODE, int WPS>
 __global__ __launch_bounds__(256, WPS) void k_gemv(
     const int32_t* __restrict__ act_hdr, const ActEntry* __restrict__ act,
     const int32_t* __restrict__ sorted_pairs, int K, const uint16_t* __restrict__ xa,
-    const uint16_t* __restrict__ xb, int R, int D, int P, int scale_f16, float* __restrict__ out) {
+    const uint16_t* __restrict__ xb, int R, int D, int P, int scale_f16, float* __restrict__ out,
+    const float* __restrict__ osx) {
   using C = UnitCodec<BITS>;
   constexpr int NM = MODE == 0 ? 2 : 1;        // matrices per expert
   constexpr int NS = MODE == 0 ? 1 : 2;        // activation rows per token (x; or h hi, lo)
@@ -152,6 +176,15 @@ __global__ __launch_bounds__(256, WPS) void k_gemv(
     const gu16_t msc = (gu16_t)(mat + gm.scales_off());
     const int row = strip * 64 + lane;
     const int g0 = ch * GPW, g1 = min(ng, g0 + GPW);
+#ifdef MOE_TRACE
+    // sampled waves (every 16th), first 8 rounds: item start, weights in, item done
+    const bool trs = (w_id & 15) == 0 && r < 8;
+    const int tslot = (MODE == 0 ? 8192 : 20480) + ((w_id >> 4) * 8 + r) * 4;
+    if (trs) {
+      MOE_TRW(tslot);
+      if ((threadIdx.x & 63) == 0) g_moe_trace[tslot + 3] = (unsigned long long)n_e;
+    }
+#endif
 
     // the item's codes and scales first: they need only the expert's address
     // (group index clamped, not branched on)
@@ -164,6 +197,12 @@ __global__ __launch_bounds__(256, WPS) void k_gemv(
       sr[i] = load_scale_dword(msc, (int64_t)row * ng + g);
     }
     asm volatile("" ::: "memory");
+#ifdef MOE_TRACE
+    if (trs) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the weights are in (trace builds only)
+      MOE_TRW(tslot + 1);
+    }
+#endif
     // staging index math from a copy of the lane id, redone per item rather than
     // hoisted out of the item loop (where it would be spilled)
     int lq = lane;
@@ -175,10 +214,12 @@ __global__ __launch_bounds__(256, WPS) void k_gemv(
       // uniform, so scalar loads, which the activation loads need not wait for
       // behind the weights
       int pid[XT];
+      if constexpr (MODE == 1) {
 #pragma unroll
-      for (int j = 0; j < XT; ++j) {
-        pid[j] = sorted_pairs[seg0 + c0 + min(j, nt - 1)];
-        asm volatile("" : "+s"(pid[j]));  // each a scalar load of its own
+        for (int j = 0; j < XT; ++j) {
+          pid[j] = sorted_pairs[seg0 + c0 + min(j, nt - 1)];
+          asm volatile("" : "+s"(pid[j]));  // each a scalar load of its own
+        }
       }
       // activations of tokens c0 .. c0+nt-1 for the item's groups, staged in
       // the wave's LDS region (lane = pair) for the offset sums; the dot
@@ -187,6 +228,8 @@ __global__ __launch_bounds__(256, WPS) void k_gemv(
       // treats the activations as read-only and turns every scalar load into a
       // 64-lane broadcast load.)  The wave's earlier LDS reads have completed
       // before the region is overwritten.
+      // (gate/up: the offset sums come precomputed per token and group in osx)
+      if constexpr (MODE == 1) {
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
 #pragma unroll
       for (int it = 0; it < IT; ++it) {
@@ -208,6 +251,7 @@ __global__ __launch_bounds__(256, WPS) void k_gemv(
           *reinterpret_cast<u32x4d*>(xs + 4 * q) = *reinterpret_cast<const u32x4d*>(src);
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's own LDS writes
+      }
 
       for (int jp = 0; jp < nt; jp += 2) {
         const bool two = jp + 1 < nt;
@@ -216,10 +260,12 @@ __global__ __launch_bounds__(256, WPS) void k_gemv(
         // the dot products take them through scalar loads, one load per 8 or 16
         // pairs for the whole wave)
         const uint32_t *r0a, *r0b, *r1a, *r1b;
+        int tk0 = 0, tk1 = 0;
         if (MODE == 0) {
-          const int t0 = sorted_pairs[seg0 + c0 + jp] / K, t1 = sorted_pairs[seg0 + c0 + j1] / K;
-          r0a = r0b = reinterpret_cast<const uint32_t*>(xa + (int64_t)t0 * D);
-          r1a = r1b = reinterpret_cast<const uint32_t*>(xa + (int64_t)t1 * D);
+          tk0 = sorted_pairs[seg0 + c0 + jp] / K;
+          tk1 = sorted_pairs[seg0 + c0 + j1] / K;
+          r0a = r0b = reinterpret_cast<const uint32_t*>(xa + (int64_t)tk0 * D);
+          r1a = r1b = reinterpret_cast<const uint32_t*>(xa + (int64_t)tk1 * D);
         } else {
           r0a = reinterpret_cast<const uint32_t*>(xa + (int64_t)(seg0 + c0 + jp) * D);
           r0b = reinterpret_cast<const uint32_t*>(xb + (int64_t)(seg0 + c0 + jp) * D);
@@ -251,9 +297,9 @@ __global__ __launch_bounds__(256, WPS) void k_gemv(
             uint32_t w[C::WORDS];
             unit_words<BITS>(cw[i], w);
             float d0 = 0.f, d1 = 0.f;
-            const float k0 = osum(x0);
+            const float k0 = MODE == 0 ? osx[(int64_t)tk0 * ng + g0 + i] : osum(x0);
             if (two) {
-              const float k1 = osum(x1);
+              const float k1 = MODE == 0 ? osx[(int64_t)tk1 * ng + g0 + i] : osum(x1);
               C::for_each_pair(w, [&](int Pp, uint32_t pr) {
                 if (NS == 2) {
                   d0 = dot2_bf16(pr, s0b[Pp], dot2_bf16(pr, s0a[Pp], d0));
@@ -283,6 +329,9 @@ __global__ __launch_bounds__(256, WPS) void k_gemv(
         }
       }
     }
+#ifdef MOE_TRACE
+    if (trs) MOE_TRW(tslot + 2);
+#endif
   }
 }
 
@@ -926,11 +975,17 @@ static hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* sh
     return hipGetLastError();
   }
 
-  MOE_LAUNCH(KID_PLAN, k_plan_decode, dim3(1), dim3(1024), 0, s, f.offsets, f.table, E, act_hdr,
-             act);
-  MOE_LAUNCH(KID_GATEUP, (k_gemv<BITS, kDecGPW, 8, 0, 3>), dim3(grid_for(items_gu, 3)),
+  float* osx = reinterpret_cast<float*>(f.ws + L.osx);
+  MOE_LAUNCH(KID_PLAN, k_plan_decode<BITS>, dim3(1 + (T * (H / C::G) + 15) / 16), dim3(1024), 0,
+             s, f.offsets, f.table, E, act_hdr, act, f.x, T, H, osx);
+// (four waves per SIMD: without the activation staging the gate/up GEMV fits
+// in 128 registers)
+#ifndef MOE_GU_WPS
+#define MOE_GU_WPS 4
+#endif
+  MOE_LAUNCH(KID_GATEUP, (k_gemv<BITS, kDecGPW, 8, 0, MOE_GU_WPS>), dim3(grid_for(items_gu, MOE_GU_WPS)),
              dim3(256), 0, s, act_hdr, act, f.sorted_pairs, K, f.x, nullptr, I, H, P, c.scale_f16,
-             gpart);
+             gpart, osx);
 #define MOE_SW(MC)                                                                            \
   MOE_LAUNCH(KID_SWIGLU, k_swiglu_sum<MC>, dim3((I + 255) / 256, P), dim3(256), 0, s, gpart,      \
              f.offsets, E, P, I, nch_gu, hh, hl)
@@ -939,7 +994,7 @@ static hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* sh
   // (launch bounds of two waves per SIMD let the down kernel's register use settle
   // at 165, still three waves per SIMD, without the spill a bound of three forces)
   MOE_LAUNCH(KID_DOWN, (k_gemv<BITS, kDecGPWd, 4, 1, 2>), dim3(grid_for(items_dn, 3)), dim3(256),
-             0, s, act_hdr, act, f.sorted_pairs, K, hh, hl, H, I, P, c.scale_f16, dpart);
+             0, s, act_hdr, act, f.sorted_pairs, K, hh, hl, H, I, P, c.scale_f16, dpart, nullptr);
   if (join) {
     const hipError_t e = hipStreamWaitEvent(s, join, 0);
     if (e != hipSuccess) return e;
