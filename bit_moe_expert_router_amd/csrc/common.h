@@ -289,6 +289,8 @@ struct WsLayout {
   int64_t act;        // decode: int32 U (64-byte header), then the active-expert list (40 B each)
   int64_t osx;        // decode: float[T][H/G]: per token and reduction group, the offset sum
                       //   sum_P off_P (x_2P + x_2P+1) of the gate/up codec
+  int64_t osh;        // decode: float[P][I/G]: the same for the down codec, per sorted
+                      //   position and group, over h hi + lo
   int64_t gpart;      // decode: float[2*NCH][P][I]: gate then up partial products per
                       //   chunk of reduction groups, rows by sorted position
   int64_t hdec;       // decode: bf16[2][P][I]: h hi rows, then h lo rows, by sorted position
@@ -322,6 +324,7 @@ __host__ inline WsLayout ws_layout(const moe_cfg& c, int T) {
   const int64_t nch_dn = (c.inter / c.group + kDecGPWd - 1) / kDecGPWd;
   L.act = take(pf ? 0 : 64 + 40 * (int64_t)c.n_experts);
   L.osx = take(pf ? 0 : (int64_t)T * (c.hidden / c.group) * 4);
+  L.osh = take(pf ? 0 : P * (c.inter / c.group) * 4);
   L.gpart = take(pf ? 0 : 2 * nch_gu * P * c.inter * 4);
   L.hdec = take(pf ? 0 : 2 * P * c.inter * 2);
   L.dpart = take(pf ? 0 : nch_dn * P * c.hidden * 4);

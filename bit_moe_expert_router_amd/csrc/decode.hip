@@ -11,10 +11,11 @@
 // then run a fixed grid of waves that take work items in a zig-zag order: an
 // item is (active expert, 64-row strip, matrix, chunk of GPW reduction groups).
 // A wave requests the item's codes and scales first (one 16-byte load per chunk
-// of a 64-row tile: 1,024 contiguous bytes per wave), then the activations of its
-// groups for up to XT of the expert's tokens, then forms the partial products of
-// its 64 rows for every token and writes them to a partial buffer, one slice per
-// chunk.  The activations reach the dot products through scalar loads (one load
+// of a 64-row tile: 1,024 contiguous bytes per wave), then forms the partial
+// products of its 64 rows for up to XT of the expert's tokens at a time and
+// writes them to a partial buffer, one slice per chunk.  The codec's offset sums
+// of each activation row and group come precomputed (the plan launch for gate/up,
+// the SwiGLU pass for down).  The activations reach the dot products through scalar loads (one load
 // of 8 pairs serves all 64 lanes); a broadcast through LDS or a vector load would
 // move every byte 64 times, which made items with several tokens LDS-bound.  No
 // item waits on another: there are no block barriers
@@ -146,20 +147,12 @@ __global__ __launch_bounds__(256, WPS) void k_gemv(
   using C = UnitCodec<BITS>;
   constexpr int NM = MODE == 0 ? 2 : 1;        // matrices per expert
   constexpr int NS = MODE == 0 ? 1 : 2;        // activation rows per token (x; or h hi, lo)
-  constexpr int PC = C::G / 8;                 // 16-byte pieces per group row
-  constexpr int NQ = XT * GPW * NS * PC;       // pieces of a staged chunk of tokens
-  constexpr int IT = (NQ + 63) / 64;
-  constexpr int XW = XT * GPW * NS * C::PAIRS;  // uint32 per wave: [token][group][row][pair]
-  static_assert(XW == 4 * NQ, "a staged piece is 16 bytes");
-  __shared__ __align__(16) uint32_t xs_all[4 * XW];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  uint32_t* xs = xs_all + wv * XW;
   const int ng = D / C::G, NCH = (ng + GPW - 1) / GPW, nstrips = R / 64;
   const int per_a = nstrips * NM * NCH;
   const int total = act_hdr[0] * per_a;
   const int nw = gridDim.x * 4;
-  const float off = lane < C::PAIRS ? C::pair_off(lane) : 0.f;
   const MatGeom gm{R, D, BITS, C::G};
 
   // zig-zag over the waves: round r takes items r*nw .. r*nw + nw-1, forwards
@@ -203,11 +196,6 @@ __global__ __launch_bounds__(256, WPS) void k_gemv(
       MOE_TRW(tslot + 1);
     }
 #endif
-    // staging index math from a copy of the lane id, redone per item rather than
-    // hoisted out of the item loop (where it would be spilled)
-    int lq = lane;
-    asm volatile("" : "+v"(lq));
-
     for (int c0 = 0; c0 < n_e; c0 += XT) {
       const int nt = min(n_e - c0, XT);
       // pair ids of positions c0 .. c0+XT-1 (clamped to the expert's last):
@@ -221,38 +209,8 @@ __global__ __launch_bounds__(256, WPS) void k_gemv(
           asm volatile("" : "+s"(pid[j]));  // each a scalar load of its own
         }
       }
-      // activations of tokens c0 .. c0+nt-1 for the item's groups, staged in
-      // the wave's LDS region (lane = pair) for the offset sums; the dot
-      // products read the same rows through scalar loads.  (A global->LDS copy
-      // instruction would save the registers, but the compiler then no longer
-      // treats the activations as read-only and turns every scalar load into a
-      // 64-lane broadcast load.)  The wave's earlier LDS reads have completed
-      // before the region is overwritten.
-      // (gate/up: the offset sums come precomputed per token and group in osx)
-      if constexpr (MODE == 1) {
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-#pragma unroll
-      for (int it = 0; it < IT; ++it) {
-        const int q = it * 64 + lq;
-        const int qc = min(q, NQ - 1);
-        const int j = min(qc / (GPW * NS * PC), nt - 1), i = (qc / (NS * PC)) % GPW;
-        const int sel = (qc / PC) % NS, pc = qc % PC;
-        const int g = min(g0 + i, g1 - 1);
-        const uint16_t* src;
-        if (MODE == 0) {
-          int pj = pid[0];
-#pragma unroll
-          for (int jj = 1; jj < XT; ++jj) pj = j == jj ? pid[jj] : pj;
-          src = xa + (int64_t)(pj / K) * D + g * C::G + 8 * pc;
-        } else {
-          src = (sel ? xb : xa) + (int64_t)(seg0 + c0 + j) * D + g * C::G + 8 * pc;
-        }
-        if (NQ % 64 == 0 || q < NQ)
-          *reinterpret_cast<u32x4d*>(xs + 4 * q) = *reinterpret_cast<const u32x4d*>(src);
-      }
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's own LDS writes
-      }
-
+      // the dot products read the activation rows through scalar loads; the
+      // offset sums of each row and group come precomputed (osx)
       for (int jp = 0; jp < nt; jp += 2) {
         const bool two = jp + 1 < nt;
         const int j1 = two ? jp + 1 : jp;
@@ -276,30 +234,21 @@ __global__ __launch_bounds__(256, WPS) void k_gemv(
 #pragma unroll
         for (int i = 0; i < GPW; ++i) {
           if (g0 + i < g1) {
-            const uint32_t* x0 = xs + (jp * GPW + i) * NS * C::PAIRS;
-            const uint32_t* x1 = xs + (j1 * GPW + i) * NS * C::PAIRS;
             const int go = (g0 + i) * C::G / 2;
             const uint32_t *s0a = r0a + go, *s0b = r0b + go, *s1a = r1a + go, *s1b = r1b + go;
             uint32_t sraw = sr[i];
             asm volatile("" : "+v"(sraw));  // convert here, not hoisted ahead of the loads
             const float sc =
                 scale_to_f32(scale_from_dword(sraw, (int64_t)row * ng + g0 + i), scale_f16);
-            // offset sums of the activations over the group (every staged row)
-            auto osum = [&](const uint32_t* xr) {
-              float t = 0.f;
-#pragma unroll
-              for (int s = 0; s < NS; ++s) {
-                const uint32_t pr = lane < C::PAIRS ? xr[s * C::PAIRS + lane] : 0u;
-                t += bf16_to_f32((uint16_t)pr) + bf16_to_f32((uint16_t)(pr >> 16));
-              }
-              return wave_sum_uniform<BITS>(off * t);
-            };
             uint32_t w[C::WORDS];
             unit_words<BITS>(cw[i], w);
             float d0 = 0.f, d1 = 0.f;
-            const float k0 = MODE == 0 ? osx[(int64_t)tk0 * ng + g0 + i] : osum(x0);
+            // offset sums: per token (gate/up) or per sorted position (down) and group
+            const int64_t o0 = MODE == 0 ? tk0 : seg0 + c0 + jp;
+            const int64_t o1 = MODE == 0 ? tk1 : seg0 + c0 + j1;
+            const float k0 = osx[o0 * ng + g0 + i];
             if (two) {
-              const float k1 = MODE == 0 ? osx[(int64_t)tk1 * ng + g0 + i] : osum(x1);
+              const float k1 = osx[o1 * ng + g0 + i];
               C::for_each_pair(w, [&](int Pp, uint32_t pr) {
                 if (NS == 2) {
                   d0 = dot2_bf16(pr, s0b[Pp], dot2_bf16(pr, s0a[Pp], d0));
@@ -809,33 +758,59 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
 // h[pos][k] = silu(sum_ch g_ch) * (sum_ch u_ch), slices added in chunk order,
 // as bf16 hi + bf16 remainder (h to ~2^-16 relative).  Positions past the
 // grouped pairs are skipped.  MC >= NCH bounds the chunk slices read per element.
-template <int MC>
+// Wave = reduction group g of the down matrix, lane = code pair P of the group
+// (elements k = g*G + 2P, 2P+1).  The same wave also forms the down codec's
+// offset sum osh[pos][g] = sum_P off_P (hi_2P + hi_2P+1 + lo_2P + lo_2P+1) (the
+// fixed-order wave sum), which the down GEMV subtracts per group.
+template <int BITS, int MC>
 __global__ __launch_bounds__(256) void k_swiglu_sum(const float* __restrict__ part,
                                                     const int32_t* __restrict__ offsets, int E,
                                                     int P, int I, int NCH,
                                                     uint16_t* __restrict__ hh,
-                                                    uint16_t* __restrict__ hl) {
+                                                    uint16_t* __restrict__ hl,
+                                                    float* __restrict__ osh) {
+  using C = UnitCodec<BITS>;
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
   const int pos = blockIdx.y;
-  const int k = blockIdx.x * 256 + threadIdx.x;
-  if (pos >= offsets[E] || k >= I) return;
-  float pg[MC], pu[MC];
+  if (pos >= offsets[E]) return;
+  const int ngd = I / C::G;
+  const int lane = threadIdx.x & 63;
+  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (g >= ngd) return;  // wave-uniform
+  const bool live = lane < C::PAIRS;
+  const int k = g * C::G + 2 * (live ? lane : 0);
+  f32x2 pg[MC], pu[MC];
 #pragma unroll
   for (int c = 0; c < MC; ++c) {
     const int cc = min(c, NCH - 1);
-    pg[c] = part[((int64_t)cc * P + pos) * I + k];
-    pu[c] = part[((int64_t)(NCH + cc) * P + pos) * I + k];
+    pg[c] = *reinterpret_cast<const f32x2*>(part + ((int64_t)cc * P + pos) * I + k);
+    pu[c] = *reinterpret_cast<const f32x2*>(part + ((int64_t)(NCH + cc) * P + pos) * I + k);
   }
-  float g = pg[0], u = pu[0];
+  uint32_t hp = 0, lp = 0;
 #pragma unroll
-  for (int c = 1; c < MC; ++c)
-    if (c < NCH) {
-      g += pg[c];
-      u += pu[c];
-    }
-  const float h = g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
-  const uint16_t hi = f32_to_bf16_rne(h);
-  hh[(int64_t)pos * I + k] = hi;
-  hl[(int64_t)pos * I + k] = f32_to_bf16_rne(h - bf16_to_f32(hi));
+  for (int e = 0; e < 2; ++e) {
+    float gs = e ? pg[0].y : pg[0].x, us = e ? pu[0].y : pu[0].x;
+#pragma unroll
+    for (int c = 1; c < MC; ++c)
+      if (c < NCH) {
+        gs += e ? pg[c].y : pg[c].x;
+        us += e ? pu[c].y : pu[c].x;
+      }
+    const float h = gs * __builtin_amdgcn_rcpf(1.f + __expf(-gs)) * us;
+    const uint16_t hi = f32_to_bf16_rne(h);
+    hp |= (uint32_t)hi << (16 * e);
+    lp |= (uint32_t)f32_to_bf16_rne(h - bf16_to_f32(hi)) << (16 * e);
+  }
+  if (live) {
+    reinterpret_cast<uint32_t*>(hh)[((int64_t)pos * I + k) / 2] = hp;
+    reinterpret_cast<uint32_t*>(hl)[((int64_t)pos * I + k) / 2] = lp;
+  }
+  const float t = live ? (bf16_to_f32((uint16_t)hp) + bf16_to_f32((uint16_t)(hp >> 16))) +
+                             (bf16_to_f32((uint16_t)lp) + bf16_to_f32((uint16_t)(lp >> 16)))
+                       : 0.f;
+  const float off = live ? C::pair_off(lane) : 0.f;
+  const float v = wave_sum_uniform<BITS>(off * t);
+  if (lane == 0) osh[(int64_t)pos * ngd + g] = v;
 }
 
 // ---------------------------------------------------------------- combine
@@ -986,15 +961,16 @@ static hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* sh
   MOE_LAUNCH(KID_GATEUP, (k_gemv<BITS, kDecGPW, 8, 0, MOE_GU_WPS>), dim3(grid_for(items_gu, MOE_GU_WPS)),
              dim3(256), 0, s, act_hdr, act, f.sorted_pairs, K, f.x, nullptr, I, H, P, c.scale_f16,
              gpart, osx);
-#define MOE_SW(MC)                                                                            \
-  MOE_LAUNCH(KID_SWIGLU, k_swiglu_sum<MC>, dim3((I + 255) / 256, P), dim3(256), 0, s, gpart,      \
-             f.offsets, E, P, I, nch_gu, hh, hl)
+  float* osh = reinterpret_cast<float*>(f.ws + L.osh);
+#define MOE_SW(MC)                                                                              \
+  MOE_LAUNCH(KID_SWIGLU, (k_swiglu_sum<BITS, MC>), dim3((I / C::G + 3) / 4, P), dim3(256), 0, s, \
+             gpart, f.offsets, E, P, I, nch_gu, hh, hl, osh)
   if (nch_gu <= 8) MOE_SW(8); else if (nch_gu <= 16) MOE_SW(16); else MOE_SW(24);
 #undef MOE_SW
-  // (launch bounds of two waves per SIMD let the down kernel's register use settle
-  // at 165, still three waves per SIMD, without the spill a bound of three forces)
-  MOE_LAUNCH(KID_DOWN, (k_gemv<BITS, kDecGPWd, 4, 1, 2>), dim3(grid_for(items_dn, 3)), dim3(256),
-             0, s, act_hdr, act, f.sorted_pairs, K, hh, hl, H, I, P, c.scale_f16, dpart, nullptr);
+  // (four waves per SIMD, as the gate/up GEMV: the offset sums come from the
+  // SwiGLU pass, so neither GEMV stages activations)
+  MOE_LAUNCH(KID_DOWN, (k_gemv<BITS, kDecGPWd, 4, 1, 4>), dim3(grid_for(items_dn, 4)), dim3(256),
+             0, s, act_hdr, act, f.sorted_pairs, K, hh, hl, H, I, P, c.scale_f16, dpart, osh);
   if (join) {
     const hipError_t e = hipStreamWaitEvent(s, join, 0);
     if (e != hipSuccess) return e;
