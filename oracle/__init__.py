@@ -57,6 +57,8 @@ def _load():
         lib.orc_permute.argtypes = [i32] * 3 + [vp] * 4
         lib.orc_expert_ffn.restype = None
         lib.orc_expert_ffn.argtypes = [i32] * 5 + [vp] * 5
+        lib.orc_expert_ffn_multi.restype = None
+        lib.orc_expert_ffn_multi.argtypes = [i32] * 5 + [vp] * 3 + [i32, vp, vp]
         lib.orc_shared_ffn.restype = None
         lib.orc_shared_ffn.argtypes = [i32, i32] + [vp] * 5
         lib.orc_moe_layer.restype = None
@@ -161,6 +163,19 @@ def expert_ffn(x, gate, up, down, H, I, bits, group, scale_f16) -> np.ndarray:
     _load().orc_expert_ffn(H, I, bits, group, int(scale_f16), _p(gate), _p(up), _p(down),
                            _p(x), _p(y))
     return y
+
+
+def expert_ffn_multi(X, gate, up, down, H, I, bits, group, scale_f16) -> np.ndarray:
+    """expert_ffn of every row of X [n, H] (each dequantised row formed once);
+    row j equals expert_ffn(X[j], ...) bit for bit"""
+    X = _c(X, np.float64).reshape(-1, H)
+    gate, up, down = (_c(a, np.uint8) for a in (gate, up, down))
+    n = X.shape[0]
+    Y = np.empty((n, H), dtype=np.float64)
+    if n:
+        _load().orc_expert_ffn_multi(H, I, bits, group, int(scale_f16), _p(gate), _p(up),
+                                     _p(down), n, _p(X), _p(Y))
+    return Y
 
 
 def shared_ffn(x, sg, su, sd) -> np.ndarray:

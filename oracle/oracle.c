@@ -278,6 +278,51 @@ void orc_expert_ffn(int H, int I, int bits, int group, int scale_f16, const uint
   free(u);
 }
 
+/* The same FFN for n input vectors X[n][H] at once, Y[n][H]: each dequantised
+ * row is formed once and applied to every vector, with the per-vector arithmetic
+ * (k ascending, fp64) of orc_matvec, so Y[j] equals orc_expert_ffn of X[j] bit
+ * for bit.  Only the tests use it, to check many pairs of one expert quickly. */
+static void orc_matmul_rows(const uint8_t* blob, int rows, int cols, int bits, int group,
+                            int scale_f16, int n, const double* V, double* Yt) {
+  /* Yt[r][j] = sum_k W[r][k] * V[j][k] */
+#pragma omp parallel
+  {
+    double* row = (double*)malloc(sizeof(double) * (size_t)cols);
+#pragma omp for schedule(static)
+    for (int r = 0; r < rows; ++r) {
+      orc_dequant_row(blob, rows, cols, bits, group, scale_f16, r, row);
+      for (int j = 0; j < n; ++j) {
+        const double* v = V + (int64_t)j * cols;
+        double acc = 0.0;
+        for (int k = 0; k < cols; ++k) acc += row[k] * v[k];
+        Yt[(int64_t)r * n + j] = acc;
+      }
+    }
+    free(row);
+  }
+}
+
+void orc_expert_ffn_multi(int H, int I, int bits, int group, int scale_f16, const uint8_t* gate,
+                          const uint8_t* up, const uint8_t* down, int n, const double* X,
+                          double* Y) {
+  double* g = (double*)malloc(sizeof(double) * (size_t)I * n);
+  double* u = (double*)malloc(sizeof(double) * (size_t)I * n);
+  double* h = (double*)malloc(sizeof(double) * (size_t)I * n);
+  double* yt = (double*)malloc(sizeof(double) * (size_t)H * n);
+  orc_matmul_rows(gate, I, H, bits, group, scale_f16, n, X, g);
+  orc_matmul_rows(up, I, H, bits, group, scale_f16, n, X, u);
+  for (int i = 0; i < I; ++i)
+    for (int j = 0; j < n; ++j)
+      h[(int64_t)j * I + i] = orc_silu(g[(int64_t)i * n + j]) * u[(int64_t)i * n + j];
+  orc_matmul_rows(down, H, I, bits, group, scale_f16, n, h, yt);
+  for (int r = 0; r < H; ++r)
+    for (int j = 0; j < n; ++j) Y[(int64_t)j * H + r] = yt[(int64_t)r * n + j];
+  free(g);
+  free(u);
+  free(h);
+  free(yt);
+}
+
 /* Same FFN with row-major bfloat16 weights (the shared expert). */
 void orc_shared_ffn(int H, int Is, const uint16_t* gate, const uint16_t* up, const uint16_t* down,
                     const double* x, double* y) {

@@ -68,6 +68,24 @@ class HostExperts:
         return oracle.expert_ffn(xf, g, u, d, cfg.hidden, cfg.inter, cfg.bits, cfg.group,
                                  cfg.scale_f16)
 
+    def ffn_pairs(self, xh, ids, pairs):
+        """oracle y(t,k) of the given pairs p = t*K + k ({p: y}); the pairs of one
+        expert go through the oracle together (each dequantised row formed once)"""
+        cfg = self.cfg
+        flat = np.asarray(ids).reshape(-1)
+        by_e = {}
+        for p in pairs:
+            by_e.setdefault(int(flat[p]), []).append(int(p))
+        out = {}
+        for e, ps in by_e.items():
+            X = synth.bf16_to_f32(np.stack([xh[p // cfg.top_k] for p in ps])).astype(np.float64)
+            g, u, d = self.blobs(e)
+            Y = oracle.expert_ffn_multi(X, g, u, d, cfg.hidden, cfg.inter, cfg.bits, cfg.group,
+                                        cfg.scale_f16)
+            for p, y in zip(ps, Y):
+                out[p] = y
+        return out
+
     def shared(self):
         if not self.cfg.shared_inter:
             return None

@@ -76,9 +76,38 @@ def test_routing_bit_exact(gpu, name, T):
 
 
 # decode batches run the GEMV kernels; T > 64 the matrix-core (prefill) kernels:
-# the 4-bit/G32/fp16-scale shape at T = 300 and the GLM shape just past the switch
+# the 4-bit/G32/fp16-scale shape at T = 300 and the GLM shape just past the switch.
+# c3 at T = 16 and 64 gives the hottest experts more tokens than one chunk of the
+# GEMVs takes (8 for gate/up, 4 for down), so their later chunks run.
 FFN_CASES = [("c1", 4), ("c1", 1), ("c1", 13), ("c2", 1), ("c2", 3), ("c3", 1), ("c3", 2),
-             ("c3", 8), ("c3", 9), ("c1", 300), ("c2", 65)]
+             ("c3", 8), ("c3", 9), ("c3", 16), ("c3", 64), ("c1", 300), ("c2", 65)]
+
+
+def check_all_pairs(cfg, xh, res, ids, w, he, label):
+    """every pair's expert output and every token's combined output against the
+    oracle; returns the worst pair error"""
+    T, K = ids.shape
+    refs = he.ffn_pairs(xh, ids, range(T * K))
+    worst = 0.0
+    for p in range(T * K):
+        r = rel_err(res["pair_out"][p], refs[p])
+        worst = max(worst, r)
+        assert r <= TOL, (label, p, int(ids.reshape(-1)[p]), r)
+    sh = he.shared()
+    if T <= 9:  # the oracle's whole layer, an independent path through the combine
+        tabs = [[he.blobs(e)[m] for e in range(cfg.n_experts)] for m in range(3)]
+        out, _ = oracle.moe_layer(xh, ids, w, *tabs, cfg.inter, cfg.bits, cfg.group,
+                                  cfg.scale_f16, sh)
+    else:  # sum_k w y(t,k) (k ascending) + shared, from the oracle's pair outputs
+        out = np.zeros((T, cfg.hidden))
+        for t in range(T):
+            for k in range(K):
+                out[t] += np.float64(w[t, k]) * refs[t * K + k]
+            if sh is not None:
+                out[t] += oracle.shared_ffn(synth.bf16_to_f32(xh[t]).astype(np.float64), *sh)
+    for t in range(T):
+        assert rel_err(res["out"][t], out[t]) <= TOL, (label, t)
+    return worst
 
 
 @pytest.mark.parametrize("name,T", FFN_CASES)
@@ -89,49 +118,91 @@ def test_expert_outputs_all_pairs(gpu, name, T):
     xh, xd = x_device(cfg, gpu, tokens=T)
     res = run_gpu(cfg, dl, xd)
     ids, w = check_routing(cfg, xh, res)
-    he = HostExperts(cfg)
-    worst = 0.0
-    for p in range(T * cfg.top_k):
-        t, e = p // cfg.top_k, ids.reshape(-1)[p]
-        y = he.ffn(xh[t], e)
-        r = rel_err(res["pair_out"][p], y)
-        worst = max(worst, r)
-        assert r <= TOL, (name, T, p, e, r)
-    # combined output of every token against the oracle's full layer
-    tabs = [[he.blobs(e)[m] for e in range(cfg.n_experts)] for m in range(3)]
-    out, _ = oracle.moe_layer(xh, ids, w, *tabs, cfg.inter, cfg.bits, cfg.group, cfg.scale_f16,
-                              he.shared())
-    for t in range(T):
-        assert rel_err(res["out"][t], out[t]) <= TOL, (name, T, t)
-    say(f"[ffn] {name} T={T} worst pair rel err {worst:.3e}")
+    counts = np.diff(res["offsets"])
+    worst = check_all_pairs(cfg, xh, res, ids, w, HostExperts(cfg), f"{name} T={T}")
+    say(f"[ffn] {name} T={T} worst pair rel err {worst:.3e}, most pairs per expert {counts.max()}")
 
 
-def test_prefill_chunk_sampled(gpu):
-    """8,192-token chunk: routing of every token is bit-exact; expert outputs are
-    checked on a sample of pairs (the hottest and coldest experts' first and last
-    pairs plus random ones) and the combined output on a sample of tokens."""
-    name, T = "c5", 8192
-    say(f"[prefill] {name} T={T}")
-    cfg = synth.CONFIGS[name]
-    dl = layer_for(name, gpu)
+@pytest.mark.parametrize("T,n_hot", [(9, 9), (40, 40), (64, 64)])
+def test_decode_long_expert_segments(gpu, T, n_hot):
+    """caller-supplied routing in which one expert takes every token (n_hot pairs)
+    and a second one every other token: the GEMVs' later token chunks (gate/up
+    takes 8 positions per chunk, down 4) all run against the oracle"""
+    say(f"[ffn] long segments c3 T={T}")
+    cfg = synth.CONFIGS["c3"]
+    dl = layer_for("c3", gpu)
     xh, xd = x_device(cfg, gpu, tokens=T)
-    res = run_gpu(cfg, dl, xd)
+    ml = make_layer_api(cfg, dl, T)
+    a = run_gpu(cfg, dl, xd, ml=ml)
+    ids, w = a["ids"].copy(), a["w"].copy()
+    hot, second = 17, 251
+    for t in range(T):
+        row = [e for e in ids[t] if e not in (hot, second)]
+        row = [hot] + ([second] if t % 2 == 0 else []) + row
+        ids[t] = np.array(row[:cfg.top_k], dtype=np.int32)
+    r = _caller_routing(ml, ids, w, cfg.n_experts, gpu)
+    b = run_gpu(cfg, dl, xd, ml=ml, routing=r)
+    counts = np.diff(b["offsets"])
+    assert counts[hot] == n_hot and counts[second] == (T + 1) // 2
+    worst = check_all_pairs(cfg, xh, b, ids, w, HostExperts(cfg), f"long T={T}")
+    say(f"[ffn] long segments T={T}: worst pair rel err {worst:.3e}")
+    ml.close()
+
+
+def _prefill_check(gpu, cfg, label):
+    """8,192-token chunk: routing of every token bit-exact; every pair of one full
+    128-position tile of the hottest expert and of the median expert, both ends of
+    the coldest expert, random pairs, and the combined output of 16 tokens"""
+    T = cfg.tokens
+    dl = layer_for("c5", gpu)
+    xh, xd = x_device(cfg, gpu, tokens=T)
+    ml = make_layer_api(cfg, dl, T)
+    r = ml.route(xd, dl.router, dl.bias if cfg.zipf else None)
+    out = torch.empty((T, cfg.hidden), dtype=torch.float32, device=gpu)
+    pair_out = torch.empty((T * cfg.top_k, cfg.hidden), dtype=torch.float32, device=gpu)
+    ml.forward(0, xd, r, out, pair_out)
+    torch.cuda.synchronize()
+    res = dict(ids=r.topk_ids.cpu().numpy(), w=r.topk_w.cpu().numpy(),
+               offsets=r.expert_offsets.cpu().numpy(), sorted=r.sorted_pairs.cpu().numpy(),
+               pos=r.pair_pos.cpu().numpy())
     ids, w = check_routing(cfg, xh, res)
     off, sp = res["offsets"], res["sorted"]
     counts = np.diff(off)
-    hot, cold = int(np.argmax(counts)), int(np.argmin(np.where(counts > 0, counts, 1 << 30)))
-    pairs = {sp[off[hot]], sp[off[hot + 1] - 1], sp[off[cold]], sp[off[cold + 1] - 1]}
+    order = np.argsort(counts, kind="stable")
+    hot = int(order[-1])
+    live = order[counts[order] > 0]
+    med = int(live[len(live) // 2])
+    cold = int(live[0])
+    pairs = set(sp[off[hot]:off[hot] + min(128, counts[hot])].tolist())
+    pairs |= set(sp[off[med]:off[med] + min(128, counts[med])].tolist())
+    pairs |= {int(sp[off[cold]]), int(sp[off[cold + 1] - 1])}
     rng = np.random.default_rng(0)
-    pairs |= set(rng.integers(0, T * cfg.top_k, size=16).tolist())
+    pairs |= set(rng.integers(0, T * cfg.top_k, size=32).tolist())
+    toks = sorted(set(rng.integers(0, T, size=16).tolist()) | {0, T - 1})
+    pairs |= {t * cfg.top_k + k for t in toks for k in range(cfg.top_k)}
     he = HostExperts(cfg)
-    for p in sorted(pairs):
-        t, e = p // cfg.top_k, ids.reshape(-1)[p]
-        r = rel_err(res["pair_out"][p], he.ffn(xh[t], e))
-        assert r <= TOL, (p, e, r)
-    for t in rng.integers(0, T, size=2).tolist():
-        ref = sum(w[t, k] * he.ffn(xh[t], ids[t, k]) for k in range(cfg.top_k))
-        assert rel_err(res["out"][t], ref) <= TOL, t
-    say(f"[prefill] hot expert {hot} has {counts[hot]} pairs")
+    refs = he.ffn_pairs(xh, ids, sorted(pairs))
+    po = pair_out.cpu().numpy()
+    worst = 0.0
+    for p, y in refs.items():
+        e = int(ids.reshape(-1)[p])
+        err = rel_err(po[p], y)
+        worst = max(worst, err)
+        assert err <= TOL, (label, p, e, err)
+    o = out.cpu().numpy()
+    for t in toks:
+        ref = sum(np.float64(w[t, k]) * refs[t * cfg.top_k + k] for k in range(cfg.top_k))
+        assert rel_err(o[t], ref) <= TOL, (label, t)
+    say(f"[prefill] {label}: hot expert {hot} {counts[hot]} pairs, median {med} {counts[med]}, "
+        f"{len(refs)} pairs checked, worst {worst:.3e}")
+    ml.close()
+
+
+@pytest.mark.parametrize("zipf", [True, False], ids=["zipf", "uniform"])
+def test_prefill_chunk(gpu, zipf):
+    cfg = synth.CONFIGS["c5"].with_(zipf=zipf)
+    say(f"[prefill] c5 T={cfg.tokens} {'zipf' if zipf else 'uniform'}")
+    _prefill_check(gpu, cfg, "zipf" if zipf else "uniform")
 
 
 def test_prefill_ragged_tiles(gpu):
@@ -155,16 +226,18 @@ def test_prefill_ragged_tiles(gpu):
     pairs |= {int(sp[off[e]]) for e in singles}
     rng = np.random.default_rng(1)
     pairs |= set(rng.integers(0, T * cfg.top_k, size=32).tolist())
+    toks = rng.integers(0, T, size=3).tolist()
+    pairs |= {t * cfg.top_k + k for t in toks for k in range(cfg.top_k)}
     he = HostExperts(cfg)
+    refs = he.ffn_pairs(xh, ids, sorted(pairs))
     worst = 0.0
-    for p in sorted(pairs):
-        t, e = p // cfg.top_k, ids.reshape(-1)[p]
-        r = rel_err(res["pair_out"][p], he.ffn(xh[t], e))
+    for p, y in refs.items():
+        r = rel_err(res["pair_out"][p], y)
         worst = max(worst, r)
-        assert r <= TOL, (p, e, r)
+        assert r <= TOL, (p, int(ids.reshape(-1)[p]), r)
     sh = he.shared()
-    for t in rng.integers(0, T, size=3).tolist():
-        ref = sum(w[t, k] * he.ffn(xh[t], ids[t, k]) for k in range(cfg.top_k))
+    for t in toks:
+        ref = sum(np.float64(w[t, k]) * refs[t * cfg.top_k + k] for k in range(cfg.top_k))
         ref = ref + oracle.shared_ffn(synth.bf16_to_f32(xh[t]).astype(np.float64), *sh)
         assert rel_err(res["out"][t], ref) <= TOL, t
     say(f"[prefill] hot expert {hot}: {counts[hot]} pairs; worst pair rel err {worst:.3e}")

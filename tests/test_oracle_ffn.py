@@ -202,3 +202,15 @@ def test_double_to_bf16_rne():
         assert oracle.double_to_bf16(v) == bits, (v, hex(oracle.double_to_bf16(v)))
     assert oracle.bf16_to_double(0x3F81) == 1 + 2 ** -7
     assert oracle.f16_to_double(0x3C00) == 1.0 and oracle.f16_to_double(0x0001) == 2 ** -24
+
+
+def test_expert_ffn_multi_equals_single():
+    """the batched form applies the same per-vector arithmetic: bit-identical rows"""
+    H, I = 256, 128
+    L = DenseLayer(H, I, 2, 3, 128, False, seed=5)
+    cfg = synth.CONFIGS["c1"]
+    x = synth.bf16_to_f32(synth.x_bf16(cfg, tokens=5)).astype(np.float64)
+    g, u, d = L.blobs[1]
+    Y = oracle.expert_ffn_multi(x, g, u, d, H, I, 3, 128, False)
+    for j in range(5):
+        assert np.array_equal(Y[j], oracle.expert_ffn(x[j], g, u, d, H, I, 3, 128, False))

@@ -36,6 +36,46 @@ def test_logits_match_definition():
     assert np.allclose(logits, ref, rtol=0, atol=1e-12)
 
 
+def test_logits_one_hot_closed_form():
+    """x = c * e_j (one nonzero bf16 entry) makes every product but one zero, so
+    l[e] = c * Wr[e, j] + bias[e] exactly: the fp64 product of a bf16 and an fp32
+    value is exact, and so is the sum of two such values of nearby magnitude.  A
+    dropped bias, a transposed router or a wrong column fails here."""
+    cfg = synth.CONFIGS["c2"]
+    Wr, b = synth.router_f32(cfg), synth.zipf_bias(cfg)
+    H = cfg.hidden
+    cols = [0, 1, 127, 128, 2559, H - 1]
+    vals = [1.0, -2.5, 0.375, -1.0, 3.0, 0.0078125]
+    x = np.zeros((len(cols), H), dtype=np.uint16)
+    for t, (j, c) in enumerate(zip(cols, vals)):
+        x[t, j] = synth.bf16_bits(np.array([c]))[0]
+    _, _, _, logits = oracle.route(x, Wr, b, cfg.top_k)
+    for t, (j, c) in enumerate(zip(cols, vals)):
+        expect = c * Wr[:, j].astype(np.float64) + b.astype(np.float64)
+        assert np.array_equal(logits[t], expect), (t, j)
+
+
+def test_logits_dyadic_exact_sum():
+    """x entries in {0, +-1/2, +-1, +-2} and router entries k/1024 with small
+    integers k: every partial sum is a multiple of 2^-11 far below 2^53, so the
+    fp64 logits are the exact rational sums, computed here with Python integers
+    (order-free).  Pins the whole reduction (every column, every row)."""
+    rng = np.random.default_rng(7)
+    T, H, E = 5, 512, 24
+    xv = rng.choice(np.array([0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0]), size=(T, H))
+    x = synth.bf16_bits(xv)
+    kr = rng.integers(-300, 301, size=(E, H))
+    Wr = (kr / 1024.0).astype(np.float32)
+    kb = rng.integers(-5000, 5001, size=E)
+    bias = (kb / 1024.0).astype(np.float32)
+    _, _, _, logits = oracle.route(x, Wr, bias, 4)
+    xi = (xv * 2).astype(np.int64)  # x * 2, integers
+    for t in range(T):
+        for e in range(E):
+            num = sum(int(xi[t, h]) * int(kr[e, h]) for h in range(H)) + 2 * int(kb[e])
+            assert logits[t, e] == num / 2048.0, (t, e)
+
+
 def test_tie_break_lower_id_first():
     """duplicated router rows give exactly equal logits; the lower id wins and is
     listed first"""
@@ -79,15 +119,19 @@ def test_weights_equal_restricted_softmax(name):
     assert np.all(np.diff(w, axis=1) <= 0)  # descending logits -> descending weights
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c5"])
-def test_config_seeds_have_no_near_ties(name):
+@pytest.mark.parametrize("name,zipf", [("c1", False), ("c2", True), ("c3", True), ("c5", True),
+                                       ("c5", False)])
+def test_config_seeds_have_no_near_ties(name, zipf):
     """Routing ids are compared bit-exactly against the GPU, so every token of the
-    fixed seeds must keep its K-th pick clear of the (K+1)-th by far more than
-    any fp64 summation-order difference (< 1e-12 here)."""
-    cfg = synth.CONFIGS[name]
+    fixed seeds must keep its K-th pick clear of the (K+1)-th, and the picks clear
+    of each other (their order is the output order), by far more than any fp64
+    summation-order difference (< 1e-12 here)."""
+    cfg = synth.CONFIGS[name].with_(zipf=zipf)
     x, Wr, b = _inputs(cfg)
     ids, _, gap, logits = oracle.route(x, Wr, b, cfg.top_k)
     assert gap.min() > 1e-9, (name, gap.min())
+    top = np.take_along_axis(logits, ids.astype(np.int64), axis=1)
+    assert np.all(-np.diff(top, axis=1) > 1e-9), name
 
 
 def test_zipf_skews_routing():
