@@ -4,26 +4,34 @@
 A step is one pass of the whole layer (routing: logits, top-k, grouping; experts:
 gate/up + SwiGLU, down; shared expert when the workload has one; weighted
 combine) over one batch of synthetic tokens whose inputs are already resident in
-HBM.  The default workload is one GLM-5.3-Flash-shaped MoE layer at decode batch
+HBM.  The headline workload is one GLM-5.3-Flash-shaped MoE layer at decode batch
 1 (hidden 5120, expert intermediate 1536, 288 experts, top-8, 3-bit group-128
-weights with bf16 scales, Zipf(1.1) router bias).  Steps rotate over several
-resident copies of the layer (distinct weights, router and bias) so that no step
-is served from the 256 MB last-level cache.  The timed steps are replays of HIP
-graphs that each hold several consecutive layer steps (a decoder replays one graph
-over all its layers), so the per-replay launch cost is shared as it is there; every
-step in a graph does the whole layer on its own layer's weights.
+weights with bf16 scales, Zipf(1.1) router bias).  Decode steps rotate over
+several resident copies of the layer (distinct weights, router and bias) so that
+no step is served from the 256 MB last-level cache.  The timed steps are replays
+of HIP graphs that each hold several consecutive layer steps (a decoder replays
+one graph over all its layers), so the per-replay launch cost is shared as it is
+there; every step in a graph does the whole layer on its own layer's weights.
 
-Prints ONE JSON line: tokens/s over the timed steps, the dominant kernel's
-achieved expert-weight bandwidth against the 8 TB/s HBM peak (prefill: matrix-core
-flops against the dense fp16 peak; kernel durations from HIP events that each
-launch timestamps at the kernel's start and end on its stream), and the fp64 CPU
-oracle timed on a bounded sample of the same workload.
+Prints ONE JSON line.  `value` is the headline workload's tokens/s.  `roofline`
+describes the longest kernel of its step: algorithmic expert-weight bytes per
+launch over the kernel's average duration against the 8 TB/s HBM peak (prefill:
+matrix-core flops against the dense fp16 peak), with durations from HIP events
+that each launch timestamps at the kernel's start and end on its own stream, and
+the HBM traffic rocprofv3 counted for that kernel (when the committed counter
+summary matches the current sources).  `extra.step` gives the whole step's
+expert bytes over the step time.  `extra.workloads` repeats all of this for the
+decode batch sweep (2, 4, 8 tokens), batch 8 with the shared expert and remapped
+table, the 42-layer stack at batch 4 and the 8,192-token prefill chunk with Zipf
+and uniform routing.  `cpu_baseline` is the fp64 CPU oracle timed on a bounded
+sample of the same workload.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -32,18 +40,26 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16/bf16 matrix peak of the MI355X
+MFMA_F64_PEAK_TFLOPS = 78.6    # dense fp64 matrix peak
 METRIC = "MoE-layer tokens/s (decode b=1..8, prefill 8K) + expert-weight HBM GB/s vs peak"
 
-WORKLOAD_TEXT = {
-    "c1": "tiny MoE layer: H 256, I 128, 16 experts, top-2, 4-bit G32 fp16 scales",
-    "c2": "one GLM-5.3-Flash-shaped MoE layer at decode: H 5120, I 1536, 288 experts, top-8, "
-          "3-bit G128 bf16 scales, Zipf(1.1) router bias",
-    "c3": "GLM-shaped MoE layer at decode batch 8 + bf16 shared expert (I 1536), expert pointer "
-          "table remapped to a seeded slot permutation, Zipf(1.1) bias",
-    "c4": "42-layer stack of GLM-shaped MoE layers at decode batch 4 (RMSNorm glue, shared experts, "
-          "remapped tables, own Zipf bias per layer)",
-    "c5": "8,192-token prefill chunk through one GLM-shaped MoE layer (3-bit G128), Zipf(1.1) bias",
+WORKLOADS = {
+    "c1": ("c1", {}, "tiny MoE layer: H 256, I 128, 16 experts, top-2, 4-bit G32 fp16 scales"),
+    "c2": ("c2", {}, "one GLM-5.3-Flash-shaped MoE layer at decode batch 1: H 5120, I 1536, "
+                     "288 experts, top-8, 3-bit G128 bf16 scales, Zipf(1.1) router bias"),
+    "c2b2": ("c2", {"tokens": 2}, "the same layer at decode batch 2"),
+    "c2b4": ("c2", {"tokens": 4}, "the same layer at decode batch 4"),
+    "c2b8": ("c2", {"tokens": 8}, "the same layer at decode batch 8"),
+    "c3": ("c3", {}, "GLM-shaped MoE layer at decode batch 8 + bf16 shared expert (I 1536), expert "
+                     "pointer table remapped to a seeded slot permutation, Zipf(1.1) bias"),
+    "c4": ("c4", {}, "42-layer stack of GLM-shaped MoE layers at decode batch 4 (RMSNorm glue, "
+                     "shared experts, remapped tables, own Zipf bias per layer)"),
+    "c5": ("c5", {}, "8,192-token prefill chunk through one GLM-shaped MoE layer (3-bit G128), "
+                     "Zipf(1.1) bias"),
+    "c5u": ("c5", {"zipf": False}, "8,192-token prefill chunk through one GLM-shaped MoE layer "
+                                   "(3-bit G128), uniform routing (no bias)"),
 }
+DEFAULT_EXTRA = "c2b2,c2b4,c2b8,c3,c4,c5,c5u"
 
 
 def parse():
@@ -51,32 +67,103 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
-    ap.add_argument("--tokens", type=int, default=None, help="batch (default: the workload's)")
-    ap.add_argument("--uniform", action="store_true", help="no Zipf router bias")
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--extra", default=DEFAULT_EXTRA,
+                    help="comma-separated further workloads reported under extra.workloads "
+                         "('' for none)")
+    ap.add_argument("--tokens", type=int, default=None, help="batch of the main workload")
     ap.add_argument("--layers", type=int, default=None,
-                    help="resident layer copies the steps rotate over (default: 16 at decode)")
+                    help="resident layer copies the decode steps rotate over (default 16)")
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--graph-steps", type=int, default=8,
                     help="consecutive layer steps captured in one HIP graph for the single-layer "
                          "workloads (as a decoder replays one graph over many layers); the largest "
                          "value up to this that divides both --steps and the rotated layer count")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="budget of the CPU-oracle baseline sample (0: skip)")
+                    help="budget of the main workload's CPU-oracle baseline (0: skip); the further "
+                         "workloads get a quarter of it each")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--no-kernel-timing", action="store_true")
     return ap.parse_args()
 
 
-def main():
-    a = parse()
-    if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; a multi-GPU run is not part of it "
-                                   "(expert or data parallel sharding is described in DESIGN.md)",
-                          "n_gpus": a.gpus}))
-        sys.exit(2)
+# ------------------------------------------------------------------ work per kernel
+def kernel_symbol(kname, T, prefill):
+    """library kernel behind a profiled name at batch T"""
+    if prefill:
+        return {"gateup": "k_gateup_mfma", "down": "k_down_mfma", "route_logits": "k_logits_mfma",
+                "combine": "k_combine"}.get(kname, kname)
+    if T <= 2:
+        return {"gateup": "k_gateup_smem", "down": "k_down_blk", "route": "k_route_small",
+                "combine": "k_combine_parts"}.get(kname, kname)
+    return {"gateup": "k_gemv<MODE 0> (gate/up)", "down": "k_gemv<MODE 1> (down)",
+            "route_logits": "k_logits_small", "combine": "k_combine_parts",
+            "swiglu": "k_swiglu_sum", "plan": "k_plan_decode",
+            "shared_gateup": "k_shared_gateup", "shared_down": "k_shared_down"}.get(kname, kname)
 
+
+def kernel_work(kname, cfg, T, u_mean, lay, prefill):
+    """(algorithmic amount per launch, kind) of a profiled kernel; kind is "bytes",
+    "f16" (matrix-core flops) or "f64" (fp64 matrix-core flops); None for the
+    latency-bound glue kernels"""
+    glay, ulay, dlay = lay
+    P = T * cfg.top_k
+    H, I, E, Is = cfg.hidden, cfg.inter, cfg.n_experts, cfg.shared_inter
+    if kname == "gateup":
+        return (4 * P * H * I, "f16") if prefill else (u_mean * (glay.nbytes + ulay.nbytes), "bytes")
+    if kname == "down":
+        return (2 * P * H * I, "f16") if prefill else (u_mean * dlay.nbytes, "bytes")
+    if kname == "route":
+        return E * H * 4 + T * H * 2, "bytes"
+    if kname == "route_logits":
+        return (2 * T * E * H, "f64") if T > 32 else (E * H * 4 + T * H * 2, "bytes")
+    if kname == "shared_gateup":
+        return 2 * Is * H * 2, "bytes"
+    if kname == "shared_down":
+        return H * Is * 2, "bytes"
+    return None
+
+
+def roofline_of(kname, avg_us, work, traffic):
+    amount, kind = work
+    if kind == "bytes":
+        ach = amount / (avg_us * 1e-6) / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "bytes_per_launch": round(amount)}
+    peak = MFMA_F16_PEAK_TFLOPS if kind == "f16" else MFMA_F64_PEAK_TFLOPS
+    ach = amount / (avg_us * 1e-6) / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(ach / peak, 4), "traffic": traffic, "flops_per_launch": round(amount),
+            "dtype": "f16" if kind == "f16" else "f64"}
+
+
+def measured_traffic(symbol, workload):
+    """HBM bytes per launch of `symbol` on `workload` from the committed counter
+    summary (profiles/traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE, calibrated
+    against a plain device copy), or None when there is none or the kernel's
+    sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        ent = json.load(fh).get("kernels", {}).get(f"{symbol}@{workload}")
+    if not ent:
+        return None
+    h = hashlib.sha256()
+    for src in ent["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != ent["sha256_16"]:
+        return None
+    return ent["hbm_bytes_per_launch"]
+
+
+# ------------------------------------------------------------------ one workload
+def run_workload(name, a, dev, cpu_budget, main_tokens=None, one_thread=True):
     import numpy as np
     import torch
 
@@ -84,16 +171,15 @@ def main():
     from synth.device import DeviceLayer
     import bit_moe_expert_router_amd as moe
 
-    dev = torch.device("cuda:0")
-    cfg = synth.CONFIGS[a.workload]
-    if a.tokens:
-        cfg = cfg.with_(tokens=a.tokens)
-    if a.uniform:
-        cfg = cfg.with_(zipf=False)
+    base, over, text = WORKLOADS[name]
+    cfg = synth.CONFIGS[base].with_(**over)
+    if main_tokens:
+        cfg = cfg.with_(tokens=main_tokens)
     T = cfg.tokens
     decode = T <= 64
     stack = cfg.layers > 1
-    L = cfg.layers if stack else (a.layers or (16 if decode else 1))
+    L = cfg.layers if stack else ((a.layers or 16) if decode else 1)
+    prefill = T > 64 and cfg.hidden % 128 == 0 and cfg.inter % 128 == 0
 
     # ---------------------------------------------------------- resident inputs
     t0 = time.time()
@@ -190,8 +276,7 @@ def main():
     tokens_per_s = T * a.steps / wall
 
     # ---------------------------------------------------------- kernel timing
-    eb = synth.expert_bytes(cfg)
-    glay, ulay, dlay = synth.expert_layouts(cfg)
+    lay = synth.expert_layouts(cfg)
     kern = {}
     kt_steps = min(a.steps, 10) if stack else a.steps
     if not a.no_kernel_timing:
@@ -205,150 +290,230 @@ def main():
     # algorithmic bytes over the kernel-timing pass (same step sequence); a stack
     # step launches every layer once
     u_steps = [U[i % L] for i in range(kt_steps)] if not stack else [u for _ in range(kt_steps) for u in U]
-    gu_bytes = sum(u * (glay.nbytes + ulay.nbytes) for u in u_steps)
-    dn_bytes = sum(u * dlay.nbytes for u in u_steps)
+    u_mean = float(np.mean(u_steps))
+    expert_bytes_step = sum(u_steps) * synth.expert_bytes(cfg) / kt_steps
+    shared_bytes_step = (L if stack else 1) * synth.shared_bytes(cfg)
+    res = {"workload": f"{name}: {text}", "tokens": T, "value": round(tokens_per_s, 1),
+           "unit": "tokens/s", "ms_per_step": round(ms_step, 5),
+           "distinct_experts_per_layer": round(u_mean, 2), "layers_rotated": L,
+           "graph_replay": graphs is not None, "steps_per_graph": G if graphs is not None else None,
+           "input_gen_s": round(gen_s, 1)}
     roof = None
-    extra = {}
-    prefill = T > 64 and cfg.hidden % 128 == 0 and cfg.inter % 128 == 0
-    # algorithmic matrix-core work of the prefill path: every pair's gate and up
-    # products (2 x 2*H*I flops) and its down product (2*I*H flops)
-    gu_flops = T * cfg.top_k * 4 * cfg.hidden * cfg.inter
-    dn_flops = T * cfg.top_k * 2 * cfg.hidden * cfg.inter
     if kern:
-        gu_ms, gu_n = kern.get("gateup", (0.0, 0))
-        dn_ms, dn_n = kern.get("down", (0.0, 0))
-        if prefill:
-            ach = gu_flops * gu_n / (gu_ms * 1e-3) / 1e12 if gu_ms else None
-            roof = {"bound": "mfma", "achieved": round(ach, 1) if ach else None,
-                    "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4) if ach else None,
-                    "traffic": measured_traffic("k_gateup_mfma", a.workload),
-                    "kernel": "k_gateup_mfma (grouped gate+up GEMM, SwiGLU epilogue)",
-                    "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
-                    "avg_us": round(gu_ms / gu_n * 1e3, 2) if gu_n else None,
-                    "flops_per_launch": gu_flops}
-            if dn_ms:
-                extra["down_TFLOPs"] = round(dn_flops * dn_n / (dn_ms * 1e-3) / 1e12, 1)
-        else:
-            ach = gu_bytes / (gu_ms * 1e-3) / 1e9 if gu_ms else None
-            gu_kernel = "k_gateup_smem" if T <= 2 else "k_gemv (gate/up)"
-            roof = {"bound": "hbm", "achieved": round(ach, 1) if ach else None, "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4) if ach else None,
-                    "traffic": measured_traffic(gu_kernel, a.workload),
-                    "kernel": gu_kernel + " (gate and up GEMV)",
-                    "avg_us": round(gu_ms / gu_n * 1e3, 2) if gu_n else None,
-                    "bytes_per_launch": round(gu_bytes / len(u_steps)),
-                    "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)"}
-            if dn_ms:
-                extra["down_GBs"] = round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1)
-        extra["kernels_us"] = {k: round(v[0] / v[1] * 1e3, 2) for k, v in kern.items() if v[1]}
-        tot_ms = sum(v[0] for v in kern.values())
-        extra["expert_bytes_per_step"] = round((gu_bytes + dn_bytes) / kt_steps)
-        extra["expert_GBs_over_kernel_time"] = round((gu_bytes + dn_bytes) / (tot_ms * 1e-3) / 1e9, 1)
-    extra["expert_GBs_over_step"] = round((gu_bytes + dn_bytes) / kt_steps / (ms_step * 1e-3) / 1e9, 1)
-    extra["distinct_experts_per_step"] = round(float(np.mean(u_steps)), 2)
-    extra["graph_replay"] = graphs is not None
-    extra["steps_per_graph"] = G if graphs is not None else None
-    extra["input_gen_s"] = round(gen_s, 1)
+        us = {k: v[0] / v[1] * 1e3 for k, v in kern.items() if v[1]}
+        per_step_us = {k: kern[k][0] * 1e3 / kt_steps for k in us}
+        res["kernels_us"] = {k: round(v, 2) for k, v in us.items()}
+        # the longest kernel of the step (time per step), with its own roofline
+        ranked = sorted(per_step_us, key=lambda k: -per_step_us[k])
+        for k in ranked:
+            work = kernel_work(k, cfg, T, u_mean, lay, prefill)
+            if work is None:
+                continue
+            sym = kernel_symbol(k, T, prefill)
+            roof = roofline_of(k, us[k], work, measured_traffic(sym, name))
+            roof.update({"kernel": sym, "avg_us": round(us[k], 2),
+                         "longest_in_step": k == ranked[0],
+                         "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                         "calibrated against a plain device copy)"})
+            break
+        others = {}
+        for k in ranked:
+            work = kernel_work(k, cfg, T, u_mean, lay, prefill)
+            if work is not None and (roof is None or kernel_symbol(k, T, prefill) != roof["kernel"]):
+                r = roofline_of(k, us[k], work, None)
+                others[k] = {"achieved": r["achieved"], "unit": r["unit"], "frac": r["frac"]}
+        res["other_kernels_roofline"] = others
+    step_bytes = expert_bytes_step + shared_bytes_step
+    step_gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    res["step"] = {"expert_bytes": round(step_bytes), "achieved_GBs": round(step_gbs, 1),
+                   "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                   "note": "routed expert bytes (once per distinct expert per layer) + shared "
+                           "expert bytes, over the whole step time"}
+    if prefill:
+        flops = 6 * T * cfg.top_k * cfg.hidden * cfg.inter
+        tf = flops / (ms_step * 1e-3) / 1e12
+        res["step"].update({"flops": flops, "achieved_TFLOPs": round(tf, 1),
+                            "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)})
+    res["roofline"] = roof
+    res["dtype"] = "f16" if prefill else "bf16"
 
-    if a.calib_copy:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        extra["calib_copy_bytes"] = 1 << 30
-
-    # ---------------------------------------------------------- CPU oracle baseline
-    cpu = None
-    if a.cpu_seconds > 0:
-        cpu = cpu_baseline(cfg, L, a.cpu_seconds, layers_per_step=L if stack else 1)
-
-    res = {
-        "metric": METRIC,
-        "value": round(tokens_per_s, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": a.steps,
-        "warmup": a.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f16" if prefill else "bf16",
-        "data": "synthetic (seeded counter-based generator; random 3-bit codes and scales, "
-                "N(0,1) bf16 activations, N(0,0.02) fp32 router)",
-        "config": {"workload": f"{a.workload}: {WORKLOAD_TEXT[a.workload]}", "tokens": T,
-                   "layers_rotated": L, "hidden": cfg.hidden, "inter": cfg.inter,
-                   "experts": cfg.n_experts, "top_k": cfg.top_k, "bits": cfg.bits,
-                   "group": cfg.group, "zipf": cfg.zipf, "shared_inter": cfg.shared_inter},
-        "roofline": roof,
-        "cpu_baseline": cpu,
-        "extra": extra,
-    }
-    print(json.dumps(res))
+    # release the device memory before the CPU leg and the next workload
+    del graphs, layers, xd, out
     ml.close()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    if cpu_budget > 0:
+        res["cpu_baseline"] = cpu_baseline(cfg, L, cpu_budget, layers_per_step=L if stack else 1,
+                                           one_thread=one_thread)
+    return res
 
 
-def measured_traffic(kernel, workload):
-    """HBM bytes per launch of `kernel` from the committed counter summary
-    (profiles/traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE, calibrated against a
-    plain device copy), or None when there is none for this workload or the kernel's
-    sources changed since the counters were taken."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as fh:
-        ent = json.load(fh).get("kernels", {}).get(kernel)
-    if not ent or ent.get("workload") != workload:
-        return None
-    h = hashlib.sha256()
-    for src in ent["sources"]:
-        with open(os.path.join(ROOT, src), "rb") as fh:
-            h.update(fh.read())
-    if h.hexdigest()[:16] != ent["sha256_16"]:
-        return None
-    return ent["hbm_bytes_per_launch"]
+def stream_ceiling(dev):
+    """A plain streaming read (torch sum over fp32) and copy of sizes around the
+    decode kernels' bytes, each timed over distinct buffers (no last-level-cache
+    reuse): the practical rate of the memory system for a launch of that size."""
+    import torch
+    res = {}
+    for mb in (24.576, 49.152, 1073.741824):
+        n = int(mb * 1e6) // 4
+        nbuf = max(2, int(600e6 // (n * 4)) + 1)
+        bufs = [torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0) for _ in range(nbuf)]
+        dst = torch.empty(n, dtype=torch.float32, device=dev)
+        reps = max(2 * nbuf, 8)
+        for b in bufs:
+            b.sum()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            bufs[i % nbuf].sum()
+        e1.record()
+        torch.cuda.synchronize()
+        rd_us = e0.elapsed_time(e1) * 1e3 / reps
+        e0.record()
+        for i in range(reps):
+            dst.copy_(bufs[i % nbuf])
+        e1.record()
+        torch.cuda.synchronize()
+        cp_us = e0.elapsed_time(e1) * 1e3 / reps
+        res[f"{mb:.1f}MB"] = {"read_us": round(rd_us, 2), "read_GBs": round(n * 4 / rd_us / 1e3, 1),
+                              "copy_us": round(cp_us, 2),
+                              "copy_GBs_read_plus_write": round(2 * n * 4 / cp_us / 1e3, 1)}
+        del bufs, dst
+        torch.cuda.empty_cache()
+    res["how"] = ("torch float32 sum (read) and copy_ (read + write) over rotating distinct "
+                  "buffers, HIP events around back-to-back launches")
+    return res
 
 
-def cpu_baseline(cfg, L, budget_s, layers_per_step=1):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(cfg, L, budget_s, layers_per_step=1, one_thread=True):
     """fp64 oracle (the test reference, untuned) on the host cores: routing, every
     pick's expert FFN and the combine of one batch per layer, rotating over the
-    same layers; timed until the budget is spent.  Batches above 16 tokens are
-    sampled: the first 16 tokens of the batch are routed and computed per layer.
-    A step of a stack is layers_per_step such layers."""
+    same layers.  Batches above 16 tokens are sampled: the first 16 tokens of the
+    batch are routed and computed per layer.  Three timed runs at the host's full
+    OpenMP thread count (median reported) and three at one thread on a one-token
+    sample; each run does at least one layer evaluation.  A step of a stack is
+    layers_per_step such layers."""
     import numpy as np
 
     import oracle
     import synth
 
     off = synth.matrix_offsets(cfg)
-    T = min(cfg.tokens, 16)
-    xh = synth.x_bf16(cfg)[:T]
     cache = {}
-    steps, spent = 0, 0.0
-    while spent < budget_s:
-        l = steps % L
+
+    def layer_inputs(l):
         if l not in cache:
             wr, bias = synth.router_f32(cfg, l), synth.zipf_bias(cfg, l)
-            ids, _, _, _ = oracle.route(xh, wr, bias, cfg.top_k)
+            xs = synth.x_bf16(cfg)[:min(cfg.tokens, 16)]
+            ids, _, _, _ = oracle.route(xs, wr, bias, cfg.top_k)
             blobs = {int(e): synth.expert_blob(cfg, l, int(e)) for e in np.unique(ids)}
             tabs = [[blobs[e][off[m]:(off[m + 1] if m < 2 else None)] if e in blobs else
                      np.zeros(16, np.uint8) for e in range(cfg.n_experts)] for m in range(3)]
             cache[l] = (wr, bias, tabs, synth.shared_weights(cfg, l))
-        wr, bias, tabs, shared = cache[l]
-        t0 = time.perf_counter()  # input generation above is not timed
-        ids, w, _, _ = oracle.route(xh, wr, bias, cfg.top_k)
-        oracle.moe_layer(xh, ids, w, *tabs, cfg.inter, cfg.bits, cfg.group, cfg.scale_f16, shared)
-        spent += time.perf_counter() - t0
-        steps += 1
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(T * steps / spent / layers_per_step, 3), "unit": "tokens/s",
-            "cores": threads, "kind": "oracle",
-            "sample": f"{steps} layer evaluations of {T} token(s) of the same workload (routing + "
-                      f"every pick's fp64 expert FFN + combine, rotating over {min(L, steps)} "
-                      f"layers; a step is {layers_per_step} layer(s)), {spent:.1f} s, "
-                      f"{threads} OpenMP threads"}
+        return cache[l]
+
+    def timed(T, budget, start):
+        xh = synth.x_bf16(cfg)[:T]
+        steps, spent = 0, 0.0
+        while spent < budget or steps == 0:
+            l = (start + steps) % L
+            wr, bias, tabs, shared = layer_inputs(l)
+            t0 = time.perf_counter()  # input generation above is not timed
+            ids, w, _, _ = oracle.route(xh, wr, bias, cfg.top_k)
+            oracle.moe_layer(xh, ids, w, *tabs, cfg.inter, cfg.bits, cfg.group, cfg.scale_f16,
+                             shared)
+            spent += time.perf_counter() - t0
+            steps += 1
+        return T * steps / spent / layers_per_step, steps, spent
+
+    nthr = oracle.max_threads()
+    T = min(cfg.tokens, 16)
+    all_runs = [timed(T, budget_s / (4 if one_thread else 3), 3 * i) for i in range(3)]
+    one_runs = []
+    if one_thread:
+        oracle.set_threads(1)
+        try:
+            one_runs = [timed(1, budget_s / 12, 3 * i) for i in range(3)]
+        finally:
+            oracle.set_threads(nthr)
+    v_all = statistics.median(r[0] for r in all_runs)
+    res = {"value": round(v_all, 3), "unit": "tokens/s", "cores": nthr, "kind": "oracle",
+           "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+           "sample": f"median of 3 runs of {'/'.join(str(r[1]) for r in all_runs)} layer "
+                     f"evaluations of {T} token(s) of the same workload (routing + every pick's "
+                     f"fp64 expert FFN + combine, rotating over the layers; a step is "
+                     f"{layers_per_step} layer(s)) at {nthr} OpenMP threads"}
+    if one_runs:
+        res["one_thread"] = round(statistics.median(r[0] for r in one_runs), 4)
+        res["sample"] += (f"; one_thread: median of 3 runs of "
+                          f"{'/'.join(str(r[1]) for r in one_runs)} one-token evaluations at 1 thread")
+    return res
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; a multi-GPU run is not part of it "
+                                   "(expert or data parallel sharding is described in DESIGN.md)",
+                          "n_gpus": a.gpus}))
+        sys.exit(2)
+
+    import torch
+    dev = torch.device("cuda:0")
+    main_res = run_workload(a.workload, a, dev, a.cpu_seconds, main_tokens=a.tokens)
+    print(f"[bench] {a.workload}: {main_res['value']} tokens/s", file=sys.stderr, flush=True)
+    extra = {}
+    for name in [w for w in a.extra.split(",") if w and w != a.workload]:
+        extra[name] = run_workload(name, a, dev, a.cpu_seconds / 4, one_thread=False)
+        print(f"[bench] {name}: {extra[name]['value']} tokens/s", file=sys.stderr, flush=True)
+    ceiling = None if a.no_ceiling else stream_ceiling(dev)
+
+    if a.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    m = main_res
+    res = {
+        "metric": METRIC,
+        "value": m["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": m["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": m["dtype"],
+        "data": "synthetic (seeded counter-based generator; random 3-bit codes and scales, "
+                "N(0,1) bf16 activations, N(0,0.02) fp32 router)",
+        "config": {"workload": m["workload"], "tokens": m["tokens"],
+                   "layers_rotated": m["layers_rotated"]},
+        "roofline": m["roofline"],
+        "cpu_baseline": m.get("cpu_baseline"),
+        "extra": {k: v for k, v in m.items() if k not in ("roofline", "cpu_baseline", "value",
+                                                           "ms_per_step", "dtype", "unit")},
+    }
+    res["extra"]["workloads"] = extra
+    res["extra"]["stream_ceiling"] = ceiling
+    if a.calib_copy:
+        res["extra"]["calib_copy_bytes"] = 1 << 30
+    print(json.dumps(res))
 
 
 if __name__ == "__main__":

@@ -147,12 +147,10 @@ moe_status set_expert_table(moe_ctx* ctx, int32_t layer, const moe_expert_ref* h
     if (!aligned(r.gate, 256) || !aligned(r.up, 256) || !aligned(r.down, 256))
       return fail(MOE_E_ARG, "set_expert_table: expert %d blob not 256-byte aligned", e);
   }
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t err = hipMemcpyAsync(ctx->d_tables + (size_t)layer * E, host_table,
-                                  sizeof(moe_expert_ref) * E, hipMemcpyHostToDevice, s);
-  if (err != hipSuccess) return hip_status(err, "set_expert_table");
-  // the host table may be reused by the caller right after return
-  err = hipStreamSynchronize(s);
+  // the entries travel as kernel arguments: the host table may be reused right
+  // after return, nothing waits, and a captured graph holds its own copy
+  const hipError_t err = moe::launch_set_table(ctx->d_tables + (size_t)layer * E, host_table, E,
+                                               (hipStream_t)stream);
   if (err != hipSuccess) return hip_status(err, "set_expert_table");
   ctx->table_set[layer] = 1;
   return ok();

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "moe.h"
 
 namespace moe {
@@ -262,6 +264,76 @@ __device__ __forceinline__ int take_ticket(int32_t* ctr) {
 constexpr int kCounters = 1024;
 constexpr int kCtrRoute = 0;
 constexpr int kCtrStrip = 64;
+// Two words of the same region are not counters.  [kCtrError] is the
+// workspace's error word (byte offset 4, MOE_WS_ERROR_OFFSET in moe.h): bit 0 is
+// set, and stays set, when moe_forward finds caller-supplied routing
+// inconsistent; only moe_workspace_init or the caller clears it.  [kCtrCallBad]
+// is the current call's verdict on its routing: written once per moe_forward by
+// the kernel that checks the routing, read by the kernels that write the
+// caller's outputs, which then write nothing.
+constexpr int kCtrError = 1;
+constexpr int kCtrCallBad = 2;
+static_assert(kCtrError * 4 == MOE_WS_ERROR_OFFSET, "error word offset");
+
+// ---------------------------------------------------------------- routing check
+// Caller-supplied routing is consistent when offsets[0] == 0, the offsets never
+// decrease, offsets[E] equals the number of pairs whose id lies in [0, E), and
+// every grouped position i < offsets[E] holds a pair p in [0, P) whose id e has
+// offsets[e] <= i < offsets[e+1], the pairs of one expert ascending.  Then
+// sorted_pairs[0 .. offsets[E]) lists exactly the pairs with a valid id, grouped
+// by expert and stable by pair index, as moe_route writes them.
+//
+// One wave checks P <= 64 pairs (every lane returns the verdict); E <= 1024.
+__device__ __forceinline__ bool routing_ok_wave(const int32_t* __restrict__ ids,
+                                                const int32_t* __restrict__ offsets,
+                                                const int32_t* __restrict__ sp, int P, int E) {
+  const int lane = threadIdx.x & 63;
+  const int id = lane < P ? ids[lane] : -1;
+  const int s = lane < P ? sp[lane] : 0;
+  const int sprev = (lane > 0 && lane < P) ? sp[lane - 1] : -1;
+  const int oE = offsets[E];
+  const int nch = (E + 63) / 64;
+  int lo[16], hi[16];
+  bool bad = false;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    if (c < nch) {
+      const int e = lane + 64 * c;
+      lo[c] = e < E ? offsets[e] : 0;
+      hi[c] = e < E ? offsets[e + 1] : 0;
+      bad |= e < E && hi[c] < lo[c];
+    }
+  }
+  bad |= lane == 0 && lo[0] != 0;
+  const int nvalid = __popcll(__ballot(id >= 0 && id < E));
+  bad |= oE != nvalid;
+  // the expert of the pair at position `lane` and its segment (shuffles: every lane)
+  const int e = __shfl(id, min(max(s, 0), 63));
+  const int ec = min(max(e, 0), E - 1);
+  int elo = 0, ehi = 0;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    if (c < nch) {
+      const int a = __shfl(lo[c], ec & 63), b = __shfl(hi[c], ec & 63);
+      if ((ec >> 6) == c) {
+        elo = a;
+        ehi = b;
+      }
+    }
+  }
+  if (lane < oE && oE <= P)
+    bad |= s < 0 || s >= P || e < 0 || e >= E || lane < elo || lane >= ehi ||
+           (lane > elo && sprev >= s);
+  return __ballot(bad) == 0;
+}
+
+// Record a call's verdict (one writer per call) and, for a bad one, set the
+// sticky error bit.
+__device__ __forceinline__ void record_routing(int32_t* ctr, bool ok) {
+  ctr[kCtrCallBad] = ok ? 0 : 1;
+  if (!ok) atomicOr(ctr + kCtrError, 1);
+}
+
 
 // Batches up to this many tokens run the GEMV (decode) kernels; larger ones the
 // matrix-core (prefill) kernels when the shape allows them.
@@ -299,6 +371,8 @@ struct WsLayout {
   int64_t xshift;     // prefill: int32[T]
   int64_t h16;        // prefill: fp16[P][I] h rows by sorted position
   int64_t tiles;      // prefill: int32[1 + 2*max_tiles] tile plan
+  int64_t vchk;       // prefill: int32[2][ceil(max(P, E) / 256)]: per block of the routing
+                      //   check, the valid-id pair count and an error flag
   int64_t pair_out;   // float[P][H] (used when the caller passes no pair_out)
   int64_t sh_part;    // float[2*4][T][Is]: shared gate and up partial sums per slice
   int64_t sh_h;       // float[T][Is]: shared expert h
@@ -332,6 +406,7 @@ __host__ inline WsLayout ws_layout(const moe_cfg& c, int T) {
   L.xshift = take(pf ? (int64_t)T * 4 : 0);
   L.h16 = take(pf ? P * c.inter * 2 : 0);
   L.tiles = take(pf ? (1 + 2 * prefill_max_tiles(P, c.n_experts)) * 4 : 0);
+  L.vchk = take(pf ? 2 * ((std::max<int64_t>(P, c.n_experts) + 255) / 256) * 4 : 0);
   L.pair_out = take(pf ? P * c.hidden * 4 : 0);
   L.sh_part = take(8 * (int64_t)T * c.shared_inter * 4);
   L.sh_h = take((int64_t)T * c.shared_inter * 4);
@@ -374,7 +449,8 @@ __host__ inline WsLayout ws_layout(const moe_cfg& c, int T) {
 // ---------------------------------------------------------------- profiling
 enum KernelId {
   KID_LOGITS = 0, KID_TOPK, KID_PERMUTE, KID_PLAN, KID_GATEUP, KID_DOWN, KID_SH_GATEUP,
-  KID_SH_DOWN, KID_COMBINE, KID_RMSNORM, KID_ZERO, KID_XPREP, KID_SWIGLU, KID_ROUTE, KID_COUNT
+  KID_SH_DOWN, KID_COMBINE, KID_RMSNORM, KID_ZERO, KID_XPREP, KID_SWIGLU, KID_ROUTE, KID_TABLE,
+  KID_COUNT
 };
 // when profiling is on: a pair of events for the next launch of kernel kid
 bool prof_events(int kid, hipEvent_t* b, hipEvent_t* e);
@@ -423,5 +499,7 @@ hipError_t launch_forward(const FwdArgs& f, hipStream_t s);
 hipError_t launch_rmsnorm(float* resid, const float* add, int T, int H, float eps, uint16_t* y,
                           hipStream_t s);
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
+hipError_t launch_set_table(moe_expert_ref* dst, const moe_expert_ref* host, int n,
+                            hipStream_t s);
 
 }  // namespace moe

@@ -56,9 +56,13 @@ constexpr int kPlanKeys = 65;  // 0..63: 63 - min(n, 63) for active experts; 64:
 // the gate/up matrices, the codec's offset sum osx[t][g] = sum_P off_P (x_2P +
 // x_2P+1) (one wave per (t, g), lane = pair, the fixed-order wave sum), which the
 // gate/up GEMV subtracts per group instead of reducing it in every work item;
-// block 0 builds the list.
+// block 0 checks the routing (thread i: expert i and grouped position i; P, E <=
+// 1024) and builds the list, or, for inconsistent routing, an empty one.
 template <int BITS>
 __global__ __launch_bounds__(1024) void k_plan_decode(const int32_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ ids,
+                                                      const int32_t* __restrict__ sorted_pairs,
+                                                      int P, int32_t* __restrict__ ctr,
                                                       const moe_expert_ref* __restrict__ table,
                                                       int E, int32_t* __restrict__ act_hdr,
                                                       ActEntry* __restrict__ act,
@@ -67,6 +71,8 @@ __global__ __launch_bounds__(1024) void k_plan_decode(const int32_t* __restrict_
   using C = UnitCodec<BITS>;
   __shared__ int cntw[16][kPlanKeys];  // per wave and key: experts (then the exclusive prefix over waves)
   __shared__ int base[kPlanKeys];      // exclusive prefix over keys of the totals
+  __shared__ int s_off[1025];
+  __shared__ int s_id[1024];
   const int e = threadIdx.x, lane = e & 63, wv = e >> 6;
   if (blockIdx.x > 0) {  // blocks 1.. : one (t, g) item per wave
     const int ngx = H / C::G;
@@ -84,7 +90,33 @@ __global__ __launch_bounds__(1024) void k_plan_decode(const int32_t* __restrict_
   }
   for (int i = e; i < 16 * kPlanKeys; i += 1024) (&cntw[0][0])[i] = 0;
   const int lo = e < E ? offsets[e] : 0;
-  const int n = e < E ? offsets[e + 1] - lo : 0;
+  const int hi = e < E ? offsets[e + 1] : 0;
+  // the routing check (as routing_ok_wave, one thread per expert and position)
+  const int idv = e < P ? ids[e] : -1;
+  const int sp_i = e < P ? sorted_pairs[e] : 0;
+  const int sp_prev = (e > 0 && e < P) ? sorted_pairs[e - 1] : -1;
+  if (e < E) s_off[e] = lo;
+  if (e == E - 1) s_off[E] = hi;
+  if (e < P) s_id[e] = idv;
+  const int nvalid = __syncthreads_count(idv >= 0 && idv < E);
+  const int oE = s_off[E];
+  bool bad = (e < E && hi < lo) || (e == 0 && (lo != 0 || oE != nvalid));
+  if (e < oE && oE <= P) {
+    const bool pin = sp_i >= 0 && sp_i < P;
+    const int ep = pin ? s_id[sp_i] : -1;
+    const bool ein = ep >= 0 && ep < E;
+    const int elo = ein ? s_off[ep] : 0, ehi = ein ? s_off[ep + 1] : 0;
+    bad |= !ein || e < elo || e >= ehi || (e > elo && sp_prev >= sp_i);
+  }
+  if (__syncthreads_or(bad)) {  // nothing runs, the outputs are left untouched
+    if (e == 0) {
+      act_hdr[0] = 0;
+      record_routing(ctr, false);
+    }
+    return;
+  }
+  if (e == 0) record_routing(ctr, true);
+  const int n = hi - lo;
   const int key = n > 0 ? 63 - min(n, 63) : 64;
   // lanes of this wave with the same key (one ballot per key bit)
   uint64_t eq = __ballot(1);
@@ -302,7 +334,8 @@ constexpr int kMaxKParts = 4;
 // ---------------------------------------------------------------- active experts
 // The a-th expert (ascending logical id) that owns at least one pair, the number
 // U of such experts, its segment of the grouping and its table entry.
-// Wave-cooperative (every lane returns the same values).  Each lane loads the
+// Wave-cooperative (every lane returns the same values); positions clamped into
+// [0, P).  Each lane loads the
 // offsets and the table entries of its candidate experts lane + 64*i in the same
 // round trip, so the expert's weight addresses are known after one memory
 // latency instead of two.  E <= 1024.
@@ -316,7 +349,7 @@ struct Active {
 
 __device__ __forceinline__ Active find_active(const int32_t* __restrict__ offsets,
                                               const moe_expert_ref* __restrict__ table, int E,
-                                              int a) {
+                                              int P, int a) {
   const int lane = threadIdx.x & 63;
   constexpr int kSpec = 5;  // candidates per lane whose table entry is fetched up front
   const int nch = (E + 63) / 64;
@@ -326,8 +359,11 @@ __device__ __forceinline__ Active find_active(const int32_t* __restrict__ offset
   for (int i = 0; i < 16; ++i) {
     if (i < nch) {  // uniform
       const int e = lane + 64 * i;
-      lo[i] = (e < E) ? offsets[e] : 0;
-      hi[i] = (e < E) ? offsets[e + 1] : 0;
+      // segments clamped into [0, P]: every position read stays inside the
+      // grouping buffers even when caller-supplied offsets are wrong (such a
+      // call is then found bad and writes nothing)
+      lo[i] = (e < E) ? min(max(offsets[e], 0), P) : 0;
+      hi[i] = (e < E) ? min(max(offsets[e + 1], lo[i]), P) : 0;
       if (i < kSpec) ref[i] = e < E ? table[e] : moe_expert_ref{nullptr, nullptr, nullptr};
     }
   }
@@ -373,7 +409,8 @@ __device__ __forceinline__ Active find_active(const int32_t* __restrict__ offset
 template <int BITS, int GPW>
 __global__ __launch_bounds__(256, 3) void k_gateup_smem(
     const moe_expert_ref* __restrict__ table, int E, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_pairs, int K,
+    const int32_t* __restrict__ sorted_pairs, int K, const int32_t* __restrict__ ids,
+    int32_t* __restrict__ ctr,
     const uint16_t* __restrict__ x,  // read-only: dot operands through scalar loads
     const uint16_t* x_vec,           // the same activations; not restrict, so that its vector
                                      // loads stay ahead of the weight loads
@@ -385,9 +422,21 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
   const int tb = 4 * (blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
   MOE_TR(tb);
 
-  const Active act = find_active(offsets, table, E, blockIdx.x);
+  // block (0, 0, 0) also checks the routing (one wave, in registers) and records
+  // the call's verdict for the down kernel, which writes the outputs
+  const bool checker = blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0;
+  auto check = [&]() {
+    if (threadIdx.x < 64) {
+      const bool ok = routing_ok_wave(ids, offsets, sorted_pairs, P, E);
+      if (threadIdx.x == 0) record_routing(ctr, ok);
+    }
+  };
+  const Active act = find_active(offsets, table, E, P, blockIdx.x);
   MOE_TR(tb + 1);
-  if (act.e < 0) return;
+  if (act.e < 0) {
+    if (checker) check();
+    return;
+  }
   const int seg0 = __builtin_amdgcn_readfirstlane(act.seg0);
   const int n_e = __builtin_amdgcn_readfirstlane(act.n);
   const int strip = blockIdx.y, m = blockIdx.z / KP, kp = blockIdx.z % KP;
@@ -425,7 +474,9 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
       xo[i] = xv32[((int64_t)t * H + g * C::G) / 2 + pl];
     }
   };
-  const int sp0 = sorted_pairs[seg0], sp1 = sorted_pairs[seg0 + min(1, n_e - 1)];
+  // pair ids clamped into [0, P): token rows stay inside x for any routing
+  auto pair_at = [&](int pos) { return min(max(sorted_pairs[pos], 0), P - 1); };
+  const int sp0 = pair_at(seg0), sp1 = pair_at(seg0 + min(1, n_e - 1));
   uint32_t xo0[GPW], xo1[GPW];
   load_xo(sp0 / K, xo0);
   load_xo(sp1 / K, xo1);  // (sp1 = sp0 for a single position)
@@ -442,8 +493,8 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
   // as it goes)
   auto pass = [&](int b0, u32x4 (&cwp)[GPW][C::CHUNKS], uint32_t (&srp)[GPW]) {
     const bool two = b0 + 1 < n_e;
-    const int t0 = sorted_pairs[seg0 + b0] / K;
-    const int t1 = two ? sorted_pairs[seg0 + b0 + 1] / K : t0;
+    const int t0 = pair_at(seg0 + b0) / K;
+    const int t1 = two ? pair_at(seg0 + b0 + 1) / K : t0;
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
@@ -512,8 +563,8 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
   // more than two positions (a token that lists the expert twice): later passes
   // request the groups again, in the same way
   for (int b0 = kTokPerPass; b0 < n_e; b0 += kTokPerPass) {
-    load_xo(sorted_pairs[seg0 + b0] / K, xo0);
-    load_xo(sorted_pairs[seg0 + min(b0 + 1, n_e - 1)] / K, xo1);
+    load_xo(pair_at(seg0 + b0) / K, xo0);
+    load_xo(pair_at(seg0 + min(b0 + 1, n_e - 1)) / K, xo1);
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < GPW; ++i)
@@ -521,6 +572,7 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
     asm volatile("" ::: "memory");
     pass(b0, cw, sr);
   }
+  if (checker) check();
   MOE_TR(tb + 3);
 }
 
@@ -627,7 +679,7 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
     const int32_t* __restrict__ sorted_pairs, int H, int I, int P, int scale_f16,
     const float* __restrict__ part, float* pair_out, const int32_t* __restrict__ ids,
     const float* __restrict__ wts, int K, int T, const float* shared, int nsh,
-    int32_t* __restrict__ ctr, float* __restrict__ out) {
+    int32_t* __restrict__ ctr, const int32_t* __restrict__ call_bad, float* __restrict__ out) {
   using C = UnitCodec<BITS>;
   using HS = HFromParts<BITS, GPW, XT, KP>;
   constexpr int XW = XT * GPW * 2 * C::PAIRS;  // uint32 per wave: [token][group][hi|lo][pair]
@@ -637,9 +689,11 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
   const int tb = 4096 + 8 * (blockIdx.x + gridDim.x * blockIdx.y);
   MOE_TR(tb);
 
-  const Active act = find_active(offsets, table, E, blockIdx.x);
+  const int bad = call_bad[0];  // the routing check's verdict (gate/up kernel)
+  const Active act = find_active(offsets, table, E, P, blockIdx.x);
   MOE_TR(tb + 1);
   const int strip = blockIdx.y;
+  if (bad) return;  // inconsistent caller routing: the outputs are left untouched
   if (act.e < 0) {  // no expert for this block; with none at all, block 0 combines
     if (out && act.U == 0 && blockIdx.x == 0)
       combine_strip(pair_out, ids, wts, K, E, H, shared, nsh, T, strip, out);
@@ -657,7 +711,7 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
 
   // pair ids of the expert's first 64 positions (lane = position), then h of the
   // first positions, all ahead of the weights
-  int pids = sorted_pairs[seg0 + min(lane, n_e - 1)];
+  int pids = sorted_pairs[seg0 + min(lane, n_e - 1)];  // (a checked routing: in [0, P))
   HS hst;
   int nt = min(n_e, XT);
   hst.load(part, P, I, seg0, nt, wv, ng - 1, lane);
@@ -823,7 +877,9 @@ __global__ __launch_bounds__(256) void k_combine_parts(const float* __restrict__
                                                        int P, const int32_t* __restrict__ ids,
                                                        const float* __restrict__ w, int K, int E,
                                                        int H, const float* __restrict__ shared,
-                                                       int nsh, int T, float* __restrict__ out,
+                                                       int nsh, int T,
+                                                       const int32_t* __restrict__ call_bad,
+                                                       float* __restrict__ out,
                                                        float* __restrict__ pair_out) {
   const int t = blockIdx.y;
   const int n = min((int)(blockIdx.x * 256 + threadIdx.x), H - 1);
@@ -835,6 +891,7 @@ __global__ __launch_bounds__(256) void k_combine_parts(const float* __restrict__
       y[k][c] = part[((int64_t)min(c, NCH - 1) * P + (int64_t)t * K + min(k, K - 1)) * H + n];
   float acc = 0.f;
   const bool in = blockIdx.x * 256 + threadIdx.x < H;
+  const int bad = call_bad[0];
 #pragma unroll
   for (int k = 0; k < KM; ++k) {
     const int id = ids[t * K + min(k, K - 1)];
@@ -844,7 +901,7 @@ __global__ __launch_bounds__(256) void k_combine_parts(const float* __restrict__
       for (int c = 1; c < MC; ++c)
         if (c < NCH) v += y[k][c];
       acc = fmaf(w[t * K + min(k, K - 1)], v, acc);
-      if (pair_out && in) pair_out[((int64_t)t * K + k) * H + n] = v;
+      if (pair_out && in && !bad) pair_out[((int64_t)t * K + k) * H + n] = v;
     }
   }
   if (shared) {  // the shared expert's slices, in slice order
@@ -852,7 +909,7 @@ __global__ __launch_bounds__(256) void k_combine_parts(const float* __restrict__
     for (int q = 0; q < nsh; ++q) sh += shared[((int64_t)q * T + t) * H + n];
     acc += sh;
   }
-  if (in) out[(int64_t)t * H + n] = acc;
+  if (in && !bad) out[(int64_t)t * H + n] = acc;
 }
 
 // ---------------------------------------------------------------- launcher
@@ -890,6 +947,8 @@ static hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* sh
   };
   const int64_t items_gu = (int64_t)maxU * (I / 64) * 2 * nch_gu;
   const int64_t items_dn = (int64_t)maxU * (H / 64) * nch_dn;
+  int32_t* ctr0 = reinterpret_cast<int32_t*>(f.ws + L.counters);
+  const int32_t* call_bad = ctr0 + kCtrCallBad;
 
   if (T <= 2) {  // block-level path: no plan kernel
     const int ngh = H / C::G;
@@ -900,8 +959,8 @@ static hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* sh
 #define MOE_GU(N)                                                                                \
   case N:                                                                                        \
     MOE_LAUNCH(KID_GATEUP, (k_gateup_smem<BITS, N>), dim3(maxU, I / 64, 2 * KP),                 \
-               dim3(64 * kGUWaves), 0, s, f.table, E, f.offsets, f.sorted_pairs, K, f.x, f.x, H, I, \
-               P, KP, c.scale_f16, gpart);                                                       \
+               dim3(64 * kGUWaves), 0, s, f.table, E, f.offsets, f.sorted_pairs, K, f.ids, ctr0, f.x, \
+               f.x, H, I, P, KP, c.scale_f16, gpart);                                            \
     break;
     switch (gpw_gu) {
       MOE_GU(1) MOE_GU(2) MOE_GU(3) MOE_GU(4) MOE_GU(5)
@@ -921,7 +980,7 @@ static hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* sh
   case N:                                                                                        \
     MOE_LAUNCH(KID_DOWN, (k_down_blk<BITS, N, 2, KPT>), dim3(maxU, H / 64), dim3(64 * kDNWaves), \
                0, s, f.table, E, f.offsets, f.sorted_pairs, H, I, P, c.scale_f16, gpart, y,      \
-               f.ids, f.w, K, T, shared_out, nsh, ctr, cout);                                    \
+               f.ids, f.w, K, T, shared_out, nsh, ctr, call_bad, cout);                          \
     break;
 #define MOE_DN_KP(KPT)                                                                           \
     switch (gpw_dn) {                                                                            \
@@ -942,17 +1001,17 @@ static hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* sh
     // y holds every pair's output in pair order: a single "chunk"
     if (K <= 8) {
       MOE_LAUNCH(KID_COMBINE, (k_combine_parts<8, 1>), dim3((H + 255) / 256, T), dim3(256), 0, s, y,
-                 1, P, f.ids, f.w, K, E, H, shared_out, nsh, T, f.out, nullptr);
+                 1, P, f.ids, f.w, K, E, H, shared_out, nsh, T, call_bad, f.out, nullptr);
     } else {
       MOE_LAUNCH(KID_COMBINE, (k_combine_parts<16, 1>), dim3((H + 255) / 256, T), dim3(256), 0, s,
-                 y, 1, P, f.ids, f.w, K, E, H, shared_out, nsh, T, f.out, nullptr);
+                 y, 1, P, f.ids, f.w, K, E, H, shared_out, nsh, T, call_bad, f.out, nullptr);
     }
     return hipGetLastError();
   }
 
   float* osx = reinterpret_cast<float*>(f.ws + L.osx);
   MOE_LAUNCH(KID_PLAN, k_plan_decode<BITS>, dim3(1 + (T * (H / C::G) + 15) / 16), dim3(1024), 0,
-             s, f.offsets, f.table, E, act_hdr, act, f.x, T, H, osx);
+             s, f.offsets, f.ids, f.sorted_pairs, P, ctr0, f.table, E, act_hdr, act, f.x, T, H, osx);
 // (four waves per SIMD: without the activation staging the gate/up GEMV fits
 // in 128 registers)
 #ifndef MOE_GU_WPS
@@ -978,7 +1037,7 @@ static hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* sh
   // MC: chunks of the down reduction read per pair (I/G <= 32 groups, 3 per chunk)
 #define MOE_CMB(KM, MC)                                                                        \
   MOE_LAUNCH(KID_COMBINE, (k_combine_parts<KM, MC>), dim3((H + 255) / 256, T), dim3(256), 0, s, \
-             dpart, nch_dn, P, f.ids, f.w, K, E, H, shared_out, nsh, T, f.out, f.pair_out)
+             dpart, nch_dn, P, f.ids, f.w, K, E, H, shared_out, nsh, T, call_bad, f.out, f.pair_out)
   if (K <= 8) {
     if (nch_dn <= 4) MOE_CMB(8, 4); else MOE_CMB(8, 12);
   } else {

@@ -30,6 +30,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ pair_
                                                  const int32_t* __restrict__ ids,
                                                  const float* __restrict__ w, int K, int E, int H,
                                                  const float* __restrict__ shared, int nsh, int T,
+                                                 const int32_t* __restrict__ call_bad,
                                                  float* __restrict__ out) {
   const int t = blockIdx.y;
   const int n = min((int)(blockIdx.x * 256 + threadIdx.x), H - 1);
@@ -47,7 +48,8 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ pair_
     for (int q = 0; q < nsh; ++q) sh += shared[((int64_t)q * T + t) * H + n];
     acc += sh;
   }
-  if (blockIdx.x * 256 + threadIdx.x < H) out[(int64_t)t * H + n] = acc;
+  // inconsistent caller routing: the output is left untouched
+  if (blockIdx.x * 256 + threadIdx.x < H && !call_bad[0]) out[(int64_t)t * H + n] = acc;
 }
 
 // ---------------------------------------------------------------- shared expert
@@ -317,6 +319,32 @@ __global__ __launch_bounds__(256) void k_rmsnorm(float* __restrict__ resid,
   }
 }
 
+// ---------------------------------------------------------------- pointer table
+// A layer's table entries travel as a kernel argument (by value, kTableChunk
+// entries per launch), so setting a table needs no host staging buffer, returns
+// without waiting, and a captured graph keeps its own copy of the entries.
+constexpr int kTableChunk = 128;  // 3 KB of kernel arguments
+struct TableChunk {
+  moe_expert_ref e[kTableChunk];
+};
+
+__global__ __launch_bounds__(kTableChunk) void k_set_table(moe_expert_ref* __restrict__ dst,
+                                                           TableChunk src, int n) {
+  const int i = threadIdx.x;
+  if (i < n) dst[i] = src.e[i];
+}
+
+hipError_t launch_set_table(moe_expert_ref* dst, const moe_expert_ref* host, int n,
+                            hipStream_t s) {
+  for (int b = 0; b < n; b += kTableChunk) {
+    TableChunk c;
+    const int m = std::min(kTableChunk, n - b);
+    for (int i = 0; i < kTableChunk; ++i) c.e[i] = host[b + std::min(i, m - 1)];
+    MOE_LAUNCH(KID_TABLE, k_set_table, dim3(1), dim3(kTableChunk), 0, s, dst + b, c, m);
+  }
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- counters init
 __global__ void k_zero_i32(int32_t* p, int n) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -357,12 +385,13 @@ hipError_t launch_forward_t(const FwdArgs& f, hipStream_t s) {
   hipError_t err = launch_prefill(f, L, pair_out, s);
   if (err == hipSuccess && join) err = hipStreamWaitEvent(s, join, 0);
   if (err != hipSuccess) return err;
+  const int32_t* call_bad = reinterpret_cast<const int32_t*>(f.ws + L.counters) + kCtrCallBad;
   if (K <= 8) {
     MOE_LAUNCH(KID_COMBINE, k_combine<8>, dim3((H + 255) / 256, T), dim3(256), 0, s, pair_out,
-               f.ids, f.w, K, E, H, sh_out, nsh, T, f.out);
+               f.ids, f.w, K, E, H, sh_out, nsh, T, call_bad, f.out);
   } else {
     MOE_LAUNCH(KID_COMBINE, k_combine<16>, dim3((H + 255) / 256, T), dim3(256), 0, s, pair_out,
-               f.ids, f.w, K, E, H, sh_out, nsh, T, f.out);
+               f.ids, f.w, K, E, H, sh_out, nsh, T, call_bad, f.out);
   }
   return hipGetLastError();
 }

@@ -79,13 +79,84 @@ __global__ __launch_bounds__(256) void k_xprep(const uint16_t* __restrict__ x, i
   }
 }
 
+// ---------------------------------------------------------------- routing check
+// The conditions of routing_ok_wave (common.h) for any number of pairs: thread i
+// checks expert i's offsets, the id of pair i and grouped position i; block b
+// writes its count of pairs with an id in [0, E) to vchk[2b] and whether any
+// check failed to vchk[2b + 1].  The tile plan combines the blocks.
+__global__ __launch_bounds__(256) void k_check_routing(const int32_t* __restrict__ ids,
+                                                       const int32_t* __restrict__ offsets,
+                                                       const int32_t* __restrict__ sp, int P,
+                                                       int E, int32_t* __restrict__ vchk) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int oE = offsets[E];
+  bool bad = false;
+  if (i < E) {
+    const int a = offsets[i], b = offsets[i + 1];
+    bad |= b < a || (i == 0 && a != 0);
+  }
+  const int idv = i < P ? ids[i] : -1;
+  if (i < oE && oE <= P) {
+    const int p = sp[i];
+    const bool pin = p >= 0 && p < P;
+    const int ep = pin ? ids[p] : -1;
+    const bool ein = ep >= 0 && ep < E;
+    const int elo = ein ? offsets[ep] : 0, ehi = ein ? offsets[ep + 1] : 0;
+    bad |= !ein || i < elo || i >= ehi || (i > elo && sp[i - 1] >= p);
+  }
+  const int cnt = __syncthreads_count(idv >= 0 && idv < E);
+  const int anyb = __syncthreads_or(bad);
+  if (threadIdx.x == 0) {
+    vchk[2 * blockIdx.x] = cnt;
+    vchk[2 * blockIdx.x + 1] = anyb;
+  }
+}
+
 // ---------------------------------------------------------------- tile plan
 // tiles[0] = number of tiles; tiles[1 + 2j] = expert, tiles[2 + 2j] = first sorted
 // position of tile j.  Experts in ascending order, ceil(n_e / 128) tiles each.
+// First the routing check's verdict (nb blocks of k_check_routing, plus offsets[E]
+// against the count of valid pairs): for inconsistent routing there are no
+// tiles, and the combine writes nothing.
 __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ offsets, int E,
+                                               const int32_t* __restrict__ vchk, int nb,
+                                               int32_t* __restrict__ ctr,
                                                int32_t* __restrict__ tiles) {
   __shared__ int wsum[16];
+  __shared__ int wbad[16];
   const int e = threadIdx.x, lane = e & 63, wv = e >> 6;
+  {
+    int cnt = 0, b = 0;
+    for (int j = e; j < nb; j += 1024) {
+      cnt += vchk[2 * j];
+      b |= vchk[2 * j + 1];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      cnt += __shfl_xor(cnt, o);
+      b |= __shfl_xor(b, o);
+    }
+    if (lane == 0) {
+      wsum[wv] = cnt;
+      wbad[wv] = b;
+    }
+    __syncthreads();
+    int total = 0, anyb = 0;
+    for (int w = 0; w < 16; ++w) {
+      total += wsum[w];
+      anyb |= wbad[w];
+    }
+    const bool ok = !anyb && offsets[E] == total;
+    __syncthreads();  // wsum is reused below
+    if (!ok) {
+      if (e == 0) {
+        tiles[0] = 0;
+        record_routing(ctr, false);
+      }
+      return;
+    }
+    if (e == 0) record_routing(ctr, true);
+  }
   const int lo = e < E ? offsets[e] : 0;
   const int n = e < E ? offsets[e + 1] - lo : 0;
   const int nt = (n + kPM - 1) / kPM;
@@ -492,7 +563,12 @@ static hipError_t launch_prefill_t(const FwdArgs& f, const WsLayout& L, float* p
   const int64_t max_tiles = prefill_max_tiles(P, E);
   auto round8 = [](int64_t n) { return (int)((n + 7) / 8 * 8); };
   MOE_LAUNCH(KID_XPREP, k_xprep, dim3(T), dim3(256), 0, s, f.x, H, x16, xshift);
-  MOE_LAUNCH(KID_PLAN, k_plan, dim3(1), dim3(1024), 0, s, f.offsets, E, tiles);
+  int32_t* vchk = reinterpret_cast<int32_t*>(f.ws + L.vchk);
+  const int nbc = (std::max(P, E) + 255) / 256;
+  MOE_LAUNCH(KID_PLAN, k_check_routing, dim3(nbc), dim3(256), 0, s, f.ids, f.offsets,
+             f.sorted_pairs, P, E, vchk);
+  MOE_LAUNCH(KID_PLAN, k_plan, dim3(1), dim3(1024), 0, s, f.offsets, E, vchk, nbc,
+             reinterpret_cast<int32_t*>(f.ws + L.counters), tiles);
   MOE_LAUNCH(KID_GATEUP, k_gateup_mfma<BITS>, dim3(round8(max_tiles * (I / kGuN))),
              dim3(256), 0, s, f.table, f.offsets, tiles, f.sorted_pairs, K, x16, xshift, H, I,
              c.scale_f16, h16);

@@ -20,7 +20,7 @@ namespace {
 const char* const kNames[KID_COUNT] = {"route_logits", "route_topk", "route_permute", "plan",
                                        "gateup",       "down",       "shared_gateup", "shared_down",
                                        "combine",      "rmsnorm",    "zero",          "xprep",        "swiglu",
-                                       "route"};
+                                       "route",        "set_table"};
 
 struct Rec {
   int kid;

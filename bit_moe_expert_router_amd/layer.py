@@ -78,6 +78,15 @@ class MoELayer:
                     r.sorted_pairs, out, pair_out, self.ws, stream)
         return out
 
+    def error_word(self) -> int:
+        """the workspace's error word (waits for the device)"""
+        from . import MOE_WS_ERROR_OFFSET
+        return int(self.ws[MOE_WS_ERROR_OFFSET:MOE_WS_ERROR_OFFSET + 4].view(torch.int32).item())
+
+    def clear_error(self):
+        from . import MOE_WS_ERROR_OFFSET
+        self.ws[MOE_WS_ERROR_OFFSET:MOE_WS_ERROR_OFFSET + 4].zero_()
+
     def rmsnorm_bf16(self, resid, add, y_bf16, eps=1e-6, stream=None):
         moe_rmsnorm_bf16(self.ctx, resid, add, resid.shape[0], eps, y_bf16, stream)
         return y_bf16

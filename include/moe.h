@@ -59,6 +59,13 @@ extern "C" {
 typedef struct moe_ctx moe_ctx;
 typedef void* moe_stream_t; /* a hipStream_t */
 
+/* The workspace's error word: an int32 at this byte offset of the workspace.
+ * moe_forward sets MOE_ERR_ROUTING in it (atomically; the bit stays set) when it
+ * finds caller-supplied routing inconsistent.  moe_workspace_init clears it; so
+ * may the caller (stream-ordered write of 0). */
+#define MOE_WS_ERROR_OFFSET 4
+#define MOE_ERR_ROUTING 1
+
 typedef enum {
   MOE_OK = 0,
   MOE_E_ARG = 1,          /* invalid argument (null, misaligned, out of range)    */
@@ -87,7 +94,9 @@ typedef struct {
   const void* down;
 } moe_expert_ref;
 
-/* Create a context for n_layers layers of shape *cfg.  Allocates only the device
+/* Create a context for n_layers layers of shape *cfg (the layer of the page
+ * "GLM-5.3-Flash EXL3 3.05bpw on 1x RTX 3090 -- RAM/NVMe expert tiering", field
+ * summary: top-8 of 288 experts per token and layer).  Allocates only the device
  * pointer tables (3 pointers per expert per layer), the shared-expert pointer
  * slots and, when shared_inter > 0, the shared expert's stream and two events.  H and I must be multiples of 64 and of G; Is a multiple of 64.
  * Returns MOE_E_UNSUPPORTED for other shapes, MOE_E_NOMEM on allocation failure. */
@@ -104,30 +113,49 @@ moe_status moe_destroy(moe_ctx* ctx);
  * (|h| must stay below 65504). */
 size_t moe_workspace_bytes(const moe_ctx* ctx, int32_t n_tokens);
 
-/* Zero the workspace's counters; must run once on a new workspace before its
- * first use (zero-filled memory also qualifies).  Every later call leaves them
- * zero again.  Uses a fill kernel, not a memset. */
+/* Zero the workspace's counters and its error word; must run once on a new
+ * workspace before its first use (zero-filled memory also qualifies).  Every
+ * later call leaves the counters zero again.  Uses a fill kernel, not a memset. */
 moe_status moe_workspace_init(const moe_ctx* ctx, void* ws, size_t ws_bytes,
                               moe_stream_t stream);
 
-/* Copy one layer's pointer table: host_table[e] (HOST array of E entries, in
- * logical expert order) gives expert e's three blobs.  The copy is
- * stream-ordered (host to device); only pointers are copied, so the blobs must
- * outlive the table entries.  A remap to other physical slots is another call;
- * results depend only on the logical ids, never on where the bytes are. */
+/* Set one layer's pointer table (page "GLM-5.3-Flash EXL3 3.05bpw on 1x RTX PRO
+ * 6000 - GPU expert cache, host-RAM streaming", field config.expert_cache.mechanism:
+ * per-layer gate, up and down pointer tables rewritten in place): host_table[e]
+ * (HOST array of E entries, logical expert order) gives expert e's three blobs.
+ * The entries reach the device as arguments of a stream-ordered kernel (up to
+ * 128 entries per launch): the host array may be reused as soon as the call
+ * returns, the call does not wait for the device, and a captured HIP graph keeps
+ * its own copy of the entries.  Only pointers are set, so the blobs must outlive
+ * their table entries.  A remap to other physical slots is another call; results
+ * depend only on the logical ids, never on where the bytes are (page
+ * "0xSero/glm53-flash-offload", paragraph "Elastic CLOCK expert cache").
+ * MOE_E_ARG for a null or misaligned blob (checked on the host first). */
 moe_status set_expert_table(moe_ctx* ctx, int32_t layer, const moe_expert_ref* host_table,
                             moe_stream_t stream);
 
 /* Device address of a layer's table (E entries of moe_expert_ref, logical
- * order), for in-place rewrites by device code.  NULL on a bad layer. */
+ * order), for in-place rewrites by device code (the cache manager of the RTX PRO
+ * 6000 page rewrites the tables on the device, field
+ * config.expert_cache.mechanism).  The context owns the table; writes must be
+ * stream-ordered before the moe_forward calls that read them.  NULL on a bad
+ * layer. */
 void* moe_expert_table_device(moe_ctx* ctx, int32_t layer);
 
 /* Set a layer's shared expert (row-major bfloat16 gate [Is][H], up [Is][H],
- * down [H][Is]); NULLs clear it.  Only pointers are kept. */
+ * down [H][Is]), the always-on expert beside the routed ones (page
+ * "0xSero/glm53-flash-offload", paragraph "Decode kernels (fast mode)"); NULLs
+ * clear it.  Only pointers are kept; host-side call, no device work. */
 moe_status moe_set_shared(moe_ctx* ctx, int32_t layer, const void* gate, const void* up,
                           const void* down);
 
-/* Route T tokens.
+/* Route T tokens: top-K of E experts per token and the grouping of the picks by
+ * expert (pages "GLM-5.3-Flash EXL3 3.05bpw on 1x RTX 3090 -- RAM/NVMe expert
+ * tiering", field summary; "0xSero/glm53-flash-offload", paragraphs "Elastic
+ * CLOCK expert cache" and "Batched decode": the picks deduplicated into the
+ * layer's expert union with each expert's tokens).  The pages do not print the
+ * router function; it is read as a softmax over the logits below, renormalised
+ * over the picks.
  *   x_bf16    [T][H] bfloat16 activations
  *   w_router  [E][H] fp32 router matrix; bias [E] fp32 or NULL
  *   logits l[t][e] = sum_h x[t][h] * w_router[e][h] + bias[e], accumulated in fp64
@@ -147,9 +175,13 @@ moe_status moe_route(moe_ctx* ctx, const void* x_bf16, int32_t T, const float* w
                      int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pair_pos,
                      void* ws, size_t ws_bytes, moe_stream_t stream);
 
-/* Expert FFNs and combine for one layer, given routing (topk_ids, topk_w,
- * expert_offsets, sorted_pairs from moe_route, or from the caller in the same
- * layout; pair_pos is not needed here).
+/* Expert FFNs and combine for one layer (page "GLM-5.3-Flash EXL3 3.05bpw on 1x
+ * RTX PRO 6000 - GPU expert cache, host-RAM streaming", field
+ * config.expert_cache.mechanism: each expert's gate, up and down reached through
+ * the layer's tables; page "0xSero/glm53-flash-offload", paragraph "Decode
+ * kernels (fast mode)": the shared expert beside the routed ones), given routing
+ * (topk_ids, topk_w, expert_offsets, sorted_pairs from moe_route, or from the
+ * caller in the same layout; pair_pos is not needed here).
  *   out       [T][H] fp32: out[t] = sum_{k=0..K-1} topk_w[t][k] * y(t,k) (k
  *             ascending, no atomics, bit-reproducible) + shared(x_t) if set
  *   pair_out  [T*K][H] fp32 or NULL: row t*K + k is the unweighted expert output
@@ -157,22 +189,32 @@ moe_status moe_route(moe_ctx* ctx, const void* x_bf16, int32_t T, const float* w
  *   y(t,k) = down . (silu(gate . x_t) * (up . x_t)) of expert topk_ids[t][k],
  *   accumulated in fp32 from exact integer codes and bf16 activations with the
  *   group scale applied per group.
- * Caller-supplied routing must be consistent (offsets and sorted_pairs from the
- * same ids); a pair whose id is outside [0, E) must be left out of the grouping
- * and then contributes nothing.  Returns MOE_E_STATE if the layer's table was
- * never set. */
+ * A pair whose id is outside [0, E) must be left out of the grouping and then
+ * contributes nothing.  The routing is checked on the device, in the call's own
+ * kernels (the host never waits): offsets[0] == 0, offsets non-decreasing,
+ * offsets[E] equal to the number of pairs with an id in [0, E), and each grouped
+ * position i < offsets[E] holding a pair p in [0, T*K) whose id e has
+ * offsets[e] <= i < offsets[e+1], ascending within an expert.  Inconsistent
+ * routing makes the call write neither out nor pair_out and set MOE_ERR_ROUTING
+ * in the workspace's error word; every read stays inside the buffers' documented
+ * extents ([T][K] ids, [E+1] offsets, [T*K] sorted pairs) whatever their values.
+ * Returns MOE_E_STATE if the layer's table was never set. */
 moe_status moe_forward(moe_ctx* ctx, int32_t layer, const void* x_bf16, int32_t T,
                        const int32_t* topk_ids, const float* topk_w,
                        const int32_t* expert_offsets, const int32_t* sorted_pairs, float* out,
                        float* pair_out, void* ws, size_t ws_bytes, moe_stream_t stream);
 
-/* Stack glue between layers: y_bf16[t] = bf16(x[t] / sqrt(mean(x[t]^2) + eps))
+/* Stack glue between the MoE layers of a stack (42 of them in the pages' model;
+ * page "GLM-5.3-Flash EXL3 2.05bpw on 2x RTX 5090 - TabbyAPI hot-expert swaps,
+ * 262K ctx, vision": MoE layers 3-44; the norm itself is not on the pages, it is
+ * read as a unit-gain RMSNorm): y_bf16[t] = bf16(x[t] / sqrt(mean(x[t]^2) + eps))
  * (unit gain, round to nearest even) for fp32 x [T][H]; and, if resid is not
  * NULL, resid[t][h] += add[t][h] first (fp32), normalising the updated resid. */
 moe_status moe_rmsnorm_bf16(const moe_ctx* ctx, float* resid, const float* add, int32_t T,
                             float eps, void* y_bf16, moe_stream_t stream);
 
-/* Kernel timing.  While enabled (process-wide), every kernel the library
+/* Kernel timing (measurement aid, not part of the layer).  While enabled
+ * (process-wide), every kernel the library
  * launches carries two HIP events that the launch timestamps at the kernel's
  * start and end (the kernel's own duration, without the dispatch latency).
  * moe_profile_read waits for the recorded events, writes up to max_kernels

@@ -33,6 +33,10 @@ def _load():
             raise RuntimeError(f"{path} is missing: run __graft_entry__.build() first")
         lib = ctypes.CDLL(path)
         vp, i32 = ctypes.c_void_p, ctypes.c_int
+        lib.orc_set_threads.restype = None
+        lib.orc_set_threads.argtypes = [i32]
+        lib.orc_max_threads.restype = i32
+        lib.orc_max_threads.argtypes = []
         lib.orc_bf16_to_double.restype = ctypes.c_double
         lib.orc_bf16_to_double.argtypes = [ctypes.c_uint16]
         lib.orc_f16_to_double.restype = ctypes.c_double
@@ -77,6 +81,15 @@ def _p(a):
 
 def _c(a, dt):
     return np.ascontiguousarray(a, dtype=dt)
+
+
+# ------------------------------------------------------------------ threads
+def set_threads(n: int):
+    _load().orc_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return _load().orc_max_threads()
 
 
 # ------------------------------------------------------------------ scalars

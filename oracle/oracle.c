@@ -44,10 +44,17 @@
  *                              P >= 60, m = P-60: bit b of c = bit 16h of w[3m+b].
  */
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* ------------------------------------------------------------ threads */
+/* OpenMP threads of the oracle's parallel loops (the CPU baseline is timed at the
+ * host's full thread count and at one thread). */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int orc_max_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------ scalar types */
 double orc_bf16_to_double(uint16_t b) {
