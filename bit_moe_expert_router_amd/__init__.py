@@ -39,8 +39,8 @@ class moe_expert_ref(ctypes.Structure):
 
 EXPORTS = ("moe_create", "moe_destroy", "moe_workspace_bytes", "moe_workspace_init",
            "set_expert_table", "moe_expert_table_device", "moe_set_shared", "moe_route",
-           "moe_forward", "moe_rmsnorm_bf16", "moe_last_error", "moe_profile_enable",
-           "moe_profile_read")
+           "moe_forward", "moe_forward_noalloc", "moe_rmsnorm_bf16", "moe_last_error",
+           "moe_profile_enable", "moe_profile_read")
 
 
 def _load():
@@ -60,6 +60,7 @@ def _load():
     lib.moe_route.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.moe_forward.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp,
                                 ctypes.c_size_t, vp]
+    lib.moe_forward_noalloc.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_rmsnorm_bf16.argtypes = [vp, vp, vp, i32, ctypes.c_float, vp, vp]
     lib.moe_last_error.restype = ctypes.c_char_p
     lib.moe_profile_enable.argtypes = [i32]
@@ -68,7 +69,8 @@ def _load():
                                      ctypes.POINTER(ctypes.c_int64)]
     lib.moe_profile_read.restype = i32
     for f in ("moe_create", "moe_destroy", "moe_workspace_init", "set_expert_table",
-              "moe_set_shared", "moe_route", "moe_forward", "moe_rmsnorm_bf16"):
+              "moe_set_shared", "moe_route", "moe_forward", "moe_forward_noalloc",
+              "moe_rmsnorm_bf16"):
         getattr(lib, f).restype = st
     return lib
 
@@ -157,6 +159,14 @@ def moe_forward(ctx: int, layer: int, x_bf16, T: int, topk_ids, topk_w, expert_o
                            _ptr(pair_out), _ptr(ws), ws.numel() * ws.element_size(),
                            _stream(stream)),
            "moe_forward")
+
+
+def moe_forward_noalloc(ctx: int, layer: int, x_bf16, T: int, topk_ids, topk_w,
+                        expert_offsets, sorted_pairs, out, pair_out, stream=None):
+    _check(lib.moe_forward_noalloc(ctx, layer, _ptr(x_bf16), T, _ptr(topk_ids), _ptr(topk_w),
+                                   _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(out),
+                                   _ptr(pair_out), _stream(stream)),
+           "moe_forward_noalloc")
 
 
 def moe_last_error() -> str:

@@ -4,10 +4,26 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <vector>
 
 #include "common.h"
+
+// Scratch of moe_forward_noalloc: the workspace of callers that cannot allocate,
+// in the library's own device memory (each GPU the library runs on holds one copy
+// until the process ends).  Host code never passes this name to a kernel or a
+// copy: it is a host-side stand-in, not a device address.  moe_create looks up
+// the device address once per device (hipGetSymbolAddress, with that device
+// current) and keeps it in s_scratch_dev; only that address is used.
+constexpr size_t kNoAllocBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex s_scratch_mu;
+void* s_scratch_dev[kMaxDevices];  // per device: scratch's device address, or null
+}  // namespace
 
 
 struct moe_ctx {
@@ -19,6 +35,7 @@ struct moe_ctx {
     const void *g, *u, *d;
   };
   std::vector<Shared> shared;     // per layer
+  uint8_t* scratch = nullptr;     // this device's copy of the no-allocation scratch
   // the shared expert runs on a second stream (default priority) between a fork
   // event recorded on the caller's stream and a join event the combine waits for
   hipStream_t side = nullptr;
@@ -92,6 +109,25 @@ moe_status moe_create(const moe_cfg* cfg, int32_t n_layers, moe_ctx** out) {
   if (hipMalloc(&c->d_tables, tb) != hipSuccess) {
     delete c;
     return fail(MOE_E_NOMEM, "moe_create: device tables (%zu bytes)", tb);
+  }
+  {  // the no-allocation scratch of this device: its address, and zero counters
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    std::lock_guard<std::mutex> lk(s_scratch_mu);
+    if (e == hipSuccess && dev >= 0 && dev < kMaxDevices && !s_scratch_dev[dev]) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e == hipSuccess) e = moe::launch_zero_i32((int32_t*)p, moe::kCounters, nullptr);
+      if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+      if (e == hipSuccess) s_scratch_dev[dev] = p;
+    }
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+      (void)hipFree(c->d_tables);
+      delete c;
+      return fail(MOE_E_HIP, "moe_create: device scratch lookup: %s",
+                  e != hipSuccess ? hipGetErrorString(e) : "device id out of range");
+    }
+    c->scratch = (uint8_t*)s_scratch_dev[dev];
   }
   if (cfg->shared_inter > 0 &&
       (hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess ||
@@ -198,28 +234,62 @@ moe_status moe_route(moe_ctx* ctx, const void* x_bf16, int32_t T, const float* w
   return hip_status(e, "moe_route launch");
 }
 
-moe_status moe_forward(moe_ctx* ctx, int32_t layer, const void* x_bf16, int32_t T,
-                       const int32_t* topk_ids, const float* topk_w,
-                       const int32_t* expert_offsets, const int32_t* sorted_pairs, float* out,
-                       float* pair_out, void* ws, size_t ws_bytes, moe_stream_t stream) {
-  if (!ctx) return fail(MOE_E_ARG, "moe_forward: null context");
+}  // extern "C"
+
+namespace {
+
+moe_status forward_impl(const char* who, moe_ctx* ctx, int32_t layer, const void* x_bf16,
+                        int32_t T, const int32_t* topk_ids, const float* topk_w,
+                        const int32_t* expert_offsets, const int32_t* sorted_pairs, float* out,
+                        float* pair_out, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  if (!ctx) return fail(MOE_E_ARG, "%s: null context", who);
   const moe_cfg& c = ctx->cfg;
-  if (layer < 0 || layer >= ctx->n_layers) return fail(MOE_E_ARG, "moe_forward: bad layer %d", layer);
-  if (T < 0 || T > c.max_tokens) return fail(MOE_E_ARG, "moe_forward: T=%d outside [0, %d]", T, c.max_tokens);
-  if (!ctx->table_set[layer]) return fail(MOE_E_STATE, "moe_forward: expert table of layer %d never set", layer);
+  if (layer < 0 || layer >= ctx->n_layers) return fail(MOE_E_ARG, "%s: bad layer %d", who, layer);
+  if (T < 0 || T > c.max_tokens) return fail(MOE_E_ARG, "%s: T=%d outside [0, %d]", who, T, c.max_tokens);
+  if (!ctx->table_set[layer]) return fail(MOE_E_STATE, "%s: expert table of layer %d never set", who, layer);
   if (T == 0) return ok();
   if (!x_bf16 || !topk_ids || !topk_w || !expert_offsets || !sorted_pairs || !out || !ws)
-    return fail(MOE_E_ARG, "moe_forward: null pointer argument");
+    return fail(MOE_E_ARG, "%s: null pointer argument", who);
   if (!aligned(x_bf16, 16) || !aligned(out, 16) || !aligned(ws, 256) || (pair_out && !aligned(pair_out, 16)))
-    return fail(MOE_E_ARG, "moe_forward: x, out, pair_out must be 16-byte aligned, ws 256-byte aligned");
+    return fail(MOE_E_ARG, "%s: x, out, pair_out must be 16-byte aligned, ws 256-byte aligned", who);
   const moe::WsLayout L = moe::ws_layout(c, T);
   if (ws_bytes < (size_t)L.total)
-    return fail(MOE_E_ARG, "moe_forward: workspace %zu bytes < %lld needed", ws_bytes, (long long)L.total);
+    return fail(MOE_E_ARG, "%s: workspace %zu bytes < %lld needed", who, ws_bytes, (long long)L.total);
   const moe_ctx::Shared& sh = ctx->shared[layer];
   moe::FwdArgs f{&c, ctx->d_tables + (size_t)layer * c.n_experts, sh.g, sh.u, sh.d,
                  (const uint16_t*)x_bf16, T, topk_ids, topk_w, expert_offsets, sorted_pairs,
                  out, pair_out, (uint8_t*)ws, ctx->side, ctx->ev_fork, ctx->ev_join};
-  return hip_status(moe::launch_forward(f, (hipStream_t)stream), "moe_forward launch");
+  return hip_status(moe::launch_forward(f, (hipStream_t)stream), who);
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(moe_ctx* ctx, int32_t layer, const void* x_bf16, int32_t T,
+                       const int32_t* topk_ids, const float* topk_w,
+                       const int32_t* expert_offsets, const int32_t* sorted_pairs, float* out,
+                       float* pair_out, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  return forward_impl("moe_forward", ctx, layer, x_bf16, T, topk_ids, topk_w, expert_offsets,
+                      sorted_pairs, out, pair_out, ws, ws_bytes, stream);
+}
+
+moe_status moe_forward_noalloc(moe_ctx* ctx, int32_t layer, const void* x_bf16, int32_t T,
+                               const int32_t* topk_ids, const float* topk_w,
+                               const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                               float* out, float* pair_out, moe_stream_t stream) {
+  if (!ctx) return fail(MOE_E_ARG, "moe_forward_noalloc: null context");
+  if (T > 0 && T <= ctx->cfg.max_tokens) {
+    const int64_t need = moe::ws_layout(ctx->cfg, T).total;
+    if ((size_t)need > kNoAllocBytes)
+      return fail(MOE_E_ARG,
+                  "moe_forward_noalloc: T=%d needs %lld bytes of scratch, more than the "
+                  "library's %zu; use moe_forward with a workspace",
+                  T, (long long)need, kNoAllocBytes);
+  }
+  return forward_impl("moe_forward_noalloc", ctx, layer, x_bf16, T, topk_ids, topk_w,
+                      expert_offsets, sorted_pairs, out, pair_out, ctx->scratch, kNoAllocBytes,
+                      stream);
 }
 
 moe_status moe_rmsnorm_bf16(const moe_ctx* ctx, float* resid, const float* add, int32_t T,

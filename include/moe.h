@@ -204,6 +204,25 @@ moe_status moe_forward(moe_ctx* ctx, int32_t layer, const void* x_bf16, int32_t 
                        const int32_t* expert_offsets, const int32_t* sorted_pairs, float* out,
                        float* pair_out, void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/* moe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels and results, with the workspace taken from a scratch array inside the
+ * library (MOE_NOALLOC_SCRATCH_BYTES of device memory per GPU, held from the
+ * first moe_create on that GPU until the process ends) instead of a caller
+ * buffer.  The call itself allocates nothing.  Arguments, layout and routing
+ * check as moe_forward; MOE_E_ARG (with a message) when T needs more scratch than
+ * the array holds (more than MOE_NOALLOC_SCRATCH_BYTES of workspace: at H = 5120,
+ * I = 1536, K = 8 with a shared expert, batches of up to 15 tokens fit).  Every call on
+ * one GPU, from any context, shares that GPU's array, which keeps the last
+ * call's contents (its counters are left zero): calls that overlap on one GPU,
+ * e.g. on two streams, race and must not be issued.  The array's error word is
+ * not exposed; inconsistent routing still leaves the outputs untouched. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+moe_status moe_forward_noalloc(moe_ctx* ctx, int32_t layer, const void* x_bf16, int32_t T,
+                               const int32_t* topk_ids, const float* topk_w,
+                               const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                               float* out, float* pair_out, moe_stream_t stream);
+
 /* Stack glue between the MoE layers of a stack (42 of them in the pages' model;
  * page "GLM-5.3-Flash EXL3 2.05bpw on 2x RTX 5090 - TabbyAPI hot-expert swaps,
  * 262K ctx, vision": MoE layers 3-44; the norm itself is not on the pages, it is
