@@ -25,7 +25,7 @@
  * Packed weight format (v1).  A matrix W[N][Kd] (N outputs, Kd reduction; N % 64
  * == 0, Kd % G == 0) stores unsigned codes c with W[n][k] = (c - 2^(bits-1)) *
  * s[n][k/G], one 16-bit scale (bf16 or fp16) per row and group of G consecutive
- * reduction elements.  Supported (bits, G): (3, 128) and (4, 32).
+ * reduction elements.  Supported (bits, G): (3, 128), (4, 32), (2, 128), (4, 128).
  *   codes region: tiles t = (n/64)*(Kd/G) + g, one per 64 rows and one group.  A
  *     tile holds 64 units, unit u = row 64*(n/64) + u, each bits*G/8 bytes split
  *     into C = bits*G/128 chunks of 16 bytes; chunk j of tile t starts at byte
@@ -33,7 +33,8 @@
  *     chunk reads 1024 contiguous bytes).  A unit's 32-bit little-endian words
  *     are its chunks' words in order.
  *   code i of a unit (reduction index g*G + i), P = i/2, half h = i%2:
- *     4-bit, G = 32, 4 words:   c = (w[P/4] >> (16h + 4*(P%4))) & 15
+ *     4-bit, G = 32 or 128, 4 or 16 words: c = (w[P/4] >> (16h + 4*(P%4))) & 15
+ *     2-bit, G = 128, 8 words:  c = (w[P/8] >> (16h + 2*(P%8))) & 3
  *     3-bit, G = 128, 12 words: P < 60: c = (w[P/5] >> (16h + off[P%5])) & 7,
  *                               off = {1, 4, 7, 10, 13};
  *                               P >= 60, m = P - 60: bit b of c is bit 16h of
@@ -80,8 +81,8 @@ typedef struct {
   int32_t inter;         /* I, routed expert intermediate size                    */
   int32_t n_experts;     /* E, routed experts per layer (<= 1024)                 */
   int32_t top_k;         /* K (1 <= K <= min(E, 16))                              */
-  int32_t bits;          /* 3 or 4                                                */
-  int32_t group;         /* 128 for 3-bit, 32 for 4-bit                           */
+  int32_t bits;          /* 2, 3 or 4                                             */
+  int32_t group;         /* 128 (2, 3 or 4 bits) or 32 (4 bits)                   */
   int32_t scale_f16;     /* 1: fp16 scales, 0: bf16 scales                        */
   int32_t shared_inter;  /* Is, 0 = no shared expert                              */
   int32_t max_tokens;    /* largest T accepted by moe_route / moe_forward         */

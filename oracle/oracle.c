@@ -38,7 +38,8 @@
  * 32-bit little-endian words are the chunks' words in order.  Scales follow at
  * the next 256-byte boundary as a row-major [N][Kd/G] array.
  * Code i of a unit (reduction index g*G + i), P = i/2, half h = i%2:
- *   4-bit, G = 32 (4 words):   c = (w[P/4] >> (16h + 4*(P%4))) & 15
+ *   4-bit, G = 32 or 128 (4 or 16 words): c = (w[P/4] >> (16h + 4*(P%4))) & 15
+ *   2-bit, G = 128 (8 words):  c = (w[P/8] >> (16h + 2*(P%8))) & 3
  *   3-bit, G = 128 (12 words): P < 60: c = (w[P/5] >> (16h + off[P%5])) & 7 with
  *                              off = {1,4,7,10,13};
  *                              P >= 60, m = P-60: bit b of c = bit 16h of w[3m+b].
@@ -128,6 +129,10 @@ int orc_code(const uint8_t* blob, int rows, int cols, int bits, int group, int n
   if (bits == 4) {
     uint32_t w = orc_unit_word(blob, &m, n, g, P / 4);
     return (int)((w >> (16 * h + 4 * (P % 4))) & 15u);
+  }
+  if (bits == 2) {
+    uint32_t w = orc_unit_word(blob, &m, n, g, P / 8);
+    return (int)((w >> (16 * h + 2 * (P % 8))) & 3u);
   }
   if (bits == 3) {
     static const int off[5] = {1, 4, 7, 10, 13};

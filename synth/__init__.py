@@ -85,6 +85,10 @@ CONFIGS = {
     "c4": MoEConfig("c4", 5120, 1536, 288, 8, 4, 3, 128, False, shared_inter=1536, layers=42,
                     seed=4, remap=True),
     "c5": MoEConfig("c5", 5120, 1536, 288, 8, 8192, 3, 128, False, seed=5),
+    # the same layer with 2-bit and 4-bit codes in groups of 128 (2.125 and 4.125
+    # bits per weight; the 2x RTX 5090 page serves a 2.05 bpw quantisation)
+    "q2": MoEConfig("q2", 5120, 1536, 288, 8, 1, 2, 128, False, seed=6),
+    "q4": MoEConfig("q4", 5120, 1536, 288, 8, 1, 4, 128, False, seed=7),
 }
 
 
@@ -290,13 +294,22 @@ def pack_unit(codes: np.ndarray, bits: int) -> np.ndarray:
     G = codes.shape[-1]
     lead = codes.shape[:-1]
     if bits == 4:
-        if G != 32:
-            raise ValueError("4-bit units hold 32 codes")
-        w = np.zeros(lead + (4,), dtype=np.uint32)
-        for P in range(16):
+        if G not in (32, 128):
+            raise ValueError("4-bit units hold 32 or 128 codes")
+        w = np.zeros(lead + (G // 8,), dtype=np.uint32)
+        for P in range(G // 2):
             d, f = P >> 2, P & 3
             w[..., d] |= (codes[..., 2 * P] & 15) << (4 * f)
             w[..., d] |= (codes[..., 2 * P + 1] & 15) << (16 + 4 * f)
+        return w
+    if bits == 2:
+        if G != 128:
+            raise ValueError("2-bit units hold 128 codes")
+        w = np.zeros(lead + (8,), dtype=np.uint32)
+        for P in range(64):
+            d, f = P >> 3, P & 7
+            w[..., d] |= (codes[..., 2 * P] & 3) << (2 * f)
+            w[..., d] |= (codes[..., 2 * P + 1] & 3) << (16 + 2 * f)
         return w
     if bits == 3:
         if G != 128:

@@ -21,7 +21,10 @@ def _single_unit_matrix(bits, G, word, bit):
     return blob
 
 
-@pytest.mark.parametrize("bits,G", [(3, 128), (4, 32)])
+CODECS = [(3, 128), (4, 32), (2, 128), (4, 128)]
+
+
+@pytest.mark.parametrize("bits,G", CODECS)
 def test_bit_bijection(bits, G):
     nwords = bits * G // 32
     seen = {}
@@ -41,7 +44,7 @@ def test_bit_bijection(bits, G):
     assert len(seen) == G * bits
 
 
-@pytest.mark.parametrize("bits,G", [(3, 128), (4, 32)])
+@pytest.mark.parametrize("bits,G", CODECS)
 def test_pairs_share_offsets_in_halves(bits, G):
     """codes 2P and 2P+1 sit at the same bit offsets of the low and high halves
     of the same word(s)"""
@@ -61,7 +64,8 @@ def test_pairs_share_offsets_in_halves(bits, G):
             assert w0 == w1 and b0 < 16 and b1 == b0 + 16
 
 
-@pytest.mark.parametrize("bits,G,N,Kd", [(3, 128, 128, 512), (4, 32, 192, 96)])
+@pytest.mark.parametrize("bits,G,N,Kd", [(3, 128, 128, 512), (4, 32, 192, 96),
+                                         (2, 128, 128, 384), (4, 128, 64, 256)])
 def test_packer_roundtrip_and_tiles(bits, G, N, Kd):
     rng = np.random.default_rng(7)
     codes = rng.integers(0, 1 << bits, size=(N, Kd))

@@ -64,7 +64,8 @@ class DenseLayer:
 
 
 @pytest.mark.parametrize("bits,G,f16,shared", [(4, 32, True, 0), (3, 128, False, 0),
-                                               (3, 128, False, 128)])
+                                               (3, 128, False, 128), (2, 128, False, 0),
+                                               (4, 128, False, 0)])
 def test_layer_equals_dense_gating(bits, G, f16, shared):
     H, I, E, K, T = 256, 128, 16, 2, 6
     L = DenseLayer(H, I, E, bits, G, f16, seed=11 + bits, shared_inter=shared)
