@@ -58,8 +58,14 @@ WORKLOADS = {
                      "Zipf(1.1) bias"),
     "c5u": ("c5", {"zipf": False}, "8,192-token prefill chunk through one GLM-shaped MoE layer "
                                    "(3-bit G128), uniform routing (no bias)"),
+    "q2": ("q2", {}, "the GLM-shaped layer at decode batch 1 with 2-bit codes in groups of 128 "
+                     "(2.125 bits per weight), Zipf(1.1) bias"),
+    "q2b8": ("q2", {"tokens": 8}, "the 2-bit layer at decode batch 8"),
+    "q4": ("q4", {}, "the GLM-shaped layer at decode batch 1 with 4-bit codes in groups of 128 "
+                     "(4.125 bits per weight), Zipf(1.1) bias"),
+    "q4b8": ("q4", {"tokens": 8}, "the 4-bit layer at decode batch 8"),
 }
-DEFAULT_EXTRA = "c2b2,c2b4,c2b8,c3,c4,c5,c5u"
+DEFAULT_EXTRA = "c2b2,c2b4,c2b8,c3,c4,c5,c5u,q2,q2b8,q4,q4b8"
 
 
 def parse():

@@ -69,8 +69,9 @@ moe_status hip_status(hipError_t e, const char* what) {
 moe_status check_cfg(const moe_cfg& c) {
   if (c.hidden <= 0 || c.inter <= 0 || c.n_experts <= 0 || c.top_k <= 0 || c.max_tokens <= 0)
     return fail(MOE_E_ARG, "cfg: sizes must be positive");
-  if (!((c.bits == 3 && c.group == 128) || (c.bits == 4 && c.group == 32)))
-    return fail(MOE_E_UNSUPPORTED, "cfg: (bits, group) = (%d, %d) unsupported; use (3,128) or (4,32)",
+  if (moe::codec_of(c.bits, c.group) < 0)
+    return fail(MOE_E_UNSUPPORTED,
+                "cfg: (bits, group) = (%d, %d) unsupported; use (3,128), (4,32), (2,128) or (4,128)",
                 c.bits, c.group);
   if (c.hidden % 64 || c.inter % 64 || c.hidden % c.group || c.inter % c.group)
     return fail(MOE_E_UNSUPPORTED, "cfg: hidden and inter must be multiples of 64 and of the group");

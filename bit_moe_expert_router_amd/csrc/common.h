@@ -76,6 +76,19 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// ---------------------------------------------------------------- codecs
+// The kernels are instantiated per codec (the template argument CODEC): 3-bit
+// codes in groups of 128, 4-bit in groups of 32, 2-bit in groups of 128 and 4-bit
+// in groups of 128.
+constexpr int kQ3G128 = 3, kQ4G32 = 4, kQ2G128 = 2, kQ4G128 = 5;
+__host__ inline int codec_of(int bits, int group) {
+  if (bits == 3 && group == 128) return kQ3G128;
+  if (bits == 4 && group == 32) return kQ4G32;
+  if (bits == 2 && group == 128) return kQ2G128;
+  if (bits == 4 && group == 128) return kQ4G128;
+  return -1;
+}
+
 // ---------------------------------------------------------------- unit decode
 // A unit (one row, one group of G codes) is decoded into G/2 registers, each a
 // pair of bfloat16 values (B + c_{2P}, B + c_{2P+1}) for a per-pair constant B:
@@ -89,12 +102,12 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 //   sum_k (q_k + off_k) x_k,  off_k = B_k + 2^(bits-1),
 // and the kernels subtract the per-group constant sum_k off_k x_k, computed once
 // per activation vector and group.
-template <int BITS>
+template <int CODEC>
 struct UnitCodec;
 
 template <>
-struct UnitCodec<3> {
-  static constexpr int G = 128, WORDS = 12, CHUNKS = 3, PAIRS = 64;
+struct UnitCodec<kQ3G128> {
+  static constexpr int BITS = 3, G = 128, WORDS = 12, CHUNKS = 3, PAIRS = 64;
   // offset of pair P: fields 0 and 2 of a word use B = 64, fields 1, 3, 4 use
   // B = 8, pairs 60..63 (the spare bits) use B = 128; zero point 4.
   __host__ __device__ static constexpr float pair_off(int P) {
@@ -148,15 +161,17 @@ struct UnitCodec<3> {
   }
 };
 
-template <>
-struct UnitCodec<4> {
-  static constexpr int G = 32, WORDS = 4, CHUNKS = 1, PAIRS = 16;
+// 4-bit codes, groups of G4 (32 or 128): word d holds pairs 4d .. 4d+3 at bit
+// offsets 0, 4, 8, 12 of both halves; B = 128 (0x4300), zero point 8.
+template <int G4>
+struct UnitCodec4 {
+  static constexpr int BITS = 4, G = G4, WORDS = G4 / 8, CHUNKS = G4 / 32, PAIRS = G4 / 2;
   __host__ __device__ static constexpr float pair_off(int) { return 136.f; }  // B 128, zero 8
   template <class F>
   __device__ __forceinline__ static void for_each_pair(const uint32_t (&w)[WORDS], F&& f) {
     const uint32_t m128 = in_vgpr(0x43004300u);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
+    for (int d = 0; d < WORDS; ++d) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) f(4 * d + k, ((w[d] >> (4 * k)) & 0x000F000Fu) | m128);
     }
@@ -164,10 +179,46 @@ struct UnitCodec<4> {
   __device__ __forceinline__ static void decode(const uint32_t (&w)[WORDS], uint32_t (&p)[PAIRS]) {
     const uint32_t m128 = in_vgpr(0x43004300u);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
+    for (int d = 0; d < WORDS; ++d) {
 #pragma unroll
       for (int f = 0; f < 4; ++f) p[4 * d + f] = ((w[d] >> (4 * f)) & 0x000F000Fu) | m128;
     }
+  }
+};
+template <>
+struct UnitCodec<kQ4G32> : UnitCodec4<32> {};
+template <>
+struct UnitCodec<kQ4G128> : UnitCodec4<128> {};
+
+// 2-bit codes, groups of 128: word d holds pairs 8d .. 8d+7 at bit offsets 2k of
+// both halves.  Fields at bits 0-1, 2-3, 4-5 of a half take the exponent
+// patterns 0x4300 (128 + c), 0x4200 (32 + c), 0x4100 (8 + c); the word shifted by
+// 6 and by 12 brings the other fields to those positions.  Zero point 2.
+template <>
+struct UnitCodec<kQ2G128> {
+  static constexpr int BITS = 2, G = 128, WORDS = 8, CHUNKS = 2, PAIRS = 64;
+  __host__ __device__ static constexpr float pair_off(int P) {
+    return (P % 8) % 3 == 0 ? 130.f : ((P % 8) % 3 == 1 ? 34.f : 10.f);
+  }
+  template <class F>
+  __device__ __forceinline__ static void for_each_pair(const uint32_t (&w)[WORDS], F&& f) {
+    const uint32_t m128 = in_vgpr(0x43004300u), m32 = in_vgpr(0x42004200u),
+                   m8 = in_vgpr(0x41004100u);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const uint32_t v = w[d], t = v >> 6, u = v >> 12;
+      f(8 * d + 0, (v & 0x00030003u) | m128);
+      f(8 * d + 1, (v & 0x000C000Cu) | m32);
+      f(8 * d + 2, (v & 0x00300030u) | m8);
+      f(8 * d + 3, (t & 0x00030003u) | m128);
+      f(8 * d + 4, (t & 0x000C000Cu) | m32);
+      f(8 * d + 5, (t & 0x00300030u) | m8);
+      f(8 * d + 6, (u & 0x00030003u) | m128);
+      f(8 * d + 7, (u & 0x000C000Cu) | m32);
+    }
+  }
+  __device__ __forceinline__ static void decode(const uint32_t (&w)[WORDS], uint32_t (&p)[PAIRS]) {
+    for_each_pair(w, [&](int P, uint32_t v) { p[P] = v; });
   }
 };
 
@@ -184,10 +235,10 @@ __device__ __forceinline__ uint16_t scale_from_dword(uint32_t w, int64_t idx) {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <int BITS>
+template <int CODEC>
 __device__ __forceinline__ void load_unit4(gbytes_t codes, int64_t tile, int lane,
-                                           u32x4 (&w)[UnitCodec<BITS>::CHUNKS]) {
-  using C = UnitCodec<BITS>;
+                                           u32x4 (&w)[UnitCodec<CODEC>::CHUNKS]) {
+  using C = UnitCodec<CODEC>;
   typedef const u32x4 __attribute__((address_space(1)))* gu4_t;
 #pragma unroll
   for (int j = 0; j < C::CHUNKS; ++j)
@@ -197,18 +248,18 @@ __device__ __forceinline__ void load_unit4(gbytes_t codes, int64_t tile, int lan
 // The unit's words, passed through an empty asm so that the decode that follows
 // stays inside the token loop (hoisting every group's decoded pairs out of it
 // would need GPW * 128 registers).
-template <int BITS>
-__device__ __forceinline__ void unit_words(const u32x4 (&c)[UnitCodec<BITS>::CHUNKS],
-                                           uint32_t (&w)[UnitCodec<BITS>::WORDS]) {
+template <int CODEC>
+__device__ __forceinline__ void unit_words(const u32x4 (&c)[UnitCodec<CODEC>::CHUNKS],
+                                           uint32_t (&w)[UnitCodec<CODEC>::WORDS]) {
 #pragma unroll
-  for (int j = 0; j < UnitCodec<BITS>::CHUNKS; ++j) {
+  for (int j = 0; j < UnitCodec<CODEC>::CHUNKS; ++j) {
     w[4 * j + 0] = c[j].x;
     w[4 * j + 1] = c[j].y;
     w[4 * j + 2] = c[j].z;
     w[4 * j + 3] = c[j].w;
   }
 #pragma unroll
-  for (int k = 0; k < UnitCodec<BITS>::WORDS; ++k) asm volatile("" : "+v"(w[k]));
+  for (int k = 0; k < UnitCodec<CODEC>::WORDS; ++k) asm volatile("" : "+v"(w[k]));
 }
 
 // Sum over the 64 lanes in a fixed order (row prefix sums by DPP, then the row
@@ -217,7 +268,7 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_shift(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
-template <int BITS>
+template <int CODEC>
 __device__ __forceinline__ float wave_sum_uniform(float v) {
   v += dpp_shift<0x111>(v);  // row_shr:1
   v += dpp_shift<0x112>(v);  // row_shr:2

@@ -1,0 +1,1051 @@
+// decode_impl.h -- the routed experts of a decode batch (at most 64 tokens) as
+// persistent, wave-level GEMVs over packed low-bit weights.  The kernels and the
+// per-codec launcher are templates; decode.hip, decode_q2.hip and decode_q4.hip
+// instantiate them, one codec family per source, so the builds run in parallel.
+//
+// Each picked expert runs gate, up and down matrices reached through the layer's
+// pointer table (page "GLM-5.3-Flash EXL3 3.05bpw on 1x RTX PRO 6000 - GPU expert
+// cache, host-RAM streaming", field config.expert_cache.mechanism); a decode step
+// reads every picked expert's bytes once, so HBM bandwidth bounds it.
+//
+// Work decomposition.  A plan kernel lists the active experts (those owning at
+// least one pair) with their pair segment and blob pointers.  The GEMV kernels
+// then run a fixed grid of waves that take work items in a zig-zag order: an
+// item is (active expert, 64-row strip, matrix, chunk of GPW reduction groups).
+// A wave requests the item's codes and scales first (one 16-byte load per chunk
+// of a 64-row tile: 1,024 contiguous bytes per wave), then forms the partial
+// products of its 64 rows for up to XT of the expert's tokens at a time and
+// writes them to a partial buffer, one slice per chunk.  The codec's offset sums
+// of each activation row and group come precomputed (the plan launch for gate/up,
+// the SwiGLU pass for down).  The activations reach the dot products through scalar loads (one load
+// of 8 pairs serves all 64 lanes); a broadcast through LDS or a vector load would
+// move every byte 64 times, which made items with several tokens LDS-bound.  No
+// item waits on another: there are no block barriers
+// and no cross-wave reductions, and a wave that finishes an item starts the
+// next one at once, so the weight stream stays in flight.  The slices are added
+// in chunk order by the SwiGLU pass (gate/up) and by the combine (down): results
+// are deterministic.
+//
+// Arithmetic (as in the unit codec): codes are expanded two at a time into bf16
+// (B + c) and multiplied with bf16 activation pairs by v_dot2_f32_bf16 in fp32; the
+// per-group constant sum_k (B_k + z) x_k is subtracted, then the group scale
+// applied.  The down matrix takes h as bf16 hi + bf16 remainder (two products per
+// code pair).
+#pragma once
+#include <algorithm>
+
+#include "common.h"
+
+namespace moe {
+
+MOE_TRACE_DECL
+
+typedef uint32_t u32x4d __attribute__((ext_vector_type(4)));
+
+struct ActEntry {
+  int32_t e, seg0, n, pad;
+  const void* ptr[3];  // gate, up, down
+};
+
+// ---------------------------------------------------------------- plan
+// act_hdr[0] = U, the number of experts owning at least one pair; act[a] for
+// a < U lists them by descending pair count (count clamped at 63), ties by
+// ascending expert id, so that the GEMVs' zig-zag item order gives every wave a
+// similar mix of heavy and light items.  The order only schedules work: where
+// an item's results land depends on the item alone.
+constexpr int kPlanKeys = 65;  // 0..63: 63 - min(n, 63) for active experts; 64: inactive
+
+// Blocks 1.. of the same launch form, for every token t and reduction group g of
+// the gate/up matrices, the codec's offset sum osx[t][g] = sum_P off_P (x_2P +
+// x_2P+1) (one wave per (t, g), lane = pair, the fixed-order wave sum), which the
+// gate/up GEMV subtracts per group instead of reducing it in every work item;
+// block 0 checks the routing (thread i: expert i and grouped position i; P, E <=
+// 1024) and builds the list, or, for inconsistent routing, an empty one.
+template <int CODEC>
+__global__ __launch_bounds__(1024) void k_plan_decode(const int32_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ ids,
+                                                      const int32_t* __restrict__ sorted_pairs,
+                                                      int P, int32_t* __restrict__ ctr,
+                                                      const moe_expert_ref* __restrict__ table,
+                                                      int E, int32_t* __restrict__ act_hdr,
+                                                      ActEntry* __restrict__ act,
+                                                      const uint16_t* __restrict__ x, int T, int H,
+                                                      float* __restrict__ osx) {
+  using C = UnitCodec<CODEC>;
+  __shared__ int cntw[16][kPlanKeys];  // per wave and key: experts (then the exclusive prefix over waves)
+  __shared__ int base[kPlanKeys];      // exclusive prefix over keys of the totals
+  __shared__ int s_off[1025];
+  __shared__ int s_id[1024];
+  const int e = threadIdx.x, lane = e & 63, wv = e >> 6;
+  if (blockIdx.x > 0) {  // blocks 1.. : one (t, g) item per wave
+    const int ngx = H / C::G;
+    const int it = (blockIdx.x - 1) * 16 + wv;
+    if (it < T * ngx) {
+      const int t = it / ngx, g = it - t * ngx;
+      const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
+      const float off = lane < C::PAIRS ? C::pair_off(lane) : 0.f;
+      const uint32_t pr = lane < C::PAIRS ? x32[((int64_t)t * H + g * C::G) / 2 + lane] : 0u;
+      const float v = wave_sum_uniform<CODEC>(off * (bf16_to_f32((uint16_t)pr) +
+                                                    bf16_to_f32((uint16_t)(pr >> 16))));
+      if (lane == 0) osx[it] = v;
+    }
+    return;
+  }
+  for (int i = e; i < 16 * kPlanKeys; i += 1024) (&cntw[0][0])[i] = 0;
+  const int lo = e < E ? offsets[e] : 0;
+  const int hi = e < E ? offsets[e + 1] : 0;
+  // the routing check (as routing_ok_wave, one thread per expert and position)
+  const int idv = e < P ? ids[e] : -1;
+  const int sp_i = e < P ? sorted_pairs[e] : 0;
+  const int sp_prev = (e > 0 && e < P) ? sorted_pairs[e - 1] : -1;
+  if (e < E) s_off[e] = lo;
+  if (e == E - 1) s_off[E] = hi;
+  if (e < P) s_id[e] = idv;
+  const int nvalid = __syncthreads_count(idv >= 0 && idv < E);
+  const int oE = s_off[E];
+  bool bad = (e < E && hi < lo) || (e == 0 && (lo != 0 || oE != nvalid));
+  if (e < oE && oE <= P) {
+    const bool pin = sp_i >= 0 && sp_i < P;
+    const int ep = pin ? s_id[sp_i] : -1;
+    const bool ein = ep >= 0 && ep < E;
+    const int elo = ein ? s_off[ep] : 0, ehi = ein ? s_off[ep + 1] : 0;
+    bad |= !ein || e < elo || e >= ehi || (e > elo && sp_prev >= sp_i);
+  }
+  if (__syncthreads_or(bad)) {  // nothing runs, the outputs are left untouched
+    if (e == 0) {
+      act_hdr[0] = 0;
+      record_routing(ctr, false);
+    }
+    return;
+  }
+  if (e == 0) record_routing(ctr, true);
+  const int n = hi - lo;
+  const int key = n > 0 ? 63 - min(n, 63) : 64;
+  // lanes of this wave with the same key (one ballot per key bit)
+  uint64_t eq = __ballot(1);
+#pragma unroll
+  for (int b = 0; b < 7; ++b) {
+    const uint64_t bal = __ballot((key >> b) & 1);
+    eq &= ((key >> b) & 1) ? bal : ~bal;
+  }
+  const uint64_t lt = (1ull << lane) - 1ull;
+  const int below = __popcll(eq & lt);
+  __syncthreads();
+  if (below == 0) cntw[wv][key] = __popcll(eq);
+  __syncthreads();
+  if (e < kPlanKeys) {  // thread k: prefix of key k over the waves, and its total
+    int run = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int c = cntw[w][e];
+      cntw[w][e] = run;
+      run += c;
+    }
+    base[e] = run;
+  }
+  __syncthreads();
+  if (e == 0) {  // exclusive prefix over the keys (65 entries)
+    int run = 0;
+    for (int k = 0; k < kPlanKeys; ++k) {
+      const int c = base[k];
+      base[k] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  if (n > 0) {
+    const int a = base[key] + cntw[wv][key] + below;
+    const moe_expert_ref r = table[e];
+    ActEntry ent;
+    ent.e = e;
+    ent.seg0 = lo;
+    ent.n = n;
+    ent.pad = 0;
+    ent.ptr[0] = r.gate;
+    ent.ptr[1] = r.up;
+    ent.ptr[2] = r.down;
+    act[a] = ent;
+  }
+  if (e == 0) act_hdr[0] = base[64];
+}
+
+// ---------------------------------------------------------------- GEMV
+// MODE 0: gate and up (R = I rows, reduction D = H); activations are the bf16
+// token rows xa[T][H]; out[(m*NCH + ch)*P + pos][row] (pos = sorted position).
+// MODE 1: down (R = H, D = I); activations are h hi rows xa[P][I] and lo rows
+// xb[P][I] by sorted position; out[ch*P + p][row] (p = pair id t*K + k).
+template <int CODEC, int GPW, int XT, int MODE, int WPS>
+__global__ __launch_bounds__(256, WPS) void k_gemv(
+    const int32_t* __restrict__ act_hdr, const ActEntry* __restrict__ act,
+    const int32_t* __restrict__ sorted_pairs, int K, const uint16_t* __restrict__ xa,
+    const uint16_t* __restrict__ xb, int R, int D, int P, int scale_f16, float* __restrict__ out,
+    const float* __restrict__ osx) {
+  using C = UnitCodec<CODEC>;
+  constexpr int NM = MODE == 0 ? 2 : 1;        // matrices per expert
+  constexpr int NS = MODE == 0 ? 1 : 2;        // activation rows per token (x; or h hi, lo)
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ng = D / C::G, NCH = (ng + GPW - 1) / GPW, nstrips = R / 64;
+  const int per_a = nstrips * NM * NCH;
+  const int total = act_hdr[0] * per_a;
+  const int nw = gridDim.x * 4;
+  const MatGeom gm{R, D, C::BITS, C::G};
+
+  // zig-zag over the waves: round r takes items r*nw .. r*nw + nw-1, forwards
+  // on even rounds and backwards on odd ones
+  const int w_id = blockIdx.x * 4 + wv;
+  for (int r = 0; r * nw < total; ++r) {
+    const int item = r * nw + ((r & 1) ? nw - 1 - w_id : w_id);
+    if (item >= total) continue;
+    const int a = item / per_a, r0 = item - a * per_a;
+    const int strip = r0 / (NM * NCH), r1 = r0 - strip * (NM * NCH);
+    const int m = r1 / NCH, ch = r1 - m * NCH;
+    const int seg0 = act[a].seg0, n_e = act[a].n;
+    const gbytes_t mat = as_global(act[a].ptr[MODE == 0 ? m : 2]);
+    const gu16_t msc = (gu16_t)(mat + gm.scales_off());
+    const int row = strip * 64 + lane;
+    const int g0 = ch * GPW, g1 = min(ng, g0 + GPW);
+#ifdef MOE_TRACE
+    // sampled waves (every 16th), first 8 rounds: item start, weights in, item done
+    const bool trs = (w_id & 15) == 0 && r < 8;
+    const int tslot = (MODE == 0 ? 8192 : 20480) + ((w_id >> 4) * 8 + r) * 4;
+    if (trs) {
+      MOE_TRW(tslot);
+      if ((threadIdx.x & 63) == 0) g_moe_trace[tslot + 3] = (unsigned long long)n_e;
+    }
+#endif
+
+    // the item's codes and scales first: they need only the expert's address
+    // (group index clamped, not branched on)
+    u32x4 cw[GPW][C::CHUNKS];
+    uint32_t sr[GPW];
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+      const int g = min(g0 + i, g1 - 1);
+      load_unit4<CODEC>(mat, (int64_t)strip * ng + g, lane, cw[i]);
+      sr[i] = load_scale_dword(msc, (int64_t)row * ng + g);
+    }
+    asm volatile("" ::: "memory");
+#ifdef MOE_TRACE
+    if (trs) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the weights are in (trace builds only)
+      MOE_TRW(tslot + 1);
+    }
+#endif
+    for (int c0 = 0; c0 < n_e; c0 += XT) {
+      const int nt = min(n_e - c0, XT);
+      // pair ids of positions c0 .. c0+XT-1 (clamped to the expert's last):
+      // uniform, so scalar loads, which the activation loads need not wait for
+      // behind the weights
+      int pid[XT];
+      if constexpr (MODE == 1) {
+#pragma unroll
+        for (int j = 0; j < XT; ++j) {
+          pid[j] = sorted_pairs[seg0 + c0 + min(j, nt - 1)];
+          asm volatile("" : "+s"(pid[j]));  // each a scalar load of its own
+        }
+      }
+      // the dot products read the activation rows through scalar loads; the
+      // offset sums of each row and group come precomputed (osx)
+      for (int jp = 0; jp < nt; jp += 2) {
+        const bool two = jp + 1 < nt;
+        const int j1 = two ? jp + 1 : jp;
+        // the two tokens' activation rows in global memory (uniform addresses:
+        // the dot products take them through scalar loads, one load per 8 or 16
+        // pairs for the whole wave)
+        const uint32_t *r0a, *r0b, *r1a, *r1b;
+        int tk0 = 0, tk1 = 0;
+        if (MODE == 0) {
+          tk0 = sorted_pairs[seg0 + c0 + jp] / K;
+          tk1 = sorted_pairs[seg0 + c0 + j1] / K;
+          r0a = r0b = reinterpret_cast<const uint32_t*>(xa + (int64_t)tk0 * D);
+          r1a = r1b = reinterpret_cast<const uint32_t*>(xa + (int64_t)tk1 * D);
+        } else {
+          r0a = reinterpret_cast<const uint32_t*>(xa + (int64_t)(seg0 + c0 + jp) * D);
+          r0b = reinterpret_cast<const uint32_t*>(xb + (int64_t)(seg0 + c0 + jp) * D);
+          r1a = reinterpret_cast<const uint32_t*>(xa + (int64_t)(seg0 + c0 + j1) * D);
+          r1b = reinterpret_cast<const uint32_t*>(xb + (int64_t)(seg0 + c0 + j1) * D);
+        }
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < GPW; ++i) {
+          if (g0 + i < g1) {
+            const int go = (g0 + i) * C::G / 2;
+            const uint32_t *s0a = r0a + go, *s0b = r0b + go, *s1a = r1a + go, *s1b = r1b + go;
+            uint32_t sraw = sr[i];
+            asm volatile("" : "+v"(sraw));  // convert here, not hoisted ahead of the loads
+            const float sc =
+                scale_to_f32(scale_from_dword(sraw, (int64_t)row * ng + g0 + i), scale_f16);
+            uint32_t w[C::WORDS];
+            unit_words<CODEC>(cw[i], w);
+            float d0 = 0.f, d1 = 0.f;
+            // offset sums: per token (gate/up) or per sorted position (down) and group
+            const int64_t o0 = MODE == 0 ? tk0 : seg0 + c0 + jp;
+            const int64_t o1 = MODE == 0 ? tk1 : seg0 + c0 + j1;
+            const float k0 = osx[o0 * ng + g0 + i];
+            if (two) {
+              const float k1 = osx[o1 * ng + g0 + i];
+              C::for_each_pair(w, [&](int Pp, uint32_t pr) {
+                if (NS == 2) {
+                  d0 = dot2_bf16(pr, s0b[Pp], dot2_bf16(pr, s0a[Pp], d0));
+                  d1 = dot2_bf16(pr, s1b[Pp], dot2_bf16(pr, s1a[Pp], d1));
+                } else {
+                  d0 = dot2_bf16(pr, s0a[Pp], d0);
+                  d1 = dot2_bf16(pr, s1a[Pp], d1);
+                }
+              });
+              a1 = fmaf(sc, d1 - k1, a1);
+            } else {
+              C::for_each_pair(w, [&](int Pp, uint32_t pr) {
+                if (NS == 2) d0 = dot2_bf16(pr, s0b[Pp], dot2_bf16(pr, s0a[Pp], d0));
+                else d0 = dot2_bf16(pr, s0a[Pp], d0);
+              });
+            }
+            a0 = fmaf(sc, d0 - k0, a0);
+          }
+        }
+        if (MODE == 0) {
+          float* o = out + ((int64_t)(m * NCH + ch) * P + seg0 + c0 + jp) * R + row;
+          o[0] = a0;
+          if (two) o[R] = a1;
+        } else {
+          out[((int64_t)ch * P + pid[jp]) * R + row] = a0;
+          if (two) out[((int64_t)ch * P + pid[jp + 1]) * R + row] = a1;
+        }
+      }
+    }
+#ifdef MOE_TRACE
+    if (trs) MOE_TRW(tslot + 2);
+#endif
+  }
+}
+
+// ---------------------------------------------------------------- one or two tokens
+// Batches of one or two tokens have a single token pass per expert, and the
+// latency chain of the step dominates; they keep a block-level schedule with one
+// kernel launch fewer: block (a, strip, m*KP + kp) finds the a-th active expert
+// itself (one round trip for the offsets and the table entries together), its
+// four waves take groups g0 + wave + 4*i of part kp of the reduction, and the
+// waves' sums meet in LDS.
+constexpr int kGUWaves = 4;
+constexpr int kTokPerPass = 2;
+#ifndef MOE_GU_AHEAD
+#define MOE_GU_AHEAD 2
+#endif
+constexpr int kGUAhead = MOE_GU_AHEAD;  // weight groups a gate/up wave has in flight
+constexpr int kMaxKParts = 4;
+
+// ---------------------------------------------------------------- active experts
+// The a-th expert (ascending logical id) that owns at least one pair, the number
+// U of such experts, its segment of the grouping and its table entry.
+// Wave-cooperative (every lane returns the same values); positions clamped into
+// [0, P).  Each lane loads the
+// offsets and the table entries of its candidate experts lane + 64*i in the same
+// round trip, so the expert's weight addresses are known after one memory
+// latency instead of two.  E <= 1024.
+struct Active {
+  int e;     // -1 if a >= U
+  int U;
+  int seg0;  // first sorted position of the expert's pairs
+  int n;     // number of pairs
+  const void* ptr[3];  // gate, up, down
+};
+
+__device__ __forceinline__ Active find_active(const int32_t* __restrict__ offsets,
+                                              const moe_expert_ref* __restrict__ table, int E,
+                                              int P, int a) {
+  const int lane = threadIdx.x & 63;
+  constexpr int kSpec = 5;  // candidates per lane whose table entry is fetched up front
+  const int nch = (E + 63) / 64;
+  int lo[16], hi[16];
+  moe_expert_ref ref[kSpec];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i < nch) {  // uniform
+      const int e = lane + 64 * i;
+      // segments clamped into [0, P]: every position read stays inside the
+      // grouping buffers even when caller-supplied offsets are wrong (such a
+      // call is then found bad and writes nothing)
+      lo[i] = (e < E) ? min(max(offsets[e], 0), P) : 0;
+      hi[i] = (e < E) ? min(max(offsets[e + 1], lo[i]), P) : 0;
+      if (i < kSpec) ref[i] = e < E ? table[e] : moe_expert_ref{nullptr, nullptr, nullptr};
+    }
+  }
+  Active r{-1, 0, 0, 0, {nullptr, nullptr, nullptr}};
+  int U = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i < nch) {
+      const bool nz = hi[i] > lo[i];
+      const uint64_t bal = __ballot(nz);
+      const int cnt = __popcll(bal);
+      if (r.e < 0 && a < U + cnt) {  // uniform: the a-th active expert is in this chunk
+        // lane holding it: the (a-U)-th set bit of bal
+        uint64_t m = bal;
+        for (int k = 0; k < a - U; ++k) m &= m - 1;
+        const int src = __ffsll((unsigned long long)m) - 1;
+        r.e = 64 * i + src;
+        r.seg0 = __shfl(lo[i], src);
+        r.n = __shfl(hi[i], src) - r.seg0;
+        if (i < kSpec) {
+          r.ptr[0] = (const void*)__shfl((long long)ref[i].gate, src);
+          r.ptr[1] = (const void*)__shfl((long long)ref[i].up, src);
+          r.ptr[2] = (const void*)__shfl((long long)ref[i].down, src);
+        } else {
+          const moe_expert_ref t = table[r.e];
+          r.ptr[0] = t.gate;
+          r.ptr[1] = t.up;
+          r.ptr[2] = t.down;
+        }
+      }
+      U += cnt;
+    }
+  }
+  r.U = U;
+  return r;
+}
+
+// Batches of one or two tokens (a single pass): the activations take the scalar
+// path instead (s_load into SGPRs, the second operand of v_dot2_f32_bf16), which
+// keeps the kernel at three waves per SIMD so the whole weight stream of a
+// decode step is in flight at once; the offset sums come from vector loads that
+// are requested before the weights.
+template <int CODEC, int GPW>
+__global__ __launch_bounds__(256, 3) void k_gateup_smem(
+    const moe_expert_ref* __restrict__ table, int E, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_pairs, int K, const int32_t* __restrict__ ids,
+    int32_t* __restrict__ ctr,
+    const uint16_t* __restrict__ x,  // read-only: dot operands through scalar loads
+    const uint16_t* x_vec,           // the same activations; not restrict, so that its vector
+                                     // loads stay ahead of the weight loads
+    int H, int I,
+    int P, int KP, int scale_f16, float* __restrict__ gu) {
+  using C = UnitCodec<CODEC>;
+  __shared__ float red[kGUWaves][kTokPerPass][64];
+  const int ng = H / C::G;
+  const int tb = 4 * (blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+  MOE_TR(tb);
+
+  // block (0, 0, 0) also checks the routing (one wave, in registers) and records
+  // the call's verdict for the down kernel, which writes the outputs
+  const bool checker = blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0;
+  auto check = [&]() {
+    if (threadIdx.x < 64) {
+      const bool ok = routing_ok_wave(ids, offsets, sorted_pairs, P, E);
+      if (threadIdx.x == 0) record_routing(ctr, ok);
+    }
+  };
+  const Active act = find_active(offsets, table, E, P, blockIdx.x);
+  MOE_TR(tb + 1);
+  if (act.e < 0) {
+    if (checker) check();
+    return;
+  }
+  const int seg0 = __builtin_amdgcn_readfirstlane(act.seg0);
+  const int n_e = __builtin_amdgcn_readfirstlane(act.n);
+  const int strip = blockIdx.y, m = blockIdx.z / KP, kp = blockIdx.z % KP;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const MatGeom gm{I, H, C::BITS, C::G};
+  const gbytes_t mat = as_global(m ? act.ptr[1] : act.ptr[0]);
+  const gu16_t msc = (gu16_t)(mat + gm.scales_off());
+  const int row = strip * 64 + lane;
+  const int gpb = (ng + KP - 1) / KP, g0 = kp * gpb, g1 = min(ng, g0 + gpb);
+  const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
+  const uint32_t* xv32 = reinterpret_cast<const uint32_t*>(x_vec);
+
+  // weights first: the first kGUAhead groups of this wave (group index clamped,
+  // not branched on, so that the waits the compiler places stay exact); they
+  // need nothing but the expert's address.  Each later group is requested right
+  // after the products of the group kGUAhead before it: the requests of the
+  // whole grid then complete in waves, and every wave's products run while its
+  // later groups are still streaming (with every group requested at once, all
+  // of a wave's data lands near the end of the stream and the products follow
+  // it).
+  auto issue = [&](int i, u32x4 (&cw)[GPW][C::CHUNKS], uint32_t (&sr)[GPW]) {
+    const int g = min(g0 + wv + kGUWaves * i, g1 - 1);
+    load_unit4<CODEC>(mat, (int64_t)strip * ng + g, lane, cw[i]);
+    sr[i] = load_scale_dword(msc, (int64_t)row * ng + g);
+  };
+  // the activation pairs of this wave's groups for the offset sums (lane =
+  // pair) go first: vector loads complete in order, and these (cache hits) are
+  // then not queued behind the weight stream
+  auto load_xo = [&](int t, uint32_t (&xo)[GPW]) {
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+      const int g = min(g0 + wv + kGUWaves * i, g1 - 1);
+      const int pl = lane < C::PAIRS ? lane : 0;
+      xo[i] = xv32[((int64_t)t * H + g * C::G) / 2 + pl];
+    }
+  };
+  // pair ids clamped into [0, P): token rows stay inside x for any routing
+  auto pair_at = [&](int pos) { return min(max(sorted_pairs[pos], 0), P - 1); };
+  const int sp0 = pair_at(seg0), sp1 = pair_at(seg0 + min(1, n_e - 1));
+  uint32_t xo0[GPW], xo1[GPW];
+  load_xo(sp0 / K, xo0);
+  load_xo(sp1 / K, xo1);  // (sp1 = sp0 for a single position)
+  asm volatile("" ::: "memory");
+  u32x4 cw[GPW][C::CHUNKS];
+  uint32_t sr[GPW];  // the aligned dword holding the scale (any 16-bit handling here would wait)
+#pragma unroll
+  for (int i = 0; i < GPW; ++i)
+    if (i < kGUAhead) issue(i, cw, sr);
+  asm volatile("" ::: "memory");
+
+  // one pass over positions b0, b0+1 of the expert with weights cwp/srp (the
+  // first kGUAhead groups already requested; the pass requests the later ones
+  // as it goes)
+  auto pass = [&](int b0, u32x4 (&cwp)[GPW][C::CHUNKS], uint32_t (&srp)[GPW]) {
+    const bool two = b0 + 1 < n_e;
+    const int t0 = pair_at(seg0 + b0) / K;
+    const int t1 = two ? pair_at(seg0 + b0 + 1) / K : t0;
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+      const int g = g0 + wv + kGUWaves * i;
+      if (g < g1) {
+        const uint32_t* x0 = x32 + ((int64_t)t0 * H + g * C::G) / 2;
+        const uint32_t* x1 = x32 + ((int64_t)t1 * H + g * C::G) / 2;
+        uint32_t sraw = srp[i];
+        asm volatile("" : "+v"(sraw));  // convert here, not hoisted ahead of the loads
+        const float sc = scale_to_f32(scale_from_dword(sraw, (int64_t)row * ng + g), scale_f16);
+        uint32_t w[C::WORDS];
+        float d0 = 0.f, d1 = 0.f;
+        unit_words<CODEC>(cwp[i], w);
+        if (two) {
+          C::for_each_pair(w, [&](int Pp, uint32_t pr) {
+            d0 = dot2_bf16(pr, x0[Pp], d0);
+            d1 = dot2_bf16(pr, x1[Pp], d1);
+          });
+          a1 = fmaf(sc, d1, a1);
+        } else {
+          C::for_each_pair(w, [&](int Pp, uint32_t pr) { d0 = dot2_bf16(pr, x0[Pp], d0); });
+        }
+        a0 = fmaf(sc, d0, a0);
+      }
+      if (i + kGUAhead < GPW) {
+        asm volatile("" ::: "memory");
+        issue(i + kGUAhead, cwp, srp);
+        asm volatile("" ::: "memory");
+      }
+    }
+    // subtract sum_g s_g * (offset sum of group g)
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+      const int g = g0 + wv + kGUWaves * i;
+      if (g < g1) {
+        uint32_t sraw = srp[i];
+        asm volatile("" : "+v"(sraw));
+        const float sc = scale_to_f32(scale_from_dword(sraw, (int64_t)row * ng + g), scale_f16);
+        const float off = lane < C::PAIRS ? C::pair_off(lane) : 0.f;
+        uint32_t xa = xo0[i], xb = xo1[i];
+        asm volatile("" : "+v"(xa), "+v"(xb));  // used here, not hoisted ahead of the weights
+        const float c0 = wave_sum_uniform<CODEC>(
+            off * bf16_to_f32((uint16_t)xa) + off * bf16_to_f32((uint16_t)(xa >> 16)));
+        a0 = fmaf(-sc, c0, a0);
+        if (two) {
+          const float c1 = wave_sum_uniform<CODEC>(
+              off * bf16_to_f32((uint16_t)xb) + off * bf16_to_f32((uint16_t)(xb >> 16)));
+          a1 = fmaf(-sc, c1, a1);
+        }
+      }
+    }
+    MOE_TR(tb + 2);
+    red[wv][0][lane] = a0;
+    red[wv][1][lane] = a1;
+    lds_barrier();
+    if (wv < (two ? 2 : 1)) {
+      const int j = wv;
+      float y = 0.f;
+#pragma unroll
+      for (int w = 0; w < kGUWaves; ++w) y += red[w][j][lane];
+      gu[((int64_t)blockIdx.z * P + seg0 + b0 + j) * I + row] = y;
+    }
+    lds_barrier();
+  };
+  pass(0, cw, sr);
+  // more than two positions (a token that lists the expert twice): later passes
+  // request the groups again, in the same way
+  for (int b0 = kTokPerPass; b0 < n_e; b0 += kTokPerPass) {
+    load_xo(pair_at(seg0 + b0) / K, xo0);
+    load_xo(pair_at(seg0 + min(b0 + 1, n_e - 1)) / K, xo1);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < GPW; ++i)
+      if (i < kGUAhead) issue(i, cw, sr);
+    asm volatile("" ::: "memory");
+    pass(b0, cw, sr);
+  }
+  if (checker) check();
+  MOE_TR(tb + 3);
+}
+
+// down of the one/two-token path
+// Block (a, strip): rows [64*strip, +64) of the down matrix of the a-th active
+// expert; 4 waves take groups g = wave + 4*i, i < GPW.  The same schedule as the
+// gate/up kernel: each wave requests h (hi and lo rows) of up to XT of the
+// expert's positions for its groups into its own LDS region, then its weights;
+// the token passes run from LDS with two dot products per code pair (hi, lo).
+// y goes to row p = t*K + k of pair_out (stored written-through).  When `out` is
+// given, the block of each strip that takes the last ticket also forms
+// that strip's 64 columns of out[t] = sum_k w[t][k] y(t,k) (k ascending, pairs
+// with an id outside [0, E) skipped) + the shared expert's slices (added in
+// order): the same arithmetic, in the same order, as the combine kernel, one
+// launch fewer.  It resets the strip's ticket counter for the next call.
+constexpr int kDNWaves = 4;
+constexpr int kCombineMaxK = 16;
+
+// columns [64*strip, +64) of out for T <= 4 tokens (thread = (t, column))
+__device__ __forceinline__ void combine_strip(const float* y, const int32_t* __restrict__ ids,
+                                              const float* __restrict__ w, int K, int E, int H,
+                                              const float* shared, int nsh, int T, int strip,
+                                              float* __restrict__ out) {
+  const int t = threadIdx.x >> 6;
+  if (t >= T) return;
+  const int n = strip * 64 + (threadIdx.x & 63);
+  float v[kCombineMaxK];
+#pragma unroll
+  for (int k = 0; k < kCombineMaxK; ++k)
+    v[k] = ld_coherent(y + ((int64_t)t * K + min(k, K - 1)) * H + n);
+  float acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < kCombineMaxK; ++k) {
+    if (k < K) {
+      const int id = ids[t * K + k];
+      if (id >= 0 && id < E) acc = fmaf(w[t * K + k], v[k], acc);
+    }
+  }
+  if (shared) {
+    float sh = 0.f;
+    for (int q = 0; q < nsh; ++q) sh += shared[((int64_t)q * T + t) * H + n];
+    acc += sh;
+  }
+  out[(int64_t)t * H + n] = acc;
+}
+
+// h of the wave's groups for up to XT positions, formed from the KP gate and up
+// partial products (added in part order, as the SwiGLU pass of the larger
+// batches does): item q = (token j, group i, pair p) of the wave; lane-strided.
+template <int CODEC, int GPW, int XT, int KP>
+struct HFromParts {
+  using C = UnitCodec<CODEC>;
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  static constexpr int NI = XT * GPW * C::PAIRS;
+  static constexpr int IT = (NI + 63) / 64;
+  f32x2 g[IT][KP], u[IT][KP];
+  __device__ __forceinline__ void load(const float* part, int P, int I, int pos0, int nt,
+                                       int gbase, int glast, int lane) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int q = min(it * 64 + lane, NI - 1);
+      const int j = q / (GPW * C::PAIRS), i = (q / C::PAIRS) % GPW, pp = q % C::PAIRS;
+      const int gg = min(gbase + kDNWaves * i, glast);
+      const int64_t pos = pos0 + min(j, nt - 1);
+      const int k = gg * C::G + 2 * pp;
+#pragma unroll
+      for (int r = 0; r < KP; ++r) {
+        g[it][r] = *reinterpret_cast<const f32x2*>(part + ((int64_t)r * P + pos) * I + k);
+        u[it][r] = *reinterpret_cast<const f32x2*>(part + ((int64_t)(KP + r) * P + pos) * I + k);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint32_t* xs, int lane) const {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int q = it * 64 + lane;
+      if (q < NI) {
+        f32x2 gs = g[it][0], us = u[it][0];
+#pragma unroll
+        for (int r = 1; r < KP; ++r) {
+          gs += g[it][r];
+          us += u[it][r];
+        }
+        uint32_t hi = 0, lo = 0;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float gv = e ? gs.y : gs.x, uv = e ? us.y : us.x;
+          const float h = gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * uv;
+          const uint16_t bh = f32_to_bf16_rne(h);
+          hi |= (uint32_t)bh << (16 * e);
+          lo |= (uint32_t)f32_to_bf16_rne(h - bf16_to_f32(bh)) << (16 * e);
+        }
+        const int j = q / (GPW * C::PAIRS), i = (q / C::PAIRS) % GPW, pp = q % C::PAIRS;
+        xs[((j * GPW + i) * 2 + 0) * C::PAIRS + pp] = hi;
+        xs[((j * GPW + i) * 2 + 1) * C::PAIRS + pp] = lo;
+      }
+    }
+  }
+};
+
+template <int CODEC, int GPW, int XT, int KP>
+__global__ __launch_bounds__(256, 2) void k_down_blk(
+    const moe_expert_ref* __restrict__ table, int E, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_pairs, int H, int I, int P, int scale_f16,
+    const float* __restrict__ part, float* pair_out, const int32_t* __restrict__ ids,
+    const float* __restrict__ wts, int K, int T, const float* shared, int nsh,
+    int32_t* __restrict__ ctr, const int32_t* __restrict__ call_bad, float* __restrict__ out) {
+  using C = UnitCodec<CODEC>;
+  using HS = HFromParts<CODEC, GPW, XT, KP>;
+  constexpr int XW = XT * GPW * 2 * C::PAIRS;  // uint32 per wave: [token][group][hi|lo][pair]
+  __shared__ float red[kDNWaves][kTokPerPass][64];
+  __shared__ __align__(16) uint32_t xs_all[kDNWaves * XW];
+  const int ng = I / C::G;
+  const int tb = 4096 + 8 * (blockIdx.x + gridDim.x * blockIdx.y);
+  MOE_TR(tb);
+
+  const int bad = call_bad[0];  // the routing check's verdict (gate/up kernel)
+  const Active act = find_active(offsets, table, E, P, blockIdx.x);
+  MOE_TR(tb + 1);
+  const int strip = blockIdx.y;
+  if (bad) return;  // inconsistent caller routing: the outputs are left untouched
+  if (act.e < 0) {  // no expert for this block; with none at all, block 0 combines
+    if (out && act.U == 0 && blockIdx.x == 0)
+      combine_strip(pair_out, ids, wts, K, E, H, shared, nsh, T, strip, out);
+    return;
+  }
+  const int seg0 = __builtin_amdgcn_readfirstlane(act.seg0);
+  const int n_e = __builtin_amdgcn_readfirstlane(act.n);
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const MatGeom gm{H, I, C::BITS, C::G};
+  const gbytes_t down = as_global(act.ptr[2]);
+  const gu16_t dsc = (gu16_t)(down + gm.scales_off());
+  const int row = strip * 64 + lane;
+  uint32_t* xs = xs_all + wv * XW;
+
+  // pair ids of the expert's first 64 positions (lane = position), then h of the
+  // first positions, all ahead of the weights
+  int pids = sorted_pairs[seg0 + min(lane, n_e - 1)];  // (a checked routing: in [0, P))
+  HS hst;
+  int nt = min(n_e, XT);
+  hst.load(part, P, I, seg0, nt, wv, ng - 1, lane);
+  asm volatile("" ::: "memory");
+
+  u32x4 cw[GPW][C::CHUNKS];
+  uint32_t sr[GPW];  // the aligned dword holding the scale (any 16-bit handling here would wait)
+#pragma unroll
+  for (int i = 0; i < GPW; ++i) {
+    const int g = min(wv + kDNWaves * i, ng - 1);
+    load_unit4<CODEC>(down, (int64_t)strip * ng + g, lane, cw[i]);
+    sr[i] = load_scale_dword(dsc, (int64_t)row * ng + g);
+  }
+  asm volatile("" ::: "memory");
+
+  const float off = lane < C::PAIRS ? C::pair_off(lane) : 0.f;
+  auto osum = [&](const uint32_t* hhp, const uint32_t* hlp) {
+    const uint32_t a = lane < C::PAIRS ? hhp[lane] : 0u, b = lane < C::PAIRS ? hlp[lane] : 0u;
+    return wave_sum_uniform<CODEC>(off * ((bf16_to_f32((uint16_t)a) + bf16_to_f32((uint16_t)(a >> 16))) +
+                                         (bf16_to_f32((uint16_t)b) + bf16_to_f32((uint16_t)(b >> 16)))));
+  };
+  hst.store(xs, lane);
+  MOE_TR(tb + 2);
+  for (int c0 = 0; c0 < n_e; c0 += XT) {
+    if (c0 > 0) {
+      nt = min(n_e - c0, XT);
+      hst.load(part, P, I, seg0 + c0, nt, wv, ng - 1, lane);
+      hst.store(xs, lane);
+      if (c0 % 64 == 0) pids = sorted_pairs[seg0 + c0 + min(lane, n_e - c0 - 1)];
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's own LDS writes
+    for (int jp = 0; jp < nt; jp += kTokPerPass) {
+      const bool two = jp + 1 < nt;
+      const int j1 = two ? jp + 1 : jp;
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < GPW; ++i) {
+        const int g = wv + kDNWaves * i;
+        if (g < ng) {
+          const uint32_t* hh0 = xs + ((jp * GPW + i) * 2 + 0) * C::PAIRS;
+          const uint32_t* hl0 = xs + ((jp * GPW + i) * 2 + 1) * C::PAIRS;
+          const uint32_t* hh1 = xs + ((j1 * GPW + i) * 2 + 0) * C::PAIRS;
+          const uint32_t* hl1 = xs + ((j1 * GPW + i) * 2 + 1) * C::PAIRS;
+          uint32_t wd[C::WORDS];
+          unit_words<CODEC>(cw[i], wd);
+          uint32_t sraw = sr[i];
+          asm volatile("" : "+v"(sraw));
+          const float sc = scale_to_f32(scale_from_dword(sraw, (int64_t)row * ng + g), scale_f16);
+          const float k0 = osum(hh0, hl0);
+          float d0 = 0.f, d1 = 0.f;
+          if (two) {
+            const float k1 = osum(hh1, hl1);
+            C::for_each_pair(wd, [&](int Pp, uint32_t pr) {
+              d0 = dot2_bf16(pr, hl0[Pp], dot2_bf16(pr, hh0[Pp], d0));
+              d1 = dot2_bf16(pr, hl1[Pp], dot2_bf16(pr, hh1[Pp], d1));
+            });
+            a1 = fmaf(sc, d1 - k1, a1);
+          } else {
+            C::for_each_pair(wd, [&](int Pp, uint32_t pr) {
+              d0 = dot2_bf16(pr, hl0[Pp], dot2_bf16(pr, hh0[Pp], d0));
+            });
+          }
+          a0 = fmaf(sc, d0 - k0, a0);
+        }
+      }
+      MOE_TR(tb + 3);
+      red[wv][0][lane] = a0;
+      red[wv][1][lane] = a1;
+      lds_barrier();
+      if (wv < (two ? 2 : 1)) {
+        const int j = wv;
+        float y = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kDNWaves; ++ww) y += red[ww][j][lane];
+        const int idx = (c0 + jp + j) % 64;  // wave-uniform
+        const int p = __builtin_amdgcn_readlane(pids, idx);
+        st_coherent(pair_out + (int64_t)p * H + row, y);
+      }
+      lds_barrier();
+    }
+  }
+  if (out) {  // the strip's last block combines
+    __shared__ int s_last;
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = take_ticket(ctr + strip) == act.U - 1;
+    MOE_TR(tb + 4);
+    lds_barrier();
+    if (s_last) {
+      combine_strip(pair_out, ids, wts, K, E, H, shared, nsh, T, strip, out);
+      if (threadIdx.x == 0) st_coherent(ctr + strip, 0);
+      MOE_TR(tb + 5);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- SwiGLU
+// h[pos][k] = silu(sum_ch g_ch) * (sum_ch u_ch), slices added in chunk order,
+// as bf16 hi + bf16 remainder (h to ~2^-16 relative).  Positions past the
+// grouped pairs are skipped.  MC >= NCH bounds the chunk slices read per element.
+// Wave = reduction group g of the down matrix, lane = code pair P of the group
+// (elements k = g*G + 2P, 2P+1).  The same wave also forms the down codec's
+// offset sum osh[pos][g] = sum_P off_P (hi_2P + hi_2P+1 + lo_2P + lo_2P+1) (the
+// fixed-order wave sum), which the down GEMV subtracts per group.
+template <int CODEC, int MC>
+__global__ __launch_bounds__(256) void k_swiglu_sum(const float* __restrict__ part,
+                                                    const int32_t* __restrict__ offsets, int E,
+                                                    int P, int I, int NCH,
+                                                    uint16_t* __restrict__ hh,
+                                                    uint16_t* __restrict__ hl,
+                                                    float* __restrict__ osh) {
+  using C = UnitCodec<CODEC>;
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const int pos = blockIdx.y;
+  if (pos >= offsets[E]) return;
+  const int ngd = I / C::G;
+  const int lane = threadIdx.x & 63;
+  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (g >= ngd) return;  // wave-uniform
+  const bool live = lane < C::PAIRS;
+  const int k = g * C::G + 2 * (live ? lane : 0);
+  f32x2 pg[MC], pu[MC];
+#pragma unroll
+  for (int c = 0; c < MC; ++c) {
+    const int cc = min(c, NCH - 1);
+    pg[c] = *reinterpret_cast<const f32x2*>(part + ((int64_t)cc * P + pos) * I + k);
+    pu[c] = *reinterpret_cast<const f32x2*>(part + ((int64_t)(NCH + cc) * P + pos) * I + k);
+  }
+  uint32_t hp = 0, lp = 0;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    float gs = e ? pg[0].y : pg[0].x, us = e ? pu[0].y : pu[0].x;
+#pragma unroll
+    for (int c = 1; c < MC; ++c)
+      if (c < NCH) {
+        gs += e ? pg[c].y : pg[c].x;
+        us += e ? pu[c].y : pu[c].x;
+      }
+    const float h = gs * __builtin_amdgcn_rcpf(1.f + __expf(-gs)) * us;
+    const uint16_t hi = f32_to_bf16_rne(h);
+    hp |= (uint32_t)hi << (16 * e);
+    lp |= (uint32_t)f32_to_bf16_rne(h - bf16_to_f32(hi)) << (16 * e);
+  }
+  if (live) {
+    reinterpret_cast<uint32_t*>(hh)[((int64_t)pos * I + k) / 2] = hp;
+    reinterpret_cast<uint32_t*>(hl)[((int64_t)pos * I + k) / 2] = lp;
+  }
+  const float t = live ? (bf16_to_f32((uint16_t)hp) + bf16_to_f32((uint16_t)(hp >> 16))) +
+                             (bf16_to_f32((uint16_t)lp) + bf16_to_f32((uint16_t)(lp >> 16)))
+                       : 0.f;
+  const float off = live ? C::pair_off(lane) : 0.f;
+  const float v = wave_sum_uniform<CODEC>(off * t);
+  if (lane == 0) osh[(int64_t)pos * ngd + g] = v;
+}
+
+// ---------------------------------------------------------------- combine
+// y(t,k) = sum_ch part[ch][t*K+k] (chunk order); out[t] = sum_k w[t][k] y(t,k)
+// (k ascending; pairs whose id is outside [0, E) are skipped) + the shared
+// expert's nsh slices shared[q][t] (added in order);
+// pair_out[t*K+k] = y(t,k) when requested.
+template <int KM, int MC>
+__global__ __launch_bounds__(256) void k_combine_parts(const float* __restrict__ part, int NCH,
+                                                       int P, const int32_t* __restrict__ ids,
+                                                       const float* __restrict__ w, int K, int E,
+                                                       int H, const float* __restrict__ shared,
+                                                       int nsh, int T,
+                                                       const int32_t* __restrict__ call_bad,
+                                                       float* __restrict__ out,
+                                                       float* __restrict__ pair_out) {
+  const int t = blockIdx.y;
+  const int n = min((int)(blockIdx.x * 256 + threadIdx.x), H - 1);
+  float y[KM][MC];
+#pragma unroll
+  for (int k = 0; k < KM; ++k)
+#pragma unroll
+    for (int c = 0; c < MC; ++c)
+      y[k][c] = part[((int64_t)min(c, NCH - 1) * P + (int64_t)t * K + min(k, K - 1)) * H + n];
+  float acc = 0.f;
+  const bool in = blockIdx.x * 256 + threadIdx.x < H;
+  const int bad = call_bad[0];
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    const int id = ids[t * K + min(k, K - 1)];
+    if (k < K && id >= 0 && id < E) {
+      float v = y[k][0];
+#pragma unroll
+      for (int c = 1; c < MC; ++c)
+        if (c < NCH) v += y[k][c];
+      acc = fmaf(w[t * K + min(k, K - 1)], v, acc);
+      if (pair_out && in && !bad) pair_out[((int64_t)t * K + k) * H + n] = v;
+    }
+  }
+  if (shared) {  // the shared expert's slices, in slice order
+    float sh = 0.f;
+    for (int q = 0; q < nsh; ++q) sh += shared[((int64_t)q * T + t) * H + n];
+    acc += sh;
+  }
+  if (in && !bad) out[(int64_t)t * H + n] = acc;
+}
+
+// ---------------------------------------------------------------- launcher
+static int compute_units() {
+  static int n = 0;
+  if (!n) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
+
+template <int CODEC>
+hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* shared_out, int nsh,
+                                  hipEvent_t join, hipStream_t s) {
+  using C = UnitCodec<CODEC>;
+  const moe_cfg& c = *f.c;
+  const int H = c.hidden, I = c.inter, E = c.n_experts, K = c.top_k, T = f.T, P = T * K;
+  int32_t* act_hdr = reinterpret_cast<int32_t*>(f.ws + L.act);
+  ActEntry* act = reinterpret_cast<ActEntry*>(f.ws + L.act + 64);
+  float* gpart = reinterpret_cast<float*>(f.ws + L.gpart);
+  static_assert(sizeof(ActEntry) == 40, "act list entries are 40 bytes");
+  float* dpart = reinterpret_cast<float*>(f.ws + L.dpart);
+  uint16_t* hh = reinterpret_cast<uint16_t*>(f.ws + L.hdec);
+  uint16_t* hl = hh + (int64_t)P * I;
+  const int maxU = min(E, P);
+  const int nch_gu = (H / C::G + kDecGPW - 1) / kDecGPW;
+  const int nch_dn = (I / C::G + kDecGPWd - 1) / kDecGPWd;
+  // blocks of four waves (one per SIMD), wps waves per SIMD resident
+  auto grid_for = [&](int64_t items, int wps) {
+    return (int)std::min<int64_t>((items + 3) / 4, (int64_t)compute_units() * wps);
+  };
+  const int64_t items_gu = (int64_t)maxU * (I / 64) * 2 * nch_gu;
+  const int64_t items_dn = (int64_t)maxU * (H / 64) * nch_dn;
+  int32_t* ctr0 = reinterpret_cast<int32_t*>(f.ws + L.counters);
+  const int32_t* call_bad = ctr0 + kCtrCallBad;
+
+  if (T <= 2) {  // block-level path: no plan kernel
+    const int ngh = H / C::G;
+    const int KP = (ngh + 5 * kGUWaves - 1) / (5 * kGUWaves);  // <= kMaxKParts for H/G <= 64
+    const int gpw_gu = ((ngh + KP - 1) / KP + kGUWaves - 1) / kGUWaves;
+    const int gpw_dn = (I / C::G + kDNWaves - 1) / kDNWaves;
+    float* y = f.pair_out ? f.pair_out : dpart;  // pair-order expert outputs
+#define MOE_GU(N)                                                                                \
+  case N:                                                                                        \
+    MOE_LAUNCH(KID_GATEUP, (k_gateup_smem<CODEC, N>), dim3(maxU, I / 64, 2 * KP),                 \
+               dim3(64 * kGUWaves), 0, s, f.table, E, f.offsets, f.sorted_pairs, K, f.ids, ctr0, f.x, \
+               f.x, H, I, P, KP, c.scale_f16, gpart);                                            \
+    break;
+    switch (gpw_gu) {
+      MOE_GU(1) MOE_GU(2) MOE_GU(3) MOE_GU(4) MOE_GU(5)
+      default: return hipErrorInvalidValue;
+    }
+#undef MOE_GU
+    // down: h formed from the KP gate and up parts while staging (no SwiGLU
+    // launch); each strip's last block combines (no combine launch)
+    const bool fuse = K <= kCombineMaxK && H / 64 <= kCounters - kCtrStrip;
+    int32_t* ctr = reinterpret_cast<int32_t*>(f.ws + L.counters) + kCtrStrip;
+    float* cout = fuse ? f.out : nullptr;
+    if (join) {  // the combine adds the shared expert's output
+      const hipError_t e = hipStreamWaitEvent(s, join, 0);
+      if (e != hipSuccess) return e;
+    }
+#define MOE_DN(N, KPT)                                                                           \
+  case N:                                                                                        \
+    MOE_LAUNCH(KID_DOWN, (k_down_blk<CODEC, N, 2, KPT>), dim3(maxU, H / 64), dim3(64 * kDNWaves), \
+               0, s, f.table, E, f.offsets, f.sorted_pairs, H, I, P, c.scale_f16, gpart, y,      \
+               f.ids, f.w, K, T, shared_out, nsh, ctr, call_bad, cout);                          \
+    break;
+#define MOE_DN_KP(KPT)                                                                           \
+    switch (gpw_dn) {                                                                            \
+      MOE_DN(1, KPT) MOE_DN(2, KPT) MOE_DN(3, KPT) MOE_DN(4, KPT)                                \
+      MOE_DN(5, KPT) MOE_DN(6, KPT) MOE_DN(7, KPT) MOE_DN(8, KPT)                                \
+      default: return hipErrorInvalidValue;                                                      \
+    }
+    switch (KP) {
+      case 1: MOE_DN_KP(1) break;
+      case 2: MOE_DN_KP(2) break;
+      case 3: MOE_DN_KP(3) break;
+      case 4: MOE_DN_KP(4) break;
+      default: return hipErrorInvalidValue;
+    }
+#undef MOE_DN_KP
+#undef MOE_DN
+    if (fuse) return hipGetLastError();
+    // y holds every pair's output in pair order: a single "chunk"
+    if (K <= 8) {
+      MOE_LAUNCH(KID_COMBINE, (k_combine_parts<8, 1>), dim3((H + 255) / 256, T), dim3(256), 0, s, y,
+                 1, P, f.ids, f.w, K, E, H, shared_out, nsh, T, call_bad, f.out, nullptr);
+    } else {
+      MOE_LAUNCH(KID_COMBINE, (k_combine_parts<16, 1>), dim3((H + 255) / 256, T), dim3(256), 0, s,
+                 y, 1, P, f.ids, f.w, K, E, H, shared_out, nsh, T, call_bad, f.out, nullptr);
+    }
+    return hipGetLastError();
+  }
+
+  float* osx = reinterpret_cast<float*>(f.ws + L.osx);
+  MOE_LAUNCH(KID_PLAN, k_plan_decode<CODEC>, dim3(1 + (T * (H / C::G) + 15) / 16), dim3(1024), 0,
+             s, f.offsets, f.ids, f.sorted_pairs, P, ctr0, f.table, E, act_hdr, act, f.x, T, H, osx);
+  // four waves per SIMD: without the activation staging the GEMVs fit in 128
+  // registers; three for 4-bit codes in groups of 128 (four 16-byte loads per unit)
+  constexpr int kWps = C::CHUNKS > 3 ? 3 : 4;
+  MOE_LAUNCH(KID_GATEUP, (k_gemv<CODEC, kDecGPW, 8, 0, kWps>), dim3(grid_for(items_gu, kWps)),
+             dim3(256), 0, s, act_hdr, act, f.sorted_pairs, K, f.x, nullptr, I, H, P, c.scale_f16,
+             gpart, osx);
+  float* osh = reinterpret_cast<float*>(f.ws + L.osh);
+#define MOE_SW(MC)                                                                              \
+  MOE_LAUNCH(KID_SWIGLU, (k_swiglu_sum<CODEC, MC>), dim3((I / C::G + 3) / 4, P), dim3(256), 0, s, \
+             gpart, f.offsets, E, P, I, nch_gu, hh, hl, osh)
+  if (nch_gu <= 8) MOE_SW(8); else if (nch_gu <= 16) MOE_SW(16); else MOE_SW(24);
+#undef MOE_SW
+  MOE_LAUNCH(KID_DOWN, (k_gemv<CODEC, kDecGPWd, 4, 1, kWps>), dim3(grid_for(items_dn, kWps)), dim3(256),
+             0, s, act_hdr, act, f.sorted_pairs, K, hh, hl, H, I, P, c.scale_f16, dpart, osh);
+  if (join) {
+    const hipError_t e = hipStreamWaitEvent(s, join, 0);
+    if (e != hipSuccess) return e;
+  }
+  // MC: chunks of the down reduction read per pair (I/G <= 32 groups, 3 per chunk)
+#define MOE_CMB(KM, MC)                                                                        \
+  MOE_LAUNCH(KID_COMBINE, (k_combine_parts<KM, MC>), dim3((H + 255) / 256, T), dim3(256), 0, s, \
+             dpart, nch_dn, P, f.ids, f.w, K, E, H, shared_out, nsh, T, call_bad, f.out, f.pair_out)
+  if (K <= 8) {
+    if (nch_dn <= 4) MOE_CMB(8, 4); else MOE_CMB(8, 12);
+  } else {
+    if (nch_dn <= 4) MOE_CMB(16, 4); else MOE_CMB(16, 12);
+  }
+#undef MOE_CMB
+  return hipGetLastError();
+}
+
+
+
+}  // namespace moe

@@ -353,8 +353,7 @@ __global__ void k_zero_i32(int32_t* p, int n) {
 
 // ---------------------------------------------------------------- launchers
 
-template <int BITS>
-hipError_t launch_forward_t(const FwdArgs& f, hipStream_t s) {
+hipError_t launch_forward(const FwdArgs& f, hipStream_t s) {
   const moe_cfg& c = *f.c;
   const int H = c.hidden, E = c.n_experts, K = c.top_k, T = f.T;
   const WsLayout L = ws_layout(c, T);
@@ -396,9 +395,6 @@ hipError_t launch_forward_t(const FwdArgs& f, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_forward(const FwdArgs& f, hipStream_t s) {
-  return f.c->bits == 3 ? launch_forward_t<3>(f, s) : launch_forward_t<4>(f, s);
-}
 
 hipError_t launch_rmsnorm(float* resid, const float* add, int T, int H, float eps, uint16_t* y,
                           hipStream_t s) {

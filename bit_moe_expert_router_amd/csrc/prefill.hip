@@ -200,14 +200,14 @@ __device__ __forceinline__ uint32_t q_times_s(uint32_t shifted, uint32_t mask, u
   return __builtin_bit_cast(uint32_t, (v + bias) * s2);                       // (c - z) * s
 }
 
-template <int BITS>
+template <int CODEC>
 struct StepLoad;
 
 // 3-bit, G = 128: half hw = 0 owns pairs 0..31 and spare pairs 60, 61 (words 0..6),
 // half 1 owns pairs 32..59 and spare pairs 62, 63 (words 6..11); each half writes
 // whole 16-byte chunks (4 pairs) of its LDS row.
 template <>
-struct StepLoad<3> {
+struct StepLoad<kQ3G128> {
   uint32_t w[8];  // hw 0: words 0..7; hw 1: words 4..11
   uint32_t sraw;
   __device__ __forceinline__ void load(gbytes_t mat, int64_t tile, int lane, int hw, gu16_t sc,
@@ -254,7 +254,7 @@ struct StepLoad<3> {
 };
 
 template <>
-struct StepLoad<4> {
+struct StepLoad<kQ4G32> {
   uint32_t w[8];
   uint32_t sraw;  // scales of the two groups (the dword holding both)
   __device__ __forceinline__ void load(gbytes_t mat, int64_t tile, int lane, int hw, gu16_t sc,
@@ -284,6 +284,72 @@ struct StepLoad<4> {
         out[4 * u + d] = u32x4p{q_times_s(x, mask, magic, z, s2), q_times_s(x >> 4, mask, magic, z, s2),
                                 q_times_s(x >> 8, mask, magic, z, s2), q_times_s(x >> 12, mask, magic, z, s2)};
       }
+    }
+  }
+};
+
+// 4-bit, G = 128 (16 words, 4 chunks): half hw owns chunks 2hw, 2hw+1 (words
+// 8hw .. 8hw+7, pairs 32hw .. 32hw+31); word d holds pairs 4d .. 4d+3 at offsets
+// 0, 4, 8, 12; one scale per step.
+template <>
+struct StepLoad<kQ4G128> {
+  uint32_t w[8];
+  uint32_t sraw;
+  __device__ __forceinline__ void load(gbytes_t mat, int64_t tile, int lane, int hw, gu16_t sc,
+                                       int64_t sidx) {
+    typedef const u32x4p __attribute__((address_space(1)))* g4;
+    const gbytes_t base = mat + tile * 4 * 1024 + 16 * lane + 2048 * hw;
+    const u32x4p a = *(g4)(base);
+    const u32x4p b = *(g4)(base + 1024);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    typedef const uint16_t __attribute__((address_space(1)))* g16;
+    sraw = *(g16)(sc + sidx);
+  }
+  __device__ __forceinline__ void expand(int hw, int scale_f16, _Float16* wr) const {
+    const _Float16 s = scale_f16 ? __builtin_bit_cast(_Float16, (uint16_t)sraw)
+                                 : (_Float16)bf16_to_f32((uint16_t)sraw);
+    const half2v s2 = {s, s};
+    const half2v z = {(_Float16)-1032.f, (_Float16)-1032.f};
+    const uint32_t mask = 0x000F000Fu, magic = 0x64006400u;
+    u32x4p* out = reinterpret_cast<u32x4p*>(wr) + 8 * hw;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const uint32_t x = w[d];
+      out[d] = u32x4p{q_times_s(x, mask, magic, z, s2), q_times_s(x >> 4, mask, magic, z, s2),
+                      q_times_s(x >> 8, mask, magic, z, s2), q_times_s(x >> 12, mask, magic, z, s2)};
+    }
+  }
+};
+
+// 2-bit, G = 128 (8 words, 2 chunks): half hw owns chunk hw (words 4hw .. 4hw+3,
+// pairs 32hw .. 32hw+31); word d holds pairs 8d .. 8d+7 at offsets 0, 2, .., 14.
+template <>
+struct StepLoad<kQ2G128> {
+  uint32_t w[4];
+  uint32_t sraw;
+  __device__ __forceinline__ void load(gbytes_t mat, int64_t tile, int lane, int hw, gu16_t sc,
+                                       int64_t sidx) {
+    typedef const u32x4p __attribute__((address_space(1)))* g4;
+    const u32x4p a = *(g4)(mat + tile * 2 * 1024 + 16 * lane + 1024 * hw);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    typedef const uint16_t __attribute__((address_space(1)))* g16;
+    sraw = *(g16)(sc + sidx);
+  }
+  __device__ __forceinline__ void expand(int hw, int scale_f16, _Float16* wr) const {
+    const _Float16 s = scale_f16 ? __builtin_bit_cast(_Float16, (uint16_t)sraw)
+                                 : (_Float16)bf16_to_f32((uint16_t)sraw);
+    const half2v s2 = {s, s};
+    const half2v z = {(_Float16)-1026.f, (_Float16)-1026.f};
+    const uint32_t mask = 0x00030003u, magic = 0x64006400u;
+    u32x4p* out = reinterpret_cast<u32x4p*>(wr) + 8 * hw;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t x = w[d];
+      out[2 * d] = u32x4p{q_times_s(x, mask, magic, z, s2), q_times_s(x >> 2, mask, magic, z, s2),
+                          q_times_s(x >> 4, mask, magic, z, s2), q_times_s(x >> 6, mask, magic, z, s2)};
+      out[2 * d + 1] = u32x4p{q_times_s(x >> 8, mask, magic, z, s2), q_times_s(x >> 10, mask, magic, z, s2),
+                              q_times_s(x >> 12, mask, magic, z, s2), q_times_s(x >> 14, mask, magic, z, s2)};
     }
   }
 };
@@ -318,13 +384,13 @@ __device__ __forceinline__ half8 lds_frag(const _Float16* base) {
 // gate and the up matrix.  Waves 2 x 2: wave (wm, wn) owns positions
 // [64wm, 64wm+64) and rows [32wn, 32wn+32) of both matrices (16 accumulator tiles
 // of 16 x 16).  h16[pos][row] = fp16(silu(g) * u), g and u rescaled by 2^s_t.
-template <int BITS>
+template <int CODEC>
 __global__ __launch_bounds__(256, 2) void k_gateup_mfma(
     const moe_expert_ref* __restrict__ table, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ sorted_pairs, int K,
     const uint16_t* __restrict__ x16, const int32_t* __restrict__ xshift, int H, int I,
     int scale_f16, uint16_t* __restrict__ h16) {
-  using C = UnitCodec<BITS>;
+  using C = UnitCodec<CODEC>;
   __shared__ __align__(16) _Float16 xs[kPM * kLdsRow];
   __shared__ __align__(16) _Float16 wsm[2 * kGuN * kLdsRow];
   __shared__ int s_shift[kPM];
@@ -350,7 +416,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(
   const int m = tid >> 7, hw = (tid >> 6) & 1, wrow = lane;
   const moe_expert_ref ref = table[e];
   const gbytes_t mat = as_global(m ? ref.up : ref.gate);
-  const MatGeom gm{I, H, BITS, C::G};
+  const MatGeom gm{I, H, C::BITS, C::G};
   const gu16_t msc = (gu16_t)(mat + gm.scales_off());
   const int ng = H / C::G;
   const int gps = kPK / C::G;  // groups per step
@@ -374,11 +440,11 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(
   // two register stages: the loads of steps s+1 and s+2 are in flight while the
   // matrix cores work on step s
   RowLoad xl[2];
-  StepLoad<BITS> wl[2];
+  StepLoad<CODEC> wl[2];
   auto issue = [&](int st, int b) {
     const int g = st * gps;
     xl[b].load(x16, roff, st * kPK);
-    wl[b].load(mat, tile0 + g, wrow, hw, msc, srow + g + (BITS == 4 ? 2 * hw : 0));
+    wl[b].load(mat, tile0 + g, wrow, hw, msc, srow + g + (C::G == 32 ? 2 * hw : 0));
   };
   auto compute = [&]() {
 #pragma unroll
@@ -442,12 +508,12 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(
 // Block: tile (expert e, positions m0 .. m0+127) x rows [128 nt, 128 nt + 128) of
 // the down matrix.  Waves 2 x 2: wave (wm, wn) owns positions [64wm, 64wm+64) and
 // rows [64wn, 64wn+64) (16 tiles).  pair_out[sorted_pairs[pos]][row] = y.
-template <int BITS>
+template <int CODEC>
 __global__ __launch_bounds__(256, 2) void k_down_mfma(
     const moe_expert_ref* __restrict__ table, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ sorted_pairs, int P,
     const uint16_t* __restrict__ h16, int H, int I, int scale_f16, float* __restrict__ pair_out) {
-  using C = UnitCodec<BITS>;
+  using C = UnitCodec<CODEC>;
   __shared__ __align__(16) _Float16 xs[kPM * kLdsRow];
   __shared__ __align__(16) _Float16 wsm[kDnN * kLdsRow];
   __shared__ int s_pair[kPM];
@@ -471,7 +537,7 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(
   // weights: thread (hw, tl, row): 64-row tile tl of the block's two
   const int hw = tid >> 7, tl = (tid >> 6) & 1, wrow = lane;
   const gbytes_t mat = as_global(table[e].down);
-  const MatGeom gm{H, I, BITS, C::G};
+  const MatGeom gm{H, I, C::BITS, C::G};
   const gu16_t msc = (gu16_t)(mat + gm.scales_off());
   const int ng = I / C::G;
   const int gps = kPK / C::G;
@@ -491,11 +557,11 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(
 
   const int nsteps = I / kPK;
   RowLoad xl[2];
-  StepLoad<BITS> wl[2];
+  StepLoad<CODEC> wl[2];
   auto issue = [&](int st, int b) {
     const int g = st * gps;
     xl[b].load(h16, roff, st * kPK);
-    wl[b].load(mat, tile0 + g, wrow, hw, msc, srow + g + (BITS == 4 ? 2 * hw : 0));
+    wl[b].load(mat, tile0 + g, wrow, hw, msc, srow + g + (C::G == 32 ? 2 * hw : 0));
   };
   auto compute = [&]() {
 #pragma unroll
@@ -551,7 +617,7 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(
 static_assert(kPM == kPrefillTileRows, "tile rows");
 static_assert(kPK == 128 && kDnN == 128 && kGuN == 64, "prefill_eligible assumes these");
 
-template <int BITS>
+template <int CODEC>
 static hipError_t launch_prefill_t(const FwdArgs& f, const WsLayout& L, float* pair_out,
                                    hipStream_t s) {
   const moe_cfg& c = *f.c;
@@ -569,18 +635,23 @@ static hipError_t launch_prefill_t(const FwdArgs& f, const WsLayout& L, float* p
              f.sorted_pairs, P, E, vchk);
   MOE_LAUNCH(KID_PLAN, k_plan, dim3(1), dim3(1024), 0, s, f.offsets, E, vchk, nbc,
              reinterpret_cast<int32_t*>(f.ws + L.counters), tiles);
-  MOE_LAUNCH(KID_GATEUP, k_gateup_mfma<BITS>, dim3(round8(max_tiles * (I / kGuN))),
+  MOE_LAUNCH(KID_GATEUP, k_gateup_mfma<CODEC>, dim3(round8(max_tiles * (I / kGuN))),
              dim3(256), 0, s, f.table, f.offsets, tiles, f.sorted_pairs, K, x16, xshift, H, I,
              c.scale_f16, h16);
-  MOE_LAUNCH(KID_DOWN, k_down_mfma<BITS>, dim3(round8(max_tiles * (H / kDnN))),
+  MOE_LAUNCH(KID_DOWN, k_down_mfma<CODEC>, dim3(round8(max_tiles * (H / kDnN))),
              dim3(256), 0, s, f.table, f.offsets, tiles, f.sorted_pairs, P, h16, H, I,
              c.scale_f16, pair_out);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill(const FwdArgs& f, const WsLayout& L, float* pair_out, hipStream_t s) {
-  return f.c->bits == 3 ? launch_prefill_t<3>(f, L, pair_out, s)
-                        : launch_prefill_t<4>(f, L, pair_out, s);
+  switch (codec_of(f.c->bits, f.c->group)) {
+    case kQ3G128: return launch_prefill_t<kQ3G128>(f, L, pair_out, s);
+    case kQ4G32: return launch_prefill_t<kQ4G32>(f, L, pair_out, s);
+    case kQ2G128: return launch_prefill_t<kQ2G128>(f, L, pair_out, s);
+    case kQ4G128: return launch_prefill_t<kQ4G128>(f, L, pair_out, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace moe

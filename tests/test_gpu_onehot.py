@@ -40,9 +40,13 @@ class StructLayer:
         self.cfg = cfg
         self.q = []      # (qg, qu, qd) signed integer codes per structured expert
         self.blobs = []  # packed (gate, up, down) per structured expert
-        s_g, s_u, s_d = (_scale_bits(v, f16) for v in (32.0, 1.0, 2.0 ** -4))
+        # gate: q in {2, 3} with scale 32 (2-bit codes: q = 1 with scale 64), so g is
+        # 64 or 96 and silu(g) = g exactly
+        self.sg = 64 if bits == 2 else 32
+        s_g, s_u, s_d = (_scale_bits(v, f16) for v in (float(self.sg), 1.0, 2.0 ** -4))
+        glo, ghi = (1, 2) if bits == 2 else (2, 4)
         for _ in range(N_STRUCT):
-            qg = rng.integers(2, 4, size=(I, H), dtype=np.int8)
+            qg = rng.integers(glo, ghi, size=(I, H), dtype=np.int8)
             qu = rng.integers(-z, z, size=(I, H), dtype=np.int8)
             qd = rng.integers(-z, z, size=(H, I), dtype=np.int8)
             self.q.append((qg, qu, qd))
@@ -68,7 +72,7 @@ class StructLayer:
         """y of expert e for one-hot tokens at columns js, from the integer codes
         (float64 matrix products of integers below 2^53: exact in any order)"""
         qg, qu, qd = self.q[e % N_STRUCT]
-        h = (qg[:, js].astype(np.int64) * 32) * qu[:, js]     # [I, n] integers
+        h = (qg[:, js].astype(np.int64) * self.sg) * qu[:, js]  # [I, n] integers
         return (qd.astype(np.float64) @ h.astype(np.float64)).T / 16.0
 
 
@@ -102,13 +106,14 @@ _struct = {}
 
 def _struct_layer(name, dev):
     if name not in _struct:
-        _struct[name] = StructLayer(synth.CONFIGS[name], dev, seed=100 + int(name[1:]))
+        _struct[name] = StructLayer(synth.CONFIGS[name], dev, seed=100 + len(_struct))
     return _struct[name]
 
 
 CASES = [("c2", 1, False), ("c2", 2, True), ("c2", 9, False), ("c2", 64, True),
          ("c2", 200, False), ("c1", 1, False), ("c1", 4, True), ("c1", 13, False),
-         ("c1", 100, False)]
+         ("c1", 100, False), ("q2", 1, False), ("q2", 64, True), ("q2", 200, False),
+         ("q4", 2, True), ("q4", 9, False), ("q4", 200, False)]
 
 
 @pytest.mark.parametrize("name,T,odd", CASES)

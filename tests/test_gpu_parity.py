@@ -80,7 +80,9 @@ def test_routing_bit_exact(gpu, name, T):
 # c3 at T = 16 and 64 gives the hottest experts more tokens than one chunk of the
 # GEMVs takes (8 for gate/up, 4 for down), so their later chunks run.
 FFN_CASES = [("c1", 4), ("c1", 1), ("c1", 13), ("c2", 1), ("c2", 3), ("c3", 1), ("c3", 2),
-             ("c3", 8), ("c3", 9), ("c3", 16), ("c3", 64), ("c1", 300), ("c2", 65)]
+             ("c3", 8), ("c3", 9), ("c3", 16), ("c3", 64), ("c1", 300), ("c2", 65),
+             ("q2", 1), ("q2", 2), ("q2", 8), ("q2", 65), ("q4", 1), ("q4", 2), ("q4", 8),
+             ("q4", 65)]
 
 
 def check_all_pairs(cfg, xh, res, ids, w, he, label):

@@ -119,15 +119,18 @@ def test_weights_equal_restricted_softmax(name):
     assert np.all(np.diff(w, axis=1) <= 0)  # descending logits -> descending weights
 
 
-@pytest.mark.parametrize("name,zipf", [("c1", False), ("c2", True), ("c3", True), ("c5", True),
-                                       ("c5", False)])
-def test_config_seeds_have_no_near_ties(name, zipf):
+@pytest.mark.parametrize("name,zipf,tokens", [("c1", False, None), ("c2", True, None),
+                                              ("c3", True, None), ("c5", True, None),
+                                              ("c5", False, None), ("q2", True, 65),
+                                              ("q4", True, 65), ("c3", True, 300),
+                                              ("c1", False, 300), ("c2", True, 65)])
+def test_config_seeds_have_no_near_ties(name, zipf, tokens):
     """Routing ids are compared bit-exactly against the GPU, so every token of the
     fixed seeds must keep its K-th pick clear of the (K+1)-th, and the picks clear
     of each other (their order is the output order), by far more than any fp64
     summation-order difference (< 1e-12 here)."""
     cfg = synth.CONFIGS[name].with_(zipf=zipf)
-    x, Wr, b = _inputs(cfg)
+    x, Wr, b = _inputs(cfg, tokens)
     ids, _, gap, logits = oracle.route(x, Wr, b, cfg.top_k)
     assert gap.min() > 1e-9, (name, gap.min())
     top = np.take_along_axis(logits, ids.astype(np.int64), axis=1)
