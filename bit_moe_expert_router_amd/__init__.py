@@ -40,7 +40,9 @@ class moe_expert_ref(ctypes.Structure):
 EXPORTS = ("moe_create", "moe_destroy", "moe_workspace_bytes", "moe_workspace_init",
            "set_expert_table", "moe_expert_table_device", "moe_set_shared", "moe_route",
            "moe_forward", "moe_forward_noalloc", "moe_rmsnorm_bf16", "moe_last_error",
-           "moe_profile_enable", "moe_profile_read")
+           "moe_profile_enable", "moe_profile_read", "moe_host_arena_create",
+           "moe_host_arena_destroy", "moe_cache_state_bytes", "moe_cache_init", "moe_cache_step")
+MOE_CACHE_LFU, MOE_CACHE_CLOCK = 0, 1
 
 
 def _load():
@@ -62,6 +64,14 @@ def _load():
                                 ctypes.c_size_t, vp]
     lib.moe_forward_noalloc.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_rmsnorm_bf16.argtypes = [vp, vp, vp, i32, ctypes.c_float, vp, vp]
+    lib.moe_host_arena_create.argtypes = [ctypes.c_size_t, ctypes.POINTER(vp), ctypes.POINTER(vp)]
+    lib.moe_host_arena_destroy.argtypes = [vp]
+    lib.moe_cache_state_bytes.argtypes = [vp, i32]
+    lib.moe_cache_state_bytes.restype = ctypes.c_size_t
+    lib.moe_cache_init.argtypes = [vp, i32, i32, i32, ctypes.c_double,
+                                   ctypes.POINTER(moe_expert_ref), vp, ctypes.c_size_t, vp,
+                                   ctypes.c_size_t, vp]
+    lib.moe_cache_step.argtypes = [vp, i32, vp, vp, vp]
     lib.moe_last_error.restype = ctypes.c_char_p
     lib.moe_profile_enable.argtypes = [i32]
     lib.moe_profile_enable.restype = st
@@ -70,7 +80,8 @@ def _load():
     lib.moe_profile_read.restype = i32
     for f in ("moe_create", "moe_destroy", "moe_workspace_init", "set_expert_table",
               "moe_set_shared", "moe_route", "moe_forward", "moe_forward_noalloc",
-              "moe_rmsnorm_bf16"):
+              "moe_rmsnorm_bf16", "moe_host_arena_create", "moe_host_arena_destroy",
+              "moe_cache_init", "moe_cache_step"):
         getattr(lib, f).restype = st
     return lib
 
@@ -167,6 +178,37 @@ def moe_forward_noalloc(ctx: int, layer: int, x_bf16, T: int, topk_ids, topk_w,
                                    _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(out),
                                    _ptr(pair_out), _stream(stream)),
            "moe_forward_noalloc")
+
+
+def moe_host_arena_create(nbytes: int):
+    """pinned host memory mapped for the device -> (host address, device address)"""
+    h, d = ctypes.c_void_p(), ctypes.c_void_p()
+    _check(lib.moe_host_arena_create(nbytes, ctypes.byref(h), ctypes.byref(d)),
+           "moe_host_arena_create")
+    return h.value, d.value
+
+
+def moe_host_arena_destroy(host: int):
+    _check(lib.moe_host_arena_destroy(host), "moe_host_arena_destroy")
+
+
+def moe_cache_state_bytes(ctx: int, slots: int) -> int:
+    return lib.moe_cache_state_bytes(ctx, slots)
+
+
+def moe_cache_init(ctx: int, layer: int, slots: int, policy: int, decay: float,
+                   home: Sequence[tuple], slot_arena, slot_bytes: int, state, stream=None):
+    """home[e] = (gate, up, down) addresses of expert e's home copy"""
+    arr = (moe_expert_ref * len(home))(*[moe_expert_ref(g, u, d) for g, u, d in home])
+    _check(lib.moe_cache_init(ctx, layer, slots, policy, decay, arr, _ptr(slot_arena), slot_bytes,
+                              _ptr(state), state.numel() * state.element_size(),
+                              _stream(stream)),
+           "moe_cache_init")
+
+
+def moe_cache_step(ctx: int, layer: int, expert_offsets, state, stream=None):
+    _check(lib.moe_cache_step(ctx, layer, _ptr(expert_offsets), _ptr(state), _stream(stream)),
+           "moe_cache_step")
 
 
 def moe_last_error() -> str:

@@ -293,6 +293,81 @@ moe_status moe_forward_noalloc(moe_ctx* ctx, int32_t layer, const void* x_bf16, 
                       stream);
 }
 
+moe_status moe_host_arena_create(size_t bytes, void** host, void** device) {
+  if (!host || !device || bytes == 0) return fail(MOE_E_ARG, "moe_host_arena_create: bad argument");
+  *host = *device = nullptr;
+  void* h = nullptr;
+  hipError_t e = hipHostMalloc(&h, bytes, hipHostMallocMapped);
+  if (e != hipSuccess) return fail(MOE_E_NOMEM, "moe_host_arena_create: %zu bytes: %s", bytes,
+                                   hipGetErrorString(e));
+  void* d = nullptr;
+  e = hipHostGetDevicePointer(&d, h, 0);
+  if (e != hipSuccess || !aligned(d, 256)) {
+    (void)hipHostFree(h);
+    return fail(MOE_E_HIP, "moe_host_arena_create: device address: %s",
+                e != hipSuccess ? hipGetErrorString(e) : "not 256-byte aligned");
+  }
+  *host = h;
+  *device = d;
+  return ok();
+}
+
+moe_status moe_host_arena_destroy(void* host) {
+  if (!host) return ok();
+  return hip_status(hipHostFree(host), "moe_host_arena_destroy");
+}
+
+size_t moe_cache_state_bytes(const moe_ctx* ctx, int32_t slots) {
+  if (!ctx || slots < 0 || slots > 1024) return 0;
+  return (size_t)moe::cache_state_bytes(ctx->cfg.n_experts, slots);
+}
+
+moe_status moe_cache_init(moe_ctx* ctx, int32_t layer, int32_t slots, int32_t policy, double decay,
+                          const moe_expert_ref* home_table, void* slot_arena, size_t slot_bytes,
+                          void* state, size_t state_bytes, moe_stream_t stream) {
+  if (!ctx || !home_table || !state) return fail(MOE_E_ARG, "moe_cache_init: null argument");
+  const moe_cfg& c = ctx->cfg;
+  if (layer < 0 || layer >= ctx->n_layers) return fail(MOE_E_ARG, "moe_cache_init: bad layer %d", layer);
+  if (slots < 0 || slots > 1024 || slots > c.n_experts)
+    return fail(MOE_E_ARG, "moe_cache_init: slots %d outside [0, min(E, 1024)]", slots);
+  if (policy != MOE_CACHE_LFU && policy != MOE_CACHE_CLOCK)
+    return fail(MOE_E_ARG, "moe_cache_init: unknown policy %d", policy);
+  if (!(decay > 0.0 && decay <= 1.0)) return fail(MOE_E_ARG, "moe_cache_init: decay outside (0, 1]");
+  const moe::MatGeom gu{c.inter, c.hidden, c.bits, c.group}, dn{c.hidden, c.inter, c.bits, c.group};
+  const int64_t need = 2 * gu.bytes() + dn.bytes();
+  if (slots > 0 && (!slot_arena || !aligned(slot_arena, 256) || slot_bytes < (size_t)need ||
+                    slot_bytes % 256))
+    return fail(MOE_E_ARG,
+                "moe_cache_init: slot arena must be 256-byte aligned with slot_bytes >= %lld, a "
+                "multiple of 256", (long long)need);
+  if (!aligned(state, 256) || state_bytes < moe_cache_state_bytes(ctx, slots))
+    return fail(MOE_E_ARG, "moe_cache_init: state must be 256-byte aligned, %zu bytes",
+                moe_cache_state_bytes(ctx, slots));
+  for (int e = 0; e < c.n_experts; ++e) {
+    const moe_expert_ref& r = home_table[e];
+    if (!r.gate || !r.up || !r.down || !aligned(r.gate, 256) || !aligned(r.up, 256) ||
+        !aligned(r.down, 256))
+      return fail(MOE_E_ARG, "moe_cache_init: home copy of expert %d null or misaligned", e);
+  }
+  const hipError_t e = moe::launch_cache_init(
+      (uint8_t*)state, c.n_experts, slots, policy, decay, (uint64_t)slot_arena, (int64_t)slot_bytes,
+      gu.bytes(), dn.bytes(), home_table, ctx->d_tables + (size_t)layer * c.n_experts,
+      (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "moe_cache_init");
+  ctx->table_set[layer] = 1;
+  return ok();
+}
+
+moe_status moe_cache_step(moe_ctx* ctx, int32_t layer, const int32_t* expert_offsets, void* state,
+                          moe_stream_t stream) {
+  if (!ctx || !expert_offsets || !state) return fail(MOE_E_ARG, "moe_cache_step: null argument");
+  if (layer < 0 || layer >= ctx->n_layers) return fail(MOE_E_ARG, "moe_cache_step: bad layer %d", layer);
+  return hip_status(moe::launch_cache_step(expert_offsets,
+                                           ctx->d_tables + (size_t)layer * ctx->cfg.n_experts,
+                                           (uint8_t*)state, (hipStream_t)stream),
+                    "moe_cache_step");
+}
+
 moe_status moe_rmsnorm_bf16(const moe_ctx* ctx, float* resid, const float* add, int32_t T,
                             float eps, void* y_bf16, moe_stream_t stream) {
   if (!ctx) return fail(MOE_E_ARG, "moe_rmsnorm_bf16: null context");

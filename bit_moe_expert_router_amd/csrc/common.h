@@ -501,7 +501,7 @@ __host__ inline WsLayout ws_layout(const moe_cfg& c, int T) {
 enum KernelId {
   KID_LOGITS = 0, KID_TOPK, KID_PERMUTE, KID_PLAN, KID_GATEUP, KID_DOWN, KID_SH_GATEUP,
   KID_SH_DOWN, KID_COMBINE, KID_RMSNORM, KID_ZERO, KID_XPREP, KID_SWIGLU, KID_ROUTE, KID_TABLE,
-  KID_COUNT
+  KID_CACHE, KID_COUNT
 };
 // when profiling is on: a pair of events for the next launch of kernel kid
 bool prof_events(int kid, hipEvent_t* b, hipEvent_t* e);
@@ -552,5 +552,12 @@ hipError_t launch_rmsnorm(float* resid, const float* add, int T, int H, float ep
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 hipError_t launch_set_table(moe_expert_ref* dst, const moe_expert_ref* host, int n,
                             hipStream_t s);
+int64_t cache_state_bytes(int E, int S);
+hipError_t launch_cache_init(uint8_t* state, int E, int S, int policy, double decay,
+                             uint64_t arena, int64_t slot_bytes, int64_t bytes_gu,
+                             int64_t bytes_dn, const moe_expert_ref* host_home,
+                             moe_expert_ref* table, hipStream_t s);
+hipError_t launch_cache_step(const int32_t* offsets, moe_expert_ref* table, uint8_t* state,
+                             hipStream_t s);
 
 }  // namespace moe

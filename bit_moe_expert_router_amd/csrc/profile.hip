@@ -20,7 +20,7 @@ namespace {
 const char* const kNames[KID_COUNT] = {"route_logits", "route_topk", "route_permute", "plan",
                                        "gateup",       "down",       "shared_gateup", "shared_down",
                                        "combine",      "rmsnorm",    "zero",          "xprep",        "swiglu",
-                                       "route",        "set_table"};
+                                       "route",        "set_table",     "cache"};
 
 struct Rec {
   int kid;

@@ -224,6 +224,45 @@ moe_status moe_forward_noalloc(moe_ctx* ctx, int32_t layer, const void* x_bf16, 
                                const int32_t* expert_offsets, const int32_t* sorted_pairs,
                                float* out, float* pair_out, moe_stream_t stream);
 
+/* Host home for experts (page "0xSero/glm53-flash-offload", paragraph "Zero-copy
+ * home": every routed expert in a pinned host arena, the pointer tables holding
+ * its device alias, read by the expert kernels with no copy).  Allocates `bytes`
+ * of pinned host memory mapped into the device's address space; *host is the
+ * host address (fill the expert blobs there), *device the address to put in
+ * pointer tables (256-byte aligned).  Blocking host call; not for use under
+ * capture.  MOE_E_NOMEM when the allocation fails. */
+moe_status moe_host_arena_create(size_t bytes, void** host, void** device);
+moe_status moe_host_arena_destroy(void* host);
+
+/* Device-side expert cache over one layer's table (page "GLM-5.3-Flash EXL3
+ * 3.05bpw on 1x RTX PRO 6000 - GPU expert cache, host-RAM streaming", field
+ * config.expert_cache.mechanism; page "0xSero/glm53-flash-offload", paragraph
+ * "Elastic CLOCK expert cache").  Every expert has a home copy (device memory or
+ * a host arena); `slots` copies fit in a caller-owned device slot arena
+ * (slot_bytes apart, each >= the three blobs of an expert laid out gate, up,
+ * down).  moe_cache_init points the layer's table at the home copies and resets
+ * the cache state (a caller-owned device buffer of moe_cache_state_bytes bytes,
+ * 256-byte aligned; one per layer).  moe_cache_step, called after the routing of
+ * a step (expert_offsets as moe_route writes them) and before moe_forward, runs
+ * one block that marks the step's experts, counts hits and misses, picks a
+ * victim slot for each miss (MOE_CACHE_LFU: scores decay by `decay` per step and
+ * gain one per use, the lowest score among the slots the step does not use is
+ * evicted; MOE_CACHE_CLOCK: reference bits and a hand), rewrites the table in
+ * place (admitted experts at their slot, evicted ones back at home), then a
+ * gather kernel copies the admitted experts into their slots.  Stream-ordered;
+ * nothing waits for the host; capturable.  Results of moe_forward do not change:
+ * the bytes are the same wherever they are read from.  The state begins with
+ * int64 steps, hits, misses (totals) and int32 hits, misses of the last step.
+ * The home copies and the arena must outlive the cache's use of the table. */
+#define MOE_CACHE_LFU 0
+#define MOE_CACHE_CLOCK 1
+size_t moe_cache_state_bytes(const moe_ctx* ctx, int32_t slots);
+moe_status moe_cache_init(moe_ctx* ctx, int32_t layer, int32_t slots, int32_t policy, double decay,
+                          const moe_expert_ref* home_table, void* slot_arena, size_t slot_bytes,
+                          void* state, size_t state_bytes, moe_stream_t stream);
+moe_status moe_cache_step(moe_ctx* ctx, int32_t layer, const int32_t* expert_offsets, void* state,
+                          moe_stream_t stream);
+
 /* Stack glue between the MoE layers of a stack (42 of them in the pages' model;
  * page "GLM-5.3-Flash EXL3 2.05bpw on 2x RTX 5090 - TabbyAPI hot-expert swaps,
  * 262K ctx, vision": MoE layers 3-44; the norm itself is not on the pages, it is
