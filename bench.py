@@ -89,6 +89,8 @@ def parse():
                     help="budget of the main workload's CPU-oracle baseline (0: skip); the further "
                          "workloads get a quarter of it each")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
+    ap.add_argument("--no-cache", action="store_true",
+                    help="skip the host-home / expert-cache measurement and the policy replay")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--no-kernel-timing", action="store_true")
@@ -355,6 +357,125 @@ def run_workload(name, a, dev, cpu_budget, main_tokens=None, one_thread=True):
     return res
 
 
+def _ar1_tokens(cfg, n, rho, seed):
+    """n bf16 tokens whose N(0,1) entries follow x_t = rho x_{t-1} + sqrt(1-rho^2) e_t
+    (consecutive decode tokens are alike): synthetic inputs for routing traces"""
+    import numpy as np
+    import synth
+    eps = synth.normal_f32(n * cfg.hidden, cfg.seed, seed, synth.SYN_X, 1.0).reshape(n, -1)
+    x = np.empty_like(eps)
+    x[0] = eps[0]
+    c = np.sqrt(1.0 - rho * rho)
+    for t in range(1, n):
+        x[t] = rho * x[t - 1] + c * eps[t]
+    return synth.bf16_bits(x)
+
+
+def cache_report(dev, steps=64):
+    """Decode of one GLM-shaped layer (batch 1, Zipf routing) with every expert in
+    a pinned host arena: read zero-copy alone, and through the device-side LFU
+    cache of 64 slots; beside the same token sequence with the layer in HBM.  Plus
+    misses per token of the five policies on a routing trace of the 42-layer
+    stack's routers (the library's own routing of correlated synthetic tokens),
+    replayed by the host tool."""
+    import numpy as np
+    import torch
+    import synth
+    import bit_moe_expert_router_amd as moe
+    from bit_moe_expert_router_amd import cachesim
+    from synth.device import DeviceLayer
+    cfg = synth.CONFIGS["c2"]
+    res = {}
+    dl = DeviceLayer.generate(cfg, 0, dev)
+    eb = synth.align(synth.expert_bytes(cfg))
+    import ctypes
+    h, d = moe.moe_host_arena_create(cfg.n_experts * eb)
+    try:
+        buf = np.ctypeslib.as_array((ctypes.c_uint8 * (cfg.n_experts * eb)).from_address(h))
+        off = synth.matrix_offsets(cfg)
+        for e in range(cfg.n_experts):
+            b = synth.expert_blob(cfg, 0, e)
+            buf[e * eb:e * eb + b.size] = b
+        host_refs = [tuple(d + e * eb + o for o in off) for e in range(cfg.n_experts)]
+        xs = torch.from_numpy(_ar1_tokens(cfg, steps, 0.95, 7).view(np.int16)).to(dev)
+        S = 64
+        arena = torch.empty(S * eb, dtype=torch.uint8, device=dev)
+
+        def run(mode):
+            ml = moe.MoELayer(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.bits,
+                              cfg.group, cfg.scale_f16, 0, 1, 1, dev)
+            state = None
+            if mode == "hbm":
+                ml.set_table(0, dl.refs)
+            elif mode == "zero_copy":
+                ml.set_table(0, host_refs)
+            else:
+                state = torch.zeros(moe.moe_cache_state_bytes(ml.ctx, S), dtype=torch.uint8,
+                                    device=dev)
+                moe.moe_cache_init(ml.ctx, 0, S, moe.MOE_CACHE_LFU, 0.995, host_refs, arena, eb,
+                                   state)
+            out = torch.empty((1, cfg.hidden), dtype=torch.float32, device=dev)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for t in range(steps):
+                x = xs[t:t + 1]
+                r = ml.route(x, dl.router, dl.bias)
+                if state is not None:
+                    moe.moe_cache_step(ml.ctx, 0, r.expert_offsets, state)
+                ml.forward(0, x, r, out)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            r = {"tokens_per_s": round(1e3 / ms, 1), "ms_per_token": round(ms, 4)}
+            if state is not None:
+                hdr = state[:24].cpu().numpy().view(np.int64)
+                r.update({"slots": S, "misses_per_token": round(float(hdr[2]) / steps, 2),
+                          "hit_rate": round(float(hdr[1]) / float(hdr[1] + hdr[2]), 3)})
+            ml.close()
+            return r
+
+        for mode in ("hbm", "zero_copy", "lfu_cache"):
+            res[mode] = run(mode)
+        res["note"] = ("batch 1, Zipf(1.1) routing, one layer, a run of correlated synthetic "
+                       f"tokens (rho 0.95), {steps} steps from a cold cache, eager launches; "
+                       "home = pinned host arena read over the host link")
+    finally:
+        moe.moe_host_arena_destroy(h)
+    del dl
+    torch.cuda.empty_cache()
+
+    # policy replay on a 42-layer routing trace
+    c4 = synth.CONFIGS["c4"]
+    ntok = 512
+    pol = {}
+    for rho in (0.0, 0.95):
+        steps_l = [[None] * c4.layers for _ in range(ntok)]
+        ml = moe.MoELayer(c4.hidden, c4.inter, c4.n_experts, c4.top_k, c4.bits, c4.group,
+                          c4.scale_f16, 0, ntok, 1, dev)
+        for l in range(c4.layers):
+            x = torch.from_numpy(_ar1_tokens(c4, ntok, rho, 1000 + l).view(np.int16)).to(dev)
+            wr = torch.from_numpy(synth.router_f32(c4, l)).to(dev)
+            b = torch.from_numpy(synth.zipf_bias(c4, l)).to(dev)
+            r = ml.route(x, wr, b)
+            ids = r.topk_ids.cpu().numpy()
+            for t in range(ntok):
+                steps_l[t][l] = ids[t].tolist()
+        ml.close()
+        trace, offs, L = cachesim.to_csr(steps_l)
+        row = {}
+        for S in (40, 80, 170):
+            row[str(S)] = {p_: round(float(cachesim.simulate(trace, offs, L, c4.n_experts, S, p_,
+                                                              0.995).sum()) / ntok, 2)
+                           for p_ in ("static", "lru", "lfu", "belady", "clock")}
+        pol[f"rho_{rho}"] = row
+    res["policy_misses_per_token"] = pol
+    res["policy_note"] = (f"{ntok} decode tokens at batch 1 through the 42 layers' routers (own "
+                          "Zipf bias each), tokens correlated step to step with coefficient rho; "
+                          "slots per layer; the host replay of host/cachesim.c")
+    return res
+
+
 def stream_ceiling(dev):
     """A plain streaming read (torch sum over fp32) and copy of sizes around the
     decode kernels' bytes, each timed over distinct buffers (no last-level-cache
@@ -486,6 +607,7 @@ def main():
         extra[name] = run_workload(name, a, dev, a.cpu_seconds / 4, one_thread=False)
         print(f"[bench] {name}: {extra[name]['value']} tokens/s", file=sys.stderr, flush=True)
     ceiling = None if a.no_ceiling else stream_ceiling(dev)
+    cache = None if a.no_cache else cache_report(dev)
 
     if a.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -517,6 +639,7 @@ def main():
     }
     res["extra"]["workloads"] = extra
     res["extra"]["stream_ceiling"] = ceiling
+    res["extra"]["cache"] = cache
     if a.calib_copy:
         res["extra"]["calib_copy_bytes"] = 1 << 30
     print(json.dumps(res))

@@ -48,6 +48,10 @@ MOE_CACHE_LFU, MOE_CACHE_CLOCK = 0, 1
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise RuntimeError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build()")
+    # PyTorch first: libmoe.so and torch resolve the same HIP runtime soname, and
+    # the process must use the runtime torch was built with, whichever module a
+    # caller imports first
+    import torch  # noqa: F401
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i32, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int
     lib.moe_create.argtypes = [ctypes.POINTER(moe_cfg), i32, ctypes.POINTER(vp)]

@@ -335,24 +335,22 @@ static_assert(kCtrError * 4 == MOE_WS_ERROR_OFFSET, "error word offset");
 // by expert and stable by pair index, as moe_route writes them.
 //
 // One wave checks P <= 64 pairs (every lane returns the verdict); E <= 1024.
-__device__ __forceinline__ bool routing_ok_wave(const int32_t* __restrict__ ids,
-                                                const int32_t* __restrict__ offsets,
-                                                const int32_t* __restrict__ sp, int P, int E) {
+// routing_ok_regs takes the raw offsets already in registers (lo[c] =
+// offsets[lane + 64c], hi[c] = offsets[lane + 64c + 1] for lane + 64c < E) and the
+// lane's id = ids[lane], s = sorted_pairs[lane], sprev = sorted_pairs[lane - 1]
+// (-1, 0, -1 for lanes at or past P; sprev -1 for lane 0).
+__device__ __forceinline__ bool routing_ok_regs(const int (&lo)[16], const int (&hi)[16], int id,
+                                                int s, int sprev, int P, int E) {
   const int lane = threadIdx.x & 63;
-  const int id = lane < P ? ids[lane] : -1;
-  const int s = lane < P ? sp[lane] : 0;
-  const int sprev = (lane > 0 && lane < P) ? sp[lane - 1] : -1;
-  const int oE = offsets[E];
   const int nch = (E + 63) / 64;
-  int lo[16], hi[16];
   bool bad = false;
+  int oE = 0;
 #pragma unroll
   for (int c = 0; c < 16; ++c) {
     if (c < nch) {
-      const int e = lane + 64 * c;
-      lo[c] = e < E ? offsets[e] : 0;
-      hi[c] = e < E ? offsets[e + 1] : 0;
-      bad |= e < E && hi[c] < lo[c];
+      bad |= lane + 64 * c < E && hi[c] < lo[c];
+      const int last = __shfl(hi[c], (E - 1) & 63);  // offsets[E] sits in chunk (E-1)/64
+      if (c == (E - 1) >> 6) oE = last;
     }
   }
   bad |= lane == 0 && lo[0] != 0;

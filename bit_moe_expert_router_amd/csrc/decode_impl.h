@@ -348,29 +348,47 @@ struct Active {
   int seg0;  // first sorted position of the expert's pairs
   int n;     // number of pairs
   const void* ptr[3];  // gate, up, down
+  bool ok;   // CHECK: the routing is consistent (routing_ok_regs)
 };
 
+// CHECK: also check the routing (P <= 64), its loads in the same round trip
+template <bool CHECK>
 __device__ __forceinline__ Active find_active(const int32_t* __restrict__ offsets,
                                               const moe_expert_ref* __restrict__ table, int E,
-                                              int P, int a) {
+                                              int P, int a, const int32_t* __restrict__ ids = nullptr,
+                                              const int32_t* __restrict__ sp = nullptr) {
   const int lane = threadIdx.x & 63;
   constexpr int kSpec = 5;  // candidates per lane whose table entry is fetched up front
   const int nch = (E + 63) / 64;
   int lo[16], hi[16];
   moe_expert_ref ref[kSpec];
+  int cid = -1, cs = 0, csp = -1;
+  if (CHECK) {
+    cid = lane < P ? ids[lane] : -1;
+    cs = lane < P ? sp[lane] : 0;
+    csp = (lane > 0 && lane < P) ? sp[lane - 1] : -1;
+  }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     if (i < nch) {  // uniform
       const int e = lane + 64 * i;
-      // segments clamped into [0, P]: every position read stays inside the
-      // grouping buffers even when caller-supplied offsets are wrong (such a
-      // call is then found bad and writes nothing)
-      lo[i] = (e < E) ? min(max(offsets[e], 0), P) : 0;
-      hi[i] = (e < E) ? min(max(offsets[e + 1], lo[i]), P) : 0;
+      lo[i] = (e < E) ? offsets[e] : 0;
+      hi[i] = (e < E) ? offsets[e + 1] : 0;
       if (i < kSpec) ref[i] = e < E ? table[e] : moe_expert_ref{nullptr, nullptr, nullptr};
     }
   }
-  Active r{-1, 0, 0, 0, {nullptr, nullptr, nullptr}};
+  Active r{-1, 0, 0, 0, {nullptr, nullptr, nullptr}, true};
+  if (CHECK) r.ok = routing_ok_regs(lo, hi, cid, cs, csp, P, E);
+  // segments clamped into [0, P]: every position read stays inside the grouping
+  // buffers even when caller-supplied offsets are wrong (such a call writes no
+  // output)
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i < nch) {
+      lo[i] = min(max(lo[i], 0), P);
+      hi[i] = min(max(hi[i], lo[i]), P);
+    }
+  }
   int U = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -412,8 +430,7 @@ __device__ __forceinline__ Active find_active(const int32_t* __restrict__ offset
 template <int CODEC, int GPW>
 __global__ __launch_bounds__(256, 3) void k_gateup_smem(
     const moe_expert_ref* __restrict__ table, int E, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_pairs, int K, const int32_t* __restrict__ ids,
-    int32_t* __restrict__ ctr,
+    const int32_t* __restrict__ sorted_pairs, int K,
     const uint16_t* __restrict__ x,  // read-only: dot operands through scalar loads
     const uint16_t* x_vec,           // the same activations; not restrict, so that its vector
                                      // loads stay ahead of the weight loads
@@ -425,21 +442,11 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
   const int tb = 4 * (blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
   MOE_TR(tb);
 
-  // block (0, 0, 0) also checks the routing (one wave, in registers) and records
-  // the call's verdict for the down kernel, which writes the outputs
-  const bool checker = blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0;
-  auto check = [&]() {
-    if (threadIdx.x < 64) {
-      const bool ok = routing_ok_wave(ids, offsets, sorted_pairs, P, E);
-      if (threadIdx.x == 0) record_routing(ctr, ok);
-    }
-  };
-  const Active act = find_active(offsets, table, E, P, blockIdx.x);
+  // (the routing is checked by the down kernel, which writes the outputs; every
+  // read here stays inside the buffers whatever the routing holds)
+  const Active act = find_active<false>(offsets, table, E, P, blockIdx.x);
   MOE_TR(tb + 1);
-  if (act.e < 0) {
-    if (checker) check();
-    return;
-  }
+  if (act.e < 0) return;
   const int seg0 = __builtin_amdgcn_readfirstlane(act.seg0);
   const int n_e = __builtin_amdgcn_readfirstlane(act.n);
   const int strip = blockIdx.y, m = blockIdx.z / KP, kp = blockIdx.z % KP;
@@ -575,7 +582,6 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
     asm volatile("" ::: "memory");
     pass(b0, cw, sr);
   }
-  if (checker) check();
   MOE_TR(tb + 3);
 }
 
@@ -682,7 +688,7 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
     const int32_t* __restrict__ sorted_pairs, int H, int I, int P, int scale_f16,
     const float* __restrict__ part, float* pair_out, const int32_t* __restrict__ ids,
     const float* __restrict__ wts, int K, int T, const float* shared, int nsh,
-    int32_t* __restrict__ ctr, const int32_t* __restrict__ call_bad, float* __restrict__ out) {
+    int32_t* __restrict__ ctr, int32_t* __restrict__ ctr0, float* __restrict__ out) {
   using C = UnitCodec<CODEC>;
   using HS = HFromParts<CODEC, GPW, XT, KP>;
   constexpr int XW = XT * GPW * 2 * C::PAIRS;  // uint32 per wave: [token][group][hi|lo][pair]
@@ -692,11 +698,13 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
   const int tb = 4096 + 8 * (blockIdx.x + gridDim.x * blockIdx.y);
   MOE_TR(tb);
 
-  const int bad = call_bad[0];  // the routing check's verdict (gate/up kernel)
-  const Active act = find_active(offsets, table, E, P, blockIdx.x);
+  // every block checks the routing with its lookup (same round trip, one wave's
+  // registers); block (0, 0) records the verdict and the error bit
+  const Active act = find_active<true>(offsets, table, E, P, blockIdx.x, ids, sorted_pairs);
   MOE_TR(tb + 1);
   const int strip = blockIdx.y;
-  if (bad) return;  // inconsistent caller routing: the outputs are left untouched
+  if (blockIdx.x == 0 && strip == 0 && threadIdx.x == 0) record_routing(ctr0, act.ok);
+  if (!act.ok) return;  // inconsistent caller routing: the outputs are left untouched
   if (act.e < 0) {  // no expert for this block; with none at all, block 0 combines
     if (out && act.U == 0 && blockIdx.x == 0)
       combine_strip(pair_out, ids, wts, K, E, H, shared, nsh, T, strip, out);
@@ -962,8 +970,8 @@ hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* shared_ou
 #define MOE_GU(N)                                                                                \
   case N:                                                                                        \
     MOE_LAUNCH(KID_GATEUP, (k_gateup_smem<CODEC, N>), dim3(maxU, I / 64, 2 * KP),                 \
-               dim3(64 * kGUWaves), 0, s, f.table, E, f.offsets, f.sorted_pairs, K, f.ids, ctr0, f.x, \
-               f.x, H, I, P, KP, c.scale_f16, gpart);                                            \
+               dim3(64 * kGUWaves), 0, s, f.table, E, f.offsets, f.sorted_pairs, K, f.x, f.x, H, I, \
+               P, KP, c.scale_f16, gpart);                                                       \
     break;
     switch (gpw_gu) {
       MOE_GU(1) MOE_GU(2) MOE_GU(3) MOE_GU(4) MOE_GU(5)
@@ -983,7 +991,7 @@ hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* shared_ou
   case N:                                                                                        \
     MOE_LAUNCH(KID_DOWN, (k_down_blk<CODEC, N, 2, KPT>), dim3(maxU, H / 64), dim3(64 * kDNWaves), \
                0, s, f.table, E, f.offsets, f.sorted_pairs, H, I, P, c.scale_f16, gpart, y,      \
-               f.ids, f.w, K, T, shared_out, nsh, ctr, call_bad, cout);                          \
+               f.ids, f.w, K, T, shared_out, nsh, ctr, ctr0, cout);                              \
     break;
 #define MOE_DN_KP(KPT)                                                                           \
     switch (gpw_dn) {                                                                            \
