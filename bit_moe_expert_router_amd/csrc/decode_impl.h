@@ -41,6 +41,7 @@ namespace moe {
 MOE_TRACE_DECL
 
 typedef uint32_t u32x4d __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 
 struct ActEntry {
   int32_t e, seg0, n, pad;
@@ -168,7 +169,11 @@ __global__ __launch_bounds__(1024) void k_plan_decode(const int32_t* __restrict_
   if (e == 0) act_hdr[0] = base[64];
 }
 
-// ---------------------------------------------------------------- GEMV
+// ---------------------------------------------------------------- GEMV, dot products
+// (the gate/up GEMV; the down GEMV is k_gemv_mma below: on the matrix cores the
+// down products, two per code pair and position here, cost less, while for
+// gate/up the staging of the activations the matrix cores need costs as much as
+// it saves on this kernel's batches of mostly one or two tokens per expert)
 // MODE 0: gate and up (R = I rows, reduction D = H); activations are the bf16
 // token rows xa[T][H]; out[(m*NCH + ch)*P + pos][row] (pos = sorted position).
 // MODE 1: down (R = H, D = I); activations are h hi rows xa[P][I] and lo rows
@@ -316,6 +321,180 @@ __global__ __launch_bounds__(256, WPS) void k_gemv(
 #ifdef MOE_TRACE
     if (trs) MOE_TRW(tslot + 2);
 #endif
+  }
+}
+
+// ---------------------------------------------------------------- GEMV, matrix cores
+// MODE 0: gate and up (R = I rows, reduction D = H); activations are the bf16
+// token rows xa[T][H]; out[(m*NCH + ch)*P + pos][row] (pos = sorted position).
+// MODE 1: down (R = H, D = I); activations are h hi rows xa[P][I] and lo rows
+// xb[P][I] by sorted position; out[ch*P + p][row] (p = pair id t*K + k).
+//
+// The products run on the matrix cores: v_mfma_f32_4x4x4bf16_1k computes 16
+// independent 4 x 4 x 4 blocks, lanes 4b..4b+3 forming block b.  The B operand
+// is the wave's own expanded weights (lane = output row; one step = 4 reduction
+// elements = two code pairs); the A operand of lane l is 4 elements of
+// activation row l % 4 of a quad of rows, and the result's register i in lane l
+// is output row l's dot product with row i of the quad (D[b][i][j] sits in lane
+// 4b + j, register i).  A quad is four tokens (gate/up) or two positions' h hi
+// and lo rows (down).  A pass takes NQ = 2 quads: both share each expanded
+// weight step, so a code pair is expanded once per pass whatever the number of
+// tokens.  The pass's activation rows (the item's reduction range) are staged in
+// the wave's own LDS region first (16-byte pieces; no block barriers), and read
+// back 8 bytes per lane per step.
+template <int CODEC, int GPW, int MODE, int WPS>
+__global__ __launch_bounds__(256, WPS) void k_gemv_mma(
+    const int32_t* __restrict__ act_hdr, const ActEntry* __restrict__ act,
+    const int32_t* __restrict__ sorted_pairs, int K, const uint16_t* __restrict__ xa,
+    const uint16_t* __restrict__ xb, int R, int D, int P, int scale_f16, float* __restrict__ out,
+    const float* __restrict__ osx) {
+  using C = UnitCodec<CODEC>;
+  typedef short s4v __attribute__((ext_vector_type(4)));
+  typedef float f4v __attribute__((ext_vector_type(4)));
+  constexpr int NM = MODE == 0 ? 2 : 1;        // matrices per expert
+  constexpr int NQ = 2;                        // quads per pass
+  constexpr int NR = 4 * NQ;                   // staged activation rows per pass
+  constexpr int XT = MODE == 0 ? NR : NR / 2;  // positions per pass
+  constexpr int KC = GPW * C::G;               // reduction elements of an item
+  constexpr int PC = KC / 8;                   // 16-byte pieces of a staged row
+  __shared__ __align__(16) uint16_t xs_all[4][NR][KC];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint16_t (*xs)[KC] = xs_all[wv];
+  const int ng = D / C::G, NCH = (ng + GPW - 1) / GPW, nstrips = R / 64;
+  const int per_a = nstrips * NM * NCH;
+  const int total = act_hdr[0] * per_a;
+  const int nw = gridDim.x * 4;
+  const MatGeom gm{R, D, C::BITS, C::G};
+
+  // zig-zag over the waves: round r takes items r*nw .. r*nw + nw-1, forwards
+  // on even rounds and backwards on odd ones
+  const int w_id = blockIdx.x * 4 + wv;
+  for (int r = 0; r * nw < total; ++r) {
+    const int item = r * nw + ((r & 1) ? nw - 1 - w_id : w_id);
+    if (item >= total) continue;
+    const int a = item / per_a, r0 = item - a * per_a;
+    const int strip = r0 / (NM * NCH), r1 = r0 - strip * (NM * NCH);
+    const int m = r1 / NCH, ch = r1 - m * NCH;
+    const int seg0 = act[a].seg0, n_e = act[a].n;
+    const gbytes_t mat = as_global(act[a].ptr[MODE == 0 ? m : 2]);
+    const gu16_t msc = (gu16_t)(mat + gm.scales_off());
+    const int row = strip * 64 + lane;
+    const int g0 = ch * GPW, g1 = min(ng, g0 + GPW);
+
+    // the item's codes and scales first: they need only the expert's address
+    // (group index clamped, not branched on)
+    u32x4 cw[GPW][C::CHUNKS];
+    uint32_t sr[GPW];
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+      const int g = min(g0 + i, g1 - 1);
+      load_unit4<CODEC>(mat, (int64_t)strip * ng + g, lane, cw[i]);
+      sr[i] = load_scale_dword(msc, (int64_t)row * ng + g);
+    }
+    asm volatile("" ::: "memory");
+    for (int c0 = 0; c0 < n_e; c0 += XT) {
+      const int nt = min(n_e - c0, XT);
+      // positions c0 .. c0+XT-1 (clamped to the expert's last); uniform
+      int pid[XT], orow[XT];
+#pragma unroll
+      for (int j = 0; j < XT; ++j) {
+        pid[j] = sorted_pairs[seg0 + c0 + min(j, nt - 1)];
+        orow[j] = MODE == 0 ? pid[j] / K : seg0 + c0 + min(j, nt - 1);  // osx row
+      }
+      // stage the pass's activation rows (row slot q: gate/up token q; down:
+      // position q/2, h hi for even q, lo for odd q), elements g0*G .. +KC
+      // (clamped inside the row); only the rows of the nt positions: a quad's
+      // other rows hold stale data, whose products land only in results that are
+      // not stored
+      constexpr int QP = MODE == 0 ? 4 : 2;       // positions per quad
+      const int nq = (nt + QP - 1) / QP;          // quads this pass
+      const int nrow = MODE == 0 ? nt : 2 * nt;   // rows staged
+#pragma unroll
+      for (int it = 0; it < (NR * PC + 63) / 64; ++it) {
+        const int pc = it * 64 + lane;
+        if (pc < nrow * PC) {
+          const int q = pc / PC, col = pc - q * PC;
+          const uint16_t* src;
+          if (MODE == 0) {
+            int tk = orow[0];
+#pragma unroll
+            for (int j = 1; j < XT; ++j)
+              if (q == j) tk = orow[j];
+            src = xa + (int64_t)tk * D;
+          } else {
+            const int pos = seg0 + c0 + min(q >> 1, nt - 1);
+            src = ((q & 1) ? xb : xa) + (int64_t)pos * D;
+          }
+          const int k = min(g0 * C::G + col * 8, D - 8);
+          *reinterpret_cast<u32x4*>(&xs[q][col * 8]) = *reinterpret_cast<const u32x4*>(src + k);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's own LDS writes
+      f4v acc[NQ];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) acc[q] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < GPW; ++i) {
+        if (g0 + i < g1) {
+          uint32_t sraw = sr[i];
+          asm volatile("" : "+v"(sraw));  // convert here, not hoisted ahead of the loads
+          const float sc =
+              scale_to_f32(scale_from_dword(sraw, (int64_t)row * ng + g0 + i), scale_f16);
+          uint32_t w[C::WORDS];
+          unit_words<CODEC>(cw[i], w);
+          f4v d[NQ];
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) d[q] = f4v{0.f, 0.f, 0.f, 0.f};
+          uint32_t even = 0;
+          C::for_each_pair(w, [&](int Pp, uint32_t pr) {
+            if ((Pp & 1) == 0) {
+              even = pr;
+              return;
+            }
+            const s4v b = __builtin_bit_cast(s4v, u32x2v{even, pr});
+            const int k = i * C::G + 2 * (Pp - 1);  // step of pairs Pp-1, Pp
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+              if (q < nq) {  // uniform
+                const s4v av = *reinterpret_cast<const s4v*>(&xs[4 * q + (lane & 3)][k]);
+                d[q] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(av, b, d[q], 0, 0, 0);
+              }
+            }
+          });
+          // subtract the codec's offset sums, apply the group scale
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) {
+            if (MODE == 0) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                acc[q][e] = fmaf(sc, d[q][e] - osx[(int64_t)orow[4 * q + e] * ng + g0 + i], acc[q][e]);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 2; ++e)
+                acc[q][2 * e] = fmaf(sc, (d[q][2 * e] + d[q][2 * e + 1]) -
+                                             osx[(int64_t)orow[2 * q + e] * ng + g0 + i],
+                                     acc[q][2 * e]);
+            }
+          }
+        }
+      }
+      // results: gate/up by sorted position, down by pair
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        if (MODE == 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * q + e < nt)
+              out[((int64_t)(m * NCH + ch) * P + seg0 + c0 + 4 * q + e) * R + row] = acc[q][e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 2; ++e)
+            if (2 * q + e < nt) out[((int64_t)ch * P + pid[2 * q + e]) * R + row] = acc[q][2 * e];
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // the pass's LDS reads, before the next staging
+    }
   }
 }
 
@@ -1035,7 +1214,8 @@ hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* shared_ou
              gpart, f.offsets, E, P, I, nch_gu, hh, hl, osh)
   if (nch_gu <= 8) MOE_SW(8); else if (nch_gu <= 16) MOE_SW(16); else MOE_SW(24);
 #undef MOE_SW
-  MOE_LAUNCH(KID_DOWN, (k_gemv<CODEC, kDecGPWd, 4, 1, kWps>), dim3(grid_for(items_dn, kWps)), dim3(256),
+  constexpr int kWpsD = C::CHUNKS > 3 ? 3 : 4;
+  MOE_LAUNCH(KID_DOWN, (k_gemv_mma<CODEC, kDecGPWd, 1, kWpsD>), dim3(grid_for(items_dn, kWpsD)), dim3(256),
              0, s, act_hdr, act, f.sorted_pairs, K, hh, hl, H, I, P, c.scale_f16, dpart, osh);
   if (join) {
     const hipError_t e = hipStreamWaitEvent(s, join, 0);
