@@ -637,6 +637,42 @@ __device__ __forceinline__ void wave_group_small(int id, int P, int E, int* s_ke
   }
 }
 
+// The same grouping for at most 16 pairs, without LDS: every lane reads the P
+// keys as wave-uniform values and counts, for its own pair, the pairs with a
+// smaller (key, pair index), and for its experts e = lane + 64*i, the valid pairs
+// with an id below e.  Integer only: bit-exact, and the same stable order.
+constexpr int kTinyPairs = 16;
+template <int NOFF>  // NOFF * 64 > E
+__device__ __forceinline__ void wave_group_tiny(int id, int P, int E,
+                                                int32_t* __restrict__ offsets,
+                                                int32_t* __restrict__ sorted_pairs,
+                                                int32_t* __restrict__ pair_pos) {
+  const int lane = threadIdx.x & 63;
+  const bool live = lane < P;
+  const bool ok = live && id >= 0 && id < E;
+  const int key = ok ? id : E;
+  int pos = 0;
+  int below[NOFF];
+#pragma unroll
+  for (int i = 0; i < NOFF; ++i) below[i] = 0;
+#pragma unroll
+  for (int q = 0; q < kTinyPairs; ++q) {
+    if (q < P) {  // uniform
+      const int kq = __builtin_amdgcn_readlane(key, q);
+      pos += (kq < key) || (kq == key && q < lane);
+#pragma unroll
+      for (int i = 0; i < NOFF; ++i) below[i] += kq < lane + 64 * i;
+    }
+  }
+  if (ok) sorted_pairs[pos] = lane;
+  if (live) pair_pos[lane] = ok ? pos : -1;
+#pragma unroll
+  for (int i = 0; i < NOFF; ++i) {
+    const int e = lane + 64 * i;
+    if (e <= E) offsets[e] = below[i];
+  }
+}
+
 // Decode batches of 3 to 16 tokens: wave t picks the top-k of token t, then the
 // first wave groups the pairs (one launch after the logits).
 template <int PER>
@@ -660,8 +696,11 @@ __global__ __launch_bounds__(1024) void k_topk_group_small(
   lds_barrier();
   if (threadIdx.x < 64) {
     const int P = T * K;
-    wave_group_small<PER + 1>(lane < P ? s_ids[lane] : -1, P, E, s_key, offsets, sorted_pairs,
-                              pair_pos);
+    if (P <= kTinyPairs)
+      wave_group_tiny<PER + 1>(lane < P ? s_ids[lane] : -1, P, E, offsets, sorted_pairs, pair_pos);
+    else
+      wave_group_small<PER + 1>(lane < P ? s_ids[lane] : -1, P, E, s_key, offsets, sorted_pairs,
+                                pair_pos);
   }
 }
 
@@ -709,8 +748,11 @@ __global__ __launch_bounds__(256) void k_route_small(
   lds_barrier();  // s_ids only; the stores above need not have completed
   if (wv == 0) {
     const int P = T * K;
-    wave_group_small<PER + 1>(lane < P ? s_ids[lane] : -1, P, E, s_key, offsets, sorted_pairs,
-                              pair_pos);
+    if (P <= kTinyPairs)
+      wave_group_tiny<PER + 1>(lane < P ? s_ids[lane] : -1, P, E, offsets, sorted_pairs, pair_pos);
+    else
+      wave_group_small<PER + 1>(lane < P ? s_ids[lane] : -1, P, E, s_key, offsets, sorted_pairs,
+                                pair_pos);
     if (lane == 0) st_coherent(ctr, 0);
   }
   MOE_TR(2001);

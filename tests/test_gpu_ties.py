@@ -67,6 +67,22 @@ CASES = [("c1", 1), ("c2", 1), ("c2", 2), ("c2", 5), ("c3", 16), ("c3", 24), ("c
          ("c3", 300), ("c5", 8192)]
 
 
+def _check_route(gpu, cfg, dl, xd, T, Wr, b, ids, w):
+    ml = make_layer_api(cfg, dl, T)
+    wr_d = torch.from_numpy(Wr).to(gpu)
+    b_d = None if b is None else torch.from_numpy(b).to(gpu)
+    r = ml.route(xd, wr_d, b_d)
+    torch.cuda.synchronize()
+    assert np.array_equal(r.topk_ids.cpu().numpy(), ids), "ids differ"
+    wg = r.topk_w.cpu().numpy()
+    assert np.all(np.abs(wg - w) <= W_TOL * np.maximum(w, 1e-30) + 1e-12)
+    off, sp, pp = oracle.permute(ids, cfg.n_experts)
+    assert np.array_equal(r.expert_offsets.cpu().numpy(), off)
+    assert np.array_equal(r.sorted_pairs.cpu().numpy()[:off[-1]], sp)
+    assert np.array_equal(r.pair_pos.cpu().numpy(), pp)
+    ml.close()
+
+
 @pytest.mark.parametrize("name,T", CASES)
 def test_routing_exact_ties(gpu, name, T):
     say(f"[ties] {name} T={T}")
@@ -82,22 +98,42 @@ def test_routing_exact_ties(gpu, name, T):
     assert np.all((d == 0) | (d > NEAR)), name
     n_tied = int(np.sum(np.any(d == 0, axis=1)))
     assert n_tied > 0, "no token has a tie among its leading logits"
-    ml = make_layer_api(cfg, dl, T)
-    wr_d = torch.from_numpy(Wr).to(gpu)
-    b_d = None if b is None else torch.from_numpy(b).to(gpu)
-    r = ml.route(xd, wr_d, b_d)
-    torch.cuda.synchronize()
-    assert np.array_equal(r.topk_ids.cpu().numpy(), ids), "ids differ"
-    wg = r.topk_w.cpu().numpy()
-    assert np.all(np.abs(wg - w) <= W_TOL * np.maximum(w, 1e-30) + 1e-12)
-    off, sp, pp = oracle.permute(ids, cfg.n_experts)
-    assert np.array_equal(r.expert_offsets.cpu().numpy(), off)
-    assert np.array_equal(r.sorted_pairs.cpu().numpy()[:off[-1]], sp)
-    assert np.array_equal(r.pair_pos.cpu().numpy(), pp)
+    _check_route(gpu, cfg, dl, xd, T, Wr, b, ids, w)
     # the lower id of each copied pair wins wherever the two tie for a place
     for s, dd in copies:
         lo, hi = min(s, dd), max(s, dd)
         has_hi = np.any(ids == hi, axis=1)
         assert np.all(np.any(ids[has_hi] == lo, axis=1)), (s, dd)
     say(f"[ties] {name} T={T}: {n_tied} tokens with a tie among their leading logits")
-    ml.close()
+
+
+MASS = [("c1", 1, "all"), ("c2", 1, "all"), ("c2", 1, "blocks"), ("c2", 2, "blocks"),
+        ("c2", 2, "all"), ("c3", 5, "blocks"), ("c3", 9, "all"), ("c3", 37, "blocks"),
+        ("c3", 300, "all")]
+
+
+@pytest.mark.parametrize("name,T,mode", MASS)
+def test_routing_mass_ties(gpu, name, T, mode):
+    """Many experts with equal logits: every router row (and bias entry) the same
+    ("all": each token's logits are all equal, the picks are ids 0..K-1 with
+    weights 1/K), or the same within blocks of consecutive ids ("blocks": the
+    leading block's ids tie, the lowest of them are picked in id order).  These
+    reach the top-k's one-round-at-a-time path (more equal leading keys than a
+    wave holds) and its ranking of equal candidates."""
+    say(f"[mass ties] {name} T={T} {mode}")
+    cfg = synth.CONFIGS[name]
+    dl = _layer(name, gpu)
+    xh, xd = x_device(cfg, gpu, tokens=T)
+    Wr = synth.router_f32(cfg).copy()
+    b = synth.zipf_bias(cfg)
+    b = None if b is None else b.copy()
+    blk = cfg.n_experts if mode == "all" else max(cfg.n_experts // 12, cfg.top_k + 1)
+    src = (np.arange(cfg.n_experts) // blk) * blk
+    Wr = np.ascontiguousarray(Wr[src])
+    if b is not None:
+        b = np.ascontiguousarray(b[src])
+    ids, w, gap, logits = oracle.route(xh, Wr, b, cfg.top_k)
+    if mode == "all":
+        assert np.array_equal(ids, np.tile(np.arange(cfg.top_k), (T, 1)))
+        assert np.allclose(w, 1.0 / cfg.top_k, rtol=1e-15)
+    _check_route(gpu, cfg, dl, xd, T, Wr, b, ids, w)
