@@ -223,8 +223,13 @@ struct UnitCodec<kQ2G128> {
 };
 
 // ---------------------------------------------------------------- unit loads (decode)
+// Scales are stored in the codes' tile order: the scale of row 64*(tile's row
+// block) + lane and the tile's group sits at index tile*64 + lane, so a wave's
+// scales of one tile are 128 contiguous bytes.
+__device__ __forceinline__ int64_t scale_idx(int64_t tile, int lane) { return tile * 64 + lane; }
 // A 16-bit scale is fetched as the aligned dword that contains it (the scales
-// region is 256-byte aligned, so the dword lies inside it) and selected at use.
+// region is 256-byte aligned, so the dword lies inside it; lanes 2i and 2i+1 load
+// the same dword) and selected at use by the index's parity (the lane's).
 __device__ __forceinline__ uint32_t load_scale_dword(gu16_t sc, int64_t idx) {
   typedef const uint32_t __attribute__((address_space(1)))* gu32_t;
   return *(gu32_t)(sc + (idx & ~(int64_t)1));

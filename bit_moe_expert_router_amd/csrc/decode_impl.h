@@ -227,7 +227,7 @@ __global__ __launch_bounds__(256, WPS) void k_gemv(
     for (int i = 0; i < GPW; ++i) {
       const int g = min(g0 + i, g1 - 1);
       load_unit4<CODEC>(mat, (int64_t)strip * ng + g, lane, cw[i]);
-      sr[i] = load_scale_dword(msc, (int64_t)row * ng + g);
+      sr[i] = load_scale_dword(msc, scale_idx((int64_t)strip * ng + g, lane));
     }
     asm volatile("" ::: "memory");
 #ifdef MOE_TRACE
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(256, WPS) void k_gemv(
             uint32_t sraw = sr[i];
             asm volatile("" : "+v"(sraw));  // convert here, not hoisted ahead of the loads
             const float sc =
-                scale_to_f32(scale_from_dword(sraw, (int64_t)row * ng + g0 + i), scale_f16);
+                scale_to_f32(scale_from_dword(sraw, lane), scale_f16);
             uint32_t w[C::WORDS];
             unit_words<CODEC>(cw[i], w);
             float d0 = 0.f, d1 = 0.f;
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(256, WPS) void k_gemv_mma(
     for (int i = 0; i < GPW; ++i) {
       const int g = min(g0 + i, g1 - 1);
       load_unit4<CODEC>(mat, (int64_t)strip * ng + g, lane, cw[i]);
-      sr[i] = load_scale_dword(msc, (int64_t)row * ng + g);
+      sr[i] = load_scale_dword(msc, scale_idx((int64_t)strip * ng + g, lane));
     }
     asm volatile("" ::: "memory");
     for (int c0 = 0; c0 < n_e; c0 += XT) {
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(256, WPS) void k_gemv_mma(
           uint32_t sraw = sr[i];
           asm volatile("" : "+v"(sraw));  // convert here, not hoisted ahead of the loads
           const float sc =
-              scale_to_f32(scale_from_dword(sraw, (int64_t)row * ng + g0 + i), scale_f16);
+              scale_to_f32(scale_from_dword(sraw, lane), scale_f16);
           uint32_t w[C::WORDS];
           unit_words<CODEC>(cw[i], w);
           f4v d[NQ];
@@ -650,7 +650,7 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
   auto issue = [&](int i, u32x4 (&cw)[GPW][C::CHUNKS], uint32_t (&sr)[GPW]) {
     const int g = min(g0 + wv + kGUWaves * i, g1 - 1);
     load_unit4<CODEC>(mat, (int64_t)strip * ng + g, lane, cw[i]);
-    sr[i] = load_scale_dword(msc, (int64_t)row * ng + g);
+    sr[i] = load_scale_dword(msc, scale_idx((int64_t)strip * ng + g, lane));
   };
   // the activation pairs of this wave's groups for the offset sums (lane =
   // pair) go first: vector loads complete in order, and these (cache hits) are
@@ -693,7 +693,7 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
         const uint32_t* x1 = x32 + ((int64_t)t1 * H + g * C::G) / 2;
         uint32_t sraw = srp[i];
         asm volatile("" : "+v"(sraw));  // convert here, not hoisted ahead of the loads
-        const float sc = scale_to_f32(scale_from_dword(sraw, (int64_t)row * ng + g), scale_f16);
+        const float sc = scale_to_f32(scale_from_dword(sraw, lane), scale_f16);
         uint32_t w[C::WORDS];
         float d0 = 0.f, d1 = 0.f;
         unit_words<CODEC>(cwp[i], w);
@@ -721,7 +721,7 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
       if (g < g1) {
         uint32_t sraw = srp[i];
         asm volatile("" : "+v"(sraw));
-        const float sc = scale_to_f32(scale_from_dword(sraw, (int64_t)row * ng + g), scale_f16);
+        const float sc = scale_to_f32(scale_from_dword(sraw, lane), scale_f16);
         const float off = lane < C::PAIRS ? C::pair_off(lane) : 0.f;
         uint32_t xa = xo0[i], xb = xo1[i];
         asm volatile("" : "+v"(xa), "+v"(xb));  // used here, not hoisted ahead of the weights
@@ -913,7 +913,7 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
   for (int i = 0; i < GPW; ++i) {
     const int g = min(wv + kDNWaves * i, ng - 1);
     load_unit4<CODEC>(down, (int64_t)strip * ng + g, lane, cw[i]);
-    sr[i] = load_scale_dword(dsc, (int64_t)row * ng + g);
+    sr[i] = load_scale_dword(dsc, scale_idx((int64_t)strip * ng + g, lane));
   }
   asm volatile("" ::: "memory");
 
@@ -949,7 +949,7 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
           unit_words<CODEC>(cw[i], wd);
           uint32_t sraw = sr[i];
           asm volatile("" : "+v"(sraw));
-          const float sc = scale_to_f32(scale_from_dword(sraw, (int64_t)row * ng + g), scale_f16);
+          const float sc = scale_to_f32(scale_from_dword(sraw, lane), scale_f16);
           const float k0 = osum(hh0, hl0);
           float d0 = 0.f, d1 = 0.f;
           if (two) {

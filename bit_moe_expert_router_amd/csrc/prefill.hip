@@ -210,8 +210,7 @@ template <>
 struct StepLoad<kQ3G128> {
   uint32_t w[8];  // hw 0: words 0..7; hw 1: words 4..11
   uint32_t sraw;
-  __device__ __forceinline__ void load(gbytes_t mat, int64_t tile, int lane, int hw, gu16_t sc,
-                                       int64_t sidx) {
+  __device__ __forceinline__ void load(gbytes_t mat, int64_t tile, int lane, int hw, gu16_t sc) {
     typedef const u32x4p __attribute__((address_space(1)))* g4;
     const gbytes_t base = mat + tile * 3 * 1024 + 16 * lane + 1024 * hw;
     const u32x4p a = *(g4)(base);
@@ -219,7 +218,7 @@ struct StepLoad<kQ3G128> {
     w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
     w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
     typedef const uint16_t __attribute__((address_space(1)))* g16;
-    sraw = *(g16)(sc + sidx);
+    sraw = *(g16)(sc + scale_idx(tile, lane));
   }
   __device__ __forceinline__ void expand(int hw, int scale_f16, _Float16* wr) const {
     const _Float16 s = scale_f16 ? __builtin_bit_cast(_Float16, (uint16_t)sraw)
@@ -256,9 +255,8 @@ struct StepLoad<kQ3G128> {
 template <>
 struct StepLoad<kQ4G32> {
   uint32_t w[8];
-  uint32_t sraw;  // scales of the two groups (the dword holding both)
-  __device__ __forceinline__ void load(gbytes_t mat, int64_t tile, int lane, int hw, gu16_t sc,
-                                       int64_t sidx) {
+  uint32_t sraw;  // scales of the two groups
+  __device__ __forceinline__ void load(gbytes_t mat, int64_t tile, int lane, int hw, gu16_t sc) {
     typedef const u32x4p __attribute__((address_space(1)))* g4;
     // tile = index of the step's first group's tile; units 2hw, 2hw+1 follow it
 #pragma unroll
@@ -266,8 +264,10 @@ struct StepLoad<kQ4G32> {
       const u32x4p a = *(g4)(mat + (tile + 2 * hw + u) * 1024 + 16 * lane);
       w[4 * u] = a.x; w[4 * u + 1] = a.y; w[4 * u + 2] = a.z; w[4 * u + 3] = a.w;
     }
-    typedef const uint32_t __attribute__((address_space(1)))* g32;
-    sraw = *(g32)(sc + sidx);  // sidx is even: both scales in one dword
+    // the scales of the half's two groups (tiles tile + 2hw + u), low half first
+    typedef const uint16_t __attribute__((address_space(1)))* g16;
+    sraw = (uint32_t)*(g16)(sc + scale_idx(tile + 2 * hw, lane)) |
+           ((uint32_t)*(g16)(sc + scale_idx(tile + 2 * hw + 1, lane)) << 16);
   }
   __device__ __forceinline__ void expand(int hw, int scale_f16, _Float16* wr) const {
     const half2v z = {(_Float16)-1032.f, (_Float16)-1032.f};
@@ -295,8 +295,7 @@ template <>
 struct StepLoad<kQ4G128> {
   uint32_t w[8];
   uint32_t sraw;
-  __device__ __forceinline__ void load(gbytes_t mat, int64_t tile, int lane, int hw, gu16_t sc,
-                                       int64_t sidx) {
+  __device__ __forceinline__ void load(gbytes_t mat, int64_t tile, int lane, int hw, gu16_t sc) {
     typedef const u32x4p __attribute__((address_space(1)))* g4;
     const gbytes_t base = mat + tile * 4 * 1024 + 16 * lane + 2048 * hw;
     const u32x4p a = *(g4)(base);
@@ -304,7 +303,7 @@ struct StepLoad<kQ4G128> {
     w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
     w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
     typedef const uint16_t __attribute__((address_space(1)))* g16;
-    sraw = *(g16)(sc + sidx);
+    sraw = *(g16)(sc + scale_idx(tile, lane));
   }
   __device__ __forceinline__ void expand(int hw, int scale_f16, _Float16* wr) const {
     const _Float16 s = scale_f16 ? __builtin_bit_cast(_Float16, (uint16_t)sraw)
@@ -328,13 +327,12 @@ template <>
 struct StepLoad<kQ2G128> {
   uint32_t w[4];
   uint32_t sraw;
-  __device__ __forceinline__ void load(gbytes_t mat, int64_t tile, int lane, int hw, gu16_t sc,
-                                       int64_t sidx) {
+  __device__ __forceinline__ void load(gbytes_t mat, int64_t tile, int lane, int hw, gu16_t sc) {
     typedef const u32x4p __attribute__((address_space(1)))* g4;
     const u32x4p a = *(g4)(mat + tile * 2 * 1024 + 16 * lane + 1024 * hw);
     w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
     typedef const uint16_t __attribute__((address_space(1)))* g16;
-    sraw = *(g16)(sc + sidx);
+    sraw = *(g16)(sc + scale_idx(tile, lane));
   }
   __device__ __forceinline__ void expand(int hw, int scale_f16, _Float16* wr) const {
     const _Float16 s = scale_f16 ? __builtin_bit_cast(_Float16, (uint16_t)sraw)
@@ -421,7 +419,6 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(
   const int ng = H / C::G;
   const int gps = kPK / C::G;  // groups per step
   const int64_t tile0 = (int64_t)nt * ng;
-  const int64_t srow = (int64_t)(nt * 64 + wrow) * ng;
   _Float16* wr = wsm + (m * kGuN + wrow) * kLdsRow;
 
   const int wm = wv >> 1, wn = wv & 1;
@@ -444,7 +441,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(
   auto issue = [&](int st, int b) {
     const int g = st * gps;
     xl[b].load(x16, roff, st * kPK);
-    wl[b].load(mat, tile0 + g, wrow, hw, msc, srow + g + (C::G == 32 ? 2 * hw : 0));
+    wl[b].load(mat, tile0 + g, wrow, hw, msc);
   };
   auto compute = [&]() {
 #pragma unroll
@@ -543,7 +540,6 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(
   const int gps = kPK / C::G;
   const int trow = nt * 2 + tl;  // 64-row tile index of the matrix
   const int64_t tile0 = (int64_t)trow * ng;
-  const int64_t srow = (int64_t)(trow * 64 + wrow) * ng;
   _Float16* wr = wsm + (tl * 64 + wrow) * kLdsRow;
 
   const int wm = wv >> 1, wn = wv & 1;
@@ -561,7 +557,7 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(
   auto issue = [&](int st, int b) {
     const int g = st * gps;
     xl[b].load(h16, roff, st * kPK);
-    wl[b].load(mat, tile0 + g, wrow, hw, msc, srow + g + (C::G == 32 ? 2 * hw : 0));
+    wl[b].load(mat, tile0 + g, wrow, hw, msc);
   };
   auto compute = [&]() {
 #pragma unroll

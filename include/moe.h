@@ -39,8 +39,10 @@
  *                               off = {1, 4, 7, 10, 13};
  *                               P >= 60, m = P - 60: bit b of c is bit 16h of
  *                               w[3m + b].
- *   scales region: at the next 256-byte boundary after the codes, row-major
- *     [N][Kd/G] 16-bit scales; the matrix blob ends at the following 256-byte
+ *   scales region: at the next 256-byte boundary after the codes, in the codes'
+ *     tile order: tile t = (n/64)*(Kd/G) + g holds the 64 16-bit scales of its
+ *     rows, scale s[n][g] at index t*64 + n%64 (one wave's scales of a tile are
+ *     128 contiguous bytes); the matrix blob ends at the following 256-byte
  *     boundary.  Blobs must be 256-byte aligned.
  * An expert is three blobs: gate [I][H], up [I][H], down [H][I].  At H = 5120,
  * I = 1536, 3-bit G = 128 an expert is 9,216,000 bytes (3.125 bits per weight).

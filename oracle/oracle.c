@@ -36,7 +36,8 @@
  * bits*G/8 bytes split into C = bits*G/128 chunks of 16 bytes: chunk j of tile t
  * starts at byte (t*C + j)*1024 and unit u's part of it at +16u; the unit's
  * 32-bit little-endian words are the chunks' words in order.  Scales follow at
- * the next 256-byte boundary as a row-major [N][Kd/G] array.
+ * the next 256-byte boundary in the same tile order: tile t holds the 64 scales
+ * of its rows, s[n][g] at index t*64 + n%64.
  * Code i of a unit (reduction index g*G + i), P = i/2, half h = i%2:
  *   4-bit, G = 32 or 128 (4 or 16 words): c = (w[P/4] >> (16h + 4*(P%4))) & 15
  *   2-bit, G = 128 (8 words):  c = (w[P/8] >> (16h + 2*(P%8))) & 3
@@ -154,7 +155,8 @@ double orc_scale(const uint8_t* blob, int rows, int cols, int bits, int group, i
                  int n, int g) {
   orc_mat m = {rows, cols, bits, group, scale_f16};
   int ng = cols / group;
-  int64_t off = orc_align256(orc_codes_bytes(&m)) + 2 * ((int64_t)n * ng + g);
+  /* scales in tile order: tile (n/64)*ng + g, 64 scales, row n%64 within it */
+  int64_t off = orc_align256(orc_codes_bytes(&m)) + 2 * (((int64_t)(n / 64) * ng + g) * 64 + n % 64);
   uint16_t s;
   memcpy(&s, blob + off, 2);
   return scale_f16 ? orc_f16_to_double(s) : orc_bf16_to_double(s);

@@ -342,8 +342,9 @@ def pack_matrix(codes: np.ndarray, scales_u16: np.ndarray, bits: int, group: int
     words = words.reshape(N // 64, ng, 64, C, 4).transpose(0, 1, 3, 2, 4)
     blob = np.zeros(lay.nbytes, dtype=np.uint8)
     blob[:lay.codes_bytes] = np.ascontiguousarray(words).view(np.uint8).reshape(-1)
-    sc = np.ascontiguousarray(scales_u16, dtype=np.uint16).reshape(N * ng)
-    blob[lay.scales_off:lay.scales_off + lay.scales_bytes] = sc.view(np.uint8)
+    # scales in tile order: tile (rb, g) holds the scales of its 64 rows
+    sc = np.asarray(scales_u16, dtype=np.uint16).reshape(N // 64, 64, ng).transpose(0, 2, 1)
+    blob[lay.scales_off:lay.scales_off + lay.scales_bytes] = np.ascontiguousarray(sc).view(np.uint8).reshape(-1)
     return blob
 
 

@@ -84,6 +84,24 @@ def test_packer_roundtrip_and_tiles(bits, G, N, Kd):
     assert np.array_equal(W, ref)
 
 
+@pytest.mark.parametrize("bits,G,N,Kd", [(3, 128, 192, 384), (4, 32, 128, 96)])
+def test_scale_tile_order(bits, G, N, Kd):
+    """the scale stored at scales_off + 2*(t*64 + u) (tile t = (n/64)*ng + g,
+    u = n % 64) is the scale of row n and group g, and of no other (row, group)"""
+    lay = synth.matrix_layout(N, Kd, bits, G)
+    ng = Kd // G
+    one = 0x3F80  # bf16 1.0
+    for n, g in [(0, 0), (1, 0), (63, ng - 1), (64, 0), (N - 1, ng - 1), (70, ng // 2)]:
+        blob = np.zeros(lay.nbytes, dtype=np.uint8)
+        t, u = (n // 64) * ng + g, n % 64
+        off = lay.scales_off + 2 * (t * 64 + u)
+        blob[off:off + 2] = np.array([one], dtype=np.uint16).view(np.uint8)
+        for nn in range(N):
+            for gg in range(ng):
+                want = 1.0 if (nn, gg) == (n, g) else 0.0
+                assert oracle.scale(blob, N, Kd, bits, G, False, nn, gg) == want, (n, g, nn, gg)
+
+
 def test_tile_chunk_addressing():
     """a bit set in chunk j of tile t at lane u lands in row 64*(t // ng) + u,
     group t % ng"""
