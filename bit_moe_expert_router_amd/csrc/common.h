@@ -285,14 +285,23 @@ __device__ __forceinline__ float wave_sum_uniform(float v) {
 }
 
 // ---------------------------------------------------------------- cross-block hand-off
-// Kernels whose last-arriving block finishes the work.  The blocks' results go
-// out as agent-scope relaxed atomic stores (written through to the memory side
-// that every compute unit shares), each block waits until its own stores have
-// completed (vmcnt(0)) before it takes its ticket, and the last block reads the
-// results with agent-scope loads (which do not hit stale L2 lines).  There is
-// no cache-wide fence: a device-scope __threadfence() writes back and
+// Kernels whose last-arriving block finishes the work.  The ordering argument:
+// (1) the blocks' results go out as agent-scope relaxed atomic stores, emitted
+// with the agent-scope cache policy, i.e. written through the XCD's L2 to the
+// memory side that every XCD shares; (2) each wave waits until its own stores
+// have completed (vmcnt(0): a write-through store retires when the coherence
+// point acknowledges it), and a block barrier orders all four waves before
+// thread 0 (3) takes its ticket, an agent-scope atomic add performed at that
+// same coherence point, whose total order puts every other block's completed
+// stores before the last ticket; (4) the last block reads the results with
+// agent-scope atomic loads, which are not served from its own L2 and so cannot
+// see a stale line; (5) the signal fences around the wait and the branch on the
+// ticket (read back through LDS after a barrier) keep the compiler from moving
+// the stores after, or the loads before, these points.  There is no cache-wide
+// fence: a device-scope __threadfence() (or an acq_rel ticket) writes back and
 // invalidates the block's whole L2, microseconds per block when hundreds of
-// blocks do it.
+// blocks do it, and orders nothing more here since every datum the hand-off
+// carries is itself written and read at agent scope.
 template <typename T>
 __device__ __forceinline__ void st_coherent(T* p, T v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
