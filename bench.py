@@ -94,6 +94,9 @@ def parse():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--stack-calls", choices=("fused", "three"), default="fused",
+                    help="stack workloads: one moe_stack_layer call per layer (default), or "
+                         "moe_rmsnorm_bf16 + moe_route + moe_forward")
     return ap.parse_args()
 
 
@@ -205,7 +208,7 @@ def run_workload(name, a, dev, cpu_budget, main_tokens=None, one_thread=True):
     gen_s = time.time() - t0
 
     if stack:
-        from bit_moe_expert_router_amd.layer import stack_forward
+        from bit_moe_expert_router_amd.layer import stack_forward, stack_forward_fused
         resid = torch.from_numpy(
             synth.normal_f32(T * cfg.hidden, cfg.seed, 0, synth.SYN_X, 1.0).reshape(T, cfg.hidden)).to(dev)
         ybuf = torch.empty((T, cfg.hidden), dtype=torch.int16, device=dev)
@@ -214,7 +217,10 @@ def run_workload(name, a, dev, cpu_budget, main_tokens=None, one_thread=True):
 
     def step(l):
         if stack:  # one pass through every layer of the stack
-            stack_forward(ml, resid, out, routers, biases, ybuf, out)
+            if a.stack_calls == "fused":
+                stack_forward_fused(ml, resid, routers, biases, ybuf, out)
+            else:
+                stack_forward(ml, resid, out, routers, biases, ybuf, out)
             return
         dl = layers[l]
         r = ml.route(xd, dl.router, dl.bias)
@@ -225,8 +231,8 @@ def run_workload(name, a, dev, cpu_budget, main_tokens=None, one_thread=True):
     if stack:
         out.zero_()
         seen = []
-        stack_forward(ml, resid, out, routers, biases, ybuf, out,
-                      on_layer=lambda l, y_, r, o_: seen.append(r.expert_offsets.clone()))
+        stack_forward_fused(ml, resid, routers, biases, ybuf, out,
+                            on_layer=lambda l, y_, r, o_: seen.append(r.expert_offsets.clone()))
         torch.cuda.synchronize()
         U = [int((np.diff(o.cpu().numpy()) > 0).sum()) for o in seen]
     else:
@@ -306,6 +312,9 @@ def run_workload(name, a, dev, cpu_budget, main_tokens=None, one_thread=True):
            "distinct_experts_per_layer": round(u_mean, 2), "layers_rotated": L,
            "graph_replay": graphs is not None, "steps_per_graph": G if graphs is not None else None,
            "input_gen_s": round(gen_s, 1)}
+    if stack:
+        res["stack_calls"] = ("one moe_stack_layer call per layer" if a.stack_calls == "fused"
+                              else "moe_rmsnorm_bf16 + moe_route + moe_forward per layer")
     roof = None
     if kern:
         us = {k: v[0] / v[1] * 1e3 for k, v in kern.items() if v[1]}

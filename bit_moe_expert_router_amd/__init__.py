@@ -41,7 +41,8 @@ EXPORTS = ("moe_create", "moe_destroy", "moe_workspace_bytes", "moe_workspace_in
            "set_expert_table", "moe_expert_table_device", "moe_set_shared", "moe_route",
            "moe_forward", "moe_forward_noalloc", "moe_rmsnorm_bf16", "moe_last_error",
            "moe_profile_enable", "moe_profile_read", "moe_host_arena_create",
-           "moe_host_arena_destroy", "moe_cache_state_bytes", "moe_cache_init", "moe_cache_step")
+           "moe_host_arena_destroy", "moe_cache_state_bytes", "moe_cache_init", "moe_cache_step",
+           "moe_stack_layer")
 MOE_CACHE_LFU, MOE_CACHE_CLOCK = 0, 1
 
 
@@ -68,6 +69,8 @@ def _load():
                                 ctypes.c_size_t, vp]
     lib.moe_forward_noalloc.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_rmsnorm_bf16.argtypes = [vp, vp, vp, i32, ctypes.c_float, vp, vp]
+    lib.moe_stack_layer.argtypes = [vp, i32, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp,
+                                    vp, vp, vp, ctypes.c_size_t, vp]
     lib.moe_host_arena_create.argtypes = [ctypes.c_size_t, ctypes.POINTER(vp), ctypes.POINTER(vp)]
     lib.moe_host_arena_destroy.argtypes = [vp]
     lib.moe_cache_state_bytes.argtypes = [vp, i32]
@@ -85,7 +88,7 @@ def _load():
     for f in ("moe_create", "moe_destroy", "moe_workspace_init", "set_expert_table",
               "moe_set_shared", "moe_route", "moe_forward", "moe_forward_noalloc",
               "moe_rmsnorm_bf16", "moe_host_arena_create", "moe_host_arena_destroy",
-              "moe_cache_init", "moe_cache_step"):
+              "moe_cache_init", "moe_cache_step", "moe_stack_layer"):
         getattr(lib, f).restype = st
     return lib
 
@@ -237,6 +240,16 @@ def moe_rmsnorm_bf16(ctx: int, resid, add, T: int, eps: float, y_bf16, stream=No
     _check(lib.moe_rmsnorm_bf16(ctx, _ptr(resid), _ptr(add), T, eps, _ptr(y_bf16),
                                 _stream(stream)),
            "moe_rmsnorm_bf16")
+
+
+def moe_stack_layer(ctx: int, layer: int, resid, T: int, eps: float, w_router, bias, topk_ids,
+                    topk_w, expert_offsets, sorted_pairs, pair_pos, xn_bf16, out, ws,
+                    stream=None):
+    _check(lib.moe_stack_layer(ctx, layer, _ptr(resid), T, eps, _ptr(w_router), _ptr(bias),
+                               _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets),
+                               _ptr(sorted_pairs), _ptr(pair_pos), _ptr(xn_bf16), _ptr(out),
+                               _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_stack_layer")
 
 
 from .layer import MoELayer, RoutingBuffers  # noqa: E402,F401

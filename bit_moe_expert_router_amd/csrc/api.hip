@@ -228,10 +228,11 @@ moe_status moe_route(moe_ctx* ctx, const void* x_bf16, int32_t T, const float* w
   if (ws_bytes < (size_t)L.total)
     return fail(MOE_E_ARG, "moe_route: workspace %zu bytes < %lld needed", ws_bytes, (long long)L.total);
   uint8_t* w8 = (uint8_t*)ws;
-  hipError_t e = moe::launch_route(c, (const uint16_t*)x_bf16, T, w_router, bias, topk_ids, topk_w,
-                                   expert_offsets, sorted_pairs, pair_pos,
-                                   (double*)(w8 + L.logits), (int32_t*)(w8 + L.ghist),
-                                   (int32_t*)(w8 + L.counters), (hipStream_t)stream);
+  const moe::RouteIn in{(const uint16_t*)x_bf16, nullptr, 0.f, nullptr};
+  hipError_t e = moe::launch_route(c, in, T, w_router, bias, topk_ids, topk_w, expert_offsets,
+                                   sorted_pairs, pair_pos, (double*)(w8 + L.logits),
+                                   (int32_t*)(w8 + L.ghist), (int32_t*)(w8 + L.counters),
+                                   (hipStream_t)stream);
   return hip_status(e, "moe_route launch");
 }
 
@@ -242,7 +243,8 @@ namespace {
 moe_status forward_impl(const char* who, moe_ctx* ctx, int32_t layer, const void* x_bf16,
                         int32_t T, const int32_t* topk_ids, const float* topk_w,
                         const int32_t* expert_offsets, const int32_t* sorted_pairs, float* out,
-                        float* pair_out, void* ws, size_t ws_bytes, moe_stream_t stream) {
+                        float* pair_out, void* ws, size_t ws_bytes, moe_stream_t stream,
+                        float* resid = nullptr) {
   if (!ctx) return fail(MOE_E_ARG, "%s: null context", who);
   const moe_cfg& c = ctx->cfg;
   if (layer < 0 || layer >= ctx->n_layers) return fail(MOE_E_ARG, "%s: bad layer %d", who, layer);
@@ -259,7 +261,7 @@ moe_status forward_impl(const char* who, moe_ctx* ctx, int32_t layer, const void
   const moe_ctx::Shared& sh = ctx->shared[layer];
   moe::FwdArgs f{&c, ctx->d_tables + (size_t)layer * c.n_experts, sh.g, sh.u, sh.d,
                  (const uint16_t*)x_bf16, T, topk_ids, topk_w, expert_offsets, sorted_pairs,
-                 out, pair_out, (uint8_t*)ws, ctx->side, ctx->ev_fork, ctx->ev_join};
+                 out, pair_out, resid, (uint8_t*)ws, ctx->side, ctx->ev_fork, ctx->ev_join};
   return hip_status(moe::launch_forward(f, (hipStream_t)stream), who);
 }
 
@@ -291,6 +293,42 @@ moe_status moe_forward_noalloc(moe_ctx* ctx, int32_t layer, const void* x_bf16, 
   return forward_impl("moe_forward_noalloc", ctx, layer, x_bf16, T, topk_ids, topk_w,
                       expert_offsets, sorted_pairs, out, pair_out, ctx->scratch, kNoAllocBytes,
                       stream);
+}
+
+moe_status moe_stack_layer(moe_ctx* ctx, int32_t layer, float* resid, int32_t T, float eps,
+                           const float* w_router, const float* bias, int32_t* topk_ids,
+                           float* topk_w, int32_t* expert_offsets, int32_t* sorted_pairs,
+                           int32_t* pair_pos, void* xn_bf16, float* out, void* ws,
+                           size_t ws_bytes, moe_stream_t stream) {
+  if (!ctx) return fail(MOE_E_ARG, "moe_stack_layer: null context");
+  const moe_cfg& c = ctx->cfg;
+  if (layer < 0 || layer >= ctx->n_layers) return fail(MOE_E_ARG, "moe_stack_layer: bad layer %d", layer);
+  if (T < 0 || T > c.max_tokens)
+    return fail(MOE_E_ARG, "moe_stack_layer: T=%d outside [0, %d]", T, c.max_tokens);
+  if (!ctx->table_set[layer])
+    return fail(MOE_E_STATE, "moe_stack_layer: expert table of layer %d never set", layer);
+  if (!(eps >= 0.f) || eps > 1.f) return fail(MOE_E_ARG, "moe_stack_layer: eps must be in [0, 1]");
+  if (T == 0) return ok();
+  if (!resid || !w_router || !topk_ids || !topk_w || !expert_offsets || !sorted_pairs || !pair_pos ||
+      !xn_bf16 || !out || !ws)
+    return fail(MOE_E_ARG, "moe_stack_layer: null pointer argument");
+  if (!aligned(resid, 16) || !aligned(w_router, 16) || !aligned(xn_bf16, 16) || !aligned(out, 16) ||
+      !aligned(ws, 256))
+    return fail(MOE_E_ARG,
+                "moe_stack_layer: resid, w_router, xn_bf16, out must be 16-byte aligned, ws 256-byte aligned");
+  const moe::WsLayout L = moe::ws_layout(c, T);
+  if (ws_bytes < (size_t)L.total)
+    return fail(MOE_E_ARG, "moe_stack_layer: workspace %zu bytes < %lld needed", ws_bytes,
+                (long long)L.total);
+  uint8_t* w8 = (uint8_t*)ws;
+  const moe::RouteIn in{nullptr, resid, eps, (uint16_t*)xn_bf16};
+  const hipError_t e = moe::launch_route(c, in, T, w_router, bias, topk_ids, topk_w, expert_offsets,
+                                         sorted_pairs, pair_pos, (double*)(w8 + L.logits),
+                                         (int32_t*)(w8 + L.ghist), (int32_t*)(w8 + L.counters),
+                                         (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "moe_stack_layer routing");
+  return forward_impl("moe_stack_layer", ctx, layer, xn_bf16, T, topk_ids, topk_w, expert_offsets,
+                      sorted_pairs, out, nullptr, ws, ws_bytes, stream, resid);
 }
 
 moe_status moe_host_arena_create(size_t bytes, void** host, void** device) {

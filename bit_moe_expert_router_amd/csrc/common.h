@@ -284,6 +284,38 @@ __device__ __forceinline__ float wave_sum_uniform(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// ---------------------------------------------------------------- RMSNorm (unit gain)
+// y = bf16(x / sqrt(mean(x^2) + eps)) of a row of H fp32 (H % 4 == 0, H <= 8192)
+// by a block of 256 threads: thread i holds float4 items i + 256*j (j ascending)
+// and sums their squares by fused multiply-adds in component order; the wave
+// sums are xor-shuffle reductions, and the four waves' sums are added in wave
+// order.  The normalisation kernel and the routing kernels that normalise their
+// own input all use these functions, so they produce the same bf16 rows.
+constexpr int kRnPieces = 8;
+typedef float rn_f4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float rms_wave_sum(const rn_f4 (&v)[kRnPieces], int H4) {
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRnPieces; ++i)
+    if ((int)threadIdx.x + 256 * i < H4) {
+      ss = fmaf(v[i].x, v[i].x, ss);
+      ss = fmaf(v[i].y, v[i].y, ss);
+      ss = fmaf(v[i].z, v[i].z, ss);
+      ss = fmaf(v[i].w, v[i].w, ss);
+    }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+  return ss;
+}
+// part[w] = wave w's sum
+__device__ __forceinline__ float rms_inv(const float* part, int H, float eps) {
+  const float tot = ((part[0] + part[1]) + part[2]) + part[3];
+  return 1.f / sqrtf(tot / (float)H + eps);
+}
+__device__ __forceinline__ uint32_t rms_bf16x2(float a, float b, float inv) {
+  return f32_to_bf16_rne(a * inv) | ((uint32_t)f32_to_bf16_rne(b * inv) << 16);
+}
+
 // ---------------------------------------------------------------- cross-block hand-off
 // Kernels whose last-arriving block finishes the work.  The ordering argument:
 // (1) the blocks' results go out as agent-scope relaxed atomic stores, emitted
@@ -544,6 +576,7 @@ struct FwdArgs {
   const int32_t* sorted_pairs;
   float* out;
   float* pair_out;              // null: workspace
+  float* resid;                 // or null: resid[t] += out[t] as the combine writes out[t]
   uint8_t* ws;
   hipStream_t side;             // shared-expert stream, fork and join events (or null)
   hipEvent_t ev_fork, ev_join;
@@ -554,7 +587,15 @@ hipError_t launch_decode(const FwdArgs& f, const WsLayout& L, float* shared_out,
                          hipEvent_t join, hipStream_t s);
 hipError_t launch_shared(const FwdArgs& f, const WsLayout& L, hipStream_t s, float** out,
                          int* nslices);
-hipError_t launch_route(const moe_cfg& c, const uint16_t* x, int T, const float* wr,
+// the routing input: bf16 rows x, or (resid != null) x = bf16(RMSNorm(resid)),
+// formed by the routing kernels themselves and written to xn
+struct RouteIn {
+  const uint16_t* x;
+  const float* resid;
+  float eps;
+  uint16_t* xn;
+};
+hipError_t launch_route(const moe_cfg& c, const RouteIn& in, int T, const float* wr,
                         const float* bias, int32_t* ids, float* w, int32_t* offsets,
                         int32_t* sorted_pairs, int32_t* pair_pos, double* logits,
                         int32_t* ghist, int32_t* counters, hipStream_t s);

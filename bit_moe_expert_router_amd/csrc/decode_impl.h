@@ -783,7 +783,7 @@ constexpr int kCombineMaxK = 16;
 __device__ __forceinline__ void combine_strip(const float* y, const int32_t* __restrict__ ids,
                                               const float* __restrict__ w, int K, int E, int H,
                                               const float* shared, int nsh, int T, int strip,
-                                              float* __restrict__ out) {
+                                              float* __restrict__ out, float* __restrict__ resid) {
   const int t = threadIdx.x >> 6;
   if (t >= T) return;
   const int n = strip * 64 + (threadIdx.x & 63);
@@ -805,6 +805,7 @@ __device__ __forceinline__ void combine_strip(const float* y, const int32_t* __r
     acc += sh;
   }
   out[(int64_t)t * H + n] = acc;
+  if (resid) resid[(int64_t)t * H + n] += acc;  // a stack layer: the residual update
 }
 
 // h of the wave's groups for up to XT positions, formed from the KP gate and up
@@ -867,7 +868,8 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
     const int32_t* __restrict__ sorted_pairs, int H, int I, int P, int scale_f16,
     const float* __restrict__ part, float* pair_out, const int32_t* __restrict__ ids,
     const float* __restrict__ wts, int K, int T, const float* shared, int nsh,
-    int32_t* __restrict__ ctr, int32_t* __restrict__ ctr0, float* __restrict__ out) {
+    int32_t* __restrict__ ctr, int32_t* __restrict__ ctr0, float* __restrict__ out,
+    float* __restrict__ resid) {
   using C = UnitCodec<CODEC>;
   using HS = HFromParts<CODEC, GPW, XT, KP>;
   constexpr int XW = XT * GPW * 2 * C::PAIRS;  // uint32 per wave: [token][group][hi|lo][pair]
@@ -886,7 +888,7 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
   if (!act.ok) return;  // inconsistent caller routing: the outputs are left untouched
   if (act.e < 0) {  // no expert for this block; with none at all, block 0 combines
     if (out && act.U == 0 && blockIdx.x == 0)
-      combine_strip(pair_out, ids, wts, K, E, H, shared, nsh, T, strip, out);
+      combine_strip(pair_out, ids, wts, K, E, H, shared, nsh, T, strip, out, resid);
     return;
   }
   const int seg0 = __builtin_amdgcn_readfirstlane(act.seg0);
@@ -991,7 +993,7 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
     MOE_TR(tb + 4);
     lds_barrier();
     if (s_last) {
-      combine_strip(pair_out, ids, wts, K, E, H, shared, nsh, T, strip, out);
+      combine_strip(pair_out, ids, wts, K, E, H, shared, nsh, T, strip, out, resid);
       if (threadIdx.x == 0) st_coherent(ctr + strip, 0);
       MOE_TR(tb + 5);
     }
@@ -1070,7 +1072,8 @@ __global__ __launch_bounds__(256) void k_combine_parts(const float* __restrict__
                                                        int nsh, int T,
                                                        const int32_t* __restrict__ call_bad,
                                                        float* __restrict__ out,
-                                                       float* __restrict__ pair_out) {
+                                                       float* __restrict__ pair_out,
+                                                       float* __restrict__ resid) {
   const int t = blockIdx.y;
   const int n = min((int)(blockIdx.x * 256 + threadIdx.x), H - 1);
   float y[KM][MC];
@@ -1099,7 +1102,10 @@ __global__ __launch_bounds__(256) void k_combine_parts(const float* __restrict__
     for (int q = 0; q < nsh; ++q) sh += shared[((int64_t)q * T + t) * H + n];
     acc += sh;
   }
-  if (in && !bad) out[(int64_t)t * H + n] = acc;
+  if (in && !bad) {
+    out[(int64_t)t * H + n] = acc;
+    if (resid) resid[(int64_t)t * H + n] += acc;  // a stack layer: the residual update
+  }
 }
 
 // ---------------------------------------------------------------- launcher
@@ -1170,7 +1176,7 @@ hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* shared_ou
   case N:                                                                                        \
     MOE_LAUNCH(KID_DOWN, (k_down_blk<CODEC, N, 2, KPT>), dim3(maxU, H / 64), dim3(64 * kDNWaves), \
                0, s, f.table, E, f.offsets, f.sorted_pairs, H, I, P, c.scale_f16, gpart, y,      \
-               f.ids, f.w, K, T, shared_out, nsh, ctr, ctr0, cout);                              \
+               f.ids, f.w, K, T, shared_out, nsh, ctr, ctr0, cout, f.resid);                     \
     break;
 #define MOE_DN_KP(KPT)                                                                           \
     switch (gpw_dn) {                                                                            \
@@ -1191,10 +1197,10 @@ hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* shared_ou
     // y holds every pair's output in pair order: a single "chunk"
     if (K <= 8) {
       MOE_LAUNCH(KID_COMBINE, (k_combine_parts<8, 1>), dim3((H + 255) / 256, T), dim3(256), 0, s, y,
-                 1, P, f.ids, f.w, K, E, H, shared_out, nsh, T, call_bad, f.out, nullptr);
+                 1, P, f.ids, f.w, K, E, H, shared_out, nsh, T, call_bad, f.out, nullptr, f.resid);
     } else {
       MOE_LAUNCH(KID_COMBINE, (k_combine_parts<16, 1>), dim3((H + 255) / 256, T), dim3(256), 0, s,
-                 y, 1, P, f.ids, f.w, K, E, H, shared_out, nsh, T, call_bad, f.out, nullptr);
+                 y, 1, P, f.ids, f.w, K, E, H, shared_out, nsh, T, call_bad, f.out, nullptr, f.resid);
     }
     return hipGetLastError();
   }
@@ -1224,7 +1230,7 @@ hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* shared_ou
   // MC: chunks of the down reduction read per pair (I/G <= 32 groups, 3 per chunk)
 #define MOE_CMB(KM, MC)                                                                        \
   MOE_LAUNCH(KID_COMBINE, (k_combine_parts<KM, MC>), dim3((H + 255) / 256, T), dim3(256), 0, s, \
-             dpart, nch_dn, P, f.ids, f.w, K, E, H, shared_out, nsh, T, call_bad, f.out, f.pair_out)
+             dpart, nch_dn, P, f.ids, f.w, K, E, H, shared_out, nsh, T, call_bad, f.out, f.pair_out, f.resid)
   if (K <= 8) {
     if (nch_dn <= 4) MOE_CMB(8, 4); else MOE_CMB(8, 12);
   } else {

@@ -31,7 +31,8 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ pair_
                                                  const float* __restrict__ w, int K, int E, int H,
                                                  const float* __restrict__ shared, int nsh, int T,
                                                  const int32_t* __restrict__ call_bad,
-                                                 float* __restrict__ out) {
+                                                 float* __restrict__ out,
+                                                 float* __restrict__ resid) {
   const int t = blockIdx.y;
   const int n = min((int)(blockIdx.x * 256 + threadIdx.x), H - 1);
   float y[KM];
@@ -49,7 +50,10 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ pair_
     acc += sh;
   }
   // inconsistent caller routing: the output is left untouched
-  if (blockIdx.x * 256 + threadIdx.x < H && !call_bad[0]) out[(int64_t)t * H + n] = acc;
+  if (blockIdx.x * 256 + threadIdx.x < H && !call_bad[0]) {
+    out[(int64_t)t * H + n] = acc;
+    if (resid) resid[(int64_t)t * H + n] += acc;  // a stack layer: the residual update
+  }
 }
 
 // ---------------------------------------------------------------- shared expert
@@ -264,24 +268,21 @@ hipError_t launch_shared(const FwdArgs& f, const WsLayout& L, hipStream_t s, flo
 // order reduction.  One block per token; each thread requests all of its 16-byte pieces of the
 // residual (and of the addend) at once, so the kernel is one memory round trip
 // deep: H/4 pieces over 256 threads, at most kRnPieces per thread (H <= 8192).
-constexpr int kRnPieces = 8;
-
 __global__ __launch_bounds__(256) void k_rmsnorm(float* __restrict__ resid,
                                                  const float* __restrict__ add, int H, float eps,
                                                  uint16_t* __restrict__ y) {
-  typedef float f4 __attribute__((ext_vector_type(4)));
   const int t = blockIdx.x;
   const int H4 = H / 4;
-  f4* r = reinterpret_cast<f4*>(resid + (int64_t)t * H);
-  const f4* ad = add ? reinterpret_cast<const f4*>(add + (int64_t)t * H) : nullptr;
-  f4 v[kRnPieces];
+  rn_f4* r = reinterpret_cast<rn_f4*>(resid + (int64_t)t * H);
+  const rn_f4* ad = add ? reinterpret_cast<const rn_f4*>(add + (int64_t)t * H) : nullptr;
+  rn_f4 v[kRnPieces];
 #pragma unroll
   for (int i = 0; i < kRnPieces; ++i) {
     const int q = min((int)threadIdx.x + 256 * i, H4 - 1);
     v[i] = r[q];
   }
   if (ad) {
-    f4 a[kRnPieces];
+    rn_f4 a[kRnPieces];
 #pragma unroll
     for (int i = 0; i < kRnPieces; ++i) a[i] = ad[min((int)threadIdx.x + 256 * i, H4 - 1)];
 #pragma unroll
@@ -291,31 +292,16 @@ __global__ __launch_bounds__(256) void k_rmsnorm(float* __restrict__ resid,
       if (q < H4) r[q] = v[i];
     }
   }
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < kRnPieces; ++i)
-    if ((int)threadIdx.x + 256 * i < H4) {
-      ss = fmaf(v[i].x, v[i].x, ss);
-      ss = fmaf(v[i].y, v[i].y, ss);
-      ss = fmaf(v[i].z, v[i].z, ss);
-      ss = fmaf(v[i].w, v[i].w, ss);
-    }
+  const float ss = rms_wave_sum(v, H4);
   __shared__ float part[4];
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
   __syncthreads();
-  const float tot = ((part[0] + part[1]) + part[2]) + part[3];
-  const float inv = 1.f / sqrtf(tot / (float)H + eps);
+  const float inv = rms_inv(part, H, eps);
   uint2* yo = reinterpret_cast<uint2*>(y + (int64_t)t * H);
 #pragma unroll
   for (int i = 0; i < kRnPieces; ++i) {
     const int q = threadIdx.x + 256 * i;
-    if (q < H4) {
-      const uint32_t lo = f32_to_bf16_rne(v[i].x * inv) | ((uint32_t)f32_to_bf16_rne(v[i].y * inv) << 16);
-      const uint32_t hi = f32_to_bf16_rne(v[i].z * inv) | ((uint32_t)f32_to_bf16_rne(v[i].w * inv) << 16);
-      yo[q] = make_uint2(lo, hi);
-    }
+    if (q < H4) yo[q] = make_uint2(rms_bf16x2(v[i].x, v[i].y, inv), rms_bf16x2(v[i].z, v[i].w, inv));
   }
 }
 
@@ -387,10 +373,10 @@ hipError_t launch_forward(const FwdArgs& f, hipStream_t s) {
   const int32_t* call_bad = reinterpret_cast<const int32_t*>(f.ws + L.counters) + kCtrCallBad;
   if (K <= 8) {
     MOE_LAUNCH(KID_COMBINE, k_combine<8>, dim3((H + 255) / 256, T), dim3(256), 0, s, pair_out,
-               f.ids, f.w, K, E, H, sh_out, nsh, T, call_bad, f.out);
+               f.ids, f.w, K, E, H, sh_out, nsh, T, call_bad, f.out, f.resid);
   } else {
     MOE_LAUNCH(KID_COMBINE, k_combine<16>, dim3((H + 255) / 256, T), dim3(256), 0, s, pair_out,
-               f.ids, f.w, K, E, H, sh_out, nsh, T, call_bad, f.out);
+               f.ids, f.w, K, E, H, sh_out, nsh, T, call_bad, f.out, f.resid);
   }
   return hipGetLastError();
 }

@@ -158,6 +158,107 @@ __device__ __forceinline__ void logits_multi_block(const uint16_t* __restrict__ 
   }
 }
 
+// ---------------------------------------------------------------- logits of normalised rows
+// The logits of experts e0 .. e0+EPB-1 for tokens t0 .. t0+NT-1 of x =
+// bf16(RMSNorm(resid)), the normalisation done in the block: thread tid holds the
+// float4 items tid + 256*j of each token's fp32 row, which are also the items it
+// takes in the logit sums; the squares are summed exactly as the normalisation
+// kernel sums them (rms_wave_sum, rms_inv), and the bf16 values it forms enter the
+// same logit arithmetic, in the same order, as the two blocks above.  So the
+// logits equal those of the plain kernels on the normalisation kernel's output,
+// bit for bit.  Blocks of the first expert chunk also store the bf16 rows to xn
+// (the experts' input).  H <= 8192.
+template <int NT, int EPB>
+__device__ __forceinline__ void logits_norm_block(const float* __restrict__ resid, float eps,
+                                                  uint16_t* __restrict__ xn, int T, int H, int E,
+                                                  const float* __restrict__ wr,
+                                                  const float* __restrict__ bias,
+                                                  double* __restrict__ logits, int e0, int t0) {
+  const int H4 = H / 4;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // router items first: they do not depend on the normalisation
+  float4 w[EPB][kRnPieces];
+#pragma unroll
+  for (int i = 0; i < kRnPieces; ++i) {
+    const int q = min(tid + 256 * i, H4 - 1);
+#pragma unroll
+    for (int j = 0; j < EPB; ++j)
+      w[j][i] = reinterpret_cast<const float4*>(wr + (int64_t)min(e0 + j, E - 1) * H)[q];
+  }
+  rn_f4 rv[NT][kRnPieces];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < kRnPieces; ++i)
+      rv[t][i] = reinterpret_cast<const rn_f4*>(resid + (int64_t)min(t0 + t, T - 1) * H)
+          [min(tid + 256 * i, H4 - 1)];
+  __shared__ float s_part[NT][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const float ss = rms_wave_sum(rv[t], H4);
+    if (lane == 0) s_part[t][wv] = ss;
+  }
+  __syncthreads();
+  float inv[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) inv[t] = rms_inv(s_part[t], H, eps);
+  double acc[EPB][NT];
+#pragma unroll
+  for (int j = 0; j < EPB; ++j)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[j][t] = 0.0;
+#pragma unroll
+  for (int i = 0; i < kRnPieces; ++i) {
+    const int q = tid + 256 * i;
+    if (q < H4) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint2 xv = make_uint2(rms_bf16x2(rv[t][i].x, rv[t][i].y, inv[t]),
+                                    rms_bf16x2(rv[t][i].z, rv[t][i].w, inv[t]));
+        if (e0 == 0 && t0 + t < T) reinterpret_cast<uint2*>(xn + (int64_t)(t0 + t) * H)[q] = xv;
+#pragma unroll
+        for (int j = 0; j < EPB; ++j) {
+          double a = acc[j][t];
+          a = fma((double)bf16_to_f32((uint16_t)xv.x), (double)w[j][i].x, a);
+          a = fma((double)bf16_to_f32((uint16_t)(xv.x >> 16)), (double)w[j][i].y, a);
+          a = fma((double)bf16_to_f32((uint16_t)xv.y), (double)w[j][i].z, a);
+          a = fma((double)bf16_to_f32((uint16_t)(xv.y >> 16)), (double)w[j][i].w, a);
+          acc[j][t] = a;
+        }
+      }
+    }
+  }
+  __shared__ double red[4][EPB * NT];
+#pragma unroll
+  for (int j = 0; j < EPB; ++j)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      double v = acc[j][t];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+      if (lane == 0) red[wv][j * NT + t] = v;
+    }
+  __syncthreads();
+  if (tid < EPB * NT) {
+    const int j = tid / NT, t = tid % NT, e = e0 + j;
+    if (e < E && t0 + t < T) {
+      double v = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+      if (bias) v += (double)bias[e];
+      st_coherent(logits + (int64_t)(t0 + t) * E + e, v);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_logits_small_norm(const float* __restrict__ resid,
+                                                           float eps, uint16_t* __restrict__ xn,
+                                                           int T, int H, int E,
+                                                           const float* __restrict__ wr,
+                                                           const float* __restrict__ bias,
+                                                           double* __restrict__ logits) {
+  logits_norm_block<kLogitTok, 1>(resid, eps, xn, T, H, E, wr, bias, logits, blockIdx.x,
+                                  blockIdx.y * kLogitTok);
+}
+
 __global__ __launch_bounds__(256) void k_logits_small(const uint16_t* __restrict__ x, int T,
                                                       int H, int E,
                                                       const float* __restrict__ wr,
@@ -714,15 +815,20 @@ __global__ __launch_bounds__(1024) void k_topk_group_small(
 // token (here the last block's four waves would take their tokens in turn:
 // 17.7 us at eight tokens against 14.8 us for the two launches).
 constexpr int kRouteMaxT = 2;
-template <int NT, int PER, int EPB>
+template <int NT, int PER, int EPB, bool NORM>
 __global__ __launch_bounds__(256) void k_route_small(
-    const uint16_t* __restrict__ x, int T, int H, int E, const float* __restrict__ wr,
+    const uint16_t* __restrict__ x, const float* __restrict__ resid, float eps,
+    uint16_t* __restrict__ xn, int T, int H, int E, const float* __restrict__ wr,
     const float* __restrict__ bias, double* logits, int K, int32_t* __restrict__ ids,
     float* __restrict__ wout, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
     int32_t* __restrict__ pair_pos, int32_t* __restrict__ ctr) {
   const int bid = blockIdx.x + gridDim.x * blockIdx.y;
   MOE_TR(4 * bid);
-  logits_multi_block<NT, EPB>(x, T, H, E, wr, bias, logits);
+  if (NORM)
+    logits_norm_block<NT, EPB>(resid, eps, xn, T, H, E, wr, bias, logits, blockIdx.x * EPB,
+                               blockIdx.y * NT);
+  else
+    logits_multi_block<NT, EPB>(x, T, H, E, wr, bias, logits);
   MOE_TR(4 * bid + 1);
   __shared__ int s_last;
   wait_stores();
@@ -759,12 +865,20 @@ __global__ __launch_bounds__(256) void k_route_small(
 }
 
 // ---------------------------------------------------------------- launchers
-hipError_t launch_route(const moe_cfg& c, const uint16_t* x, int T, const float* wr,
+hipError_t launch_route(const moe_cfg& c, const RouteIn& in, int T, const float* wr,
                         const float* bias, int32_t* ids, float* w, int32_t* offsets,
                         int32_t* sorted_pairs, int32_t* pair_pos, double* logits,
                         int32_t* ghist, int32_t* counters, hipStream_t s) {
   const int H = c.hidden, E = c.n_experts, K = c.top_k, P = T * K;
   const int per = (E + 63) / 64;
+  bool norm = in.resid != nullptr;
+  const uint16_t* x = norm ? in.xn : in.x;
+  if (norm && T > 32) {  // the matrix-core logits take the normalisation kernel's output
+    const hipError_t e = launch_rmsnorm(const_cast<float*>(in.resid), nullptr, T, H, in.eps,
+                                        in.xn, s);
+    if (e != hipSuccess) return e;
+    norm = false;
+  }
 #define MOE_PER_SWITCH(X)                                                    \
   switch (per <= 8 ? per : 16) {                                             \
     X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(16)                            \
@@ -773,20 +887,27 @@ hipError_t launch_route(const moe_cfg& c, const uint16_t* x, int T, const float*
   if (T <= kRouteMaxT && P <= 64) {  // one launch
     int32_t* ctr = counters + kCtrRoute;
     const dim3 g1((E + 1) / 2);  // two experts per logit block
+#define MOE_RS1(NT, N, NORM)                                                                    \
+  MOE_LAUNCH(KID_ROUTE, (k_route_small<NT, N, 2, NORM>), g1, dim3(256), 0, s, x, in.resid,       \
+             in.eps, in.xn, T, H, E, wr, bias, logits, K, ids, w, offsets, sorted_pairs, pair_pos, \
+             ctr)
 #define MOE_RS(N)                                                                               \
   case N:                                                                                       \
-    if (T == 1)                                                                                 \
-      MOE_LAUNCH(KID_ROUTE, (k_route_small<1, N, 2>), g1, dim3(256), 0, s, x, T, H, E, wr,     \
-                 bias, logits, K, ids, w, offsets, sorted_pairs, pair_pos, ctr);                \
-    else                                                                                        \
-      MOE_LAUNCH(KID_ROUTE, (k_route_small<2, N, 2>), g1, dim3(256), 0, s, x, T, H, E, wr,     \
-                 bias, logits, K, ids, w, offsets, sorted_pairs, pair_pos, ctr);                \
+    if (T == 1) {                                                                               \
+      if (norm) MOE_RS1(1, N, true); else MOE_RS1(1, N, false);                                 \
+    } else {                                                                                    \
+      if (norm) MOE_RS1(2, N, true); else MOE_RS1(2, N, false);                                 \
+    }                                                                                           \
     break;
     MOE_PER_SWITCH(MOE_RS)
 #undef MOE_RS
+#undef MOE_RS1
     return hipGetLastError();
   }
-  if (T <= 32) {
+  if (T <= 32 && norm) {
+    MOE_LAUNCH(KID_LOGITS, k_logits_small_norm, dim3(E, (T + kLogitTok - 1) / kLogitTok),
+               dim3(256), 0, s, in.resid, in.eps, in.xn, T, H, E, wr, bias, logits);
+  } else if (T <= 32) {
     MOE_LAUNCH(KID_LOGITS, k_logits_small, dim3(E, (T + kLogitTok - 1) / kLogitTok), dim3(256), 0, s,
                x, T, H, E, wr, bias, logits);
   } else {

@@ -91,6 +91,16 @@ class MoELayer:
         moe_rmsnorm_bf16(self.ctx, resid, add, resid.shape[0], eps, y_bf16, stream)
         return y_bf16
 
+    def stack_layer(self, layer, resid, w_router, bias, xn_bf16, out, eps=1e-6, stream=None):
+        """resid += MoE_layer(bf16(RMSNorm(resid))) in one library call; returns the routing"""
+        from . import moe_stack_layer
+        T = resid.shape[0]
+        r = self.routing(T)
+        moe_stack_layer(self.ctx, layer, resid, T, eps, w_router, bias, r.topk_ids, r.topk_w,
+                        r.expert_offsets, r.sorted_pairs, r.pair_pos, xn_bf16, out, self.ws,
+                        stream)
+        return r
+
 
 def stack_forward(ml: MoELayer, resid, add, routers, biases, y, out, on_layer=None, stream=None):
     """One pass of a stack of MoE layers on the residual stream:
@@ -110,3 +120,15 @@ def stack_forward(ml: MoELayer, resid, add, routers, biases, y, out, on_layer=No
         if on_layer is not None:
             on_layer(l, y, r, out)
     return resid, out
+
+
+def stack_forward_fused(ml: MoELayer, resid, routers, biases, y, out, on_layer=None, stream=None):
+    """The same stack pass with one moe_stack_layer call per layer: resid is
+    updated in place to the stack's output (x <- x + MoE_l(bf16(RMSNorm(x)))
+    for every layer); y and out hold the last layer's normalised input and
+    output.  on_layer(l, y, r, out) is called after layer l is enqueued."""
+    for l in range(len(routers)):
+        r = ml.stack_layer(l, resid, routers[l], biases[l], y, out, stream=stream)
+        if on_layer is not None:
+            on_layer(l, y, r, out)
+    return resid

@@ -274,6 +274,25 @@ moe_status moe_cache_step(moe_ctx* ctx, int32_t layer, const int32_t* expert_off
 moe_status moe_rmsnorm_bf16(const moe_ctx* ctx, float* resid, const float* add, int32_t T,
                             float eps, void* y_bf16, moe_stream_t stream);
 
+/* One MoE layer of a stack on its residual stream, in one call:
+ *   xn_bf16 = bf16(RMSNorm(resid))    (exactly as moe_rmsnorm_bf16 with add NULL)
+ *   routing of xn_bf16                (as moe_route, into the routing buffers)
+ *   out = MoE_layer(xn_bf16)          (as moe_forward; pair_out not written)
+ *   resid += out                      (fp32, elementwise)
+ * so that repeated over the layers it computes x <- x + MoE(bf16(RMSNorm(x)))
+ * (the stack glue named beside moe_rmsnorm_bf16 below).  The normalisation is
+ * done inside the routing kernels of batches up to 32 tokens (one launch fewer
+ * per layer) and the residual update inside the combine; the results are bit for
+ * bit those of moe_rmsnorm_bf16(resid, NULL) + moe_route + moe_forward followed by
+ * resid += out.  resid fp32 [T][H] (read and written), xn_bf16 [T][H] and out fp32
+ * [T][H] caller-owned device buffers, 16-byte aligned; eps in [0, 1]; workspace as
+ * for moe_forward.  Stream-ordered, nothing waits for the host, capturable. */
+moe_status moe_stack_layer(moe_ctx* ctx, int32_t layer, float* resid, int32_t T, float eps,
+                           const float* w_router, const float* bias, int32_t* topk_ids,
+                           float* topk_w, int32_t* expert_offsets, int32_t* sorted_pairs,
+                           int32_t* pair_pos, void* xn_bf16, float* out, void* ws,
+                           size_t ws_bytes, moe_stream_t stream);
+
 /* Kernel timing (measurement aid, not part of the layer).  While enabled
  * (process-wide), every kernel the library
  * launches carries two HIP events that the launch timestamps at the kernel's
