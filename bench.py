@@ -79,9 +79,9 @@ def parse():
                          "('' for none)")
     ap.add_argument("--tokens", type=int, default=None, help="batch of the main workload")
     ap.add_argument("--layers", type=int, default=None,
-                    help="resident layer copies the decode steps rotate over (default 16)")
+                    help="resident layer copies the decode steps rotate over (default 20)")
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying HIP graphs")
-    ap.add_argument("--graph-steps", type=int, default=8,
+    ap.add_argument("--graph-steps", type=int, default=10,
                     help="consecutive layer steps captured in one HIP graph for the single-layer "
                          "workloads (as a decoder replays one graph over many layers); the largest "
                          "value up to this that divides both --steps and the rotated layer count")
@@ -109,7 +109,7 @@ def kernel_symbol(kname, T, prefill):
     if T <= 2:
         return {"gateup": "k_gateup_smem", "down": "k_down_blk", "route": "k_route_small",
                 "combine": "k_combine_parts"}.get(kname, kname)
-    return {"gateup": "k_gemv<MODE 0> (gate/up)", "down": "k_gemv<MODE 1> (down)",
+    return {"gateup": "k_gemv<MODE 0> (gate/up)", "down": "k_gemv_mma<MODE 1> (down)",
             "route_logits": "k_logits_small", "combine": "k_combine_parts",
             "swiglu": "k_swiglu_sum", "plan": "k_plan_decode",
             "shared_gateup": "k_shared_gateup", "shared_down": "k_shared_down"}.get(kname, kname)
@@ -189,7 +189,7 @@ def run_workload(name, a, dev, cpu_budget, main_tokens=None, one_thread=True):
     T = cfg.tokens
     decode = T <= 64
     stack = cfg.layers > 1
-    L = cfg.layers if stack else ((a.layers or 16) if decode else 1)
+    L = cfg.layers if stack else ((a.layers or 20) if decode else 1)
     prefill = T > 64 and cfg.hidden % 128 == 0 and cfg.inter % 128 == 0
 
     # ---------------------------------------------------------- resident inputs
@@ -486,40 +486,49 @@ def cache_report(dev, steps=64):
 
 
 def stream_ceiling(dev):
-    """A plain streaming read (torch sum over fp32) and copy of sizes around the
-    decode kernels' bytes, each timed over distinct buffers (no last-level-cache
-    reuse): the practical rate of the memory system for a launch of that size."""
+    """The practical HBM read rate for a launch of the decode kernels' sizes: the
+    library's streaming-read probe (moe_stream_read: the weight stream's access
+    pattern, 16-byte loads, each wave instruction on 1,024 contiguous bytes) over
+    rotating distinct buffers (no last-level-cache reuse), its kernel-own
+    duration from the library's HIP-event timing; plus a torch copy for
+    reference."""
     import torch
+    import bit_moe_expert_router_amd as moe
     res = {}
-    for mb in (24.576, 49.152, 1073.741824):
-        n = int(mb * 1e6) // 4
-        nbuf = max(2, int(600e6 // (n * 4)) + 1)
-        bufs = [torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0) for _ in range(nbuf)]
-        dst = torch.empty(n, dtype=torch.float32, device=dev)
+    sink = torch.empty(4096 * 256, dtype=torch.int32, device=dev)
+    for mb in (24.576, 49.152, 73.728, 1073.741824):
+        nbytes = int(mb * 1e6) // 16 * 16
+        nbuf = max(2, int(600e6 // nbytes) + 1)
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1) for _ in range(nbuf)]
         reps = max(2 * nbuf, 8)
         for b in bufs:
-            b.sum()
+            moe.moe_stream_read(b, nbytes, sink)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        moe.moe_profile_read()
+        moe.moe_profile_enable(True)
         for i in range(reps):
-            bufs[i % nbuf].sum()
-        e1.record()
+            moe.moe_stream_read(bufs[i % nbuf], nbytes, sink)
         torch.cuda.synchronize()
-        rd_us = e0.elapsed_time(e1) * 1e3 / reps
+        prof = moe.moe_profile_read()
+        moe.moe_profile_enable(False)
+        ms, n = prof["stream_read"]
+        rd_us = ms * 1e3 / n
+        dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(reps):
             dst.copy_(bufs[i % nbuf])
         e1.record()
         torch.cuda.synchronize()
         cp_us = e0.elapsed_time(e1) * 1e3 / reps
-        res[f"{mb:.1f}MB"] = {"read_us": round(rd_us, 2), "read_GBs": round(n * 4 / rd_us / 1e3, 1),
+        res[f"{mb:.1f}MB"] = {"read_us": round(rd_us, 2), "read_GBs": round(nbytes / rd_us / 1e3, 1),
                               "copy_us": round(cp_us, 2),
-                              "copy_GBs_read_plus_write": round(2 * n * 4 / cp_us / 1e3, 1)}
+                              "copy_GBs_read_plus_write": round(2 * nbytes / cp_us / 1e3, 1)}
         del bufs, dst
         torch.cuda.empty_cache()
-    res["how"] = ("torch float32 sum (read) and copy_ (read + write) over rotating distinct "
-                  "buffers, HIP events around back-to-back launches")
+    res["how"] = ("read: the library's streaming-read probe (moe_stream_read) over rotating "
+                  "distinct buffers, kernel-own durations from its HIP-event timing; copy: "
+                  "torch copy_ (read + write), HIP events around back-to-back launches")
     return res
 
 

@@ -42,7 +42,7 @@ EXPORTS = ("moe_create", "moe_destroy", "moe_workspace_bytes", "moe_workspace_in
            "moe_forward", "moe_forward_noalloc", "moe_rmsnorm_bf16", "moe_last_error",
            "moe_profile_enable", "moe_profile_read", "moe_host_arena_create",
            "moe_host_arena_destroy", "moe_cache_state_bytes", "moe_cache_init", "moe_cache_step",
-           "moe_stack_layer")
+           "moe_stack_layer", "moe_stream_read")
 MOE_CACHE_LFU, MOE_CACHE_CLOCK = 0, 1
 
 
@@ -69,6 +69,7 @@ def _load():
                                 ctypes.c_size_t, vp]
     lib.moe_forward_noalloc.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_rmsnorm_bf16.argtypes = [vp, vp, vp, i32, ctypes.c_float, vp, vp]
+    lib.moe_stream_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
     lib.moe_stack_layer.argtypes = [vp, i32, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp,
                                     vp, vp, vp, ctypes.c_size_t, vp]
     lib.moe_host_arena_create.argtypes = [ctypes.c_size_t, ctypes.POINTER(vp), ctypes.POINTER(vp)]
@@ -88,7 +89,7 @@ def _load():
     for f in ("moe_create", "moe_destroy", "moe_workspace_init", "set_expert_table",
               "moe_set_shared", "moe_route", "moe_forward", "moe_forward_noalloc",
               "moe_rmsnorm_bf16", "moe_host_arena_create", "moe_host_arena_destroy",
-              "moe_cache_init", "moe_cache_step", "moe_stack_layer"):
+              "moe_cache_init", "moe_cache_step", "moe_stack_layer", "moe_stream_read"):
         getattr(lib, f).restype = st
     return lib
 
@@ -250,6 +251,10 @@ def moe_stack_layer(ctx: int, layer: int, resid, T: int, eps: float, w_router, b
                                _ptr(sorted_pairs), _ptr(pair_pos), _ptr(xn_bf16), _ptr(out),
                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "moe_stack_layer")
+
+
+def moe_stream_read(src, nbytes: int, sink, stream=None):
+    _check(lib.moe_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "moe_stream_read")
 
 
 from .layer import MoELayer, RoutingBuffers  # noqa: E402,F401

@@ -545,7 +545,7 @@ __host__ inline WsLayout ws_layout(const moe_cfg& c, int T) {
 enum KernelId {
   KID_LOGITS = 0, KID_TOPK, KID_PERMUTE, KID_PLAN, KID_GATEUP, KID_DOWN, KID_SH_GATEUP,
   KID_SH_DOWN, KID_COMBINE, KID_RMSNORM, KID_ZERO, KID_XPREP, KID_SWIGLU, KID_ROUTE, KID_TABLE,
-  KID_CACHE, KID_COUNT
+  KID_CACHE, KID_STREAM, KID_COUNT
 };
 // when profiling is on: a pair of events for the next launch of kernel kid
 bool prof_events(int kid, hipEvent_t* b, hipEvent_t* e);

@@ -8,6 +8,7 @@
 // checks one flag.  Not for use under stream capture.
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -20,7 +21,7 @@ namespace {
 const char* const kNames[KID_COUNT] = {"route_logits", "route_topk", "route_permute", "plan",
                                        "gateup",       "down",       "shared_gateup", "shared_down",
                                        "combine",      "rmsnorm",    "zero",          "xprep",        "swiglu",
-                                       "route",        "set_table",     "cache"};
+                                       "route",        "set_table",     "cache",         "stream_read"};
 
 struct Rec {
   int kid;
@@ -72,9 +73,46 @@ bool prof_events(int kid, hipEvent_t* b, hipEvent_t* e) {
   return true;
 }
 
+// Streaming-read probe: 16-byte loads, eight in flight per thread, each wave
+// instruction reading 1,024 contiguous bytes, a grid-stride walk over the buffer.
+// The loaded words are XOR-folded per thread; a thread stores its fold only if it
+// equals a value no input here produces, so the loads cannot be dropped and the
+// writes are nil.
+constexpr int kStreamUnroll = 8;
+constexpr int64_t kStreamMaxBlocks = 4096;  // 16 blocks of four waves per compute unit
+__global__ __launch_bounds__(256) void k_stream_read(const uint4* __restrict__ src, int64_t n16,
+                                                     uint32_t* __restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * 256 * kStreamUnroll;
+  uint32_t acc = 0;
+  for (int64_t base = (int64_t)blockIdx.x * 256 * kStreamUnroll + threadIdx.x; base < n16;
+       base += stride) {
+    uint4 v[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) {
+      const int64_t i = base + 256 * u;
+      v[u] = i < n16 ? src[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9E3779B9u) sink[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 }  // namespace moe
 
 extern "C" {
+
+moe_status moe_stream_read(const void* src, size_t bytes, void* sink, moe_stream_t stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16 || ((uintptr_t)src & 15))
+    return MOE_E_ARG;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  const int64_t per_block = 256 * moe::kStreamUnroll;
+  const int grid = (int)std::min<int64_t>((n16 + per_block - 1) / per_block, moe::kStreamMaxBlocks);
+  hipStream_t s = (hipStream_t)stream;
+  MOE_LAUNCH(moe::KID_STREAM, moe::k_stream_read, dim3(grid), dim3(256), 0, s, (const uint4*)src,
+             n16, (uint32_t*)sink);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
 
 moe_status moe_profile_enable(int32_t on) {
   moe::Profiler& p = moe::prof();

@@ -304,6 +304,16 @@ moe_status moe_stack_layer(moe_ctx* ctx, int32_t layer, float* resid, int32_t T,
 moe_status moe_profile_enable(int32_t on);
 int32_t moe_profile_read(int32_t max_kernels, char* names, double* total_ms, int64_t* launches);
 
+/* Streaming-read probe (measurement aid, not part of the layer): reads `bytes`
+ * (a multiple of 16) of device memory at src (16-byte aligned) once, with the
+ * access pattern of the decode kernels' weight stream (16-byte loads, each wave
+ * instruction covering 1,024 contiguous bytes, eight loads in flight per thread,
+ * up to 4,096 blocks of 256 threads walking the buffer).  sink: device memory of
+ * 4,096 x 256 words that the kernel may write (it writes nothing in practice).
+ * Timed with moe_profile_* (kernel "stream_read") it gives the practical HBM
+ * read rate of one launch of that size.  MOE_E_ARG for bad arguments. */
+moe_status moe_stream_read(const void* src, size_t bytes, void* sink, moe_stream_t stream);
+
 /* Detail string of the last non-OK status on this thread ("" if none). */
 const char* moe_last_error(void);
 

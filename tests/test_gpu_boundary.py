@@ -237,3 +237,18 @@ def test_table_rewritten_on_device(gpu):
     torch.cuda.synchronize()
     assert not torch.equal(out_c[0], out_a[0])
     ml.close()
+
+
+def test_stream_read_probe(gpu):
+    """the streaming-read probe (a measurement aid) reads without writing, and
+    refuses sizes that are not whole 16-byte vectors"""
+    import bit_moe_expert_router_amd as m
+    say("[boundary] stream-read probe")
+    src = torch.arange(1 << 18, dtype=torch.int32, device=gpu)  # 1 MiB
+    sink = torch.zeros(4096 * 256, dtype=torch.int32, device=gpu)
+    m.moe_stream_read(src, src.numel() * 4, sink)
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum().item()) == 0
+    with pytest.raises(m.MoEError) as ei:
+        m.moe_stream_read(src, 1000, sink)
+    assert ei.value.status == m.MOE_E_ARG
