@@ -17,7 +17,10 @@ Prints ONE JSON line.  `value` is the headline workload's tokens/s.  `roofline`
 describes the longest kernel of its step: algorithmic expert-weight bytes per
 launch over the kernel's average duration against the 8 TB/s HBM peak (prefill:
 matrix-core flops against the dense fp16 peak), with durations from HIP events
-that each launch timestamps at the kernel's start and end on its own stream, and
+that each launch timestamps at the kernel's start and end on its own stream (the
+average of a kernel's launches within twice their median: an event pair is now
+and then held back by the host side of a launch; raw means and medians are given
+too), and
 the HBM traffic rocprofv3 counted for that kernel (when the committed counter
 summary matches the current sources).  `extra.step` gives the whole step's
 expert bytes over the step time.  `extra.workloads` repeats all of this for the
@@ -174,7 +177,7 @@ def measured_traffic(symbol, workload):
 
 
 # ------------------------------------------------------------------ one workload
-def run_workload(name, a, dev, cpu_budget, main_tokens=None, one_thread=True):
+def run_workload(name, a, dev, cpu_budget, cpu_jobs, main_tokens=None, one_thread=True):
     import numpy as np
     import torch
 
@@ -294,13 +297,18 @@ def run_workload(name, a, dev, cpu_budget, main_tokens=None, one_thread=True):
     kern = {}
     kt_steps = min(a.steps, 10) if stack else a.steps
     if not a.no_kernel_timing:
+        # one untimed eager pass first: the timing pass then starts from the same
+        # warm state as the steps before it
+        for i in range(kt_steps):
+            step(i % L)
+        torch.cuda.synchronize()
         moe.moe_profile_read()  # drop anything recorded before
         moe.moe_profile_enable(True)
         for i in range(kt_steps):
             step(i % L)
         torch.cuda.synchronize()
         moe.moe_profile_enable(False)
-        kern = moe.moe_profile_read()
+        kern = moe.moe_profile_read_stats()
     # algorithmic bytes over the kernel-timing pass (same step sequence); a stack
     # step launches every layer once
     u_steps = [U[i % L] for i in range(kt_steps)] if not stack else [u for _ in range(kt_steps) for u in U]
@@ -317,9 +325,13 @@ def run_workload(name, a, dev, cpu_budget, main_tokens=None, one_thread=True):
                               else "moe_rmsnorm_bf16 + moe_route + moe_forward per layer")
     roof = None
     if kern:
-        us = {k: v[0] / v[1] * 1e3 for k, v in kern.items() if v[1]}
-        per_step_us = {k: kern[k][0] * 1e3 / kt_steps for k in us}
+        # a kernel's duration: the mean of its launches within twice their median (an
+        # event pair is occasionally held back by the host side of a launch)
+        us = {k: v[2] * 1e3 for k, v in kern.items() if v[3]}
+        per_step_us = {k: us[k] * kern[k][3] / kt_steps for k in us}
         res["kernels_us"] = {k: round(v, 2) for k, v in us.items()}
+        res["kernels_us_median"] = {k: round(kern[k][1] * 1e3, 2) for k in us}
+        res["kernels_us_raw_mean"] = {k: round(kern[k][0] / kern[k][3] * 1e3, 2) for k in us}
         # the longest kernel of the step (time per step), with its own roofline
         ranked = sorted(per_step_us, key=lambda k: -per_step_us[k])
         for k in ranked:
@@ -360,9 +372,9 @@ def run_workload(name, a, dev, cpu_budget, main_tokens=None, one_thread=True):
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
 
-    if cpu_budget > 0:
-        res["cpu_baseline"] = cpu_baseline(cfg, L, cpu_budget, layers_per_step=L if stack else 1,
-                                           one_thread=one_thread)
+    if cpu_budget > 0:  # run after every GPU measurement (busy host threads slow the launches)
+        cpu_jobs.append((res, (cfg, L, cpu_budget), dict(layers_per_step=L if stack else 1,
+                                                         one_thread=one_thread)))
     return res
 
 
@@ -509,10 +521,9 @@ def stream_ceiling(dev):
         for i in range(reps):
             moe.moe_stream_read(bufs[i % nbuf], nbytes, sink)
         torch.cuda.synchronize()
-        prof = moe.moe_profile_read()
+        prof = moe.moe_profile_read_stats()
         moe.moe_profile_enable(False)
-        ms, n = prof["stream_read"]
-        rd_us = ms * 1e3 / n
+        rd_us = prof["stream_read"][2] * 1e3  # mean of the launches within twice the median
         dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -618,14 +629,17 @@ def main():
 
     import torch
     dev = torch.device("cuda:0")
-    main_res = run_workload(a.workload, a, dev, a.cpu_seconds, main_tokens=a.tokens)
+    cpu_jobs = []
+    main_res = run_workload(a.workload, a, dev, a.cpu_seconds, cpu_jobs, main_tokens=a.tokens)
     print(f"[bench] {a.workload}: {main_res['value']} tokens/s", file=sys.stderr, flush=True)
     extra = {}
     for name in [w for w in a.extra.split(",") if w and w != a.workload]:
-        extra[name] = run_workload(name, a, dev, a.cpu_seconds / 4, one_thread=False)
+        extra[name] = run_workload(name, a, dev, a.cpu_seconds / 4, cpu_jobs, one_thread=False)
         print(f"[bench] {name}: {extra[name]['value']} tokens/s", file=sys.stderr, flush=True)
     ceiling = None if a.no_ceiling else stream_ceiling(dev)
     cache = None if a.no_cache else cache_report(dev)
+    for res_w, args, kw in cpu_jobs:  # the CPU oracle baselines, after all GPU work
+        res_w["cpu_baseline"] = cpu_baseline(*args, **kw)
 
     if a.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

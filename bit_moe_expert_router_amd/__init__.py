@@ -42,7 +42,7 @@ EXPORTS = ("moe_create", "moe_destroy", "moe_workspace_bytes", "moe_workspace_in
            "moe_forward", "moe_forward_noalloc", "moe_rmsnorm_bf16", "moe_last_error",
            "moe_profile_enable", "moe_profile_read", "moe_host_arena_create",
            "moe_host_arena_destroy", "moe_cache_state_bytes", "moe_cache_init", "moe_cache_step",
-           "moe_stack_layer", "moe_stream_read")
+           "moe_stack_layer", "moe_stream_read", "moe_profile_read_stats")
 MOE_CACHE_LFU, MOE_CACHE_CLOCK = 0, 1
 
 
@@ -86,6 +86,11 @@ def _load():
     lib.moe_profile_read.argtypes = [i32, ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_int64)]
     lib.moe_profile_read.restype = i32
+    lib.moe_profile_read_stats.argtypes = [i32, ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                           ctypes.POINTER(ctypes.c_double),
+                                           ctypes.POINTER(ctypes.c_double),
+                                           ctypes.POINTER(ctypes.c_int64)]
+    lib.moe_profile_read_stats.restype = i32
     for f in ("moe_create", "moe_destroy", "moe_workspace_init", "set_expert_table",
               "moe_set_shared", "moe_route", "moe_forward", "moe_forward_noalloc",
               "moe_rmsnorm_bf16", "moe_host_arena_create", "moe_host_arena_destroy",
@@ -235,6 +240,20 @@ def moe_profile_read(max_kernels: int = 32) -> dict:
     k = lib.moe_profile_read(max_kernels, names, ms, n)
     raw = names.raw
     return {raw[32 * i:32 * i + 32].split(b"\0")[0].decode(): (ms[i], n[i]) for i in range(k)}
+
+
+def moe_profile_read_stats(max_kernels: int = 32) -> dict:
+    """{kernel name: (total ms, median ms, typical mean ms, launches)} since the last
+    read; the typical mean is the mean of the launches within twice the median"""
+    names = ctypes.create_string_buffer(32 * max_kernels)
+    ms = (ctypes.c_double * max_kernels)()
+    med = (ctypes.c_double * max_kernels)()
+    tm = (ctypes.c_double * max_kernels)()
+    n = (ctypes.c_int64 * max_kernels)()
+    k = lib.moe_profile_read_stats(max_kernels, names, ms, med, tm, n)
+    raw = names.raw
+    return {raw[32 * i:32 * i + 32].split(b"\0")[0].decode(): (ms[i], med[i], tm[i], n[i])
+            for i in range(k)}
 
 
 def moe_rmsnorm_bf16(ctx: int, resid, add, T: int, eps: float, y_bf16, stream=None):

@@ -121,33 +121,52 @@ moe_status moe_profile_enable(int32_t on) {
   return MOE_OK;
 }
 
-int32_t moe_profile_read(int32_t max_kernels, char* names, double* total_ms, int64_t* launches) {
+int32_t moe_profile_read_stats(int32_t max_kernels, char* names, double* total_ms,
+                               double* median_ms, double* typical_mean_ms, int64_t* launches) {
   moe::Profiler& p = moe::prof();
   std::lock_guard<std::mutex> g(p.mu);
-  double ms[moe::KID_COUNT] = {0};
-  int64_t n[moe::KID_COUNT] = {0};
+  std::vector<double> t_of[moe::KID_COUNT];
   for (const moe::Rec& r : p.recs) {
     float t = 0.f;
-    if (hipEventSynchronize(r.e) == hipSuccess && hipEventElapsedTime(&t, r.b, r.e) == hipSuccess) {
-      ms[r.kid] += t;
-      n[r.kid] += 1;
-    }
+    if (hipEventSynchronize(r.e) == hipSuccess && hipEventElapsedTime(&t, r.b, r.e) == hipSuccess)
+      t_of[r.kid].push_back(t);
     p.pool.push_back(r.b);
     p.pool.push_back(r.e);
   }
   p.recs.clear();
   int32_t out = 0;
   for (int k = 0; k < moe::KID_COUNT && out < max_kernels; ++k) {
-    if (!n[k]) continue;
+    std::vector<double>& v = t_of[k];
+    if (v.empty()) continue;
     if (names) {
       strncpy(names + 32 * out, moe::kNames[k], 31);
       names[32 * out + 31] = 0;
     }
-    if (total_ms) total_ms[out] = ms[k];
-    if (launches) launches[out] = n[k];
+    double sum = 0.0;
+    for (double x : v) sum += x;
+    if (total_ms) total_ms[out] = sum;
+    std::sort(v.begin(), v.end());
+    const size_t m = v.size();
+    const double med = m % 2 ? v[m / 2] : 0.5 * (v[m / 2 - 1] + v[m / 2]);
+    if (median_ms) median_ms[out] = med;
+    if (typical_mean_ms) {  // the mean of the launches within twice the median
+      double s2 = 0.0;
+      int64_t c = 0;
+      for (double x : v)
+        if (x <= 2.0 * med) {
+          s2 += x;
+          ++c;
+        }
+      typical_mean_ms[out] = s2 / (double)c;
+    }
+    if (launches) launches[out] = (int64_t)v.size();
     ++out;
   }
   return out;
+}
+
+int32_t moe_profile_read(int32_t max_kernels, char* names, double* total_ms, int64_t* launches) {
+  return moe_profile_read_stats(max_kernels, names, total_ms, nullptr, nullptr, launches);
 }
 
 }  // extern "C"

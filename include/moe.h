@@ -303,6 +303,13 @@ moe_status moe_stack_layer(moe_ctx* ctx, int32_t layer, float* resid, int32_t T,
  * returns the number of entries.  Not for use while a stream is being captured. */
 moe_status moe_profile_enable(int32_t on);
 int32_t moe_profile_read(int32_t max_kernels, char* names, double* total_ms, int64_t* launches);
+/* The same, also giving each kernel's median launch duration and the mean of its
+ * launches within twice that median (median_ms, typical_mean_ms: HOST arrays, or
+ * NULL).  A launch's start event is occasionally held back by the host side of
+ * the launch by hundreds of microseconds; these two figures are not moved by
+ * such outliers. */
+int32_t moe_profile_read_stats(int32_t max_kernels, char* names, double* total_ms,
+                               double* median_ms, double* typical_mean_ms, int64_t* launches);
 
 /* Streaming-read probe (measurement aid, not part of the layer): reads `bytes`
  * (a multiple of 16) of device memory at src (16-byte aligned) once, with the
