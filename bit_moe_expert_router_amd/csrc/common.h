@@ -371,6 +371,10 @@ constexpr int kCtrStrip = 64;
 constexpr int kCtrError = 1;
 constexpr int kCtrCallBad = 2;
 static_assert(kCtrError * 4 == MOE_WS_ERROR_OFFSET, "error word offset");
+// the error word's bit for a matrix-core (prefill) call that met a value fp16
+// cannot hold exactly (a group scale, or h = silu(g)*u)
+constexpr int kErrRange = 4;
+static_assert(kErrRange == MOE_ERR_RANGE, "error bit");
 
 // ---------------------------------------------------------------- routing check
 // Caller-supplied routing is consistent when offsets[0] == 0, the offsets never

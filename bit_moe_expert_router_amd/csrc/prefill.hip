@@ -200,6 +200,13 @@ __device__ __forceinline__ uint32_t q_times_s(uint32_t shifted, uint32_t mask, u
   return __builtin_bit_cast(uint32_t, (v + bias) * s2);                       // (c - z) * s
 }
 
+// A group scale whose products q*s (|q| <= 8) are not all exact in fp16: zero
+// is fine, magnitudes below 2^-14 (fp16 subnormals) or above 65504/8 are not.
+__device__ __forceinline__ bool scale_inexact(float s) {
+  const float a = fabsf(s);
+  return !(a == 0.f || (a >= 6.103515625e-05f && a <= 8188.f));
+}
+
 template <int CODEC>
 struct StepLoad;
 
@@ -220,9 +227,11 @@ struct StepLoad<kQ3G128> {
     typedef const uint16_t __attribute__((address_space(1)))* g16;
     sraw = *(g16)(sc + scale_idx(tile, lane));
   }
-  __device__ __forceinline__ void expand(int hw, int scale_f16, _Float16* wr) const {
-    const _Float16 s = scale_f16 ? __builtin_bit_cast(_Float16, (uint16_t)sraw)
-                                 : (_Float16)bf16_to_f32((uint16_t)sraw);
+  // returns whether the scale is outside the range where q*s is exact in fp16
+  __device__ __forceinline__ bool expand(int hw, int scale_f16, _Float16* wr) const {
+    const float sf = scale_f16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)sraw)
+                               : bf16_to_f32((uint16_t)sraw);
+    const _Float16 s = (_Float16)sf;
     const half2v s2 = {s, s};
     const half2v z = {(_Float16)-1028.f, (_Float16)-1028.f};
     const uint32_t mask = 0x00070007u, magic = 0x64006400u;
@@ -249,6 +258,7 @@ struct StepLoad<kQ3G128> {
         out[q] = u32x4p{pair(4 * q, 4), pair(4 * q + 1, 4), pair(4 * q + 2, 4), pair(4 * q + 3, 4)};
       *reinterpret_cast<u32x2*>(reinterpret_cast<uint32_t*>(wr) + 62) = u32x2{spare(2, 4), spare(3, 4)};
     }
+    return scale_inexact(sf);
   }
 };
 
@@ -269,14 +279,18 @@ struct StepLoad<kQ4G32> {
     sraw = (uint32_t)*(g16)(sc + scale_idx(tile + 2 * hw, lane)) |
            ((uint32_t)*(g16)(sc + scale_idx(tile + 2 * hw + 1, lane)) << 16);
   }
-  __device__ __forceinline__ void expand(int hw, int scale_f16, _Float16* wr) const {
+  // returns whether a scale is outside the range where q*s is exact in fp16
+  __device__ __forceinline__ bool expand(int hw, int scale_f16, _Float16* wr) const {
     const half2v z = {(_Float16)-1032.f, (_Float16)-1032.f};
     const uint32_t mask = 0x000F000Fu, magic = 0x64006400u;
     u32x4p* out = reinterpret_cast<u32x4p*>(wr) + 8 * hw;
+    bool bad = false;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const uint16_t sb = (uint16_t)(sraw >> (16 * u));
-      const _Float16 s = scale_f16 ? __builtin_bit_cast(_Float16, sb) : (_Float16)bf16_to_f32(sb);
+      const float sf = scale_f16 ? (float)__builtin_bit_cast(_Float16, sb) : bf16_to_f32(sb);
+      bad |= scale_inexact(sf);
+      const _Float16 s = (_Float16)sf;
       const half2v s2 = {s, s};
 #pragma unroll
       for (int d = 0; d < 4; ++d) {  // word d of the unit holds pairs 4d .. 4d+3
@@ -285,6 +299,7 @@ struct StepLoad<kQ4G32> {
                                 q_times_s(x >> 8, mask, magic, z, s2), q_times_s(x >> 12, mask, magic, z, s2)};
       }
     }
+    return bad;
   }
 };
 
@@ -305,9 +320,11 @@ struct StepLoad<kQ4G128> {
     typedef const uint16_t __attribute__((address_space(1)))* g16;
     sraw = *(g16)(sc + scale_idx(tile, lane));
   }
-  __device__ __forceinline__ void expand(int hw, int scale_f16, _Float16* wr) const {
-    const _Float16 s = scale_f16 ? __builtin_bit_cast(_Float16, (uint16_t)sraw)
-                                 : (_Float16)bf16_to_f32((uint16_t)sraw);
+  // returns whether the scale is outside the range where q*s is exact in fp16
+  __device__ __forceinline__ bool expand(int hw, int scale_f16, _Float16* wr) const {
+    const float sf = scale_f16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)sraw)
+                               : bf16_to_f32((uint16_t)sraw);
+    const _Float16 s = (_Float16)sf;
     const half2v s2 = {s, s};
     const half2v z = {(_Float16)-1032.f, (_Float16)-1032.f};
     const uint32_t mask = 0x000F000Fu, magic = 0x64006400u;
@@ -318,6 +335,7 @@ struct StepLoad<kQ4G128> {
       out[d] = u32x4p{q_times_s(x, mask, magic, z, s2), q_times_s(x >> 4, mask, magic, z, s2),
                       q_times_s(x >> 8, mask, magic, z, s2), q_times_s(x >> 12, mask, magic, z, s2)};
     }
+    return scale_inexact(sf);
   }
 };
 
@@ -334,9 +352,11 @@ struct StepLoad<kQ2G128> {
     typedef const uint16_t __attribute__((address_space(1)))* g16;
     sraw = *(g16)(sc + scale_idx(tile, lane));
   }
-  __device__ __forceinline__ void expand(int hw, int scale_f16, _Float16* wr) const {
-    const _Float16 s = scale_f16 ? __builtin_bit_cast(_Float16, (uint16_t)sraw)
-                                 : (_Float16)bf16_to_f32((uint16_t)sraw);
+  // returns whether the scale is outside the range where q*s is exact in fp16
+  __device__ __forceinline__ bool expand(int hw, int scale_f16, _Float16* wr) const {
+    const float sf = scale_f16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)sraw)
+                               : bf16_to_f32((uint16_t)sraw);
+    const _Float16 s = (_Float16)sf;
     const half2v s2 = {s, s};
     const half2v z = {(_Float16)-1026.f, (_Float16)-1026.f};
     const uint32_t mask = 0x00030003u, magic = 0x64006400u;
@@ -349,6 +369,7 @@ struct StepLoad<kQ2G128> {
       out[2 * d + 1] = u32x4p{q_times_s(x >> 8, mask, magic, z, s2), q_times_s(x >> 10, mask, magic, z, s2),
                               q_times_s(x >> 12, mask, magic, z, s2), q_times_s(x >> 14, mask, magic, z, s2)};
     }
+    return scale_inexact(sf);
   }
 };
 
@@ -387,7 +408,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(
     const moe_expert_ref* __restrict__ table, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ sorted_pairs, int K,
     const uint16_t* __restrict__ x16, const int32_t* __restrict__ xshift, int H, int I,
-    int scale_f16, uint16_t* __restrict__ h16) {
+    int scale_f16, uint16_t* __restrict__ h16, int32_t* __restrict__ err) {
   using C = UnitCodec<CODEC>;
   __shared__ __align__(16) _Float16 xs[kPM * kLdsRow];
   __shared__ __align__(16) _Float16 wsm[2 * kGuN * kLdsRow];
@@ -468,9 +489,10 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(
   };
   // every issue is unconditional (past the end it repeats the last step), so the
   // waits before a stage's use count only the loads of the other stage
+  bool inexact = false;  // a scale or an h value outside fp16's exact range
   auto run_stage = [&](int b, int next) {
     xl[b].store(xs, row0, chunk);
-    wl[b].expand(hw, scale_f16, wr);
+    inexact |= wl[b].expand(hw, scale_f16, wr);
     lds_barrier();
     issue(min(next, nsteps - 1), b);
     compute();
@@ -496,9 +518,13 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(
         const float g = ldexpf(acc[0][i][j][q], sh), u = ldexpf(acc[1][i][j][q], sh);
         const float h = g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
         const int col = nt * kGuN + 32 * wn + 16 * j + fr;
-        if (pr < rows) h16[(int64_t)(m0 + pr) * I + col] = __builtin_bit_cast(uint16_t, (_Float16)h);
+        if (pr < rows) {
+          h16[(int64_t)(m0 + pr) * I + col] = __builtin_bit_cast(uint16_t, (_Float16)h);
+          inexact |= !(fabsf(h) < 65504.f);
+        }
       }
     }
+  if (__any(inexact) && lane == 0) atomicOr(err, kErrRange);
 }
 
 // ---------------------------------------------------------------- down
@@ -509,7 +535,8 @@ template <int CODEC>
 __global__ __launch_bounds__(256, 2) void k_down_mfma(
     const moe_expert_ref* __restrict__ table, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ sorted_pairs, int P,
-    const uint16_t* __restrict__ h16, int H, int I, int scale_f16, float* __restrict__ pair_out) {
+    const uint16_t* __restrict__ h16, int H, int I, int scale_f16, float* __restrict__ pair_out,
+    int32_t* __restrict__ err) {
   using C = UnitCodec<CODEC>;
   __shared__ __align__(16) _Float16 xs[kPM * kLdsRow];
   __shared__ __align__(16) _Float16 wsm[kDnN * kLdsRow];
@@ -579,9 +606,10 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(
   };
   // every issue is unconditional (past the end it repeats the last step), so the
   // waits before a stage's use count only the loads of the other stage
+  bool inexact = false;  // a scale or an h value outside fp16's exact range
   auto run_stage = [&](int b, int next) {
     xl[b].store(xs, row0, chunk);
-    wl[b].expand(hw, scale_f16, wr);
+    inexact |= wl[b].expand(hw, scale_f16, wr);
     lds_barrier();
     issue(min(next, nsteps - 1), b);
     compute();
@@ -607,6 +635,7 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(
           pair_out[(int64_t)p * H + nt * kDnN + 64 * wn + 16 * j + fr] = acc[i][j][q];
       }
     }
+  if (__any(inexact) && lane == 0) atomicOr(err, kErrRange);
 }
 
 // ---------------------------------------------------------------- launcher
@@ -622,6 +651,7 @@ static hipError_t launch_prefill_t(const FwdArgs& f, const WsLayout& L, float* p
   int32_t* xshift = reinterpret_cast<int32_t*>(f.ws + L.xshift);
   uint16_t* h16 = reinterpret_cast<uint16_t*>(f.ws + L.h16);
   int32_t* tiles = reinterpret_cast<int32_t*>(f.ws + L.tiles);
+  int32_t* err = reinterpret_cast<int32_t*>(f.ws + L.counters) + kCtrError;
   const int64_t max_tiles = prefill_max_tiles(P, E);
   auto round8 = [](int64_t n) { return (int)((n + 7) / 8 * 8); };
   MOE_LAUNCH(KID_XPREP, k_xprep, dim3(T), dim3(256), 0, s, f.x, H, x16, xshift);
@@ -633,10 +663,10 @@ static hipError_t launch_prefill_t(const FwdArgs& f, const WsLayout& L, float* p
              reinterpret_cast<int32_t*>(f.ws + L.counters), tiles);
   MOE_LAUNCH(KID_GATEUP, k_gateup_mfma<CODEC>, dim3(round8(max_tiles * (I / kGuN))),
              dim3(256), 0, s, f.table, f.offsets, tiles, f.sorted_pairs, K, x16, xshift, H, I,
-             c.scale_f16, h16);
+             c.scale_f16, h16, err);
   MOE_LAUNCH(KID_DOWN, k_down_mfma<CODEC>, dim3(round8(max_tiles * (H / kDnN))),
              dim3(256), 0, s, f.table, f.offsets, tiles, f.sorted_pairs, P, h16, H, I,
-             c.scale_f16, pair_out);
+             c.scale_f16, pair_out, err);
   return hipGetLastError();
 }
 

@@ -64,10 +64,16 @@ typedef void* moe_stream_t; /* a hipStream_t */
 
 /* The workspace's error word: an int32 at this byte offset of the workspace.
  * moe_forward sets MOE_ERR_ROUTING in it (atomically; the bit stays set) when it
- * finds caller-supplied routing inconsistent.  moe_workspace_init clears it; so
- * may the caller (stream-ordered write of 0). */
+ * finds caller-supplied routing inconsistent, and MOE_ERR_RANGE (below) when the
+ * matrix-core path meets a value outside fp16's exact range.  moe_workspace_init
+ * clears it; so may the caller (stream-ordered write of 0). */
 #define MOE_WS_ERROR_OFFSET 4
 #define MOE_ERR_ROUTING 1
+/* Set by a call on the matrix-core path (T > 64) that met a value fp16 does not
+ * hold exactly: a group scale s with |s| < 2^-14 or |s| > 8188 (so q*s, |q| <= 8,
+ * is not exact), or h = silu(g)*u with |h| >= 65504 (or not finite).  That call's
+ * outputs are then not to be trusted; the GEMV path (T <= 64) has no such limit. */
+#define MOE_ERR_RANGE 4
 
 typedef enum {
   MOE_OK = 0,

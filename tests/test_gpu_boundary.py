@@ -252,3 +252,49 @@ def test_stream_read_probe(gpu):
     with pytest.raises(m.MoEError) as ei:
         m.moe_stream_read(src, 1000, sink)
     assert ei.value.status == m.MOE_E_ARG
+
+
+def test_prefill_range_flag(gpu):
+    """The matrix-core path (T > 64) holds expanded weights q*s and h = silu(g)*u
+    in fp16: it sets MOE_ERR_RANGE when a value leaves fp16's exact range.
+    Ordinary inputs leave the error word clear; activations scaled by 2^9 make
+    |h| exceed 65504; one group scale of 2^14 in a used expert makes q*s inexact
+    (restored afterwards).  No value here can fault: they are only numbers."""
+    import bit_moe_expert_router_amd as m
+    cfg = synth.CONFIGS["c3"]
+    T = 100
+    say("[boundary] prefill fp16 range flag")
+    dl = _layer("c3", gpu)
+    ml = make_layer_api(cfg, dl, T)
+    xh, xd = x_device(cfg, gpu, tokens=T)
+    out = torch.empty((T, cfg.hidden), dtype=torch.float32, device=gpu)
+
+    def run(x):
+        ml.clear_error()
+        r = ml.route(x, dl.router, dl.bias)
+        ml.forward(0, x, r, out)
+        torch.cuda.synchronize()
+        return ml.error_word(), r
+
+    e0, r = run(xd)
+    assert e0 == 0, e0
+    big = (xd.view(torch.bfloat16).float() * 512.0).to(torch.bfloat16).view(torch.int16)
+    e1, _ = run(big)
+    assert e1 & m.MOE_ERR_RANGE, e1
+    # one scale of the hottest expert's gate matrix set to 2^14 (bf16 0x4680)
+    off = r.expert_offsets.cpu().numpy()
+    hot = int(np.argmax(np.diff(off)))
+    lay = synth.matrix_layout(cfg.inter, cfg.hidden, cfg.bits, cfg.group)
+    addr = dl.refs[hot][0] + lay.scales_off
+    a = addr - dl.arena.data_ptr()
+    saved = dl.arena[a:a + 2].clone()
+    dl.arena[a:a + 2] = torch.tensor([0x80, 0x46], dtype=torch.uint8, device=gpu)
+    try:
+        e2, _ = run(xd)
+    finally:
+        dl.arena[a:a + 2] = saved
+    torch.cuda.synchronize()
+    assert e2 & m.MOE_ERR_RANGE, e2
+    e3, _ = run(xd)
+    assert e3 == 0, e3
+    ml.close()
