@@ -769,7 +769,9 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
 // expert; 4 waves take groups g = wave + 4*i, i < GPW.  The same schedule as the
 // gate/up kernel: each wave requests h (hi and lo rows) of up to XT of the
 // expert's positions for its groups into its own LDS region, then its weights;
-// the token passes run from LDS with two dot products per code pair (hi, lo).
+// the products run on the matrix cores (4 x 4 x 4 bf16 blocks: the rows of A are
+// the positions' h hi and lo from LDS, B the lanes' expanded code pairs), one
+// instruction per two code pairs for both positions and both halves of h.
 // y goes to row p = t*K + k of pair_out (stored written-through).  When `out` is
 // given, the block of each strip that takes the last ticket also forms
 // that strip's 64 columns of out[t] = sum_k w[t][k] y(t,k) (k ascending, pairs
@@ -872,6 +874,8 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
     float* __restrict__ resid) {
   using C = UnitCodec<CODEC>;
   using HS = HFromParts<CODEC, GPW, XT, KP>;
+  typedef short s4v __attribute__((ext_vector_type(4)));
+  typedef float f4v __attribute__((ext_vector_type(4)));
   constexpr int XW = XT * GPW * 2 * C::PAIRS;  // uint32 per wave: [token][group][hi|lo][pair]
   __shared__ float red[kDNWaves][kTokPerPass][64];
   __shared__ __align__(16) uint32_t xs_all[kDNWaves * XW];
@@ -939,6 +943,11 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
       const bool two = jp + 1 < nt;
       const int j1 = two ? jp + 1 : jp;
       float a0 = 0.f, a1 = 0.f;
+      // the matrix-core operand A holds four h rows: (position jp, hi), (jp, lo),
+      // (j1, hi), (j1, lo); lane l supplies row l & 3 (every 4 x 4 block the same
+      // rows), and the weights' code pairs 2s, 2s+1 of lane l are column l of B
+      const int jr = (lane & 2) ? j1 : jp;
+      const uint32_t* arow = xs + (jr * GPW * 2 + (lane & 1)) * C::PAIRS;
 #pragma unroll
       for (int i = 0; i < GPW; ++i) {
         const int g = wv + kDNWaves * i;
@@ -947,26 +956,26 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
           const uint32_t* hl0 = xs + ((jp * GPW + i) * 2 + 1) * C::PAIRS;
           const uint32_t* hh1 = xs + ((j1 * GPW + i) * 2 + 0) * C::PAIRS;
           const uint32_t* hl1 = xs + ((j1 * GPW + i) * 2 + 1) * C::PAIRS;
+          const uint32_t* ar = arow + i * 2 * C::PAIRS;
           uint32_t wd[C::WORDS];
           unit_words<CODEC>(cw[i], wd);
           uint32_t sraw = sr[i];
           asm volatile("" : "+v"(sraw));
           const float sc = scale_to_f32(scale_from_dword(sraw, lane), scale_f16);
           const float k0 = osum(hh0, hl0);
-          float d0 = 0.f, d1 = 0.f;
-          if (two) {
-            const float k1 = osum(hh1, hl1);
-            C::for_each_pair(wd, [&](int Pp, uint32_t pr) {
-              d0 = dot2_bf16(pr, hl0[Pp], dot2_bf16(pr, hh0[Pp], d0));
-              d1 = dot2_bf16(pr, hl1[Pp], dot2_bf16(pr, hh1[Pp], d1));
-            });
-            a1 = fmaf(sc, d1 - k1, a1);
-          } else {
-            C::for_each_pair(wd, [&](int Pp, uint32_t pr) {
-              d0 = dot2_bf16(pr, hl0[Pp], dot2_bf16(pr, hh0[Pp], d0));
-            });
-          }
-          a0 = fmaf(sc, d0 - k0, a0);
+          f4v d = f4v{0.f, 0.f, 0.f, 0.f};
+          uint32_t even = 0;
+          C::for_each_pair(wd, [&](int Pp, uint32_t pr) {
+            if ((Pp & 1) == 0) {
+              even = pr;
+              return;
+            }
+            const s4v b = __builtin_bit_cast(s4v, u32x2v{even, pr});
+            const s4v av = *reinterpret_cast<const s4v*>(ar + Pp - 1);
+            d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(av, b, d, 0, 0, 0);
+          });
+          a0 = fmaf(sc, (d[0] + d[1]) - k0, a0);
+          if (two) a1 = fmaf(sc, (d[2] + d[3]) - osum(hh1, hl1), a1);
         }
       }
       MOE_TR(tb + 3);
