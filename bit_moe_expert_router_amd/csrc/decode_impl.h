@@ -601,22 +601,27 @@ __device__ __forceinline__ Active find_active(const int32_t* __restrict__ offset
   return r;
 }
 
-// Batches of one or two tokens (a single pass): the activations take the scalar
-// path instead (s_load into SGPRs, the second operand of v_dot2_f32_bf16), which
-// keeps the kernel at three waves per SIMD so the whole weight stream of a
-// decode step is in flight at once; the offset sums come from vector loads that
-// are requested before the weights.
+// Batches of one or two tokens (a single pass).  Each wave first requests the
+// slices of the tokens' activation rows that its groups reduce over (cache
+// hits), then its weights, and stages the slices in its own LDS region; the
+// products run on the matrix cores: v_mfma_f32_4x4x4bf16_1k with the token rows
+// as A (lane l supplies row l & 3, which holds token l & 1) and the lane's two
+// expanded code pairs as column l of B, one instruction per two code pairs for
+// both tokens.  Three waves per SIMD keep the whole weight stream of a decode
+// step in flight at once.
 template <int CODEC, int GPW>
 __global__ __launch_bounds__(256, 3) void k_gateup_smem(
     const moe_expert_ref* __restrict__ table, int E, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_pairs, int K,
-    const uint16_t* __restrict__ x,  // read-only: dot operands through scalar loads
-    const uint16_t* x_vec,           // the same activations; not restrict, so that its vector
-                                     // loads stay ahead of the weight loads
-    int H, int I,
+    const int32_t* __restrict__ sorted_pairs, int K, const uint16_t* __restrict__ x, int H, int I,
     int P, int KP, int scale_f16, float* __restrict__ gu) {
   using C = UnitCodec<CODEC>;
+  typedef short s4v __attribute__((ext_vector_type(4)));
+  typedef float f4v __attribute__((ext_vector_type(4)));
+  constexpr int PC = C::G / 8;                    // 16-byte pieces of a group's row slice
+  constexpr int NPC = kTokPerPass * GPW * PC;     // pieces a wave stages
+  constexpr int NIT = (NPC + 63) / 64;
   __shared__ float red[kGUWaves][kTokPerPass][64];
+  __shared__ __align__(16) uint16_t xs_all[kGUWaves][kTokPerPass * GPW * C::G];
   const int ng = H / C::G;
   const int tb = 4 * (blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
   MOE_TR(tb);
@@ -636,39 +641,50 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
   const gu16_t msc = (gu16_t)(mat + gm.scales_off());
   const int row = strip * 64 + lane;
   const int gpb = (ng + KP - 1) / KP, g0 = kp * gpb, g1 = min(ng, g0 + gpb);
-  const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
-  const uint32_t* xv32 = reinterpret_cast<const uint32_t*>(x_vec);
+  uint16_t* xs = xs_all[wv];  // [token slot][group i][G]
+  const uint32_t* xs32 = reinterpret_cast<const uint32_t*>(xs);
 
-  // weights first: the first kGUAhead groups of this wave (group index clamped,
-  // not branched on, so that the waits the compiler places stay exact); they
-  // need nothing but the expert's address.  Each later group is requested right
-  // after the products of the group kGUAhead before it: the requests of the
-  // whole grid then complete in waves, and every wave's products run while its
-  // later groups are still streaming (with every group requested at once, all
-  // of a wave's data lands near the end of the stream and the products follow
-  // it).
+  // weights: the first kGUAhead groups of this wave are requested up front
+  // (group index clamped, not branched on, so that the waits the compiler places
+  // stay exact); each later group right after the products of the group
+  // kGUAhead before it, so that the requests of the whole grid complete in
+  // waves and every wave's products run while its later groups still stream
+  // (with every group requested at once, all of a wave's data lands near the
+  // end of the stream and the products follow it).
   auto issue = [&](int i, u32x4 (&cw)[GPW][C::CHUNKS], uint32_t (&sr)[GPW]) {
     const int g = min(g0 + wv + kGUWaves * i, g1 - 1);
     load_unit4<CODEC>(mat, (int64_t)strip * ng + g, lane, cw[i]);
     sr[i] = load_scale_dword(msc, scale_idx((int64_t)strip * ng + g, lane));
   };
-  // the activation pairs of this wave's groups for the offset sums (lane =
-  // pair) go first: vector loads complete in order, and these (cache hits) are
-  // then not queued behind the weight stream
-  auto load_xo = [&](int t, uint32_t (&xo)[GPW]) {
+  // the row slices of tokens t0 (slot 0) and t1 (slot 1): piece q = (slot, group
+  // i, 16-byte column), loaded ahead of the weights (vector loads complete in
+  // order, so these cache hits do not queue behind the weight stream) and
+  // written to LDS once they are in
+  auto load_x = [&](int t0, int t1, u32x4 (&xr)[NIT]) {
 #pragma unroll
-    for (int i = 0; i < GPW; ++i) {
+    for (int it = 0; it < NIT; ++it) {
+      const int q = min(it * 64 + lane, NPC - 1);
+      const int j = q / (GPW * PC), r = q - j * (GPW * PC), i = r / PC, col = r - i * PC;
       const int g = min(g0 + wv + kGUWaves * i, g1 - 1);
-      const int pl = lane < C::PAIRS ? lane : 0;
-      xo[i] = xv32[((int64_t)t * H + g * C::G) / 2 + pl];
+      xr[it] = *reinterpret_cast<const u32x4*>(x + (int64_t)(j ? t1 : t0) * H + g * C::G + col * 8);
     }
+  };
+  auto store_x = [&](const u32x4 (&xr)[NIT]) {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it)
+      if (it * 64 + lane < NPC) *reinterpret_cast<u32x4*>(xs + (it * 64 + lane) * 8) = xr[it];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's own LDS writes
   };
   // pair ids clamped into [0, P): token rows stay inside x for any routing
   auto pair_at = [&](int pos) { return min(max(sorted_pairs[pos], 0), P - 1); };
-  const int sp0 = pair_at(seg0), sp1 = pair_at(seg0 + min(1, n_e - 1));
-  uint32_t xo0[GPW], xo1[GPW];
-  load_xo(sp0 / K, xo0);
-  load_xo(sp1 / K, xo1);  // (sp1 = sp0 for a single position)
+  auto tokens = [&](int b0, int& t0, int& t1) {
+    t0 = pair_at(seg0 + b0) / K;
+    t1 = b0 + 1 < n_e ? pair_at(seg0 + b0 + 1) / K : t0;
+  };
+  int t0, t1;
+  tokens(0, t0, t1);
+  u32x4 xr[NIT];
+  load_x(t0, t1, xr);
   asm volatile("" ::: "memory");
   u32x4 cw[GPW][C::CHUNKS];
   uint32_t sr[GPW];  // the aligned dword holding the scale (any 16-bit handling here would wait)
@@ -676,55 +692,56 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
   for (int i = 0; i < GPW; ++i)
     if (i < kGUAhead) issue(i, cw, sr);
   asm volatile("" ::: "memory");
+  store_x(xr);
 
-  // one pass over positions b0, b0+1 of the expert with weights cwp/srp (the
-  // first kGUAhead groups already requested; the pass requests the later ones
-  // as it goes)
-  auto pass = [&](int b0, u32x4 (&cwp)[GPW][C::CHUNKS], uint32_t (&srp)[GPW]) {
+  // one pass over positions b0, b0+1 of the expert (their row slices staged; the
+  // first kGUAhead groups already requested, the later ones requested as the
+  // pass goes)
+  auto pass = [&](int b0) {
     const bool two = b0 + 1 < n_e;
-    const int t0 = pair_at(seg0 + b0) / K;
-    const int t1 = two ? pair_at(seg0 + b0 + 1) / K : t0;
+    const uint16_t* arow = xs + (lane & 1) * (GPW * C::G);
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
       const int g = g0 + wv + kGUWaves * i;
       if (g < g1) {
-        const uint32_t* x0 = x32 + ((int64_t)t0 * H + g * C::G) / 2;
-        const uint32_t* x1 = x32 + ((int64_t)t1 * H + g * C::G) / 2;
-        uint32_t sraw = srp[i];
+        uint32_t sraw = sr[i];
         asm volatile("" : "+v"(sraw));  // convert here, not hoisted ahead of the loads
         const float sc = scale_to_f32(scale_from_dword(sraw, lane), scale_f16);
         uint32_t w[C::WORDS];
-        float d0 = 0.f, d1 = 0.f;
-        unit_words<CODEC>(cwp[i], w);
-        if (two) {
-          C::for_each_pair(w, [&](int Pp, uint32_t pr) {
-            d0 = dot2_bf16(pr, x0[Pp], d0);
-            d1 = dot2_bf16(pr, x1[Pp], d1);
-          });
-          a1 = fmaf(sc, d1, a1);
-        } else {
-          C::for_each_pair(w, [&](int Pp, uint32_t pr) { d0 = dot2_bf16(pr, x0[Pp], d0); });
-        }
-        a0 = fmaf(sc, d0, a0);
+        unit_words<CODEC>(cw[i], w);
+        const uint16_t* ar = arow + i * C::G;
+        f4v d = f4v{0.f, 0.f, 0.f, 0.f};
+        uint32_t even = 0;
+        C::for_each_pair(w, [&](int Pp, uint32_t pr) {
+          if ((Pp & 1) == 0) {
+            even = pr;
+            return;
+          }
+          const s4v b = __builtin_bit_cast(s4v, u32x2v{even, pr});
+          const s4v av = *reinterpret_cast<const s4v*>(ar + 2 * (Pp - 1));
+          d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(av, b, d, 0, 0, 0);
+        });
+        a0 = fmaf(sc, d[0], a0);
+        a1 = fmaf(sc, d[1], a1);  // (one position: slot 1 holds the same token)
       }
       if (i + kGUAhead < GPW) {
         asm volatile("" ::: "memory");
-        issue(i + kGUAhead, cwp, srp);
+        issue(i + kGUAhead, cw, sr);
         asm volatile("" ::: "memory");
       }
     }
-    // subtract sum_g s_g * (offset sum of group g)
+    // subtract sum_g s_g * (offset sum of group g), the pairs read from the slices
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
       const int g = g0 + wv + kGUWaves * i;
       if (g < g1) {
-        uint32_t sraw = srp[i];
+        uint32_t sraw = sr[i];
         asm volatile("" : "+v"(sraw));
         const float sc = scale_to_f32(scale_from_dword(sraw, lane), scale_f16);
         const float off = lane < C::PAIRS ? C::pair_off(lane) : 0.f;
-        uint32_t xa = xo0[i], xb = xo1[i];
-        asm volatile("" : "+v"(xa), "+v"(xb));  // used here, not hoisted ahead of the weights
+        const int pl = lane < C::PAIRS ? lane : 0;
+        const uint32_t xa = xs32[i * C::PAIRS + pl], xb = xs32[(GPW + i) * C::PAIRS + pl];
         const float c0 = wave_sum_uniform<CODEC>(
             off * bf16_to_f32((uint16_t)xa) + off * bf16_to_f32((uint16_t)(xa >> 16)));
         a0 = fmaf(-sc, c0, a0);
@@ -748,18 +765,19 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
     }
     lds_barrier();
   };
-  pass(0, cw, sr);
+  pass(0);
   // more than two positions (a token that lists the expert twice): later passes
-  // request the groups again, in the same way
+  // stage their rows and request the groups again, in the same way
   for (int b0 = kTokPerPass; b0 < n_e; b0 += kTokPerPass) {
-    load_xo(pair_at(seg0 + b0) / K, xo0);
-    load_xo(pair_at(seg0 + min(b0 + 1, n_e - 1)) / K, xo1);
+    tokens(b0, t0, t1);
+    load_x(t0, t1, xr);
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < GPW; ++i)
       if (i < kGUAhead) issue(i, cw, sr);
     asm volatile("" ::: "memory");
-    pass(b0, cw, sr);
+    store_x(xr);
+    pass(b0);
   }
   MOE_TR(tb + 3);
 }
@@ -1164,8 +1182,8 @@ hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* shared_ou
 #define MOE_GU(N)                                                                                \
   case N:                                                                                        \
     MOE_LAUNCH(KID_GATEUP, (k_gateup_smem<CODEC, N>), dim3(maxU, I / 64, 2 * KP),                 \
-               dim3(64 * kGUWaves), 0, s, f.table, E, f.offsets, f.sorted_pairs, K, f.x, f.x, H, I, \
-               P, KP, c.scale_f16, gpart);                                                       \
+               dim3(64 * kGUWaves), 0, s, f.table, E, f.offsets, f.sorted_pairs, K, f.x, H, I, P,    \
+               KP, c.scale_f16, gpart);                                                          \
     break;
     switch (gpw_gu) {
       MOE_GU(1) MOE_GU(2) MOE_GU(3) MOE_GU(4) MOE_GU(5)
