@@ -65,6 +65,10 @@ __device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
 // memory, which on gfx950 waits for every outstanding vector load (vmcnt(0)),
 // including weight loads issued ahead on purpose; here only this wave's LDS
 // operations are waited for.
+// the wave's index in its block, as a wave-uniform (scalar) value
+__device__ __forceinline__ int wv_of_thread() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }

@@ -882,7 +882,7 @@ struct HFromParts {
   }
 };
 
-template <int CODEC, int GPW, int XT, int KP>
+template <int CODEC, int GPW, int XT, int KP, bool SPEC>
 __global__ __launch_bounds__(256, 2) void k_down_blk(
     const moe_expert_ref* __restrict__ table, int E, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pairs, int H, int I, int P, int scale_f16,
@@ -901,6 +901,14 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
   const int tb = 4096 + 8 * (blockIdx.x + gridDim.x * blockIdx.y);
   MOE_TR(tb);
 
+  // SPEC (one token): when the routing is consistent and the token lists each
+  // expert once, the a-th active expert's pair sits at sorted position a, so the
+  // block requests the h parts of position a before its lookup, and uses them
+  // only if the lookup confirms that position (otherwise it requests them again)
+  HS hsp;
+  if (SPEC) hsp.load(part, P, I, min((int)blockIdx.x, P - 1), 1, wv_of_thread(), ng - 1,
+                     threadIdx.x & 63);
+  asm volatile("" ::: "memory");
   // every block checks the routing with its lookup (same round trip, one wave's
   // registers); block (0, 0) records the verdict and the error bit
   const Active act = find_active<true>(offsets, table, E, P, blockIdx.x, ids, sorted_pairs);
@@ -916,7 +924,7 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
   const int seg0 = __builtin_amdgcn_readfirstlane(act.seg0);
   const int n_e = __builtin_amdgcn_readfirstlane(act.n);
   const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wv = wv_of_thread();
   const MatGeom gm{H, I, C::BITS, C::G};
   const gbytes_t down = as_global(act.ptr[2]);
   const gu16_t dsc = (gu16_t)(down + gm.scales_off());
@@ -926,9 +934,10 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
   // pair ids of the expert's first 64 positions (lane = position), then h of the
   // first positions, all ahead of the weights
   int pids = sorted_pairs[seg0 + min(lane, n_e - 1)];  // (a checked routing: in [0, P))
+  const bool spec = SPEC && seg0 == (int)blockIdx.x && n_e == 1;  // uniform
   HS hst;
   int nt = min(n_e, XT);
-  hst.load(part, P, I, seg0, nt, wv, ng - 1, lane);
+  if (!spec) hst.load(part, P, I, seg0, nt, wv, ng - 1, lane);
   asm volatile("" ::: "memory");
 
   u32x4 cw[GPW][C::CHUNKS];
@@ -947,7 +956,15 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
     return wave_sum_uniform<CODEC>(off * ((bf16_to_f32((uint16_t)a) + bf16_to_f32((uint16_t)(a >> 16))) +
                                          (bf16_to_f32((uint16_t)b) + bf16_to_f32((uint16_t)(b >> 16)))));
   };
-  hst.store(xs, lane);
+  // (each path stores its own registers: a merged store would wait for the
+  // whole weight stream before the first products)
+  if (spec) {
+    hsp.store(xs, lane);
+    asm volatile("" ::: "memory");
+  } else {
+    hst.store(xs, lane);
+    asm volatile("" ::: "memory");
+  }
   MOE_TR(tb + 2);
   for (int c0 = 0; c0 < n_e; c0 += XT) {
     if (c0 > 0) {
@@ -1199,11 +1216,13 @@ hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* shared_ou
       const hipError_t e = hipStreamWaitEvent(s, join, 0);
       if (e != hipSuccess) return e;
     }
+#define MOE_DN1(N, KPT, SPEC)                                                                     \
+  MOE_LAUNCH(KID_DOWN, (k_down_blk<CODEC, N, 2, KPT, SPEC>), dim3(maxU, H / 64),                   \
+             dim3(64 * kDNWaves), 0, s, f.table, E, f.offsets, f.sorted_pairs, H, I, P, c.scale_f16, \
+             gpart, y, f.ids, f.w, K, T, shared_out, nsh, ctr, ctr0, cout, f.resid)
 #define MOE_DN(N, KPT)                                                                           \
   case N:                                                                                        \
-    MOE_LAUNCH(KID_DOWN, (k_down_blk<CODEC, N, 2, KPT>), dim3(maxU, H / 64), dim3(64 * kDNWaves), \
-               0, s, f.table, E, f.offsets, f.sorted_pairs, H, I, P, c.scale_f16, gpart, y,      \
-               f.ids, f.w, K, T, shared_out, nsh, ctr, ctr0, cout, f.resid);                     \
+    if (T == 1) MOE_DN1(N, KPT, true); else MOE_DN1(N, KPT, false);                             \
     break;
 #define MOE_DN_KP(KPT)                                                                           \
     switch (gpw_dn) {                                                                            \
@@ -1220,6 +1239,7 @@ hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* shared_ou
     }
 #undef MOE_DN_KP
 #undef MOE_DN
+#undef MOE_DN1
     if (fuse) return hipGetLastError();
     // y holds every pair's output in pair order: a single "chunk"
     if (K <= 8) {
