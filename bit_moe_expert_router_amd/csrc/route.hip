@@ -416,7 +416,7 @@ __device__ __forceinline__ int coarse_key(double v) {
   return f == 0.f ? 0 : (b ^ ((b >> 31) & 0x7FFFFFFF));
 }
 
-// this lane's pick (lane < K) and its weight; -1 for other lanes.
+// this lane's pick (lane < K; -1 for other lanes) and its logit (*lk).
 // Each lane first sorts its PER candidates (experts lane + 64i) by descending
 // logit with an odd-even transposition network (swaps only on a strictly larger
 // value, so equal logits keep ascending id order).  Round k then finds the wave
@@ -424,8 +424,8 @@ __device__ __forceinline__ int coarse_key(double v) {
 // when several lanes share the largest key, exactly in fp64 among those lanes,
 // the lowest id winning on equal logits.  The winning lane pops its head.
 template <int PER>
-__device__ __forceinline__ int wave_topk(const double* __restrict__ l, int E, int K, float* wk,
-                                         int trace = -1) {
+__device__ __forceinline__ int wave_topk_pick(const double* __restrict__ l, int E, int K,
+                                              double* lk, int trace = -1) {
   const int lane = threadIdx.x & 63;
   double v[PER];
   int id[PER];
@@ -481,12 +481,28 @@ __device__ __forceinline__ int wave_topk(const double* __restrict__ l, int E, in
     }
   }
   if (trace >= 0) MOE_TR(trace + 1);
-  const double l0 = readlane_f64(my_l, 0);
-  const double term = lane < K ? exp(my_l - l0) : 0.0;
+  *lk = my_l;
+  return lane < K ? my_id : -1;
+}
+
+// the weight of this lane's pick (lane < K) from the picks' logits lk (lane k
+// holds the k-th largest): exp(l_k - l_0) / sum_j exp(l_j - l_0), the sum in pick
+// order
+__device__ __forceinline__ float topk_weight(double lk, int K) {
+  const int lane = threadIdx.x & 63;
+  const double l0 = readlane_f64(lk, 0);
+  const double term = lane < K ? exp(lk - l0) : 0.0;
   double den = 0.0;
   for (int k = 0; k < K; ++k) den += readlane_f64(term, k);
-  *wk = (float)(term / den);
-  return lane < K ? my_id : -1;
+  return (float)(term / den);
+}
+
+template <int PER>
+__device__ __forceinline__ int wave_topk(const double* __restrict__ l, int E, int K, float* wk) {
+  double lk;
+  const int id = wave_topk_pick<PER>(l, E, K, &lk);
+  *wk = topk_weight(lk, K);
+  return id;
 }
 
 template <int PER>
@@ -774,8 +790,9 @@ __device__ __forceinline__ void wave_group_tiny(int id, int P, int E,
   }
 }
 
-// Decode batches of 3 to 16 tokens: wave t picks the top-k of token t, then the
-// first wave groups the pairs (one launch after the logits).
+// Decode batches of 3 to 16 tokens: wave t picks the top-k of token t; once every
+// token's picks are in LDS, wave T (wave 0 at 16 tokens) groups the pairs while
+// the picking waves form their weights.
 template <int PER>
 __global__ __launch_bounds__(1024) void k_topk_group_small(
     const double* __restrict__ logits, int T, int E, int K, int32_t* __restrict__ ids,
@@ -784,24 +801,27 @@ __global__ __launch_bounds__(1024) void k_topk_group_small(
   __shared__ int32_t s_ids[64];
   __shared__ int s_key[128];
   const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
+  double lk = 0.0;
   if (t < T) {
-    float wk;
-    const int id = wave_topk<PER>(logits + (int64_t)t * E, E, K, &wk);
+    const int id = wave_topk_pick<PER>(logits + (int64_t)t * E, E, K, &lk);
     if (lane < K) {
       ids[t * K + lane] = id;
-      wout[t * K + lane] = wk;
       s_ids[t * K + lane] = id;
     }
   }
   // (an LDS-only barrier: __syncthreads() would also wait for the stores above)
   lds_barrier();
-  if (threadIdx.x < 64) {
+  if (t == (T < 16 ? T : 0)) {
     const int P = T * K;
     if (P <= kTinyPairs)
       wave_group_tiny<PER + 1>(lane < P ? s_ids[lane] : -1, P, E, offsets, sorted_pairs, pair_pos);
     else
       wave_group_small<PER + 1>(lane < P ? s_ids[lane] : -1, P, E, s_key, offsets, sorted_pairs,
                                 pair_pos);
+  }
+  if (t < T) {
+    const float wk = topk_weight(lk, K);
+    if (lane < K) wout[t * K + lane] = wk;
   }
 }
 
@@ -841,18 +861,19 @@ __global__ __launch_bounds__(256) void k_route_small(
   __shared__ int s_key[128];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  for (int t = wv; t < T; t += 4) {
-    float wk;
-    const int id = wave_topk<PER>(logits + (int64_t)t * E, E, K, &wk, t == 0 ? 2002 : -1);
+  // waves 0 and 1 pick (one token each); once the picks are in LDS, wave 2 groups
+  // the pairs while the picking waves form their weights
+  double lk = 0.0;
+  if (wv < T) {
+    const int id = wave_topk_pick<PER>(logits + (int64_t)wv * E, E, K, &lk, wv == 0 ? 2002 : -1);
     if (lane < K) {
-      ids[t * K + lane] = id;
-      wout[t * K + lane] = wk;
-      s_ids[t * K + lane] = id;
+      ids[wv * K + lane] = id;
+      s_ids[wv * K + lane] = id;
     }
   }
   MOE_TR(2000);
   lds_barrier();  // s_ids only; the stores above need not have completed
-  if (wv == 0) {
+  if (wv == kRouteMaxT) {
     const int P = T * K;
     if (P <= kTinyPairs)
       wave_group_tiny<PER + 1>(lane < P ? s_ids[lane] : -1, P, E, offsets, sorted_pairs, pair_pos);
@@ -860,8 +881,12 @@ __global__ __launch_bounds__(256) void k_route_small(
       wave_group_small<PER + 1>(lane < P ? s_ids[lane] : -1, P, E, s_key, offsets, sorted_pairs,
                                 pair_pos);
     if (lane == 0) st_coherent(ctr, 0);
+    MOE_TR(2001);
   }
-  MOE_TR(2001);
+  if (wv < T) {
+    const float wk = topk_weight(lk, K);
+    if (lane < K) wout[wv * K + lane] = wk;
+  }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -917,8 +942,8 @@ hipError_t launch_route(const moe_cfg& c, const RouteIn& in, int T, const float*
   if (T <= 16 && P <= 64) {
 #define MOE_TGS(N)                                                                             \
   case N:                                                                                      \
-    MOE_LAUNCH(KID_TOPK, k_topk_group_small<N>, dim3(1), dim3(64 * T), 0, s, logits, T, E, K,  \
-               ids, w, offsets, sorted_pairs, pair_pos);                                       \
+    MOE_LAUNCH(KID_TOPK, k_topk_group_small<N>, dim3(1), dim3(64 * std::min(T + 1, 16)), 0, s, \
+               logits, T, E, K, ids, w, offsets, sorted_pairs, pair_pos);                      \
     break;
     MOE_PER_SWITCH(MOE_TGS)
 #undef MOE_TGS
