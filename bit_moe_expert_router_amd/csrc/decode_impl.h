@@ -613,7 +613,8 @@ template <int CODEC, int GPW>
 __global__ __launch_bounds__(256, 3) void k_gateup_smem(
     const moe_expert_ref* __restrict__ table, int E, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pairs, int K, const uint16_t* __restrict__ x, int H, int I,
-    int P, int KP, int scale_f16, float* __restrict__ gu) {
+    int P, int KP, int scale_f16, float* __restrict__ gu, const int32_t* __restrict__ ids,
+    int32_t* __restrict__ ctr0) {
   using C = UnitCodec<CODEC>;
   typedef short s4v __attribute__((ext_vector_type(4)));
   typedef float f4v __attribute__((ext_vector_type(4)));
@@ -626,9 +627,17 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
   const int tb = 4 * (blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
   MOE_TR(tb);
 
-  // (the routing is checked by the down kernel, which writes the outputs; every
-  // read here stays inside the buffers whatever the routing holds)
-  const Active act = find_active<false>(offsets, table, E, P, blockIdx.x);
+  // block (0, 0, 0) also checks the caller's routing, with its lookup (same round
+  // trip), and records the verdict for the down kernel, which writes the outputs;
+  // every read here stays inside the buffers whatever the routing holds
+  const bool first = (blockIdx.x | blockIdx.y | blockIdx.z) == 0;  // uniform
+  Active act;
+  if (first) {
+    act = find_active<true>(offsets, table, E, P, blockIdx.x, ids, sorted_pairs);
+    if (threadIdx.x == 0) record_routing(ctr0, act.ok);
+  } else {
+    act = find_active<false>(offsets, table, E, P, blockIdx.x);
+  }
   MOE_TR(tb + 1);
   if (act.e < 0) return;
   const int seg0 = __builtin_amdgcn_readfirstlane(act.seg0);
@@ -909,13 +918,13 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
   if (SPEC) hsp.load(part, P, I, min((int)blockIdx.x, P - 1), 1, wv_of_thread(), ng - 1,
                      threadIdx.x & 63);
   asm volatile("" ::: "memory");
-  // every block checks the routing with its lookup (same round trip, one wave's
-  // registers); block (0, 0) records the verdict and the error bit
-  const Active act = find_active<true>(offsets, table, E, P, blockIdx.x, ids, sorted_pairs);
+  // the gate/up kernel's verdict on the caller's routing, read in the lookup's
+  // round trip
+  const int call_bad = ctr0[kCtrCallBad];
+  const Active act = find_active<false>(offsets, table, E, P, blockIdx.x);
   MOE_TR(tb + 1);
   const int strip = blockIdx.y;
-  if (blockIdx.x == 0 && strip == 0 && threadIdx.x == 0) record_routing(ctr0, act.ok);
-  if (!act.ok) return;  // inconsistent caller routing: the outputs are left untouched
+  if (call_bad) return;  // inconsistent caller routing: the outputs are left untouched
   if (act.e < 0) {  // no expert for this block; with none at all, block 0 combines
     if (out && act.U == 0 && blockIdx.x == 0)
       combine_strip(pair_out, ids, wts, K, E, H, shared, nsh, T, strip, out, resid);
@@ -1200,7 +1209,7 @@ hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* shared_ou
   case N:                                                                                        \
     MOE_LAUNCH(KID_GATEUP, (k_gateup_smem<CODEC, N>), dim3(maxU, I / 64, 2 * KP),                 \
                dim3(64 * kGUWaves), 0, s, f.table, E, f.offsets, f.sorted_pairs, K, f.x, H, I, P,    \
-               KP, c.scale_f16, gpart);                                                          \
+               KP, c.scale_f16, gpart, f.ids, ctr0);                                             \
     break;
     switch (gpw_gu) {
       MOE_GU(1) MOE_GU(2) MOE_GU(3) MOE_GU(4) MOE_GU(5)
