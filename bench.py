@@ -113,7 +113,7 @@ def kernel_symbol(kname, T, prefill):
         return {"gateup": "k_gateup_smem", "down": "k_down_blk", "route": "k_route_small",
                 "combine": "k_combine_parts"}.get(kname, kname)
     return {"gateup": "k_gemv<MODE 0> (gate/up)", "down": "k_gemv_mma<MODE 1> (down)",
-            "route_logits": "k_logits_small", "combine": "k_combine_parts",
+            "route_logits": "k_logits_multi", "combine": "k_combine_parts",
             "swiglu": "k_swiglu_sum", "plan": "k_plan_decode",
             "shared_gateup": "k_shared_gateup", "shared_down": "k_shared_down"}.get(kname, kname)
 

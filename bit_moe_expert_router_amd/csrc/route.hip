@@ -22,76 +22,18 @@ namespace moe {
 MOE_TRACE_DECL
 
 // ---------------------------------------------------------------- logits, small T
-// Block = one expert x up to NT (1, 2 or 4) tokens; 256 threads stride over H in
-// float4 steps, each thread issuing all its loads of a batch (8 float4 of the
-// router row and the matching activations of every token) before using any, so
-// a 5120-wide row costs one memory round trip.  Items past the row end load the
-// last item and use a zero router value.
-constexpr int kLogitTok = 4;
-constexpr int kLogitBatch = 8;
-
-// Block (e, token chunk): logits of expert e for tokens t0 .. t0+NT-1.
-template <int NT>
-__device__ __forceinline__ void logits_small_block(const uint16_t* __restrict__ x, int T, int H,
-                                                   int E, const float* __restrict__ wr,
-                                                   const float* __restrict__ bias,
-                                                   double* __restrict__ logits) {
-  constexpr int kLogitTok = NT;
-  const int e = blockIdx.x;
-  const int t0 = blockIdx.y * kLogitTok;
-  const int nt = min(kLogitTok, T - t0);
-  const int H4 = H / 4;
-  const float4* w4 = reinterpret_cast<const float4*>(wr + (int64_t)e * H);
-  double acc[kLogitTok];
-#pragma unroll
-  for (int j = 0; j < kLogitTok; ++j) acc[j] = 0.0;
-  for (int b = 0; b < H4; b += 256 * kLogitBatch) {
-    float4 w[kLogitBatch];
-    uint2 xv[kLogitTok][kLogitBatch];
-#pragma unroll
-    for (int r = 0; r < kLogitBatch; ++r) {
-      const int i = min(b + (int)threadIdx.x + 256 * r, H4 - 1);
-      w[r] = w4[i];
-#pragma unroll
-      for (int j = 0; j < kLogitTok; ++j)
-        xv[j][r] = reinterpret_cast<const uint2*>(x + (int64_t)(t0 + min(j, nt - 1)) * H)[i];
-    }
-#pragma unroll
-    for (int r = 0; r < kLogitBatch; ++r) {
-      if (b + (int)threadIdx.x + 256 * r >= H4) w[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int j = 0; j < kLogitTok; ++j) {
-        acc[j] = fma((double)bf16_to_f32((uint16_t)xv[j][r].x), (double)w[r].x, acc[j]);
-        acc[j] = fma((double)bf16_to_f32((uint16_t)(xv[j][r].x >> 16)), (double)w[r].y, acc[j]);
-        acc[j] = fma((double)bf16_to_f32((uint16_t)xv[j][r].y), (double)w[r].z, acc[j]);
-        acc[j] = fma((double)bf16_to_f32((uint16_t)(xv[j][r].y >> 16)), (double)w[r].w, acc[j]);
-      }
-    }
-  }
-  __shared__ double red[4][kLogitTok];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-  for (int j = 0; j < kLogitTok; ++j) {
-    if (j < nt) {
-      double v = acc[j];
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-      if (lane == 0) red[wv][j] = v;
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x < nt) {
-    const int j = threadIdx.x;
-    double v = ((red[0][j] + red[1][j]) + red[2][j]) + red[3][j];
-    if (bias) v += (double)bias[e];
-    st_coherent(logits + (int64_t)(t0 + j) * E + e, v);
-  }
-}
-
-// Block (b, c) = experts b*EPB .. b*EPB+EPB-1 x tokens c*NT .. c*NT+NT-1: the same per-thread order
-// as the block above (items tid + 256*r of the row, r ascending), so the logits
-// are the same; one block for several experts cuts the number of blocks that
-// meet at the routing kernel's ticket counter, where every arrival is serialised.
+// Block (b, c) = experts b*EPB .. b*EPB+EPB-1 x tokens c*NT .. c*NT+NT-1; 256
+// threads stride over H in float4 steps (items tid + 256*r of the row, r
+// ascending), each thread issuing all its loads of a batch (the router rows'
+// float4 and the matching activations of every token) before using any, so a
+// 5120-wide row costs one memory round trip; items past the row end load the
+// last item and add nothing.  Each thread's fp64 sum, then the wave's butterfly
+// and the fixed-order sum of the four waves: the logits do not depend on EPB or
+// NT.  Several experts per block read the activation rows once per EPB experts
+// and, in the one-launch routing kernel, cut the number of blocks that meet at
+// its ticket counter, where every arrival is serialised.
+constexpr int kLogitTok = 4;  // tokens per block, 3 to 32 tokens
+constexpr int kLogitEPB = 2;  // experts per block, 3 to 32 tokens
 constexpr int kRowBatch = 5;  // float4 items of a row per thread per round trip
 template <int NT, int EPB>
 __device__ __forceinline__ void logits_multi_block(const uint16_t* __restrict__ x, int T, int H,
@@ -164,7 +106,7 @@ __device__ __forceinline__ void logits_multi_block(const uint16_t* __restrict__ 
 // float4 items tid + 256*j of each token's fp32 row, which are also the items it
 // takes in the logit sums; the squares are summed exactly as the normalisation
 // kernel sums them (rms_wave_sum, rms_inv), and the bf16 values it forms enter the
-// same logit arithmetic, in the same order, as the two blocks above.  So the
+// same logit arithmetic, in the same order, as the block above.  So the
 // logits equal those of the plain kernels on the normalisation kernel's output,
 // bit for bit.  Blocks of the first expert chunk also store the bf16 rows to xn
 // (the experts' input).  H <= 8192.
@@ -249,22 +191,23 @@ __device__ __forceinline__ void logits_norm_block(const float* __restrict__ resi
   }
 }
 
-__global__ __launch_bounds__(256) void k_logits_small_norm(const float* __restrict__ resid,
+// batches of 3 to 32 tokens (block (b, c) as above)
+template <int NT, int EPB>
+__global__ __launch_bounds__(256) void k_logits_multi(const uint16_t* __restrict__ x, int T, int H,
+                                                      int E, const float* __restrict__ wr,
+                                                      const float* __restrict__ bias,
+                                                      double* __restrict__ logits) {
+  logits_multi_block<NT, EPB>(x, T, H, E, wr, bias, logits);
+}
+template <int NT, int EPB>
+__global__ __launch_bounds__(256) void k_logits_multi_norm(const float* __restrict__ resid,
                                                            float eps, uint16_t* __restrict__ xn,
                                                            int T, int H, int E,
                                                            const float* __restrict__ wr,
                                                            const float* __restrict__ bias,
                                                            double* __restrict__ logits) {
-  logits_norm_block<kLogitTok, 1>(resid, eps, xn, T, H, E, wr, bias, logits, blockIdx.x,
-                                  blockIdx.y * kLogitTok);
-}
-
-__global__ __launch_bounds__(256) void k_logits_small(const uint16_t* __restrict__ x, int T,
-                                                      int H, int E,
-                                                      const float* __restrict__ wr,
-                                                      const float* __restrict__ bias,
-                                                      double* __restrict__ logits) {
-  logits_small_block<kLogitTok>(x, T, H, E, wr, bias, logits);
+  logits_norm_block<NT, EPB>(resid, eps, xn, T, H, E, wr, bias, logits, blockIdx.x * EPB,
+                             blockIdx.y * NT);
 }
 
 // ---------------------------------------------------------------- logits, large T
@@ -929,12 +872,14 @@ hipError_t launch_route(const moe_cfg& c, const RouteIn& in, int T, const float*
 #undef MOE_RS1
     return hipGetLastError();
   }
-  if (T <= 32 && norm) {
-    MOE_LAUNCH(KID_LOGITS, k_logits_small_norm, dim3(E, (T + kLogitTok - 1) / kLogitTok),
-               dim3(256), 0, s, in.resid, in.eps, in.xn, T, H, E, wr, bias, logits);
-  } else if (T <= 32) {
-    MOE_LAUNCH(KID_LOGITS, k_logits_small, dim3(E, (T + kLogitTok - 1) / kLogitTok), dim3(256), 0, s,
-               x, T, H, E, wr, bias, logits);
+  if (T <= 32) {
+    const dim3 g((E + kLogitEPB - 1) / kLogitEPB, (T + kLogitTok - 1) / kLogitTok);
+    if (norm)
+      MOE_LAUNCH(KID_LOGITS, (k_logits_multi_norm<kLogitTok, kLogitEPB>), g, dim3(256), 0, s,
+                 in.resid, in.eps, in.xn, T, H, E, wr, bias, logits);
+    else
+      MOE_LAUNCH(KID_LOGITS, (k_logits_multi<kLogitTok, kLogitEPB>), g, dim3(256), 0, s, x, T, H,
+                 E, wr, bias, logits);
   } else {
     MOE_LAUNCH(KID_LOGITS, k_logits_mfma, dim3((E + kLE - 1) / kLE, (T + kLT - 1) / kLT), dim3(256),
                0, s, x, T, H, E, wr, bias, logits);
