@@ -4,10 +4,11 @@ combine) against the three-call sequence moe_rmsnorm_bf16 + moe_route +
 moe_forward it replaces, on three layers of the 42-layer stack's shape (shared
 expert, remapped tables), through the C-ABI: every layer's normalised input,
 routing and output, and the final residual, bit for bit, on each routing and
-expert path (one-launch routing at 1 and 2 tokens; the small-batch logits at 4,
-9 and 32; the normalisation kernel before the matrix-core logits at 40; the
-prefill experts at 100).  The three-call sequence itself is checked against the
-oracle layer by layer in test_gpu_stack.py."""
+expert path (one-launch routing at 1 and 2 tokens; the small-batch logits at 3
+to 32; the normalisation kernel before the matrix-core logits at 40; the
+prefill experts at 100), and with 2-bit, 4-bit G128 and 4-bit G32 codes at 4
+tokens.  The three-call sequence itself is checked against the oracle layer by
+layer in test_gpu_stack.py."""
 import numpy as np
 import pytest
 import torch
@@ -19,30 +20,34 @@ from tests.gpu_util import say
 pytestmark = pytest.mark.gpu
 
 L = 3
-_layers = []
+_layers = {}
 
 
-def _stack(gpu):
-    if not _layers:
-        cfg = synth.CONFIGS["c4"]
-        _layers.extend(DeviceLayer.generate(cfg, l, gpu) for l in range(L))
-    return _layers
+def _stack(gpu, name="c4"):
+    if name not in _layers:
+        cfg = synth.CONFIGS[name]
+        _layers[name] = [DeviceLayer.generate(cfg, l, gpu) for l in range(L)]
+    return _layers[name]
 
 
-@pytest.mark.parametrize("T", [1, 2, 4, 9, 32, 40, 100])
-def test_stack_layer_equals_three_calls(gpu, T):
+CASES = [("c4", T) for T in (1, 2, 3, 4, 8, 9, 32, 40, 100)] + [("q2", 4), ("q4", 4), ("c1", 4)]
+
+
+@pytest.mark.parametrize("name,T", CASES)
+def test_stack_layer_equals_three_calls(gpu, name, T):
     from bit_moe_expert_router_amd import MoELayer
     from bit_moe_expert_router_amd.layer import stack_forward, stack_forward_fused
 
-    cfg = synth.CONFIGS["c4"]
+    cfg = synth.CONFIGS[name]
     H = cfg.hidden
-    say(f"[stack fused] T={T}")
-    layers = _stack(gpu)
+    say(f"[stack fused] {name} T={T}")
+    layers = _stack(gpu, name)
     ml = MoELayer(H, cfg.inter, cfg.n_experts, cfg.top_k, cfg.bits, cfg.group, cfg.scale_f16,
                   cfg.shared_inter, T, L, gpu)
     for l, dl in enumerate(layers):
         ml.set_table(l, dl.refs)
-        ml.set_shared(l, *dl.shared)
+        if dl.shared is not None:
+            ml.set_shared(l, *dl.shared)
     x0 = torch.from_numpy(synth.normal_f32(T * H, cfg.seed, 50 + T, synth.SYN_X, 1.0)
                           .reshape(T, H)).to(gpu)
     routers = [dl.router for dl in layers]
@@ -73,7 +78,7 @@ def test_stack_layer_equals_three_calls(gpu, T):
             assert torch.equal(a, b), (T, l, name)
     assert torch.equal(ra, rb), T
     assert bool(torch.isfinite(rb).all())
-    say(f"[stack fused] T={T}: {L} layers bit-identical")
+    say(f"[stack fused] {name} T={T}: {L} layers bit-identical")
     ml.close()
 
 
