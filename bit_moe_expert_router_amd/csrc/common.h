@@ -441,6 +441,8 @@ __device__ __forceinline__ void record_routing(int32_t* ctr, bool ok) {
 // Batches up to this many tokens run the GEMV (decode) kernels; larger ones the
 // matrix-core (prefill) kernels when the shape allows them.
 constexpr int kDecodeMaxTokens = 64;
+// slices of the shared expert's output that a combine reads (its down kernel's split)
+constexpr int kMaxShared = 2;
 constexpr int kPrefillTileRows = 128;  // sorted pair positions per prefill tile
 __host__ __device__ inline bool prefill_eligible(const moe_cfg& c, int T) {
   return T > kDecodeMaxTokens && c.hidden % 128 == 0 && c.inter % 128 == 0;

@@ -93,6 +93,9 @@ __global__ __launch_bounds__(1024) void k_plan_decode(const int32_t* __restrict_
     return;
   }
   for (int i = e; i < 16 * kPlanKeys; i += 1024) (&cntw[0][0])[i] = 0;
+  // expert e's table entry with its offsets (one round trip; used if it is active)
+  moe_expert_ref r{nullptr, nullptr, nullptr};
+  if (e < E) r = table[e];
   const int lo = e < E ? offsets[e] : 0;
   const int hi = e < E ? offsets[e + 1] : 0;
   // the routing check (as routing_ok_wave, one thread per expert and position)
@@ -155,7 +158,6 @@ __global__ __launch_bounds__(1024) void k_plan_decode(const int32_t* __restrict_
   __syncthreads();
   if (n > 0) {
     const int a = base[key] + cntw[wv][key] + below;
-    const moe_expert_ref r = table[e];
     ActEntry ent;
     ent.e = e;
     ent.seg0 = lo;
@@ -1071,13 +1073,16 @@ __global__ __launch_bounds__(256) void k_swiglu_sum(const float* __restrict__ pa
   using C = UnitCodec<CODEC>;
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   const int pos = blockIdx.y;
-  if (pos >= offsets[E]) return;
   const int ngd = I / C::G;
   const int lane = threadIdx.x & 63;
   const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (g >= ngd) return;  // wave-uniform
   const bool live = lane < C::PAIRS;
   const int k = g * C::G + 2 * (live ? lane : 0);
+  // the number of grouped positions and the partial sums in one round trip (every
+  // position < P has its rows in the buffer; positions past the grouped pairs
+  // store nothing)
+  const int n_grouped = offsets[E];
   f32x2 pg[MC], pu[MC];
 #pragma unroll
   for (int c = 0; c < MC; ++c) {
@@ -1085,6 +1090,8 @@ __global__ __launch_bounds__(256) void k_swiglu_sum(const float* __restrict__ pa
     pg[c] = *reinterpret_cast<const f32x2*>(part + ((int64_t)cc * P + pos) * I + k);
     pu[c] = *reinterpret_cast<const f32x2*>(part + ((int64_t)(NCH + cc) * P + pos) * I + k);
   }
+  asm volatile("" ::: "memory");
+  if (pos >= n_grouped) return;
   uint32_t hp = 0, lp = 0;
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
@@ -1135,6 +1142,13 @@ __global__ __launch_bounds__(256) void k_combine_parts(const float* __restrict__
 #pragma unroll
     for (int c = 0; c < MC; ++c)
       y[k][c] = part[((int64_t)min(c, NCH - 1) * P + (int64_t)t * K + min(k, K - 1)) * H + n];
+  // the shared expert's slices (at most kMaxShared) and the residual, in the same
+  // round trip as the partial sums
+  float shv[kMaxShared];
+#pragma unroll
+  for (int q = 0; q < kMaxShared; ++q)
+    shv[q] = shared ? shared[((int64_t)min(q, nsh - 1) * T + t) * H + n] : 0.f;
+  const float rv = resid ? resid[(int64_t)t * H + n] : 0.f;
   float acc = 0.f;
   const bool in = blockIdx.x * 256 + threadIdx.x < H;
   const int bad = call_bad[0];
@@ -1152,12 +1166,14 @@ __global__ __launch_bounds__(256) void k_combine_parts(const float* __restrict__
   }
   if (shared) {  // the shared expert's slices, in slice order
     float sh = 0.f;
-    for (int q = 0; q < nsh; ++q) sh += shared[((int64_t)q * T + t) * H + n];
+#pragma unroll
+    for (int q = 0; q < kMaxShared; ++q)
+      if (q < nsh) sh += shv[q];
     acc += sh;
   }
   if (in && !bad) {
     out[(int64_t)t * H + n] = acc;
-    if (resid) resid[(int64_t)t * H + n] += acc;  // a stack layer: the residual update
+    if (resid) resid[(int64_t)t * H + n] = rv + acc;  // a stack layer: the residual update
   }
 }
 

@@ -70,6 +70,7 @@ constexpr int kNT = 8;       // tokens per pass
 constexpr int kShSteps = 8;  // 256-element steps per slice, at most
 constexpr int kShareSlicesGU = 4;
 constexpr int kShareSlicesDN = 2;
+static_assert(kShareSlicesDN <= kMaxShared, "the decode combine reads at most kMaxShared slices");
 
 __device__ __forceinline__ float half_wave_sum(float v) {
 #pragma unroll
