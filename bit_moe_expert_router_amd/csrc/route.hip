@@ -211,11 +211,13 @@ __global__ __launch_bounds__(256) void k_logits_multi_norm(const float* __restri
 }
 
 // ---------------------------------------------------------------- logits, large T
-// fp64 matrix cores (v_mfma_f64_16x16x4_f64): block = 64 tokens x 64 experts, four
-// waves of 32 x 32; the reduction dim in steps of 32 staged through LDS as fp64
+// fp64 matrix cores (v_mfma_f64_16x16x4_f64): block = 32 tokens x 96 experts, four
+// waves of 16 x 48; the reduction dim in steps of 32 staged through LDS as fp64
 // (bf16 and fp32 inputs widen exactly), the next step's global loads in flight
 // during the current step's products.  Every product is exact; the sums are fp64.
-constexpr int kLT = 64, kLE = 64, kLK = 32;
+// 96 experts per block divide the 288 experts of the pages' model without padding,
+// and 8,192 tokens give 768 blocks, three per CU.
+constexpr int kLT = 32, kLE = 96, kLK = 32;
 constexpr int kLRow = kLK + 4;  // doubles per LDS row (2-way bank conflicts at most)
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
@@ -227,38 +229,49 @@ __global__ __launch_bounds__(256) void k_logits_mfma(const uint16_t* __restrict_
   __shared__ __align__(16) double ws[kLE * kLRow];
   const int t0 = blockIdx.y * kLT, e0 = blockIdx.x * kLE;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  // loader: thread (row, 8 consecutive k)
+  // loader: thread (row, 8 consecutive k): token rows lr < 32 (threads 0..127)
+  // and expert rows lr and 64 + lr (the second for lr < 32)
   const int lr = tid >> 2, lk = (tid & 3) * 8;
-  const bool xok = t0 + lr < T, wok = e0 + lr < E;
-  const uint16_t* xp = x + (int64_t)min(t0 + lr, T - 1) * H + lk;
+  const bool xl = lr < kLT, w2 = lr + 64 < kLE;
+  const bool xok = xl && t0 + lr < T, wok = e0 + lr < E, wok2 = w2 && e0 + 64 + lr < E;
+  const uint16_t* xp = x + (int64_t)min(t0 + min(lr, kLT - 1), T - 1) * H + lk;
   const float* wp = wr + (int64_t)min(e0 + lr, E - 1) * H + lk;
+  const float* wp2 = wr + (int64_t)min(e0 + 64 + min(lr, kLE - 65), E - 1) * H + lk;
   uint4 xv;
-  float4 wv0, wv1;
+  float4 wv0, wv1, wv2, wv3;
   auto load = [&](int k0) {
     xv = *reinterpret_cast<const uint4*>(xp + k0);
     wv0 = *reinterpret_cast<const float4*>(wp + k0);
     wv1 = *reinterpret_cast<const float4*>(wp + k0 + 4);
+    wv2 = *reinterpret_cast<const float4*>(wp2 + k0);
+    wv3 = *reinterpret_cast<const float4*>(wp2 + k0 + 4);
   };
   auto stage = [&]() {
-    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-    double* xd = xs + lr * kLRow + lk;
-    double* wd = ws + lr * kLRow + lk;
+    if (xl) {
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+      double* xd = xs + lr * kLRow + lk;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      xd[2 * j] = xok ? (double)bf16_to_f32((uint16_t)xw[j]) : 0.0;
-      xd[2 * j + 1] = xok ? (double)bf16_to_f32((uint16_t)(xw[j] >> 16)) : 0.0;
+      for (int j = 0; j < 4; ++j) {
+        xd[2 * j] = xok ? (double)bf16_to_f32((uint16_t)xw[j]) : 0.0;
+        xd[2 * j + 1] = xok ? (double)bf16_to_f32((uint16_t)(xw[j] >> 16)) : 0.0;
+      }
     }
     const float wf[8] = {wv0.x, wv0.y, wv0.z, wv0.w, wv1.x, wv1.y, wv1.z, wv1.w};
+    double* wd = ws + lr * kLRow + lk;
 #pragma unroll
     for (int j = 0; j < 8; ++j) wd[j] = wok ? (double)wf[j] : 0.0;
+    if (w2) {
+      const float wg[8] = {wv2.x, wv2.y, wv2.z, wv2.w, wv3.x, wv3.y, wv3.z, wv3.w};
+      double* wd2 = ws + (64 + lr) * kLRow + lk;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) wd2[j] = wok2 ? (double)wg[j] : 0.0;
+    }
   };
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wm = wv >> 1, wn = wv & 1;  // wave tile: tokens 16wm.., experts 48wn..
   const int fr = lane & 15, fk = lane >> 4;
-  f64x4 acc[2][2];
+  f64x4 acc[1][3];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int j = 0; j < 3; ++j) acc[0][j] = f64x4{0.0, 0.0, 0.0, 0.0};
   load(0);
   for (int k0 = 0; k0 < H; k0 += kLK) {
     stage();
@@ -266,31 +279,26 @@ __global__ __launch_bounds__(256) void k_logits_mfma(const uint16_t* __restrict_
     if (k0 + kLK < H) load(k0 + kLK);
 #pragma unroll
     for (int kk = 0; kk < kLK; kk += 4) {
-      double a[2], b[2];
+      double a, b[3];
+      a = xs[(16 * wm + fr) * kLRow + kk + fk];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = xs[(32 * wm + 16 * i + fr) * kLRow + kk + fk];
+      for (int j = 0; j < 3; ++j) b[j] = ws[(48 * wn + 16 * j + fr) * kLRow + kk + fk];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = ws[(32 * wn + 16 * j + fr) * kLRow + kk + fk];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 3; ++j)
+        acc[0][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b[j], acc[0][j], 0, 0, 0);
     }
     __syncthreads();
   }
   // lane holds expert column fr, token rows fk + 4q of each 16 x 16 tile
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < 3; ++j) {
+    const int e = e0 + 48 * wn + 16 * j + fr;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int e = e0 + 32 * wn + 16 * j + fr;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int t = t0 + 32 * wm + 16 * i + fk + 4 * q;
-        if (t < T && e < E) logits[(int64_t)t * E + e] = acc[i][j][q] + (bias ? (double)bias[e] : 0.0);
-      }
+    for (int q = 0; q < 4; ++q) {
+      const int t = t0 + 16 * wm + fk + 4 * q;
+      if (t < T && e < E) logits[(int64_t)t * E + e] = acc[0][j][q] + (bias ? (double)bias[e] : 0.0);
     }
+  }
 }
 
 // ---------------------------------------------------------------- top-k + weights
