@@ -298,3 +298,40 @@ def test_prefill_range_flag(gpu):
     e3, _ = run(xd)
     assert e3 == 0, e3
     ml.close()
+
+
+def test_profile_stats_match_raw_reads(gpu):
+    """per-kernel timing: the same steps read once as totals and once as
+    statistics give the same kernels and launch counts; medians and typical
+    means are positive, and the typical mean (launches within twice the median)
+    is at most twice the median"""
+    import bit_moe_expert_router_amd as m
+    cfg = synth.CONFIGS["c1"]
+    say("[boundary] profile statistics")
+    dl = _layer("c1", gpu)
+    T, steps = 4, 6
+    ml = make_layer_api(cfg, dl, T)
+    xh, xd = x_device(cfg, gpu, tokens=T)
+    out = torch.empty((T, cfg.hidden), dtype=torch.float32, device=gpu)
+
+    def run():
+        for _ in range(steps):
+            r = ml.route(xd, dl.router, dl.bias)
+            ml.forward(0, xd, r, out)
+        torch.cuda.synchronize()
+
+    run()  # warm
+    m.moe_profile_read()  # drop anything recorded before
+    m.moe_profile_enable(True)
+    run()
+    raw = m.moe_profile_read()
+    run()
+    stats = m.moe_profile_read_stats()
+    m.moe_profile_enable(False)
+    assert raw and set(raw) == set(stats), (raw.keys(), stats.keys())
+    for k, (total, n) in raw.items():
+        t2, med, typ, n2 = stats[k]
+        assert n == n2 and n % steps == 0 and n > 0, (k, n, n2)
+        assert total > 0 and t2 > 0 and med > 0 and typ > 0, k
+        assert typ <= 2 * med * (1 + 1e-9) and med <= t2, (k, med, typ, t2)
+    ml.close()
