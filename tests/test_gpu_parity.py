@@ -346,26 +346,29 @@ def test_small_batch_all_pairs_dropped(gpu, name, T):
 
 
 @pytest.mark.parametrize("name", ["c2", "c3"])
-def test_small_batch_repeated_expert(gpu, name):
-    """two tokens that list one expert twice each (caller-supplied routing): the
-    expert owns four positions, more than a single pass of the one/two-token
-    kernels takes, so their later passes run; every pair and the combined output
-    against the oracle"""
-    say(f"[ffn] repeated expert {name} T=2")
+@pytest.mark.parametrize("T", [1, 2])
+def test_small_batch_repeated_expert(gpu, name, T):
+    """caller-supplied routing that lists one expert twice per token: at two
+    tokens the expert owns four positions, more than a single pass of the
+    one/two-token kernels takes, so their later passes run; at one token it owns
+    two, and every expert above it sits one position later than its rank, so the
+    down kernel's early h requests (position a for the a-th expert) miss there
+    and are made again; every pair and the combined output against the oracle"""
+    say(f"[ffn] repeated expert {name} T={T}")
     cfg = synth.CONFIGS[name]
     dl = layer_for(name, gpu)
-    T = 2
     xh, xd = x_device(cfg, gpu, tokens=T)
     ml = make_layer_api(cfg, dl, T)
     a = run_gpu(cfg, dl, xd, ml=ml)
     ids, w = a["ids"].copy(), a["w"].copy()
     e = int(ids[0, 0])
     ids[0, 1] = e
-    ids[1, 0] = e
-    ids[1, 1] = e
+    if T == 2:
+        ids[1, 0] = e
+        ids[1, 1] = e
     r = _caller_routing(ml, ids, w, cfg.n_experts, gpu)
     b = run_gpu(cfg, dl, xd, ml=ml, routing=r)
-    assert np.diff(b["offsets"])[e] == 4
+    assert np.diff(b["offsets"])[e] == 2 * T
     he = HostExperts(cfg)
     for t in range(T):
         for k in range(cfg.top_k):
