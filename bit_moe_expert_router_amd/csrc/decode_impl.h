@@ -8,29 +8,38 @@
 // cache, host-RAM streaming", field config.expert_cache.mechanism); a decode step
 // reads every picked expert's bytes once, so HBM bandwidth bounds it.
 //
-// Work decomposition.  A plan kernel lists the active experts (those owning at
-// least one pair) with their pair segment and blob pointers.  The GEMV kernels
-// then run a fixed grid of waves that take work items in a zig-zag order: an
-// item is (active expert, 64-row strip, matrix, chunk of GPW reduction groups).
-// A wave requests the item's codes and scales first (one 16-byte load per chunk
-// of a 64-row tile: 1,024 contiguous bytes per wave), then forms the partial
-// products of its 64 rows for up to XT of the expert's tokens at a time and
-// writes them to a partial buffer, one slice per chunk.  The codec's offset sums
-// of each activation row and group come precomputed (the plan launch for gate/up,
-// the SwiGLU pass for down).  The activations reach the dot products through scalar loads (one load
-// of 8 pairs serves all 64 lanes); a broadcast through LDS or a vector load would
-// move every byte 64 times, which made items with several tokens LDS-bound.  No
-// item waits on another: there are no block barriers
-// and no cross-wave reductions, and a wave that finishes an item starts the
-// next one at once, so the weight stream stays in flight.  The slices are added
-// in chunk order by the SwiGLU pass (gate/up) and by the combine (down): results
-// are deterministic.
+// Work decomposition, three or more tokens.  A plan kernel lists the active
+// experts (those owning at least one pair) with their pair segment and blob
+// pointers.  The GEMV kernels then run a fixed grid of waves that take work items
+// in a zig-zag order: an item is (active expert, 64-row strip, matrix, chunk of
+// GPW reduction groups).  A wave requests the item's codes and scales first (one
+// 16-byte load per chunk of a 64-row tile: 1,024 contiguous bytes per wave), then
+// forms the partial products of its 64 rows for the expert's tokens and writes
+// them to a partial buffer, one slice per chunk.  The codec's offset sums of each
+// activation row and group come precomputed (the plan launch for gate/up, the
+// SwiGLU pass for down).  The gate/up GEMV takes the activations through scalar
+// loads into v_dot2_f32_bf16 (one load of 8 pairs serves all 64 lanes; a
+// broadcast through LDS or a vector load would move every byte 64 times); the
+// down GEMV stages its positions' h rows in the wave's LDS region and runs on the
+// matrix cores.  No item waits on another: there are no block barriers and no
+// cross-wave reductions, and a wave that finishes an item starts the next one at
+// once, so the weight stream stays in flight.  The slices are added in chunk
+// order by the SwiGLU pass (gate/up) and by the combine (down): results are
+// deterministic.
+//
+// One or two tokens.  Block-level kernels without the plan launch: each block
+// finds its expert itself (one round trip for the offsets and the table), gate/up
+// splits the reduction over the block's waves and two blocks, and the down kernel
+// forms h from the gate/up parts while staging it and, in the block that
+// arrives last at its 64-row strip, the strip of the combined output.  Both run
+// their products on the matrix cores.
 //
 // Arithmetic (as in the unit codec): codes are expanded two at a time into bf16
-// (B + c) and multiplied with bf16 activation pairs by v_dot2_f32_bf16 in fp32; the
-// per-group constant sum_k (B_k + z) x_k is subtracted, then the group scale
-// applied.  The down matrix takes h as bf16 hi + bf16 remainder (two products per
-// code pair).
+// (B + c) and multiplied with bf16 activations in fp32 (v_dot2_f32_bf16, or
+// 4 x 4 x 4 bf16 matrix-core blocks); the per-group constant sum_k (B_k + z) x_k is
+// subtracted, then the group scale applied.  The down matrix takes h as bf16 hi +
+// bf16 remainder (two products per code pair, or two rows of the matrix-core
+// operand).
 #pragma once
 #include <algorithm>
 
