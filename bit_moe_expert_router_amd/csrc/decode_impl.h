@@ -541,75 +541,96 @@ struct Active {
   bool ok;   // CHECK: the routing is consistent (routing_ok_regs)
 };
 
+// The lookup in two halves, so that a kernel can request other data between the
+// lookup's loads and their use: issue() requests the offsets and table entries
+// (and with CHECK the routing check's inputs, P <= 64), resolve() finds the a-th
+// active expert from them.
+template <bool CHECK>
+struct ActiveLookup {
+  static constexpr int kSpec = 5;  // candidates per lane whose table entry is fetched up front
+  int nch;
+  int lo[16], hi[16];
+  moe_expert_ref ref[kSpec];
+  int cid, cs, csp;
+  __device__ __forceinline__ void issue(const int32_t* __restrict__ offsets,
+                                        const moe_expert_ref* __restrict__ table, int E, int P,
+                                        const int32_t* __restrict__ ids = nullptr,
+                                        const int32_t* __restrict__ sp = nullptr) {
+    const int lane = threadIdx.x & 63;
+    nch = (E + 63) / 64;
+    cid = -1, cs = 0, csp = -1;
+    if (CHECK) {
+      cid = lane < P ? ids[lane] : -1;
+      cs = lane < P ? sp[lane] : 0;
+      csp = (lane > 0 && lane < P) ? sp[lane - 1] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i < nch) {  // uniform
+        const int e = lane + 64 * i;
+        lo[i] = (e < E) ? offsets[e] : 0;
+        hi[i] = (e < E) ? offsets[e + 1] : 0;
+        if (i < kSpec) ref[i] = e < E ? table[e] : moe_expert_ref{nullptr, nullptr, nullptr};
+      }
+    }
+  }
+  __device__ __forceinline__ Active resolve(const moe_expert_ref* __restrict__ table, int E,
+                                            int P, int a) {
+    Active r{-1, 0, 0, 0, {nullptr, nullptr, nullptr}, true};
+    if (CHECK) r.ok = routing_ok_regs(lo, hi, cid, cs, csp, P, E);
+    // segments clamped into [0, P]: every position read stays inside the grouping
+    // buffers even when caller-supplied offsets are wrong (such a call writes no
+    // output)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i < nch) {
+        lo[i] = min(max(lo[i], 0), P);
+        hi[i] = min(max(hi[i], lo[i]), P);
+      }
+    }
+    int U = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i < nch) {
+        const bool nz = hi[i] > lo[i];
+        const uint64_t bal = __ballot(nz);
+        const int cnt = __popcll(bal);
+        if (r.e < 0 && a < U + cnt) {  // uniform: the a-th active expert is in this chunk
+          // lane holding it: the (a-U)-th set bit of bal
+          uint64_t m = bal;
+          for (int k = 0; k < a - U; ++k) m &= m - 1;
+          const int src = __ffsll((unsigned long long)m) - 1;
+          r.e = 64 * i + src;
+          r.seg0 = __shfl(lo[i], src);
+          r.n = __shfl(hi[i], src) - r.seg0;
+          if (i < kSpec) {
+            r.ptr[0] = (const void*)__shfl((long long)ref[i].gate, src);
+            r.ptr[1] = (const void*)__shfl((long long)ref[i].up, src);
+            r.ptr[2] = (const void*)__shfl((long long)ref[i].down, src);
+          } else {
+            const moe_expert_ref t = table[r.e];
+            r.ptr[0] = t.gate;
+            r.ptr[1] = t.up;
+            r.ptr[2] = t.down;
+          }
+        }
+        U += cnt;
+      }
+    }
+    r.U = U;
+    return r;
+  }
+};
+
 // CHECK: also check the routing (P <= 64), its loads in the same round trip
 template <bool CHECK>
 __device__ __forceinline__ Active find_active(const int32_t* __restrict__ offsets,
                                               const moe_expert_ref* __restrict__ table, int E,
                                               int P, int a, const int32_t* __restrict__ ids = nullptr,
                                               const int32_t* __restrict__ sp = nullptr) {
-  const int lane = threadIdx.x & 63;
-  constexpr int kSpec = 5;  // candidates per lane whose table entry is fetched up front
-  const int nch = (E + 63) / 64;
-  int lo[16], hi[16];
-  moe_expert_ref ref[kSpec];
-  int cid = -1, cs = 0, csp = -1;
-  if (CHECK) {
-    cid = lane < P ? ids[lane] : -1;
-    cs = lane < P ? sp[lane] : 0;
-    csp = (lane > 0 && lane < P) ? sp[lane - 1] : -1;
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (i < nch) {  // uniform
-      const int e = lane + 64 * i;
-      lo[i] = (e < E) ? offsets[e] : 0;
-      hi[i] = (e < E) ? offsets[e + 1] : 0;
-      if (i < kSpec) ref[i] = e < E ? table[e] : moe_expert_ref{nullptr, nullptr, nullptr};
-    }
-  }
-  Active r{-1, 0, 0, 0, {nullptr, nullptr, nullptr}, true};
-  if (CHECK) r.ok = routing_ok_regs(lo, hi, cid, cs, csp, P, E);
-  // segments clamped into [0, P]: every position read stays inside the grouping
-  // buffers even when caller-supplied offsets are wrong (such a call writes no
-  // output)
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (i < nch) {
-      lo[i] = min(max(lo[i], 0), P);
-      hi[i] = min(max(hi[i], lo[i]), P);
-    }
-  }
-  int U = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (i < nch) {
-      const bool nz = hi[i] > lo[i];
-      const uint64_t bal = __ballot(nz);
-      const int cnt = __popcll(bal);
-      if (r.e < 0 && a < U + cnt) {  // uniform: the a-th active expert is in this chunk
-        // lane holding it: the (a-U)-th set bit of bal
-        uint64_t m = bal;
-        for (int k = 0; k < a - U; ++k) m &= m - 1;
-        const int src = __ffsll((unsigned long long)m) - 1;
-        r.e = 64 * i + src;
-        r.seg0 = __shfl(lo[i], src);
-        r.n = __shfl(hi[i], src) - r.seg0;
-        if (i < kSpec) {
-          r.ptr[0] = (const void*)__shfl((long long)ref[i].gate, src);
-          r.ptr[1] = (const void*)__shfl((long long)ref[i].up, src);
-          r.ptr[2] = (const void*)__shfl((long long)ref[i].down, src);
-        } else {
-          const moe_expert_ref t = table[r.e];
-          r.ptr[0] = t.gate;
-          r.ptr[1] = t.up;
-          r.ptr[2] = t.down;
-        }
-      }
-      U += cnt;
-    }
-  }
-  r.U = U;
-  return r;
+  ActiveLookup<CHECK> l;
+  l.issue(offsets, table, E, P, ids, sp);
+  return l.resolve(table, E, P, a);
 }
 
 // Batches of one or two tokens (a single pass).  Each wave first requests the
@@ -923,16 +944,21 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
 
   // SPEC (one token): when the routing is consistent and the token lists each
   // expert once, the a-th active expert's pair sits at sorted position a, so the
-  // block requests the h parts of position a before its lookup, and uses them
-  // only if the lookup confirms that position (otherwise it requests them again)
+  // block requests the h parts of position a before its lookup completes, and
+  // uses them only if the lookup confirms that position (otherwise it requests
+  // them again).  The lookup's loads go first: loads return in order, so the
+  // lookup does not wait for the h parts.
+  ActiveLookup<false> lk;
+  lk.issue(offsets, table, E, P);
+  // the gate/up kernel's verdict on the caller's routing, read in the lookup's
+  // round trip
+  const int call_bad = ctr0[kCtrCallBad];
+  asm volatile("" ::: "memory");
   HS hsp;
   if (SPEC) hsp.load(part, P, I, min((int)blockIdx.x, P - 1), 1, wv_of_thread(), ng - 1,
                      threadIdx.x & 63);
   asm volatile("" ::: "memory");
-  // the gate/up kernel's verdict on the caller's routing, read in the lookup's
-  // round trip
-  const int call_bad = ctr0[kCtrCallBad];
-  const Active act = find_active<false>(offsets, table, E, P, blockIdx.x);
+  const Active act = lk.resolve(table, E, P, blockIdx.x);
   MOE_TR(tb + 1);
   const int strip = blockIdx.y;
   if (call_bad) return;  // inconsistent caller routing: the outputs are left untouched
