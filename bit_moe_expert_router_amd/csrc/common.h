@@ -292,7 +292,7 @@ __device__ __forceinline__ float wave_sum_uniform(float v) {
 // y = bf16(x / sqrt(mean(x^2) + eps)) of a row of H fp32 (H % 4 == 0, H <= 8192)
 // by a block of 256 threads: thread i holds float4 items i + 256*j (j ascending)
 // and sums their squares by fused multiply-adds in component order; the wave
-// sums are xor-shuffle reductions, and the four waves' sums are added in wave
+// sums are fixed-order DPP reductions, and the four waves' sums are added in wave
 // order.  The normalisation kernel and the routing kernels that normalise their
 // own input all use these functions, so they produce the same bf16 rows.
 constexpr int kRnPieces = 8;
@@ -307,9 +307,14 @@ __device__ __forceinline__ float rms_wave_sum(const rn_f4 (&v)[kRnPieces], int H
       ss = fmaf(v[i].z, v[i].z, ss);
       ss = fmaf(v[i].w, v[i].w, ss);
     }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-  return ss;
+  // the wave sum by DPP row prefixes and row totals (no LDS round trips)
+  ss += dpp_shift<0x111>(ss);
+  ss += dpp_shift<0x112>(ss);
+  ss += dpp_shift<0x114>(ss);
+  ss += dpp_shift<0x118>(ss);
+  ss += dpp_shift<0x142>(ss);
+  ss += dpp_shift<0x143>(ss);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ss), 63));
 }
 // part[w] = wave w's sum
 __device__ __forceinline__ float rms_inv(const float* part, int H, float eps) {

@@ -21,13 +21,35 @@ namespace moe {
 
 MOE_TRACE_DECL
 
+// Sum of a double over the wave in a fixed order, returned to every lane: row
+// prefix sums by DPP shifts (1, 2, 4, 8), then the row totals carried by
+// row_bcast 15 and 31 into lane 63 (no LDS round trips, unlike a shuffle
+// butterfly).
+template <int CTRL>
+__device__ __forceinline__ double dpp_shift_f64(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_shift_f64<0x111>(v);  // row_shr:1
+  v += dpp_shift_f64<0x112>(v);  // row_shr:2
+  v += dpp_shift_f64<0x114>(v);  // row_shr:4
+  v += dpp_shift_f64<0x118>(v);  // row_shr:8
+  v += dpp_shift_f64<0x142>(v);  // row_bcast:15
+  v += dpp_shift_f64<0x143>(v);  // row_bcast:31
+  const int lo = __builtin_amdgcn_readlane(__double2loint(v), 63);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(v), 63);
+  return __hiloint2double(hi, lo);
+}
+
 // ---------------------------------------------------------------- logits, small T
 // Block (b, c) = experts b*EPB .. b*EPB+EPB-1 x tokens c*NT .. c*NT+NT-1; 256
 // threads stride over H in float4 steps (items tid + 256*r of the row, r
 // ascending), each thread issuing all its loads of a batch (the router rows'
 // float4 and the matching activations of every token) before using any, so a
 // 5120-wide row costs one memory round trip; items past the row end load the
-// last item and add nothing.  Each thread's fp64 sum, then the wave's butterfly
+// last item and add nothing.  Each thread's fp64 sum, then the wave sum (DPP)
 // and the fixed-order sum of the four waves: the logits do not depend on EPB or
 // NT.  Several experts per block read the activation rows once per EPB experts
 // and, in the one-launch routing kernel, cut the number of blocks that meet at
@@ -84,9 +106,7 @@ __device__ __forceinline__ void logits_multi_block(const uint16_t* __restrict__ 
   for (int j = 0; j < EPB; ++j)
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      double v = acc[j][t];
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+      const double v = wave_sum_f64(acc[j][t]);
       if (lane == 0) red[wv][j * NT + t] = v;
     }
   __syncthreads();
@@ -175,9 +195,7 @@ __device__ __forceinline__ void logits_norm_block(const float* __restrict__ resi
   for (int j = 0; j < EPB; ++j)
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      double v = acc[j][t];
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+      const double v = wave_sum_f64(acc[j][t]);
       if (lane == 0) red[wv][j * NT + t] = v;
     }
   __syncthreads();
