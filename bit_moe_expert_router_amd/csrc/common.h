@@ -365,11 +365,21 @@ __device__ __forceinline__ int take_ticket(int32_t* ctr) {
 // ---------------------------------------------------------------- workspace
 // counters reserved for cross-block signalling (kept zero between calls): the
 // block that finds itself last to arrive does a kernel's final step and resets
-// its counter.  [kCtrRoute]: the routing kernel of small batches; [kCtrStrip +
-// s]: the blocks of 64-row strip s of the one/two-token down kernel.
-constexpr int kCounters = 1024;
+// its counter.  [kCtrRoute]: the routing kernel of small batches, whose blocks
+// first count in kRouteGroups group counters at [kCtrRouteGrp + g*kCtrStride];
+// [kCtrStrip + s*kCtrStride]: the blocks of 64-row strip s of the one/two-token
+// down kernel.  Each counter has a 128-byte line of its own: agent-scope atomics
+// on one line are performed one after another at the memory side (about 11 ns
+// each here), so 144 arrivals on one counter spread over 1.6 us, and the strips'
+// arrivals queued behind each other while their counters shared lines.
+constexpr int kCtrStride = 32;
 constexpr int kCtrRoute = 0;
-constexpr int kCtrStrip = 64;
+constexpr int kCtrStrip = kCtrStride;
+constexpr int kMaxStrips = 160;  // H <= 10240 for the fused strip combine
+constexpr int kCtrRouteGrp = kCtrStrip + kMaxStrips * kCtrStride;
+constexpr int kRouteGroups = 16;
+constexpr int kCounters = MOE_WS_COUNTER_BYTES / 4;
+static_assert(kCtrRouteGrp + kRouteGroups * kCtrStride <= kCounters, "counter region");
 // Two words of the same region are not counters.  [kCtrError] is the
 // workspace's error word (byte offset 4, MOE_WS_ERROR_OFFSET in moe.h): bit 0 is
 // set, and stays set, when moe_forward finds caller-supplied routing

@@ -1079,12 +1079,12 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
     __shared__ int s_last;
     wait_stores();
     __syncthreads();
-    if (threadIdx.x == 0) s_last = take_ticket(ctr + strip) == act.U - 1;
+    if (threadIdx.x == 0) s_last = take_ticket(ctr + strip * kCtrStride) == act.U - 1;
     MOE_TR(tb + 4);
     lds_barrier();
     if (s_last) {
       combine_strip(pair_out, ids, wts, K, E, H, shared, nsh, T, strip, out, resid);
-      if (threadIdx.x == 0) st_coherent(ctr + strip, 0);
+      if (threadIdx.x == 0) st_coherent(ctr + strip * kCtrStride, 0);
       MOE_TR(tb + 5);
     }
   }
@@ -1269,7 +1269,7 @@ hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* shared_ou
 #undef MOE_GU
     // down: h formed from the KP gate and up parts while staging (no SwiGLU
     // launch); each strip's last block combines (no combine launch)
-    const bool fuse = K <= kCombineMaxK && H / 64 <= kCounters - kCtrStrip;
+    const bool fuse = K <= kCombineMaxK && H / 64 <= kMaxStrips;
     int32_t* ctr = reinterpret_cast<int32_t*>(f.ws + L.counters) + kCtrStrip;
     float* cout = fuse ? f.out : nullptr;
     if (join) {  // the combine adds the shared expert's output

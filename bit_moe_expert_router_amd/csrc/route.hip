@@ -796,10 +796,12 @@ __global__ __launch_bounds__(1024) void k_topk_group_small(
 
 // ---------------------------------------------------------------- one launch, small T
 // Logits, top-k and grouping of a batch of one or two tokens in one kernel: the
-// multi-expert logit blocks above (logits stored written-through), then the
-// block that takes the last ticket, whose loads see every block's logits, picks
-// the top-k of every token (wave w takes tokens w, w+4, ...) and its first wave
-// groups the pairs.  It resets the ticket counter for the next call.  Larger
+// logit blocks above, one expert each (logits stored written-through), then the
+// block that takes the last ticket, whose loads see every block's logits: wave t
+// picks the top-k of token t and wave 2 groups the pairs.  The ticket has two
+// levels (a block counts in its group's counter, the last of a group in the
+// kernel's), so that no counter takes more than a few dozen arrivals; each
+// counter is reset by the block that finds it complete.  Larger
 // batches pick their tokens faster in a kernel of their own with one wave per
 // token (here the last block's four waves would take their tokens in turn:
 // 17.7 us at eight tokens against 14.8 us for the two launches).
@@ -822,7 +824,19 @@ __global__ __launch_bounds__(256) void k_route_small(
   __shared__ int s_last;
   wait_stores();
   __syncthreads();
-  if (threadIdx.x == 0) s_last = take_ticket(ctr) == (int)(gridDim.x * gridDim.y) - 1;
+  if (threadIdx.x == 0) {
+    const int nb = gridDim.x * gridDim.y;
+    // two levels: the last block of each group counts in the kernel's counter
+    // (each block's logits were stored and acknowledged before its group ticket)
+    const int g = bid % kRouteGroups, gsize = nb / kRouteGroups + (g < nb % kRouteGroups);
+    int32_t* cg = ctr + kCtrRouteGrp + g * kCtrStride;
+    bool last = false;
+    if (take_ticket(cg) == gsize - 1) {
+      st_coherent(cg, 0);  // every block of the group has counted
+      last = take_ticket(ctr) == min(kRouteGroups, nb) - 1;
+    }
+    s_last = last;
+  }
   MOE_TR(4 * bid + 2);
   lds_barrier();
   if (!s_last) return;
@@ -880,9 +894,9 @@ hipError_t launch_route(const moe_cfg& c, const RouteIn& in, int T, const float*
   }
   if (T <= kRouteMaxT && P <= 64) {  // one launch
     int32_t* ctr = counters + kCtrRoute;
-    const dim3 g1((E + 1) / 2);  // two experts per logit block
+    const dim3 g1(E);  // one expert per logit block
 #define MOE_RS1(NT, N, NORM)                                                                    \
-  MOE_LAUNCH(KID_ROUTE, (k_route_small<NT, N, 2, NORM>), g1, dim3(256), 0, s, x, in.resid,       \
+  MOE_LAUNCH(KID_ROUTE, (k_route_small<NT, N, 1, NORM>), g1, dim3(256), 0, s, x, in.resid,       \
              in.eps, in.xn, T, H, E, wr, bias, logits, K, ids, w, offsets, sorted_pairs, pair_pos, \
              ctr)
 #define MOE_RS(N)                                                                               \

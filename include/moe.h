@@ -68,6 +68,10 @@ typedef void* moe_stream_t; /* a hipStream_t */
  * matrix-core path meets a value outside fp16's exact range.  moe_workspace_init
  * clears it; so may the caller (stream-ordered write of 0). */
 #define MOE_WS_ERROR_OFFSET 4
+/* The workspace's first MOE_WS_COUNTER_BYTES bytes hold its cross-block
+ * counters, the error word and the current call's routing verdict; every call
+ * leaves them zero again, apart from the error word. */
+#define MOE_WS_COUNTER_BYTES 32768
 #define MOE_ERR_ROUTING 1
 /* Set by a call on the matrix-core path (T > 64) that met a value fp16 does not
  * hold exactly: a group scale s with |s| < 2^-14 or |s| > 8188 (so q*s, |q| <= 8,

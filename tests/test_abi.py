@@ -37,6 +37,14 @@ def test_binding_exports_match_header():
         assert callable(getattr(m, n))
 
 
+def test_binding_constants_match_header():
+    import bit_moe_expert_router_amd as m
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    defs = dict(re.findall(r"#define\s+(MOE_[A-Z_]+)\s+(\d+)", src))
+    for n in ("MOE_WS_ERROR_OFFSET", "MOE_WS_COUNTER_BYTES", "MOE_ERR_ROUTING", "MOE_ERR_RANGE"):
+        assert int(defs[n]) == getattr(m, n), n
+
+
 def test_binding_refuses_missing_library(tmp_path, monkeypatch):
     import importlib
     import sys

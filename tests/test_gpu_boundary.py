@@ -9,6 +9,8 @@ import numpy as np
 import pytest
 import torch
 
+import bit_moe_expert_router_amd as moe
+
 import oracle
 import synth
 from synth.device import DeviceLayer, x_device
@@ -129,7 +131,7 @@ def test_inconsistent_routing_sets_error_word(gpu, name, T):
         out, po = _forward(ml, xd, good, T, H, K, True)
         assert torch.equal(out, ref_out) and torch.equal(po, ref_po), label
         assert ml.error_word() == 0, label
-    ctr = ml.ws[:4096].view(torch.int32)
+    ctr = ml.ws[:moe.MOE_WS_COUNTER_BYTES].view(torch.int32)
     assert int(torch.count_nonzero(ctr)) == 0
     ml.close()
 

@@ -10,6 +10,8 @@ import numpy as np
 import pytest
 import torch
 
+import bit_moe_expert_router_amd as moe
+
 import oracle
 import synth
 from synth.device import DeviceLayer, x_device
@@ -392,7 +394,7 @@ def test_counters_left_zero(gpu):
         _, xd = x_device(cfg, gpu, tokens=T)
         for _ in range(2):
             run_gpu(cfg, dl, xd, ml=ml)
-        ctr = ml.ws[:4096].view(torch.int32)
+        ctr = ml.ws[:moe.MOE_WS_COUNTER_BYTES].view(torch.int32)
         assert int(torch.count_nonzero(ctr)) == 0, T
     ml.close()
 
