@@ -20,9 +20,10 @@ _LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_E_ARG, MOE_E_UNSUPPORTED, MOE_E_NOMEM, MOE_E_HIP, MOE_E_STATE = range(6)
 MOE_WS_ERROR_OFFSET = 4  # byte offset of the workspace's int32 error word (moe.h)
-MOE_WS_COUNTER_BYTES = 32768  # the workspace's leading counter region (moe.h)
+MOE_WS_COUNTER_BYTES = 167936  # the workspace's leading counter region (moe.h)
 MOE_ERR_ROUTING = 1
 MOE_ERR_RANGE = 4
+MOE_ERR_COMBINE = 8
 _STATUS = {0: "MOE_OK", 1: "MOE_E_ARG", 2: "MOE_E_UNSUPPORTED", 3: "MOE_E_NOMEM",
            4: "MOE_E_HIP", 5: "MOE_E_STATE"}
 

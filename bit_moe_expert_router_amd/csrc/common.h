@@ -363,23 +363,25 @@ __device__ __forceinline__ int take_ticket(int32_t* ctr) {
 }
 
 // ---------------------------------------------------------------- workspace
-// counters reserved for cross-block signalling (kept zero between calls): the
-// block that finds itself last to arrive does a kernel's final step and resets
-// its counter.  [kCtrRoute]: the routing kernel of small batches, whose blocks
-// first count in kRouteGroups group counters at [kCtrRouteGrp + g*kCtrStride];
-// [kCtrStrip + s*kCtrStride]: the blocks of 64-row strip s of the one/two-token
-// down kernel.  Each counter has a 128-byte line of its own: agent-scope atomics
-// on one line are performed one after another at the memory side (about 11 ns
-// each here), so 144 arrivals on one counter spread over 1.6 us, and the strips'
-// arrivals queued behind each other while their counters shared lines.
+// The workspace's leading region (MOE_WS_COUNTER_BYTES, kept zero between calls
+// apart from the error word).  Counters for cross-block signalling: the block
+// that finds itself last to arrive does a kernel's final step and resets the
+// counter.  [kCtrRoute]: the routing kernel of small batches, whose blocks first
+// count in kRouteGroups group counters at [kCtrRouteGrp + g*kCtrStride].  Each
+// counter has a 128-byte line of its own: agent-scope atomics on one line are
+// performed one after another at the memory side (about 11 ns each here), so
+// 144 arrivals on one counter spread over 1.6 us.  From int32 index kFxAcc: the
+// one/two-token combine's accumulator words, uint64[2][kMaxStrips * 64] (token,
+// output column), each zeroed again by the lane that completes it.
 constexpr int kCtrStride = 32;
 constexpr int kCtrRoute = 0;
-constexpr int kCtrStrip = kCtrStride;
-constexpr int kMaxStrips = 160;  // H <= 10240 for the fused strip combine
-constexpr int kCtrRouteGrp = kCtrStrip + kMaxStrips * kCtrStride;
+constexpr int kCtrRouteGrp = kCtrStride;
 constexpr int kRouteGroups = 16;
+constexpr int kMaxStrips = 160;  // H <= 10240 for the fused combine
+constexpr int kFxAcc = 1024;
 constexpr int kCounters = MOE_WS_COUNTER_BYTES / 4;
-static_assert(kCtrRouteGrp + kRouteGroups * kCtrStride <= kCounters, "counter region");
+static_assert(kCtrRouteGrp + kRouteGroups * kCtrStride <= kFxAcc, "counter region");
+static_assert(kFxAcc * 4 + 2 * kMaxStrips * 64 * 8 == MOE_WS_COUNTER_BYTES, "accumulator region");
 // Two words of the same region are not counters.  [kCtrError] is the
 // workspace's error word (byte offset 4, MOE_WS_ERROR_OFFSET in moe.h): bit 0 is
 // set, and stays set, when moe_forward finds caller-supplied routing
@@ -394,6 +396,8 @@ static_assert(kCtrError * 4 == MOE_WS_ERROR_OFFSET, "error word offset");
 // cannot hold exactly (a group scale, or h = silu(g)*u)
 constexpr int kErrRange = 4;
 static_assert(kErrRange == MOE_ERR_RANGE, "error bit");
+constexpr int kErrCombine = 8;
+static_assert(kErrCombine == MOE_ERR_COMBINE, "error bit");
 
 // ---------------------------------------------------------------- routing check
 // Caller-supplied routing is consistent when offsets[0] == 0, the offsets never

@@ -831,42 +831,48 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
 // the products run on the matrix cores (4 x 4 x 4 bf16 blocks: the rows of A are
 // the positions' h hi and lo from LDS, B the lanes' expanded code pairs), one
 // instruction per two code pairs for both positions and both halves of h.
-// y goes to row p = t*K + k of pair_out (stored written-through).  When `out` is
-// given, the block of each strip that takes the last ticket also forms
-// that strip's 64 columns of out[t] = sum_k w[t][k] y(t,k) (k ascending, pairs
-// with an id outside [0, E) skipped) + the shared expert's slices (added in
-// order): the same arithmetic, in the same order, as the combine kernel, one
-// launch fewer.  It resets the strip's ticket counter for the next call.
+// y goes to row p = t*K + k of pair_out when the caller asks for the pair
+// outputs (or the combine kernel reads them).  When `out` is given, the blocks
+// also form out[t] = sum_k w[t][k] y(t,k) (pairs with an id outside [0, E)
+// skipped) + the shared expert's slices through the fixed-point accumulator
+// words below: one launch fewer than a combine kernel, and no hand-off of the
+// pair outputs through memory.
 constexpr int kDNWaves = 4;
 constexpr int kCombineMaxK = 16;
+static_assert(kCombineMaxK < 32, "a combine word counts at most 31 pairs");
 
-// columns [64*strip, +64) of out for T <= 4 tokens (thread = (t, column))
-__device__ __forceinline__ void combine_strip(const float* y, const int32_t* __restrict__ ids,
-                                              const float* __restrict__ w, int K, int E, int H,
-                                              const float* shared, int nsh, int T, int strip,
-                                              float* __restrict__ out, float* __restrict__ resid) {
-  const int t = threadIdx.x >> 6;
-  if (t >= T) return;
-  const int n = strip * 64 + (threadIdx.x & 63);
-  float v[kCombineMaxK];
-#pragma unroll
-  for (int k = 0; k < kCombineMaxK; ++k)
-    v[k] = ld_coherent(y + ((int64_t)t * K + min(k, K - 1)) * H + n);
-  float acc = 0.f;
-#pragma unroll
-  for (int k = 0; k < kCombineMaxK; ++k) {
-    if (k < K) {
-      const int id = ids[t * K + k];
-      if (id >= 0 && id < E) acc = fmaf(w[t * K + k], v[k], acc);
-    }
-  }
+// The fixed-point combine of the one/two-token down kernel.  Every block adds,
+// per token t and output column n, its pairs' terms w*y (each exact in fp64,
+// rounded once to a multiple of 2^-28) into one 64-bit word of the workspace
+// with a single agent-scope atomic add: bits 0-4 count the pairs added, bits
+// 5-9 the pairs whose term was out of range (|w*y| >= 2^21 or not finite, added
+// as 0), bits 10-63 the signed sum (|sum| < 16 * 2^49 units).  Integer sums do
+// not depend on the order of the adds, so the result is the same on every run;
+// the lane whose add brings the count to the token's number of valid pairs holds
+// the complete sum in the add's return value, writes out[t][n] and zeroes the
+// word for the next call.  No data hand-off through memory, no ticket.
+__device__ __forceinline__ uint64_t fx_term(float w, float y) {
+  const double term = (double)w * (double)y;  // exact: 24 x 24 significant bits
+  const bool ok = fabs(term) < 0x1p21;        // false for NaN
+  const int64_t q = ok ? (int64_t)__builtin_rint(term * 0x1p28) : 0;
+  return ((uint64_t)q << 10) + (ok ? 1u : 33u);
+}
+__device__ __forceinline__ float fx_value(uint64_t tot) {
+  if ((tot >> 5) & 31) return __builtin_nanf("");
+  return (float)((double)((int64_t)tot >> 10) * 0x1p-28);  // |sum| < 2^53: exact in fp64
+}
+// out[t][n] = v + the shared expert's slices (added in slice order); a stack
+// layer also adds it to the residual
+__device__ __forceinline__ void fx_finish(float v, const float* shared, int nsh, int T, int t,
+                                          int n, int H, float* __restrict__ out,
+                                          float* __restrict__ resid) {
   if (shared) {
     float sh = 0.f;
     for (int q = 0; q < nsh; ++q) sh += shared[((int64_t)q * T + t) * H + n];
-    acc += sh;
+    v += sh;
   }
-  out[(int64_t)t * H + n] = acc;
-  if (resid) resid[(int64_t)t * H + n] += acc;  // a stack layer: the residual update
+  out[(int64_t)t * H + n] = v;
+  if (resid) resid[(int64_t)t * H + n] += v;
 }
 
 // h of the wave's groups for up to XT positions, formed from the KP gate and up
@@ -929,8 +935,8 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
     const int32_t* __restrict__ sorted_pairs, int H, int I, int P, int scale_f16,
     const float* __restrict__ part, float* pair_out, const int32_t* __restrict__ ids,
     const float* __restrict__ wts, int K, int T, const float* shared, int nsh,
-    int32_t* __restrict__ ctr, int32_t* __restrict__ ctr0, float* __restrict__ out,
-    float* __restrict__ resid) {
+    int32_t* __restrict__ ctr0, float* __restrict__ out, float* __restrict__ resid,
+    uint64_t* __restrict__ fxw, int store_y) {
   using C = UnitCodec<CODEC>;
   using HS = HFromParts<CODEC, GPW, XT, KP>;
   typedef short s4v __attribute__((ext_vector_type(4)));
@@ -962,9 +968,23 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
   MOE_TR(tb + 1);
   const int strip = blockIdx.y;
   if (call_bad) return;  // inconsistent caller routing: the outputs are left untouched
-  if (act.e < 0) {  // no expert for this block; with none at all, block 0 combines
-    if (out && act.U == 0 && blockIdx.x == 0)
-      combine_strip(pair_out, ids, wts, K, E, H, shared, nsh, T, strip, out, resid);
+  // each token's number of valid pairs: the count that completes its words
+  int nval0 = 0, nval1 = 0;
+  if (out) {
+    for (int k = 0; k < K; ++k) {
+      const int i0 = ids[k];
+      nval0 += i0 >= 0 && i0 < E;
+      if (T > 1) {
+        const int i1 = ids[K + k];
+        nval1 += i1 >= 0 && i1 < E;
+      }
+    }
+  }
+  if (act.e < 0) {  // no expert for this block
+    // block 0 writes the tokens without a valid pair (the shared expert only)
+    const int t = threadIdx.x >> 6;
+    if (out && blockIdx.x == 0 && t < T && (t ? nval1 : nval0) == 0)
+      fx_finish(0.f, shared, nsh, T, t, strip * 64 + (threadIdx.x & 63), H, out, resid);
     return;
   }
   const int seg0 = __builtin_amdgcn_readfirstlane(act.seg0);
@@ -980,6 +1000,8 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
   // pair ids of the expert's first 64 positions (lane = position), then h of the
   // first positions, all ahead of the weights
   int pids = sorted_pairs[seg0 + min(lane, n_e - 1)];  // (a checked routing: in [0, P))
+  float wpos = out ? wts[min(max(pids, 0), P - 1)] : 0.f;  // the pair's weight
+  uint64_t fa0 = 0, fa1 = 0;  // this wave's combine words, tokens 0 and 1
   const bool spec = SPEC && seg0 == (int)blockIdx.x && n_e == 1;  // uniform
   HS hst;
   int nt = min(n_e, XT);
@@ -1017,7 +1039,10 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
       nt = min(n_e - c0, XT);
       hst.load(part, P, I, seg0 + c0, nt, wv, ng - 1, lane);
       hst.store(xs, lane);
-      if (c0 % 64 == 0) pids = sorted_pairs[seg0 + c0 + min(lane, n_e - c0 - 1)];
+      if (c0 % 64 == 0) {
+        pids = sorted_pairs[seg0 + c0 + min(lane, n_e - c0 - 1)];
+        if (out) wpos = wts[min(max(pids, 0), P - 1)];
+      }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's own LDS writes
     for (int jp = 0; jp < nt; jp += kTokPerPass) {
@@ -1070,22 +1095,39 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
         for (int ww = 0; ww < kDNWaves; ++ww) y += red[ww][j][lane];
         const int idx = (c0 + jp + j) % 64;  // wave-uniform
         const int p = __builtin_amdgcn_readlane(pids, idx);
-        st_coherent(pair_out + (int64_t)p * H + row, y);
+        if (store_y) pair_out[(int64_t)p * H + row] = y;
+        if (out) {
+          const float wk = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wpos), idx));
+          const uint64_t d = fx_term(wk, y);
+          if (p >= K) fa1 += d; else fa0 += d;  // token p / K (T <= 2)
+        }
       }
       lds_barrier();
     }
   }
-  if (out) {  // the strip's last block combines
-    __shared__ int s_last;
-    wait_stores();
+  if (out) {  // the block's words, then one atomic add per token and column
+    __shared__ uint64_t fxs[kDNWaves][2][64];
+    fxs[wv][0][lane] = fa0;
+    fxs[wv][1][lane] = fa1;
     __syncthreads();
-    if (threadIdx.x == 0) s_last = take_ticket(ctr + strip * kCtrStride) == act.U - 1;
-    MOE_TR(tb + 4);
-    lds_barrier();
-    if (s_last) {
-      combine_strip(pair_out, ids, wts, K, E, H, shared, nsh, T, strip, out, resid);
-      if (threadIdx.x == 0) st_coherent(ctr + strip * kCtrStride, 0);
-      MOE_TR(tb + 5);
+    if (wv < T) {
+      const int t = wv;
+      uint64_t mine = 0;
+#pragma unroll
+      for (int ww = 0; ww < kDNWaves; ++ww) mine += fxs[ww][t][lane];
+      if (mine != 0) {  // the block holds pairs of token t (count >= 1)
+        uint64_t* wp = fxw + (int64_t)t * H + row;
+        const uint64_t tot =
+            __hip_atomic_fetch_add(wp, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + mine;
+        if ((int)(tot & 31) == (t ? nval1 : nval0)) {  // every pair of token t is in
+          st_coherent(wp, (uint64_t)0);
+          if ((tot >> 5) & 31) atomicOr(ctr0 + kCtrError, kErrCombine);
+          fx_finish(fx_value(tot), shared, nsh, T, t, row, H, out, resid);
+        }
+      } else if (blockIdx.x == 0 && (t ? nval1 : nval0) == 0) {
+        fx_finish(0.f, shared, nsh, T, t, row, H, out, resid);
+      }
     }
   }
 }
@@ -1268,10 +1310,13 @@ hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* shared_ou
     }
 #undef MOE_GU
     // down: h formed from the KP gate and up parts while staging (no SwiGLU
-    // launch); each strip's last block combines (no combine launch)
+    // launch); the blocks combine through the accumulator words (no combine
+    // launch)
     const bool fuse = K <= kCombineMaxK && H / 64 <= kMaxStrips;
-    int32_t* ctr = reinterpret_cast<int32_t*>(f.ws + L.counters) + kCtrStrip;
     float* cout = fuse ? f.out : nullptr;
+    // pair outputs are stored when the caller asks for them or the combine
+    // kernel reads them
+    const int store_y = f.pair_out != nullptr || !fuse;
     if (join) {  // the combine adds the shared expert's output
       const hipError_t e = hipStreamWaitEvent(s, join, 0);
       if (e != hipSuccess) return e;
@@ -1279,7 +1324,8 @@ hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* shared_ou
 #define MOE_DN1(N, KPT, SPEC)                                                                     \
   MOE_LAUNCH(KID_DOWN, (k_down_blk<CODEC, N, 2, KPT, SPEC>), dim3(maxU, H / 64),                   \
              dim3(64 * kDNWaves), 0, s, f.table, E, f.offsets, f.sorted_pairs, H, I, P, c.scale_f16, \
-             gpart, y, f.ids, f.w, K, T, shared_out, nsh, ctr, ctr0, cout, f.resid)
+             gpart, y, f.ids, f.w, K, T, shared_out, nsh, ctr0, cout, f.resid,                \
+             reinterpret_cast<uint64_t*>(ctr0 + kFxAcc), store_y)
 #define MOE_DN(N, KPT)                                                                           \
   case N:                                                                                        \
     if (T == 1) MOE_DN1(N, KPT, true); else MOE_DN1(N, KPT, false);                             \

@@ -69,15 +69,20 @@ typedef void* moe_stream_t; /* a hipStream_t */
  * clears it; so may the caller (stream-ordered write of 0). */
 #define MOE_WS_ERROR_OFFSET 4
 /* The workspace's first MOE_WS_COUNTER_BYTES bytes hold its cross-block
- * counters, the error word and the current call's routing verdict; every call
- * leaves them zero again, apart from the error word. */
-#define MOE_WS_COUNTER_BYTES 32768
+ * counters, the one/two-token combine's accumulators, the error word and the
+ * current call's routing verdict; every call leaves them zero again, apart from
+ * the error word. */
+#define MOE_WS_COUNTER_BYTES 167936
 #define MOE_ERR_ROUTING 1
 /* Set by a call on the matrix-core path (T > 64) that met a value fp16 does not
  * hold exactly: a group scale s with |s| < 2^-14 or |s| > 8188 (so q*s, |q| <= 8,
  * is not exact), or h = silu(g)*u with |h| >= 65504 (or not finite).  That call's
  * outputs are then not to be trusted; the GEMV path (T <= 64) has no such limit. */
 #define MOE_ERR_RANGE 4
+/* Set by a call of one or two tokens whose combine met a pair term w*y with
+ * |w*y| >= 2^21 (or not finite): that token's affected outputs are NaN.  The
+ * combine of these calls sums the terms exactly in 28-bit fixed point. */
+#define MOE_ERR_COMBINE 8
 
 typedef enum {
   MOE_OK = 0,

@@ -337,3 +337,47 @@ def test_profile_stats_match_raw_reads(gpu):
         assert total > 0 and t2 > 0 and med > 0 and typ > 0, k
         assert typ <= 2 * med * (1 + 1e-9) and med <= t2, (k, med, typ, t2)
     ml.close()
+
+
+@pytest.mark.parametrize("name,T", [("c2", 1), ("c2", 2), ("c3", 2)])
+def test_one_two_token_combine(gpu, name, T):
+    """The one/two-token combine sums the terms w*y in fixed point: the combined
+    output equals sum_k w[t][k] y(t,k), formed in fp64 from the call's own pair
+    outputs, to rounding (no shared expert); a term |w*y| >= 2^21 or not finite
+    gives NaN in the affected outputs of that token only and sets MOE_ERR_COMBINE;
+    the next call is unaffected and the workspace's leading region is zero again."""
+    cfg = synth.CONFIGS[name]
+    say(f"[boundary] combine {name} T={T}")
+    dl = _layer(name, gpu)
+    xh, xd = x_device(cfg, gpu, tokens=T + 1)
+    xh = xh[:T]
+    ml = make_layer_api(cfg, dl, T)
+    H, K, E = cfg.hidden, cfg.top_k, cfg.n_experts
+    ids, w, _, _ = oracle.route(xh, synth.router_f32(cfg), synth.zipf_bias(cfg), K)
+    off, sp, _ = oracle.permute(ids, E)
+    ref_out, ref_po = _forward(ml, xd, _routing(ml, ids, w, off, sp, gpu), T, H, K, True)
+    assert ml.error_word() == 0
+    po = ref_po.cpu().numpy().astype(np.float64)
+    if cfg.shared_inter == 0:
+        for t in range(T):
+            want = sum(float(w[t, k]) * po[t * K + k] for k in range(K))
+            got = ref_out[t].cpu().numpy().astype(np.float64)
+            assert np.linalg.norm(got - want) <= 1e-6 * np.linalg.norm(want), t
+    for label, val in (("huge", 1e30), ("nan", float("nan"))):
+        w2 = w.copy()
+        w2[0, 3] = val
+        out, po2 = _forward(ml, xd, _routing(ml, ids, w2, off, sp, gpu), T, H, K, True)
+        assert torch.equal(po2, ref_po), label  # the pair outputs do not depend on w
+        o0 = out[0].cpu().numpy()
+        bad = np.ones(H, bool) if label == "nan" else po[3] != 0
+        assert np.isnan(o0[bad]).all() and not np.isnan(o0[~bad]).any(), label
+        if T > 1:
+            assert torch.equal(out[1:], ref_out[1:]), label
+        assert ml.error_word() == moe.MOE_ERR_COMBINE, label
+        ml.clear_error()
+        out, _ = _forward(ml, xd, _routing(ml, ids, w, off, sp, gpu), T, H, K, True)
+        assert torch.equal(out, ref_out), label
+        assert ml.error_word() == 0, label
+    ctr = ml.ws[:moe.MOE_WS_COUNTER_BYTES].view(torch.int32)
+    assert int(torch.count_nonzero(ctr)) == 0
+    ml.close()
