@@ -476,3 +476,69 @@ def test_graph_replay_matches_eager(gpu, name, T):
         ml.forward(0, x_other, ro, other)
         torch.cuda.synchronize()
     ml.close()
+
+
+def _out_only(ml, xd, r, H):
+    out = torch.empty((xd.shape[0], H), dtype=torch.float32, device=xd.device)
+    ml.forward(0, xd, r, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+COMBINE_CASES = [("c1", 4), ("c2", 1), ("c2", 2), ("c2", 3), ("c3", 2), ("c3", 4), ("c3", 8),
+                 ("c3", 9), ("q2", 8), ("q4", 5)]
+
+
+@pytest.mark.parametrize("name,T", COMBINE_CASES)
+def test_combined_output_without_pair_outputs(gpu, name, T):
+    """a call that asks for the combined output only (decode batches of up to
+    eight tokens then combine inside the down kernel): every token against the
+    oracle's layer, against the same call with pair outputs (a different
+    summation of the same terms), and bit-identical on a second run"""
+    say(f"[ffn] out only {name} T={T}")
+    cfg = synth.CONFIGS[name]
+    dl = layer_for(name, gpu)
+    xh, xd = x_device(cfg, gpu, tokens=T)
+    ml = make_layer_api(cfg, dl, T)
+    a = run_gpu(cfg, dl, xd, ml=ml)
+    r = _caller_routing(ml, a["ids"], a["w"], cfg.n_experts, gpu)
+    b = _out_only(ml, xd, r, cfg.hidden)
+    c = _out_only(ml, xd, r, cfg.hidden)
+    assert np.array_equal(b, c)
+    he = HostExperts(cfg)
+    tabs = [[he.blobs(q)[m] for q in range(cfg.n_experts)] for m in range(3)]
+    ref, _ = oracle.moe_layer(xh, a["ids"], a["w"].astype(np.float64), *tabs, cfg.inter,
+                              cfg.bits, cfg.group, cfg.scale_f16, he.shared())
+    for t in range(T):
+        assert rel_err(b[t], ref[t]) <= TOL, t
+        assert rel_err(b[t], a["out"][t].astype(np.float64)) <= 1e-5, t
+    ml.close()
+
+
+@pytest.mark.parametrize("name,T", [("c3", 4), ("c2", 8)])
+def test_combined_output_dropped_pairs(gpu, name, T):
+    """combined output only, with caller routing in which token 1 has no valid
+    pair (its output is the shared expert's alone) and token 2 one pair left out"""
+    say(f"[ffn] out only, dropped pairs {name} T={T}")
+    cfg = synth.CONFIGS[name]
+    dl = layer_for(name, gpu)
+    xh, xd = x_device(cfg, gpu, tokens=T)
+    ml = make_layer_api(cfg, dl, T)
+    a = run_gpu(cfg, dl, xd, ml=ml)
+    ids, w = a["ids"].copy(), a["w"].copy()
+    ids[1, :] = -1
+    ids[2, 3] = cfg.n_experts
+    b = _out_only(ml, xd, _caller_routing(ml, ids, w, cfg.n_experts, gpu), cfg.hidden)
+    assert ml.error_word() == 0
+    he = HostExperts(cfg)
+    tabs = [[he.blobs(q)[m] for q in range(cfg.n_experts)] for m in range(3)]
+    ref, _ = oracle.moe_layer(xh, ids, w.astype(np.float64), *tabs, cfg.inter, cfg.bits,
+                              cfg.group, cfg.scale_f16, he.shared())
+    for t in range(T):
+        if t == 1 and he.shared() is None:
+            assert not np.any(b[t])
+        else:
+            assert rel_err(b[t], ref[t]) <= TOL, t
+    ctr = ml.ws[:moe.MOE_WS_COUNTER_BYTES].view(torch.int32)
+    assert int(torch.count_nonzero(ctr)) == 0
+    ml.close()
