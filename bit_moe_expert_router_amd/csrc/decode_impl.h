@@ -27,12 +27,13 @@
 // order by the SwiGLU pass (gate/up) and by the combine (down): results are
 // deterministic.
 //
-// One or two tokens.  Block-level kernels without the plan launch: each block
-// finds its expert itself (one round trip for the offsets and the table), gate/up
-// splits the reduction over the block's waves and two blocks, and the down kernel
-// forms h from the gate/up parts while staging it and, in the block that
-// arrives last at its 64-row strip, the strip of the combined output.  Both run
-// their products on the matrix cores.
+// One or two tokens.  Block-level kernels without the plan launch: each gate/up
+// block finds its expert itself (one round trip for the offsets and the table)
+// and one block per expert hands that entry to the down kernel; gate/up splits
+// the reduction over the block's waves and two blocks, and the down kernel forms
+// h from the gate/up parts while staging it and adds its weighted outputs into
+// the combine's integer words, whose last add writes the combined output.  Both
+// run their products on the matrix cores.
 //
 // Arithmetic (as in the unit codec): codes are expanded two at a time into bf16
 // (B + c) and multiplied with bf16 activations in fp32 (v_dot2_f32_bf16, or
@@ -513,9 +514,9 @@ __global__ __launch_bounds__(256, WPS) void k_gemv_mma(
 // Batches of one or two tokens have a single token pass per expert, and the
 // latency chain of the step dominates; they keep a block-level schedule with one
 // kernel launch fewer: block (a, strip, m*KP + kp) finds the a-th active expert
-// itself (one round trip for the offsets and the table entries together), its
-// four waves take groups g0 + wave + 4*i of part kp of the reduction, and the
-// waves' sums meet in LDS.
+// itself (one round trip for the offsets and the table entries together; block
+// (a, 0, 0) stores the result for the down kernel), its four waves take groups
+// g0 + wave + 4*i of part kp of the reduction, and the waves' sums meet in LDS.
 constexpr int kGUWaves = 4;
 constexpr int kTokPerPass = 2;
 #ifndef MOE_GU_AHEAD
@@ -646,7 +647,7 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
     const moe_expert_ref* __restrict__ table, int E, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pairs, int K, const uint16_t* __restrict__ x, int H, int I,
     int P, int KP, int scale_f16, float* __restrict__ gu, const int32_t* __restrict__ ids,
-    int32_t* __restrict__ ctr0) {
+    int32_t* __restrict__ ctr0, ActEntry* __restrict__ dact) {
   using C = UnitCodec<CODEC>;
   typedef short s4v __attribute__((ext_vector_type(4)));
   typedef float f4v __attribute__((ext_vector_type(4)));
@@ -671,6 +672,18 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
     act = find_active<false>(offsets, table, E, P, blockIdx.x);
   }
   MOE_TR(tb + 1);
+  // block (a, 0, 0) hands its lookup to the down kernel's blocks of expert a
+  if ((blockIdx.y | blockIdx.z) == 0 && threadIdx.x == 0) {
+    ActEntry ent;
+    ent.e = act.e;
+    ent.seg0 = act.seg0;
+    ent.n = act.n;
+    ent.pad = act.U;
+    ent.ptr[0] = nullptr;
+    ent.ptr[1] = nullptr;
+    ent.ptr[2] = act.ptr[2];
+    dact[blockIdx.x] = ent;
+  }
   if (act.e < 0) return;
   const int seg0 = __builtin_amdgcn_readfirstlane(act.seg0);
   const int n_e = __builtin_amdgcn_readfirstlane(act.n);
@@ -825,7 +838,8 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
 
 // down of the one/two-token path
 // Block (a, strip): rows [64*strip, +64) of the down matrix of the a-th active
-// expert; 4 waves take groups g = wave + 4*i, i < GPW.  The same schedule as the
+// expert (looked up by the gate/up kernel); 4 waves take groups g = wave + 4*i,
+// i < GPW.  The same schedule as the
 // gate/up kernel: each wave requests h (hi and lo rows) of up to XT of the
 // expert's positions for its groups into its own LDS region, then its weights;
 // the products run on the matrix cores (4 x 4 x 4 bf16 blocks: the rows of A are
@@ -931,12 +945,11 @@ struct HFromParts {
 
 template <int CODEC, int GPW, int XT, int KP, bool SPEC>
 __global__ __launch_bounds__(256, 2) void k_down_blk(
-    const moe_expert_ref* __restrict__ table, int E, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_pairs, int H, int I, int P, int scale_f16,
+    int E, const int32_t* __restrict__ sorted_pairs, int H, int I, int P, int scale_f16,
     const float* __restrict__ part, float* pair_out, const int32_t* __restrict__ ids,
     const float* __restrict__ wts, int K, int T, const float* shared, int nsh,
     int32_t* __restrict__ ctr0, float* __restrict__ out, float* __restrict__ resid,
-    uint64_t* __restrict__ fxw, int store_y) {
+    uint64_t* __restrict__ fxw, int store_y, const ActEntry* __restrict__ dact) {
   using C = UnitCodec<CODEC>;
   using HS = HFromParts<CODEC, GPW, XT, KP>;
   typedef short s4v __attribute__((ext_vector_type(4)));
@@ -948,23 +961,23 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
   const int tb = 4096 + 8 * (blockIdx.x + gridDim.x * blockIdx.y);
   MOE_TR(tb);
 
-  // SPEC (one token): when the routing is consistent and the token lists each
-  // expert once, the a-th active expert's pair sits at sorted position a, so the
-  // block requests the h parts of position a before its lookup completes, and
-  // uses them only if the lookup confirms that position (otherwise it requests
-  // them again).  The lookup's loads go first: loads return in order, so the
-  // lookup does not wait for the h parts.
-  ActiveLookup<false> lk;
-  lk.issue(offsets, table, E, P);
-  // the gate/up kernel's verdict on the caller's routing, read in the lookup's
-  // round trip
+  // The a-th active expert as block (a, 0, 0) of the gate/up kernel found it
+  // (its entry in dact: expert, segment, U in the pad field, the down matrix):
+  // scalar loads, one round trip, no lookup of its own.  SPEC (one token): when
+  // the routing is consistent and the token lists each expert once, the a-th
+  // active expert's pair sits at sorted position a, so the block requests the h
+  // parts of position a in the same round trip, and uses them only if the entry
+  // confirms that position (otherwise it requests them again).
+  const ActEntry* ae = dact + blockIdx.x;
+  const int ae_e = ae->e, ae_seg0 = ae->seg0, ae_n = ae->n, ae_u = ae->pad;
+  const void* ae_down = ae->ptr[2];
   const int call_bad = ctr0[kCtrCallBad];
   asm volatile("" ::: "memory");
   HS hsp;
   if (SPEC) hsp.load(part, P, I, min((int)blockIdx.x, P - 1), 1, wv_of_thread(), ng - 1,
                      threadIdx.x & 63);
   asm volatile("" ::: "memory");
-  const Active act = lk.resolve(table, E, P, blockIdx.x);
+  const Active act{ae_e, ae_u, ae_seg0, ae_n, {nullptr, nullptr, ae_down}, true};
   MOE_TR(tb + 1);
   const int strip = blockIdx.y;
   if (call_bad) return;  // inconsistent caller routing: the outputs are left untouched
@@ -1120,10 +1133,12 @@ __global__ __launch_bounds__(256, 2) void k_down_blk(
         uint64_t* wp = fxw + (int64_t)t * H + row;
         const uint64_t tot =
             __hip_atomic_fetch_add(wp, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + mine;
+        MOE_TR(tb + 4);
         if ((int)(tot & 31) == (t ? nval1 : nval0)) {  // every pair of token t is in
           st_coherent(wp, (uint64_t)0);
           if ((tot >> 5) & 31) atomicOr(ctr0 + kCtrError, kErrCombine);
           fx_finish(fx_value(tot), shared, nsh, T, t, row, H, out, resid);
+          MOE_TR(tb + 5);
         }
       } else if (blockIdx.x == 0 && (t ? nval1 : nval0) == 0) {
         fx_finish(0.f, shared, nsh, T, t, row, H, out, resid);
@@ -1302,7 +1317,7 @@ hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* shared_ou
   case N:                                                                                        \
     MOE_LAUNCH(KID_GATEUP, (k_gateup_smem<CODEC, N>), dim3(maxU, I / 64, 2 * KP),                 \
                dim3(64 * kGUWaves), 0, s, f.table, E, f.offsets, f.sorted_pairs, K, f.x, H, I, P,    \
-               KP, c.scale_f16, gpart, f.ids, ctr0);                                             \
+               KP, c.scale_f16, gpart, f.ids, ctr0, act);                                        \
     break;
     switch (gpw_gu) {
       MOE_GU(1) MOE_GU(2) MOE_GU(3) MOE_GU(4) MOE_GU(5)
@@ -1323,9 +1338,9 @@ hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* shared_ou
     }
 #define MOE_DN1(N, KPT, SPEC)                                                                     \
   MOE_LAUNCH(KID_DOWN, (k_down_blk<CODEC, N, 2, KPT, SPEC>), dim3(maxU, H / 64),                   \
-             dim3(64 * kDNWaves), 0, s, f.table, E, f.offsets, f.sorted_pairs, H, I, P, c.scale_f16, \
+             dim3(64 * kDNWaves), 0, s, E, f.sorted_pairs, H, I, P, c.scale_f16,                   \
              gpart, y, f.ids, f.w, K, T, shared_out, nsh, ctr0, cout, f.resid,                \
-             reinterpret_cast<uint64_t*>(ctr0 + kFxAcc), store_y)
+             reinterpret_cast<uint64_t*>(ctr0 + kFxAcc), store_y, act)
 #define MOE_DN(N, KPT)                                                                           \
   case N:                                                                                        \
     if (T == 1) MOE_DN1(N, KPT, true); else MOE_DN1(N, KPT, false);                             \
