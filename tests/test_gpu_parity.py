@@ -57,7 +57,8 @@ def test_device_fill_matches_host_generator(gpu):
                 assert np.array_equal(dev_t.cpu().numpy().view(np.uint16), h)
 
 
-ROUTE_CASES = [("c1", 4), ("c1", 1), ("c1", 16), ("c1", 37), ("c2", 1), ("c2", 2), ("c2", 5),
+ROUTE_CASES = [("c1", 4), ("c1", 1), ("c1", 3), ("c1", 16), ("c1", 37), ("c2", 1), ("c2", 2),
+               ("c2", 3), ("c2", 4), ("c2", 5),
                ("c3", 8), ("c3", 64), ("c3", 65), ("c3", 300), ("c5", 8192)]
 
 

@@ -63,7 +63,7 @@ def tied_router(cfg, xh, n_src):
     return Wr, b, copies
 
 
-CASES = [("c1", 1), ("c2", 1), ("c2", 2), ("c2", 5), ("c3", 16), ("c3", 24), ("c3", 37),
+CASES = [("c1", 1), ("c2", 1), ("c2", 2), ("c2", 3), ("c2", 4), ("c2", 5), ("c3", 16), ("c3", 24), ("c3", 37),
          ("c3", 300), ("c5", 8192)]
 
 
@@ -108,7 +108,7 @@ def test_routing_exact_ties(gpu, name, T):
 
 
 MASS = [("c1", 1, "all"), ("c2", 1, "all"), ("c2", 1, "blocks"), ("c2", 2, "blocks"),
-        ("c2", 2, "all"), ("c3", 5, "blocks"), ("c3", 9, "all"), ("c3", 37, "blocks"),
+        ("c2", 2, "all"), ("c2", 4, "blocks"), ("c2", 3, "all"), ("c3", 5, "blocks"), ("c3", 9, "all"), ("c3", 37, "blocks"),
         ("c3", 300, "all")]
 
 
