@@ -84,7 +84,7 @@ def parse():
     ap.add_argument("--layers", type=int, default=None,
                     help="resident layer copies the decode steps rotate over (default 20)")
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying HIP graphs")
-    ap.add_argument("--graph-steps", type=int, default=10,
+    ap.add_argument("--graph-steps", type=int, default=20,
                     help="consecutive layer steps captured in one HIP graph for the single-layer "
                          "workloads (as a decoder replays one graph over many layers); the largest "
                          "value up to this that divides both --steps and the rotated layer count")
