@@ -84,6 +84,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=None,
                     help="resident layer copies the decode steps rotate over (default 20)")
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--layer-calls", choices=("fused", "split"), default="fused",
+                    help="single-layer workloads: one moe_layer_forward call per step (fused) or "
+                         "moe_route then moe_forward (split)")
     ap.add_argument("--graph-steps", type=int, default=20,
                     help="consecutive layer steps captured in one HIP graph for the single-layer "
                          "workloads (as a decoder replays one graph over many layers); the largest "
@@ -226,8 +229,11 @@ def run_workload(name, a, dev, cpu_budget, cpu_jobs, main_tokens=None, one_threa
                 stack_forward(ml, resid, out, routers, biases, ybuf, out)
             return
         dl = layers[l]
-        r = ml.route(xd, dl.router, dl.bias)
-        ml.forward(l, xd, r, out)
+        if a.layer_calls == "fused":  # moe_layer_forward: routing and experts in one call
+            ml.layer_forward(l, xd, dl.router, dl.bias, out)
+        else:
+            r = ml.route(xd, dl.router, dl.bias)
+            ml.forward(l, xd, r, out)
 
     # distinct experts per layer (deterministic: same x, same layer -> same routing)
     U = []

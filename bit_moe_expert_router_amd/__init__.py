@@ -45,7 +45,7 @@ EXPORTS = ("moe_create", "moe_destroy", "moe_workspace_bytes", "moe_workspace_in
            "moe_forward", "moe_forward_noalloc", "moe_rmsnorm_bf16", "moe_last_error",
            "moe_profile_enable", "moe_profile_read", "moe_host_arena_create",
            "moe_host_arena_destroy", "moe_cache_state_bytes", "moe_cache_init", "moe_cache_step",
-           "moe_stack_layer", "moe_stream_read", "moe_profile_read_stats")
+           "moe_stack_layer", "moe_layer_forward", "moe_stream_read", "moe_profile_read_stats")
 MOE_CACHE_LFU, MOE_CACHE_CLOCK = 0, 1
 
 
@@ -75,6 +75,8 @@ def _load():
     lib.moe_stream_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
     lib.moe_stack_layer.argtypes = [vp, i32, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp,
                                     vp, vp, vp, ctypes.c_size_t, vp]
+    lib.moe_layer_forward.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      ctypes.c_size_t, vp]
     lib.moe_host_arena_create.argtypes = [ctypes.c_size_t, ctypes.POINTER(vp), ctypes.POINTER(vp)]
     lib.moe_host_arena_destroy.argtypes = [vp]
     lib.moe_cache_state_bytes.argtypes = [vp, i32]
@@ -97,7 +99,8 @@ def _load():
     for f in ("moe_create", "moe_destroy", "moe_workspace_init", "set_expert_table",
               "moe_set_shared", "moe_route", "moe_forward", "moe_forward_noalloc",
               "moe_rmsnorm_bf16", "moe_host_arena_create", "moe_host_arena_destroy",
-              "moe_cache_init", "moe_cache_step", "moe_stack_layer", "moe_stream_read"):
+              "moe_cache_init", "moe_cache_step", "moe_stack_layer", "moe_layer_forward",
+              "moe_stream_read"):
         getattr(lib, f).restype = st
     return lib
 
@@ -186,6 +189,15 @@ def moe_forward(ctx: int, layer: int, x_bf16, T: int, topk_ids, topk_w, expert_o
                            _ptr(pair_out), _ptr(ws), ws.numel() * ws.element_size(),
                            _stream(stream)),
            "moe_forward")
+
+
+def moe_layer_forward(ctx: int, layer: int, x_bf16, T: int, w_router, bias, topk_ids, topk_w,
+                      expert_offsets, sorted_pairs, pair_pos, out, pair_out, ws, stream=None):
+    _check(lib.moe_layer_forward(ctx, layer, _ptr(x_bf16), T, _ptr(w_router), _ptr(bias),
+                                 _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets),
+                                 _ptr(sorted_pairs), _ptr(pair_pos), _ptr(out), _ptr(pair_out),
+                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_layer_forward")
 
 
 def moe_forward_noalloc(ctx: int, layer: int, x_bf16, T: int, topk_ids, topk_w,

@@ -244,7 +244,7 @@ moe_status forward_impl(const char* who, moe_ctx* ctx, int32_t layer, const void
                         int32_t T, const int32_t* topk_ids, const float* topk_w,
                         const int32_t* expert_offsets, const int32_t* sorted_pairs, float* out,
                         float* pair_out, void* ws, size_t ws_bytes, moe_stream_t stream,
-                        float* resid = nullptr) {
+                        float* resid = nullptr, int pre_entries = 0) {
   if (!ctx) return fail(MOE_E_ARG, "%s: null context", who);
   const moe_cfg& c = ctx->cfg;
   if (layer < 0 || layer >= ctx->n_layers) return fail(MOE_E_ARG, "%s: bad layer %d", who, layer);
@@ -262,6 +262,7 @@ moe_status forward_impl(const char* who, moe_ctx* ctx, int32_t layer, const void
   moe::FwdArgs f{&c, ctx->d_tables + (size_t)layer * c.n_experts, sh.g, sh.u, sh.d,
                  (const uint16_t*)x_bf16, T, topk_ids, topk_w, expert_offsets, sorted_pairs,
                  out, pair_out, resid, (uint8_t*)ws, ctx->side, ctx->ev_fork, ctx->ev_join};
+  f.pre_entries = pre_entries;
   return hip_status(moe::launch_forward(f, (hipStream_t)stream), who);
 }
 
@@ -321,14 +322,61 @@ moe_status moe_stack_layer(moe_ctx* ctx, int32_t layer, float* resid, int32_t T,
     return fail(MOE_E_ARG, "moe_stack_layer: workspace %zu bytes < %lld needed", ws_bytes,
                 (long long)L.total);
   uint8_t* w8 = (uint8_t*)ws;
-  const moe::RouteIn in{nullptr, resid, eps, (uint16_t*)xn_bf16};
+  moe::RouteIn in{nullptr, resid, eps, (uint16_t*)xn_bf16};
+  int pre = 0;
+  if (!moe::prefill_eligible(c, T)) {  // the routing may hand over the expert entries
+    in.table = ctx->d_tables + (size_t)layer * c.n_experts;
+    in.entries = moe::act_entries(w8, L);
+    in.wrote_entries = &pre;
+  }
   const hipError_t e = moe::launch_route(c, in, T, w_router, bias, topk_ids, topk_w, expert_offsets,
                                          sorted_pairs, pair_pos, (double*)(w8 + L.logits),
                                          (int32_t*)(w8 + L.ghist), (int32_t*)(w8 + L.counters),
                                          (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e, "moe_stack_layer routing");
   return forward_impl("moe_stack_layer", ctx, layer, xn_bf16, T, topk_ids, topk_w, expert_offsets,
-                      sorted_pairs, out, nullptr, ws, ws_bytes, stream, resid);
+                      sorted_pairs, out, nullptr, ws, ws_bytes, stream, resid, pre);
+}
+
+moe_status moe_layer_forward(moe_ctx* ctx, int32_t layer, const void* x_bf16, int32_t T,
+                             const float* w_router, const float* bias, int32_t* topk_ids,
+                             float* topk_w, int32_t* expert_offsets, int32_t* sorted_pairs,
+                             int32_t* pair_pos, float* out, float* pair_out, void* ws,
+                             size_t ws_bytes, moe_stream_t stream) {
+  if (!ctx) return fail(MOE_E_ARG, "moe_layer_forward: null context");
+  const moe_cfg& c = ctx->cfg;
+  if (layer < 0 || layer >= ctx->n_layers) return fail(MOE_E_ARG, "moe_layer_forward: bad layer %d", layer);
+  if (T < 0 || T > c.max_tokens)
+    return fail(MOE_E_ARG, "moe_layer_forward: T=%d outside [0, %d]", T, c.max_tokens);
+  if (!ctx->table_set[layer])
+    return fail(MOE_E_STATE, "moe_layer_forward: expert table of layer %d never set", layer);
+  if (T == 0) return ok();
+  if (!x_bf16 || !w_router || !topk_ids || !topk_w || !expert_offsets || !sorted_pairs || !pair_pos ||
+      !out || !ws)
+    return fail(MOE_E_ARG, "moe_layer_forward: null pointer argument");
+  if (!aligned(x_bf16, 16) || !aligned(w_router, 16) || !aligned(out, 16) || !aligned(ws, 256) ||
+      (pair_out && !aligned(pair_out, 16)))
+    return fail(MOE_E_ARG,
+                "moe_layer_forward: x, w_router, out, pair_out must be 16-byte aligned, ws 256-byte aligned");
+  const moe::WsLayout L = moe::ws_layout(c, T);
+  if (ws_bytes < (size_t)L.total)
+    return fail(MOE_E_ARG, "moe_layer_forward: workspace %zu bytes < %lld needed", ws_bytes,
+                (long long)L.total);
+  uint8_t* w8 = (uint8_t*)ws;
+  moe::RouteIn in{(const uint16_t*)x_bf16, nullptr, 0.f, nullptr};
+  int pre = 0;
+  if (!moe::prefill_eligible(c, T)) {
+    in.table = ctx->d_tables + (size_t)layer * c.n_experts;
+    in.entries = moe::act_entries(w8, L);
+    in.wrote_entries = &pre;
+  }
+  const hipError_t e = moe::launch_route(c, in, T, w_router, bias, topk_ids, topk_w, expert_offsets,
+                                         sorted_pairs, pair_pos, (double*)(w8 + L.logits),
+                                         (int32_t*)(w8 + L.ghist), (int32_t*)(w8 + L.counters),
+                                         (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "moe_layer_forward routing");
+  return forward_impl("moe_layer_forward", ctx, layer, x_bf16, T, topk_ids, topk_w, expert_offsets,
+                      sorted_pairs, out, pair_out, ws, ws_bytes, stream, nullptr, pre);
 }
 
 moe_status moe_host_arena_create(size_t bytes, void** host, void** device) {

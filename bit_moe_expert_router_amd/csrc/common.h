@@ -478,6 +478,15 @@ constexpr int kDecGPWd = 3;
 
 // Layout of the caller's workspace for T tokens (byte offsets, 256-aligned).
 // Regions a mode does not use have size 0.
+// an active expert as the decode kernels use it: logical id (-1: none), its
+// first sorted position and pair count, and its table entry; pad holds U, the
+// number of active experts, where the one/two-token kernels store it
+struct ActEntry {
+  int32_t e, seg0, n, pad;
+  const void* ptr[3];  // gate, up, down
+};
+
+constexpr int kActHdrBytes = 64;  // the decode plan's header (U), then the entries
 struct WsLayout {
   int64_t counters;   // int32[kCounters]: zero between calls
   int64_t logits;     // double[T][E]
@@ -504,6 +513,11 @@ struct WsLayout {
   int64_t total;
 };
 
+static_assert(sizeof(ActEntry) == 40, "active-expert entries are 40 bytes");
+__host__ inline ActEntry* act_entries(uint8_t* ws, const WsLayout& L) {
+  return reinterpret_cast<ActEntry*>(ws + L.act + kActHdrBytes);
+}
+
 __host__ inline WsLayout ws_layout(const moe_cfg& c, int T) {
   WsLayout L{};
   int64_t P = (int64_t)T * c.top_k;
@@ -520,7 +534,7 @@ __host__ inline WsLayout ws_layout(const moe_cfg& c, int T) {
   // chunks of kDecGPW (gate/up) and kDecGPWd (down) reduction groups per decode work item
   const int64_t nch_gu = (c.hidden / c.group + kDecGPW - 1) / kDecGPW;
   const int64_t nch_dn = (c.inter / c.group + kDecGPWd - 1) / kDecGPWd;
-  L.act = take(pf ? 0 : 64 + 40 * (int64_t)c.n_experts);
+  L.act = take(pf ? 0 : kActHdrBytes + 40 * (int64_t)c.n_experts);
   L.osx = take(pf ? 0 : (int64_t)T * (c.hidden / c.group) * 4);
   L.osh = take(pf ? 0 : P * (c.inter / c.group) * 4);
   L.gpart = take(pf ? 0 : 2 * nch_gu * P * c.inter * 4);
@@ -609,6 +623,7 @@ struct FwdArgs {
   uint8_t* ws;
   hipStream_t side;             // shared-expert stream, fork and join events (or null)
   hipEvent_t ev_fork, ev_join;
+  int pre_entries = 0;          // the routing kernel stored the active experts' entries
 };
 
 hipError_t launch_prefill(const FwdArgs& f, const WsLayout& L, float* pair_out, hipStream_t s);
@@ -623,6 +638,11 @@ struct RouteIn {
   const float* resid;
   float eps;
   uint16_t* xn;
+  // optional (a layer call): the layer's table; the one-launch routing then also
+  // stores the active experts' entries at `entries` and sets *wrote_entries
+  const moe_expert_ref* table = nullptr;
+  ActEntry* entries = nullptr;
+  int* wrote_entries = nullptr;
 };
 hipError_t launch_route(const moe_cfg& c, const RouteIn& in, int T, const float* wr,
                         const float* bias, int32_t* ids, float* w, int32_t* offsets,

@@ -53,10 +53,6 @@ MOE_TRACE_DECL
 typedef uint32_t u32x4d __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 
-struct ActEntry {
-  int32_t e, seg0, n, pad;
-  const void* ptr[3];  // gate, up, down
-};
 
 // ---------------------------------------------------------------- plan
 // act_hdr[0] = U, the number of experts owning at least one pair; act[a] for
@@ -642,7 +638,7 @@ __device__ __forceinline__ Active find_active(const int32_t* __restrict__ offset
 // expanded code pairs as column l of B, one instruction per two code pairs for
 // both tokens.  Three waves per SIMD keep the whole weight stream of a decode
 // step in flight at once.
-template <int CODEC, int GPW>
+template <int CODEC, int GPW, bool PRE>
 __global__ __launch_bounds__(256, 3) void k_gateup_smem(
     const moe_expert_ref* __restrict__ table, int E, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pairs, int K, const uint16_t* __restrict__ x, int H, int I,
@@ -665,7 +661,11 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
   // every read here stays inside the buffers whatever the routing holds
   const bool first = (blockIdx.x | blockIdx.y | blockIdx.z) == 0;  // uniform
   Active act;
-  if (first) {
+  if (PRE) {  // the routing kernel of the same call stored the entries (scalar loads)
+    const ActEntry* ae = dact + blockIdx.x;
+    act = Active{ae->e, ae->pad, ae->seg0, ae->n, {ae->ptr[0], ae->ptr[1], ae->ptr[2]}, true};
+    if (first && threadIdx.x == 0) record_routing(ctr0, true);
+  } else if (first) {
     act = find_active<true>(offsets, table, E, P, blockIdx.x, ids, sorted_pairs);
     if (threadIdx.x == 0) record_routing(ctr0, act.ok);
   } else {
@@ -673,7 +673,7 @@ __global__ __launch_bounds__(256, 3) void k_gateup_smem(
   }
   MOE_TR(tb + 1);
   // block (a, 0, 0) hands its lookup to the down kernel's blocks of expert a
-  if ((blockIdx.y | blockIdx.z) == 0 && threadIdx.x == 0) {
+  if (!PRE && (blockIdx.y | blockIdx.z) == 0 && threadIdx.x == 0) {
     ActEntry ent;
     ent.e = act.e;
     ent.seg0 = act.seg0;
@@ -1289,9 +1289,8 @@ hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* shared_ou
   const moe_cfg& c = *f.c;
   const int H = c.hidden, I = c.inter, E = c.n_experts, K = c.top_k, T = f.T, P = T * K;
   int32_t* act_hdr = reinterpret_cast<int32_t*>(f.ws + L.act);
-  ActEntry* act = reinterpret_cast<ActEntry*>(f.ws + L.act + 64);
+  ActEntry* act = act_entries(f.ws, L);
   float* gpart = reinterpret_cast<float*>(f.ws + L.gpart);
-  static_assert(sizeof(ActEntry) == 40, "act list entries are 40 bytes");
   float* dpart = reinterpret_cast<float*>(f.ws + L.dpart);
   uint16_t* hh = reinterpret_cast<uint16_t*>(f.ws + L.hdec);
   uint16_t* hl = hh + (int64_t)P * I;
@@ -1313,17 +1312,20 @@ hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* shared_ou
     const int gpw_gu = ((ngh + KP - 1) / KP + kGUWaves - 1) / kGUWaves;
     const int gpw_dn = (I / C::G + kDNWaves - 1) / kDNWaves;
     float* y = f.pair_out ? f.pair_out : dpart;  // pair-order expert outputs
+#define MOE_GU1(N, PRE)                                                                          \
+    MOE_LAUNCH(KID_GATEUP, (k_gateup_smem<CODEC, N, PRE>), dim3(maxU, I / 64, 2 * KP),            \
+               dim3(64 * kGUWaves), 0, s, f.table, E, f.offsets, f.sorted_pairs, K, f.x, H, I, P,    \
+               KP, c.scale_f16, gpart, f.ids, ctr0, act)
 #define MOE_GU(N)                                                                                \
   case N:                                                                                        \
-    MOE_LAUNCH(KID_GATEUP, (k_gateup_smem<CODEC, N>), dim3(maxU, I / 64, 2 * KP),                 \
-               dim3(64 * kGUWaves), 0, s, f.table, E, f.offsets, f.sorted_pairs, K, f.x, H, I, P,    \
-               KP, c.scale_f16, gpart, f.ids, ctr0, act);                                        \
+    if (f.pre_entries) MOE_GU1(N, true); else MOE_GU1(N, false);                                 \
     break;
     switch (gpw_gu) {
       MOE_GU(1) MOE_GU(2) MOE_GU(3) MOE_GU(4) MOE_GU(5)
       default: return hipErrorInvalidValue;
     }
 #undef MOE_GU
+#undef MOE_GU1
     // down: h formed from the KP gate and up parts while staging (no SwiGLU
     // launch); the blocks combine through the accumulator words (no combine
     // launch)

@@ -806,13 +806,19 @@ __global__ __launch_bounds__(1024) void k_topk_group_small(
 // token (here the last block's four waves would take their tokens in turn:
 // 17.7 us at eight tokens against 14.8 us for the two launches).
 constexpr int kRouteMaxT = 2;
-template <int NT, int PER, int EPB, bool NORM>
+// ENT (a layer call): the grouping wave also stores the active experts' entries
+// for the expert kernels of the same call (entry a: the a-th active expert in
+// ascending id, its first sorted position, pair count, U and table entry; the
+// entries a in [U, min(E, P)) say "none"), so that those kernels need no lookup
+// of their own.  The routing here is consistent by construction.
+template <int NT, int PER, int EPB, bool NORM, bool ENT>
 __global__ __launch_bounds__(256) void k_route_small(
     const uint16_t* __restrict__ x, const float* __restrict__ resid, float eps,
     uint16_t* __restrict__ xn, int T, int H, int E, const float* __restrict__ wr,
     const float* __restrict__ bias, double* logits, int K, int32_t* __restrict__ ids,
     float* __restrict__ wout, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
-    int32_t* __restrict__ pair_pos, int32_t* __restrict__ ctr) {
+    int32_t* __restrict__ pair_pos, int32_t* __restrict__ ctr,
+    const moe_expert_ref* __restrict__ table, ActEntry* __restrict__ ent) {
   const int bid = blockIdx.x + gridDim.x * blockIdx.y;
   MOE_TR(4 * bid);
   if (NORM)
@@ -858,12 +864,54 @@ __global__ __launch_bounds__(256) void k_route_small(
   lds_barrier();  // s_ids only; the stores above need not have completed
   if (wv == kRouteMaxT) {
     const int P = T * K;
+    const int key = lane < P ? s_ids[lane] : -1;
+    // ENT: the pair's table entry, requested first, and its entry index, formed
+    // before the grouping's stores
+    int cnt = 0, less = 0, a = 0, U = 0;
+    bool first = false;
+    moe_expert_ref r{nullptr, nullptr, nullptr};
+    if (ENT && lane < P) r = table[key];  // (picked ids are in [0, E); P <= 64)
+    if (ENT) {
+      first = lane < P;
+      for (int q = 0; q < P; ++q) {
+        const int kq = __builtin_amdgcn_readlane(key, q);
+        cnt += kq == key;
+        less += kq < key;
+        first = first && !(kq == key && q < lane);
+      }
+      const uint64_t F = __ballot(first);
+      for (int q = 0; q < P; ++q)
+        if ((F >> q) & 1) a += __builtin_amdgcn_readlane(key, q) < key;
+      U = __popcll(F);
+    }
     if (P <= kTinyPairs)
-      wave_group_tiny<PER + 1>(lane < P ? s_ids[lane] : -1, P, E, offsets, sorted_pairs, pair_pos);
+      wave_group_tiny<PER + 1>(key, P, E, offsets, sorted_pairs, pair_pos);
     else
-      wave_group_small<PER + 1>(lane < P ? s_ids[lane] : -1, P, E, s_key, offsets, sorted_pairs,
-                                pair_pos);
+      wave_group_small<PER + 1>(key, P, E, s_key, offsets, sorted_pairs, pair_pos);
     if (lane == 0) st_coherent(ctr, 0);
+    if (ENT) {
+      const int maxU = min(E, P);
+      if (first) {
+        ActEntry v;
+        v.e = key;
+        v.seg0 = less;
+        v.n = cnt;
+        v.pad = U;
+        v.ptr[0] = r.gate;
+        v.ptr[1] = r.up;
+        v.ptr[2] = r.down;
+        ent[a] = v;
+      }
+      if (lane >= U && lane < maxU) {
+        ActEntry v;
+        v.e = -1;
+        v.seg0 = 0;
+        v.n = 0;
+        v.pad = U;
+        v.ptr[0] = v.ptr[1] = v.ptr[2] = nullptr;
+        ent[lane] = v;
+      }
+    }
     MOE_TR(2001);
   }
   if (wv < T) {
@@ -895,21 +943,26 @@ hipError_t launch_route(const moe_cfg& c, const RouteIn& in, int T, const float*
   if (T <= kRouteMaxT && P <= 64) {  // one launch
     int32_t* ctr = counters + kCtrRoute;
     const dim3 g1(E);  // one expert per logit block
-#define MOE_RS1(NT, N, NORM)                                                                    \
-  MOE_LAUNCH(KID_ROUTE, (k_route_small<NT, N, 1, NORM>), g1, dim3(256), 0, s, x, in.resid,       \
+    const bool ent = in.table != nullptr && in.entries != nullptr;
+#define MOE_RS2(NT, N, NORM, ENT)                                                               \
+  MOE_LAUNCH(KID_ROUTE, (k_route_small<NT, N, 1, NORM, ENT>), g1, dim3(256), 0, s, x, in.resid,  \
              in.eps, in.xn, T, H, E, wr, bias, logits, K, ids, w, offsets, sorted_pairs, pair_pos, \
-             ctr)
+             ctr, in.table, in.entries)
+#define MOE_RS1(NT, N, NORM)                                                                    \
+  if (ent) MOE_RS2(NT, N, NORM, true); else MOE_RS2(NT, N, NORM, false);
 #define MOE_RS(N)                                                                               \
   case N:                                                                                       \
     if (T == 1) {                                                                               \
-      if (norm) MOE_RS1(1, N, true); else MOE_RS1(1, N, false);                                 \
+      if (norm) { MOE_RS1(1, N, true) } else { MOE_RS1(1, N, false) }                           \
     } else {                                                                                    \
-      if (norm) MOE_RS1(2, N, true); else MOE_RS1(2, N, false);                                 \
+      if (norm) { MOE_RS1(2, N, true) } else { MOE_RS1(2, N, false) }                           \
     }                                                                                           \
     break;
     MOE_PER_SWITCH(MOE_RS)
 #undef MOE_RS
 #undef MOE_RS1
+#undef MOE_RS2
+    if (ent && in.wrote_entries) *in.wrote_entries = 1;
     return hipGetLastError();
   }
   if (T <= 32) {

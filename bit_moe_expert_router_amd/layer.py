@@ -78,6 +78,17 @@ class MoELayer:
                     r.sorted_pairs, out, pair_out, self.ws, stream)
         return out
 
+    def layer_forward(self, layer, x_bf16, w_router, bias, out, pair_out=None,
+                      stream=None) -> RoutingBuffers:
+        """routing + experts + combine of one layer in one library call; returns the routing"""
+        from . import moe_layer_forward
+        T = x_bf16.shape[0]
+        r = self.routing(T)
+        moe_layer_forward(self.ctx, layer, x_bf16, T, w_router, bias, r.topk_ids, r.topk_w,
+                          r.expert_offsets, r.sorted_pairs, r.pair_pos, out, pair_out, self.ws,
+                          stream)
+        return r
+
     def error_word(self) -> int:
         """the workspace's error word (waits for the device)"""
         from . import MOE_WS_ERROR_OFFSET

@@ -200,8 +200,9 @@ moe_status moe_route(moe_ctx* ctx, const void* x_bf16, int32_t T, const float* w
  * kernels (fast mode)": the shared expert beside the routed ones), given routing
  * (topk_ids, topk_w, expert_offsets, sorted_pairs from moe_route, or from the
  * caller in the same layout; pair_pos is not needed here).
- *   out       [T][H] fp32: out[t] = sum_{k=0..K-1} topk_w[t][k] * y(t,k) (k
- *             ascending, no atomics, bit-reproducible) + shared(x_t) if set
+ *   out       [T][H] fp32: out[t] = sum_{k=0..K-1} topk_w[t][k] * y(t,k) + shared(x_t)
+ *             if set, bit-reproducible: a fixed-order fp32 sum (k ascending), or
+ *             for one and two tokens an exact fixed-point sum (MOE_ERR_COMBINE)
  *   pair_out  [T*K][H] fp32 or NULL: row t*K + k is the unweighted expert output
  *             y(t,k); rows of pairs left out of the grouping are not written
  *   y(t,k) = down . (silu(gate . x_t) * (up . x_t)) of expert topk_ids[t][k],
@@ -288,6 +289,21 @@ moe_status moe_cache_step(moe_ctx* ctx, int32_t layer, const int32_t* expert_off
  * NULL, resid[t][h] += add[t][h] first (fp32), normalising the updated resid. */
 moe_status moe_rmsnorm_bf16(const moe_ctx* ctx, float* resid, const float* add, int32_t T,
                             float eps, void* y_bf16, moe_stream_t stream);
+
+/* One MoE layer in one call (page "0xSero/glm53-flash-offload", bullet "Decode
+ * kernels (fast mode)": a decode layer's launches fused): the routing of x_bf16
+ * into the routing buffers exactly as moe_route, then the expert FFNs and combine
+ * exactly as moe_forward on that routing, with the same results bit for bit.
+ * Because no caller code can run between the two, batches of one or two tokens
+ * let the routing kernel hand each active expert's table entry to the expert
+ * kernels, which then skip their own lookup.  Arguments, layouts, alignment and
+ * workspace as for moe_route and moe_forward; stream-ordered, capturable.
+ * Returns MOE_E_STATE if the layer's table was never set. */
+moe_status moe_layer_forward(moe_ctx* ctx, int32_t layer, const void* x_bf16, int32_t T,
+                             const float* w_router, const float* bias, int32_t* topk_ids,
+                             float* topk_w, int32_t* expert_offsets, int32_t* sorted_pairs,
+                             int32_t* pair_pos, float* out, float* pair_out, void* ws,
+                             size_t ws_bytes, moe_stream_t stream);
 
 /* One MoE layer of a stack on its residual stream, in one call:
  *   xn_bf16 = bf16(RMSNorm(resid))    (exactly as moe_rmsnorm_bf16 with add NULL)

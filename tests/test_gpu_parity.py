@@ -543,3 +543,39 @@ def test_combined_output_dropped_pairs(gpu, name, T):
     ctr = ml.ws[:moe.MOE_WS_COUNTER_BYTES].view(torch.int32)
     assert int(torch.count_nonzero(ctr)) == 0
     ml.close()
+
+
+LAYER_CASES = [("c1", 1), ("c1", 2), ("c1", 4), ("c2", 1), ("c2", 2), ("c3", 1), ("c3", 2),
+               ("c3", 8), ("q2", 1), ("q4", 2), ("c2", 65)]
+
+
+@pytest.mark.parametrize("name,T", LAYER_CASES)
+def test_layer_forward_equals_route_then_forward(gpu, name, T):
+    """moe_layer_forward (routing and experts in one call; at one and two tokens
+    the routing kernel hands the expert entries to the expert kernels) gives the
+    routing and the outputs of moe_route followed by moe_forward, bit for bit,
+    with and without pair outputs"""
+    say(f"[ffn] layer call {name} T={T}")
+    cfg = synth.CONFIGS[name]
+    dl = layer_for(name, gpu)
+    xh, xd = x_device(cfg, gpu, tokens=T)
+    ml = make_layer_api(cfg, dl, T)
+    a = run_gpu(cfg, dl, xd, ml=ml)
+    for with_po in (True, False):
+        out = torch.empty((T, cfg.hidden), dtype=torch.float32, device=gpu)
+        po = (torch.empty((T * cfg.top_k, cfg.hidden), dtype=torch.float32, device=gpu)
+              if with_po else None)
+        r = ml.layer_forward(0, xd, dl.router, dl.bias, out, po)
+        torch.cuda.synchronize()
+        assert np.array_equal(r.topk_ids.cpu().numpy(), a["ids"])
+        assert np.array_equal(r.topk_w.cpu().numpy(), a["w"])
+        assert np.array_equal(r.expert_offsets.cpu().numpy(), a["offsets"])
+        assert np.array_equal(r.sorted_pairs.cpu().numpy(), a["sorted"])
+        assert np.array_equal(r.pair_pos.cpu().numpy(), a["pos"])
+        assert np.array_equal(out.cpu().numpy(), a["out"]), with_po
+        if with_po:
+            assert np.array_equal(po.cpu().numpy(), a["pair_out"])
+    assert ml.error_word() == 0
+    ctr = ml.ws[:moe.MOE_WS_COUNTER_BYTES].view(torch.int32)
+    assert int(torch.count_nonzero(ctr)) == 0
+    ml.close()
