@@ -806,8 +806,8 @@ __global__ __launch_bounds__(1024) void k_topk_group_small(
 // token (here the last block's four waves would take their tokens in turn:
 // 17.7 us at eight tokens against 14.8 us for the two launches).
 constexpr int kRouteMaxT = 2;
-// ENT (a layer call): the grouping wave also stores the active experts' entries
-// for the expert kernels of the same call (entry a: the a-th active expert in
+// ENT (a layer call): the last block's fourth wave, beside the grouping wave,
+// stores the active experts' entries for the expert kernels of the same call (entry a: the a-th active expert in
 // ascending id, its first sorted position, pair count, U and table entry; the
 // entries a in [U, min(E, P)) say "none"), so that those kernels need no lookup
 // of their own.  The routing here is consistent by construction.
@@ -865,54 +865,50 @@ __global__ __launch_bounds__(256) void k_route_small(
   if (wv == kRouteMaxT) {
     const int P = T * K;
     const int key = lane < P ? s_ids[lane] : -1;
-    // ENT: the pair's table entry, requested first, and its entry index, formed
-    // before the grouping's stores
-    int cnt = 0, less = 0, a = 0, U = 0;
-    bool first = false;
-    moe_expert_ref r{nullptr, nullptr, nullptr};
-    if (ENT && lane < P) r = table[key];  // (picked ids are in [0, E); P <= 64)
-    if (ENT) {
-      first = lane < P;
-      for (int q = 0; q < P; ++q) {
-        const int kq = __builtin_amdgcn_readlane(key, q);
-        cnt += kq == key;
-        less += kq < key;
-        first = first && !(kq == key && q < lane);
-      }
-      const uint64_t F = __ballot(first);
-      for (int q = 0; q < P; ++q)
-        if ((F >> q) & 1) a += __builtin_amdgcn_readlane(key, q) < key;
-      U = __popcll(F);
-    }
     if (P <= kTinyPairs)
       wave_group_tiny<PER + 1>(key, P, E, offsets, sorted_pairs, pair_pos);
     else
       wave_group_small<PER + 1>(key, P, E, s_key, offsets, sorted_pairs, pair_pos);
     if (lane == 0) st_coherent(ctr, 0);
-    if (ENT) {
-      const int maxU = min(E, P);
-      if (first) {
-        ActEntry v;
-        v.e = key;
-        v.seg0 = less;
-        v.n = cnt;
-        v.pad = U;
-        v.ptr[0] = r.gate;
-        v.ptr[1] = r.up;
-        v.ptr[2] = r.down;
-        ent[a] = v;
-      }
-      if (lane >= U && lane < maxU) {
-        ActEntry v;
-        v.e = -1;
-        v.seg0 = 0;
-        v.n = 0;
-        v.pad = U;
-        v.ptr[0] = v.ptr[1] = v.ptr[2] = nullptr;
-        ent[lane] = v;
-      }
-    }
     MOE_TR(2001);
+  }
+  if (ENT && wv == kRouteMaxT + 1) {  // beside the grouping: the expert entries
+    const int P = T * K;
+    const int key = lane < P ? s_ids[lane] : -1;  // (picked ids are in [0, E); P <= 64)
+    moe_expert_ref r{nullptr, nullptr, nullptr};
+    if (lane < P) r = table[key];  // requested first
+    int cnt = 0, less = 0, a = 0;
+    bool first = lane < P;
+    for (int q = 0; q < P; ++q) {
+      const int kq = __builtin_amdgcn_readlane(key, q);
+      cnt += kq == key;
+      less += kq < key;
+      first = first && !(kq == key && q < lane);
+    }
+    const uint64_t F = __ballot(first);
+    for (int q = 0; q < P; ++q)
+      if ((F >> q) & 1) a += __builtin_amdgcn_readlane(key, q) < key;
+    const int U = __popcll(F), maxU = min(E, P);
+    if (first) {
+      ActEntry v;
+      v.e = key;
+      v.seg0 = less;
+      v.n = cnt;
+      v.pad = U;
+      v.ptr[0] = r.gate;
+      v.ptr[1] = r.up;
+      v.ptr[2] = r.down;
+      ent[a] = v;
+    }
+    if (lane >= U && lane < maxU) {
+      ActEntry v;
+      v.e = -1;
+      v.seg0 = 0;
+      v.n = 0;
+      v.pad = U;
+      v.ptr[0] = v.ptr[1] = v.ptr[2] = nullptr;
+      ent[lane] = v;
+    }
   }
   if (wv < T) {
     const float wk = topk_weight(lk, K);
