@@ -334,7 +334,9 @@ __device__ __forceinline__ uint32_t rms_bf16x2(float a, float b, float inv) {
 // point acknowledges it), and a block barrier orders all four waves before
 // thread 0 (3) takes its ticket, an agent-scope atomic add performed at that
 // same coherence point, whose total order puts every other block's completed
-// stores before the last ticket; (4) the last block reads the results with
+// stores before the last ticket (a two-level ticket chains this: a group's
+// last block counts at the next level only after its group ticket returned);
+// (4) the last block reads the results with
 // agent-scope atomic loads, which are not served from its own L2 and so cannot
 // see a stale line; (5) the signal fences around the wait and the branch on the
 // ticket (read back through LDS after a barrier) keep the compiler from moving

@@ -52,8 +52,8 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 // last item and add nothing.  Each thread's fp64 sum, then the wave sum (DPP)
 // and the fixed-order sum of the four waves: the logits do not depend on EPB or
 // NT.  Several experts per block read the activation rows once per EPB experts
-// and, in the one-launch routing kernel, cut the number of blocks that meet at
-// its ticket counter, where every arrival is serialised.
+// (the one-launch routing kernel takes one expert per block: its two-level
+// ticket keeps the arrivals serialised on any one counter few).
 constexpr int kLogitTok = 4;  // tokens per block, 3 to 32 tokens
 constexpr int kLogitEPB = 2;  // experts per block, 3 to 32 tokens
 constexpr int kRowBatch = 5;  // float4 items of a row per thread per round trip
