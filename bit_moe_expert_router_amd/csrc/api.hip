@@ -324,10 +324,14 @@ moe_status moe_stack_layer(moe_ctx* ctx, int32_t layer, float* resid, int32_t T,
   uint8_t* w8 = (uint8_t*)ws;
   moe::RouteIn in{nullptr, resid, eps, (uint16_t*)xn_bf16};
   int pre = 0;
-  if (!moe::prefill_eligible(c, T)) {  // the routing may hand over the expert entries
+  if (!moe::prefill_eligible(c, T)) {  // the routing may do the experts' lookup and plan
     in.table = ctx->d_tables + (size_t)layer * c.n_experts;
     in.entries = moe::act_entries(w8, L);
     in.wrote_entries = &pre;
+    in.act_hdr = (int32_t*)(w8 + L.act);
+    in.osx = (float*)(w8 + L.osx);
+    in.ctr0 = (int32_t*)(w8 + L.counters);
+    in.codec = moe::codec_of(c.bits, c.group);
   }
   const hipError_t e = moe::launch_route(c, in, T, w_router, bias, topk_ids, topk_w, expert_offsets,
                                          sorted_pairs, pair_pos, (double*)(w8 + L.logits),
@@ -365,10 +369,14 @@ moe_status moe_layer_forward(moe_ctx* ctx, int32_t layer, const void* x_bf16, in
   uint8_t* w8 = (uint8_t*)ws;
   moe::RouteIn in{(const uint16_t*)x_bf16, nullptr, 0.f, nullptr};
   int pre = 0;
-  if (!moe::prefill_eligible(c, T)) {
+  if (!moe::prefill_eligible(c, T)) {  // the routing may do the experts' lookup and plan
     in.table = ctx->d_tables + (size_t)layer * c.n_experts;
     in.entries = moe::act_entries(w8, L);
     in.wrote_entries = &pre;
+    in.act_hdr = (int32_t*)(w8 + L.act);
+    in.osx = (float*)(w8 + L.osx);
+    in.ctr0 = (int32_t*)(w8 + L.counters);
+    in.codec = moe::codec_of(c.bits, c.group);
   }
   const hipError_t e = moe::launch_route(c, in, T, w_router, bias, topk_ids, topk_w, expert_offsets,
                                          sorted_pairs, pair_pos, (double*)(w8 + L.logits),

@@ -230,6 +230,23 @@ struct UnitCodec<kQ2G128> {
 // Scales are stored in the codes' tile order: the scale of row 64*(tile's row
 // block) + lane and the tile's group sits at index tile*64 + lane, so a wave's
 // scales of one tile are 128 contiguous bytes.
+// a codec's pair offsets (the pairs per group returned), for kernels that are
+// not templated on the codec
+template <class C>
+__host__ inline int fill_pair_offsets(float* off) {
+  for (int P = 0; P < C::PAIRS; ++P) off[P] = C::pair_off(P);
+  return C::PAIRS;
+}
+__host__ inline int codec_pair_offsets(int codec, float* off) {
+  switch (codec) {
+    case kQ3G128: return fill_pair_offsets<UnitCodec<kQ3G128>>(off);
+    case kQ4G32: return fill_pair_offsets<UnitCodec<kQ4G32>>(off);
+    case kQ2G128: return fill_pair_offsets<UnitCodec<kQ2G128>>(off);
+    case kQ4G128: return fill_pair_offsets<UnitCodec<kQ4G128>>(off);
+    default: return 0;
+  }
+}
+
 __device__ __forceinline__ int64_t scale_idx(int64_t tile, int lane) { return tile * 64 + lane; }
 // A 16-bit scale is fetched as the aligned dword that contains it (the scales
 // region is 256-byte aligned, so the dword lies inside it; lanes 2i and 2i+1 load
@@ -641,10 +658,28 @@ struct RouteIn {
   float eps;
   uint16_t* xn;
   // optional (a layer call): the layer's table; the one-launch routing then also
-  // stores the active experts' entries at `entries` and sets *wrote_entries
+  // stores the active experts' entries at `entries`, and the routing of 3 to 8
+  // tokens does the decode plan's work (the active list at act_hdr / entries and
+  // the offset sums osx of the gate/up codec, whose pair offsets and group size
+  // are given); either sets *wrote_entries
   const moe_expert_ref* table = nullptr;
   ActEntry* entries = nullptr;
   int* wrote_entries = nullptr;
+  int32_t* act_hdr = nullptr;
+  float* osx = nullptr;
+  int32_t* ctr0 = nullptr;  // the workspace's counters (the routing verdict)
+  int codec = 0;
+};
+// the decode plan's work done by the routing kernel of 3 to 8 tokens
+struct PlanIn {
+  const moe_expert_ref* table;
+  int32_t* act_hdr;
+  ActEntry* act;
+  const uint16_t* x;  // the experts' input rows (bf16)
+  float* osx;         // [T][H/G]
+  int32_t* ctr0;
+  int H, G, pairs;
+  float off[64];      // the codec's pair offsets
 };
 hipError_t launch_route(const moe_cfg& c, const RouteIn& in, int T, const float* wr,
                         const float* bias, int32_t* ids, float* w, int32_t* offsets,

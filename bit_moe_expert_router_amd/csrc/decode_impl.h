@@ -1376,8 +1376,10 @@ hipError_t launch_decode_t(const FwdArgs& f, const WsLayout& L, float* shared_ou
   }
 
   float* osx = reinterpret_cast<float*>(f.ws + L.osx);
-  MOE_LAUNCH(KID_PLAN, k_plan_decode<CODEC>, dim3(1 + (T * (H / C::G) + 15) / 16), dim3(1024), 0,
-             s, f.offsets, f.ids, f.sorted_pairs, P, ctr0, f.table, E, act_hdr, act, f.x, T, H, osx);
+  if (!f.pre_entries)  // (in a layer call of up to 8 tokens the routing launch did the plan)
+    MOE_LAUNCH(KID_PLAN, k_plan_decode<CODEC>, dim3(1 + (T * (H / C::G) + 15) / 16), dim3(1024),
+               0, s, f.offsets, f.ids, f.sorted_pairs, P, ctr0, f.table, E, act_hdr, act, f.x, T,
+               H, osx);
   // four waves per SIMD: without the activation staging the GEMVs fit in 128
   // registers; three for 4-bit codes in groups of 128 (four 16-byte loads per unit)
   constexpr int kWps = C::CHUNKS > 3 ? 3 : 4;

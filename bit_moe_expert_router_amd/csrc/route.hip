@@ -664,6 +664,24 @@ __global__ __launch_bounds__(64) void k_group_scatter(const int32_t* __restrict_
 }
 
 // ---------------------------------------------------------------- grouping, small T
+// Among the live lanes: how many hold a key smaller than this lane's, and (eq) the
+// lanes that hold the same key, by one ballot per key bit from the top (keys in
+// [0, 2^nbits)).  Integer only.
+__device__ __forceinline__ int wave_rank(int key, bool live, int nbits, uint64_t& eq) {
+  eq = __ballot(live);
+  int less = 0;
+  for (int b = nbits - 1; b >= 0; --b) {
+    const uint64_t bal = __ballot(live && ((key >> b) & 1));
+    if ((key >> b) & 1) {
+      less += __popcll(eq & ~bal);
+      eq &= bal;
+    } else {
+      eq &= ~bal;
+    }
+  }
+  return less;
+}
+
 // Grouping of at most 64 pairs by one wave.  Lane p (pair p < P) has key id_p
 // (E for an id outside [0, E)).  Its sorted position is the number of pairs with
 // a smaller (key, pair index), counted from the top key bit down with one ballot
@@ -762,14 +780,34 @@ __device__ __forceinline__ void wave_group_tiny(int id, int P, int E,
 // Decode batches of 3 to 16 tokens: wave t picks the top-k of token t; once every
 // token's picks are in LDS, wave T (wave 0 at 16 tokens) groups the pairs while
 // the picking waves form their weights.
-template <int PER>
+// PLAN (a layer call of 3 to 8 tokens, whose routing is consistent by
+// construction): the launch also does the decode plan's work, so that the plan
+// launch is skipped.  Blocks 1.. form the gate/up codec's offset sums osx[t][g]
+// (one wave per (t, g), the same arithmetic as the plan kernel); block 0's wave
+// 15, beside the grouping wave, lists the active experts in the plan's order
+// (more pairs first, then lower id) with their table entries, stores U and
+// records the routing as consistent.
+template <int PER, bool PLAN>
 __global__ __launch_bounds__(1024) void k_topk_group_small(
     const double* __restrict__ logits, int T, int E, int K, int32_t* __restrict__ ids,
     float* __restrict__ wout, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
-    int32_t* __restrict__ pair_pos) {
+    int32_t* __restrict__ pair_pos, PlanIn pl) {
   __shared__ int32_t s_ids[64];
   __shared__ int s_key[128];
   const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
+  if (PLAN && blockIdx.x > 0) {  // the offset sums
+    const int ngx = pl.H / pl.G, it = (blockIdx.x - 1) * 16 + t;
+    if (it < T * ngx) {
+      const int tt = it / ngx, g = it - tt * ngx;
+      const uint32_t* x32 = reinterpret_cast<const uint32_t*>(pl.x);
+      const float off = lane < pl.pairs ? pl.off[lane] : 0.f;
+      const uint32_t pr = lane < pl.pairs ? x32[((int64_t)tt * pl.H + g * pl.G) / 2 + lane] : 0u;
+      const float v = wave_sum_uniform<kQ3G128>(off * (bf16_to_f32((uint16_t)pr) +
+                                                       bf16_to_f32((uint16_t)(pr >> 16))));
+      if (lane == 0) pl.osx[it] = v;
+    }
+    return;
+  }
   double lk = 0.0;
   if (t < T) {
     const int id = wave_topk_pick<PER>(logits + (int64_t)t * E, E, K, &lk);
@@ -787,6 +825,37 @@ __global__ __launch_bounds__(1024) void k_topk_group_small(
     else
       wave_group_small<PER + 1>(lane < P ? s_ids[lane] : -1, P, E, s_key, offsets, sorted_pairs,
                                 pair_pos);
+  }
+  if (PLAN && t == 15) {  // the active list (P <= 64; picked ids are in [0, E <= 1024))
+    const int P = T * K;
+    const bool live = lane < P;
+    const int key = live ? s_ids[lane] : 0;
+    moe_expert_ref r{nullptr, nullptr, nullptr};
+    if (live) r = pl.table[key];  // requested first
+    uint64_t eq;
+    const int less = wave_rank(key, live, 10, eq);  // pairs with a smaller id; same id: eq
+    const int cnt = __popcll(eq);
+    const bool first = live && (eq & ((1ull << lane) - 1ull)) == 0;
+    // the plan's order: more pairs first, then the lower id
+    const int key2 = ((63 - min(cnt, 63)) << 10) | key;
+    uint64_t eq2;
+    const int a = wave_rank(key2, first, 16, eq2);
+    const uint64_t F = __ballot(first);
+    if (first) {
+      ActEntry v;
+      v.e = key;
+      v.seg0 = less;
+      v.n = cnt;
+      v.pad = 0;
+      v.ptr[0] = r.gate;
+      v.ptr[1] = r.up;
+      v.ptr[2] = r.down;
+      pl.act[a] = v;
+    }
+    if (lane == 0) {
+      pl.act_hdr[0] = __popcll(F);
+      record_routing(pl.ctr0, true);
+    }
   }
   if (t < T) {
     const float wk = topk_weight(lk, K);
@@ -974,13 +1043,33 @@ hipError_t launch_route(const moe_cfg& c, const RouteIn& in, int T, const float*
                0, s, x, T, H, E, wr, bias, logits);
   }
   if (T <= 16 && P <= 64) {
+    PlanIn pl{};
+    const int ngx = c.group > 0 ? H / c.group : 0;
+    const bool plan = in.table && in.entries && in.act_hdr && in.osx && in.ctr0 && T <= 8 &&
+                      (pl.pairs = codec_pair_offsets(in.codec, pl.off)) > 0;
+    if (plan) {
+      pl.table = in.table;
+      pl.act_hdr = in.act_hdr;
+      pl.act = in.entries;
+      pl.x = norm ? in.xn : in.x;
+      pl.osx = in.osx;
+      pl.ctr0 = in.ctr0;
+      pl.H = H;
+      pl.G = c.group;
+    }
 #define MOE_TGS(N)                                                                             \
   case N:                                                                                      \
-    MOE_LAUNCH(KID_TOPK, k_topk_group_small<N>, dim3(1), dim3(64 * std::min(T + 1, 16)), 0, s, \
-               logits, T, E, K, ids, w, offsets, sorted_pairs, pair_pos);                      \
+    if (plan)                                                                                  \
+      MOE_LAUNCH(KID_TOPK, (k_topk_group_small<N, true>), dim3(1 + (T * ngx + 15) / 16),       \
+                 dim3(1024), 0, s, logits, T, E, K, ids, w, offsets, sorted_pairs, pair_pos, pl); \
+    else                                                                                       \
+      MOE_LAUNCH(KID_TOPK, (k_topk_group_small<N, false>), dim3(1),                            \
+                 dim3(64 * std::min(T + 1, 16)), 0, s, logits, T, E, K, ids, w, offsets,        \
+                 sorted_pairs, pair_pos, pl);                                                  \
     break;
     MOE_PER_SWITCH(MOE_TGS)
 #undef MOE_TGS
+    if (plan && in.wrote_entries) *in.wrote_entries = 1;
     return hipGetLastError();
   }
 #define MOE_TK(N)                                                                              \
