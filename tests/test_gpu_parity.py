@@ -545,16 +545,18 @@ def test_combined_output_dropped_pairs(gpu, name, T):
     ml.close()
 
 
-LAYER_CASES = [("c1", 1), ("c1", 2), ("c1", 4), ("c2", 1), ("c2", 2), ("c3", 1), ("c3", 2),
-               ("c3", 8), ("q2", 1), ("q4", 2), ("c2", 65)]
+LAYER_CASES = [("c1", 1), ("c1", 2), ("c1", 4), ("c1", 8), ("c2", 1), ("c2", 2), ("c2", 3),
+               ("c3", 1), ("c3", 2), ("c3", 8), ("c3", 9), ("q2", 1), ("q2", 8), ("q4", 2),
+               ("q4", 5), ("c2", 65)]
 
 
 @pytest.mark.parametrize("name,T", LAYER_CASES)
 def test_layer_forward_equals_route_then_forward(gpu, name, T):
     """moe_layer_forward (routing and experts in one call; at one and two tokens
-    the routing kernel hands the expert entries to the expert kernels) gives the
-    routing and the outputs of moe_route followed by moe_forward, bit for bit,
-    with and without pair outputs"""
+    the routing kernel hands the expert entries to the expert kernels, at three to
+    eight it also does the decode plan: the active list and the codec's offset
+    sums) gives the routing and the outputs of moe_route followed by moe_forward,
+    bit for bit, with and without pair outputs"""
     say(f"[ffn] layer call {name} T={T}")
     cfg = synth.CONFIGS[name]
     dl = layer_for(name, gpu)
